@@ -1,0 +1,258 @@
+/*
+ * csa.h -- C ABI of the compressed sparse attention (CSA / HCA) step for gfx950.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [P1] "Token 的一生：DSV4 架构与 DSpark" (security.zone.ci):
+ *        §1 (DSA -> DSV4 pipeline), §2.1 (C4 compressor), §2.2 (C4 KV cache
+ *        size, PagedIndexerMetadata), §3.1 (FP8/FP4 indexer query),
+ *        §3.2 (top-512 transform), §4 (Hadamard rotation).
+ *   [P2] "DeepSeek-V4 的交錯壓縮注意力（CSA/HCA）：將百萬標記長上下文變為可用資源"
+ *        (agents-report.net): section "架構突破" (CSA and HCA paragraphs) and
+ *        section "低精度與儲存策略的配合" (FP8 KV, BF16 RoPE dims, FP4 indexer).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is DEVICE memory owned by the caller, unless the
+ *    argument's comment says otherwise. The library never allocates, frees or
+ *    synchronises; it only enqueues kernels on the given stream and returns.
+ *  - All shape / format / null checks run on the host before any launch. On a
+ *    failed check the call returns CSA_ERR_INVALID (or CSA_ERR_UNSUPPORTED for a
+ *    well-formed but unimplemented combination) and touches no buffer.
+ *    A launch error reported by the runtime returns CSA_ERR_HIP.
+ *  - Device-resident integers (page tables, lengths, positions, indices) are
+ *    int32; -1 marks an empty selection slot. Values read from device memory
+ *    cannot be checked on the host: a page id outside [0, num_pages), a length
+ *    beyond the row's capacity or a position beyond the pool is a breach of
+ *    the caller's contract and its result is undefined.
+ *  - The library holds no mutable global state: calls on different streams are
+ *    independent and every call can be captured into a HIP graph.
+ *
+ * KV entry (one compressed or raw token), 576 dims = 512 latent + 64 RoPE
+ * ([P2] "低精度與儲存策略的配合": most KV dims in FP8, RoPE dims in BF16):
+ *    CSA_FP8_E4M3 pool: latent  uint8  [num_pages][page_size][512]  OCP e4m3fn codes
+ *                       scale   float  [num_pages][page_size]       one scale per entry,
+ *                                                                  value = code * scale
+ *                       rope    bf16   [num_pages][page_size][64]
+ *    CSA_F32 pool:      latent  float  [num_pages][page_size][512]
+ *                       rope    float  [num_pages][page_size][64]   (scale unused)
+ *  Slot of logical entry j of sequence s:
+ *      page_table[s * pt_stride + j / page_size] * page_size + j % page_size
+ *  ([P1] §2.2: raw pages hold 256 tokens, a C4 page page_size/4 = 64 entries.)
+ *
+ * Index-K pool (one row per compressed entry, dim = indexer head dim):
+ *    CSA_F32:      data float [num_pages][page_size][dim]                 (scale unused)
+ *    CSA_FP8_E4M3: data uint8 [num_pages][page_size][dim], scale float [num_pages][page_size]
+ *    CSA_MXFP4:    data uint8 [num_pages][page_size][dim/2]  two e2m1 codes per byte,
+ *                  element 2i in the low nibble; scale uint8 [num_pages][page_size][dim/32]
+ *                  e8m0 exponents (value = code * 2^(byte-127)), OCP MX v1.0.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed sizes of the method. */
+#define CSA_TOPK        512   /* [P1] §3.2: top-512 compressed entries per query   */
+#define CSA_C4_RATIO    4     /* [P1] §2.1: 4 raw tokens -> 1 compressed entry     */
+#define CSA_HCA_RATIO   128   /* [P2] HCA paragraph: about 128x compression        */
+#define CSA_RAW_PAGE    256   /* [P1] §2.2: page_size = 256 raw tokens            */
+#define CSA_C4_PAGE     64    /* [P1] §2.2: c4_page_size = page_size / 4          */
+#define CSA_KV_DIM      576   /* latent 512 + RoPE 64                              */
+#define CSA_LATENT_DIM  512
+#define CSA_ROPE_DIM    64
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID = 1,      /* bad argument; nothing launched, nothing written  */
+  CSA_ERR_UNSUPPORTED = 2,  /* valid but unimplemented format / shape combo     */
+  CSA_ERR_WORKSPACE = 3,    /* workspace too small (see csa_workspace_size)     */
+  CSA_ERR_HIP = 4           /* the HIP runtime reported a launch error          */
+} csa_status;
+
+typedef enum {
+  CSA_F32 = 0,
+  CSA_BF16 = 1,
+  CSA_FP8_E4M3 = 2,  /* OCP e4m3fn: bias 7, max 448, no infinities */
+  CSA_MXFP4 = 3      /* OCP MX v1.0: e2m1 elements, one e8m0 scale per 32 */
+} csa_fmt;
+
+/* Index preparation flags ([P1] §4: q and K go rope -> hadamard -> quant). */
+#define CSA_PREP_HADAMARD 1u  /* v <- H_D v / sqrt(D), Sylvester order */
+#define CSA_PREP_QUANT    2u  /* quantise to the index pool's format   */
+
+typedef struct {
+  void*   latent;        /* see the KV entry layout above */
+  float*  latent_scale;  /* FP8 pools only; NULL for F32 */
+  void*   rope;
+  int32_t fmt;           /* CSA_FP8_E4M3 or CSA_F32 */
+  int32_t page_size;     /* entries per page (64 compressed, 256 raw) */
+  int64_t num_pages;
+} csa_kv_pool;
+
+typedef struct {
+  void*   data;
+  void*   scale;         /* float [P][ps] for FP8, uint8 [P][ps][dim/32] for MXFP4, NULL for F32 */
+  int32_t fmt;           /* CSA_F32, CSA_FP8_E4M3 or CSA_MXFP4 */
+  int32_t dim;           /* indexer head dim: 64 or 128 (multiple of 32 for MXFP4) */
+  int32_t page_size;
+  int64_t num_pages;
+} csa_index_pool;
+
+/*
+ * c4_compress -- softmax-gated pooling of each block of `ratio` raw KV rows into
+ * one compressed entry, then quantised into a KV pool.
+ * Defined by [P1] §2.1 (block k covers raw positions [4k, 4k+3] and is emitted
+ * once position 4k+3 exists; output is seqlen//4 entries) and [P2] CSA paragraph
+ * (softmax-gated pooling with a learned positional bias); HCA uses the same
+ * form with ratio 128 ([P2] HCA paragraph).
+ * For block k of sequence b with rows x_i (i = 0..ratio-1, raw position ratio*k+i):
+ *     g_i = sum_d gate_w[d] * x_i[d] + gate_b[i],  a = softmax(g),  c = sum_i a_i x_i.
+ * c (576 dims) is stored at logical entry k of sequence b in `out`:
+ *   FP8 pool: scale = max(amax(c[0:512]), FLT_MIN) / 448, latent code = e4m3_rne(c/scale)
+ *   saturated at +-448, rope = bf16_rne(c[512:576]); F32 pool: stored as is.
+ * ratio == 1 stores each row unchanged apart from that quantisation (used to
+ * append raw tokens to the window pool).
+ *
+ *  x         [cu_rows[B]][576], CSA_BF16 or CSA_F32, row-major.
+ *  cu_rows   HOST int32[B+1]: rows of sequence b are x[cu_rows[b] .. cu_rows[b+1]).
+ *  start_pos HOST int32[B]: raw position of the first row of sequence b; must be
+ *            a multiple of ratio. Only complete blocks are emitted: entries
+ *            start_pos/ratio + i for i < (cu_rows[b+1]-cu_rows[b]) / ratio.
+ *  gate_w    float[576]; gate_b float[ratio].
+ *  page_table int32 [B][pt_stride] over out.page_size-entry pages.
+ * Returns CSA_ERR_INVALID if ratio is not 1, 4 or 128, a start_pos is not a
+ * multiple of ratio, cu_rows decreases, or a pointer is NULL.
+ */
+csa_status c4_compress(const void* x, csa_fmt x_fmt, const int32_t* cu_rows,
+                       const int32_t* start_pos, int32_t B, int32_t ratio,
+                       const float* gate_w, const float* gate_b,
+                       const int32_t* page_table, int32_t pt_stride,
+                       csa_kv_pool out, hipStream_t stream);
+
+/*
+ * csa_index_prep -- Hadamard rotation and quantisation of indexer rows (q rows
+ * or index-K rows): [P1] §3.1 and §4 (rope -> hadamard -> FP8/FP4 quant; RoPE
+ * is applied upstream of this library).
+ *   v       [rows][dim] CSA_BF16 or CSA_F32.
+ *   flags   CSA_PREP_HADAMARD: v <- H v / sqrt(dim), H the Sylvester Hadamard
+ *           matrix (dim a power of two, <= 128), computed in fp32.
+ *   out_fmt CSA_FP8_E4M3: out uint8 [*][dim] + out_scale float[*], per row
+ *                         scale = max(amax, FLT_MIN)/448, code = e4m3_rne(v/scale).
+ *           CSA_MXFP4:    out uint8 [*][dim/2] + out_scale uint8 [*][dim/32]; per 32
+ *                         elements X = floor(log2 amax) - 2 (X = -127 if amax == 0),
+ *                         code = e2m1_rne(v / 2^X) saturated at +-6, byte = X + 127.
+ *           CSA_F32:      out float [*][dim] (out_scale unused).
+ *   dst_rows optional int32[rows]: row i is written to output row dst_rows[i]
+ *           (e.g. a pool slot); NULL writes row i to output row i.
+ */
+csa_status csa_index_prep(const void* v, csa_fmt v_fmt, int64_t rows, int32_t dim,
+                          uint32_t flags, csa_fmt out_fmt, void* out, void* out_scale,
+                          const int32_t* dst_rows, hipStream_t stream);
+
+/*
+ * indexer_score -- lightning-indexer logits of every visible compressed entry
+ * ([P1] §3 C4Indexer, §3.2 `logits [bs, c4_seqlen]`; [P2] CSA paragraph: a light
+ * low-precision indexer scores compressed blocks for each query):
+ *     logits[t*ld + j] = sum_h w[t][h] * ReLU(qhat[t][h] . khat[j]),   0 <= j < row_len[t]
+ * with khat the dequantised index-K row of logical entry j of sequence row_seq[t]
+ * and qhat the dequantised query. Entries j >= row_len[t] are not written.
+ *   q        [T][H_I][D_I]. q_fmt CSA_BF16 / CSA_F32 (raw; prep flags decide what
+ *            happens before scoring) or CSA_FP8_E4M3 / CSA_MXFP4 (already
+ *            prepared, scales in q_scale: float [T][H_I] for FP8, uint8
+ *            [T][H_I][D_I/32] e8m0 for MXFP4). A prepared q must match k.fmt.
+ *   prep     0 or CSA_PREP_HADAMARD | CSA_PREP_QUANT for raw q: rotate and
+ *            quantise q exactly as csa_index_prep does, to k.fmt. An F32 pool takes
+ *            raw F32 q with prep 0.
+ *   w        float [T][H_I] head weights (w >= 0).
+ *   row_seq, row_len  int32 [T]: sequence and visible length of each query row
+ *            (decode: row_len = c4 length; prefill: row_len = min(N, (p+1)/4)).
+ *   logits   float, row stride ld >= max row_len.
+ *   q_used, q_used_scale  optional (NULL or both set): the prepared q codes and
+ *            scales in q_scale's layout, for inspection.
+ * Supported: F32 pool with D_I in {64,128}; FP8 / MXFP4 pools with D_I = 128.
+ */
+csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint32_t prep,
+                         const float* w, int32_t T, int32_t H_I, int32_t D_I,
+                         const int32_t* row_seq, const int32_t* row_len,
+                         const int32_t* page_table, int32_t pt_stride, csa_index_pool k,
+                         float* logits, int64_t ld, void* q_used, void* q_used_scale,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * topk512_page_select -- the fixed top-512 transform ([P1] §3.2): per row, the
+ * 512 largest logits among j < row_len[r], translated through the page table
+ * to physical slots page_table[row_seq[r]][j / c4_page_size] * c4_page_size
+ * + j % c4_page_size.
+ * Order: by logit descending, equal logits by lower j; -0 equals +0; NaN ranks
+ * below -inf. If row_len <= 512 every entry is selected. The selected entries are
+ * written in ascending j; the unused tail of a row is -1.
+ *   phys_idx    int32 [R][512] (required); logical_idx int32 [R][512] or NULL.
+ */
+csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
+                               const int32_t* row_len, const int32_t* row_seq,
+                               const int32_t* page_table, int32_t pt_stride,
+                               int32_t c4_page_size, int32_t* phys_idx,
+                               int32_t* logical_idx, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/*
+ * csa_sparse_attn -- MLA-style sparse attention of each query over its selected
+ * compressed entries plus a sliding window of raw tokens ([P1] §1: attention
+ * reads the 512 selected compressed KV; [P2] CSA paragraph: a sliding-window
+ * branch keeps recent uncompressed tokens). For query t at raw position
+ * p = q_pos[t] of sequence s = q_seq[t], head h:
+ *   E = { c4 slot phys_idx[t][i] : i < k_sel, != -1 }
+ *       U { raw slot of positions max(0, p-window+1) .. p via raw_page_table[s] }
+ *   score_e = softmax_scale * sum_{d<576} q[t][h][d] * kv_e[d]
+ *   out[t][h][:] = sum_e softmax(score)_e * kv_e[0:512]
+ * kv_e is the dequantised entry. All H heads share the KV (MQA).
+ *   q    [T][H][576] CSA_BF16 or CSA_F32; out [T][H][512] CSA_BF16 or CSA_F32.
+ *   c4 and raw pools must have the same fmt; raw.page_size is the raw page size.
+ *   Requires 1 <= window <= 128 + 1024 and k_sel <= 512.
+ */
+csa_status csa_sparse_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
+                           const int32_t* q_seq, const int32_t* q_pos,
+                           const int32_t* phys_idx, int32_t k_sel, csa_kv_pool c4,
+                           csa_kv_pool raw, const int32_t* raw_page_table,
+                           int32_t raw_pt_stride, int32_t window, float softmax_scale,
+                           void* out, csa_fmt out_fmt, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * hca_dense_attn -- heavily compressed attention ([P2] HCA paragraph: ~128x
+ * compression, then dense attention over the compressed blocks), plus the same
+ * sliding window as CSA. As csa_sparse_attn with
+ *   E = { hca entry j of sequence s : ratio*j + ratio - 1 <= p }  U  window(p).
+ */
+csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
+                          const int32_t* q_seq, const int32_t* q_pos, int32_t ratio,
+                          csa_kv_pool hca, const int32_t* hca_page_table,
+                          int32_t hca_pt_stride, csa_kv_pool raw,
+                          const int32_t* raw_page_table, int32_t raw_pt_stride,
+                          int32_t window, float softmax_scale, void* out,
+                          csa_fmt out_fmt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace sizes (bytes) for the calls that take `ws`.
+ * op: CSA_OP_INDEXER, CSA_OP_TOPK, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN.
+ * rows = T or R, max_len = longest row (entries), heads = H. */
+#define CSA_OP_INDEXER  0
+#define CSA_OP_TOPK     1
+#define CSA_OP_CSA_ATTN 2
+#define CSA_OP_HCA_ATTN 3
+size_t csa_workspace_size(int32_t op, int64_t rows, int64_t max_len, int32_t heads);
+
+const char* csa_status_string(csa_status s);
+
+/* Library version, e.g. "0.1.0". */
+const char* csa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

@@ -1,0 +1,440 @@
+"""Pins of the CPU oracle against facts fixed by the pages, by published format
+specifications and by mathematics -- never against the oracle itself.
+
+Each test names what it pins. Sources: [P1] "Token 的一生：DSV4 架构与 DSpark";
+[P2] "DeepSeek-V4 的交錯壓縮注意力（CSA/HCA）：將百萬標記長上下文變為可用資源".
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import csa_oracle as O
+from tests.conftest import read_golden
+
+# ---------------------------------------------------------------- constants
+
+
+def test_constants_match_pages():
+    consts = {ln.split()[0]: int(ln.split()[1]) for ln in read_golden("constants.txt")}
+    assert consts["c4_ratio"] == 4
+    assert consts["raw_page_size"] == O.RAW_PAGE
+    assert consts["c4_page_size"] == O.C4_PAGE == consts["raw_page_size"] // consts["c4_ratio"]
+    assert consts["topk"] == O.TOPK
+    assert consts["kv_rope_dims"] == O.ROPE_DIM and O.LATENT_DIM + O.ROPE_DIM == O.KV_DIM
+
+
+# ---------------------------------------------------------------- FP8 e4m3fn
+
+
+def test_e4m3_table_matches_torch_decode():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = O.E4M3_VALUES
+    finite = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[finite], ref[finite])
+    assert O.E4M3_VALUES[0x7E] == 448.0 and O.E4M3_VALUES[1] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_cast():
+    """torch's CPU cast is round-to-nearest-even but does not saturate, so the
+    input is clamped to +-448 first (the saturation the reading adopts)."""
+    g = np.random.default_rng(7)
+    v = np.concatenate([
+        g.standard_normal(200000) * 100,
+        g.standard_normal(50000) * 1e-3,            # subnormal range
+        O.E4M3_VALUES[np.isfinite(O.E4M3_VALUES)],  # exact codes
+        (O.E4M3_VALUES[1:126] + O.E4M3_VALUES[2:127]) / 2,  # exact midpoints (ties)
+        [0.0, -0.0, 447.9, 448.0, 449.0, -1e9, 1e9],
+    ]).astype(np.float32)
+    ref = torch.from_numpy(np.clip(v, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(v), ref)
+
+
+def test_e4m3_roundtrip_all_codes():
+    vals = O.E4M3_VALUES
+    codes = np.arange(256, dtype=np.uint8)
+    finite = np.isfinite(vals)
+    assert np.array_equal(O.e4m3_encode(vals[finite]), codes[finite])
+
+
+def test_quant_fp8_rows_scale_and_error_bound():
+    g = np.random.default_rng(3)
+    v = g.standard_normal((64, 128)).astype(np.float32)
+    codes, scale = O.quant_fp8_rows(v)
+    amax = np.abs(v).max(axis=1)
+    assert np.array_equal(scale, (amax / np.float32(448)).astype(np.float32))
+    # the largest element maps to (about) 448; relative error of e4m3 RNE <= 2^-4
+    deq = O.dequant_fp8_rows(codes, scale)
+    big = np.abs(v) >= scale[:, None] * 2 ** -6  # normal range of e4m3
+    assert np.all(np.abs(deq - v)[big] <= np.abs(v)[big] * 2 ** -4 * (1 + 1e-6))
+    assert np.all(np.abs(deq - v)[~big] <= (scale[:, None] * 2 ** -10 * (1 + 1e-6)).repeat(128, 1)[~big])
+
+
+def test_bf16_matches_torch_cast():
+    g = np.random.default_rng(5)
+    v = np.concatenate([g.standard_normal(100000), g.standard_normal(1000) * 1e-30,
+                        [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8]]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_bits(v), ref)
+    assert np.array_equal(O.bf16_decode(ref), torch.from_numpy(v).to(torch.bfloat16).double().numpy())
+
+
+# ---------------------------------------------------------------- MXFP4
+
+
+def test_e2m1_table_matches_ocp_spec():
+    rows = [ln.split() for ln in read_golden("e2m1_codes.txt")]
+    table = {int(c): float(v) for c, v in rows}
+    for code in range(8):
+        assert O.E2M1_VALUES[code] == table[code]
+        assert -O.E2M1_VALUES[code] == table[code + 8]
+
+
+def test_mxfp4_hand_worked_blocks():
+    for ln in read_golden("mxfp4_blocks.txt"):
+        vals, sbyte, codes = [p.split() for p in ln.split("|")]
+        v = np.zeros(32, dtype=np.float32)
+        v[:4] = [float(x) for x in vals]
+        packed, sc = O.quant_mxfp4_rows(v[None])
+        unpacked = np.empty(32, dtype=np.uint8)
+        unpacked[0::2] = packed[0] & 0xF
+        unpacked[1::2] = packed[0] >> 4
+        assert int(sc[0, 0]) == int(sbyte[0])
+        assert [int(c) for c in unpacked[:4]] == [int(c) for c in codes]
+
+
+def test_mxfp4_brute_force_nearest_even():
+    """Every element code is the nearest e2m1 value to v / 2^X (ties to the even
+    code), checked by exhaustive search over the 8 magnitudes."""
+    g = np.random.default_rng(11)
+    v = (g.standard_normal((300, 128)) * np.exp(g.uniform(-8, 8, (300, 1)))).astype(np.float32)
+    v[0, :32] = 0.0  # all-zero block
+    packed, sc = O.quant_mxfp4_rows(v)
+    X = sc.astype(np.int64) - 127
+    code = np.empty(v.shape, dtype=np.uint8)
+    code[:, 0::2] = packed & 0xF
+    code[:, 1::2] = packed >> 4
+    for r in range(0, 300, 7):
+        for blk in range(4):
+            x = X[r, blk]
+            seg = v[r, blk * 32:(blk + 1) * 32].astype(np.float64)
+            amax = np.abs(seg).max()
+            if amax == 0:
+                assert x == -127
+            else:
+                assert 2.0 ** (x + 2) <= amax < 2.0 ** (x + 3)  # top binade of e2m1 (4 <= amax/2^X < 8)
+            for i, val in enumerate(seg):
+                target = min(abs(val) / 2.0 ** x, 6.0)
+                d = np.abs(O.E2M1_VALUES - target)
+                best = np.flatnonzero(d == d.min())
+                best = best[best % 2 == 0][0] if len(best) > 1 else best[0]
+                c = code[r, blk * 32 + i]
+                assert (c & 7) == best
+                assert bool(c & 8) == bool(np.signbit(val))
+    deq = O.dequant_mxfp4_rows(packed, sc)
+    assert np.all(np.abs(deq) <= 6.0 * np.exp2(X).repeat(32, axis=1))
+
+
+# ---------------------------------------------------------------- Hadamard ([P1] §4)
+
+
+@pytest.mark.parametrize("D", [2, 8, 64, 128])
+def test_hadamard_equals_sylvester_matrix(D):
+    g = np.random.default_rng(D)
+    v = g.standard_normal((5, D))
+    H = scipy.linalg.hadamard(D).astype(np.float64)  # Sylvester construction
+    np.testing.assert_allclose(O.hadamard_rotate(v), v @ H.T / math.sqrt(D), rtol=0, atol=1e-12)
+    assert np.array_equal(H @ H.T, D * np.eye(D))
+
+
+def test_hadamard_preserves_scores():
+    """Rotating both q and k leaves unquantised indexer logits unchanged."""
+    g = np.random.default_rng(1)
+    q = g.standard_normal((64, 128))
+    k = g.standard_normal((300, 128))
+    w = g.uniform(0, 1, 64)
+    a = O.indexer_logits(q, w, k)
+    b = O.indexer_logits(O.hadamard_rotate(q), w, O.hadamard_rotate(k))
+    np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-9)
+
+
+# ---------------------------------------------------------------- compressor ([P1] §2.1, [P2])
+
+
+def test_compress_uniform_gate_is_block_mean():
+    g = np.random.default_rng(2)
+    x = g.standard_normal((64, 576))
+    out = O.compress_blocks(x, 0, 4, np.zeros(576), np.full(4, 0.37))
+    np.testing.assert_allclose(out, x.reshape(16, 4, 576).mean(axis=1), rtol=0, atol=1e-14)
+
+
+def test_compress_closed_form_bias_weights():
+    g = np.random.default_rng(4)
+    for ln in read_golden("compress_closed_form.txt"):
+        r, ms = ln.split("|")
+        ratio = int(r)
+        m = np.array([float(t) for t in ms.split()])
+        x = g.standard_normal((3 * ratio, 576))
+        out = O.compress_blocks(x, 8, ratio, np.zeros(576), np.log(m))
+        want = (m[None, :, None] * x.reshape(3, ratio, 576)).sum(axis=1) / m.sum()
+        np.testing.assert_allclose(out, want, rtol=0, atol=1e-13)
+
+
+def test_compress_one_hot_limit_and_bias_position():
+    """A bias of +60 on position i of the block selects row i (to e^-60)."""
+    g = np.random.default_rng(6)
+    x = g.standard_normal((40, 576))
+    for i in range(4):
+        b = np.zeros(4)
+        b[i] = 60.0
+        out = O.compress_blocks(x, 0, 4, np.zeros(576), b)
+        np.testing.assert_allclose(out, x[i::4], rtol=0, atol=1e-20 + 1e-24 + 1e-12)
+
+
+def test_compress_data_term_and_shift_invariance():
+    g = np.random.default_rng(8)
+    x = g.standard_normal((16, 576))
+    w = g.standard_normal(576) / 24
+    b = g.standard_normal(4) * 0.3
+    a = O.compress_blocks(x, 4, 4, w, b)
+    np.testing.assert_allclose(a, O.compress_blocks(x, 4, 4, w, b + 5.0), rtol=1e-12, atol=1e-14)
+    # the data term: doubling w on rows whose gates differ changes the result
+    assert not np.allclose(a, O.compress_blocks(x, 4, 4, 2 * w, b))
+    # explicit two-row check of the gate: softmax of w.x_i + b_i
+    g0 = x[4:8] @ w + b
+    p = np.exp(g0 - g0.max())
+    p /= p.sum()
+    np.testing.assert_allclose(a[1], p @ x[4:8], rtol=1e-12)
+    # partial tail block is not compressed
+    assert O.compress_blocks(x[:7], 0, 4, w, b).shape == (1, 576)
+
+
+def test_compress_ratio_one_is_identity():
+    g = np.random.default_rng(9)
+    x = g.standard_normal((10, 576))
+    np.testing.assert_array_equal(O.compress_blocks(x, 3, 1, g.standard_normal(576), [0.5]), x)
+
+
+def test_hca_ratio_128_mean():
+    g = np.random.default_rng(10)
+    x = g.standard_normal((300, 576))
+    out = O.compress_blocks(x, 0, 128, np.zeros(576), np.zeros(128))
+    assert out.shape == (2, 576)
+    np.testing.assert_allclose(out, x[:256].reshape(2, 128, 576).mean(axis=1), atol=1e-13)
+
+
+def test_kv_entry_storage():
+    g = np.random.default_rng(12)
+    c = g.standard_normal((20, 576))
+    lat, sc, rp = O.quant_kv_entries(c, "fp8")
+    assert lat.shape == (20, 512) and sc.shape == (20,) and rp.shape == (20, 64)
+    deq = O.dequant_kv_entries(lat, sc, rp, "fp8")
+    np.testing.assert_allclose(deq[:, 512:], c[:, 512:], rtol=2 ** -8)
+    assert np.all(np.abs(deq[:, :512] - c[:, :512]) <= np.maximum(np.abs(c[:, :512]) * 2 ** -4, sc[:, None] * 2 ** -9) * 1.0001)
+
+
+# ---------------------------------------------------------------- indexer ([P1] §3, [P2])
+
+
+def test_indexer_single_head_is_relu_dot():
+    g = np.random.default_rng(13)
+    q = g.standard_normal((1, 64))
+    k = g.standard_normal((50, 64))
+    np.testing.assert_allclose(O.indexer_logits(q, [1.0], k), np.maximum(k @ q[0], 0), rtol=1e-13)
+
+
+def test_indexer_relu_per_head_before_weighting():
+    """Two heads with q.k = 2 and -3, weights 1 and 1: the score is 2
+    (ReLU per head, then the weighted sum), not -1 and not 5."""
+    k = np.array([[1.0, 0.0]])
+    q = np.array([[2.0, 0.0], [-3.0, 0.0]])
+    assert O.indexer_logits(q, [1.0, 1.0], k)[0] == 2.0
+    assert O.indexer_logits(q, [0.5, 7.0], k)[0] == 1.0
+
+
+def test_indexer_scale_factoring():
+    """ReLU(a x) = a ReLU(x) for a > 0: folding a positive q scale into w."""
+    g = np.random.default_rng(14)
+    q = g.standard_normal((8, 64))
+    k = g.standard_normal((30, 64))
+    w = g.uniform(0, 1, 8)
+    a = g.uniform(0.1, 3, 8)
+    np.testing.assert_allclose(O.indexer_logits(q * a[:, None], w, k), O.indexer_logits(q, w * a, k), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- top-512 ([P1] §3.2)
+
+
+def test_topk_short_row_selects_everything():
+    g = np.random.default_rng(15)
+    for n in (0, 1, 100, 512):
+        logits = g.standard_normal(n)
+        assert np.array_equal(O.topk_logical(logits, n), np.arange(n))
+        phys, logical = O.topk_page_select(logits, n, np.arange(16))
+        assert np.array_equal(logical[:n], np.arange(n)) and np.all(logical[n:] == -1)
+        assert np.array_equal(phys, logical)  # identity page table
+
+
+def test_topk_all_equal_takes_lowest_indices():
+    assert np.array_equal(O.topk_logical(np.full(2000, 3.5), 2000), np.arange(512))
+
+
+def test_topk_equals_stable_argsort():
+    g = np.random.default_rng(16)
+    for n in (513, 1000, 4096, 33000):
+        logits = np.round(g.standard_normal(n) * 8) / 8  # many ties
+        ref = np.sort(np.argsort(-logits, kind="stable")[:512])
+        assert np.array_equal(O.topk_logical(logits, n), ref)
+
+
+def test_topk_signed_zero_nan_and_inf():
+    v = np.zeros(1000)
+    v[::2] = -0.0
+    assert np.array_equal(O.topk_logical(v, 1000), np.arange(512))  # -0 == +0
+    v = np.full(600, -np.inf)
+    v[:90] = 1.0
+    v[100] = np.nan
+    sel = O.topk_logical(v, 600)
+    assert 100 not in sel and len(sel) == 512 and set(range(90)) <= set(sel)
+    assert np.array_equal(sel[90:], np.array([j for j in range(90, 600) if j != 100][:422]))
+
+
+def test_topk_respects_row_len():
+    v = np.arange(3000, dtype=np.float64)
+    assert np.array_equal(O.topk_logical(v, 1000), np.arange(488, 1000))
+
+
+def test_page_table_identity_and_permutation_covariance():
+    g = np.random.default_rng(17)
+    n = 64 * 20
+    logits = g.standard_normal(n)
+    phys, logical = O.topk_page_select(logits, n, np.arange(20))
+    assert np.array_equal(phys, logical)
+    perm = g.permutation(40)[:20]
+    phys2, logical2 = O.topk_page_select(logits, n, perm)
+    assert np.array_equal(logical2, logical)
+    assert np.array_equal(phys2, perm[logical // 64] * 64 + logical % 64)
+
+
+# ---------------------------------------------------------------- attention ([P1] §1, [P2])
+
+
+def _sdpa(q, kv, scale):
+    """Library reference: torch's CPU scaled_dot_product_attention in float64."""
+    qt = torch.from_numpy(q)[None]
+    kt = torch.from_numpy(kv)[None]
+    vt = torch.from_numpy(np.ascontiguousarray(kv[:, :512]))[None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[0].numpy()
+
+
+def test_attention_matches_sdpa():
+    g = np.random.default_rng(18)
+    q = g.standard_normal((16, 576))
+    kv = g.standard_normal((300, 576))
+    s = 576 ** -0.5
+    np.testing.assert_allclose(O.attend(q, kv, s), _sdpa(q, kv, s), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_single_entry_and_convex_hull():
+    g = np.random.default_rng(19)
+    q = g.standard_normal((4, 576))
+    kv = g.standard_normal((1, 576))
+    np.testing.assert_allclose(O.attend(q, kv, 0.04), np.repeat(kv[:, :512], 4, 0), atol=1e-15)
+    kv = g.standard_normal((50, 576))
+    o = O.attend(q, kv, 0.5)
+    assert np.all(o <= kv[:, :512].max(0) + 1e-12) and np.all(o >= kv[:, :512].min(0) - 1e-12)
+
+
+def _mk_pools(g, n_c4, n_raw, fmt="f32", idx_fmt="f32", D=64):
+    c = g.standard_normal((n_c4, 576))
+    r = g.standard_normal((n_raw, 576))
+    c4 = O.KVPool(*O.quant_kv_entries(c, fmt), fmt)
+    raw = O.KVPool(*O.quant_kv_entries(r, fmt), fmt)
+    k = g.standard_normal((n_c4, D))
+    data, sc = O.index_prep(k, idx_fmt != "f32", idx_fmt)
+    return c4, raw, O.IndexPool(data, sc, idx_fmt)
+
+
+def test_csa_short_context_equals_dense_attention():
+    """c4 length <= 512: top-512 keeps everything, so CSA is dense attention
+    over all compressed entries plus the window (the method's special case)."""
+    g = np.random.default_rng(20)
+    L = 1800
+    n = L // 4
+    c4, raw, ip = _mk_pools(g, 64 * 8, 256 * 8)
+    pt = np.arange(8)
+    q_idx = g.standard_normal((8, 64))
+    w = g.uniform(0, 1, 8)
+    q = g.standard_normal((16, 576))
+    s = 576 ** -0.5
+    _, sel, out = O.csa_query(q_idx, w, ip, c4, raw, pt, pt, n, L - 1, q, 128, s)
+    assert np.array_equal(sel, np.arange(n))
+    kv = np.concatenate([c4.rows(np.arange(n)), raw.rows(np.arange(L - 128, L))])
+    np.testing.assert_allclose(out, _sdpa(q, kv, s), rtol=1e-10, atol=1e-12)
+
+
+def test_csa_brute_force_masked_attention():
+    """Brute force: score every compressed entry, mask the unselected ones to
+    -inf, softmax with the window, compare. Uses a random page table."""
+    g = np.random.default_rng(21)
+    L = 4096 + 4 * 37 + 2  # ragged tail
+    n = L // 4
+    pages = (L + 255) // 256
+    c4, raw, ip = _mk_pools(g, 64 * 40, 256 * 40, fmt="fp8", idx_fmt="fp8", D=128)
+    pt = g.permutation(40)[:pages]
+    q_idx_codes, q_sc = O.index_prep(g.standard_normal((64, 128)), True, "fp8")
+    q_hat = O.dequant_fp8_rows(q_idx_codes, q_sc)
+    w = g.uniform(0, 1, 64)
+    q = g.standard_normal((8, 576))
+    s = 576 ** -0.5
+    logits, sel, out = O.csa_query(q_hat, w, ip, c4, raw, pt, pt, n, L - 1, q, 128, s)
+    allk = c4.rows(O.page_slot(pt, np.arange(n), 64))
+    scores = s * q @ allk.T
+    mask = np.full(n, -np.inf)
+    order = sorted(range(n), key=lambda j: (-logits[j], j))[:512]
+    mask[order] = 0.0
+    win = raw.rows(O.page_slot(pt, np.arange(L - 128, L), 256))
+    full = np.concatenate([scores + mask, s * q @ win.T], axis=1)
+    p = np.exp(full - full.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    want = p @ np.concatenate([allk, win])[:, :512]
+    np.testing.assert_allclose(out, want, rtol=1e-10, atol=1e-12)
+
+
+def test_hca_short_context_is_window_only():
+    g = np.random.default_rng(22)
+    c4, raw, _ = _mk_pools(g, 64, 256)
+    q = g.standard_normal((4, 576))
+    pt = np.array([0])
+    out = O.hca_query(c4, raw, pt, pt, 100, 128, q, 128, 0.05)
+    np.testing.assert_allclose(out, _sdpa(q, raw.rows(np.arange(101)), 0.05), rtol=1e-10, atol=1e-12)
+
+
+def test_hca_at_ratio_4_equals_csa_when_short():
+    """Cross-mode: dense attention over all ratio-4 entries equals CSA when the
+    c4 length is <= 512 (everything selected)."""
+    g = np.random.default_rng(23)
+    c4, raw, ip = _mk_pools(g, 64 * 8, 256 * 8)
+    pt = np.arange(8)
+    L = 2000
+    q = g.standard_normal((8, 576))
+    _, _, a = O.csa_query(g.standard_normal((8, 64)), g.uniform(0, 1, 8), ip, c4, raw, pt, pt,
+                          L // 4, L - 1, q, 128, 0.04)
+    b = O.hca_query(c4, raw, pt, pt, L - 1, 4, q, 128, 0.04)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def test_prefill_query_equals_decode_at_that_length():
+    """Causal visibility 4j+3 <= p: a prefill query at p sees exactly the
+    entries a decode step with L = p+1 sees."""
+    for p in (0, 2, 3, 4, 7, 130, 131075):
+        n_vis = O.causal_row_len(p, 10 ** 9)
+        assert all(4 * j + 3 <= p for j in range(max(0, n_vis - 3), n_vis))
+        assert 4 * n_vis + 3 > p
+        assert n_vis == (p + 1) // 4
+    assert O.causal_row_len(131075, 33792) == 32769
+    assert O.hca_visible(127, 128) == 1 and O.hca_visible(126, 128) == 0
