@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: CSA decode at 128K context, batch 32 (32768 compressed entries per
+sequence, paged 64 per page under a random page table over 16384 pages;
+FP8 index-K with Hadamard rotation, 64 indexer heads x 128; 64 attention
+heads; top-512 plus a 128-token window). One step = the whole hot path for one
+new token of every sequence: compress the block the token completes, append
+the token to the raw window pool, prepare its index-K row, rotate + quantise
+the indexer query, score every compressed entry, select the top 512 through
+the page table, attend. Inputs are resident in HBM before timing; three
+copies of the large pools rotate across steps so no step is served from the
+last-level cache by its predecessor.
+
+Prints one JSON line. `roofline` is for the dominant kernel (the indexer scan),
+timed with HIP events on the launch stream; `cpu_baseline` is the plain CPU
+oracle timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-queries", type=int, default=8)
+    return ap.parse_args()
+
+
+def kernel_source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "compressed_sparse_attention_c4_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, src_hash: str, launches_bytes_key="bytes_per_launch"):
+    """HBM traffic per launch measured by rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy kernel), if taken on this exact kernel
+    source; else None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(kernel)
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return e.get(launches_bytes_key)
+
+
+def time_steps(W, steps, warmup, copies):
+    import torch
+    for i in range(warmup):
+        W.step(i % copies)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        W.step(i % copies, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    idx_ms = [a.elapsed_time(b) for a, b in evs]
+    return ms, float(np.mean(idx_ms)), float(np.median(idx_ms))
+
+
+def cpu_baseline(W, n_queries: int):
+    """The oracle, as it stands, on n_queries of the same decode step: rotate +
+    quantise the query, score all entries, top-512 through the page table,
+    attend. The oracle's pools are quantised by the oracle from the same
+    seeded raw draws (setup, not timed)."""
+    import torch
+    from oracle import csa_oracle as O
+    from workloads import gen
+    from workloads.device import _CHUNK
+    from threadpoolctl import threadpool_info
+
+    wl = W.wl
+    seed = wl.seed * 10
+    n_queries = min(n_queries, W.B)
+    rows_needed = {}
+    for b in range(n_queries):
+        n = int(W.N[b])
+        rows_needed[b] = O.page_slot(W.pt_host[b], np.arange(n), 64)
+    all_rows = np.unique(np.concatenate(list(rows_needed.values())))
+
+    def regen(rows, dim, seed_base):
+        out = np.empty((len(rows), dim), np.float32)
+        chunks = rows // _CHUNK
+        for c in np.unique(chunks):
+            sel = np.flatnonzero(chunks == c)
+            n = min(_CHUNK, W.P * 64 - c * _CHUNK)
+            v = gen.device_normal((n, dim), seed_base * 1000 + int(c))
+            out[sel] = v[torch.as_tensor(rows[sel] - c * _CHUNK, device="cuda")].float().cpu().numpy()
+        return out
+
+    kraw = regen(all_rows, wl.index_dim, seed + 1)
+    kvraw = regen(all_rows, 576, seed + 2)
+    codes, sc = O.index_prep(kraw, wl.hadamard, wl.index_fmt)
+    ipool_rows = {r: i for i, r in enumerate(all_rows)}
+    lat, lsc, rope = O.quant_kv_entries(kvraw, "fp8")
+    q_idx = W.q_idx[:n_queries].float().cpu().numpy()
+    w_idx = W.w_idx[:n_queries].cpu().numpy()
+    q_att = W.q_attn[:n_queries].float().cpu().numpy()
+    # window rows: regenerate the raw tail draw
+    tail = 2 * 256
+    x = gen.device_normal((int(sum(np.minimum(W.lens, tail))), 576), seed + 3).float().cpu().numpy()
+    raw_rows = O.quant_kv_entries(x, "fp8")
+    cu = np.concatenate([[0], np.cumsum(np.minimum(W.lens, tail))])
+
+    t0 = time.perf_counter()
+    for b in range(n_queries):
+        slots = rows_needed[b]
+        loc = np.array([ipool_rows[s] for s in slots])
+        n = len(slots)
+        qc, qs = O.index_prep(q_idx[b], wl.hadamard, wl.index_fmt)
+        qhat = O.index_dequant(qc, qs, wl.index_fmt)
+        khat = O.index_dequant(codes[loc], sc[loc], wl.index_fmt)
+        logits = O.indexer_logits(qhat, w_idx[b], khat)
+        sel = O.topk_logical(logits, n)
+        c4rows = O.dequant_kv_entries(lat[loc[sel]], lsc[loc[sel]], rope[loc[sel]], "fp8")
+        p = int(W.lens[b]) - 1
+        wpos = O.window_positions(p, wl.window) - (int(W.lens[b]) - min(int(W.lens[b]), tail))
+        r0 = cu[b]
+        rr = O.dequant_kv_entries(raw_rows[0][r0 + wpos], raw_rows[1][r0 + wpos], raw_rows[2][r0 + wpos], "fp8")
+        O.csa_attention_query(q_att[b], c4rows, rr, wl.softmax_scale)
+    dt = time.perf_counter() - t0
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    return {"value": n_queries / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_queries} of {W.B} decode queries at 128K (q prep, indexer over "
+                      f"{int(W.N[0])} entries x 64 heads in float64, top-512, attention); "
+                      f"{dt:.2f} s of CPU work"}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from workloads import specs
+    from workloads.device import CsaDecode
+
+    torch.cuda.set_device(0)
+    wl = specs.DECODE_128K
+    W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
+    ms, idx_ms, idx_med = time_steps(W, a.steps, a.warmup, a.copies)
+    qps = W.B / (ms / 1e3)
+    ibytes = W.indexer_bytes()
+    achieved = ibytes / (idx_ms / 1e3) / 1e9
+    src_hash = kernel_source_hash("indexer.hip", "csa_device.hpp")
+    traffic = stored_traffic("indexer_mfma_kernel<false>", src_hash)
+    line = {
+        "metric": "CSA decode queries/s @128K ctx",
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": W.B, "seq_len": wl.seq_len,
+                   "compressed_entries": int(W.N[0]), "index_format": "fp8_e4m3+hadamard",
+                   "index_heads": wl.index_heads, "attn_heads": wl.heads, "topk": 512,
+                   "window": wl.window, "pool_copies": a.copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "indexer_mfma_kernel<false>",
+                     "kernel_ms": round(idx_ms, 5), "bytes_per_launch": ibytes},
+        "step_hbm_frac": round(W.step_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(W, a.cpu_queries)
+        line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 3)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

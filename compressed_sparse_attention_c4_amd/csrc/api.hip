@@ -1,0 +1,177 @@
+// api.hip -- the extern "C" entry points declared in include/csa.h: host-side
+// argument checks (before any launch), then the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include "../../include/csa.h"
+#include "csa_internal.hpp"
+
+using namespace csa;
+
+namespace {
+
+inline csa_status hip_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_HIP; }
+
+inline bool kv_pool_ok(const csa_kv_pool& p) {
+  if (!p.latent || !p.rope || p.page_size <= 0 || p.num_pages < 0) return false;
+  if (p.fmt == CSA_FP8_E4M3) return p.latent_scale != nullptr;
+  return p.fmt == CSA_F32;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_version(void) { return "0.1.0"; }
+
+const char* csa_status_string(csa_status s) {
+  switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_INVALID: return "invalid argument";
+    case CSA_ERR_UNSUPPORTED: return "unsupported format or shape";
+    case CSA_ERR_WORKSPACE: return "workspace too small";
+    case CSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t csa_workspace_size(int32_t op, int64_t rows, int64_t max_len, int32_t heads) {
+  if (rows < 0 || max_len < 0 || heads <= 0) return 0;
+  switch (op) {
+    case CSA_OP_INDEXER: return indexer_ws_bytes(rows, heads);
+    case CSA_OP_TOPK: return topk_ws_bytes(rows, max_len);
+    case CSA_OP_CSA_ATTN:
+    case CSA_OP_HCA_ATTN: return attention_ws_bytes(rows, max_len, heads);
+    default: return 0;
+  }
+}
+
+csa_status c4_compress(const void* x, csa_fmt x_fmt, const int32_t* cu_rows,
+                       const int32_t* start_pos, int32_t B, int32_t max_rows, int32_t ratio,
+                       const float* gate_w, const float* gate_b, const int32_t* page_table,
+                       int32_t pt_stride, csa_kv_pool out, hipStream_t stream) {
+  if (B < 0 || max_rows < 0 || ratio < 1 || ratio > 1024 || pt_stride <= 0) return CSA_ERR_INVALID;
+  if (x_fmt != CSA_BF16 && x_fmt != CSA_F32) return CSA_ERR_INVALID;
+  if (!kv_pool_ok(out)) return CSA_ERR_INVALID;
+  if (B == 0 || max_rows < ratio) return CSA_OK;
+  if (!x || !cu_rows || !start_pos || !gate_w || !gate_b || !page_table) return CSA_ERR_INVALID;
+  return hip_status(launch_compress(x, x_fmt, cu_rows, start_pos, B, max_rows, ratio, gate_w,
+                                    gate_b, page_table, pt_stride, out, stream));
+}
+
+csa_status csa_index_prep(const void* v, csa_fmt v_fmt, int64_t rows, int32_t dim,
+                          uint32_t flags, csa_fmt out_fmt, void* out, void* out_scale,
+                          const int32_t* dst_rows, hipStream_t stream) {
+  if (rows < 0 || (dim != 64 && dim != 128)) return CSA_ERR_INVALID;
+  if (v_fmt != CSA_BF16 && v_fmt != CSA_F32) return CSA_ERR_INVALID;
+  if (flags & ~(CSA_PREP_HADAMARD | CSA_PREP_QUANT)) return CSA_ERR_INVALID;
+  if (out_fmt != CSA_F32 && out_fmt != CSA_FP8_E4M3 && out_fmt != CSA_MXFP4) return CSA_ERR_INVALID;
+  if (rows == 0) return CSA_OK;
+  if (!v || !out || (out_fmt != CSA_F32 && !out_scale)) return CSA_ERR_INVALID;
+  return hip_status(launch_index_prep(v, v_fmt, rows, dim, flags, out_fmt, out, out_scale,
+                                      dst_rows, stream));
+}
+
+csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint32_t prep,
+                         const float* w, int32_t T, int32_t H_I, int32_t D_I,
+                         const int32_t* row_seq, const int32_t* row_len, int32_t max_row_len,
+                         const int32_t* page_table, int32_t pt_stride, csa_index_pool k,
+                         float* logits, int64_t ld, void* q_used, void* q_used_scale, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || H_I <= 0 || max_row_len < 0 || pt_stride <= 0 || ld < max_row_len) return CSA_ERR_INVALID;
+  if (k.page_size <= 0 || k.dim != D_I) return CSA_ERR_INVALID;
+  if ((q_used == nullptr) != (q_used_scale == nullptr)) return CSA_ERR_INVALID;
+  if (prep & ~(CSA_PREP_HADAMARD | CSA_PREP_QUANT)) return CSA_ERR_INVALID;
+  if (k.fmt == CSA_F32) {
+    if (q_fmt != CSA_F32 || prep != 0) return CSA_ERR_INVALID;
+    if (D_I != 64 && D_I != 128) return CSA_ERR_UNSUPPORTED;
+    if ((size_t)H_I * D_I > 8192) return CSA_ERR_UNSUPPORTED;
+    if (q_used) return CSA_ERR_INVALID;
+  } else if (k.fmt == CSA_FP8_E4M3 || k.fmt == CSA_MXFP4) {
+    if (H_I != 64 || D_I != 128) return CSA_ERR_UNSUPPORTED;
+    if (!k.scale) return CSA_ERR_INVALID;
+    if (q_fmt == CSA_BF16 || q_fmt == CSA_F32) {
+      if (!(prep & CSA_PREP_QUANT)) return CSA_ERR_INVALID;
+      if (!q_used && ws_bytes < indexer_ws_bytes(T, H_I)) return CSA_ERR_WORKSPACE;
+      if (!q_used && !ws) return CSA_ERR_WORKSPACE;
+    } else if (q_fmt == k.fmt) {
+      if (prep != 0 || !q_scale) return CSA_ERR_INVALID;
+    } else {
+      return CSA_ERR_INVALID;
+    }
+  } else {
+    return CSA_ERR_INVALID;
+  }
+  if (T == 0 || max_row_len == 0) return CSA_OK;
+  if (!q || !w || !row_seq || !row_len || !page_table || !k.data || !logits) return CSA_ERR_INVALID;
+  return hip_status(launch_indexer(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len,
+                                   max_row_len, page_table, pt_stride, k, logits, ld, q_used,
+                                   q_used_scale, ws, stream));
+}
+
+csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
+                               const int32_t* row_len, const int32_t* row_seq,
+                               const int32_t* page_table, int32_t pt_stride,
+                               int32_t c4_page_size, int32_t* phys_idx, int32_t* logical_idx,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws_bytes;
+  if (R < 0 || ld < 0 || pt_stride <= 0 || c4_page_size <= 0) return CSA_ERR_INVALID;
+  if (R == 0) return CSA_OK;
+  if (!logits || !row_len || !row_seq || !page_table || !phys_idx) return CSA_ERR_INVALID;
+  return hip_status(launch_topk(logits, ld, R, row_len, row_seq, page_table, pt_stride,
+                                c4_page_size, 0, phys_idx, logical_idx, ws, stream));
+}
+
+static csa_status attn_common(AttnArgs& a, hipStream_t stream) {
+  if (a.T < 0 || a.H <= 0 || a.window < 1 || a.window > 4096) return CSA_ERR_INVALID;
+  if (!kv_pool_ok(a.comp) || !kv_pool_ok(a.raw) || a.comp.fmt != a.raw.fmt) return CSA_ERR_INVALID;
+  if (a.raw_pt_stride <= 0) return CSA_ERR_INVALID;
+  if (a.comp.fmt == CSA_F32) {
+    if (a.q_fmt != CSA_F32 || a.out_fmt != CSA_F32) return CSA_ERR_INVALID;
+    if ((size_t)(a.max_comp + a.window) * 4 + 576 * 4 > 150 * 1024) return CSA_ERR_UNSUPPORTED;
+  } else {
+    if (a.q_fmt != CSA_BF16) return CSA_ERR_INVALID;
+    if (a.out_fmt != CSA_BF16 && a.out_fmt != CSA_F32) return CSA_ERR_INVALID;
+    if (a.H % 16 != 0 || a.H == 48 || (a.H > 64 && a.H % 64 != 0) || a.H > 1024) return CSA_ERR_UNSUPPORTED;
+    const size_t need = attention_ws_bytes(a.T, a.max_comp + a.window, a.H);
+    if (need > a.ws_bytes || (need > 0 && !a.ws)) return CSA_ERR_WORKSPACE;
+  }
+  if (a.T == 0) return CSA_OK;
+  if (!a.q || !a.q_seq || !a.q_pos || !a.raw_pt || !a.out) return CSA_ERR_INVALID;
+  return hip_status(launch_attention(a, stream));
+}
+
+csa_status csa_sparse_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
+                           const int32_t* q_seq, const int32_t* q_pos, const int32_t* phys_idx,
+                           int32_t k_sel, csa_kv_pool c4, csa_kv_pool raw,
+                           const int32_t* raw_page_table, int32_t raw_pt_stride, int32_t window,
+                           float softmax_scale, void* out, csa_fmt out_fmt, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (k_sel < 0 || k_sel > CSA_TOPK) return CSA_ERR_INVALID;
+  if (k_sel > 0 && !phys_idx && T > 0) return CSA_ERR_INVALID;
+  AttnArgs a{};
+  a.q = q; a.q_fmt = q_fmt; a.T = T; a.H = H; a.q_seq = q_seq; a.q_pos = q_pos;
+  a.hca = false; a.phys_idx = phys_idx; a.k_sel = k_sel; a.ratio = 1; a.comp = c4; a.comp_pt = nullptr;
+  a.comp_pt_stride = 1; a.max_comp = k_sel; a.raw = raw; a.raw_pt = raw_page_table;
+  a.raw_pt_stride = raw_pt_stride; a.window = window; a.scale = softmax_scale; a.out = out;
+  a.out_fmt = out_fmt; a.ws = ws; a.ws_bytes = ws_bytes;
+  return attn_common(a, stream);
+}
+
+csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
+                          const int32_t* q_seq, const int32_t* q_pos, int32_t max_len,
+                          int32_t ratio, csa_kv_pool hca, const int32_t* hca_page_table,
+                          int32_t hca_pt_stride, csa_kv_pool raw, const int32_t* raw_page_table,
+                          int32_t raw_pt_stride, int32_t window, float softmax_scale, void* out,
+                          csa_fmt out_fmt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (ratio < 1 || max_len < 0 || hca_pt_stride <= 0) return CSA_ERR_INVALID;
+  if (T > 0 && !hca_page_table) return CSA_ERR_INVALID;
+  AttnArgs a{};
+  a.q = q; a.q_fmt = q_fmt; a.T = T; a.H = H; a.q_seq = q_seq; a.q_pos = q_pos;
+  a.hca = true; a.phys_idx = nullptr; a.k_sel = 0; a.ratio = ratio; a.comp = hca; a.comp_pt = hca_page_table;
+  a.comp_pt_stride = hca_pt_stride; a.max_comp = max_len / ratio; a.raw = raw;
+  a.raw_pt = raw_page_table; a.raw_pt_stride = raw_pt_stride; a.window = window;
+  a.scale = softmax_scale; a.out = out; a.out_fmt = out_fmt; a.ws = ws; a.ws_bytes = ws_bytes;
+  return attn_common(a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// csa_internal.hpp -- launch functions behind the C ABI (host side, internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+// Each launcher enqueues on `s` and returns hipGetLastError().
+hipError_t launch_compress(const void* x, int x_fmt, const int32_t* cu_rows,
+                           const int32_t* start_pos, int B, int max_rows, int ratio,
+                           const float* gate_w, const float* gate_b,
+                           const int32_t* page_table, int pt_stride, const csa_kv_pool& out,
+                           hipStream_t s);
+
+hipError_t launch_index_prep(const void* v, int v_fmt, int64_t rows, int dim, uint32_t flags,
+                             int out_fmt, void* out, void* out_scale, const int32_t* dst_rows,
+                             hipStream_t s);
+
+hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_t prep,
+                          const float* w, int T, int H_I, int D_I, const int32_t* row_seq,
+                          const int32_t* row_len, int max_row_len, const int32_t* page_table,
+                          int pt_stride, const csa_index_pool& k, float* logits, int64_t ld,
+                          void* q_used, void* q_used_scale, void* ws, hipStream_t s);
+
+hipError_t launch_topk(const float* logits, int64_t ld, int R, const int32_t* row_len,
+                       const int32_t* row_seq, const int32_t* page_table, int pt_stride,
+                       int c4_page_size, int max_row_len, int32_t* phys_idx,
+                       int32_t* logical_idx, void* ws, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;
+  int q_fmt;
+  int T, H;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  // compressed part: CSA selects through phys_idx; HCA takes every visible entry
+  bool hca;
+  const int32_t* phys_idx;  // CSA: [T][k_sel]; NULL for HCA
+  int k_sel;
+  int ratio;                // HCA: visible entries (p+1)/ratio
+  csa_kv_pool comp;
+  const int32_t* comp_pt;   // HCA page table
+  int comp_pt_stride;
+  int max_comp;             // upper bound of compressed entries per query
+  csa_kv_pool raw;
+  const int32_t* raw_pt;
+  int raw_pt_stride;
+  int window;
+  float scale;
+  void* out;
+  int out_fmt;
+  void* ws;
+  size_t ws_bytes;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+size_t attention_ws_bytes(int64_t T, int64_t max_entries, int H);
+size_t topk_ws_bytes(int64_t R, int64_t max_len);
+size_t indexer_ws_bytes(int64_t T, int H_I);
+
+}  // namespace csa

@@ -1,0 +1,238 @@
+// indexer.hip -- lightning-indexer logits over the paged index-K pool.
+//
+// "Token 的一生：DSV4 架构与 DSpark" §3 (C4Indexer: FP8 or FP4 query and index-K,
+// head weights fused with the query scale; §3.2 logits [bs, c4_seqlen] feed the
+// top-512); "DeepSeek-V4 的交錯壓縮注意力（CSA/HCA）" CSA paragraph (a light,
+// low-precision indexer scores every compressed block for each query).
+//
+//   logits[t][j] = sum_h w[t][h] * ReLU(qhat[t][h] . khat[j])
+//
+// Per query row the 64 heads share each index-K row, so scoring one entry is a
+// [64 x 128] x [128] contraction: 16 KFLOP against 132 B (FP8) or 68 B (MXFP4)
+// of index-K. At 8 TB/s that is ~1-2 PFLOP/s, beyond the fp32 vector units, so
+// the scan runs on the gfx950 matrix cores: one v_mfma_scale_f32_16x16x128
+// (FP8 e4m3, or MXFP4 with the e8m0 block scales applied by the instruction)
+// scores 16 heads x 16 entries; four of them cover the 64 heads. Index-K rows
+// stream from HBM straight into the B operand (each 16-entry group is one
+// contiguous 2 KB / 1 KB read), the query sits in registers, and ReLU, the
+// head weights and the 64-head reduction run in the epilogue on the
+// accumulators.
+#include "csa_device.hpp"
+#include "csa_internal.hpp"
+
+namespace csa {
+namespace {
+
+constexpr int kHeads = 64;   // indexer heads handled by the MFMA path
+constexpr int kDim = 128;    // indexer head dim handled by the MFMA path
+constexpr int kWaves = 4;
+constexpr int kUnroll = 4;   // 16-entry groups in flight per wave
+constexpr int kWgEntries = kWaves * kUnroll * 16;
+
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, v4f c) {
+  // format 0 = FP8 e4m3 for both operands; e8m0 scale 127 = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ v4f mfma_fp4(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  // format 4 = FP4 e2m1 for both operands (low 4 registers used); per-lane e8m0 scales
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+}
+
+// Operand layout of v_mfma_*_16x16x128 (64 lanes): lane l supplies row / column
+// (l % 16) and the 32 K-elements [(l/16)*32, (l/16)*32 + 32) of it; with MXFP4
+// that K-range is one 32-element scale block, whose e8m0 byte the lane
+// supplies as its scale. The result lane l holds rows 4*(l/16) + 0..3 of
+// column l % 16.
+template <bool kFp4>
+__global__ void __launch_bounds__(kWaves * 64)
+indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
+                    const float* __restrict__ w, const int32_t* __restrict__ row_seq,
+                    const int32_t* __restrict__ row_len, const int32_t* __restrict__ pt,
+                    int pt_stride, const uint8_t* __restrict__ kdata,
+                    const void* __restrict__ kscale, int page_size, float* __restrict__ logits,
+                    int64_t ld, int chunk) {
+  constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K / q row
+  const int t = blockIdx.y;
+  const int n = row_len[t];
+  const int c0 = blockIdx.x * chunk;
+  if (c0 >= n) return;
+  const int c1 = min(c0 + chunk, n);
+  const int seq = row_seq[t];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  // Query operands: head hb*16 + col, K-elements grp*32 .. grp*32+31.
+  v8i a[4];
+  int sa[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int head = hb * 16 + col;
+    const uint8_t* p = qc + ((int64_t)t * kHeads + head) * kRowBytes + grp * (kRowBytes / 4);
+    if (kFp4) {
+      uint4 x = *reinterpret_cast<const uint4*>(p);
+      a[hb] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+      sa[hb] = reinterpret_cast<const uint8_t*>(qs)[((int64_t)t * kHeads + head) * 4 + grp];
+    } else {
+      uint4 x = *reinterpret_cast<const uint4*>(p);
+      uint4 y = *reinterpret_cast<const uint4*>(p + 16);
+      a[hb] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      sa[hb] = 127;
+    }
+  }
+  // Head weights for the accumulator rows this lane holds (FP8: q scale folded
+  // in, valid because ReLU(s x) = s ReLU(x) for s > 0).
+  float wq[16];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = hb * 16 + grp * 4 + r;
+      float v = w[(int64_t)t * kHeads + h];
+      if (!kFp4) v *= reinterpret_cast<const float*>(qs)[(int64_t)t * kHeads + h];
+      wq[hb * 4 + r] = v;
+    }
+
+  const int32_t* ptrow = pt + (int64_t)seq * pt_stride;
+  for (int base = c0 + wave * 16; base < c1; base += kWgEntries) {
+    v8i b[kUnroll];
+    int sb[kUnroll];
+    int64_t slot[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = base + u * kWaves * 16 + col;
+      const bool valid = j < c1;
+      slot[u] = valid ? (int64_t)ptrow[j / page_size] * page_size + j % page_size : 0;
+      const uint8_t* p = kdata + slot[u] * kRowBytes + grp * (kRowBytes / 4);
+      if (kFp4) {
+        uint4 x = valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+        b[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        sb[u] = valid ? reinterpret_cast<const uint8_t*>(kscale)[slot[u] * 4 + grp] : 127;
+      } else {
+        uint4 x = valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+        uint4 y = valid ? *reinterpret_cast<const uint4*>(p + 16) : make_uint4(0, 0, 0, 0);
+        b[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        sb[u] = 127;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float v = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        acc = kFp4 ? mfma_fp4(a[hb], b[u], acc, sa[hb], sb[u]) : mfma_fp8(a[hb], b[u], acc);
+        v = fmaf(wq[hb * 4 + 0], fmaxf(acc[0], 0.f), v);
+        v = fmaf(wq[hb * 4 + 1], fmaxf(acc[1], 0.f), v);
+        v = fmaf(wq[hb * 4 + 2], fmaxf(acc[2], 0.f), v);
+        v = fmaf(wq[hb * 4 + 3], fmaxf(acc[3], 0.f), v);
+      }
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      const int j = base + u * kWaves * 16 + col;
+      if (grp == 0 && j < c1) {
+        if (!kFp4) v *= reinterpret_cast<const float*>(kscale)[slot[u]];
+        logits[(int64_t)t * ld + j] = v;
+      }
+    }
+  }
+}
+
+// fp32 path (small indexers, any H_I, D_I in {64, 128}): one thread per entry,
+// the row's query in LDS.
+__global__ void __launch_bounds__(256)
+indexer_f32_kernel(const float* __restrict__ q, const float* __restrict__ w, int H, int D,
+                   const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_len,
+                   const int32_t* __restrict__ pt, int pt_stride,
+                   const float* __restrict__ kdata, int page_size, float* __restrict__ logits,
+                   int64_t ld) {
+  extern __shared__ float sq[];  // [H][D] then w[H]
+  const int t = blockIdx.y;
+  for (int i = threadIdx.x; i < H * D; i += blockDim.x) sq[i] = q[(int64_t)t * H * D + i];
+  for (int i = threadIdx.x; i < H; i += blockDim.x) sq[H * D + i] = w[(int64_t)t * H + i];
+  __syncthreads();
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= row_len[t]) return;
+  const int64_t slot = (int64_t)pt[(int64_t)row_seq[t] * pt_stride + j / page_size] * page_size + j % page_size;
+  const float* k = kdata + slot * D;
+  float acc = 0.f;
+  for (int h = 0; h < H; ++h) {
+    float d = 0.f;
+    for (int i = 0; i < D; i += 4) {
+      float4 kv = *reinterpret_cast<const float4*>(k + i);
+      d = fmaf(sq[h * D + i], kv.x, d);
+      d = fmaf(sq[h * D + i + 1], kv.y, d);
+      d = fmaf(sq[h * D + i + 2], kv.z, d);
+      d = fmaf(sq[h * D + i + 3], kv.w, d);
+    }
+    acc = fmaf(sq[H * D + h], fmaxf(d, 0.f), acc);
+  }
+  logits[(int64_t)t * ld + j] = acc;
+}
+
+}  // namespace
+
+size_t indexer_ws_bytes(int64_t T, int H_I) {
+  // prepared query codes (<= 128 B per head) + scales (<= 4 B per head), 256-B aligned
+  const size_t codes = ((size_t)T * H_I * kDim + 255) & ~(size_t)255;
+  return codes + (((size_t)T * H_I * 4 + 255) & ~(size_t)255);
+}
+
+hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_t prep,
+                          const float* w, int T, int H_I, int D_I, const int32_t* row_seq,
+                          const int32_t* row_len, int max_row_len, const int32_t* page_table,
+                          int pt_stride, const csa_index_pool& k, float* logits, int64_t ld,
+                          void* q_used, void* q_used_scale, void* ws, hipStream_t s) {
+  if (T == 0 || max_row_len == 0) return hipSuccess;
+  if (k.fmt == CSA_F32) {
+    dim3 grid((max_row_len + 255) / 256, T);
+    const size_t lds = ((size_t)H_I * D_I + H_I) * sizeof(float);
+    hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), lds, s, (const float*)q, w, H_I,
+                       D_I, row_seq, row_len, page_table, pt_stride, (const float*)k.data,
+                       k.page_size, logits, ld);
+    return hipGetLastError();
+  }
+  const uint8_t* qc = (const uint8_t*)q;
+  const void* qs = q_scale;
+  if (prep & CSA_PREP_QUANT) {
+    // Prepare the query rows once (rotation + quantisation) into q_used or the
+    // workspace, then score from the prepared codes.
+    void* dst = q_used;
+    void* dsts = q_used_scale;
+    if (!dst) {
+      dst = ws;
+      dsts = (uint8_t*)ws + (((size_t)T * H_I * kDim + 255) & ~(size_t)255);
+    }
+    hipError_t e = launch_index_prep(q, q_fmt, (int64_t)T * H_I, D_I, prep, k.fmt, dst, dsts,
+                                     nullptr, s);
+    if (e != hipSuccess) return e;
+    qc = (const uint8_t*)dst;
+    qs = dsts;
+  } else if (q_used) {
+    const size_t code_bytes = (size_t)T * H_I * (k.fmt == CSA_MXFP4 ? kDim / 2 : kDim);
+    const size_t scale_bytes = (size_t)T * H_I * 4;
+    hipError_t e = hipMemcpyAsync(q_used, q, code_bytes, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(q_used_scale, q_scale, scale_bytes, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  // Chunk the rows so the grid has >= ~2048 workgroups.
+  int64_t total = (int64_t)T * max_row_len;
+  int64_t chunk = total / 2048;
+  chunk = ((chunk + kWgEntries - 1) / kWgEntries) * kWgEntries;
+  if (chunk < kWgEntries) chunk = kWgEntries;
+  if (chunk > 16 * kWgEntries) chunk = 16 * kWgEntries;
+  dim3 grid((unsigned)((max_row_len + chunk - 1) / chunk), T);
+  if (k.fmt == CSA_MXFP4)
+    hipLaunchKernelGGL(indexer_mfma_kernel<true>, grid, dim3(kWaves * 64), 0, s, qc, qs, w,
+                       row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data,
+                       k.scale, k.page_size, logits, ld, (int)chunk);
+  else
+    hipLaunchKernelGGL(indexer_mfma_kernel<false>, grid, dim3(kWaves * 64), 0, s, qc, qs, w,
+                       row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data,
+                       k.scale, k.page_size, logits, ld, (int)chunk);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -120,17 +120,18 @@ typedef struct {
  * append raw tokens to the window pool).
  *
  *  x         [cu_rows[B]][576], CSA_BF16 or CSA_F32, row-major.
- *  cu_rows   HOST int32[B+1]: rows of sequence b are x[cu_rows[b] .. cu_rows[b+1]).
- *  start_pos HOST int32[B]: raw position of the first row of sequence b; must be
- *            a multiple of ratio. Only complete blocks are emitted: entries
- *            start_pos/ratio + i for i < (cu_rows[b+1]-cu_rows[b]) / ratio.
+ *  cu_rows   int32[B+1]: rows of sequence b are x[cu_rows[b] .. cu_rows[b+1]).
+ *  start_pos int32[B]: raw position of the first row of sequence b. Every
+ *            complete aligned block [ratio*k, ratio*k + ratio) inside the rows
+ *            is emitted; rows of a partial block at either end are skipped.
+ *  max_rows  HOST: an upper bound of cu_rows[b+1] - cu_rows[b] over b (sizes the grid).
  *  gate_w    float[576]; gate_b float[ratio].
  *  page_table int32 [B][pt_stride] over out.page_size-entry pages.
- * Returns CSA_ERR_INVALID if ratio is not 1, 4 or 128, a start_pos is not a
- * multiple of ratio, cu_rows decreases, or a pointer is NULL.
+ * Returns CSA_ERR_INVALID if ratio is outside [1, 1024], B or max_rows is
+ * negative, a pointer is NULL, or the pool format is not FP8 / F32.
  */
 csa_status c4_compress(const void* x, csa_fmt x_fmt, const int32_t* cu_rows,
-                       const int32_t* start_pos, int32_t B, int32_t ratio,
+                       const int32_t* start_pos, int32_t B, int32_t max_rows, int32_t ratio,
                        const float* gate_w, const float* gate_b,
                        const int32_t* page_table, int32_t pt_stride,
                        csa_kv_pool out, hipStream_t stream);
@@ -172,6 +173,7 @@ csa_status csa_index_prep(const void* v, csa_fmt v_fmt, int64_t rows, int32_t di
  *   w        float [T][H_I] head weights (w >= 0).
  *   row_seq, row_len  int32 [T]: sequence and visible length of each query row
  *            (decode: row_len = c4 length; prefill: row_len = min(N, (p+1)/4)).
+ *   max_row_len HOST: an upper bound of row_len (sizes the grid); ld >= max_row_len.
  *   logits   float, row stride ld >= max row_len.
  *   q_used, q_used_scale  optional (NULL or both set): the prepared q codes and
  *            scales in q_scale's layout, for inspection.
@@ -179,7 +181,7 @@ csa_status csa_index_prep(const void* v, csa_fmt v_fmt, int64_t rows, int32_t di
  */
 csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint32_t prep,
                          const float* w, int32_t T, int32_t H_I, int32_t D_I,
-                         const int32_t* row_seq, const int32_t* row_len,
+                         const int32_t* row_seq, const int32_t* row_len, int32_t max_row_len,
                          const int32_t* page_table, int32_t pt_stride, csa_index_pool k,
                          float* logits, int64_t ld, void* q_used, void* q_used_scale,
                          void* ws, size_t ws_bytes, hipStream_t stream);
@@ -212,9 +214,13 @@ csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
  *   score_e = softmax_scale * sum_{d<576} q[t][h][d] * kv_e[d]
  *   out[t][h][:] = sum_e softmax(score)_e * kv_e[0:512]
  * kv_e is the dequantised entry. All H heads share the KV (MQA).
- *   q    [T][H][576] CSA_BF16 or CSA_F32; out [T][H][512] CSA_BF16 or CSA_F32.
+ *   q    [T][H][576]: CSA_BF16 with FP8 pools (H a multiple of 16, <= 128), or
+ *        CSA_F32 with F32 pools (any H). out [T][H][512] CSA_BF16 or CSA_F32
+ *        (F32 pools: CSA_F32 only).
  *   c4 and raw pools must have the same fmt; raw.page_size is the raw page size.
- *   Requires 1 <= window <= 128 + 1024 and k_sel <= 512.
+ *   Requires 1 <= window <= 4096 and 0 <= k_sel <= 512.
+ *   ws   workspace of csa_workspace_size(CSA_OP_CSA_ATTN, T, k_sel + window, H)
+ *        bytes (may be 0 bytes / NULL when that size is 0).
  */
 csa_status csa_sparse_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
                            const int32_t* q_seq, const int32_t* q_pos,
@@ -229,9 +235,12 @@ csa_status csa_sparse_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
  * compression, then dense attention over the compressed blocks), plus the same
  * sliding window as CSA. As csa_sparse_attn with
  *   E = { hca entry j of sequence s : ratio*j + ratio - 1 <= p }  U  window(p).
+ *   max_len HOST: an upper bound of q_pos[t] + 1 (sizes the split of the entry
+ *           list); ws: csa_workspace_size(CSA_OP_HCA_ATTN, T, max_len/ratio + window, H).
  */
 csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
-                          const int32_t* q_seq, const int32_t* q_pos, int32_t ratio,
+                          const int32_t* q_seq, const int32_t* q_pos, int32_t max_len,
+                          int32_t ratio,
                           csa_kv_pool hca, const int32_t* hca_page_table,
                           int32_t hca_pt_stride, csa_kv_pool raw,
                           const int32_t* raw_page_table, int32_t raw_pt_stride,
@@ -239,8 +248,10 @@ csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
                           csa_fmt out_fmt, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace sizes (bytes) for the calls that take `ws`.
- * op: CSA_OP_INDEXER, CSA_OP_TOPK, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN.
- * rows = T or R, max_len = longest row (entries), heads = H. */
+ * op: CSA_OP_INDEXER (rows = T, heads = H_I; needed only when the query is
+ *     prepared inside the call and q_used is NULL), CSA_OP_TOPK (0),
+ *     CSA_OP_CSA_ATTN / CSA_OP_HCA_ATTN (rows = T, max_len = most entries of
+ *     one query's list, heads = H). */
 #define CSA_OP_INDEXER  0
 #define CSA_OP_TOPK     1
 #define CSA_OP_CSA_ATTN 2

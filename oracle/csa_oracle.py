@@ -205,14 +205,35 @@ def hadamard_rotate(v: np.ndarray) -> np.ndarray:
     return y / np.sqrt(D)
 
 
+def hadamard_rotate_f32(v: np.ndarray) -> np.ndarray:
+    """The same rotation evaluated in float32 by the textbook fast Walsh-Hadamard
+    butterflies (y_e = a + b, y_{e+h} = a - b for spans h = 1, 2, 4, ..., D/2 in
+    that order), then one float32 multiply by fl32(1/sqrt(D)). Every step is a
+    correctly rounded float32 add, subtract or multiply, so this fixes the exact
+    float32 value on which a quantisation decision is taken."""
+    y = np.array(v, dtype=np.float32, copy=True)
+    D = y.shape[-1]
+    assert D & (D - 1) == 0, "Hadamard size must be a power of two"
+    h = 1
+    while h < D:
+        y = y.reshape(y.shape[:-1] + (D // (2 * h), 2, h))
+        a = y[..., 0, :].copy()
+        b = y[..., 1, :].copy()
+        y[..., 0, :] = a + b
+        y[..., 1, :] = a - b
+        y = y.reshape(y.shape[:-3] + (D,))
+        h *= 2
+    return (y * np.float32(1.0 / np.sqrt(D))).astype(np.float32)
+
+
 def index_prep(v: np.ndarray, hadamard: bool, fmt: str):
     """Indexer row preparation ([P1] §3.1, §4): optional Hadamard rotation, then
-    quantisation to fmt ('fp8', 'mxfp4' or 'f32'). The rotated value is taken to
-    float32 before quantising. Returns (codes, scale) or (float32 rows, None)."""
-    x = np.asarray(v, dtype=np.float64)
+    quantisation to fmt ('fp8', 'mxfp4' or 'f32'). Reading: the quantised codes
+    are decided in float32, on the float32 butterfly evaluation of the rotation
+    (hadamard_rotate_f32). Returns (codes, scale) or (float32 rows, None)."""
+    x32 = np.asarray(v, dtype=np.float32)
     if hadamard:
-        x = hadamard_rotate(x)
-    x32 = x.astype(np.float32)
+        x32 = hadamard_rotate_f32(x32)
     if fmt == "fp8":
         return quant_fp8_rows(x32)
     if fmt == "mxfp4":

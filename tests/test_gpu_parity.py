@@ -1,0 +1,389 @@
+"""GPU parity: each entry point of libcsa.so against the CPU oracle on the same
+seeded inputs, at sizes the oracle finishes in seconds that still span
+several tiles / pages and a ragged tail.
+
+Bars: index and selection work bit-exact; quantised codes equal except a
+one-code step where the oracle's fp32 pre-rounding value sits within 1e-5 of
+the midpoint (two correct fp32 evaluations may round apart there); logits
+within 1e-4 of the row's max magnitude; attention within 1e-4 (relative to
+the row's max) for the fp32 path and 2e-2 max-abs for the bf16 / FP8 path.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+from tests.gpu_helpers import (DEV, fp8_codes_match, index_pool_to_device, kv_pool_to_device,
+                               t_dev, unpack_e2m1)
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def csa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_sparse_attention_c4_amd as m
+    return m
+
+
+def _bf16(x):
+    """float32 array -> (torch bf16 device tensor, float32 host values it holds)."""
+    bits = gen.to_bf16_bits(x)
+    return t_dev(bits.view(np.int16)).view(torch.bfloat16), gen.bf16_bits_to_f32(bits)
+
+
+# ------------------------------------------------------------------ index prep
+
+
+@pytest.mark.parametrize("rows", [1, 77, 3000])
+def test_index_prep_fp8_hadamard(csa, rows):
+    g = gen.rng(100 + rows)
+    v, vh = _bf16(gen.normal(g, (rows, 128)))
+    out = torch.full((rows, 128), 0xAB, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(rows, dtype=torch.float32, device=DEV)
+    csa.csa_index_prep(v, 128, csa.CSA_PREP_HADAMARD, csa.CSA_FP8_E4M3, out, sc)
+    codes, scale = O.index_prep(vh, True, "fp8")
+    # the decision is taken on the same float32 butterfly values: bit-exact
+    assert np.array_equal(sc.cpu().numpy(), scale)
+    assert np.array_equal(out.cpu().numpy(), codes)
+
+
+@pytest.mark.parametrize("rows", [5, 1000])
+def test_index_prep_mxfp4_hadamard(csa, rows):
+    g = gen.rng(200 + rows)
+    v, vh = _bf16(gen.normal(g, (rows, 128)))
+    out = torch.empty((rows, 64), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((rows, 4), dtype=torch.uint8, device=DEV)
+    csa.csa_index_prep(v, 128, csa.CSA_PREP_HADAMARD, csa.CSA_MXFP4, out, sc)
+    codes, sbytes = O.index_prep(vh, True, "mxfp4")
+    assert np.array_equal(sc.cpu().numpy(), sbytes)
+    assert np.array_equal(out.cpu().numpy(), codes)
+
+
+def test_index_prep_f32_dst_rows(csa):
+    g = gen.rng(300)
+    v = gen.normal(g, (50, 64))
+    dst = np.random.default_rng(1).permutation(80)[:50].astype(np.int32)
+    out = torch.full((80, 64), float("nan"), dtype=torch.float32, device=DEV)
+    csa.csa_index_prep(t_dev(v), 64, csa.CSA_PREP_HADAMARD, csa.CSA_F32, out, None, t_dev(dst))
+    want = O.hadamard_rotate_f32(v)
+    got = out.cpu().numpy()
+    assert np.array_equal(got[dst], want)
+    untouched = np.setdiff1d(np.arange(80), dst)
+    assert np.all(np.isnan(got[untouched]))
+
+
+# ------------------------------------------------------------------ compressor
+
+
+def _compress_case(csa, ratio, fmt, seqs, rows_per_seq, starts, seed):
+    g = gen.rng(seed)
+    w, b = gen.gate_params(g, ratio)
+    xs = [gen.normal(g, (n, 576)) for n in rows_per_seq]
+    x, xh = _bf16(np.concatenate(xs))
+    cu = np.concatenate([[0], np.cumsum(rows_per_seq)]).astype(np.int32)
+    ps = 64
+    blocks = [(s + n) // ratio for s, n in zip(starts, rows_per_seq)]
+    pages_per_seq = max(blocks) // ps + 2
+    num_pages = seqs * pages_per_seq + 3
+    pt = gen.page_table(g, seqs, pages_per_seq, num_pages)
+    out = csa.alloc_kv_pool(num_pages, ps, csa.CSA_FP8_E4M3 if fmt == "fp8" else csa.CSA_F32)
+    csa.c4_compress(x, t_dev(cu), t_dev(np.array(starts, np.int32)), max(rows_per_seq), ratio,
+                    t_dev(w), t_dev(b), t_dev(pt), out)
+    torch.cuda.synchronize()
+    return g, w, b, xh, cu, pt, out
+
+
+@pytest.mark.parametrize("ratio,rows,starts", [
+    (4, [4096, 37, 4], [0, 8, 4096]),          # several pages, ragged tail, single block
+    (128, [2000, 128 * 3 + 5], [0, 1024]),     # HCA ratio
+    (1, [300], [100]),                         # raw-token append
+])
+def test_compress_f32_pool(csa, ratio, rows, starts):
+    g, w, b, xh, cu, pt, out = _compress_case(csa, ratio, "f32", len(rows), rows, starts, 400 + ratio)
+    lat = out.latent.cpu().numpy().reshape(-1, 512)
+    rope = out.rope.cpu().numpy().reshape(-1, 64)
+    written = np.zeros(lat.shape[0], bool)
+    for s in range(len(rows)):
+        want = O.compress_blocks(xh[cu[s]:cu[s + 1]], starts[s], ratio, w, b)
+        kb0 = starts[s] // ratio
+        slots = O.page_slot(pt[s], np.arange(kb0, kb0 + len(want)), 64)
+        got = np.concatenate([lat[slots], rope[slots]], axis=1)
+        np.testing.assert_allclose(got, want, rtol=2e-5, atol=2e-6)
+        written[slots] = True
+    assert np.all(np.isnan(lat[~written])), "compress wrote outside its blocks"
+
+
+@pytest.mark.parametrize("ratio", [4, 128])
+def test_compress_fp8_pool(csa, ratio):
+    rows = [4096 + 13, 1000]
+    starts = [0, 256]
+    g, w, b, xh, cu, pt, out = _compress_case(csa, ratio, "fp8", 2, rows, starts, 500 + ratio)
+    lat = out.latent.cpu().numpy().reshape(-1, 512)
+    sc = out.scale.cpu().numpy().reshape(-1)
+    rope = out.rope.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1, 64)
+    total_bad = 0
+    for s in range(2):
+        c = O.compress_blocks(xh[cu[s]:cu[s + 1]], starts[s], ratio, w, b)
+        ocodes, oscale, orope = O.quant_kv_entries(c, "fp8")
+        kb0 = starts[s] // ratio
+        slots = O.page_slot(pt[s], np.arange(kb0, kb0 + len(c)), 64)
+        # scales agree to fp32 rounding of amax of two fp32 evaluations of c
+        np.testing.assert_allclose(sc[slots], oscale, rtol=3e-6)
+        ratio_o = c[:, :512].astype(np.float32) / oscale[:, None]
+        ok, nbad = fp8_codes_match(lat[slots], ocodes, ratio_o, rel=2e-5)
+        assert ok
+        total_bad += nbad
+        # bf16 RoPE dims: one bf16 rounding of two fp32 evaluations of c
+        gr, orr = O.bf16_decode(rope[slots]), O.bf16_decode(orope)
+        assert np.all(np.abs(gr - orr) <= 2.0 ** -7 * np.abs(orr) + 1e-5)
+    assert total_bad <= 20
+
+
+# ------------------------------------------------------------------ indexer
+
+
+def _index_case(g, fmt, seqs, lens, H=64, D=128, ps=64, extra_pages=5):
+    pages = [(n + ps - 1) // ps for n in lens]
+    pps = max(pages)
+    num_pages = seqs * pps + extra_pages
+    pt = gen.page_table(g, seqs, pps, num_pages)
+    kraw = gen.normal(g, (num_pages * ps, D))
+    data, sc = O.index_prep(kraw, fmt != "f32", fmt)
+    pool = O.IndexPool(data, sc, fmt)
+    return pt, pool, num_pages
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_indexer_prepared_query(csa, fmt):
+    """Both sides score the same stored bytes: logits within 1e-4 of row max."""
+    g = gen.rng(600 + len(fmt))
+    lens = [5000, 513, 64 * 7 + 3, 17]
+    pt, pool, num_pages = _index_case(g, fmt, len(lens), lens)
+    qraw = gen.normal(g, (len(lens), 64, 128))
+    qcodes, qsc = O.index_prep(qraw, True, fmt)
+    w = gen.uniform(g, (len(lens), 64))
+    ld = 5008
+    logits = torch.full((len(lens), ld), float("nan"), device=DEV)
+    dpool = index_pool_to_device(pool, 64, 128)
+    qfmt = csa.CSA_FP8_E4M3 if fmt == "fp8" else csa.CSA_MXFP4
+    qs = t_dev(qsc.astype(np.float32)) if fmt == "fp8" else t_dev(qsc)
+    csa.indexer_score(t_dev(qcodes), t_dev(w), t_dev(np.arange(len(lens), dtype=np.int32)),
+                      t_dev(np.array(lens, np.int32)), max(lens), t_dev(pt), dpool, logits,
+                      q_fmt=qfmt, q_scale=qs)
+    got = logits.cpu().numpy()
+    qhat = O.index_dequant(qcodes, qsc, fmt)
+    for t, n in enumerate(lens):
+        slots = O.page_slot(pt[t], np.arange(n), 64)
+        want = O.indexer_logits(qhat[t], w[t], pool.rows(slots))
+        np.testing.assert_allclose(got[t, :n], want, rtol=0, atol=1e-4 * np.abs(want).max())
+        assert np.all(np.isnan(got[t, n:])), "wrote past row_len"
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_indexer_fused_query_prep(csa, fmt):
+    """bf16 query rotated and quantised inside the call: the prepared codes
+    (q_used) match the oracle's, and the logits match where they do."""
+    g = gen.rng(700 + len(fmt))
+    lens = [3000, 1000]
+    pt, pool, _ = _index_case(g, fmt, 2, lens)
+    q, qh = _bf16(gen.normal(g, (2, 64, 128)))
+    w = gen.uniform(g, (2, 64))
+    logits = torch.full((2, 3000), float("nan"), device=DEV)
+    if fmt == "fp8":
+        qu = torch.empty((2, 64, 128), dtype=torch.uint8, device=DEV)
+        qus = torch.empty((2, 64), dtype=torch.float32, device=DEV)
+    else:
+        qu = torch.empty((2, 64, 64), dtype=torch.uint8, device=DEV)
+        qus = torch.empty((2, 64, 4), dtype=torch.uint8, device=DEV)
+    csa.indexer_score(q, t_dev(w), t_dev(np.arange(2, dtype=np.int32)), t_dev(np.array(lens, np.int32)),
+                      3000, t_dev(pt), index_pool_to_device(pool, 64, 128), logits,
+                      prep=csa.CSA_PREP_HADAMARD | csa.CSA_PREP_QUANT, q_used=qu, q_used_scale=qus)
+    qcodes, qsc = O.index_prep(qh, True, fmt)
+    assert np.array_equal(qu.cpu().numpy(), qcodes)
+    assert np.array_equal(qus.cpu().numpy(), qsc)
+    qhat = O.index_dequant(qcodes, qsc, fmt)
+    got = logits.cpu().numpy()
+    for t, n in enumerate(lens):
+        want = O.indexer_logits(qhat[t], w[t], pool.rows(O.page_slot(pt[t], np.arange(n), 64)))
+        np.testing.assert_allclose(got[t, :n], want, rtol=0, atol=1e-4 * np.abs(want).max())
+
+
+def test_indexer_f32(csa):
+    g = gen.rng(800)
+    lens = [1024, 700]
+    pt, pool, _ = _index_case(g, "f32", 2, lens, H=8, D=64)
+    q = gen.normal(g, (2, 8, 64))
+    w = gen.uniform(g, (2, 8))
+    logits = torch.full((2, 1024), float("nan"), device=DEV)
+    csa.indexer_score(t_dev(q), t_dev(w), t_dev(np.arange(2, dtype=np.int32)),
+                      t_dev(np.array(lens, np.int32)), 1024, t_dev(pt),
+                      index_pool_to_device(pool, 64, 64), logits)
+    got = logits.cpu().numpy()
+    for t, n in enumerate(lens):
+        want = O.indexer_logits(q[t], w[t], pool.rows(O.page_slot(pt[t], np.arange(n), 64)))
+        np.testing.assert_allclose(got[t, :n], want, rtol=1e-5, atol=1e-5 * np.abs(want).max())
+
+
+# ------------------------------------------------------------------ top-512
+
+
+def _run_topk(csa, logits, lens, pt):
+    R = len(lens)
+    phys = torch.full((R, 512), -7, dtype=torch.int32, device=DEV)
+    logi = torch.full((R, 512), -7, dtype=torch.int32, device=DEV)
+    csa.topk512_page_select(t_dev(logits.astype(np.float32)), t_dev(np.array(lens, np.int32)),
+                            t_dev(np.arange(R, dtype=np.int32)), t_dev(pt), phys, logi)
+    return phys.cpu().numpy(), logi.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["random", "ties", "short", "special", "long"])
+def test_topk_bit_exact(csa, case):
+    g = gen.rng(900 + len(case))
+    if case == "random":
+        lens = [32768, 4097, 513, 10000]
+    elif case == "ties":
+        lens = [20000, 3000]
+    elif case == "short":
+        lens = [0, 1, 511, 512, 100]
+    elif case == "special":
+        lens = [2000, 1500]
+    else:
+        lens = [262144]
+    L = max(max(lens), 1)
+    pps = (L + 63) // 64
+    pt = gen.page_table(g, len(lens), pps, len(lens) * pps + 7)
+    logits = g.standard_normal((len(lens), L)).astype(np.float32) * 10
+    if case == "ties":
+        logits = np.round(logits / 4) * 4  # few distinct values, heavy ties
+    if case == "special":
+        logits[0, ::3] = -0.0
+        logits[0, 1::3] = 0.0
+        logits[0, 5:900] = 0.0
+        logits[1, :] = -np.inf
+        logits[1, 100:300] = 1.0
+        logits[1, 7] = np.nan
+        logits[1, 1000] = np.inf
+    phys, logi = _run_topk(csa, logits, lens, pt)
+    for r, n in enumerate(lens):
+        wp, wl = O.topk_page_select(logits[r], n, pt[r])
+        assert np.array_equal(logi[r], wl), f"row {r}: logical indices differ"
+        assert np.array_equal(phys[r], wp), f"row {r}: physical slots differ"
+
+
+def test_topk_identity_table_and_all_equal(csa):
+    logits = np.full((1, 5000), 2.5, np.float32)
+    pt = np.arange(79, dtype=np.int32)[None]
+    phys, logi = _run_topk(csa, logits, [5000], pt)
+    assert np.array_equal(logi[0], np.arange(512)) and np.array_equal(phys[0], np.arange(512))
+
+
+# ------------------------------------------------------------------ attention
+
+
+def _attn_case(g, fmt, B, Ls, H, ps_c=64, extra=3):
+    """Pools with random page tables; raw pool shares the c4 page table."""
+    pps = max((L + 255) // 256 for L in Ls)
+    num_pages = B * pps + extra
+    pt = gen.page_table(g, B, pps, num_pages)
+    c4 = O.KVPool(*O.quant_kv_entries(gen.normal(g, (num_pages * ps_c, 576)), fmt), fmt)
+    raw = O.KVPool(*O.quant_kv_entries(gen.normal(g, (num_pages * 256, 576)), fmt), fmt)
+    return pt, c4, raw
+
+
+@pytest.mark.parametrize("H,fmt,Ls", [
+    (64, "fp8", [131072 // 16, 700, 100, 2 * 4 + 1]),  # full 512 + window, short, p < 127
+    (128, "fp8", [20000, 3000]),
+    (16, "f32", [4096, 333]),
+])
+def test_csa_attention(csa, H, fmt, Ls):
+    g = gen.rng(1000 + H)
+    B = len(Ls)
+    pt, c4, raw = _attn_case(g, fmt, B, Ls, H)
+    sel_phys = np.full((B, 512), -1, np.int32)
+    for t, L in enumerate(Ls):
+        n = L // 4
+        logits = g.standard_normal(n)
+        sel_phys[t] = O.topk_page_select(logits, n, pt[t])[0]
+    qf = gen.normal(g, (B, H, 576))
+    if fmt == "fp8":
+        q, qh = _bf16(qf)
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    else:
+        q, qh = t_dev(qf), qf
+        out = torch.empty((B, H, 512), dtype=torch.float32, device=DEV)
+    dc4, draw = kv_pool_to_device(c4, 64), kv_pool_to_device(raw, 256)
+    scale = 576 ** -0.5
+    csa.csa_sparse_attn(q, t_dev(np.arange(B, dtype=np.int32)), t_dev(np.array(Ls, np.int32) - 1),
+                        t_dev(sel_phys), dc4, draw, t_dev(pt), 128, scale, out)
+    got = out.float().cpu().numpy()
+    for t, L in enumerate(Ls):
+        p = L - 1
+        sel = sel_phys[t][sel_phys[t] >= 0]
+        win = O.page_slot(pt[t], O.window_positions(p, 128), 256)
+        want = O.csa_attention_query(qh[t], c4.rows(sel), raw.rows(win), scale)
+        if fmt == "f32":
+            err = np.abs(got[t] - want).max(axis=1) / np.abs(want).max(axis=1)
+            assert err.max() <= 1e-4, err.max()
+        else:
+            assert np.abs(got[t] - want).max() <= 2e-2
+
+
+@pytest.mark.parametrize("fmt,Ls,H", [("fp8", [100, 128 * 40 + 77, 1048576 // 8], 64),
+                                      ("f32", [127, 128 * 9], 16)])
+def test_hca_attention(csa, fmt, Ls, H):
+    g = gen.rng(1100 + H)
+    B = len(Ls)
+    ratio = 128
+    # HCA pool: its own page table with 64 entries per page
+    hpp = max(L // ratio // 64 + 1 for L in Ls)
+    hca_pages = B * hpp + 2
+    hpt = gen.page_table(g, B, hpp, hca_pages)
+    hca = O.KVPool(*O.quant_kv_entries(gen.normal(g, (hca_pages * 64, 576)), fmt), fmt)
+    # raw pool: only the window's pages are read; every other page of the
+    # table points at page 0, which holds values that must not matter
+    rpp = max((L + 255) // 256 for L in Ls)
+    rpt = np.zeros((B, rpp), np.int32)
+    nxt = 1
+    for t, L in enumerate(Ls):
+        for pg in sorted(set(O.window_positions(L - 1, 128) // 256)):
+            rpt[t, pg] = nxt
+            nxt += 1
+    raw = O.KVPool(*O.quant_kv_entries(gen.normal(g, (nxt * 256, 576)), fmt), fmt)
+    qf = gen.normal(g, (B, H, 576))
+    if fmt == "fp8":
+        q, qh = _bf16(qf)
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    else:
+        q, qh = t_dev(qf), qf
+        out = torch.empty((B, H, 512), dtype=torch.float32, device=DEV)
+    scale = 576 ** -0.5
+    csa.hca_dense_attn(q, t_dev(np.arange(B, dtype=np.int32)), t_dev(np.array(Ls, np.int32) - 1),
+                       max(Ls), ratio, kv_pool_to_device(hca, 64), t_dev(hpt),
+                       kv_pool_to_device(raw, 256), t_dev(rpt), 128, scale, out)
+    got = out.float().cpu().numpy()
+    for t, L in enumerate(Ls):
+        want = O.hca_query(hca, raw, hpt[t], rpt[t], L - 1, ratio, qh[t], 128, scale)
+        if fmt == "f32":
+            err = np.abs(got[t] - want).max(axis=1) / np.abs(want).max(axis=1)
+            assert err.max() <= 1e-4, err.max()
+        else:
+            assert np.abs(got[t] - want).max() <= 2e-2
+
+
+# ------------------------------------------------------------------ argument checks
+
+
+def test_invalid_arguments_touch_nothing(csa):
+    out = torch.full((2, 512), -5, dtype=torch.int32, device=DEV)
+    logits = torch.zeros((2, 100), device=DEV)
+    with pytest.raises(csa.CsaError) as e:
+        csa.topk512_page_select(logits, torch.zeros(2, dtype=torch.int32, device=DEV),
+                                torch.zeros(2, dtype=torch.int32, device=DEV),
+                                torch.zeros((2, 1), dtype=torch.int32, device=DEV), out,
+                                c4_page_size=0)
+    assert e.value.status == csa.CSA_ERR_INVALID
+    torch.cuda.synchronize()
+    assert torch.all(out == -5)

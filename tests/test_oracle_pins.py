@@ -151,6 +151,20 @@ def test_hadamard_equals_sylvester_matrix(D):
     assert np.array_equal(H @ H.T, D * np.eye(D))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_hadamard_f32_butterflies_within_rounding_of_exact(D):
+    """The float32 butterfly evaluation differs from the exact rotation only by
+    float32 rounding: at most log2(D) + 1 roundings of values bounded by the
+    row's 2-norm."""
+    g = np.random.default_rng(40 + D)
+    v = g.standard_normal((500, D)).astype(np.float32)
+    exact = v.astype(np.float64) @ scipy.linalg.hadamard(D).T / math.sqrt(D)
+    got = O.hadamard_rotate_f32(v).astype(np.float64)
+    bound = (math.log2(D) + 2) * 2.0 ** -24 * np.linalg.norm(v, axis=1, keepdims=True) * math.sqrt(D)
+    assert np.all(np.abs(got - exact) <= bound)
+    assert O.hadamard_rotate_f32(v).dtype == np.float32
+
+
 def test_hadamard_preserves_scores():
     """Rotating both q and k leaves unquantised indexer logits unchanged."""
     g = np.random.default_rng(1)
