@@ -43,7 +43,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-queries", type=int, default=8)
+    ap.add_argument("--cpu-queries", type=int, default=32)
+    ap.add_argument("--no-graph", action="store_true")
     return ap.parse_args()
 
 
@@ -70,21 +71,56 @@ def stored_traffic(kernel: str, src_hash: str, launches_bytes_key="bytes_per_lau
     return e.get(launches_bytes_key)
 
 
-def time_steps(W, steps, warmup, copies):
+def capture_graphs(W, copies):
+    """One HIP graph per pool copy, each holding a whole step (every launch of
+    the library goes to the capturing stream; the step allocates nothing)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in range(copies):
+            W.step(c)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            W.step(c)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_steps(W, steps, warmup, copies, graph=True):
+    """(ms per step over the timed region, mean / median indexer kernel ms).
+    The step time is taken over `steps` graph replays (or eager steps); the
+    indexer kernel's duration from HIP events recorded around its launch on
+    the launch stream during `steps` eager steps of the same work."""
     import torch
     for i in range(warmup):
         W.step(i % copies)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    graphs = capture_graphs(W, copies) if graph else None
+    if graphs:
+        for i in range(warmup):
+            graphs[i % copies].replay()
     torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
-        W.step(i % copies, evs[i])
+        if graphs:
+            graphs[i % copies].replay()
+        else:
+            W.step(i % copies)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        W.step(i % copies, evs[i])
+    torch.cuda.synchronize()
     idx_ms = [a.elapsed_time(b) for a, b in evs]
     return ms, float(np.mean(idx_ms)), float(np.median(idx_ms))
 
@@ -173,7 +209,7 @@ def main():
     torch.cuda.set_device(0)
     wl = specs.DECODE_128K
     W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
-    ms, idx_ms, idx_med = time_steps(W, a.steps, a.warmup, a.copies)
+    ms, idx_ms, idx_med = time_steps(W, a.steps, a.warmup, a.copies, graph=not a.no_graph)
     qps = W.B / (ms / 1e3)
     ibytes = W.indexer_bytes()
     achieved = ibytes / (idx_ms / 1e3) / 1e9
@@ -195,7 +231,7 @@ def main():
         "config": {"workload": wl.name, "batch": W.B, "seq_len": wl.seq_len,
                    "compressed_entries": int(W.N[0]), "index_format": "fp8_e4m3+hadamard",
                    "index_heads": wl.index_heads, "attn_heads": wl.heads, "topk": 512,
-                   "window": wl.window, "pool_copies": a.copies},
+                   "window": wl.window, "pool_copies": a.copies, "hip_graph": not a.no_graph},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "indexer_mfma_kernel<false>",

@@ -171,12 +171,16 @@ def indexer_score(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPool,
 
 
 def topk512_page_select(logits, row_len, row_seq, page_table, phys_idx, logical_idx=None,
-                        c4_page_size=CSA_C4_PAGE, stream=None):
+                        c4_page_size=CSA_C4_PAGE, ws=None, stream=None):
     R = row_len.numel()
+    ld = logits.shape[-1]
+    if ws is None:
+        n = csa_workspace_size(CSA_OP_TOPK, R, ld, 1)
+        ws = torch.empty(n, dtype=torch.uint8, device=logits.device) if n else None
     _check("topk512_page_select", _topk(
-        _ptr(logits), logits.shape[-1], R, _ptr(row_len), _ptr(row_seq), _ptr(page_table),
-        page_table.shape[-1], int(c4_page_size), _ptr(phys_idx), _ptr(logical_idx), None, 0,
-        _stream(stream)))
+        _ptr(logits), ld, R, _ptr(row_len), _ptr(row_seq), _ptr(page_table),
+        page_table.shape[-1], int(c4_page_size), _ptr(phys_idx), _ptr(logical_idx), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def _attn_ws(op, T, entries, H, device, ws):

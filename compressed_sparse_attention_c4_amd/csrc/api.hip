@@ -38,7 +38,7 @@ size_t csa_workspace_size(int32_t op, int64_t rows, int64_t max_len, int32_t hea
   if (rows < 0 || max_len < 0 || heads <= 0) return 0;
   switch (op) {
     case CSA_OP_INDEXER: return indexer_ws_bytes(rows, heads);
-    case CSA_OP_TOPK: return topk_ws_bytes(rows, max_len);
+    case CSA_OP_TOPK: return topk_ws_bytes(rows, max_len);  // max_len = ld
     case CSA_OP_CSA_ATTN:
     case CSA_OP_HCA_ATTN: return attention_ws_bytes(rows, max_len, heads);
     default: return 0;
@@ -88,6 +88,7 @@ csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint
     if (q_used) return CSA_ERR_INVALID;
   } else if (k.fmt == CSA_FP8_E4M3 || k.fmt == CSA_MXFP4) {
     if (H_I != 64 || D_I != 128) return CSA_ERR_UNSUPPORTED;
+    if (k.page_size % 16 != 0) return CSA_ERR_UNSUPPORTED;
     if (!k.scale) return CSA_ERR_INVALID;
     if (q_fmt == CSA_BF16 || q_fmt == CSA_F32) {
       if (!(prep & CSA_PREP_QUANT)) return CSA_ERR_INVALID;
@@ -113,10 +114,12 @@ csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
                                const int32_t* page_table, int32_t pt_stride,
                                int32_t c4_page_size, int32_t* phys_idx, int32_t* logical_idx,
                                void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws_bytes;
   if (R < 0 || ld < 0 || pt_stride <= 0 || c4_page_size <= 0) return CSA_ERR_INVALID;
+  if (ld > topk_max_len()) return CSA_ERR_UNSUPPORTED;
   if (R == 0) return CSA_OK;
   if (!logits || !row_len || !row_seq || !page_table || !phys_idx) return CSA_ERR_INVALID;
+  const size_t need = topk_ws_bytes(R, ld);
+  if (need > ws_bytes || (need > 0 && !ws)) return CSA_ERR_WORKSPACE;
   return hip_status(launch_topk(logits, ld, R, row_len, row_seq, page_table, pt_stride,
                                 c4_page_size, 0, phys_idx, logical_idx, ws, stream));
 }

@@ -14,11 +14,13 @@
 // latent score term and folded into P for the value product.
 //
 // A workgroup owns one query and a contiguous range of its entry list; wave w
-// owns heads 16w..16w+15. Entries are gathered 32 at a time into LDS (codes
-// row-major for S, bf16 V^T for the value product), then every wave runs its
-// heads against the shared tile with an online softmax. Long entry lists are
-// split over several workgroups whose partial (max, sum, O) are merged by a
-// second kernel.
+// owns heads 16w..16w+15. Entries are gathered 32 at a time: each thread loads
+// an 8-entry x 8-dim block of codes, converts it with v_cvt_scalef32_pk_bf16_fp8
+// and writes it both row-major (K for S) and transposed (V^T for P V) with
+// 16-byte LDS stores; the next tile's gathers are issued before the current
+// tile's matrix work. Every wave then runs its heads against the shared tile
+// with an online softmax. Long entry lists are split over several workgroups
+// whose partial (max, sum, O) are merged by a second kernel.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -26,10 +28,10 @@ namespace csa {
 namespace {
 
 constexpr int kTile = 32;             // entries per LDS tile
-constexpr int kLatStride = 528;       // bytes per row of the fp8 code tile
+constexpr int kKStride = kKvDim + 8;  // bf16 elements per row of the K tile
 constexpr int kVtStride = kTile + 8;  // bf16 elements per row of V^T
-constexpr int kRopeStride = 72;       // bf16 elements per row of the RoPE tile
 constexpr int kPStride = kTile + 8;   // bf16 elements per row of P
+constexpr int kMaxSplit = 1024;       // entries one workgroup handles, at most
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -70,25 +72,40 @@ __device__ __forceinline__ int64_t entry_slot(int i, const EntryList& L, int t, 
   return -1;
 }
 
+// Two e4m3 codes (bytes 0,1 or 2,3 of w) -> two bf16 (exact), one instruction.
+template <bool kHi>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
+// The two pools are passed as plain pointers so that the per-entry choice
+// between them is a register select (a struct chosen at run time would be
+// copied to private memory).
 template <int kNW, bool kOutF32>
 __global__ void __launch_bounds__(kNW * 64)
 attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
                  const int32_t* __restrict__ q_pos, bool hca, const int32_t* __restrict__ phys_idx,
-                 int k_sel, int ratio, csa_kv_pool comp, const int32_t* __restrict__ comp_pt,
-                 int comp_pt_stride, csa_kv_pool raw, const int32_t* __restrict__ raw_pt,
+                 int k_sel, int ratio, const uint8_t* __restrict__ c_lat,
+                 const float* __restrict__ c_sc, const uint16_t* __restrict__ c_rope, int c_ps,
+                 const int32_t* __restrict__ comp_pt, int comp_pt_stride,
+                 const uint8_t* __restrict__ r_lat, const float* __restrict__ r_sc,
+                 const uint16_t* __restrict__ r_rope, int r_ps, const int32_t* __restrict__ raw_pt,
                  int raw_pt_stride, int window, float scale, void* __restrict__ out,
                  float* __restrict__ part, int split_len, int nsplit) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_lat[kTile * kLatStride];
+  // K tile, row-major bf16 [entry][576] (latent codes as exact bf16, then the
+  // RoPE dims), and the value tile transposed, bf16 [dim][entry].
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kTile * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[kLatent * kVtStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_rope[kTile * kRopeStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_p[kNW][16 * kPStride];
   __shared__ float s_scale[kTile];
-  __shared__ int s_valid[kTile];
+  __shared__ int32_t s_eslot[kMaxSplit];  // entry slots of this split: slot*2 + pool, -1 masked
+  __shared__ float s_escale[kMaxSplit];   // and their FP8 scales
 
   const int t = blockIdx.y;
   const int split = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int seq = q_seq[t];
@@ -98,7 +115,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
   const int e_begin = split * split_len;
   const int e_end = min(total, e_begin + split_len);
 
-  // Heads of this wave: hbase + 16*wave .. +15 (grid.z splits H in blocks of 16*kNW).
+  // Heads of this wave: hbase .. hbase+15 (grid.z splits H in blocks of 16*kNW).
   const int hbase = blockIdx.z * kNW * 16 + wave * 16;
   // Query operand (A): head hbase + col, dims step*32 + grp*8 .. +7.
   v4i qa[18];
@@ -118,61 +135,113 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
 #pragma unroll
   for (int n = 0; n < 32; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int nthreads = kNW * 64;
-  for (int tile0 = e_begin; tile0 < e_end; tile0 += kTile) {
-    // ---- gather the tile into LDS
-    if (threadIdx.x < kTile) {
-      const int i = tile0 + threadIdx.x;
-      int pool = 0;
-      int64_t slot = -1;
-      if (i < e_end)
-        slot = entry_slot(i, L, t, seq, hca, phys_idx, k_sel, comp_pt, comp_pt_stride,
-                          comp.page_size, raw_pt, raw_pt_stride, raw.page_size, pool);
-      s_valid[threadIdx.x] = slot >= 0 ? (int)(slot * 2 + pool) + 1 : 0;  // packed, 0 = masked
+  // Slots and scales of every entry of this split, resolved once (one round of
+  // page-table / index reads for the whole split, all threads in parallel), so
+  // the tile gathers below depend on LDS only.
+  for (int i = tid; i < e_end - e_begin; i += kNW * 64) {
+    int pool = 0;
+    const int64_t slot = entry_slot(e_begin + i, L, t, seq, hca, phys_idx, k_sel, comp_pt,
+                                    comp_pt_stride, c_ps, raw_pt, raw_pt_stride, r_ps, pool);
+    s_eslot[i] = slot >= 0 ? (int32_t)(slot * 2 + pool) : -1;
+    float sc = 0.f;
+    if (slot >= 0) {
+      // both loads issued (one at index 0) so they cannot be merged into a
+      // load through a selected pointer
+      const float rs = r_sc[pool ? slot : 0];
+      const float cs = c_sc[pool ? 0 : slot];
+      sc = pool ? rs : cs;
     }
-    __syncthreads();
-    // latent codes: 32 entries x 32 chunks of 16 B
-    for (int c = threadIdx.x; c < kTile * 32; c += nthreads) {
-      const int e = c & (kTile - 1);
-      const int ch = c >> 5;
-      const int v = s_valid[e];
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (v) {
-        const int64_t slot = (int64_t)((v - 1) >> 1);
-        const uint8_t* base = (const uint8_t*)(((v - 1) & 1) ? raw.latent : comp.latent);
-        x = *reinterpret_cast<const uint4*>(base + slot * kLatent + ch * 16);
-      }
-      *reinterpret_cast<uint4*>(s_lat + e * kLatStride + ch * 16) = x;
-      const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+    s_escale[i] = sc;
+  }
+  __syncthreads();
+
+  // Staging task of this thread (256 tasks per tile: kNW*64 threads loop):
+  // an 8-entry x 8-dim block of latent codes, entries 8*eg.., dims 8*c..,
+  // plus one 8-dim RoPE chunk (entry re, dims 512 + 8*rc).
+  constexpr int kTasks = 256 / (kNW * 64);  // staging tasks per thread
+  uint2 codes[kTasks][8];
+  uint4 ropev[kTasks];
+  auto issue_loads = [&](int tile0) {
+    const int lt0 = tile0 - e_begin;  // tile start within the split
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t code = (w4[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        s_vt[(ch * 16 + i) * kVtStride + e] = (uint16_t)e4m3_to_bf16(code);
+    for (int k = 0; k < kTasks; ++k) {
+      const int task = tid + k * kNW * 64;
+      const int eg = task & 3, c = task >> 2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int li = lt0 + 8 * eg + j;
+        const int es = li < e_end - e_begin ? s_eslot[li] : -1;
+        uint2 v = make_uint2(0, 0);
+        if (es >= 0) {
+          const int64_t slot = es >> 1;
+          // one global load per pool under a lane predicate (a selected
+          // pointer would be lowered to a private-memory table)
+          if (es & 1) v = *reinterpret_cast<const uint2*>(r_lat + slot * kLatent + 8 * c);
+          else v = *reinterpret_cast<const uint2*>(c_lat + slot * kLatent + 8 * c);
+        }
+        codes[k][j] = v;
       }
-    }
-    // RoPE dims: 32 entries x 8 chunks of 16 B; scales
-    for (int c = threadIdx.x; c < kTile * 8; c += nthreads) {
-      const int e = c & (kTile - 1);
-      const int ch = c >> 5;
-      const int v = s_valid[e];
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (v) {
-        const int64_t slot = (int64_t)((v - 1) >> 1);
-        const uint16_t* base = (const uint16_t*)(((v - 1) & 1) ? raw.rope : comp.rope);
-        x = *reinterpret_cast<const uint4*>(base + slot * kRope + ch * 8);
+      const int re = task & 31, rc = task >> 5;
+      const int li = lt0 + re;
+      const int es = li < e_end - e_begin ? s_eslot[li] : -1;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (es >= 0) {
+        const int64_t slot = es >> 1;
+        if (es & 1) v = *reinterpret_cast<const uint4*>(r_rope + slot * kRope + 8 * rc);
+        else v = *reinterpret_cast<const uint4*>(c_rope + slot * kRope + 8 * rc);
       }
-      *reinterpret_cast<uint4*>(s_rope + e * kRopeStride + ch * 8) = x;
+      ropev[k] = v;
     }
-    if (threadIdx.x < kTile) {
-      const int v = s_valid[threadIdx.x];
-      float sc = 0.f;
-      if (v) {
-        const int64_t slot = (int64_t)((v - 1) >> 1);
-        sc = (((v - 1) & 1) ? raw.latent_scale : comp.latent_scale)[slot];
+  };
+  float scale_reg = 0.f;  // threads < kTile: scale of entry tile0 + tid
+  auto issue_scale = [&](int tile0) {
+    const int li = tile0 - e_begin + tid;
+    scale_reg = (tid < kTile && li < e_end - e_begin) ? s_escale[li] : 0.f;
+  };
+
+  if (e_begin < e_end) {
+    issue_loads(e_begin);
+    issue_scale(e_begin);
+  }
+  for (int tile0 = e_begin; tile0 < e_end; tile0 += kTile) {
+    // ---- write the staged tile to LDS (exact fp8 -> bf16 conversion)
+#pragma unroll
+    for (int k = 0; k < kTasks; ++k) {
+      const int task = tid + k * kNW * 64;
+      const int eg = task & 3, c = task >> 2;
+      uint32_t kb[8][4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kb[j][0] = fp8x2_to_bf16x2<false>(codes[k][j].x);
+        kb[j][1] = fp8x2_to_bf16x2<true>(codes[k][j].x);
+        kb[j][2] = fp8x2_to_bf16x2<false>(codes[k][j].y);
+        kb[j][3] = fp8x2_to_bf16x2<true>(codes[k][j].y);
+        *reinterpret_cast<uint4*>(&s_k[(8 * eg + j) * kKStride + 8 * c]) =
+            make_uint4(kb[j][0], kb[j][1], kb[j][2], kb[j][3]);
       }
-      s_scale[threadIdx.x] = sc;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int w = i >> 1;
+        uint32_t d[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t a = kb[2 * jj][w], b = kb[2 * jj + 1][w];
+          d[jj] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+        }
+        *reinterpret_cast<uint4*>(&s_vt[(8 * c + i) * kVtStride + 8 * eg]) =
+            make_uint4(d[0], d[1], d[2], d[3]);
+      }
+      const int re = task & 31, rc = task >> 5;
+      *reinterpret_cast<uint4*>(&s_k[re * kKStride + kLatent + 8 * rc]) = ropev[k];
     }
+    if (tid < kTile) s_scale[tid] = scale_reg;
     __syncthreads();
+    // ---- prefetch the next tile while this one is computed
+    const int next = tile0 + kTile;
+    if (next < e_end) {
+      issue_loads(next);
+      issue_scale(next);
+    }
 
     // ---- S = Q K^T for 16 heads x 32 entries (two 16-column blocks)
     float sv[2][4];
@@ -182,20 +251,15 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
       v4f acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const uint2 c8 = *reinterpret_cast<const uint2*>(s_lat + e * kLatStride + s * 32 + grp * 8);
-        v4i bk;
-        bk[0] = (int)(e4m3_to_bf16(c8.x & 0xFF) | (e4m3_to_bf16((c8.x >> 8) & 0xFF) << 16));
-        bk[1] = (int)(e4m3_to_bf16((c8.x >> 16) & 0xFF) | (e4m3_to_bf16(c8.x >> 24) << 16));
-        bk[2] = (int)(e4m3_to_bf16(c8.y & 0xFF) | (e4m3_to_bf16((c8.y >> 8) & 0xFF) << 16));
-        bk[3] = (int)(e4m3_to_bf16((c8.y >> 16) & 0xFF) | (e4m3_to_bf16(c8.y >> 24) << 16));
-        acc_l = mfma_bf16(qa[s], bk, acc_l);
+        const uint4 kk = *reinterpret_cast<const uint4*>(&s_k[e * kKStride + s * 32 + grp * 8]);
+        acc_l = mfma_bf16(qa[s], v4i{(int)kk.x, (int)kk.y, (int)kk.z, (int)kk.w}, acc_l);
       }
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint4 r8 = *reinterpret_cast<const uint4*>(s_rope + e * kRopeStride + s * 32 + grp * 8);
-        acc_r = mfma_bf16(qa[16 + s], v4i{(int)r8.x, (int)r8.y, (int)r8.z, (int)r8.w}, acc_r);
+      for (int s = 16; s < 18; ++s) {
+        const uint4 kk = *reinterpret_cast<const uint4*>(&s_k[e * kKStride + s * 32 + grp * 8]);
+        acc_r = mfma_bf16(qa[s], v4i{(int)kk.x, (int)kk.y, (int)kk.z, (int)kk.w}, acc_r);
       }
-      const bool valid = s_valid[e] != 0;
+      const bool valid = tile0 + e < e_end && s_eslot[tile0 - e_begin + e] >= 0;
       const float sc = s_scale[e];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -379,11 +443,14 @@ attn_f32_kernel(const float* __restrict__ q, int H, const int32_t* __restrict__ 
 }
 
 int pick_splits(int T, int H, int max_entries) {
-  // Aim for ~1024 waves in flight, each split at least two tiles long.
-  const int nw = H / 16;
+  // About one workgroup per CU (256), each split at least two tiles long and
+  // at most kMaxSplit entries.
+  const int hblocks = H >= 64 ? H / 64 : 1;
   const int max_split = (max_entries + 2 * kTile - 1) / (2 * kTile);
-  int s = (1024 + T * nw - 1) / (T * nw);
+  int s = (256 + T * hblocks - 1) / (T * hblocks);
   if (s > max_split) s = max_split;
+  const int min_split = (max_entries + kMaxSplit - 1) / kMaxSplit;
+  if (s < min_split) s = min_split;
   return s < 1 ? 1 : s;
 }
 
@@ -413,11 +480,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   float* part = nsplit > 1 ? (float*)a.ws : nullptr;
   const int nw = a.H >= 64 ? 4 : a.H / 16;  // waves per workgroup (16 heads each)
   dim3 grid(nsplit, a.T, a.H / (16 * nw));
-#define CSA_ATTN(NW, FO)                                                                   \
-  hipLaunchKernelGGL((attn_mfma_kernel<NW, FO>), grid, dim3(NW * 64), 0, s,               \
-                     (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel, \
-                     a.ratio, a.comp, a.comp_pt, a.comp_pt_stride, a.raw, a.raw_pt,      \
-                     a.raw_pt_stride, a.window, a.scale, a.out, part, split_len, nsplit)
+#define CSA_ATTN(NW, FO)                                                                      \
+  hipLaunchKernelGGL((attn_mfma_kernel<NW, FO>), grid, dim3(NW * 64), 0, s,                  \
+                     (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,   \
+                     a.ratio, (const uint8_t*)a.comp.latent, a.comp.latent_scale,             \
+                     (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt,              \
+                     a.comp_pt_stride, (const uint8_t*)a.raw.latent, a.raw.latent_scale,      \
+                     (const uint16_t*)a.raw.rope, a.raw.page_size, a.raw_pt, a.raw_pt_stride, \
+                     a.window, a.scale, a.out, part, split_len, nsplit)
   if (nw == 4) { if (f32o) CSA_ATTN(4, true); else CSA_ATTN(4, false); }
   else if (nw == 2) { if (f32o) CSA_ATTN(2, true); else CSA_ATTN(2, false); }
   else { if (f32o) CSA_ATTN(1, true); else CSA_ATTN(1, false); }

@@ -57,6 +57,7 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 size_t attention_ws_bytes(int64_t T, int64_t max_entries, int H);
 size_t topk_ws_bytes(int64_t R, int64_t max_len);
+int64_t topk_max_len();
 size_t indexer_ws_bytes(int64_t T, int H_I);
 
 }  // namespace csa

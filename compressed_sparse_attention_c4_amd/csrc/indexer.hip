@@ -26,8 +26,9 @@ namespace {
 constexpr int kHeads = 64;   // indexer heads handled by the MFMA path
 constexpr int kDim = 128;    // indexer head dim handled by the MFMA path
 constexpr int kWaves = 4;
-constexpr int kUnroll = 4;   // 16-entry groups in flight per wave
+constexpr int kUnroll = 8;   // 16-entry groups in flight per wave
 constexpr int kWgEntries = kWaves * kUnroll * 16;
+constexpr int kMaxChunk = 8 * kWgEntries;  // entries per workgroup, at most
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, v4f c) {
   // format 0 = FP8 e4m3 for both operands; e8m0 scale 127 = 2^0
@@ -52,6 +53,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     const void* __restrict__ kscale, int page_size, float* __restrict__ logits,
                     int64_t ld, int chunk) {
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K / q row
+  __shared__ int32_t s_pages[kMaxChunk / 16 + 2];      // physical pages of this chunk
   const int t = blockIdx.y;
   const int n = row_len[t];
   const int c0 = blockIdx.x * chunk;
@@ -62,6 +64,13 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
+
+  // Page ids of the chunk, once: the scan below then issues its index-K loads
+  // without waiting on page-table reads.
+  const int32_t* ptrow = pt + (int64_t)seq * pt_stride;
+  const int pg0 = c0 / page_size;
+  const int npg = (c1 - 1) / page_size - pg0 + 1;
+  for (int i = threadIdx.x; i < npg; i += kWaves * 64) s_pages[i] = ptrow[pg0 + i];
 
   // Query operands: head hb*16 + col, K-elements grp*32 .. grp*32+31.
   v8i a[4];
@@ -93,26 +102,38 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
       if (!kFp4) v *= reinterpret_cast<const float*>(qs)[(int64_t)t * kHeads + h];
       wq[hb * 4 + r] = v;
     }
+  __syncthreads();
 
-  const int32_t* ptrow = pt + (int64_t)seq * pt_stride;
+  // Groups of 16 entries never straddle a page (page_size % 16 == 0 and the
+  // chunk starts on a multiple of 16), so a group's page is wave-uniform.
   for (int base = c0 + wave * 16; base < c1; base += kWgEntries) {
     v8i b[kUnroll];
     int sb[kUnroll];
+    float ks[kUnroll];
     int64_t slot[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int j = base + u * kWaves * 16 + col;
+      const int g0 = base + u * kWaves * 16;  // first entry of the group
+      const int j = g0 + col;
       const bool valid = j < c1;
-      slot[u] = valid ? (int64_t)ptrow[j / page_size] * page_size + j % page_size : 0;
+      const int pg = s_pages[min(g0, c1 - 1) / page_size - pg0];
+      slot[u] = valid ? (int64_t)pg * page_size + j % page_size : 0;
+      // unconditional loads (slot 0 for an invalid lane), zeroed afterwards
       const uint8_t* p = kdata + slot[u] * kRowBytes + grp * (kRowBytes / 4);
       if (kFp4) {
-        uint4 x = valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+        const uint4 x = *reinterpret_cast<const uint4*>(p);
         b[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        sb[u] = valid ? reinterpret_cast<const uint8_t*>(kscale)[slot[u] * 4 + grp] : 127;
+        sb[u] = reinterpret_cast<const uint8_t*>(kscale)[slot[u] * 4 + grp];
+        ks[u] = 1.f;
       } else {
-        uint4 x = valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-        uint4 y = valid ? *reinterpret_cast<const uint4*>(p + 16) : make_uint4(0, 0, 0, 0);
+        const uint4 x = *reinterpret_cast<const uint4*>(p);
+        const uint4 y = *reinterpret_cast<const uint4*>(p + 16);
         b[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        sb[u] = 127;
+        ks[u] = reinterpret_cast<const float*>(kscale)[slot[u]];
+      }
+      if (!valid) {
+        b[u] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
         sb[u] = 127;
       }
     }
@@ -131,10 +152,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
       const int j = base + u * kWaves * 16 + col;
-      if (grp == 0 && j < c1) {
-        if (!kFp4) v *= reinterpret_cast<const float*>(kscale)[slot[u]];
-        logits[(int64_t)t * ld + j] = v;
-      }
+      if (grp == 0 && j < c1) logits[(int64_t)t * ld + j] = v * ks[u];
     }
   }
 }
@@ -217,12 +235,12 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
       e = hipMemcpyAsync(q_used_scale, q_scale, scale_bytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
-  // Chunk the rows so the grid has >= ~2048 workgroups.
+  // Chunk the rows so the grid has ~1024 workgroups (4 per CU).
   int64_t total = (int64_t)T * max_row_len;
-  int64_t chunk = total / 2048;
+  int64_t chunk = total / 1024;
   chunk = ((chunk + kWgEntries - 1) / kWgEntries) * kWgEntries;
   if (chunk < kWgEntries) chunk = kWgEntries;
-  if (chunk > 16 * kWgEntries) chunk = 16 * kWgEntries;
+  if (chunk > kMaxChunk) chunk = kMaxChunk;
   dim3 grid((unsigned)((max_row_len + chunk - 1) / chunk), T);
   if (k.fmt == CSA_MXFP4)
     hipLaunchKernelGGL(indexer_mfma_kernel<true>, grid, dim3(kWaves * 64), 0, s, qc, qs, w,

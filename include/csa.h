@@ -195,6 +195,9 @@ csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint
  * below -inf. If row_len <= 512 every entry is selected. The selected entries are
  * written in ascending j; the unused tail of a row is -1.
  *   phys_idx    int32 [R][512] (required); logical_idx int32 [R][512] or NULL.
+ *   ws          csa_workspace_size(CSA_OP_TOPK, R, ld, 1) bytes: rows longer than
+ *               32768 entries, and rows longer than 8192 when R < 128, are reduced
+ *               in two launches through it; otherwise 0 bytes. ld up to 2097152.
  */
 csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
                                const int32_t* row_len, const int32_t* row_seq,
@@ -249,7 +252,8 @@ csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
 
 /* Workspace sizes (bytes) for the calls that take `ws`.
  * op: CSA_OP_INDEXER (rows = T, heads = H_I; needed only when the query is
- *     prepared inside the call and q_used is NULL), CSA_OP_TOPK (0),
+ *     prepared inside the call and q_used is NULL), CSA_OP_TOPK (rows = R,
+ *     max_len = ld),
  *     CSA_OP_CSA_ATTN / CSA_OP_HCA_ATTN (rows = T, max_len = most entries of
  *     one query's list, heads = H). */
 #define CSA_OP_INDEXER  0

@@ -1,0 +1,130 @@
+"""CPU checks of the C ABI: libcsa.so loads, exports every function that
+include/csa.h declares, and rejects bad arguments on the host before any
+launch (no GPU call is made on these paths)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "csa.h")
+LIB = os.path.join(ROOT, "compressed_sparse_attention_c4_amd", "libcsa.so")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:csa_status|size_t|const char\s*\*|char\s*\*)\s*\**\s*(\w+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libcsa.so not built")
+    return C.CDLL(LIB)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("c4_compress", "csa_index_prep", "indexer_score", "topk512_page_select",
+              "csa_sparse_attn", "hca_dense_attn", "csa_workspace_size", "csa_status_string",
+              "csa_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in csa.h but not exported"
+
+
+class KvPoolC(C.Structure):
+    _fields_ = [("latent", C.c_void_p), ("latent_scale", C.c_void_p), ("rope", C.c_void_p),
+                ("fmt", C.c_int32), ("page_size", C.c_int32), ("num_pages", C.c_int64)]
+
+
+class IndexPoolC(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("scale", C.c_void_p), ("fmt", C.c_int32),
+                ("dim", C.c_int32), ("page_size", C.c_int32), ("num_pages", C.c_int64)]
+
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+FAKE = 0x1000  # never dereferenced: every call below fails its host checks
+
+
+def test_status_strings_and_version(lib):
+    lib.csa_status_string.restype = C.c_char_p
+    lib.csa_version.restype = C.c_char_p
+    assert lib.csa_status_string(0) == b"ok"
+    assert lib.csa_status_string(1) == b"invalid argument"
+    assert lib.csa_version().count(b".") == 2
+
+
+def test_workspace_sizes(lib):
+    lib.csa_workspace_size.restype = C.c_size_t
+    lib.csa_workspace_size.argtypes = [C.c_int32, C.c_int64, C.c_int64, C.c_int32]
+    assert lib.csa_workspace_size(1, 32, 32768, 64) == 0          # top-k needs none
+    assert lib.csa_workspace_size(0, 32, 0, 64) >= 32 * 64 * 132  # prepared query
+    assert lib.csa_workspace_size(2, -1, 10, 64) == 0
+
+
+def test_compress_rejects_bad_arguments(lib):
+    f = lib.c4_compress
+    f.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, KvPoolC, C.c_void_p]
+    good = KvPoolC(FAKE, FAKE, FAKE, 2, 64, 10)
+    assert f(FAKE, 1, FAKE, FAKE, 1, 16, 0, FAKE, FAKE, FAKE, 4, good, None) == INVALID      # ratio 0
+    assert f(FAKE, 1, FAKE, FAKE, 1, 16, 2000, FAKE, FAKE, FAKE, 4, good, None) == INVALID   # ratio > 1024
+    assert f(FAKE, 3, FAKE, FAKE, 1, 16, 4, FAKE, FAKE, FAKE, 4, good, None) == INVALID      # x fmt MXFP4
+    bad_pool = KvPoolC(FAKE, None, FAKE, 2, 64, 10)                                          # FP8 without scale
+    assert f(FAKE, 1, FAKE, FAKE, 1, 16, 4, FAKE, FAKE, FAKE, 4, bad_pool, None) == INVALID
+    assert f(None, 1, FAKE, FAKE, 1, 16, 4, FAKE, FAKE, FAKE, 4, good, None) == INVALID      # null x
+    assert f(FAKE, 1, FAKE, FAKE, 0, 16, 4, FAKE, FAKE, FAKE, 4, good, None) == 0            # B = 0: no-op
+
+
+def test_indexer_rejects_bad_arguments(lib):
+    f = lib.indexer_score
+    f.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_uint32, C.c_void_p, C.c_int32, C.c_int32,
+                  C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, IndexPoolC,
+                  C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    fp8 = IndexPoolC(FAKE, FAKE, 2, 128, 64, 10)
+    # raw bf16 query without the quant flag
+    assert f(FAKE, 1, None, 1, FAKE, 4, 64, 128, FAKE, FAKE, 100, FAKE, 2, fp8, FAKE, 100, None, None,
+             FAKE, 1 << 20, None) == INVALID
+    # 32 heads on the MFMA path
+    assert f(FAKE, 2, FAKE, 0, FAKE, 4, 32, 128, FAKE, FAKE, 100, FAKE, 2, fp8, FAKE, 100, None, None,
+             None, 0, None) == UNSUPPORTED
+    # ld smaller than the longest row
+    assert f(FAKE, 2, FAKE, 0, FAKE, 4, 64, 128, FAKE, FAKE, 100, FAKE, 2, fp8, FAKE, 99, None, None,
+             None, 0, None) == INVALID
+    # in-call preparation without workspace or q_used
+    assert f(FAKE, 1, None, 3, FAKE, 4, 64, 128, FAKE, FAKE, 100, FAKE, 2, fp8, FAKE, 100, None, None,
+             None, 0, None) == WORKSPACE
+    # prepared query of the wrong format
+    assert f(FAKE, 3, FAKE, 0, FAKE, 4, 64, 128, FAKE, FAKE, 100, FAKE, 2, fp8, FAKE, 100, None, None,
+             None, 0, None) == INVALID
+
+
+def test_topk_and_attention_reject_bad_arguments(lib):
+    t = lib.topk512_page_select
+    t.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                  C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    assert t(FAKE, 100, 2, FAKE, FAKE, FAKE, 4, 0, FAKE, None, None, 0, None) == INVALID
+    assert t(FAKE, 100, 2, FAKE, FAKE, FAKE, 4, 64, None, None, None, 0, None) == INVALID
+    assert t(FAKE, 100, 0, FAKE, FAKE, FAKE, 4, 64, FAKE, None, None, 0, None) == 0
+    a = lib.csa_sparse_attn
+    a.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                  C.c_int32, KvPoolC, KvPoolC, C.c_void_p, C.c_int32, C.c_int32, C.c_float,
+                  C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]
+    fp8 = KvPoolC(FAKE, FAKE, FAKE, 2, 64, 10)
+    raw = KvPoolC(FAKE, FAKE, FAKE, 2, 256, 10)
+    f32 = KvPoolC(FAKE, None, FAKE, 0, 256, 10)
+    assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 513, fp8, raw, FAKE, 4, 128, 0.04, FAKE, 1, FAKE, 1 << 30, None) == INVALID
+    assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 512, fp8, f32, FAKE, 4, 128, 0.04, FAKE, 1, FAKE, 1 << 30, None) == INVALID
+    assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 512, fp8, raw, FAKE, 4, 0, 0.04, FAKE, 1, FAKE, 1 << 30, None) == INVALID
+    assert a(FAKE, 1, 2, 48, FAKE, FAKE, FAKE, 512, fp8, raw, FAKE, 4, 128, 0.04, FAKE, 1, FAKE, 1 << 30, None) == UNSUPPORTED
+    # two queries over 640 entries are split over several workgroups: needs a workspace
+    assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 512, fp8, raw, FAKE, 4, 128, 0.04, FAKE, 1, None, 0, None) == WORKSPACE

@@ -239,7 +239,7 @@ def _run_topk(csa, logits, lens, pt):
     return phys.cpu().numpy(), logi.cpu().numpy()
 
 
-@pytest.mark.parametrize("case", ["random", "ties", "short", "special", "long"])
+@pytest.mark.parametrize("case", ["random", "ties", "short", "special", "long", "near_ties", "positive"])
 def test_topk_bit_exact(csa, case):
     g = gen.rng(900 + len(case))
     if case == "random":
@@ -250,6 +250,8 @@ def test_topk_bit_exact(csa, case):
         lens = [0, 1, 511, 512, 100]
     elif case == "special":
         lens = [2000, 1500]
+    elif case in ("near_ties", "positive"):
+        lens = [32768, 5000, 600]
     else:
         lens = [262144]
     L = max(max(lens), 1)
@@ -258,6 +260,10 @@ def test_topk_bit_exact(csa, case):
     logits = g.standard_normal((len(lens), L)).astype(np.float32) * 10
     if case == "ties":
         logits = np.round(logits / 4) * 4  # few distinct values, heavy ties
+    if case == "near_ties":  # equal values inside the threshold bucket, bucket fits in LDS
+        logits = np.round(logits * 20) / 20
+    if case == "positive":  # indexer-like: positive, crowded into few exponent buckets
+        logits = np.abs(logits) * 3 + 200
     if case == "special":
         logits[0, ::3] = -0.0
         logits[0, 1::3] = 0.0
@@ -387,3 +393,13 @@ def test_invalid_arguments_touch_nothing(csa):
     assert e.value.status == csa.CSA_ERR_INVALID
     torch.cuda.synchronize()
     assert torch.all(out == -5)
+
+
+# ------------------------------------------------------------------ end to end
+
+
+@pytest.mark.parametrize("seed_offset", [0, 1])
+def test_tiny_fp32_decode_end_to_end(csa, seed_offset):
+    from tests.e2e_tiny import run_tiny_decode_check
+    res = run_tiny_decode_check(csa, torch, seed_offset)
+    assert res["topk_equal"] or "attn_rel_err" not in res

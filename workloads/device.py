@@ -137,6 +137,8 @@ class CsaDecode:
         self.out = torch.empty((B, self.H, 512), dtype=torch.bfloat16, device=DEV)
         n = csa.csa_workspace_size(csa.CSA_OP_CSA_ATTN, B, 512 + wl.window, self.H)
         self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        n = csa.csa_workspace_size(csa.CSA_OP_TOPK, B, self.maxN, 1)
+        self.topk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         torch.cuda.synchronize()
 
     # algorithmic bytes of one indexer launch: index-K rows + prepared q +
@@ -180,6 +182,7 @@ class CsaDecode:
                           idx, self.logits, q_fmt=self.fmt, q_scale=self.q_scale)
         if ev is not None:
             ev[1].record()
-        csa.topk512_page_select(self.logits, self.row_len, self.row_seq, self.pt, self.phys)
+        csa.topk512_page_select(self.logits, self.row_len, self.row_seq, self.pt, self.phys,
+                                ws=self.topk_ws)
         csa.csa_sparse_attn(self.q_attn, self.row_seq, self.q_pos, self.phys, kv, self.raw, self.pt,
                             wl.window, wl.softmax_scale, self.out, ws=self.attn_ws)
