@@ -45,6 +45,10 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-queries", type=int, default=32)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the 1M decode, prefill and HCA workloads")
+    ap.add_argument("--profile-only", choices=["decode_128k", "decode_1m", "prefill", "hca_ragged"],
+                    help="run only this workload's steps (eager, for a profiler) and print nothing else")
     return ap.parse_args()
 
 
@@ -123,6 +127,81 @@ def time_steps(W, steps, warmup, copies, graph=True):
     torch.cuda.synchronize()
     idx_ms = [a.elapsed_time(b) for a, b in evs]
     return ms, float(np.mean(idx_ms)), float(np.median(idx_ms))
+
+
+def secondary(a):
+    """The other workloads of the method, each timed the same way (graph
+    replays for the step, HIP events around the indexer launch)."""
+    import torch
+    from workloads import specs
+    from workloads.device import CsaDecode, CsaPrefill, HcaCsaRagged, hca_build_input
+    import compressed_sparse_attention_c4_amd as csa
+    out = {}
+    steps = max(10, a.steps // 2)
+    # decode at 1M context, batch 4, MXFP4 index-K, 128 heads
+    wl = specs.DECODE_1M
+    W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
+    ms, idx_ms, _ = time_steps(W, steps, a.warmup, a.copies, graph=not a.no_graph)
+    gbs = W.indexer_bytes() / (idx_ms / 1e3) / 1e9
+    out[wl.name] = {"queries_per_s": round(W.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
+                    "indexer": {"kernel": "indexer_mfma_kernel<true>", "kernel_ms": round(idx_ms, 5),
+                                "bytes_per_launch": W.indexer_bytes(), "achieved_GBs": round(gbs, 1),
+                                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+                    "step_hbm_frac": round(W.step_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del W
+    torch.cuda.empty_cache()
+    # chunked prefill: 4096 new tokens on a 131072-token context
+    wl = specs.PREFILL_4K
+    W = CsaPrefill(wl)
+    ms, idx_ms, _ = time_steps(W, max(5, steps // 4), 2, 1, graph=not a.no_graph)
+    tf = W.indexer_flops() / (idx_ms / 1e3) / 1e12
+    out[wl.name] = {"tokens_per_s": round(W.new / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+                    "indexer_gemm": {"kernel": "indexer_mfma_kernel<false>", "kernel_ms": round(idx_ms, 4),
+                                     "flop_per_launch": W.indexer_flops(), "achieved_TFLOPs": round(tf, 1),
+                                     "fp8_mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}}
+    del W
+    torch.cuda.empty_cache()
+    # HCA layer + CSA layer over 16 ragged sequences
+    wl = specs.HCA_RAGGED
+    W = HcaCsaRagged(wl, copies=a.copies)
+    ms, idx_ms, _ = time_steps(W, steps, a.warmup, a.copies, graph=not a.no_graph)
+    step_bytes = W.csa.step_bytes() + W.hca_bytes()
+    out[wl.name] = {"queries_per_s": round(W.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
+                    "raw_lengths": [int(x) for x in W.lens],
+                    "step_hbm_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    lens = W.lens
+    del W
+    torch.cuda.empty_cache()
+    # HCA cache build (ratio 128 over every raw row)
+    x, cu, st = hca_build_input(lens, wl.seed * 10 + 11)
+    from workloads import gen
+    gw, gb = gen.gate_params(gen.rng(wl.seed + 3), wl.hca_ratio)
+    gw, gb = torch.from_numpy(gw).cuda(), torch.from_numpy(gb).cuda()
+    hpages = [int(l) // wl.hca_ratio // 64 + 1 for l in lens]
+    pool = csa.alloc_kv_pool(sum(hpages), 64, csa.CSA_FP8_E4M3)
+    pt = np.zeros((len(lens), max(hpages)), np.int32)
+    o = 0
+    for b, k in enumerate(hpages):
+        pt[b, :k] = np.arange(o, o + k)
+        o += k
+    ptd = torch.from_numpy(pt).cuda()
+    args = (x, cu, st, int(max(lens)), wl.hca_ratio, gw, gb, ptd, pool)
+    csa.c4_compress(*args)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        csa.c4_compress(*args)
+    e1.record()
+    torch.cuda.synchronize()
+    bms = e0.elapsed_time(e1) / 3
+    nbytes = x.numel() * 2 + int(np.sum(np.asarray(lens) // wl.hca_ratio)) * 644
+    out["hca_cache_build_r128"] = {"raw_rows": int(np.sum(lens)), "ms": round(bms, 3),
+                                   "GBs": round(nbytes / (bms / 1e3) / 1e9, 1),
+                                   "hbm_frac": round(nbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del x, pool
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(W, n_queries: int):
@@ -207,6 +286,24 @@ def main():
     from workloads.device import CsaDecode
 
     torch.cuda.set_device(0)
+    if a.profile_only:
+        from workloads.device import CsaPrefill, HcaCsaRagged
+        if a.profile_only == "decode_128k":
+            wl = specs.DECODE_128K
+            W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
+        elif a.profile_only == "decode_1m":
+            wl = specs.DECODE_1M
+            W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
+        elif a.profile_only == "prefill":
+            W = CsaPrefill(specs.PREFILL_4K)
+            a.copies = 1
+        else:
+            W = HcaCsaRagged(specs.HCA_RAGGED, copies=a.copies)
+        for i in range(a.warmup + a.steps):
+            W.step(i % a.copies)
+        torch.cuda.synchronize()
+        print(f"profiled {a.profile_only}: {a.warmup + a.steps} eager steps", flush=True)
+        return
     wl = specs.DECODE_128K
     W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
     ms, idx_ms, idx_med = time_steps(W, a.steps, a.warmup, a.copies, graph=not a.no_graph)
@@ -241,6 +338,10 @@ def main():
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W, a.cpu_queries)
         line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 3)
+    del W
+    torch.cuda.empty_cache()
+    if not a.no_secondary:
+        line["secondary"] = secondary(a)
     print(json.dumps(line), flush=True)
 
 

@@ -186,3 +186,150 @@ class CsaDecode:
                                 ws=self.topk_ws)
         csa.csa_sparse_attn(self.q_attn, self.row_seq, self.q_pos, self.phys, kv, self.raw, self.pt,
                             wl.window, wl.softmax_scale, self.out, ws=self.attn_ws)
+
+
+class CsaPrefill:
+    """Chunked prefill: `new` query tokens appended to a context of `ctx` raw
+    tokens (batch 1). One step: compress the new tokens' blocks and append
+    them to the raw pool, prepare their index-K rows, prepare every query's
+    indexer q, score with the causal rule 4j+3 <= p, select per query, attend."""
+
+    def __init__(self, wl: Workload, copies: int = 1):
+        self.wl = wl
+        new = wl.new_tokens
+        L = wl.seq_len
+        ctx = L - new
+        self.ctx, self.new, self.L = ctx, new, L
+        self.N = N = L // 4
+        g = gen.rng(wl.seed)
+        pages = L // RAW_PAGE
+        self.P = P = pages
+        pt = g.permutation(P).astype(np.int32)[None]
+        self.pt_host = pt
+        self.pt = _i32(pt)
+        fmt = _FMT[wl.index_fmt]
+        self.fmt = fmt
+        seed = wl.seed * 10
+        self.idx = csa.alloc_index_pool(P, C4_PAGE, wl.index_dim, fmt, poison=False)
+        fill_index_pool(self.idx, seed + 1, hadamard=wl.hadamard)
+        self.c4 = csa.alloc_kv_pool(P, C4_PAGE, csa.CSA_FP8_E4M3, poison=False)
+        fill_kv_pool_physical(self.c4, seed + 2)
+        self.raw = csa.alloc_kv_pool(P, RAW_PAGE, csa.CSA_FP8_E4M3, poison=True)
+        w0, b0 = torch.zeros(576, device=DEV), torch.zeros(1, device=DEV)
+        self.zero_w, self.zero_b = w0, b0
+        xt = gen.device_normal((RAW_PAGE, 576), seed + 3)  # context tail (window of the first queries)
+        csa.c4_compress(xt, _i32([0, RAW_PAGE]), _i32([ctx - RAW_PAGE]), RAW_PAGE, 1, w0, b0, self.pt,
+                        self.raw)
+        gw, gb = gen.gate_params(g, 4)
+        self.gate_w, self.gate_b = torch.from_numpy(gw).to(DEV), torch.from_numpy(gb).to(DEV)
+        self.x_new = gen.device_normal((new, 576), seed + 4)
+        self.cu_new, self.start_new = _i32([0, new]), _i32([ctx])
+        nk = new // 4
+        self.k_new = gen.device_normal((nk, wl.index_dim), seed + 5)
+        ent = np.arange(ctx // 4, ctx // 4 + nk)
+        self.k_dst = _i32(pt[0, ent // C4_PAGE] * C4_PAGE + ent % C4_PAGE)
+        self.q_idx = gen.device_normal((new, wl.index_heads, wl.index_dim), seed + 6)
+        self.w_idx = gen.device_uniform((new, wl.index_heads), seed + 7)
+        self.q_attn = gen.device_normal((new, wl.heads, 576), seed + 8)
+        self.q_codes = torch.empty((new, wl.index_heads, wl.index_dim), dtype=torch.uint8, device=DEV)
+        self.q_scale = torch.empty((new, wl.index_heads), dtype=torch.float32, device=DEV)
+        self.logits = torch.empty((new, N), dtype=torch.float32, device=DEV)
+        pos = ctx + np.arange(new)
+        self.pos_host = pos
+        self.row_len_host = np.minimum(N, (pos + 1) // 4)
+        self.row_seq = _i32(np.zeros(new))
+        self.row_len = _i32(self.row_len_host)
+        self.q_pos = _i32(pos)
+        self.phys = torch.empty((new, 512), dtype=torch.int32, device=DEV)
+        self.out = torch.empty((new, wl.heads, 512), dtype=torch.bfloat16, device=DEV)
+        n = csa.csa_workspace_size(csa.CSA_OP_CSA_ATTN, new, 512 + wl.window, wl.heads)
+        self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        n = csa.csa_workspace_size(csa.CSA_OP_TOPK, new, N, 1)
+        self.topk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        torch.cuda.synchronize()
+
+    def indexer_flops(self) -> float:
+        """Causal indexer GEMM flops: 2 * heads * dim per visible (query, entry)."""
+        return 2.0 * self.wl.index_heads * self.wl.index_dim * float(self.row_len_host.sum())
+
+    def step(self, c: int = 0, ev=None):
+        wl = self.wl
+        csa.c4_compress(self.x_new, self.cu_new, self.start_new, self.new, 4, self.gate_w,
+                        self.gate_b, self.pt, self.c4)
+        csa.c4_compress(self.x_new, self.cu_new, self.start_new, self.new, 1, self.zero_w,
+                        self.zero_b, self.pt, self.raw)
+        kd = self.idx.data.view(-1, self.idx.data.shape[-1])
+        ks = self.idx.scale.view(kd.shape[0], -1)
+        csa.csa_index_prep(self.k_new, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt, kd, ks, self.k_dst)
+        csa.csa_index_prep(self.q_idx, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt, self.q_codes,
+                           self.q_scale)
+        if ev is not None:
+            ev[0].record()
+        csa.indexer_score(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.N, self.pt,
+                          self.idx, self.logits, q_fmt=self.fmt, q_scale=self.q_scale)
+        if ev is not None:
+            ev[1].record()
+        csa.topk512_page_select(self.logits, self.row_len, self.row_seq, self.pt, self.phys,
+                                ws=self.topk_ws)
+        csa.csa_sparse_attn(self.q_attn, self.row_seq, self.q_pos, self.phys, self.c4, self.raw,
+                            self.pt, wl.window, wl.softmax_scale, self.out, ws=self.attn_ws)
+
+
+class HcaCsaRagged:
+    """One decode step of an HCA layer and a CSA layer over a ragged batch
+    (raw lengths log-uniform in [lo, hi]); the two layers share the raw
+    window pool and its page table."""
+
+    def __init__(self, wl: Workload, copies: int = 3):
+        self.wl = wl
+        n, lo, hi = wl.ragged
+        self.lens = gen.ragged_lengths(gen.rng(wl.seed), n, lo, hi)
+        self.csa = CsaDecode(wl, self.lens, copies=copies, seed_offset=1)
+        g = gen.rng(wl.seed + 2)
+        R = wl.hca_ratio
+        nh = self.lens // R
+        hpages = [max(1, (int(x) + C4_PAGE - 1) // C4_PAGE) for x in nh]
+        Ph = int(sum(hpages))
+        perm = g.permutation(Ph).astype(np.int32)
+        hpt = np.zeros((n, max(hpages)), np.int32)
+        o = 0
+        for b, k in enumerate(hpages):
+            hpt[b, :k] = perm[o:o + k]
+            o += k
+        self.hpt_host = hpt
+        self.hpt = _i32(hpt)
+        base = csa.alloc_kv_pool(Ph, C4_PAGE, csa.CSA_FP8_E4M3, poison=False)
+        fill_kv_pool_physical(base, wl.seed * 10 + 9)
+        self.hca_pools = [base] + [clone_kv_pool(base) for _ in range(copies - 1)]
+        self.q_hca = gen.device_normal((n, wl.heads, 576), wl.seed * 10 + 10)
+        self.out_hca = torch.empty((n, wl.heads, 512), dtype=torch.bfloat16, device=DEV)
+        self.max_len = int(self.lens.max())
+        k = csa.csa_workspace_size(csa.CSA_OP_HCA_ATTN, n, self.max_len // R + wl.window, wl.heads)
+        self.hca_ws = torch.empty(max(k, 1), dtype=torch.uint8, device=DEV)
+        self.B = n
+        torch.cuda.synchronize()
+
+    def hca_bytes(self) -> int:
+        """Entries streamed by the HCA layer (visible compressed + window), 644 B each."""
+        vis = self.lens // self.wl.hca_ratio
+        win = np.minimum(self.lens, self.wl.window)
+        return int((vis + win).sum()) * 644 + self.q_hca.numel() * 2 + self.out_hca.numel() * 2
+
+    def step(self, c: int = 0, ev=None):
+        wl = self.wl
+        csa.hca_dense_attn(self.q_hca, self.csa.row_seq, self.csa.q_pos, self.max_len, wl.hca_ratio,
+                           self.hca_pools[c], self.hpt, self.csa.raw, self.csa.pt, wl.window,
+                           wl.softmax_scale, self.out_hca, ws=self.hca_ws)
+        self.csa.step(c, ev)
+
+
+def hca_build_input(lens, seed: int):
+    """Raw rows of every sequence (bf16), drawn on the device in chunks, with
+    their cu_rows; for timing the R=128 cache build."""
+    total = int(np.sum(lens))
+    x = torch.empty((total, 576), dtype=torch.bfloat16, device=DEV)
+    for i, r0 in enumerate(range(0, total, 1 << 20)):
+        r1 = min(total, r0 + (1 << 20))
+        x[r0:r1] = gen.device_normal((r1 - r0, 576), seed * 1000 + i)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return x, _i32(cu), _i32(np.zeros(len(lens)))
