@@ -17,6 +17,8 @@
 // contiguous 2 KB / 1 KB read), the query sits in registers, and ReLU, the
 // head weights and the 64-head reduction run in the epilogue on the
 // accumulators.
+#include <stdlib.h>
+
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -106,39 +108,45 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
 
   // Groups of 16 entries never straddle a page (page_size % 16 == 0 and the
   // chunk starts on a multiple of 16), so a group's page is wave-uniform.
-  for (int base = c0 + wave * 16; base < c1; base += kWgEntries) {
-    v8i b[kUnroll];
-    int sb[kUnroll];
-    float ks[kUnroll];
-    int64_t slot[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int g0 = base + u * kWaves * 16;  // first entry of the group
-      const int j = g0 + col;
-      const bool valid = j < c1;
-      const int pg = s_pages[min(g0, c1 - 1) / page_size - pg0];
-      slot[u] = valid ? (int64_t)pg * page_size + j % page_size : 0;
-      // unconditional loads (slot 0 for an invalid lane), zeroed afterwards
-      const uint8_t* p = kdata + slot[u] * kRowBytes + grp * (kRowBytes / 4);
-      if (kFp4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(p);
-        b[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        sb[u] = reinterpret_cast<const uint8_t*>(kscale)[slot[u] * 4 + grp];
-        ks[u] = 1.f;
-      } else {
-        const uint4 x = *reinterpret_cast<const uint4*>(p);
-        const uint4 y = *reinterpret_cast<const uint4*>(p + 16);
-        b[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-        sb[u] = 127;
-        ks[u] = reinterpret_cast<const float*>(kscale)[slot[u]];
-      }
-      if (!valid) {
-        b[u] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        sb[u] = 127;
-      }
+  // This wave takes groups g = 0, 1, ... at entries c0 + 16*wave + 64*g and
+  // keeps the loads of the next kUnroll groups in flight while it scores the
+  // current one (a register ring: slot u holds group g with g % kUnroll == u).
+  // The loop is branch-free so the compiler can count outstanding loads
+  // exactly: groups past the chunk load entry 0 of the chunk's first page, and
+  // logits go through a buffer resource bounded to this chunk, so stores of
+  // lanes past the chunk end are dropped by the hardware.
+  const int ngroups = (c1 - c0 - 16 * wave + kWaves * 16 - 1) / (kWaves * 16);
+  const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      logits + (int64_t)t * ld + c0, (short)0, (c1 - c0) * 4, 0x00020000);
+  v8i b[kUnroll];
+  int sb[kUnroll];
+  float ks[kUnroll];
+  auto issue = [&](int g, int u) {
+    const int g0 = c0 + wave * 16 + g * kWaves * 16;  // first entry of the group
+    const bool in = g0 < c1;
+    const int j = g0 + col;
+    const int pg = s_pages[in ? g0 / page_size - pg0 : 0];
+    const int64_t slot = (j < c1) ? (int64_t)pg * page_size + j % page_size : (int64_t)s_pages[0] * page_size;
+    const uint8_t* p = kdata + slot * kRowBytes + grp * (kRowBytes / 4);
+    if (kFp4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      b[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+      sb[u] = reinterpret_cast<const uint8_t*>(kscale)[slot * 4 + grp];
+      ks[u] = 1.f;
+    } else {
+      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      const uint4 y = *reinterpret_cast<const uint4*>(p + 16);
+      b[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      sb[u] = 127;
+      ks[u] = reinterpret_cast<const float*>(kscale)[slot];
     }
+  };
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) issue(u, u);
+  for (int g0 = 0; g0 < ngroups; g0 += kUnroll) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      const int g = g0 + u;
       float v = 0.f;
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) {
@@ -151,8 +159,10 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
       }
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
-      const int j = base + u * kWaves * 16 + col;
-      if (grp == 0 && j < c1) logits[(int64_t)t * ld + j] = v * ks[u];
+      const int jl = wave * 16 + g * kWaves * 16 + col;  // entry index within the chunk
+      const int off = (grp == 0 && g < ngroups) ? jl * 4 : 0x7FFFFFFF;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * ks[u]), out_rsrc, off, 0, 0);
+      issue(g + kUnroll, u);  // refill the slot just consumed
     }
   }
 }
@@ -235,9 +245,12 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
       e = hipMemcpyAsync(q_used_scale, q_scale, scale_bytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
-  // Chunk the rows so the grid has ~1024 workgroups (4 per CU).
+  // Chunk the rows so the grid has ~512 workgroups (2 per CU), each wave a
+  // long stream; CSA_TUNE_INDEXER_WGS overrides the target (tuning only).
+  int64_t target = 512;
+  if (const char* e = getenv("CSA_TUNE_INDEXER_WGS")) target = atoll(e) > 0 ? atoll(e) : target;
   int64_t total = (int64_t)T * max_row_len;
-  int64_t chunk = total / 1024;
+  int64_t chunk = total / target;
   chunk = ((chunk + kWgEntries - 1) / kWgEntries) * kWgEntries;
   if (chunk < kWgEntries) chunk = kWgEntries;
   if (chunk > kMaxChunk) chunk = kMaxChunk;
