@@ -19,6 +19,8 @@
 // accumulators.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -121,7 +123,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   v8i b[kUnroll];
   int sb[kUnroll];
   float ks[kUnroll];
-  auto issue = [&](int g, int u) {
+  auto issue = [&](int g, int u) __attribute__((always_inline)) {
     const int g0 = c0 + wave * 16 + g * kWaves * 16;  // first entry of the group
     const bool in = g0 < c1;
     const int j = g0 + col;
@@ -147,22 +149,207 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int g = g0 + u;
+      v4f acc[4];
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        acc[hb] = kFp4 ? mfma_fp4(a[hb], b[u], v4f{0.f, 0.f, 0.f, 0.f}, sa[hb], sb[u])
+                       : mfma_fp8(a[hb], b[u], v4f{0.f, 0.f, 0.f, 0.f});
       float v = 0.f;
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        acc = kFp4 ? mfma_fp4(a[hb], b[u], acc, sa[hb], sb[u]) : mfma_fp8(a[hb], b[u], acc);
-        v = fmaf(wq[hb * 4 + 0], fmaxf(acc[0], 0.f), v);
-        v = fmaf(wq[hb * 4 + 1], fmaxf(acc[1], 0.f), v);
-        v = fmaf(wq[hb * 4 + 2], fmaxf(acc[2], 0.f), v);
-        v = fmaf(wq[hb * 4 + 3], fmaxf(acc[3], 0.f), v);
-      }
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v = fmaf(wq[hb * 4 + r], fmaxf(acc[hb][r], 0.f), v);
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
       const int jl = wave * 16 + g * kWaves * 16 + col;  // entry index within the chunk
       const int off = (grp == 0 && g < ngroups) ? jl * 4 : 0x7FFFFFFF;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * ks[u]), out_rsrc, off, 0, 0);
       issue(g + kUnroll, u);  // refill the slot just consumed
+    }
+  }
+}
+
+// Many query rows (prefill): a workgroup of 8 waves owns 8 consecutive rows
+// (one row's 64 heads per wave, in registers) and walks the index-K pages of
+// their sequence once: each 64-entry page is staged into LDS with one
+// coalesced 16-byte load per thread (double-buffered, 16-byte chunks
+// XOR-swizzled by entry so the MFMA operand reads are conflict-free) and
+// scored by all 8 waves, so index-K is read from L2 once per 8 rows instead
+// of once per row. Row ends (the causal rule) are enforced by per-row buffer
+// stores bounded to row_len. A row of another sequence than the workgroup's
+// first row reads its own pages straight from memory.
+constexpr int kRowsPerWG = 8;
+
+template <bool kFp4>
+__global__ void __launch_bounds__(kRowsPerWG * 64)
+indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
+                    const float* __restrict__ w, const int32_t* __restrict__ row_seq,
+                    const int32_t* __restrict__ row_len, int T, const int32_t* __restrict__ pt,
+                    int pt_stride, const uint8_t* __restrict__ kdata,
+                    const void* __restrict__ kscale, float* __restrict__ logits, int64_t ld) {
+  constexpr int kPage = 64;                          // entries per page (= tile)
+  constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K row
+  constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kPage * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t s_bs[2][kPage];  // fp32 scale / 4 e8m0 bytes
+  __shared__ int s_len[kRowsPerWG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the row state scalar
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int t0 = blockIdx.x * kRowsPerWG;
+  const int t = t0 + wave;
+  const bool row_ok = t < T;
+  const int seq0 = row_seq[t0];
+  const int seqw = row_ok ? row_seq[t] : seq0;
+  const bool own = seqw == seq0;
+  const int nw = row_ok ? row_len[t] : 0;
+  if (lane == 0) s_len[wave] = own ? nw : -nw - 1;  // rows of another sequence stored negated
+
+  // query operands and head weights of this wave's row
+  v8i a[4];
+  int sa[4];
+  float wq[16];
+  const int tq = row_ok ? t : t0;
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int head = hb * 16 + col;
+    const uint8_t* p = qc + ((int64_t)tq * kHeads + head) * kRowBytes + grp * (kRowBytes / 4);
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    if (kFp4) {
+      a[hb] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+      sa[hb] = reinterpret_cast<const uint8_t*>(qs)[((int64_t)tq * kHeads + head) * 4 + grp];
+    } else {
+      const uint4 y = *reinterpret_cast<const uint4*>(p + 16);
+      a[hb] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      sa[hb] = 127;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = hb * 16 + grp * 4 + r;
+      float v = w[(int64_t)tq * kHeads + h];
+      if (!kFp4) v *= reinterpret_cast<const float*>(qs)[(int64_t)tq * kHeads + h];
+      wq[hb * 4 + r] = v;
+    }
+  }
+  __syncthreads();
+  int maxown = 0, maxall = 0;  // staging covers the first sequence's rows only
+#pragma unroll
+  for (int i = 0; i < kRowsPerWG; ++i) {
+    const int v = s_len[i];
+    maxown = max(maxown, v);
+    maxall = max(maxall, v >= 0 ? v : -v - 1);
+  }
+  const int npages = (maxall + kPage - 1) / kPage;
+  const int nstage = (maxown + kPage - 1) / kPage;
+  const __amdgpu_buffer_rsrc_t out_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(logits + (int64_t)tq * ld, (short)0, nw * 4, 0x00020000);
+  const int32_t* pt0 = pt + (int64_t)seq0 * pt_stride;
+  const int32_t* ptw = pt + (int64_t)seqw * pt_stride;
+
+  // staging: thread i < kPage*kChunks moves chunk (i % kChunks) of entry i / kChunks.
+  // Every thread issues the loads (spare threads duplicate a chunk) so that
+  // the loop holds no conditional load and outstanding loads stay countable.
+  const bool stager = tid < kPage * kChunks;
+  const int stid = tid % (kPage * kChunks);
+  const int se = stid / kChunks, sc = stid % kChunks;
+  const int sw = kFp4 ? (sc ^ ((se >> 2) & 3)) : (sc ^ (se & 7));  // swizzled chunk position
+  const bool scaler = tid < kPage / 4;  // 16 threads also move the page's 256 B of scales
+  const int sce = (tid % (kPage / 4)) * 4;  // first of 4 entries whose scales this thread moves
+  // pages are loaded kDepth pages ahead into a register ring (slot p % kDepth)
+  constexpr int kDepth = 3;
+  v4i stage[kDepth], sstage[kDepth];  // native vectors (HIP's uint4 struct blocks promotion)
+  auto load_page = [&](int p, auto K) __attribute__((always_inline)) {
+    constexpr int k = decltype(K)::value;
+    // clamped, never skipped; with no page to stage, pool page 0 stands in
+    const int64_t base = nstage > 0 ? (int64_t)pt0[min(p, nstage - 1)] * kPage : 0;
+    stage[k] = *reinterpret_cast<const v4i*>(kdata + (base + se) * kRowBytes + sc * 16);
+    sstage[k] = *reinterpret_cast<const v4i*>(reinterpret_cast<const uint8_t*>(kscale) + (base + sce) * 4);
+  };
+  // issue order fixed (slot 0 oldest) so the loop head waits only for slot 0
+  load_page(0, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  load_page(1, std::integral_constant<int, 1>{});
+  __builtin_amdgcn_sched_barrier(0);
+  load_page(2, std::integral_constant<int, 2>{});
+  __builtin_amdgcn_sched_barrier(0);
+  // 64 heads x 16 entries: 4 MFMAs, ReLU, head weights, 64-head reduction,
+  // logit store (lanes of rows past their row_len are dropped by the buffer)
+  auto score_store = [&](const v8i& bb, int sb, float ks, int jrow) __attribute__((always_inline)) {
+    v4f acc[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+      acc[hb] = kFp4 ? mfma_fp4(a[hb], bb, v4f{0.f, 0.f, 0.f, 0.f}, sa[hb], sb)
+                     : mfma_fp8(a[hb], bb, v4f{0.f, 0.f, 0.f, 0.f});
+    float v = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v = fmaf(wq[hb * 4 + r], fmaxf(acc[hb][r], 0.f), v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    const int off = grp == 0 ? jrow * 4 : 0x7FFFFFFF;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * ks), out_rsrc, off, 0, 0);
+  };
+  auto page_step = [&](const int p, auto K) __attribute__((always_inline)) {
+    constexpr int k = decltype(K)::value;
+    const int buf = p & 1;
+    if (stager) *reinterpret_cast<v4i*>(&s_b[buf][se * kRowBytes + sw * 16]) = stage[k];
+    if (scaler) *reinterpret_cast<v4i*>(&s_bs[buf][sce]) = sstage[k];
+    __syncthreads();
+    load_page(p + kDepth, K);  // refill the slot just written to LDS
+    if (own && p * kPage < nw) {
+#pragma unroll
+      for (int g = 0; g < kPage / 16; ++g) {
+        const int e = g * 16 + col;
+        v8i bb;
+        int sb = 127;
+        float ks = 1.f;
+        if (kFp4) {
+          const int pos = grp ^ ((e >> 2) & 3);
+          const v4i x = *reinterpret_cast<const v4i*>(&s_b[buf][e * kRowBytes + pos * 16]);
+          bb = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+          sb = (s_bs[buf][e] >> (8 * grp)) & 0xFF;
+        } else {
+          const v4i x = *reinterpret_cast<const v4i*>(&s_b[buf][e * kRowBytes + ((2 * grp) ^ (e & 7)) * 16]);
+          const v4i y = *reinterpret_cast<const v4i*>(&s_b[buf][e * kRowBytes + ((2 * grp + 1) ^ (e & 7)) * 16]);
+          bb = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+          ks = __uint_as_float(s_bs[buf][e]);
+        }
+        score_store(bb, sb, ks, p * kPage + e);
+      }
+    }
+  };
+  static_assert(kDepth == 3, "the page loop below is unrolled by hand for three slots");
+  // steps past the last page only stage (clamped) and synchronise: no branch
+  // inside the loop keeps the load counters exact across its back edge
+  for (int p0 = 0; p0 < npages; p0 += kDepth) {
+    page_step(p0, std::integral_constant<int, 0>{});
+    page_step(p0 + 1, std::integral_constant<int, 1>{});
+    page_step(p0 + 2, std::integral_constant<int, 2>{});
+  }
+  // a row of another sequence: its own pages, read straight from memory
+  if (!own && row_ok) {
+    for (int j0 = 0; j0 < nw; j0 += 16) {
+      const int e = j0 + col;
+      const int ee = min(e, nw - 1);
+      const int64_t slot = (int64_t)ptw[ee / kPage] * kPage + ee % kPage;
+      const uint8_t* q = kdata + slot * kRowBytes + grp * (kRowBytes / 4);
+      const v4i x = *reinterpret_cast<const v4i*>(q);
+      v8i bb;
+      int sb = 127;
+      float ks = 1.f;
+      if (kFp4) {
+        bb = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+        sb = reinterpret_cast<const uint8_t*>(kscale)[slot * 4 + grp];
+      } else {
+        const v4i y = *reinterpret_cast<const v4i*>(q + 16);
+        bb = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        ks = reinterpret_cast<const float*>(kscale)[slot];
+      }
+      score_store(bb, sb, ks, e);
     }
   }
 }
@@ -254,6 +441,18 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
   chunk = ((chunk + kWgEntries - 1) / kWgEntries) * kWgEntries;
   if (chunk < kWgEntries) chunk = kWgEntries;
   if (chunk > kMaxChunk) chunk = kMaxChunk;
+  if (T >= kRowsPerWG * 32 && k.page_size == 64 && !getenv("CSA_TUNE_INDEXER_NO_ROWS")) {
+    dim3 g2((T + kRowsPerWG - 1) / kRowsPerWG);
+    if (k.fmt == CSA_MXFP4)
+      hipLaunchKernelGGL(indexer_rows_kernel<true>, g2, dim3(kRowsPerWG * 64), 0, s, qc, qs, w,
+                         row_seq, row_len, T, page_table, pt_stride, (const uint8_t*)k.data,
+                         k.scale, logits, ld);
+    else
+      hipLaunchKernelGGL(indexer_rows_kernel<false>, g2, dim3(kRowsPerWG * 64), 0, s, qc, qs, w,
+                         row_seq, row_len, T, page_table, pt_stride, (const uint8_t*)k.data,
+                         k.scale, logits, ld);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((max_row_len + chunk - 1) / chunk), T);
   if (k.fmt == CSA_MXFP4)
     hipLaunchKernelGGL(indexer_mfma_kernel<true>, grid, dim3(kWaves * 64), 0, s, qc, qs, w,

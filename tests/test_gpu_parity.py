@@ -403,3 +403,44 @@ def test_tiny_fp32_decode_end_to_end(csa, seed_offset):
     from tests.e2e_tiny import run_tiny_decode_check
     res = run_tiny_decode_check(csa, torch, seed_offset)
     assert res["topk_equal"] or "attn_rel_err" not in res
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_indexer_many_rows_causal(csa, fmt):
+    """Prefill shape: hundreds of query rows of one sequence with the causal
+    row length min(N, (p+1)/4), plus a block of rows from a second sequence
+    (read from its own pages) and a group whose first rows are empty; every
+    row within 1e-4 of its max."""
+    g = gen.rng(1200 + len(fmt))
+    L1, L2 = 21000, 9000
+    N1, N2 = L1 // 4, L2 // 4
+    pt, pool, _ = _index_case(g, fmt, 2, [N1, N2])
+    T = 300
+    pos = np.arange(L1 - T, L1)
+    row_seq = np.zeros(T, np.int32)
+    row_len = np.minimum(N1, (pos + 1) // 4).astype(np.int32)
+    row_seq[100:108] = 1
+    row_len[100:108] = N2 - np.arange(8)
+    # a group of rows whose first sequence has nothing to score: the other
+    # sequence's rows still run
+    row_len[200:204] = 0
+    row_seq[204:208] = 1
+    row_len[204:208] = N2 // 2 + np.arange(4)
+    qraw = gen.normal(g, (T, 64, 128))
+    qcodes, qsc = O.index_prep(qraw, True, fmt)
+    w = gen.uniform(g, (T, 64))
+    logits = torch.full((T, N1), float("nan"), device=DEV)
+    qfmt = csa.CSA_FP8_E4M3 if fmt == "fp8" else csa.CSA_MXFP4
+    qs = t_dev(qsc.astype(np.float32)) if fmt == "fp8" else t_dev(qsc)
+    csa.indexer_score(t_dev(qcodes), t_dev(w), t_dev(row_seq), t_dev(row_len), N1, t_dev(pt),
+                      index_pool_to_device(pool, 64, 128), logits, q_fmt=qfmt, q_scale=qs)
+    got = logits.cpu().numpy()
+    qhat = O.index_dequant(qcodes, qsc, fmt)
+    for t in list(range(0, 12)) + list(range(96, 112)) + list(range(198, 210)) + list(range(T - 12, T)):
+        n = int(row_len[t])
+        if n == 0:
+            assert np.all(np.isnan(got[t])), f"row {t} has no entries but was written"
+            continue
+        want = O.indexer_logits(qhat[t], w[t], pool.rows(O.page_slot(pt[row_seq[t]], np.arange(n), 64)))
+        np.testing.assert_allclose(got[t, :n], want, rtol=0, atol=1e-4 * np.abs(want).max())
+        assert np.all(np.isnan(got[t, n:])), f"row {t} wrote past row_len"
