@@ -47,8 +47,12 @@ def _args():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the 1M decode, prefill and HCA workloads")
-    ap.add_argument("--profile-only", choices=["decode_128k", "decode_1m", "prefill", "hca_ragged"],
-                    help="run only this workload's steps (eager, for a profiler) and print nothing else")
+    ap.add_argument("--profile-only", choices=["decode_128k", "decode_1m", "prefill", "hca_ragged", "copy"],
+                    help="run only this workload's steps (eager, for a profiler) and print nothing else; "
+                         "'copy' is a plain 1 GiB device copy that calibrates the HBM byte counters")
+    ap.add_argument("--counters-from", metavar="DIR",
+                    help="reduce rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv output of the decode_128k and "
+                         "copy runs under DIR into profiles/counters.json, then exit (no GPU)")
     return ap.parse_args()
 
 
@@ -73,6 +77,64 @@ def stored_traffic(kernel: str, src_hash: str, launches_bytes_key="bytes_per_lau
     if not e or e.get("source_hash") != src_hash:
         return None
     return e.get(launches_bytes_key)
+
+
+COPY_BYTES = 4 << 28  # bytes read (and written) by one launch of the calibration copy
+
+
+def _counter_means(csv_path, counter):
+    """Mean value of `counter` per dispatch, by kernel name, from a rocprofv3
+    counter_collection.csv."""
+    import csv
+    tot, cnt = {}, {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            k = r["Kernel_Name"]
+            tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+            cnt[k] = cnt.get(k, 0) + 1
+    return {k: (tot[k] / cnt[k], cnt[k]) for k in tot}
+
+
+def _find_csv(d, stem):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", f"{stem}*counter_collection.csv"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no {stem}*counter_collection.csv under {d}")
+    return hits[-1]
+
+
+def reduce_counters(d):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode indexer,
+    scaled by what the same counters read for a copy of COPY_BYTES, written
+    with the hash of the kernel source they were taken on."""
+    out = {}
+    cf = _counter_means(_find_csv(d, "copy_fetch"), "FETCH_SIZE")
+    cw = _counter_means(_find_csv(d, "copy_write"), "WRITE_SIZE")
+    copy_k = max(cf, key=lambda k: cf[k][0])  # the copy is the largest reader in its run
+    f_scale = COPY_BYTES / (cf[copy_k][0] * 1024)
+    w_scale = COPY_BYTES / (cw[copy_k][0] * 1024)
+    kf = _counter_means(_find_csv(d, "decode128k_fetch"), "FETCH_SIZE")
+    kw = _counter_means(_find_csv(d, "decode128k_write"), "WRITE_SIZE")
+    name = "indexer_mfma_kernel<false>"
+    hits = [k for k in kf if "indexer_mfma_kernel<false>" in k]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one {name} in the fetch run, found {hits}")
+    k = hits[0]
+    fetch = kf[k][0] * 1024 * f_scale
+    write = kw[k][0] * 1024 * w_scale
+    out[name] = {"source_hash": kernel_source_hash("indexer.hip", "csa_device.hpp"),
+                 "bytes_per_launch": round(fetch + write),
+                 "fetch_bytes": round(fetch), "write_bytes": round(write),
+                 "fetch_kib_raw": kf[k][0], "write_kib_raw": kw[k][0], "dispatches": kf[k][1],
+                 "copy_kernel": copy_k, "copy_fetch_kib": cf[copy_k][0], "copy_write_kib": cw[copy_k][0],
+                 "fetch_scale": f_scale, "write_scale": w_scale}
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def capture_graphs(W, copies):
@@ -156,7 +218,7 @@ def secondary(a):
     ms, idx_ms, _ = time_steps(W, max(5, steps // 4), 2, 1, graph=not a.no_graph)
     tf = W.indexer_flops() / (idx_ms / 1e3) / 1e12
     out[wl.name] = {"tokens_per_s": round(W.new / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
-                    "indexer_gemm": {"kernel": "indexer_mfma_kernel<false>", "kernel_ms": round(idx_ms, 4),
+                    "indexer_gemm": {"kernel": "indexer_rows_kernel<false>", "kernel_ms": round(idx_ms, 4),
                                      "flop_per_launch": W.indexer_flops(), "achieved_TFLOPs": round(tf, 1),
                                      "fp8_mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}}
     del W
@@ -279,8 +341,11 @@ def main():
     a = _args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
+    if a.counters_from:
+        reduce_counters(a.counters_from)
+        return
     import torch
     from workloads import specs
     from workloads.device import CsaDecode
@@ -294,6 +359,15 @@ def main():
         elif a.profile_only == "decode_1m":
             wl = specs.DECODE_1M
             W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
+        elif a.profile_only == "copy":
+            n = 1 << 28  # 1 GiB of float32 read and 1 GiB written per copy
+            src = torch.ones(n, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(a.warmup + a.steps):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            print(f"profiled copy: {a.warmup + a.steps} copies of {4 * n} B", flush=True)
+            return
         elif a.profile_only == "prefill":
             W = CsaPrefill(specs.PREFILL_4K)
             a.copies = 1
