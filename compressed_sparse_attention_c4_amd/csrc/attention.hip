@@ -269,21 +269,13 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
     float corr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float mt = fmaxf(sv[0][r], sv[1][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 1, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 2, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 4, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 8, 64));
+      const float mt = row16_max(fmaxf(sv[0][r], sv[1][r]));
       const float mn = fmaxf(m[r], mt);
       const bool dead = mn == -INFINITY;
       corr[r] = dead ? 1.f : __expf(m[r] - mn);
       const float p0 = dead ? 0.f : __expf(sv[0][r] - mn);
       const float p1 = dead ? 0.f : __expf(sv[1][r] - mn);
-      float ps = p0 + p1;
-      ps += __shfl_xor(ps, 1, 64);
-      ps += __shfl_xor(ps, 2, 64);
-      ps += __shfl_xor(ps, 4, 64);
-      ps += __shfl_xor(ps, 8, 64);
+      const float ps = row16_sum(p0 + p1);
       l[r] = l[r] * corr[r] + ps;
       m[r] = mn;
       // P' = p * (value dequant scale), bf16, stored row-major [head][entry]

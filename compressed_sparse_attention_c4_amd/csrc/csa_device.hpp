@@ -87,22 +87,112 @@ __device__ __forceinline__ int mx_block_exponent(float amax) {
 }
 
 // ---------------------------------------------------------------- wave ops
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+// Cross-lane moves stay on the vector ALU: DPP within 16-lane rows and the
+// permlane swaps across rows. (The generic shuffle goes through the LDS
+// crossbar, ds_bpermute, and the wave waits for its round trip.) Layouts:
+// permlane16_swap(v, v) gives {row 2k's value, row 2k+1's value} to both rows
+// 2k and 2k+1 (a row is 16 lanes); permlane32_swap(v, v) gives {the value of
+// lane l % 32, the value of lane l % 32 + 32}.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowShl = 0x100;     // + n: lane l reads l + n within its row
+constexpr int kDppRowShr = 0x110;     // + n: lane l reads l - n within its row
+constexpr int kDppRowMirror = 0x140;  // lane l reads 15 - l within its row
+constexpr int kDppRowHalfMirror = 0x141;  // lane l reads 7 - l within its half row
+
+// The swaps are written as instructions: the compiler's generic combine of
+// the swap intrinsic treats its two results as the same value and folds one
+// into the other. The nops cover the VALU-write-to-permlane hazard.
+__device__ __forceinline__ float2 permlane16_pair(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return make_float2(a, b);
 }
-// Max over groups of `width` consecutive lanes (width a power of two <= 64).
+__device__ __forceinline__ float2 permlane32_pair(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return make_float2(a, b);
+}
+
+// The value held by lane (l ^ kM), kM in {1, 2, 4, 8} (within a row).
+template <int kM>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (kM == 1) {
+    return dpp_mov<kDppQuadXor1>(v);
+  } else if constexpr (kM == 2) {
+    return dpp_mov<kDppQuadXor2>(v);
+  } else {
+    static_assert(kM == 4 || kM == 8, "lane_xor: 1, 2, 4 or 8");
+    const float from_below = dpp_mov<kDppRowShr + kM>(v);
+    const float from_above = dpp_mov<kDppRowShl + kM>(v);
+    return (lane & kM) ? from_below : from_above;
+  }
+}
+
+// Max / sum over the 16 lanes of each row, in every lane of the row (every
+// lane gets the bitwise same value).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
+  return fmaxf(v, dpp_mov<kDppRowMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<kDppQuadXor1>(v);
+  v += dpp_mov<kDppQuadXor2>(v);
+  v += dpp_mov<kDppRowHalfMirror>(v);
+  return v + dpp_mov<kDppRowMirror>(v);
+}
+// Sum / max over the four lanes l % 16 + {0, 16, 32, 48}, in each of them.
+__device__ __forceinline__ float cross_row_sum(float v) {
+  const float2 a = permlane16_pair(v);
+  const float2 b = permlane32_pair(a.x + a.y);
+  return b.x + b.y;
+}
+__device__ __forceinline__ float cross_row_max(float v) {
+  const float2 a = permlane16_pair(v);
+  const float2 b = permlane32_pair(fmaxf(a.x, a.y));
+  return fmaxf(b.x, b.y);
+}
+__device__ __forceinline__ float wave_sum(float v) { return cross_row_sum(row16_sum(v)); }
+__device__ __forceinline__ float wave_max(float v) { return cross_row_max(row16_max(v)); }
+// Max over groups of `width` consecutive lanes (16, 32 or 64).
 template <int width>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  static_assert(width == 16 || width == 32 || width == 64, "group_max: 16, 32 or 64 lanes");
+  v = row16_max(v);
+  if constexpr (width == 32) {
+    const float2 a = permlane16_pair(v);
+    v = fmaxf(a.x, a.y);
+  } else if constexpr (width == 64) {
+    v = cross_row_max(v);
+  }
   return v;
+}
+
+// One butterfly span m across lanes: of the pair (a in the lane with bit m
+// clear, b in its partner), the lower lane keeps a + b and the upper a - b.
+template <int kM>
+__device__ __forceinline__ void fwht_stage(float& x0, float& x1, int lane) {
+  const bool upper = (lane & kM) != 0;
+  if constexpr (kM <= 8) {
+    const float p0 = lane_xor<kM>(x0);
+    const float p1 = lane_xor<kM>(x1);
+    x0 = upper ? (p0 - x0) : (x0 + p0);
+    x1 = upper ? (p1 - x1) : (x1 + p1);
+  } else {
+    // the swap hands both lanes of a pair (a, b) = (lower's, upper's) value
+    const float2 a = kM == 16 ? permlane16_pair(x0) : permlane32_pair(x0);
+    const float2 b = kM == 16 ? permlane16_pair(x1) : permlane32_pair(x1);
+    x0 = upper ? (a.x - a.y) : (a.x + a.y);
+    x1 = upper ? (b.x - b.y) : (b.x + b.y);
+  }
 }
 
 // Fast Walsh-Hadamard transform of a 128-vector held two elements per lane
@@ -114,14 +204,12 @@ __device__ __forceinline__ void fwht128_wave(float& x0, float& x1) {
   float a = x0, b = x1;
   x0 = a + b;
   x1 = a - b;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    float p0 = __shfl_xor(x0, m, kWave);
-    float p1 = __shfl_xor(x1, m, kWave);
-    bool upper = (lane & m) != 0;
-    x0 = upper ? (p0 - x0) : (x0 + p0);
-    x1 = upper ? (p1 - x1) : (x1 + p1);
-  }
+  fwht_stage<1>(x0, x1, lane);
+  fwht_stage<2>(x0, x1, lane);
+  fwht_stage<4>(x0, x1, lane);
+  fwht_stage<8>(x0, x1, lane);
+  fwht_stage<16>(x0, x1, lane);
+  fwht_stage<32>(x0, x1, lane);
   const float s = 0.0883883476483184405f;  // 1/sqrt(128) rounded to fp32
   x0 *= s;
   x1 *= s;
@@ -134,14 +222,11 @@ __device__ __forceinline__ void fwht64_halfwave(float& x0, float& x1) {
   float a = x0, b = x1;
   x0 = a + b;
   x1 = a - b;
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) {
-    float p0 = __shfl_xor(x0, m, kWave);
-    float p1 = __shfl_xor(x1, m, kWave);
-    bool upper = (lane & m) != 0;
-    x0 = upper ? (p0 - x0) : (x0 + p0);
-    x1 = upper ? (p1 - x1) : (x1 + p1);
-  }
+  fwht_stage<1>(x0, x1, lane);
+  fwht_stage<2>(x0, x1, lane);
+  fwht_stage<4>(x0, x1, lane);
+  fwht_stage<8>(x0, x1, lane);
+  fwht_stage<16>(x0, x1, lane);
   const float s = 0.125f;  // 1/sqrt(64)
   x0 *= s;
   x1 *= s;

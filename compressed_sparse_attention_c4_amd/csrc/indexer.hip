@@ -159,8 +159,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
       for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) v = fmaf(wq[hb * 4 + r], fmaxf(acc[hb][r], 0.f), v);
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
+      v = cross_row_sum(v);
       const int jl = wave * 16 + g * kWaves * 16 + col;  // entry index within the chunk
       const int off = (grp == 0 && g < ngroups) ? jl * 4 : 0x7FFFFFFF;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * ks[u]), out_rsrc, off, 0, 0);
@@ -288,8 +287,7 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
     for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) v = fmaf(wq[hb * 4 + r], fmaxf(acc[hb][r], 0.f), v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+    v = cross_row_sum(v);
     const int off = grp == 0 ? jrow * 4 : 0x7FFFFFFF;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * ks), out_rsrc, off, 0, 0);
   };
