@@ -30,8 +30,10 @@ index_prep_kernel(const void* __restrict__ v, int64_t rows, uint32_t flags, int 
     const bool valid = r < rows;
     float x0 = 0.f, x1 = 0.f;
     if (valid) load_pair<kF32In>(v, r * D + e0, x0, x1);
-    const int64_t dst = valid ? (dst_rows ? (int64_t)dst_rows[r] : r) : 0;
-    prep_and_store<D>(x0, x1, valid, flags & CSA_PREP_HADAMARD, out_fmt, out, out_scale, dst);
+    const int64_t d = valid ? (dst_rows ? (int64_t)dst_rows[r] : r) : 0;
+    const bool store = valid && d >= 0;  // a negative destination skips the row
+    prep_and_store<D>(x0, x1, store, flags & CSA_PREP_HADAMARD, out_fmt, out, out_scale,
+                      store ? d : 0);
   }
 }
 

@@ -150,7 +150,9 @@ csa_status c4_compress(const void* x, csa_fmt x_fmt, const int32_t* cu_rows,
  *                         code = e2m1_rne(v / 2^X) saturated at +-6, byte = X + 127.
  *           CSA_F32:      out float [*][dim] (out_scale unused).
  *   dst_rows optional int32[rows]: row i is written to output row dst_rows[i]
- *           (e.g. a pool slot); NULL writes row i to output row i.
+ *           (e.g. a pool slot), and not written at all when dst_rows[i] < 0 (a
+ *           decode step where a sequence completes no block); NULL writes row i
+ *           to output row i.
  */
 csa_status csa_index_prep(const void* v, csa_fmt v_fmt, int64_t rows, int32_t dim,
                           uint32_t flags, csa_fmt out_fmt, void* out, void* out_scale,

@@ -1,0 +1,164 @@
+"""Full-size parity: the benchmark workloads at their real sizes, run through
+the library exactly as bench.py runs them (same entry points, same shapes and
+so the same launch configurations; the 128K decode also as a HIP-graph
+replay), checked on sampled sequences / query rows against the oracle, which
+rebuilds those rows from the same seeded draws (tests/fullsize.py).
+
+Bars (as in the small parity tests): logits within 1e-4 of the row's largest
+|logit|; the top-512 equal to the oracle's outside the band of entries whose
+logit is within that tolerance of the 512-th largest; attention (bf16 out)
+within 2e-2 absolute where the selections are equal; the step's freshly
+compressed KV entry / index-K row checked directly.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+from tests import fullsize as F
+from tests.gpu_helpers import fp8_codes_match
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_TOL = 1e-4
+ATTN_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def csa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_sparse_attention_c4_amd as m
+    return m
+
+
+def _check_csa_row(st: F.SeqState, g_logits, g_phys, pt_row, g_out, label):
+    o_logits, o_sel, o_out = st.csa()
+    n = st.row_len
+    tol = LOGIT_TOL * np.abs(o_logits).max()
+    err = np.abs(g_logits[:n] - o_logits).max()
+    assert err <= tol, f"{label}: logits differ by {err} (tol {tol})"
+    g_log = F.logical_of_phys(g_phys, pt_row)
+    ok, equal, nband = F.topk_agrees(o_logits, g_log, 512, tol)
+    assert ok, f"{label}: top-512 differs outside the near-tie band ({nband} in band)"
+    if equal:
+        aerr = np.abs(g_out - o_out).max()
+        assert aerr <= ATTN_TOL, f"{label}: attention differs by {aerr}"
+    return equal
+
+
+def _check_step_writes(W, b, label):
+    """The step's compressed entry N-1 and its index-K row, from the pools."""
+    L, N = int(W.lens[b]), int(W.N[b])
+    slot = int(O.page_slot(W.pt_host[b], N - 1, 64))
+    x_new = F.host(W.x_new).reshape(W.B, 4, 576)[b]
+    c = O.compress_blocks(x_new, L - 4, 4, F.host(W.gate_w), F.host(W.gate_b))
+    oc, osc, orope = O.quant_kv_entries(c, "fp8")
+    kv = W.c4_pools[0]
+    lat = kv.latent.view(-1, 512)[slot].cpu().numpy()[None]
+    sc = kv.scale.view(-1)[slot].cpu().numpy()
+    np.testing.assert_allclose(sc, osc[0], rtol=3e-6, err_msg=label)
+    ok, _ = fp8_codes_match(lat, oc, c[:, :512].astype(np.float32) / osc[:, None], rel=2e-5)
+    assert ok, f"{label}: compressed latent differs"
+    rope = kv.rope.view(-1, 64)[slot].float().cpu().numpy()
+    orr = O.bf16_decode(orope[0])
+    assert np.all(np.abs(rope - orr) <= 2.0 ** -7 * np.abs(orr) + 1e-5), f"{label}: rope differs"
+    codes, scale = O.index_prep(F.host(W.k_new)[b:b + 1], W.wl.hadamard, W.wl.index_fmt)
+    idx = W.index_pools[0]
+    g_codes = idx.data.view(-1, idx.data.shape[-1])[slot].cpu().numpy()
+    g_scale = idx.scale.view(idx.data.view(-1, idx.data.shape[-1]).shape[0], -1)[slot].cpu().numpy()
+    assert np.array_equal(g_codes, codes[0]), f"{label}: index-K codes differ"
+    assert np.array_equal(g_scale.reshape(-1), np.asarray(scale[0]).reshape(-1)), f"{label}: index-K scale differs"
+
+
+def test_decode_128k_sampled(csa):
+    """32 x 128K decode (fp8 index-K, 64 + 64 heads): eager step, then the same
+    step replayed from a HIP graph must reproduce it bit for bit."""
+    from workloads import specs
+    from workloads.device import CsaDecode
+    wl = specs.DECODE_128K
+    W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=1, pool_pages=wl.pool_pages)
+    W.step(0)
+    torch.cuda.synchronize()
+    logits, phys, out = W.logits.clone(), W.phys.clone(), W.out.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        W.step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        W.step(0)
+    for _ in range(2):
+        W.logits.fill_(float("nan"))
+        W.out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(W.logits, logits) and torch.equal(W.phys, phys)
+        assert torch.equal(W.out.view(torch.int16), out.view(torch.int16))
+    gl, gp, go = logits.cpu().numpy(), phys.cpu().numpy(), out.float().cpu().numpy()
+    compared = 0
+    for b in (0, 13, 31):
+        _check_step_writes(W, b, f"seq {b}")
+        st = F.decode_seq(W, b)
+        compared += _check_csa_row(st, gl[b], gp[b], W.pt_host[b], go[b], f"seq {b}")
+    assert compared >= 1, "no sampled sequence had an unambiguous top-512"
+
+
+def test_decode_1m_sampled(csa):
+    """4 x 1M decode (MXFP4 index-K, 128 attention heads)."""
+    from workloads import specs
+    from workloads.device import CsaDecode
+    wl = specs.DECODE_1M
+    W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=1, pool_pages=wl.pool_pages)
+    W.step(0)
+    torch.cuda.synchronize()
+    gl, gp, go = W.logits.cpu().numpy(), W.phys.cpu().numpy(), W.out.float().cpu().numpy()
+    compared = 0
+    for b in (1, 3):
+        st = F.decode_seq(W, b)
+        compared += _check_csa_row(st, gl[b], gp[b], W.pt_host[b], go[b], f"seq {b}")
+    assert compared >= 1
+
+
+def test_prefill_4096_on_128k_sampled(csa):
+    """Chunked prefill: 4096 new tokens on a 131072-token context, causal
+    indexer rows; sampled rows at the start, middle and end of the chunk."""
+    from workloads import specs
+    from workloads.device import CsaPrefill
+    W = CsaPrefill(specs.PREFILL_4K)
+    W.step(0)
+    torch.cuda.synchronize()
+    compared = 0
+    for t in (0, 1709, 4095):
+        st = F.prefill_row(W, t)
+        gl = W.logits[t].cpu().numpy()
+        gp, go = W.phys[t].cpu().numpy(), W.out[t].float().cpu().numpy()
+        compared += _check_csa_row(st, gl, gp, W.pt_host[0], go, f"row {t}")
+        n = st.row_len
+        assert np.all(np.isfinite(gl[:n]))
+    assert compared >= 1
+
+
+def test_hca_csa_ragged_sampled(csa):
+    """16 ragged sequences (8K..1M tokens): HCA dense attention of every
+    sampled sequence, and the CSA layer of the same step."""
+    from workloads import specs
+    from workloads.device import HcaCsaRagged
+    Wh = HcaCsaRagged(specs.HCA_RAGGED, copies=1)
+    Wh.step(0)
+    torch.cuda.synchronize()
+    ho = Wh.out_hca.float().cpu().numpy()
+    W = Wh.csa
+    gl, gp, go = W.logits.cpu().numpy(), W.phys.cpu().numpy(), W.out.float().cpu().numpy()
+    order = np.argsort(Wh.lens)
+    compared = 0
+    for b in (int(order[0]), int(order[7]), int(order[-1])):
+        want = F.hca_oracle(Wh, b)
+        err = np.abs(ho[b] - want).max()
+        assert err <= ATTN_TOL, f"HCA seq {b} (L={Wh.lens[b]}): differs by {err}"
+        st = F.decode_seq(W, b)
+        compared += _check_csa_row(st, gl[b], gp[b], W.pt_host[b], go[b], f"CSA seq {b}")
+    assert compared >= 1

@@ -63,15 +63,18 @@ def test_index_prep_mxfp4_hadamard(csa, rows):
 
 
 def test_index_prep_f32_dst_rows(csa):
+    """Rows go to dst_rows[i]; a negative destination skips the row."""
     g = gen.rng(300)
     v = gen.normal(g, (50, 64))
     dst = np.random.default_rng(1).permutation(80)[:50].astype(np.int32)
+    dst[[3, 17, 49]] = -1
     out = torch.full((80, 64), float("nan"), dtype=torch.float32, device=DEV)
     csa.csa_index_prep(t_dev(v), 64, csa.CSA_PREP_HADAMARD, csa.CSA_F32, out, None, t_dev(dst))
     want = O.hadamard_rotate_f32(v)
     got = out.cpu().numpy()
-    assert np.array_equal(got[dst], want)
-    untouched = np.setdiff1d(np.arange(80), dst)
+    keep = dst >= 0
+    assert np.array_equal(got[dst[keep]], want[keep])
+    untouched = np.setdiff1d(np.arange(80), dst[keep])
     assert np.all(np.isnan(got[untouched]))
 
 

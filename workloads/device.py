@@ -88,6 +88,7 @@ class CsaDecode:
         self.P = P
         fmt = _FMT[wl.index_fmt]
         seed = wl.seed * 10 + seed_offset
+        self.seed = seed  # base of every draw below (fills use seed*1000 + chunk)
         base_idx = csa.alloc_index_pool(P, C4_PAGE, wl.index_dim, fmt, poison=False)
         fill_index_pool(base_idx, seed + 1, hadamard=wl.hadamard)
         base_kv = csa.alloc_kv_pool(P, C4_PAGE, csa.CSA_FP8_E4M3, poison=False)
@@ -116,8 +117,11 @@ class CsaDecode:
         self.cu_tok = _i32(np.arange(B + 1))
         self.start_tok = _i32(self.lens - 1)
         self.k_new = gen.device_normal((B, wl.index_dim), seed + 5)
+        # the current token completes block N-1 only when L % 4 == 0; the
+        # compressor skips the partial block and the index-K row is not stored
         last = self.N - 1
-        self.k_dst = _i32(pt[np.arange(B), last // C4_PAGE] * C4_PAGE + last % C4_PAGE)
+        dst = pt[np.arange(B), last // C4_PAGE] * C4_PAGE + last % C4_PAGE
+        self.k_dst = _i32(np.where(self.lens % 4 == 0, dst, -1))
         self.q_idx = gen.device_normal((B, wl.index_heads, wl.index_dim), seed + 6)
         self.w_idx = gen.device_uniform((B, wl.index_heads), seed + 7)
         self.q_attn = gen.device_normal((B, self.H, 576), seed + 8)
@@ -210,6 +214,7 @@ class CsaPrefill:
         fmt = _FMT[wl.index_fmt]
         self.fmt = fmt
         seed = wl.seed * 10
+        self.seed = seed
         self.idx = csa.alloc_index_pool(P, C4_PAGE, wl.index_dim, fmt, poison=False)
         fill_index_pool(self.idx, seed + 1, hadamard=wl.hadamard)
         self.c4 = csa.alloc_kv_pool(P, C4_PAGE, csa.CSA_FP8_E4M3, poison=False)
@@ -298,8 +303,10 @@ class HcaCsaRagged:
             o += k
         self.hpt_host = hpt
         self.hpt = _i32(hpt)
+        self.Ph = Ph
+        self.hca_seed = wl.seed * 10 + 9
         base = csa.alloc_kv_pool(Ph, C4_PAGE, csa.CSA_FP8_E4M3, poison=False)
-        fill_kv_pool_physical(base, wl.seed * 10 + 9)
+        fill_kv_pool_physical(base, self.hca_seed)
         self.hca_pools = [base] + [clone_kv_pool(base) for _ in range(copies - 1)]
         self.q_hca = gen.device_normal((n, wl.heads, 576), wl.seed * 10 + 10)
         self.out_hca = torch.empty((n, wl.heads, 512), dtype=torch.bfloat16, device=DEV)
