@@ -34,6 +34,7 @@ constexpr int kPStride = kTile + 8;   // bf16 elements per row of P
 constexpr int kMaxSplit = 1024;       // entries one workgroup handles, at most
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v4f mfma_bf16(const v4i& a, const v4i& b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -365,6 +366,308 @@ attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two-phase path for few queries (decode). With T small, the split kernel
+// needs many splits per query and each writes a 64 x 512 fp32 partial, more
+// bytes than the KV it reads. Here phase A computes, for each 64-entry chunk
+// of a query's entry list, all heads' scores, the chunk's softmax max m_c and
+// sum l_c, and the weights P' = exp(s - m_c) * (value FP8 scale) in bf16;
+// phase B merges the chunks' (m_c, l_c) into the exact normaliser and sums
+// f_c * (P' V) for one 64-dim slice of the value, f_c = exp(m_c - M) / L. The
+// only intermediate is P' (2 bytes per head and entry), and no merge follows.
+constexpr int kChunk = 64;                // entries per phase-A workgroup
+constexpr int kSlice = 64;                // value dims per phase-B workgroup
+constexpr int kRound = 256;               // entries per phase-B staging round
+constexpr int kRoundStride = kRound + 8;  // bf16 per V^T row in LDS
+constexpr int kTwoPhaseMaxE = 2048;       // entry lists up to this length
+constexpr int kMaxChunks = kTwoPhaseMaxE / kChunk;
+
+// Entry -> pool choice as 64-bit masks (bitwise selects keep gathers
+// straight-line; masked entries read a stand-in and are zeroed).
+struct Pick {
+  int64_t slot;
+  uint64_t mc, mr, md;
+};
+__device__ __forceinline__ Pick pick_of(int es) {
+  Pick k;
+  k.slot = es >= 0 ? (es >> 1) : 0;
+  k.md = es < 0 ? ~0ull : 0ull;
+  k.mr = (es >= 0 && (es & 1)) ? ~0ull : 0ull;
+  k.mc = ~(k.md | k.mr);
+  return k;
+}
+__device__ __forceinline__ uint64_t pick_base(const Pick& k, const void* c, const void* r,
+                                              const void* d) {
+  return ((uint64_t)c & k.mc) | ((uint64_t)r & k.mr) | ((uint64_t)d & k.md);
+}
+
+__global__ void __launch_bounds__(256)
+attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
+                   const int32_t* __restrict__ q_pos, bool hca, const int32_t* __restrict__ phys_idx,
+                   int k_sel, int ratio, const uint8_t* __restrict__ c_lat,
+                   const float* __restrict__ c_sc, const uint16_t* __restrict__ c_rope, int c_ps,
+                   const int32_t* __restrict__ comp_pt, int comp_pt_stride,
+                   const uint8_t* __restrict__ r_lat, const float* __restrict__ r_sc,
+                   const uint16_t* __restrict__ r_rope, int r_ps,
+                   const int32_t* __restrict__ raw_pt, int raw_pt_stride, int window, float scale,
+                   uint16_t* __restrict__ pw, float2* __restrict__ stats, int e_pad) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kChunk * kKStride];
+  __shared__ int32_t s_es[kChunk];
+  __shared__ float s_sc[kChunk];
+  const int chunk = blockIdx.x, t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int seq = q_seq[t], p = q_pos[t];
+  const EntryList L = entry_list(p, k_sel, hca, ratio, window);
+  const int total = min(L.n1 + L.n2, e_pad);  // a list longer than the stated bound is cut
+  const int e0 = chunk * kChunk;
+  if (e0 >= total) return;  // past this query's list: phase B reads no such chunk
+  const int hbase = blockIdx.z * 64 + wave * 16;
+  v4i qa[18];
+  {
+    const uint16_t* qrow = q + ((int64_t)t * H + hbase + col) * kKvDim + grp * 8;
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qa[s] = *reinterpret_cast<const v4i*>(qrow + s * 32);
+  }
+  if (tid < kChunk) {
+    const int i = e0 + tid;
+    int pool = 0;
+    const int64_t slot = i < total ? entry_slot(i, L, t, seq, hca, phys_idx, k_sel, comp_pt,
+                                                comp_pt_stride, c_ps, raw_pt, raw_pt_stride,
+                                                r_ps, pool)
+                                   : -1;
+    s_es[tid] = slot >= 0 ? (int32_t)(slot * 2 + pool) : -1;
+  }
+  __syncthreads();
+  // gathers: 64 entries x 32 latent chunks of 16 B (8 per thread, one entry
+  // row per 32 lanes), 64 x 8 RoPE chunks (2 per thread), 64 scales
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + (int64_t)t * H * kKvDim);
+  v4i lat[8], rp[2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
+    const Pick pk = pick_of(s_es[e]);
+    const v4i x = *reinterpret_cast<const v4i*>(pick_base(pk, c_lat, r_lat, dummy) +
+                                                pk.slot * kLatent + 16 * c);
+    lat[k] = pk.md ? v4i{0, 0, 0, 0} : x;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = tid + k * 256, e = idx >> 3, c = idx & 7;
+    const Pick pk = pick_of(s_es[e]);
+    rp[k] = *reinterpret_cast<const v4i*>(pick_base(pk, c_rope, r_rope, dummy) +
+                                          pk.slot * (kRope * 2) + 16 * c);
+  }
+  float scv;
+  {
+    const Pick pk = pick_of(s_es[tid & (kChunk - 1)]);
+    const float x = *reinterpret_cast<const float*>(pick_base(pk, c_sc, r_sc, dummy) + pk.slot * 4);
+    scv = pk.md ? 0.f : x;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
+    uint32_t b[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      b[2 * w] = fp8x2_to_bf16x2<false>((uint32_t)lat[k][w]);
+      b[2 * w + 1] = fp8x2_to_bf16x2<true>((uint32_t)lat[k][w]);
+    }
+    uint16_t* dst = &s_k[e * kKStride + 16 * c];
+    *reinterpret_cast<v4i*>(dst) = v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    *reinterpret_cast<v4i*>(dst + 8) = v4i{(int)b[4], (int)b[5], (int)b[6], (int)b[7]};
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = tid + k * 256, e = idx >> 3, c = idx & 7;
+    *reinterpret_cast<v4i*>(&s_k[e * kKStride + kLatent + 8 * c]) = rp[k];
+  }
+  if (tid < kChunk) s_sc[tid] = scv;
+  __syncthreads();
+
+  // scores of 16 heads x 64 entries (four 16-column blocks)
+  float sv[4][4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int e = cb * 16 + col;
+    v4f acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      acc_l = mfma_bf16(qa[s], *reinterpret_cast<const v4i*>(&s_k[e * kKStride + s * 32 + grp * 8]),
+                        acc_l);
+#pragma unroll
+    for (int s = 16; s < 18; ++s)
+      acc_r = mfma_bf16(qa[s], *reinterpret_cast<const v4i*>(&s_k[e * kKStride + s * 32 + grp * 8]),
+                        acc_r);
+    const bool valid = s_es[e] >= 0;
+    const float sc = s_sc[e];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[cb][r] = valid ? scale * fmaf(sc, acc_l[r], acc_r[r]) : -INFINITY;
+  }
+  const int n_chunks = e_pad / kChunk;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = hbase + grp * 4 + r;
+    const float m = row16_max(fmaxf(fmaxf(sv[0][r], sv[1][r]), fmaxf(sv[2][r], sv[3][r])));
+    const bool dead = m == -INFINITY;
+    float ps = 0.f;
+    uint16_t* prow = pw + ((int64_t)t * H + h) * e_pad + e0;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const float pr = dead ? 0.f : __expf(sv[cb][r] - m);
+      ps += pr;
+      prow[cb * 16 + col] = f32_to_bf16(pr * s_sc[cb * 16 + col]);
+    }
+    const float l = row16_sum(ps);
+    if (col == 0) stats[((int64_t)t * H + h) * n_chunks + chunk] = make_float2(m, l);
+  }
+}
+
+template <bool kOutF32>
+__global__ void __launch_bounds__(256)
+attn_pv_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
+               const int32_t* __restrict__ q_pos, bool hca, const int32_t* __restrict__ phys_idx,
+               int k_sel, int ratio, const uint8_t* __restrict__ c_lat, int c_ps,
+               const int32_t* __restrict__ comp_pt, int comp_pt_stride,
+               const uint8_t* __restrict__ r_lat, int r_ps, const int32_t* __restrict__ raw_pt,
+               int raw_pt_stride, int window, const uint16_t* __restrict__ pw,
+               const float2* __restrict__ stats, int e_pad, void* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kSlice * kRoundStride];
+  __shared__ int32_t s_es[kTwoPhaseMaxE];
+  __shared__ float s_f[64][kMaxChunks];
+  const int slice = blockIdx.x, t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int seq = q_seq[t], p = q_pos[t];
+  const EntryList L = entry_list(p, k_sel, hca, ratio, window);
+  const int total = min(L.n1 + L.n2, e_pad);  // as in phase A
+  const int nch = (total + kChunk - 1) / kChunk;
+  const int n_chunks = e_pad / kChunk;
+  const int hb0 = blockIdx.z * 64;
+  for (int i = tid; i < total; i += 256) {
+    int pool = 0;
+    const int64_t slot = entry_slot(i, L, t, seq, hca, phys_idx, k_sel, comp_pt, comp_pt_stride,
+                                    c_ps, raw_pt, raw_pt_stride, r_ps, pool);
+    s_es[i] = slot >= 0 ? (int32_t)(slot * 2 + pool) : -1;
+  }
+  if (tid < 64) {
+    // exact normaliser of head hb0 + tid from its chunks' (m_c, l_c)
+    const float2* st = stats + ((int64_t)t * H + hb0 + tid) * n_chunks;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, st[c].x);
+    float Ls = 0.f;
+    for (int c = 0; c < nch; ++c)
+      if (st[c].x != -INFINITY) Ls = fmaf(st[c].y, __expf(st[c].x - M), Ls);
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    for (int c = 0; c < nch; ++c)
+      s_f[tid][c] = st[c].x == -INFINITY ? 0.f : __expf(st[c].x - M) * inv;
+  }
+  __syncthreads();
+  if (total == 0) {  // nothing visible: zero output
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t ob = ((int64_t)t * H + hb0 + wave * 16 + grp * 4 + r) * kLatent + slice * kSlice + col;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        if (kOutF32) reinterpret_cast<float*>(out)[ob + db * 16] = 0.f;
+        else reinterpret_cast<uint16_t*>(out)[ob + db * 16] = 0;
+      }
+    }
+    return;
+  }
+
+  // staging task: 8 entries x 8 value dims (lanes 8k..8k+7 read 64 contiguous
+  // bytes of one entry), written transposed to V^T [dim][entry]
+  const int dg = tid & 7, eg = tid >> 3;
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + (int64_t)t * H * kKvDim);
+  const int hl = wave * 16 + col;  // A-operand row (head within the block)
+  const uint16_t* prow = pw + ((int64_t)t * H + hb0 + hl) * e_pad + grp * 8;
+  v2i codes[8];
+  v4i pa_next[8];
+  auto issue = [&](int r0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = r0 + 8 * eg + j;
+      const int es0 = s_es[min(e, total - 1)];
+      const Pick pk = pick_of(e < total ? es0 : -1);
+      const v2i x = *reinterpret_cast<const v2i*>(pick_base(pk, c_lat, r_lat, dummy) +
+                                                  pk.slot * kLatent + slice * kSlice + 8 * dg);
+      codes[j] = pk.md ? v2i{0, 0} : x;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      pa_next[ks] = *reinterpret_cast<const v4i*>(prow + min(r0 + ks * 32, e_pad - 32));
+  };
+  v4f o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  issue(0);
+  int buf = 0;
+  for (int r0 = 0; r0 < total; r0 += kRound, buf ^= 1) {
+    // codes[j] holds dims 8*dg .. +7 of entry 8*eg + j as two words of four
+    uint32_t kb[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      kb[j][0] = fp8x2_to_bf16x2<false>((uint32_t)codes[j][0]);
+      kb[j][1] = fp8x2_to_bf16x2<true>((uint32_t)codes[j][0]);
+      kb[j][2] = fp8x2_to_bf16x2<false>((uint32_t)codes[j][1]);
+      kb[j][3] = fp8x2_to_bf16x2<true>((uint32_t)codes[j][1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // dim 8*dg + i of the slice, entries 8*eg .. +7
+      const int w = i >> 1;
+      uint32_t d[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t a = kb[2 * jj][w], b = kb[2 * jj + 1][w];
+        d[jj] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+      }
+      *reinterpret_cast<v4i*>(&s_vt[buf][(8 * dg + i) * kRoundStride + 8 * eg]) =
+          v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+    }
+    v4i pa[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) pa[ks] = pa_next[ks];
+    __syncthreads();
+    if (r0 + kRound < total) issue(r0 + kRound);
+#pragma unroll
+    for (int cc = 0; cc < kRound / kChunk; ++cc) {
+      const int c = r0 / kChunk + cc;
+      if (c >= nch) break;  // uniform: chunks past the list were never written
+      v4f acc[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          acc[db] = mfma_bf16(pa[cc * 2 + ks],
+                              *reinterpret_cast<const v4i*>(
+                                  &s_vt[buf][(db * 16 + col) * kRoundStride + cc * 64 + ks * 32 + grp * 8]),
+                              acc[db]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = s_f[wave * 16 + grp * 4 + r][c];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db][r] = fmaf(f, acc[db][r], o[db][r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t ob = ((int64_t)t * H + hb0 + wave * 16 + grp * 4 + r) * kLatent + slice * kSlice + col;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      if (kOutF32) reinterpret_cast<float*>(out)[ob + db * 16] = o[db][r];
+      else reinterpret_cast<uint16_t*>(out)[ob + db * 16] = f32_to_bf16(o[db][r]);
+    }
+  }
+}
+
+bool use_two_phase(int T, int H, int max_entries) {
+  return H % 64 == 0 && T * (H / 64) <= 128 && max_entries <= kTwoPhaseMaxE && max_entries > 0;
+}
+
 // fp32 pools and queries (small configurations): one workgroup per (query,
 // head); scores in LDS, exact two-pass softmax, then the value sum.
 __global__ void __launch_bounds__(256)
@@ -449,6 +752,11 @@ int pick_splits(int T, int H, int max_entries) {
 }  // namespace
 
 size_t attention_ws_bytes(int64_t T, int64_t max_entries, int H) {
+  if (use_two_phase((int)T, H, (int)max_entries)) {
+    const int64_t e_pad = (max_entries + kChunk - 1) / kChunk * kChunk;
+    const size_t pw = ((size_t)T * H * e_pad * 2 + 255) / 256 * 256;
+    return pw + (size_t)T * H * (e_pad / kChunk) * sizeof(float2);
+  }
   const int s = pick_splits((int)T, H, (int)max_entries);
   if (s <= 1) return 0;
   return (size_t)T * s * H * (kLatent + 2) * sizeof(float);
@@ -463,6 +771,30 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
                        a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel, a.ratio, a.comp, a.comp_pt,
                        a.comp_pt_stride, a.raw, a.raw_pt, a.raw_pt_stride, a.window, a.scale,
                        (float*)a.out);
+    return hipGetLastError();
+  }
+  if (use_two_phase(a.T, a.H, max_entries)) {
+    const int e_pad = (max_entries + kChunk - 1) / kChunk * kChunk;
+    uint16_t* pw = (uint16_t*)a.ws;
+    float2* st = (float2*)((char*)a.ws + ((size_t)a.T * a.H * e_pad * 2 + 255) / 256 * 256);
+    hipLaunchKernelGGL(attn_scores_kernel, dim3(e_pad / kChunk, a.T, a.H / 64), dim3(256), 0, s,
+                       (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,
+                       a.ratio, (const uint8_t*)a.comp.latent, a.comp.latent_scale,
+                       (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt, a.comp_pt_stride,
+                       (const uint8_t*)a.raw.latent, a.raw.latent_scale,
+                       (const uint16_t*)a.raw.rope, a.raw.page_size, a.raw_pt, a.raw_pt_stride,
+                       a.window, a.scale, pw, st, e_pad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+#define CSA_PV(FO)                                                                             \
+  hipLaunchKernelGGL(attn_pv_kernel<FO>, dim3(kLatent / kSlice, a.T, a.H / 64), dim3(256), 0, s, \
+                     (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,    \
+                     a.ratio, (const uint8_t*)a.comp.latent, a.comp.page_size, a.comp_pt,        \
+                     a.comp_pt_stride, (const uint8_t*)a.raw.latent, a.raw.page_size, a.raw_pt, \
+                     a.raw_pt_stride, a.window, pw, st, e_pad, a.out)
+    if (a.out_fmt == CSA_F32) CSA_PV(true);
+    else CSA_PV(false);
+#undef CSA_PV
     return hipGetLastError();
   }
   const int nsplit = pick_splits(a.T, a.H, max_entries);

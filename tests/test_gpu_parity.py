@@ -305,6 +305,7 @@ def _attn_case(g, fmt, B, Ls, H, ps_c=64, extra=3):
 @pytest.mark.parametrize("H,fmt,Ls", [
     (64, "fp8", [131072 // 16, 700, 100, 2 * 4 + 1]),  # full 512 + window, short, p < 127
     (128, "fp8", [20000, 3000]),
+    (64, "fp8", [20 + 3 * i for i in range(130)]),  # > 128 queries: split + combine path
     (16, "f32", [4096, 333]),
 ])
 def test_csa_attention(csa, H, fmt, Ls):
@@ -341,6 +342,7 @@ def test_csa_attention(csa, H, fmt, Ls):
 
 
 @pytest.mark.parametrize("fmt,Ls,H", [("fp8", [100, 128 * 40 + 77, 1048576 // 8], 64),
+                                      ("fp8", [400000, 1000], 64),  # > 2048 entries: split path
                                       ("f32", [127, 128 * 9], 16)])
 def test_hca_attention(csa, fmt, Ls, H):
     g = gen.rng(1100 + H)
