@@ -5,7 +5,7 @@ This package is a thin ctypes binding: it takes torch tensors, passes their
 device pointers, sizes and the current HIP stream to libcsa.so, and raises on
 a non-OK status. Every step of the computation runs in the library's HIP
 kernels; there is no fallback. Importing fails if libcsa.so is not built
-(`python -m compressed_sparse_attention_c4_amd.build`).
+(`python compressed_sparse_attention_c4_amd/build.py`).
 """
 from __future__ import annotations
 

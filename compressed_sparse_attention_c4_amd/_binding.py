@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_PKG, "libcsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m compressed_sparse_attention_c4_amd.build` "
+        f"{LIB_PATH} is not built; run `python compressed_sparse_attention_c4_amd/build.py` "
         "(hipcc, gfx950). There is no fallback implementation.")
 lib = C.CDLL(LIB_PATH)
 

@@ -1,6 +1,8 @@
 """Build libcsa.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m compressed_sparse_attention_c4_amd.build
+    python compressed_sparse_attention_c4_amd/build.py
+
+(run as a script: importing the package needs the library this builds).
 
 Each HIP source compiles to its own object (in parallel), then one link.
 Packed fp32 instructions are disabled on every HIP compile line.
