@@ -377,10 +377,21 @@ attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
 // only intermediate is P' (2 bytes per head and entry), and no merge follows.
 constexpr int kChunk = 64;                // entries per phase-A workgroup
 constexpr int kSlice = 64;                // value dims per phase-B workgroup
-constexpr int kRound = 256;               // entries per phase-B staging round
-constexpr int kRoundStride = kRound + 8;  // bf16 per V^T row in LDS
-constexpr int kTwoPhaseMaxE = 2048;       // entry lists up to this length
+constexpr int kRound = 256;               // entries per phase-B staging task round
+constexpr int kTwoPhaseMaxE = 768;        // entry lists up to this length (3 rounds)
+constexpr int kRounds = kTwoPhaseMaxE / kRound;
+constexpr int kPvStride = kTwoPhaseMaxE + 8;  // bf16 per V^T row in phase B's LDS
 constexpr int kMaxChunks = kTwoPhaseMaxE / kChunk;
+
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations
+// only (not for its outstanding global loads, as __syncthreads would), then
+// s_barrier.
+__device__ __forceinline__ void lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Entry -> pool choice as 64-bit masks (bitwise selects keep gathers
 // straight-line; masked entries read a stand-in and are zeroed).
@@ -410,7 +421,8 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
                    const uint8_t* __restrict__ r_lat, const float* __restrict__ r_sc,
                    const uint16_t* __restrict__ r_rope, int r_ps,
                    const int32_t* __restrict__ raw_pt, int raw_pt_stride, int window, float scale,
-                   uint16_t* __restrict__ pw, float2* __restrict__ stats, int e_pad) {
+                   uint16_t* __restrict__ pw, float2* __restrict__ stats,
+                   int32_t* __restrict__ eslots, int e_pad) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kChunk * kKStride];
   __shared__ int32_t s_es[kChunk];
   __shared__ float s_sc[kChunk];
@@ -421,14 +433,22 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   const EntryList L = entry_list(p, k_sel, hca, ratio, window);
   const int total = min(L.n1 + L.n2, e_pad);  // a list longer than the stated bound is cut
   const int e0 = chunk * kChunk;
-  if (e0 >= total) return;  // past this query's list: phase B reads no such chunk
-  const int hbase = blockIdx.z * 64 + wave * 16;
-  v4i qa[18];
-  {
-    const uint16_t* qrow = q + ((int64_t)t * H + hbase + col) * kKvDim + grp * 8;
-#pragma unroll
-    for (int s = 0; s < 18; ++s) qa[s] = *reinterpret_cast<const v4i*>(qrow + s * 32);
+  const int n_chunks = e_pad / kChunk;
+  const int hb0 = blockIdx.z * 64;
+  if (e0 >= total) {
+    // past this query's list: masked slots, zero weights, dead statistics, so
+    // that phase B reads every chunk without knowing the list's length
+    const int hh = tid >> 2, part = tid & 3;
+    v4i* prow = reinterpret_cast<v4i*>(pw + ((int64_t)t * H + hb0 + hh) * e_pad + e0 + part * 16);
+    prow[0] = v4i{0, 0, 0, 0};
+    prow[1] = v4i{0, 0, 0, 0};
+    if (tid < kChunk) {
+      stats[((int64_t)t * H + hb0 + tid) * n_chunks + chunk] = make_float2(-INFINITY, 0.f);
+      if (blockIdx.z == 0) eslots[(int64_t)t * e_pad + e0 + tid] = -1;
+    }
+    return;
   }
+  const int hbase = hb0 + wave * 16;
   if (tid < kChunk) {
     const int i = e0 + tid;
     int pool = 0;
@@ -436,9 +456,20 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
                                                 comp_pt_stride, c_ps, raw_pt, raw_pt_stride,
                                                 r_ps, pool)
                                    : -1;
-    s_es[tid] = slot >= 0 ? (int32_t)(slot * 2 + pool) : -1;
+    const int32_t w = slot >= 0 ? (int32_t)(slot * 2 + pool) : -1;
+    s_es[tid] = w;
+    if (blockIdx.z == 0) eslots[(int64_t)t * e_pad + e0 + tid] = w;
   }
-  __syncthreads();
+  // the query operand is loaded after the slot reads, so that waiting for
+  // those does not wait for these
+  __builtin_amdgcn_sched_barrier(0);
+  v4i qa[18];
+  {
+    const uint16_t* qrow = q + ((int64_t)t * H + hbase + col) * kKvDim + grp * 8;
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qa[s] = *reinterpret_cast<const v4i*>(qrow + s * 32);
+  }
+  lds_sync();
   // gathers: 64 entries x 32 latent chunks of 16 B (8 per thread, one entry
   // row per 32 lanes), 64 x 8 RoPE chunks (2 per thread), 64 scales
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + (int64_t)t * H * kKvDim);
@@ -483,7 +514,7 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
     *reinterpret_cast<v4i*>(&s_k[e * kKStride + kLatent + 8 * c]) = rp[k];
   }
   if (tid < kChunk) s_sc[tid] = scv;
-  __syncthreads();
+  lds_sync();
 
   // scores of 16 heads x 64 entries (four 16-column blocks)
   float sv[4][4];
@@ -504,7 +535,6 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
 #pragma unroll
     for (int r = 0; r < 4; ++r) sv[cb][r] = valid ? scale * fmaf(sc, acc_l[r], acc_r[r]) : -INFINITY;
   }
-  const int n_chunks = e_pad / kChunk;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = hbase + grp * 4 + r;
@@ -523,98 +553,91 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   }
 }
 
+// Phase B needs nothing of the query but phase A's outputs: the slot words,
+// the weights and the chunk statistics of all e_pad entries (chunks past a
+// list were written as masked / zero / dead). Round 1 loads all of those at
+// once; round 2 gathers the value slice of every entry at once; then the
+// value tile is transposed into LDS and the products run.
 template <bool kOutF32>
 __global__ void __launch_bounds__(256)
-attn_pv_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
-               const int32_t* __restrict__ q_pos, bool hca, const int32_t* __restrict__ phys_idx,
-               int k_sel, int ratio, const uint8_t* __restrict__ c_lat, int c_ps,
-               const int32_t* __restrict__ comp_pt, int comp_pt_stride,
-               const uint8_t* __restrict__ r_lat, int r_ps, const int32_t* __restrict__ raw_pt,
-               int raw_pt_stride, int window, const uint16_t* __restrict__ pw,
+attn_pv_kernel(int H, const uint8_t* __restrict__ c_lat, const uint8_t* __restrict__ r_lat,
+               const int32_t* __restrict__ eslots, const uint16_t* __restrict__ pw,
                const float2* __restrict__ stats, int e_pad, void* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kSlice * kRoundStride];
-  __shared__ int32_t s_es[kTwoPhaseMaxE];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kSlice * kPvStride];
   __shared__ float s_f[64][kMaxChunks];
   const int slice = blockIdx.x, t = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int seq = q_seq[t], p = q_pos[t];
-  const EntryList L = entry_list(p, k_sel, hca, ratio, window);
-  const int total = min(L.n1 + L.n2, e_pad);  // as in phase A
-  const int nch = (total + kChunk - 1) / kChunk;
-  const int n_chunks = e_pad / kChunk;
   const int hb0 = blockIdx.z * 64;
-  for (int i = tid; i < total; i += 256) {
-    int pool = 0;
-    const int64_t slot = entry_slot(i, L, t, seq, hca, phys_idx, k_sel, comp_pt, comp_pt_stride,
-                                    c_ps, raw_pt, raw_pt_stride, r_ps, pool);
-    s_es[i] = slot >= 0 ? (int32_t)(slot * 2 + pool) : -1;
-  }
-  if (tid < 64) {
-    // exact normaliser of head hb0 + tid from its chunks' (m_c, l_c)
-    const float2* st = stats + ((int64_t)t * H + hb0 + tid) * n_chunks;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, st[c].x);
-    float Ls = 0.f;
-    for (int c = 0; c < nch; ++c)
-      if (st[c].x != -INFINITY) Ls = fmaf(st[c].y, __expf(st[c].x - M), Ls);
-    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    for (int c = 0; c < nch; ++c)
-      s_f[tid][c] = st[c].x == -INFINITY ? 0.f : __expf(st[c].x - M) * inv;
-  }
-  __syncthreads();
-  if (total == 0) {  // nothing visible: zero output
+  const int n_chunks = e_pad / kChunk;
+  // staging task of this thread in each round: entries r*256 + 8*eg .. +7,
+  // value dims slice*64 + 8*dg .. +7 (lanes 8k..8k+7: 64 contiguous bytes)
+  const int dg = tid & 7, eg = tid >> 3;
+
+  // ---- round 1: slot words, weights, statistics
+  v4i sw[kRounds][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t ob = ((int64_t)t * H + hb0 + wave * 16 + grp * 4 + r) * kLatent + slice * kSlice + col;
+  for (int r = 0; r < kRounds; ++r) {
+    const int e = min(r * kRound + 8 * eg, e_pad - 8);
+    const v4i* src = reinterpret_cast<const v4i*>(eslots + (int64_t)t * e_pad + e);
+    sw[r][0] = src[0];
+    sw[r][1] = src[1];
+  }
+  const uint16_t* prow = pw + ((int64_t)t * H + hb0 + wave * 16 + col) * e_pad + grp * 8;
+  v4i pa[kRounds * 8];  // A operands: 32-entry steps of this wave's 16 heads
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        if (kOutF32) reinterpret_cast<float*>(out)[ob + db * 16] = 0.f;
-        else reinterpret_cast<uint16_t*>(out)[ob + db * 16] = 0;
-      }
-    }
-    return;
+  for (int ks = 0; ks < kRounds * 8; ++ks)
+    pa[ks] = *reinterpret_cast<const v4i*>(prow + min(ks * 32, e_pad - 32));
+  float2 st[kMaxChunks];
+  {
+    const float2* sp = stats + ((int64_t)t * H + hb0 + (tid & 63)) * n_chunks;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) st[c] = sp[min(c, n_chunks - 1)];
   }
 
-  // staging task: 8 entries x 8 value dims (lanes 8k..8k+7 read 64 contiguous
-  // bytes of one entry), written transposed to V^T [dim][entry]
-  const int dg = tid & 7, eg = tid >> 3;
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + (int64_t)t * H * kKvDim);
-  const int hl = wave * 16 + col;  // A-operand row (head within the block)
-  const uint16_t* prow = pw + ((int64_t)t * H + hb0 + hl) * e_pad + grp * 8;
-  v2i codes[8];
-  v4i pa_next[8];
-  auto issue = [&](int r0) __attribute__((always_inline)) {
+  // ---- round 2: the value slice of every entry
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(pw);
+  v2i codes[kRounds][8];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int e = r0 + 8 * eg + j;
-      const int es0 = s_es[min(e, total - 1)];
-      const Pick pk = pick_of(e < total ? es0 : -1);
+      const int live = r * kRound + 8 * eg + j < e_pad;
+      const int es = live ? sw[r][j >> 2][j & 3] : -1;
+      const Pick pk = pick_of(es);
       const v2i x = *reinterpret_cast<const v2i*>(pick_base(pk, c_lat, r_lat, dummy) +
                                                   pk.slot * kLatent + slice * kSlice + 8 * dg);
-      codes[j] = pk.md ? v2i{0, 0} : x;
+      codes[r][j] = pk.md ? v2i{0, 0} : x;
     }
+
+  // chunk factors f_c = exp(m_c - M) / L (threads 0..63: head hb0 + tid)
+  if (tid < 64) {
+    float M = -INFINITY;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      pa_next[ks] = *reinterpret_cast<const v4i*>(prow + min(r0 + ks * 32, e_pad - 32));
-  };
-  v4f o[4];
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < n_chunks) M = fmaxf(M, st[c].x);
+    float Ls = 0.f;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
-  issue(0);
-  int buf = 0;
-  for (int r0 = 0; r0 < total; r0 += kRound, buf ^= 1) {
-    // codes[j] holds dims 8*dg .. +7 of entry 8*eg + j as two words of four
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < n_chunks && st[c].x != -INFINITY) Ls = fmaf(st[c].y, __expf(st[c].x - M), Ls);
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      s_f[tid][c] = (c < n_chunks && st[c].x != -INFINITY) ? __expf(st[c].x - M) * inv : 0.f;
+  }
+  // V^T [dim][entry] in bf16 (exact): an 8 x 8 block per thread and round
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
     uint32_t kb[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      kb[j][0] = fp8x2_to_bf16x2<false>((uint32_t)codes[j][0]);
-      kb[j][1] = fp8x2_to_bf16x2<true>((uint32_t)codes[j][0]);
-      kb[j][2] = fp8x2_to_bf16x2<false>((uint32_t)codes[j][1]);
-      kb[j][3] = fp8x2_to_bf16x2<true>((uint32_t)codes[j][1]);
+      kb[j][0] = fp8x2_to_bf16x2<false>((uint32_t)codes[r][j][0]);
+      kb[j][1] = fp8x2_to_bf16x2<true>((uint32_t)codes[r][j][0]);
+      kb[j][2] = fp8x2_to_bf16x2<false>((uint32_t)codes[r][j][1]);
+      kb[j][3] = fp8x2_to_bf16x2<true>((uint32_t)codes[r][j][1]);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {  // dim 8*dg + i of the slice, entries 8*eg .. +7
+    for (int i = 0; i < 8; ++i) {
       const int w = i >> 1;
       uint32_t d[4];
 #pragma unroll
@@ -622,18 +645,18 @@ attn_pv_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict_
         const uint32_t a = kb[2 * jj][w], b = kb[2 * jj + 1][w];
         d[jj] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
       }
-      *reinterpret_cast<v4i*>(&s_vt[buf][(8 * dg + i) * kRoundStride + 8 * eg]) =
+      *reinterpret_cast<v4i*>(&s_vt[(8 * dg + i) * kPvStride + r * kRound + 8 * eg]) =
           v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
     }
-    v4i pa[8];
+  }
+  lds_sync();
+
+  v4f o[4];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) pa[ks] = pa_next[ks];
-    __syncthreads();
-    if (r0 + kRound < total) issue(r0 + kRound);
+  for (int db = 0; db < 4; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cc = 0; cc < kRound / kChunk; ++cc) {
-      const int c = r0 / kChunk + cc;
-      if (c >= nch) break;  // uniform: chunks past the list were never written
+  for (int c = 0; c < kMaxChunks; ++c) {
+    if (c < n_chunks) {  // uniform; no early exit, so pa stays in registers
       v4f acc[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[db] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -641,9 +664,9 @@ attn_pv_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict_
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          acc[db] = mfma_bf16(pa[cc * 2 + ks],
+          acc[db] = mfma_bf16(pa[c * 2 + ks],
                               *reinterpret_cast<const v4i*>(
-                                  &s_vt[buf][(db * 16 + col) * kRoundStride + cc * 64 + ks * 32 + grp * 8]),
+                                  &s_vt[(db * 16 + col) * kPvStride + c * kChunk + ks * 32 + grp * 8]),
                               acc[db]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -666,6 +689,20 @@ attn_pv_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict_
 
 bool use_two_phase(int T, int H, int max_entries) {
   return H % 64 == 0 && T * (H / 64) <= 128 && max_entries <= kTwoPhaseMaxE && max_entries > 0;
+}
+
+// Workspace of the two-phase path: P' [T][H][e_pad] bf16, then the chunk
+// statistics [T][H][e_pad/64] float2, then the slot words [T][e_pad] int32.
+struct TwoPhaseWs {
+  size_t pw, stats, eslots, total;
+};
+TwoPhaseWs two_phase_ws(int64_t T, int H, int e_pad) {
+  TwoPhaseWs w;
+  w.pw = 0;
+  w.stats = ((size_t)T * H * e_pad * 2 + 255) / 256 * 256;
+  w.eslots = w.stats + ((size_t)T * H * (e_pad / kChunk) * sizeof(float2) + 255) / 256 * 256;
+  w.total = w.eslots + (size_t)T * e_pad * sizeof(int32_t);
+  return w;
 }
 
 // fp32 pools and queries (small configurations): one workgroup per (query,
@@ -752,11 +789,8 @@ int pick_splits(int T, int H, int max_entries) {
 }  // namespace
 
 size_t attention_ws_bytes(int64_t T, int64_t max_entries, int H) {
-  if (use_two_phase((int)T, H, (int)max_entries)) {
-    const int64_t e_pad = (max_entries + kChunk - 1) / kChunk * kChunk;
-    const size_t pw = ((size_t)T * H * e_pad * 2 + 255) / 256 * 256;
-    return pw + (size_t)T * H * (e_pad / kChunk) * sizeof(float2);
-  }
+  if (use_two_phase((int)T, H, (int)max_entries))
+    return two_phase_ws(T, H, (int)((max_entries + kChunk - 1) / kChunk * kChunk)).total;
   const int s = pick_splits((int)T, H, (int)max_entries);
   if (s <= 1) return 0;
   return (size_t)T * s * H * (kLatent + 2) * sizeof(float);
@@ -775,23 +809,23 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   if (use_two_phase(a.T, a.H, max_entries)) {
     const int e_pad = (max_entries + kChunk - 1) / kChunk * kChunk;
-    uint16_t* pw = (uint16_t*)a.ws;
-    float2* st = (float2*)((char*)a.ws + ((size_t)a.T * a.H * e_pad * 2 + 255) / 256 * 256);
+    const TwoPhaseWs w = two_phase_ws(a.T, a.H, e_pad);
+    uint16_t* pw = (uint16_t*)((char*)a.ws + w.pw);
+    float2* st = (float2*)((char*)a.ws + w.stats);
+    int32_t* es = (int32_t*)((char*)a.ws + w.eslots);
     hipLaunchKernelGGL(attn_scores_kernel, dim3(e_pad / kChunk, a.T, a.H / 64), dim3(256), 0, s,
                        (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,
                        a.ratio, (const uint8_t*)a.comp.latent, a.comp.latent_scale,
                        (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt, a.comp_pt_stride,
                        (const uint8_t*)a.raw.latent, a.raw.latent_scale,
                        (const uint16_t*)a.raw.rope, a.raw.page_size, a.raw_pt, a.raw_pt_stride,
-                       a.window, a.scale, pw, st, e_pad);
+                       a.window, a.scale, pw, st, es, e_pad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 #define CSA_PV(FO)                                                                             \
   hipLaunchKernelGGL(attn_pv_kernel<FO>, dim3(kLatent / kSlice, a.T, a.H / 64), dim3(256), 0, s, \
-                     (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,    \
-                     a.ratio, (const uint8_t*)a.comp.latent, a.comp.page_size, a.comp_pt,        \
-                     a.comp_pt_stride, (const uint8_t*)a.raw.latent, a.raw.page_size, a.raw_pt, \
-                     a.raw_pt_stride, a.window, pw, st, e_pad, a.out)
+                     a.H, (const uint8_t*)a.comp.latent, (const uint8_t*)a.raw.latent, es, pw, st, \
+                     e_pad, a.out)
     if (a.out_fmt == CSA_F32) CSA_PV(true);
     else CSA_PV(false);
 #undef CSA_PV

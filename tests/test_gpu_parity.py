@@ -341,8 +341,9 @@ def test_csa_attention(csa, H, fmt, Ls):
             assert np.abs(got[t] - want).max() <= 2e-2
 
 
-@pytest.mark.parametrize("fmt,Ls,H", [("fp8", [100, 128 * 40 + 77, 1048576 // 8], 64),
-                                      ("fp8", [400000, 1000], 64),  # > 2048 entries: split path
+@pytest.mark.parametrize("fmt,Ls,H", [("fp8", [100, 128 * 40 + 77, 60000], 64),  # two-phase path
+                                      ("fp8", [100, 128 * 40 + 77, 1048576 // 8], 64),
+                                      ("fp8", [400000, 1000], 64),  # long list: many splits
                                       ("f32", [127, 128 * 9], 16)])
 def test_hca_attention(csa, fmt, Ls, H):
     g = gen.rng(1100 + H)

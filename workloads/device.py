@@ -66,7 +66,7 @@ class CsaDecode:
     (the current token is the last raw token, p = L - 1)."""
 
     def __init__(self, wl: Workload, lens, copies: int = 3, pool_pages: int | None = None,
-                 seed_offset: int = 0, with_compress: bool = True):
+                 seed_offset: int = 0, with_compress: bool = True, parallel_writes: bool = False):
         self.wl = wl
         self.B = B = len(lens)
         self.lens = np.asarray(lens, dtype=np.int64)
@@ -143,6 +143,12 @@ class CsaDecode:
         self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         n = csa.csa_workspace_size(csa.CSA_OP_TOPK, B, self.maxN, 1)
         self.topk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        # parallel_writes: the KV writes of the step (compressed block, raw
+        # token) do not feed the indexer and may run on a second stream
+        # (default priority), joined before attention. Measured on MI355X, the
+        # two-branch graph is slower (113 vs 102 us per 128K step): the
+        # cross-queue join costs more than the overlap saves. Off by default.
+        self.side = torch.cuda.Stream() if parallel_writes else None
         torch.cuda.synchronize()
 
     # algorithmic bytes of one indexer launch: index-K rows + prepared q +
@@ -167,13 +173,18 @@ class CsaDecode:
     def step(self, c: int, ev=None):
         idx, kv = self.index_pools[c], self.c4_pools[c]
         wl = self.wl
+        main = torch.cuda.current_stream()
         if self.with_compress:
-            # the current token completes block N-1: compress it, append the
-            # token to the raw window pool, prepare its index-K row
-            csa.c4_compress(self.x_new, self.cu_new, self.start_new, 4, 4, self.gate_w, self.gate_b,
-                            self.pt, kv)
-            csa.c4_compress(self.x_tok, self.cu_tok, self.start_tok, 1, 1, self.zero_w, self.zero_b,
-                            self.pt, self.raw)
+            # the current token completes block N-1 (when L % 4 == 0): compress
+            # it and append the token to the raw window pool (second stream),
+            # prepare its index-K row (this stream: the indexer reads it)
+            side = self.side or main
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                csa.c4_compress(self.x_new, self.cu_new, self.start_new, 4, 4, self.gate_w,
+                                self.gate_b, self.pt, kv)
+                csa.c4_compress(self.x_tok, self.cu_tok, self.start_tok, 1, 1, self.zero_w,
+                                self.zero_b, self.pt, self.raw)
             kd = idx.data.view(-1, idx.data.shape[-1])
             ks = idx.scale.view(kd.shape[0], -1)
             csa.csa_index_prep(self.k_new, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt, kd, ks,
@@ -188,6 +199,8 @@ class CsaDecode:
             ev[1].record()
         csa.topk512_page_select(self.logits, self.row_len, self.row_seq, self.pt, self.phys,
                                 ws=self.topk_ws)
+        if self.with_compress and self.side is not None:
+            main.wait_stream(self.side)
         csa.csa_sparse_attn(self.q_attn, self.row_seq, self.q_pos, self.phys, kv, self.raw, self.pt,
                             wl.window, wl.softmax_scale, self.out, ws=self.attn_ws)
 
