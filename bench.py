@@ -117,8 +117,8 @@ def reduce_counters(d):
     w_scale = COPY_BYTES / (cw[copy_k][0] * 1024)
     kf = _counter_means(_find_csv(d, "decode128k_fetch"), "FETCH_SIZE")
     kw = _counter_means(_find_csv(d, "decode128k_write"), "WRITE_SIZE")
-    name = "indexer_mfma_kernel<false>"
-    hits = [k for k in kf if "indexer_mfma_kernel<false>" in k]
+    name = "indexer_mfma_kernel<false, true>"
+    hits = [k for k in kf if "indexer_mfma_kernel<false, true>" in k]
     if len(hits) != 1:
         raise SystemExit(f"expected one {name} in the fetch run, found {hits}")
     k = hits[0]
@@ -206,7 +206,7 @@ def secondary(a):
     ms, idx_ms, _ = time_steps(W, steps, a.warmup, a.copies, graph=not a.no_graph)
     gbs = W.indexer_bytes() / (idx_ms / 1e3) / 1e9
     out[wl.name] = {"queries_per_s": round(W.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
-                    "indexer": {"kernel": "indexer_mfma_kernel<true>", "kernel_ms": round(idx_ms, 5),
+                    "indexer": {"kernel": "indexer_mfma_kernel<true, true>", "kernel_ms": round(idx_ms, 5),
                                 "bytes_per_launch": W.indexer_bytes(), "achieved_GBs": round(gbs, 1),
                                 "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
                     "step_hbm_frac": round(W.step_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -385,7 +385,7 @@ def main():
     ibytes = W.indexer_bytes()
     achieved = ibytes / (idx_ms / 1e3) / 1e9
     src_hash = kernel_source_hash("indexer.hip", "csa_device.hpp")
-    traffic = stored_traffic("indexer_mfma_kernel<false>", src_hash)
+    traffic = stored_traffic("indexer_mfma_kernel<false, true>", src_hash)
     line = {
         "metric": "CSA decode queries/s @128K ctx",
         "value": round(qps, 1),
@@ -405,7 +405,7 @@ def main():
                    "window": wl.window, "pool_copies": a.copies, "hip_graph": not a.no_graph},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "indexer_mfma_kernel<false>",
+                     "traffic": traffic, "kernel": "indexer_mfma_kernel<false, true>",
                      "kernel_ms": round(idx_ms, 5), "bytes_per_launch": ibytes},
         "step_hbm_frac": round(W.step_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
     }

@@ -119,6 +119,26 @@ __device__ __forceinline__ float2 permlane32_pair(float v) {
   return make_float2(a, b);
 }
 
+// Swap of two registers across rows: permlane16 gives a = [a.r0, b.r0, a.r2,
+// b.r2], b = [a.r1, b.r1, a.r3, b.r3] (rows of 16 lanes); permlane32 gives
+// a = [a.lo, b.lo], b = [a.hi, b.hi] (halves of 32 lanes).
+__device__ __forceinline__ void permlane16_swap2(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap2(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+// Four values per lane, p[k] = a row's partial of column group k: returns, in
+// every lane of row r, the sum of p[r] over the four rows (a reduce-scatter:
+// three swaps instead of four full reductions).
+__device__ __forceinline__ float rows4_reduce_scatter(float p0, float p1, float p2, float p3) {
+  permlane16_swap2(p0, p1);
+  permlane16_swap2(p2, p3);
+  float qa = p0 + p1, qb = p2 + p3;
+  permlane32_swap2(qa, qb);
+  return qa + qb;
+}
+
 // The value held by lane (l ^ kM), kM in {1, 2, 4, 8} (within a row).
 template <int kM>
 __device__ __forceinline__ float lane_xor(float v) {

@@ -30,8 +30,8 @@ namespace {
 constexpr int kHeads = 64;   // indexer heads handled by the MFMA path
 constexpr int kDim = 128;    // indexer head dim handled by the MFMA path
 constexpr int kWaves = 4;
-constexpr int kUnroll = 8;   // 16-entry groups in flight per wave
-constexpr int kWgEntries = kWaves * kUnroll * 16;
+constexpr int kRing = 2;     // 64-entry batches in flight per wave
+constexpr int kWgEntries = kWaves * kRing * 64;
 constexpr int kMaxChunk = 8 * kWgEntries;  // entries per workgroup, at most
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, v4f c) {
@@ -48,7 +48,7 @@ __device__ __forceinline__ v4f mfma_fp4(const v8i& a, const v8i& b, v4f c, int s
 // that K-range is one 32-element scale block, whose e8m0 byte the lane
 // supplies as its scale. The result lane l holds rows 4*(l/16) + 0..3 of
 // column l % 16.
-template <bool kFp4>
+template <bool kFp4, bool kPage64>
 __global__ void __launch_bounds__(kWaves * 64)
 indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     const float* __restrict__ w, const int32_t* __restrict__ row_seq,
@@ -58,6 +58,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     int64_t ld, int chunk) {
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K / q row
   __shared__ int32_t s_pages[kMaxChunk / 16 + 2];      // physical pages of this chunk
+  __shared__ __attribute__((aligned(16))) float s_out[kMaxChunk + 64];  // the chunk's logits
   const int t = blockIdx.y;
   const int n = row_len[t];
   const int c0 = blockIdx.x * chunk;
@@ -65,7 +66,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   const int c1 = min(c0 + chunk, n);
   const int seq = row_seq[t];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop
   const int col = lane & 15;
   const int grp = lane >> 4;
 
@@ -108,64 +109,103 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
     }
   __syncthreads();
 
-  // Groups of 16 entries never straddle a page (page_size % 16 == 0 and the
-  // chunk starts on a multiple of 16), so a group's page is wave-uniform.
-  // This wave takes groups g = 0, 1, ... at entries c0 + 16*wave + 64*g and
-  // keeps the loads of the next kUnroll groups in flight while it scores the
-  // current one (a register ring: slot u holds group g with g % kUnroll == u).
-  // The loop is branch-free so the compiler can count outstanding loads
-  // exactly: groups past the chunk load entry 0 of the chunk's first page, and
-  // logits go through a buffer resource bounded to this chunk, so stores of
-  // lanes past the chunk end are dropped by the hardware.
-  const int ngroups = (c1 - c0 - 16 * wave + kWaves * 16 - 1) / (kWaves * 16);
-  const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      logits + (int64_t)t * ld + c0, (short)0, (c1 - c0) * 4, 0x00020000);
-  v8i b[kUnroll];
-  int sb[kUnroll];
-  float ks[kUnroll];
-  auto issue = [&](int g, int u) __attribute__((always_inline)) {
-    const int g0 = c0 + wave * 16 + g * kWaves * 16;  // first entry of the group
-    const bool in = g0 < c1;
-    const int j = g0 + col;
-    const int pg = s_pages[in ? g0 / page_size - pg0 : 0];
-    const int64_t slot = (j < c1) ? (int64_t)pg * page_size + j % page_size : (int64_t)s_pages[0] * page_size;
-    const uint8_t* p = kdata + slot * kRowBytes + grp * (kRowBytes / 4);
-    if (kFp4) {
-      const uint4 x = *reinterpret_cast<const uint4*>(p);
-      b[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-      sb[u] = reinterpret_cast<const uint8_t*>(kscale)[slot * 4 + grp];
-      ks[u] = 1.f;
-    } else {
-      const uint4 x = *reinterpret_cast<const uint4*>(p);
-      const uint4 y = *reinterpret_cast<const uint4*>(p + 16);
-      b[u] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-      sb[u] = 127;
-      ks[u] = reinterpret_cast<const float*>(kscale)[slot];
-    }
+  // Entries go in batches of 64 (four 16-entry groups; a group never
+  // straddles a page since page_size % 16 == 0 and the chunk starts on a
+  // multiple of 16, so its page is wave-uniform). Wave w takes batches w,
+  // w + kWaves, ... and keeps kRing batches of loads in flight (a register
+  // ring, slot = batch % kRing). After the 16 MFMAs of a batch, one
+  // reduce-scatter across the four lane rows leaves in row r the 64-head sum
+  // of group r, so each lane stores one logit and a wave writes the batch's
+  // 64 logits as one contiguous 256-byte store; the lane also loads the FP8
+  // scale of exactly that entry. The logits collect in LDS and are written
+  // out after the loop: a global store inside it would sit in the same
+  // in-order memory counter as the loads and delay every later wait. The loop
+  // is branch-free: batches past the chunk load entry 0 of its first page (or
+  // their page), and their logits land in LDS past the chunk and are dropped.
+  const int nbatch = (c1 - c0 + 63) / 64;
+  const int nb = (nbatch - wave + kWaves - 1) / kWaves;  // batches of this wave
+  v8i b[kRing][4];
+  int sb[kRing][4];
+  float ks[kRing];
+  auto slot_of = [&](int j, int g0) __attribute__((always_inline)) {
+    const int pg = s_pages[g0 < c1 ? g0 / page_size - pg0 : 0];
+    return (j < c1) ? (int64_t)pg * page_size + j % page_size : (int64_t)s_pages[0] * page_size;
   };
+  // 64-entry pages (the C4 layout): a batch is one page (the chunk starts on a
+  // page), found with no division; entries past the chunk read their page
+  // anyway (their logits are dropped)
+  const int last_pg = npg - 1;
+  auto batch_page = [&](int i) __attribute__((always_inline)) {
+    return (int64_t)s_pages[min(i * kWaves + wave, last_pg)] * 64;
+  };
+  auto issue = [&](int i, auto R) __attribute__((always_inline)) {
+    constexpr int r = decltype(R)::value;
+    const int e0 = c0 + (i * kWaves + wave) * 64;  // first entry of the batch
+    const int64_t pbase = kPage64 ? batch_page(i) : 0;
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) issue(u, u);
-  for (int g0 = 0; g0 < ngroups; g0 += kUnroll) {
+    for (int k = 0; k < 4; ++k) {
+      const int g0 = e0 + 16 * k;
+      const int64_t slot = kPage64 ? pbase + 16 * k + col : slot_of(g0 + col, g0);
+      const uint8_t* p = kdata + slot * kRowBytes + grp * (kRowBytes / 4);
+      if (kFp4) {
+        const v4i x = *reinterpret_cast<const v4i*>(p);
+        b[r][k] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+        // the entry's four block-scale bytes as one word; the lane's byte is
+        // taken at the use (a byte load would be narrowed and re-extended at
+        // the loop head, where it waits for every outstanding load)
+        sb[r][k] = reinterpret_cast<const int32_t*>(kscale)[slot];
+      } else {
+        const v4i x = *reinterpret_cast<const v4i*>(p);
+        const v4i y = *reinterpret_cast<const v4i*>(p + 16);
+        b[r][k] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        sb[r][k] = 127;
+      }
+    }
+    if (!kFp4) {  // scale of the entry this lane stores: group grp, column col
+      const int g0 = e0 + 16 * grp;
+      const int64_t slot = kPage64 ? pbase + 16 * grp + col : slot_of(g0 + col, g0);
+      ks[r] = reinterpret_cast<const float*>(kscale)[slot];
+    } else {
+      ks[r] = 1.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads together, in issue order
+  };
+  auto step = [&](int i, auto R) __attribute__((always_inline)) {
+    constexpr int r = decltype(R)::value;
+    float pk[4];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int g = g0 + u;
+    for (int k = 0; k < 4; ++k) {
       v4f acc[4];
+      const int sbk = kFp4 ? (int)__builtin_amdgcn_ubfe((uint32_t)sb[r][k], 8 * grp, 8) : 127;
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
-        acc[hb] = kFp4 ? mfma_fp4(a[hb], b[u], v4f{0.f, 0.f, 0.f, 0.f}, sa[hb], sb[u])
-                       : mfma_fp8(a[hb], b[u], v4f{0.f, 0.f, 0.f, 0.f});
+        acc[hb] = kFp4 ? mfma_fp4(a[hb], b[r][k], v4f{0.f, 0.f, 0.f, 0.f}, sa[hb], sbk)
+                       : mfma_fp8(a[hb], b[r][k], v4f{0.f, 0.f, 0.f, 0.f});
       float v = 0.f;
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v = fmaf(wq[hb * 4 + r], fmaxf(acc[hb][r], 0.f), v);
-      v = cross_row_sum(v);
-      const int jl = wave * 16 + g * kWaves * 16 + col;  // entry index within the chunk
-      const int off = (grp == 0 && g < ngroups) ? jl * 4 : 0x7FFFFFFF;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * ks[u]), out_rsrc, off, 0, 0);
-      issue(g + kUnroll, u);  // refill the slot just consumed
+        for (int q = 0; q < 4; ++q) v = fmaf(wq[hb * 4 + q], fmaxf(acc[hb][q], 0.f), v);
+      pk[k] = v;
     }
+    const float tot = rows4_reduce_scatter(pk[0], pk[1], pk[2], pk[3]);
+    // entry within the chunk; a batch past this wave's last lands in the
+    // spare 64 slots at the end
+    const int jl = i < nb ? (i * kWaves + wave) * 64 + 16 * grp + col : kMaxChunk + lane;
+    s_out[jl] = tot * ks[r];
+    issue(i + kRing, R);  // refill the slot just consumed
+  };
+  static_assert(kRing == 2, "the batch loop below is unrolled by hand for two slots");
+  issue(0, std::integral_constant<int, 0>{});
+  issue(1, std::integral_constant<int, 1>{});
+  for (int i0 = 0; i0 < nb; i0 += kRing) {
+    step(i0, std::integral_constant<int, 0>{});
+    step(i0 + 1, std::integral_constant<int, 1>{});
   }
+  __syncthreads();
+  float* orow = logits + (int64_t)t * ld + c0;
+  const int n_out = c1 - c0;
+  for (int j = threadIdx.x; j < n_out; j += kWaves * 64) orow[j] = s_out[j];
 }
 
 // Many query rows (prefill): a workgroup of 8 waves owns 8 consecutive rows
@@ -430,9 +470,11 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
       e = hipMemcpyAsync(q_used_scale, q_scale, scale_bytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
-  // Chunk the rows so the grid has ~512 workgroups (2 per CU), each wave a
-  // long stream; CSA_TUNE_INDEXER_WGS overrides the target (tuning only).
-  int64_t target = 512;
+  // Chunk the rows so the grid has ~256 workgroups (one per CU), each wave a
+  // long stream: measured on MI355X, one workgroup per CU streams faster than
+  // two (fewer concurrent page streams); CSA_TUNE_INDEXER_WGS overrides the
+  // target (tuning only).
+  int64_t target = 256;
   if (const char* e = getenv("CSA_TUNE_INDEXER_WGS")) target = atoll(e) > 0 ? atoll(e) : target;
   int64_t total = (int64_t)T * max_row_len;
   int64_t chunk = total / target;
@@ -452,14 +494,19 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
     return hipGetLastError();
   }
   dim3 grid((unsigned)((max_row_len + chunk - 1) / chunk), T);
-  if (k.fmt == CSA_MXFP4)
-    hipLaunchKernelGGL(indexer_mfma_kernel<true>, grid, dim3(kWaves * 64), 0, s, qc, qs, w,
-                       row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data,
-                       k.scale, k.page_size, logits, ld, (int)chunk);
-  else
-    hipLaunchKernelGGL(indexer_mfma_kernel<false>, grid, dim3(kWaves * 64), 0, s, qc, qs, w,
-                       row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data,
-                       k.scale, k.page_size, logits, ld, (int)chunk);
+#define CSA_IDX(FP4, P64)                                                                      \
+  hipLaunchKernelGGL((indexer_mfma_kernel<FP4, P64>), grid, dim3(kWaves * 64), 0, s, qc, qs, w, \
+                     row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data, k.scale,    \
+                     k.page_size, logits, ld, (int)chunk)
+  const bool p64 = k.page_size == 64;
+  if (k.fmt == CSA_MXFP4) {
+    if (p64) CSA_IDX(true, true);
+    else CSA_IDX(true, false);
+  } else {
+    if (p64) CSA_IDX(false, true);
+    else CSA_IDX(false, false);
+  }
+#undef CSA_IDX
   return hipGetLastError();
 }
 
