@@ -182,6 +182,46 @@ __device__ __forceinline__ float cross_row_max(float v) {
 }
 __device__ __forceinline__ float wave_sum(float v) { return cross_row_sum(row16_sum(v)); }
 __device__ __forceinline__ float wave_max(float v) { return cross_row_max(row16_max(v)); }
+// Unsigned 32-bit wave reductions and an inclusive wave scan on the same
+// VALU paths (the permlane swaps move bits, so floats carry the integers).
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = min(v, dpp_u32<kDppQuadXor1>(v));
+  v = min(v, dpp_u32<kDppQuadXor2>(v));
+  v = min(v, dpp_u32<kDppRowHalfMirror>(v));
+  v = min(v, dpp_u32<kDppRowMirror>(v));
+  const float2 a = permlane16_pair(__uint_as_float(v));
+  v = min(__float_as_uint(a.x), __float_as_uint(a.y));
+  const float2 b = permlane32_pair(__uint_as_float(v));
+  return min(__float_as_uint(b.x), __float_as_uint(b.y));
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, dpp_u32<kDppQuadXor1>(v));
+  v = max(v, dpp_u32<kDppQuadXor2>(v));
+  v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+  v = max(v, dpp_u32<kDppRowMirror>(v));
+  const float2 a = permlane16_pair(__uint_as_float(v));
+  v = max(__float_as_uint(a.x), __float_as_uint(a.y));
+  const float2 b = permlane32_pair(__uint_as_float(v));
+  return max(__float_as_uint(b.x), __float_as_uint(b.y));
+}
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row feeds the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 feeds rows 2 and 3
+// Inclusive prefix sum over the 64 lanes (lane order); lanes with no source
+// in a DPP step add the 0 of the update's old value.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += dpp_u32<kDppRowShr + 1>(x);
+  x += dpp_u32<kDppRowShr + 2>(x);
+  x += dpp_u32<kDppRowShr + 4>(x);
+  x += dpp_u32<kDppRowShr + 8>(x);
+  x += dpp_u32<kDppRowBcast15, 0xA>(x);
+  x += dpp_u32<kDppRowBcast31, 0xC>(x);
+  return x;
+}
+
 // Max over groups of `width` consecutive lanes (16, 32 or 64).
 template <int width>
 __device__ __forceinline__ float group_max(float v) {

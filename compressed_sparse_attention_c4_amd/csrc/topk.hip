@@ -70,7 +70,7 @@ __device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t bin, bool
   uint64_t active = __ballot(valid);
   for (int it = 0; it < 8 && active; ++it) {
     const int leader = __ffsll((unsigned long long)active) - 1;
-    const uint32_t lb = __shfl(bin, leader, 64);
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
     const uint64_t same = __ballot(valid && bin == lb) & active;
     const uint32_t cnt = (uint32_t)__popcll(same);
     if (lane == leader) atomicAdd(&hist[lb], cnt);
@@ -90,14 +90,11 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int nbins, uin
   for (int q = 0; q < per; ++q) c += hist[nbins - 1 - per * threadIdx.x - q];
   // block exclusive scan of c in thread order (thread 0 = top bins)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = c;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  (void)lane;
+  (void)wave;
+  const uint32_t x = wave_inclusive_scan(c);
   uint32_t tot;
-  const uint32_t woff = wave_offsets(__shfl(x, 63, 64), scan_sh, tot);
+  const uint32_t woff = wave_offsets((uint32_t)__builtin_amdgcn_readlane((int)x, 63), scan_sh, tot);
   uint32_t above = woff + x - c;
   if (above < k && above + c >= k) {
     for (int q = 0; q < per; ++q) {
@@ -126,6 +123,7 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t red[2 * kWaves];
   __shared__ uint32_t sel_bin, sel_above;
+  __shared__ uint32_t s_thr, s_need;  // threshold of a short bucket
   __shared__ uint32_t s_cand[kCandCap];  // keys of the threshold bucket
 
   const int r = blockIdx.y;
@@ -146,6 +144,8 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
   const int E = (n + kThreads - 1) / kThreads;             // keys per lane (<= kMaxE)
   const int seg = wave * 64 * E;                           // first element of this wave
 
+  // the histogram is cleared while the keys are in flight
+  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
   // keys in LDS; an element's index is base + e, or (candidates) re-read at
   // emission, which touches only the <= 512 selected ones
   const int nv = n - seg - lane;  // element i of this lane exists iff i < E and 64*i < nv
@@ -184,16 +184,12 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
         kmax = max(kmax, k);
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-    }
+    kmin = wave_umin(kmin);
+    kmax = wave_umax(kmax);
     if (lane == 0) {
       red[wave] = kmin;
       red[kWaves + wave] = kmax;
     }
-    for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
     __syncthreads();
     kmin = 0xFFFFFFFFu;
     kmax = 0u;
@@ -231,6 +227,34 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
     }
     uint32_t low = 0;  // threshold's low bits, built from the top
     int width = bstar == 0u ? 0 : sh;
+    if (listed && nb <= (uint32_t)kThreads) {
+      // a short bucket: each listed key counts the keys above and equal to
+      // it; the key whose range of ranks covers k is the threshold (every
+      // thread holding that key writes the same values)
+      if (threadIdx.x < nb) {
+        const uint32_t c = s_cand[threadIdx.x];
+        uint32_t gt = 0, eq = 0;
+        int i = 0;
+        for (; i + 4 <= (int)nb; i += 4) {
+          const uint4 x = *reinterpret_cast<const uint4*>(&s_cand[i]);
+          gt += (x.x > c) + (x.y > c) + (x.z > c) + (x.w > c);
+          eq += (x.x == c) + (x.y == c) + (x.z == c) + (x.w == c);
+        }
+        for (; i < (int)nb; ++i) {
+          const uint32_t x = s_cand[i];
+          gt += x > c;
+          eq += x == c;
+        }
+        if (gt < k && k <= gt + eq) {
+          s_thr = c;
+          s_need = k - gt;
+        }
+      }
+      __syncthreads();
+      thr = s_thr;
+      need = s_need;
+      width = -1;  // done
+    }
     uint32_t got_mask = 0;  // bits of the low part fixed so far
     while (width > 0) {
       const int w = min(11, width);
@@ -259,8 +283,10 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
       got_mask |= dmask << shift;
       width -= w;
     }
-    thr = bstar == 0u ? 0u : kmin + ((bstar - 1u) << sh) + low;
-    need = k;
+    if (width == 0) {
+      thr = bstar == 0u ? 0u : kmin + ((bstar - 1u) << sh) + low;
+      need = k;
+    }
   }
 
   // ---- 4. ordered placement: pos = #(key > thr before) + min(#(key == thr before), need)
