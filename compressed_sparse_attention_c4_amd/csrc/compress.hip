@@ -11,7 +11,8 @@
 // 16-byte bf16 load per row) and RoPE dim 512+l, so every row is read with
 // coalesced loads and the FP8 store of the entry is one 8-byte store per lane.
 // The softmax over the block's rows runs online (running max and sum), so the
-// rows are read once even for ratio 128.
+// rows are read once even for ratio 128; they are loaded four at a time, all
+// four loads in flight together.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -63,6 +64,9 @@ compress_kernel(const void* __restrict__ x, const int32_t* __restrict__ cu_rows,
   if (kb >= last) return;
   const int64_t rbase = (int64_t)row0 + (int64_t)kb * ratio - s0;
 
+  // the entry's page is looked up now, beside the row loads, not after them
+  const int64_t slot = (int64_t)page_table[(int64_t)b * pt_stride + kb / page_size] * page_size +
+                       kb % page_size;
   float w[9];
 #pragma unroll
   for (int i = 0; i < 8; ++i) w[i] = gate_w[8 * lane + i];
@@ -73,28 +77,36 @@ compress_kernel(const void* __restrict__ x, const int32_t* __restrict__ cu_rows,
 #pragma unroll
   for (int i = 0; i < 9; ++i) acc[i] = 0.f;
 
-  for (int r = 0; r < ratio; ++r) {
-    float v[9];
-    load_row<kF32In>(x, rbase + r, v);
-    float d = 0.f;
+  // rows in batches of kRowBatch, all loads of a batch issued before any of
+  // its rows is used (rows past the block repeat its first row, unused)
+  constexpr int kRowBatch = 4;
+  for (int r0 = 0; r0 < ratio; r0 += kRowBatch) {
+    float v[kRowBatch][9];
 #pragma unroll
-    for (int i = 0; i < 9; ++i) d = fmaf(w[i], v[i], d);
-    const float g = wave_sum(d) + gate_b[r];
-    const float mn = fmaxf(m, g);
-    const float corr = expf(m - mn);  // exp(-inf) = 0 on the first row
-    const float p = expf(g - mn);
-    l = l * corr + p;
+    for (int u = 0; u < kRowBatch; ++u) load_row<kF32In>(x, rbase + (r0 + u < ratio ? r0 + u : 0), v[u]);
 #pragma unroll
-    for (int i = 0; i < 9; ++i) acc[i] = fmaf(p, v[i], acc[i] * corr);
-    m = mn;
+    for (int u = 0; u < kRowBatch; ++u) {
+      // rows past the block get gate -inf: weight 0, and the running max
+      // (finite from the block's first row on) is unchanged
+      const bool in = r0 + u < ratio;
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < 9; ++i) d = fmaf(w[i], v[u][i], d);
+      const float g = in ? wave_sum(d) + gate_b[in ? r0 + u : 0] : -INFINITY;
+      const float mn = fmaxf(m, g);
+      const float corr = expf(m - mn);  // exp(-inf) = 0 on the first row
+      const float p = expf(g - mn);
+      l = l * corr + p;
+#pragma unroll
+      for (int i = 0; i < 9; ++i) acc[i] = fmaf(p, v[u][i], acc[i] * corr);
+      m = mn;
+    }
   }
   const float inv = 1.0f / l;
   float c[9];
 #pragma unroll
   for (int i = 0; i < 9; ++i) c[i] = acc[i] * inv;
 
-  const int64_t slot = (int64_t)page_table[(int64_t)b * pt_stride + kb / page_size] * page_size +
-                       kb % page_size;
   if (kF32Out) {
     float* lat = reinterpret_cast<float*>(out_latent) + slot * kLatent + 8 * lane;
     *reinterpret_cast<float4*>(lat) = make_float4(c[0], c[1], c[2], c[3]);
