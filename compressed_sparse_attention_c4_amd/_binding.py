@@ -46,6 +46,9 @@ def _decl(name, args, res=C.c_int):
 
 _c4_compress = _decl("c4_compress", [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _KvPoolC, _vp])
 _csa_index_prep = _decl("csa_index_prep", [_vp, _i32, _i64, _i32, _u32, _i32, _vp, _vp, _vp, _vp])
+_decode_prep = _decl("csa_decode_prep", [_vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _KvPoolC,
+                                         _vp, _i32, _KvPoolC, _vp, _vp, _i32, _i32, _u32,
+                                         _IndexPoolC, _vp, _vp, _vp])
 _indexer_score = _decl("indexer_score", [_vp, _i32, _vp, _u32, _vp, _i32, _i32, _i32, _vp, _vp, _i32,
                                          _vp, _i32, _IndexPoolC, _vp, _i64, _vp, _vp, _vp, _sz, _vp])
 _topk = _decl("topk512_page_select", [_vp, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
@@ -153,6 +156,21 @@ def csa_index_prep(v, dim, flags, out_fmt, out, out_scale=None, dst_rows=None, s
     _check("csa_index_prep", _csa_index_prep(
         _ptr(v), _fmt_of(v), rows, int(dim), int(flags), int(out_fmt), _ptr(out), _ptr(out_scale),
         _ptr(dst_rows), _stream(stream)))
+
+
+def csa_decode_prep(x, pos, gate_w, gate_b, page_table, c4: KvPool, raw_page_table, raw: KvPool,
+                    k_rows=None, q_rows=None, kpool: IndexPool | None = None, q_out=None,
+                    q_out_scale=None, flags=CSA_PREP_HADAMARD, stream=None):
+    """x [B][ratio][576]; pos int32 [B]; k_rows [B][dim], q_rows [B][H_I][dim] (bf16 or f32)."""
+    B, ratio = x.shape[0], x.shape[1]
+    kq = k_rows if k_rows is not None else q_rows
+    H_I = q_rows.shape[1] if q_rows is not None else 0
+    kp = kpool.c() if kpool is not None else _IndexPoolC(None, None, CSA_F32, 128, c4.page_size, 0)
+    _check("csa_decode_prep", _decode_prep(
+        _ptr(x), _fmt_of(x), _ptr(pos), B, ratio, _ptr(gate_w), _ptr(gate_b), _ptr(page_table),
+        page_table.shape[-1], c4.c(), _ptr(raw_page_table), raw_page_table.shape[-1], raw.c(),
+        _ptr(k_rows), _ptr(q_rows), _fmt_of(kq) if kq is not None else CSA_BF16, H_I, int(flags),
+        kp, _ptr(q_out), _ptr(q_out_scale), _stream(stream)))
 
 
 def indexer_score(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPool, logits, *,

@@ -71,6 +71,41 @@ csa_status csa_index_prep(const void* v, csa_fmt v_fmt, int64_t rows, int32_t di
                                       dst_rows, stream));
 }
 
+csa_status csa_decode_prep(const void* x, csa_fmt x_fmt, const int32_t* pos, int32_t B,
+                           int32_t ratio, const float* gate_w, const float* gate_b,
+                           const int32_t* page_table, int32_t pt_stride, csa_kv_pool c4,
+                           const int32_t* raw_page_table, int32_t raw_pt_stride,
+                           csa_kv_pool raw, const void* k_rows, const void* q_rows,
+                           csa_fmt kq_fmt, int32_t H_I, uint32_t flags, csa_index_pool kpool,
+                           void* q_out, void* q_out_scale, hipStream_t stream) {
+  if (B < 0 || ratio < 1 || ratio > 128 || pt_stride <= 0 || raw_pt_stride <= 0 || H_I < 0)
+    return CSA_ERR_INVALID;
+  if (x_fmt != CSA_BF16 && x_fmt != CSA_F32) return CSA_ERR_INVALID;
+  if (!kv_pool_ok(c4) || !kv_pool_ok(raw) || c4.fmt != raw.fmt) return CSA_ERR_INVALID;
+  if (flags & ~(uint32_t)CSA_PREP_HADAMARD) return CSA_ERR_INVALID;
+  const bool kq = k_rows || q_rows;
+  if (kq) {
+    if (kq_fmt != CSA_BF16 && kq_fmt != CSA_F32) return CSA_ERR_INVALID;
+    if (kpool.dim != 64 && kpool.dim != 128) return CSA_ERR_INVALID;
+    if (kpool.fmt != CSA_F32 && kpool.fmt != CSA_FP8_E4M3 && kpool.fmt != CSA_MXFP4)
+      return CSA_ERR_INVALID;
+    if (kpool.fmt != CSA_F32 && !kpool.scale && k_rows) return CSA_ERR_INVALID;
+    if (k_rows && (!kpool.data || kpool.page_size != c4.page_size)) return CSA_ERR_INVALID;
+    if (q_rows && (!q_out || (kpool.fmt != CSA_F32 && !q_out_scale) || H_I == 0))
+      return CSA_ERR_INVALID;
+  }
+  if (B == 0) return CSA_OK;
+  if (!x || !pos || !gate_w || !gate_b || !page_table || !raw_page_table) return CSA_ERR_INVALID;
+  DecodePrepArgs a{};
+  a.x = x; a.x_fmt = x_fmt; a.pos = pos; a.B = B; a.ratio = ratio; a.gate_w = gate_w;
+  a.gate_b = gate_b; a.page_table = page_table; a.pt_stride = pt_stride; a.c4 = c4;
+  a.raw_page_table = raw_page_table; a.raw_pt_stride = raw_pt_stride; a.raw = raw;
+  a.k_rows = k_rows; a.q_rows = q_rows; a.kq_fmt = kq_fmt; a.H_I = H_I; a.flags = flags;
+  a.kpool = kpool; a.q_out = q_out; a.q_out_scale = q_out_scale;
+  if (!kq) a.kpool.dim = 128;  // sizes the (unused) row layout only
+  return hip_status(launch_decode_prep(a, stream));
+}
+
 csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint32_t prep,
                          const float* w, int32_t T, int32_t H_I, int32_t D_I,
                          const int32_t* row_seq, const int32_t* row_len, int32_t max_row_len,

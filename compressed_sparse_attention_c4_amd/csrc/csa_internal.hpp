@@ -14,6 +14,30 @@ hipError_t launch_compress(const void* x, int x_fmt, const int32_t* cu_rows,
                            const int32_t* page_table, int pt_stride, const csa_kv_pool& out,
                            hipStream_t s);
 
+struct DecodePrepArgs {
+  const void* x;  // [B][ratio][576]
+  int x_fmt;
+  const int32_t* pos;
+  int B, ratio;
+  const float* gate_w;
+  const float* gate_b;
+  const int32_t* page_table;  // c4 pool and index pool (same entries, same page size)
+  int pt_stride;
+  csa_kv_pool c4;
+  const int32_t* raw_page_table;
+  int raw_pt_stride;
+  csa_kv_pool raw;
+  const void* k_rows;  // [B][dim] or NULL
+  const void* q_rows;  // [B][H_I][dim] or NULL
+  int kq_fmt;
+  int H_I;
+  uint32_t flags;
+  csa_index_pool kpool;
+  void* q_out;
+  void* q_out_scale;
+};
+hipError_t launch_decode_prep(const DecodePrepArgs& a, hipStream_t s);
+
 hipError_t launch_index_prep(const void* v, int v_fmt, int64_t rows, int dim, uint32_t flags,
                              int out_fmt, void* out, void* out_scale, const int32_t* dst_rows,
                              hipStream_t s);

@@ -159,6 +159,40 @@ csa_status csa_index_prep(const void* v, csa_fmt v_fmt, int64_t rows, int32_t di
                           const int32_t* dst_rows, hipStream_t stream);
 
 /*
+ * csa_decode_prep -- every per-sequence write and the query preparation of one
+ * decode step, in one launch ([P1] §1: the new token updates the compressed
+ * cache, the raw window and the indexer's K cache before the indexer runs).
+ * For sequence b with p = pos[b], the raw position of its current token:
+ *   - if (p + 1) % ratio == 0 (the token completes block kb = (p+1)/ratio - 1),
+ *     rows x[b][0 .. ratio) (positions p+1-ratio .. p) are compressed exactly
+ *     as c4_compress does and stored at entry kb of c4, and, if k_rows is set,
+ *     k_rows[b] is prepared exactly as csa_index_prep does and stored at entry
+ *     kb of kpool;
+ *   - row x[b][ratio-1] (the token) is stored at position p of raw, exactly as
+ *     c4_compress with ratio 1 stores it;
+ *   - if q_rows is set, q_rows[b][h] (h < H_I) are prepared as csa_index_prep
+ *     does into q_out [B*H_I][...] and q_out_scale, in kpool.fmt.
+ *  x        [B][ratio][576], CSA_BF16 or CSA_F32; ratio in [1, 128].
+ *  pos      int32 [B].
+ *  gate_w   float[576]; gate_b float[ratio].
+ *  page_table int32 [B][pt_stride]: pages of c4 and of kpool (both page_size
+ *           entries per page: kpool.page_size must equal c4.page_size).
+ *  raw_page_table int32 [B][raw_pt_stride] over raw.page_size-token pages.
+ *  k_rows, q_rows  [B][dim] and [B][H_I][dim] in kq_fmt (CSA_BF16 / CSA_F32),
+ *           dim = kpool.dim; either may be NULL.
+ *  flags    0 or CSA_PREP_HADAMARD, for both k and q rows.
+ * c4 and raw must have the same format (FP8 or F32). Returns CSA_ERR_INVALID
+ * on a bad pointer, size or format, CSA_OK (nothing enqueued) when B == 0.
+ */
+csa_status csa_decode_prep(const void* x, csa_fmt x_fmt, const int32_t* pos, int32_t B,
+                           int32_t ratio, const float* gate_w, const float* gate_b,
+                           const int32_t* page_table, int32_t pt_stride, csa_kv_pool c4,
+                           const int32_t* raw_page_table, int32_t raw_pt_stride,
+                           csa_kv_pool raw, const void* k_rows, const void* q_rows,
+                           csa_fmt kq_fmt, int32_t H_I, uint32_t flags, csa_index_pool kpool,
+                           void* q_out, void* q_out_scale, hipStream_t stream);
+
+/*
  * indexer_score -- lightning-indexer logits of every visible compressed entry
  * ([P1] §3 C4Indexer, §3.2 `logits [bs, c4_seqlen]`; [P2] CSA paragraph: a light
  * low-precision indexer scores compressed blocks for each query):

@@ -30,7 +30,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("c4_compress", "csa_index_prep", "indexer_score", "topk512_page_select",
+    for n in ("c4_compress", "csa_index_prep", "csa_decode_prep", "indexer_score", "topk512_page_select",
               "csa_sparse_attn", "hca_dense_attn", "csa_workspace_size", "csa_status_string",
               "csa_version"):
         assert n in names
@@ -85,6 +85,34 @@ def test_compress_rejects_bad_arguments(lib):
     assert f(FAKE, 1, FAKE, FAKE, 1, 16, 4, FAKE, FAKE, FAKE, 4, bad_pool, None) == INVALID
     assert f(None, 1, FAKE, FAKE, 1, 16, 4, FAKE, FAKE, FAKE, 4, good, None) == INVALID      # null x
     assert f(FAKE, 1, FAKE, FAKE, 0, 16, 4, FAKE, FAKE, FAKE, 4, good, None) == 0            # B = 0: no-op
+
+
+def test_decode_prep_rejects_bad_arguments(lib):
+    f = lib.csa_decode_prep
+    f.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                  C.c_void_p, C.c_int32, KvPoolC, C.c_void_p, C.c_int32, KvPoolC, C.c_void_p,
+                  C.c_void_p, C.c_int32, C.c_int32, C.c_uint32, IndexPoolC, C.c_void_p,
+                  C.c_void_p, C.c_void_p]
+    c4 = KvPoolC(FAKE, FAKE, FAKE, 2, 64, 10)
+    raw = KvPoolC(FAKE, FAKE, FAKE, 2, 256, 10)
+    kp = IndexPoolC(FAKE, FAKE, 2, 128, 64, 10)
+
+    def call(x=FAKE, x_fmt=1, B=2, ratio=4, c4p=c4, rawp=raw, k=FAKE, q=FAKE, kq_fmt=1, H_I=64,
+             flags=1, kpool=kp, q_out=FAKE, q_sc=FAKE):
+        return f(x, x_fmt, FAKE, B, ratio, FAKE, FAKE, FAKE, 8, c4p, FAKE, 4, rawp, k, q, kq_fmt,
+                 H_I, flags, kpool, q_out, q_sc, None)
+
+    assert call(ratio=0) == INVALID
+    assert call(ratio=129) == INVALID
+    assert call(x_fmt=2) == INVALID                                    # x must be bf16 / f32
+    assert call(rawp=KvPoolC(FAKE, FAKE, FAKE, 0, 256, 10)) == INVALID  # c4 FP8, raw F32
+    assert call(flags=2) == INVALID                                    # only the Hadamard flag
+    assert call(kpool=IndexPoolC(FAKE, FAKE, 2, 96, 64, 10)) == INVALID  # dim 96
+    assert call(kpool=IndexPoolC(FAKE, FAKE, 2, 128, 32, 10)) == INVALID  # page size != c4's
+    assert call(q_out=None) == INVALID                                 # q rows without an output
+    assert call(kq_fmt=2) == INVALID                                   # k / q rows must be raw
+    assert call(x=None) == INVALID
+    assert call(B=0) == 0                                              # nothing to do
 
 
 def test_indexer_rejects_bad_arguments(lib):

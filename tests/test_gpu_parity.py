@@ -450,3 +450,80 @@ def test_indexer_many_rows_causal(csa, fmt):
         want = O.indexer_logits(qhat[t], w[t], pool.rows(O.page_slot(pt[row_seq[t]], np.arange(n), 64)))
         np.testing.assert_allclose(got[t, :n], want, rtol=0, atol=1e-4 * np.abs(want).max())
         assert np.all(np.isnan(got[t, n:])), f"row {t} wrote past row_len"
+
+
+# ------------------------------------------------------------------ fused decode preparation
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_decode_prep(csa, fmt):
+    """csa_decode_prep against the oracle: the block a token completes (and only
+    then) is compressed into the C4 pool and its index-K row prepared into the
+    index pool; the token is stored in the raw pool; the query rows are
+    prepared. Sequences whose token completes no block (L % 4 != 0, or p < 3)
+    leave both pools untouched."""
+    g = gen.rng(1300 + len(fmt))
+    lens = np.array([4096, 4099, 12, 3, 8192 + 256, 5], np.int64)
+    B, ratio, H_I = len(lens), 4, 64
+    pos = (lens - 1).astype(np.int32)
+    pps = int(max((L + 255) // 256 for L in lens))
+    P = B * pps + 3
+    pt = gen.page_table(g, B, pps, P)
+    w, b = gen.gate_params(g, ratio)
+    x, xh = _bf16(gen.normal(g, (B, ratio, 576)))
+    k, kh = _bf16(gen.normal(g, (B, 128)))
+    q, qh = _bf16(gen.normal(g, (B, H_I, 128)))
+    kfmt = csa.CSA_FP8_E4M3 if fmt == "fp8" else csa.CSA_MXFP4
+    c4 = csa.alloc_kv_pool(P, 64, csa.CSA_FP8_E4M3)
+    raw = csa.alloc_kv_pool(P, 256, csa.CSA_FP8_E4M3)
+    kpool = csa.alloc_index_pool(P, 64, 128, kfmt)
+    if fmt == "fp8":
+        q_out = torch.empty((B, H_I, 128), dtype=torch.uint8, device=DEV)
+        q_sc = torch.empty((B, H_I), dtype=torch.float32, device=DEV)
+    else:
+        q_out = torch.empty((B, H_I, 64), dtype=torch.uint8, device=DEV)
+        q_sc = torch.empty((B, H_I, 4), dtype=torch.uint8, device=DEV)
+    csa.csa_decode_prep(x, t_dev(pos), t_dev(w), t_dev(b), t_dev(pt), c4, t_dev(pt), raw,
+                        k_rows=k, q_rows=q, kpool=kpool, q_out=q_out, q_out_scale=q_sc)
+    torch.cuda.synchronize()
+    lat = c4.latent.cpu().numpy().reshape(-1, 512)
+    sc = c4.scale.cpu().numpy().reshape(-1)
+    rope = c4.rope.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1, 64)
+    kd = kpool.data.cpu().numpy().reshape(P * 64, -1)
+    ks = kpool.scale.cpu().numpy().reshape(P * 64, -1)
+    written = np.zeros(P * 64, bool)
+    for s in range(B):
+        L = int(lens[s])
+        if L % ratio or L < ratio:
+            continue
+        kb = L // ratio - 1
+        slot = int(O.page_slot(pt[s], kb, 64))
+        written[slot] = True
+        c = O.compress_blocks(xh[s], L - ratio, ratio, w, b)
+        oc, osc, orope = O.quant_kv_entries(c, "fp8")
+        np.testing.assert_allclose(sc[slot], osc[0], rtol=3e-6)
+        ok, _ = fp8_codes_match(lat[slot][None], oc, c[:, :512].astype(np.float32) / osc[:, None],
+                                rel=2e-5)
+        assert ok, f"sequence {s}: compressed latent differs"
+        gr, orr = O.bf16_decode(rope[slot]), O.bf16_decode(orope[0])
+        assert np.all(np.abs(gr - orr) <= 2.0 ** -7 * np.abs(orr) + 1e-5)
+        codes, scale = O.index_prep(kh[s:s + 1], True, fmt)
+        assert np.array_equal(kd[slot], codes[0].reshape(-1)), f"sequence {s}: index-K row differs"
+        assert np.array_equal(ks[slot].view(np.uint8), np.asarray(scale[0]).reshape(-1).view(np.uint8))
+    # nothing else of either pool was written (poison bytes 0xFF remain)
+    assert np.all(lat[~written] == 0xFF) and np.all(kd[~written] == 0xFF)
+    # the token of every sequence, in the raw pool
+    rl = raw.latent.cpu().numpy().reshape(-1, 512)
+    rs = raw.scale.cpu().numpy().reshape(-1)
+    rr = raw.rope.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1, 64)
+    for s in range(B):
+        p = int(pos[s])
+        slot = int(O.page_slot(pt[s], p, 256))
+        oc, osc, orope = O.quant_kv_entries(xh[s, ratio - 1:ratio], "fp8")
+        assert rs[slot] == np.float32(osc[0])
+        assert np.array_equal(rl[slot], oc[0]) and np.array_equal(rr[slot], orope[0])
+    # the prepared query rows
+    codes, scale = O.index_prep(qh.reshape(-1, 128), True, fmt)
+    assert np.array_equal(q_out.cpu().numpy().reshape(B * H_I, -1), codes.reshape(B * H_I, -1))
+    assert np.array_equal(q_sc.cpu().numpy().reshape(B * H_I, -1).view(np.uint8),
+                          np.asarray(scale).reshape(B * H_I, -1).view(np.uint8))

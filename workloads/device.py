@@ -66,7 +66,7 @@ class CsaDecode:
     (the current token is the last raw token, p = L - 1)."""
 
     def __init__(self, wl: Workload, lens, copies: int = 3, pool_pages: int | None = None,
-                 seed_offset: int = 0, with_compress: bool = True, parallel_writes: bool = False):
+                 seed_offset: int = 0, with_compress: bool = True):
         self.wl = wl
         self.B = B = len(lens)
         self.lens = np.asarray(lens, dtype=np.int64)
@@ -108,20 +108,9 @@ class CsaDecode:
         # step inputs
         gw, gb = gen.gate_params(g, 4)
         self.gate_w, self.gate_b = torch.from_numpy(gw).to(DEV), torch.from_numpy(gb).to(DEV)
-        self.zero_w, self.zero_b = w0, b0  # ratio-1 store of the raw token
         self.with_compress = with_compress
-        self.x_new = gen.device_normal((B * 4, 576), seed + 4)          # last block's raw rows
-        self.x_tok = self.x_new.view(B, 4, 576)[:, 3].contiguous()      # the current token
-        self.cu_new = _i32(np.arange(0, 4 * B + 1, 4))
-        self.start_new = _i32(self.lens - 4)
-        self.cu_tok = _i32(np.arange(B + 1))
-        self.start_tok = _i32(self.lens - 1)
-        self.k_new = gen.device_normal((B, wl.index_dim), seed + 5)
-        # the current token completes block N-1 only when L % 4 == 0; the
-        # compressor skips the partial block and the index-K row is not stored
-        last = self.N - 1
-        dst = pt[np.arange(B), last // C4_PAGE] * C4_PAGE + last % C4_PAGE
-        self.k_dst = _i32(np.where(self.lens % 4 == 0, dst, -1))
+        self.x_new = gen.device_normal((B * 4, 576), seed + 4)  # the last 4 raw rows (token last)
+        self.k_new = gen.device_normal((B, wl.index_dim), seed + 5)  # index-K row of that block
         self.q_idx = gen.device_normal((B, wl.index_heads, wl.index_dim), seed + 6)
         self.w_idx = gen.device_uniform((B, wl.index_heads), seed + 7)
         self.q_attn = gen.device_normal((B, self.H, 576), seed + 8)
@@ -143,12 +132,6 @@ class CsaDecode:
         self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         n = csa.csa_workspace_size(csa.CSA_OP_TOPK, B, self.maxN, 1)
         self.topk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
-        # parallel_writes: the KV writes of the step (compressed block, raw
-        # token) do not feed the indexer and may run on a second stream
-        # (default priority), joined before attention. Measured on MI355X, the
-        # two-branch graph is slower (113 vs 102 us per 128K step): the
-        # cross-queue join costs more than the overlap saves. Off by default.
-        self.side = torch.cuda.Stream() if parallel_writes else None
         torch.cuda.synchronize()
 
     # algorithmic bytes of one indexer launch: index-K rows + prepared q +
@@ -166,31 +149,24 @@ class CsaDecode:
         ent = 644
         att = self.B * (512 + self.wl.window) * ent + self.q_attn.numel() * 2 + self.out.numel() * 2
         topk = int(self.N.sum()) * 4 + self.B * 512 * 4
-        comp = self.x_new.numel() * 2 + self.B * ent + self.x_tok.numel() * 2 + self.B * ent
+        comp = self.x_new.numel() * 2 + self.B * ent + self.B * ent  # rows read, entry + token stored
         prep = self.k_new.numel() * 2 + self.q_idx.numel() * 2 + self.B * 132 * (1 + self.wl.index_heads)
         return self.indexer_bytes() + topk + att + comp + prep
 
     def step(self, c: int, ev=None):
         idx, kv = self.index_pools[c], self.c4_pools[c]
         wl = self.wl
-        main = torch.cuda.current_stream()
         if self.with_compress:
-            # the current token completes block N-1 (when L % 4 == 0): compress
-            # it and append the token to the raw window pool (second stream),
-            # prepare its index-K row (this stream: the indexer reads it)
-            side = self.side or main
-            side.wait_stream(main)
-            with torch.cuda.stream(side):
-                csa.c4_compress(self.x_new, self.cu_new, self.start_new, 4, 4, self.gate_w,
-                                self.gate_b, self.pt, kv)
-                csa.c4_compress(self.x_tok, self.cu_tok, self.start_tok, 1, 1, self.zero_w,
-                                self.zero_b, self.pt, self.raw)
-            kd = idx.data.view(-1, idx.data.shape[-1])
-            ks = idx.scale.view(kd.shape[0], -1)
-            csa.csa_index_prep(self.k_new, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt, kd, ks,
-                               self.k_dst)
-        csa.csa_index_prep(self.q_idx, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt, self.q_codes,
-                           self.q_scale)
+            # the current token: compress the block it completes (L % 4 == 0),
+            # append it to the raw window pool, prepare that block's index-K
+            # row, and prepare the queries -- one launch
+            csa.csa_decode_prep(self.x_new.view(self.B, 4, 576), self.q_pos, self.gate_w,
+                                self.gate_b, self.pt, kv, self.pt, self.raw, k_rows=self.k_new,
+                                q_rows=self.q_idx, kpool=idx, q_out=self.q_codes,
+                                q_out_scale=self.q_scale, flags=csa.CSA_PREP_HADAMARD)
+        else:
+            csa.csa_index_prep(self.q_idx, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt,
+                               self.q_codes, self.q_scale)
         if ev is not None:
             ev[0].record()
         csa.indexer_score(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.maxN, self.pt,
@@ -199,8 +175,6 @@ class CsaDecode:
             ev[1].record()
         csa.topk512_page_select(self.logits, self.row_len, self.row_seq, self.pt, self.phys,
                                 ws=self.topk_ws)
-        if self.with_compress and self.side is not None:
-            main.wait_stream(self.side)
         csa.csa_sparse_attn(self.q_attn, self.row_seq, self.q_pos, self.phys, kv, self.raw, self.pt,
                             wl.window, wl.softmax_scale, self.out, ws=self.attn_ws)
 
