@@ -6,9 +6,10 @@
 // Order: larger logit first, equal logits by lower index; -0 equals +0; NaN
 // ranks below -inf. Keys are the order-preserving uint32 image of the float.
 //
-// A 1024-thread workgroup holds up to 32768 keys of a row in LDS (wave w owns a
-// contiguous segment, lane-interleaved so every load is coalesced), so the row
-// is read from memory once. Selection is a radix select, never a sort:
+// A 1024-thread workgroup holds up to 32768 keys of a row in registers (up to
+// 32 per lane; wave w owns a contiguous segment, lane-interleaved so every load
+// is coalesced), so the row is read from memory once and every pass below is
+// register and LDS work. Selection is a radix select, never a sort:
 //   1. the key range [kmin, kmax] of the row is found; keys are binned by
 //      (key - kmin) >> sh into at most 2048 buckets (monotone in the key), so
 //      logits that crowd into a narrow range still spread over the buckets;
@@ -20,13 +21,15 @@
 //   4. one ordered pass places every selected entry at
 //      #(key > thr before it) + min(#(key == thr before it), need), using
 //      wavefront ballots and one workgroup scan, which yields ascending index
-//      order directly.
+//      order directly; the entries are parked in LDS by position and written
+//      out (index and page lookups included) one position per thread.
 // Longer rows (and long rows in small batches, to spread the work over more
 // CUs) run in two launches: chunks of the row are reduced to their own top-512
 // (key, index) in index order, then the candidates of all chunks are reduced
 // again. Any entry of the row's top-512 is in its chunk's top-512, so the
 // result is exact.
 #include <limits.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -36,23 +39,24 @@
 namespace csa {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 1024;             // workgroup of whole rows and of the final merge
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxE = 32;                    // keys per lane (held in LDS)
+constexpr int kMaxE = 32;                    // keys per lane (held in registers)
 constexpr int kRegRow = kThreads * kMaxE;    // longest row selected in one launch
-constexpr int kBins = 3072;                  // >= 2049 buckets, multiple of kThreads
+constexpr int kBins = 3072;                  // >= 2049 buckets, multiple of every workgroup size
 constexpr int kCandCap = 2048;               // threshold-bucket keys listed in LDS
 
 enum Mode { kRowFinal = 0, kChunkCand = 1, kCandFinal = 2 };
 
 // Exclusive scan of one uint32 per wave (value taken from lane 0 of each
-// wave) over the workgroup's 16 waves; returns this wave's offset, sets total.
+// wave) over the workgroup's TH/64 waves; returns this wave's offset, sets total.
+template <int TH>
 __device__ __forceinline__ uint32_t wave_offsets(uint32_t v, uint32_t* sh, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) sh[wave] = v;
   __syncthreads();
   uint32_t off = 0, tot = 0;
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < TH / 64; ++w) {
     const uint32_t x = sh[w];
     off += (w < wave) ? x : 0u;
     tot += x;
@@ -82,10 +86,11 @@ __device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t bin, bool
 
 // Bucket (scanning from the top of hist[0..nbins)) where the running count
 // reaches k; *sel_bin = bucket, *sel_above = count strictly above it.
+template <int TH>
 __device__ __forceinline__ void find_bucket(const uint32_t* hist, int nbins, uint32_t k,
                                             uint32_t* scan_sh, uint32_t* sel_bin,
                                             uint32_t* sel_above) {
-  const int per = nbins / kThreads;
+  const int per = nbins / TH;
   uint32_t c = 0;
   for (int q = 0; q < per; ++q) c += hist[nbins - 1 - per * threadIdx.x - q];
   // block exclusive scan of c in thread order (thread 0 = top bins)
@@ -94,7 +99,8 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int nbins, uin
   (void)wave;
   const uint32_t x = wave_inclusive_scan(c);
   uint32_t tot;
-  const uint32_t woff = wave_offsets((uint32_t)__builtin_amdgcn_readlane((int)x, 63), scan_sh, tot);
+  const uint32_t woff =
+      wave_offsets<TH>((uint32_t)__builtin_amdgcn_readlane((int)x, 63), scan_sh, tot);
   uint32_t above = woff + x - c;
   if (above < k && above + c >= k) {
     for (int q = 0; q < per; ++q) {
@@ -111,20 +117,22 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int nbins, uin
   __syncthreads();
 }
 
-template <int kMode>
-__global__ void __launch_bounds__(kThreads)
+template <int kMode, int kE, int TH>
+__global__ void __launch_bounds__(TH)
 topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __restrict__ ckeys,
             const int32_t* __restrict__ cjs, int ncand, int chunk,
             const int32_t* __restrict__ row_len, const int32_t* __restrict__ row_seq,
             const int32_t* __restrict__ pt, int pt_stride, int c4_page_size,
             int32_t* __restrict__ phys_idx, int32_t* __restrict__ logical_idx,
             uint32_t* __restrict__ okeys, int32_t* __restrict__ ojs) {
-  __shared__ uint32_t skey[kRegRow];
+  static_assert(kE >= 1 && kE <= kMaxE, "keys per lane");
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t red[2 * kWaves];
   __shared__ uint32_t sel_bin, sel_above;
-  __shared__ uint32_t s_thr, s_need;  // threshold of a short bucket
+  __shared__ uint32_t s_thr, s_need;     // threshold of a short bucket
   __shared__ uint32_t s_cand[kCandCap];  // keys of the threshold bucket
+  __shared__ int32_t s_out_e[kTopK];     // element placed at each output position
+  __shared__ uint32_t s_out_k[kTopK];    // and its key
 
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -141,47 +149,40 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
     n = ncand;
   }
   const int K = min(kTopK, kMode == kCandFinal ? rl : n);  // entries to select
-  const int E = (n + kThreads - 1) / kThreads;             // keys per lane (<= kMaxE)
-  const int seg = wave * 64 * E;                           // first element of this wave
+  const int seg = wave * 64 * kE;                          // first element of this wave
 
   // the histogram is cleared while the keys are in flight
-  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
-  // keys in LDS; an element's index is base + e, or (candidates) re-read at
-  // emission, which touches only the <= 512 selected ones
-  const int nv = n - seg - lane;  // element i of this lane exists iff i < E and 64*i < nv
+  for (int i = threadIdx.x; i < kBins; i += TH) hist[i] = 0u;
+  // Keys stay in registers: element seg + 64 i + lane is key kr[i] of this
+  // lane (coalesced loads, all issued at once). An element's index is
+  // base + e, or (candidates) re-read at emission, which touches only the
+  // selected ones. Absent elements (e >= n) read element 0 of the row and
+  // take key 0, the key of NaN: they sort below every present element
+  // (present NaNs come first by index), and K <= n, so none is ever selected
+  // and no pass needs a separate validity mask.
+  const int nv = n - seg - lane;  // element i of this lane exists iff 64*i < nv
+  uint32_t kr[kE];
   {
-    // batches of 8 unconditional loads (absent elements read element 0 of the
-    // row and are dropped), so 8 loads per lane are in flight at once
     const float* lrow = logits + (int64_t)r * ld + base;
     const uint32_t* crow = ckeys + (int64_t)r * ncand;
-    for (int i0 = 0; i0 < E; i0 += 8) {
-      uint32_t kk[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u;
-        const bool ok = i < E && 64 * i < nv;
-        const int e = ok ? seg + 64 * i + lane : 0;
-        const uint32_t k = kMode == kCandFinal ? crow[e] : float_key(lrow[e]);
-        kk[u] = ok ? k : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (i0 + u < E) skey[seg + 64 * (i0 + u) + lane] = kk[u];
+    for (int i = 0; i < kE; ++i) {
+      const bool ok = 64 * i < nv;
+      const int e = ok ? seg + 64 * i + lane : 0;
+      const uint32_t k = kMode == kCandFinal ? crow[e] : float_key(lrow[e]);
+      kr[i] = ok ? k : 0u;
     }
   }
-  auto valid_at = [&](int i) { return i < E && 64 * i < nv; };
-  auto key_at = [&](int i) { return skey[seg + 64 * i + lane]; };
-
   uint32_t thr = 0, need = 0;
   const bool take_all = n <= K;  // every element is selected
   if (!take_all) {
     // ---- 1. key range of the non-NaN keys
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for (int i = 0; i < E; ++i) {
-      const uint32_t k = key_at(i);
-      if (valid_at(i) && k != 0u) {
-        kmin = min(kmin, k);
-        kmax = max(kmax, k);
+#pragma unroll
+    for (int i = 0; i < kE; ++i) {
+      if (kr[i] != 0u) {
+        kmin = min(kmin, kr[i]);
+        kmax = max(kmax, kr[i]);
       }
     }
     kmin = wave_umin(kmin);
@@ -193,7 +194,7 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
     __syncthreads();
     kmin = 0xFFFFFFFFu;
     kmax = 0u;
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < TH / 64; ++w) {
       kmin = min(kmin, red[w]);
       kmax = max(kmax, red[kWaves + w]);
     }
@@ -203,31 +204,31 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
     auto bin_of = [&](uint32_t k) -> uint32_t { return k == 0u ? 0u : 1u + ((k - kmin) >> sh); };
 
     // ---- 2. bucket of the K-th largest key
-    for (int i = 0; i < E; ++i)
-      if (valid_at(i)) atomicAdd(&hist[bin_of(key_at(i))], 1u);
+#pragma unroll
+    for (int i = 0; i < kE; ++i) atomicAdd(&hist[bin_of(kr[i])], 1u);
     __syncthreads();
-    find_bucket(hist, kBins, (uint32_t)K, red, &sel_bin, &sel_above);
+    find_bucket<TH>(hist, kBins, (uint32_t)K, red, &sel_bin, &sel_above);
     const uint32_t bstar = sel_bin;
     uint32_t k = (uint32_t)K - sel_above;
 
     // ---- 3. exact threshold inside the bucket (its keys share everything
-    // above the low sh bits of key - kmin; NaN bucket 0 holds only key 0).
-    // The bucket's members are gathered into a short LDS list when they fit.
+    // above the low sh bits of key - kmin; bucket 0 holds only key 0, so it
+    // needs no refinement). The bucket's members are gathered into a short
+    // LDS list when they fit.
     const uint32_t nb = hist[bstar];
-    const bool listed = nb <= (uint32_t)kCandCap;
+    const bool listed = bstar != 0u && nb <= (uint32_t)kCandCap;
     __syncthreads();
     if (listed) {
       if (threadIdx.x == 0) sel_above = 0;  // reused as the list length
       __syncthreads();
-      for (int i = 0; i < E; ++i) {
-        const uint32_t kk = key_at(i);
-        if (valid_at(i) && bin_of(kk) == bstar) s_cand[atomicAdd(&sel_above, 1u)] = kk;
-      }
+#pragma unroll
+      for (int i = 0; i < kE; ++i)
+        if (bin_of(kr[i]) == bstar) s_cand[atomicAdd(&sel_above, 1u)] = kr[i];
       __syncthreads();
     }
     uint32_t low = 0;  // threshold's low bits, built from the top
     int width = bstar == 0u ? 0 : sh;
-    if (listed && nb <= (uint32_t)kThreads) {
+    if (listed && nb <= (uint32_t)TH) {
       // a short bucket: each listed key counts the keys above and equal to
       // it; the key whose range of ranks covers k is the threshold (every
       // thread holding that key writes the same values)
@@ -261,23 +262,24 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
       const int shift = width - w;
       const uint32_t dmask = (1u << w) - 1u;
       __syncthreads();
-      for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
+      for (int i = threadIdx.x; i < kBins; i += TH) hist[i] = 0u;
       __syncthreads();
       if (listed) {
-        for (int i = threadIdx.x; i < (int)nb; i += kThreads) {
+        for (int i = threadIdx.x; i < (int)nb; i += TH) {
           const uint32_t lo = (s_cand[i] - kmin) & ((1u << sh) - 1u);  // sh <= 21
           if ((lo & got_mask) == low) atomicAdd(&hist[(lo >> shift) & dmask], 1u);
         }
       } else {
-        for (int i = 0; i < E; ++i) {
-          const uint32_t kk = key_at(i);
+#pragma unroll
+        for (int i = 0; i < kE; ++i) {
+          const uint32_t kk = kr[i];
           const uint32_t lo = (kk - kmin) & ((1u << sh) - 1u);
-          const bool in = valid_at(i) && kk != 0u && bin_of(kk) == bstar && (lo & got_mask) == low;
+          const bool in = kk != 0u && bin_of(kk) == bstar && (lo & got_mask) == low;
           wave_hist_add(hist, (lo >> shift) & dmask, in);
         }
       }
       __syncthreads();
-      find_bucket(hist, kBins, k, red, &sel_bin, &sel_above);
+      find_bucket<TH>(hist, kBins, k, red, &sel_bin, &sel_above);
       k -= sel_above;
       low |= sel_bin << shift;
       got_mask |= dmask << shift;
@@ -289,74 +291,145 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
     }
   }
 
-  // ---- 4. ordered placement: pos = #(key > thr before) + min(#(key == thr before), need)
+  // ---- 4. ordered placement: pos = #(key > thr before) + min(#(key == thr before), need).
+  // Taking every present element is thr = 0 (NaN) with need = the present
+  // NaNs, which come before the absent elements. Positions are settled from
+  // ballots over the registers; the selected elements are parked in LDS by
+  // position and emitted afterwards, one output position per thread, so the
+  // index and page-table reads of all 512 run in parallel.
   uint32_t gt_w = 0, eq_w = 0;
-  for (int i = 0; i < E; ++i) {
-    const bool v = valid_at(i);
-    const uint32_t k = key_at(i);
-    gt_w += (uint32_t)__popcll(__ballot(v && (take_all || k > thr)));
-    eq_w += (uint32_t)__popcll(__ballot(v && !take_all && k == thr));
+#pragma unroll
+  for (int i = 0; i < kE; ++i) {
+    gt_w += (uint32_t)__popcll(__ballot(kr[i] > thr));
+    eq_w += (uint32_t)__popcll(__ballot(kr[i] == thr));
   }
   uint32_t tot;
-  const uint32_t off = wave_offsets(gt_w | (eq_w << 16), red, tot);
+  const uint32_t off = wave_offsets<TH>(gt_w | (eq_w << 16), red, tot);
+  if (take_all) need = (uint32_t)n - (tot & 0xFFFFu);
   uint32_t g = off & 0xFFFFu, q = off >> 16;
   const uint64_t lt = (1ull << lane) - 1ull;
-  for (int i = 0; i < E; ++i) {
-    const bool v = valid_at(i);
-    const uint32_t k = key_at(i);
-    const bool isgt = v && (take_all || k > thr);
-    const bool iseq = v && !take_all && k == thr;
+  // the lane index again, by a route the compiler cannot match to the one the
+  // loads used, so it does not keep kE element indices live in between
+  const int lane_b = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+#pragma unroll
+  for (int i = 0; i < kE; ++i) {
+    const bool isgt = kr[i] > thr;
+    const bool iseq = kr[i] == thr;
     const uint64_t bg = __ballot(isgt), be = __ballot(iseq);
     const uint32_t gb = g + (uint32_t)__popcll(bg & lt);
     const uint32_t qb = q + (uint32_t)__popcll(be & lt);
     if (isgt || (iseq && qb < need)) {
       const uint32_t pos = gb + min(qb, need);
-      const int e = seg + 64 * i + lane;
-      const int j = kMode == kCandFinal ? cjs[(int64_t)r * ncand + e] : base + e;
-      if (kMode == kChunkCand) {
-        const int64_t o = ((int64_t)r * gridDim.x + blockIdx.x) * kTopK + pos;
-        okeys[o] = k;
-        ojs[o] = j;
-      } else {
-        phys_idx[(int64_t)r * kTopK + pos] =
-            (int32_t)((int64_t)pt[(int64_t)row_seq[r] * pt_stride + j / c4_page_size] * c4_page_size +
-                      j % c4_page_size);
-        if (logical_idx) logical_idx[(int64_t)r * kTopK + pos] = j;
-      }
+      s_out_e[pos] = seg + 64 * i + lane_b;
+      s_out_k[pos] = kr[i];
     }
     g += (uint32_t)__popcll(bg);
     q += (uint32_t)__popcll(be);
   }
-  // ---- padding
-  for (int i = K + threadIdx.x; i < kTopK; i += kThreads) {
+  __syncthreads();
+  // ---- emission (positions K..511 are padding)
+  for (int p = threadIdx.x; p < kTopK; p += TH) {
     if (kMode == kChunkCand) {
-      const int64_t o = ((int64_t)r * gridDim.x + blockIdx.x) * kTopK + i;
-      okeys[o] = 0u;
-      ojs[o] = INT_MAX;
+      const int64_t o = ((int64_t)r * gridDim.x + blockIdx.x) * kTopK + p;
+      okeys[o] = p < K ? s_out_k[p] : 0u;
+      ojs[o] = p < K ? base + s_out_e[p] : INT_MAX;
     } else {
-      phys_idx[(int64_t)r * kTopK + i] = -1;
-      if (logical_idx) logical_idx[(int64_t)r * kTopK + i] = -1;
+      int32_t phys = -1, j = -1;
+      if (p < K) {
+        const int e = s_out_e[p];
+        j = kMode == kCandFinal ? cjs[(int64_t)r * ncand + e] : e;
+        phys = (int32_t)((int64_t)pt[(int64_t)row_seq[r] * pt_stride + j / c4_page_size] *
+                             c4_page_size +
+                         j % c4_page_size);
+      }
+      phys_idx[(int64_t)r * kTopK + p] = phys;
+      if (logical_idx) logical_idx[(int64_t)r * kTopK + p] = j;
     }
   }
 }
 
-int chunks_for(int64_t R, int64_t ld) {
-  // enough chunks to put >= ~128 workgroups on the GPU, each within kRegRow
-  int64_t want = (128 + R - 1) / R;
-  int64_t c = (ld + want - 1) / want;
-  c = std::max<int64_t>(c, 4096);
-  c = std::min<int64_t>(c, kRegRow);
+// keys per lane for n elements over th threads: the next power of two >= n / th
+int keys_per_lane(int64_t n, int th) {
+  int e = 1;
+  while ((int64_t)e * th < n) e *= 2;
+  return e;
+}
+
+template <int kMode>
+void launch_mode(int th, int e, dim3 grid, hipStream_t s, const float* logits, int64_t ld,
+                 const uint32_t* ckeys, const int32_t* cjs, int ncand, int chunk,
+                 const int32_t* row_len, const int32_t* row_seq, const int32_t* pt, int pt_stride,
+                 int c4_page_size, int32_t* phys_idx, int32_t* logical_idx, uint32_t* okeys,
+                 int32_t* ojs) {
+#define CSA_TOPK(E, TH)                                                                         \
+  hipLaunchKernelGGL((topk_kernel<kMode, E, TH>), grid, dim3(TH), 0, s, logits, ld, ckeys, cjs, \
+                     ncand, chunk, row_len, row_seq, pt, pt_stride, c4_page_size, phys_idx,      \
+                     logical_idx, okeys, ojs)
+#define CSA_TOPK_E(TH)             \
+  switch (e) {                     \
+    case 1: CSA_TOPK(1, TH); break;   \
+    case 2: CSA_TOPK(2, TH); break;   \
+    case 4: CSA_TOPK(4, TH); break;   \
+    case 8: CSA_TOPK(8, TH); break;   \
+    case 16: CSA_TOPK(16, TH); break; \
+    default: CSA_TOPK(32, TH); break; \
+  }
+  if (th == 256) {
+    CSA_TOPK_E(256)
+  } else {
+    CSA_TOPK_E(1024)
+  }
+#undef CSA_TOPK_E
+#undef CSA_TOPK
+}
+
+// How one launch_topk call splits its rows. Every workgroup holds at most 32
+// keys per lane (16 preferred: 32 costs spills at 1024 threads).
+//  - Whole rows, one 1024-thread workgroup each, when a row fits 16 keys per
+//    lane and either the rows alone fill the GPU (>= 128) or they are short.
+//  - Otherwise chunks of a row are reduced to their top-512 candidates and the
+//    candidates of a row are reduced again. With >= 128 rows the rows already
+//    fill the GPU: chunks of 256 x 16 keys go to 256-thread workgroups, several
+//    of which share a CU, so one workgroup's barrier waits overlap another's
+//    work. With fewer rows, ~128 workgroups of 1024 threads, each >= 4096 keys.
+//  - At most 64 chunks per row, so a row's candidates fit one final workgroup.
+struct TopkPlan {
+  bool whole_rows;
+  int chunks, chunk, chunk_th, final_th;
+};
+
+TopkPlan topk_plan(int64_t R, int64_t ld) {
+  TopkPlan p{false, 1, (int)ld, kThreads, kThreads};
+  if (ld <= kRegRow / 2 && (R >= 128 || ld <= 8192)) {
+    p.whole_rows = true;
+    return p;
+  }
+  int64_t c;
+  if (R >= 128) {
+    int ke = 16;
+    if (const char* v = getenv("CSA_TUNE_TOPK_KE")) ke = std::min(32, std::max(1, atoi(v)));
+    c = 256 * (int64_t)ke;
+  } else {
+    const int64_t want = (128 + R - 1) / R;
+    c = std::max<int64_t>((ld + want - 1) / want, 4096);
+    c = std::min<int64_t>(c, kRegRow / 2);
+  }
   int64_t chunks = (ld + c - 1) / c;
-  if (chunks * kTopK > kRegRow) chunks = kRegRow / kTopK;  // candidates must fit one launch
-  return (int)chunks;
+  if (chunks * kTopK > kRegRow) chunks = kRegRow / kTopK;
+  c = (ld + chunks - 1) / chunks;
+  p.chunks = (int)((ld + c - 1) / c);
+  p.chunk = (int)c;
+  p.chunk_th = (R >= 128 && c <= 256 * kMaxE) ? 256 : kThreads;
+  p.final_th = (R >= 128 && (int64_t)p.chunks * kTopK <= 256 * kMaxE) ? 256 : kThreads;
+  return p;
 }
 
 }  // namespace
 
 size_t topk_ws_bytes(int64_t R, int64_t max_len) {
-  if (max_len <= kRegRow && (R >= 128 || max_len <= 8192)) return 0;
-  const int chunks = chunks_for(R, max_len);
-  return (size_t)R * chunks * kTopK * (sizeof(uint32_t) + sizeof(int32_t));
+  const TopkPlan p = topk_plan(R, max_len);
+  if (p.whole_rows) return 0;
+  return (size_t)R * p.chunks * kTopK * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
 int64_t topk_max_len() { return (int64_t)(kRegRow / kTopK) * kRegRow; }
@@ -367,24 +440,24 @@ hipError_t launch_topk(const float* logits, int64_t ld, int R, const int32_t* ro
                        int32_t* logical_idx, void* ws, hipStream_t s) {
   (void)max_row_len;
   if (R == 0) return hipSuccess;
-  if (ld <= kRegRow && (R >= 128 || ld <= 8192)) {
-    hipLaunchKernelGGL(topk_kernel<kRowFinal>, dim3(1, R), dim3(kThreads), 0, s, logits, ld,
-                       nullptr, nullptr, 0, 0, row_len, row_seq, page_table, pt_stride,
-                       c4_page_size, phys_idx, logical_idx, nullptr, nullptr);
+  const TopkPlan p = topk_plan(R, ld);
+  if (p.whole_rows) {
+    launch_mode<kRowFinal>(kThreads, keys_per_lane(ld, kThreads), dim3(1, R), s, logits, ld,
+                           nullptr, nullptr, 0, 0, row_len, row_seq, page_table, pt_stride,
+                           c4_page_size, phys_idx, logical_idx, nullptr, nullptr);
     return hipGetLastError();
   }
-  const int chunks = chunks_for(R, ld);
-  const int chunk = (int)((ld + chunks - 1) / chunks);
+  const int ncand = p.chunks * kTopK;
   uint32_t* ck = (uint32_t*)ws;
-  int32_t* cj = (int32_t*)((uint8_t*)ws + (size_t)R * chunks * kTopK * sizeof(uint32_t));
-  hipLaunchKernelGGL(topk_kernel<kChunkCand>, dim3(chunks, R), dim3(kThreads), 0, s, logits, ld,
-                     nullptr, nullptr, 0, chunk, row_len, row_seq, page_table, pt_stride,
-                     c4_page_size, nullptr, nullptr, ck, cj);
+  int32_t* cj = (int32_t*)((uint8_t*)ws + (size_t)R * ncand * sizeof(uint32_t));
+  launch_mode<kChunkCand>(p.chunk_th, keys_per_lane(p.chunk, p.chunk_th), dim3(p.chunks, R), s,
+                          logits, ld, nullptr, nullptr, 0, p.chunk, row_len, row_seq, page_table,
+                          pt_stride, c4_page_size, nullptr, nullptr, ck, cj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel<kCandFinal>, dim3(1, R), dim3(kThreads), 0, s, nullptr, 0, ck,
-                     cj, chunks * kTopK, 0, row_len, row_seq, page_table, pt_stride,
-                     c4_page_size, phys_idx, logical_idx, nullptr, nullptr);
+  launch_mode<kCandFinal>(p.final_th, keys_per_lane(ncand, p.final_th), dim3(1, R), s, nullptr,
+                          0, ck, cj, ncand, 0, row_len, row_seq, page_table, pt_stride,
+                          c4_page_size, phys_idx, logical_idx, nullptr, nullptr);
   return hipGetLastError();
 }
 

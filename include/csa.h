@@ -231,9 +231,10 @@ csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint
  * below -inf. If row_len <= 512 every entry is selected. The selected entries are
  * written in ascending j; the unused tail of a row is -1.
  *   phys_idx    int32 [R][512] (required); logical_idx int32 [R][512] or NULL.
- *   ws          csa_workspace_size(CSA_OP_TOPK, R, ld, 1) bytes: rows longer than
- *               32768 entries, and rows longer than 8192 when R < 128, are reduced
- *               in two launches through it; otherwise 0 bytes. ld up to 2097152.
+ *   ws          csa_workspace_size(CSA_OP_TOPK, R, ld, 1) bytes: when ld > 16384,
+ *               or ld > 8192 and R < 128, rows are reduced in two launches through
+ *               it (chunk candidates, then the row); otherwise 0 bytes. ld up to
+ *               2097152.
  */
 csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
                                const int32_t* row_len, const int32_t* row_seq,

@@ -282,6 +282,31 @@ def test_topk_bit_exact(csa, case):
         assert np.array_equal(phys[r], wp), f"row {r}: physical slots differ"
 
 
+@pytest.mark.parametrize("R,L", [(130, 20000),   # chunks on 256-thread workgroups
+                                 (128, 9000)])   # one workgroup per row, 16 keys per lane
+def test_topk_many_rows(csa, R, L):
+    """Batches of >= 128 rows take their own launch plan; rows of every kind
+    (random, heavy ties, short, NaN / -inf / -0, all equal) in one batch."""
+    g = gen.rng(950 + R)
+    lens = g.integers(L // 2, L + 1, size=R)
+    lens[:6] = [0, 1, 511, 512, 513, L]
+    pps = (L + 63) // 64
+    pt = gen.page_table(g, R, pps, R * pps + 3)
+    logits = (g.standard_normal((R, L)) * 10).astype(np.float32)
+    logits[6:20] = np.round(logits[6:20] / 4) * 4
+    logits[20] = 1.5
+    logits[21, ::2] = -np.inf
+    logits[21, 3::7] = np.nan
+    logits[22, ::3] = -0.0
+    logits[22, 1::3] = 0.0
+    logits[23:30] = np.abs(logits[23:30]) * 3 + 200
+    phys, logi = _run_topk(csa, logits, lens.tolist(), pt)
+    for r, n in enumerate(lens):
+        wp, wl = O.topk_page_select(logits[r], int(n), pt[r])
+        assert np.array_equal(logi[r], wl), f"row {r} (len {n}): logical indices differ"
+        assert np.array_equal(phys[r], wp), f"row {r} (len {n}): physical slots differ"
+
+
 def test_topk_identity_table_and_all_equal(csa):
     logits = np.full((1, 5000), 2.5, np.float32)
     pt = np.arange(79, dtype=np.int32)[None]
