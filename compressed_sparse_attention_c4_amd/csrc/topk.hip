@@ -361,18 +361,18 @@ void launch_mode(int th, int e, dim3 grid, hipStream_t s, const float* logits, i
                  const int32_t* row_len, const int32_t* row_seq, const int32_t* pt, int pt_stride,
                  int c4_page_size, int32_t* phys_idx, int32_t* logical_idx, uint32_t* okeys,
                  int32_t* ojs) {
-#define CSA_TOPK(E, TH)                                                                         \
-  hipLaunchKernelGGL((topk_kernel<kMode, E, TH>), grid, dim3(TH), 0, s, logits, ld, ckeys, cjs, \
-                     ncand, chunk, row_len, row_seq, pt, pt_stride, c4_page_size, phys_idx,      \
-                     logical_idx, okeys, ojs)
-#define CSA_TOPK_E(TH)             \
-  switch (e) {                     \
-    case 1: CSA_TOPK(1, TH); break;   \
-    case 2: CSA_TOPK(2, TH); break;   \
-    case 4: CSA_TOPK(4, TH); break;   \
-    case 8: CSA_TOPK(8, TH); break;   \
-    case 16: CSA_TOPK(16, TH); break; \
-    default: CSA_TOPK(32, TH); break; \
+#define CSA_TOPK_LAUNCH(E, TH)                                                             \
+  hipLaunchKernelGGL((topk_kernel<kMode, E, TH>), grid, dim3(TH), 0, s, logits, ld, ckeys,    \
+                     cjs, ncand, chunk, row_len, row_seq, pt, pt_stride, c4_page_size,         \
+                     phys_idx, logical_idx, okeys, ojs)
+#define CSA_TOPK_E(TH)                       \
+  switch (e) {                               \
+    case 1: CSA_TOPK_LAUNCH(1, TH); break;   \
+    case 2: CSA_TOPK_LAUNCH(2, TH); break;   \
+    case 4: CSA_TOPK_LAUNCH(4, TH); break;   \
+    case 8: CSA_TOPK_LAUNCH(8, TH); break;   \
+    case 16: CSA_TOPK_LAUNCH(16, TH); break; \
+    default: CSA_TOPK_LAUNCH(32, TH); break; \
   }
   if (th == 256) {
     CSA_TOPK_E(256)
@@ -380,7 +380,7 @@ void launch_mode(int th, int e, dim3 grid, hipStream_t s, const float* logits, i
     CSA_TOPK_E(1024)
   }
 #undef CSA_TOPK_E
-#undef CSA_TOPK
+#undef CSA_TOPK_LAUNCH
 }
 
 // How one launch_topk call splits its rows. Every workgroup holds at most 32
