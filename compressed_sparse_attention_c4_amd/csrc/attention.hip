@@ -412,6 +412,33 @@ __device__ __forceinline__ uint64_t pick_base(const Pick& k, const void* c, cons
   return ((uint64_t)c & k.mc) | ((uint64_t)r & k.mr) | ((uint64_t)d & k.md);
 }
 
+// Workgroup coordinates (a = chunk or value slice, t = query, z = 64-head
+// block) from a 1-D grid that groups each query's workgroups by XCD.
+// Workgroup b runs on XCD b % 8; with g = min(8, T rounded up to a power of
+// two), query t gets the workgroups with b % g == t % g, i.e. 8 / g XCDs
+// (one when T >= 8). The query's operands, P' and the cache lines its value
+// slices share are then fetched into those XCDs' L2 only, not into all eight.
+// b past the last query maps to t >= T, which the kernels skip.
+struct Coord {
+  int a, t, z;
+};
+__device__ __forceinline__ Coord block_coord(int na, int nz, int g) {
+  const int b = blockIdx.x;
+  int r = b / g;
+  const int a = r % na;
+  r /= na;
+  return {a, (r / nz) * g + b % g, r % nz};
+}
+int xcd_group(int T) {
+  int g = 1;
+  while (g < T && g < 8) g *= 2;
+  return g;
+}
+dim3 xcd_grid(int na, int nz, int T) {
+  const int g = xcd_group(T);
+  return dim3((unsigned)(g * na * nz * ((T + g - 1) / g)));
+}
+
 __global__ void __launch_bounds__(256)
 attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
                    const int32_t* __restrict__ q_pos, bool hca, const int32_t* __restrict__ phys_idx,
@@ -422,19 +449,21 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
                    const uint16_t* __restrict__ r_rope, int r_ps,
                    const int32_t* __restrict__ raw_pt, int raw_pt_stride, int window, float scale,
                    uint16_t* __restrict__ pw, float2* __restrict__ stats,
-                   int32_t* __restrict__ eslots, int e_pad) {
+                   int32_t* __restrict__ eslots, int e_pad, int T, int nz, int g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kChunk * kKStride];
   __shared__ int32_t s_es[kChunk];
   __shared__ float s_sc[kChunk];
-  const int chunk = blockIdx.x, t = blockIdx.y;
+  const int n_chunks = e_pad / kChunk;
+  const Coord bc = block_coord(n_chunks, nz, g);
+  const int chunk = bc.a, t = bc.t;
+  if (t >= T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int seq = q_seq[t], p = q_pos[t];
   const EntryList L = entry_list(p, k_sel, hca, ratio, window);
   const int total = min(L.n1 + L.n2, e_pad);  // a list longer than the stated bound is cut
   const int e0 = chunk * kChunk;
-  const int n_chunks = e_pad / kChunk;
-  const int hb0 = blockIdx.z * 64;
+  const int hb0 = bc.z * 64;
   if (e0 >= total) {
     // past this query's list: masked slots, zero weights, dead statistics, so
     // that phase B reads every chunk without knowing the list's length
@@ -444,7 +473,7 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
     prow[1] = v4i{0, 0, 0, 0};
     if (tid < kChunk) {
       stats[((int64_t)t * H + hb0 + tid) * n_chunks + chunk] = make_float2(-INFINITY, 0.f);
-      if (blockIdx.z == 0) eslots[(int64_t)t * e_pad + e0 + tid] = -1;
+      if (bc.z == 0) eslots[(int64_t)t * e_pad + e0 + tid] = -1;
     }
     return;
   }
@@ -458,7 +487,7 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
                                    : -1;
     const int32_t w = slot >= 0 ? (int32_t)(slot * 2 + pool) : -1;
     s_es[tid] = w;
-    if (blockIdx.z == 0) eslots[(int64_t)t * e_pad + e0 + tid] = w;
+    if (bc.z == 0) eslots[(int64_t)t * e_pad + e0 + tid] = w;
   }
   // the query operand is loaded after the slot reads, so that waiting for
   // those does not wait for these
@@ -562,13 +591,16 @@ template <bool kOutF32>
 __global__ void __launch_bounds__(256)
 attn_pv_kernel(int H, const uint8_t* __restrict__ c_lat, const uint8_t* __restrict__ r_lat,
                const int32_t* __restrict__ eslots, const uint16_t* __restrict__ pw,
-               const float2* __restrict__ stats, int e_pad, void* __restrict__ out) {
+               const float2* __restrict__ stats, int e_pad, void* __restrict__ out, int T,
+               int nz, int g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[kSlice * kPvStride];
   __shared__ float s_f[64][kMaxChunks];
-  const int slice = blockIdx.x, t = blockIdx.y;
+  const Coord bc = block_coord(kLatent / kSlice, nz, g);
+  const int slice = bc.a, t = bc.t;
+  if (t >= T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int hb0 = blockIdx.z * 64;
+  const int hb0 = bc.z * 64;
   const int n_chunks = e_pad / kChunk;
   // staging task of this thread in each round: entries r*256 + 8*eg .. +7,
   // value dims slice*64 + 8*dg .. +7 (lanes 8k..8k+7: 64 contiguous bytes)
@@ -651,29 +683,30 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ c_lat, const uint8_t* __restri
   }
   lds_sync();
 
+  // Every chunk slot is computed, straight-line: a chunk past the list has
+  // f_c = 0 (and finite weights and values), and without a branch per chunk
+  // the LDS reads and matrix ops of neighbouring chunks overlap.
   v4f o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
-    if (c < n_chunks) {  // uniform; no early exit, so pa stays in registers
-      v4f acc[4];
+    v4f acc[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < 4; ++db) acc[db] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[db] = mfma_bf16(pa[c * 2 + ks],
-                              *reinterpret_cast<const v4i*>(
-                                  &s_vt[(db * 16 + col) * kPvStride + c * kChunk + ks * 32 + grp * 8]),
-                              acc[db]);
+      for (int db = 0; db < 4; ++db)
+        acc[db] = mfma_bf16(pa[c * 2 + ks],
+                            *reinterpret_cast<const v4i*>(
+                                &s_vt[(db * 16 + col) * kPvStride + c * kChunk + ks * 32 + grp * 8]),
+                            acc[db]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float f = s_f[wave * 16 + grp * 4 + r][c];
+    for (int r = 0; r < 4; ++r) {
+      const float f = s_f[wave * 16 + grp * 4 + r][c];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) o[db][r] = fmaf(f, acc[db][r], o[db][r]);
-      }
+      for (int db = 0; db < 4; ++db) o[db][r] = fmaf(f, acc[db][r], o[db][r]);
     }
   }
 #pragma unroll
@@ -813,19 +846,21 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     uint16_t* pw = (uint16_t*)((char*)a.ws + w.pw);
     float2* st = (float2*)((char*)a.ws + w.stats);
     int32_t* es = (int32_t*)((char*)a.ws + w.eslots);
-    hipLaunchKernelGGL(attn_scores_kernel, dim3(e_pad / kChunk, a.T, a.H / 64), dim3(256), 0, s,
+    const int nz = a.H / 64;
+    const int g = xcd_group(a.T);
+    hipLaunchKernelGGL(attn_scores_kernel, xcd_grid(e_pad / kChunk, nz, a.T), dim3(256), 0, s,
                        (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,
                        a.ratio, (const uint8_t*)a.comp.latent, a.comp.latent_scale,
                        (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt, a.comp_pt_stride,
                        (const uint8_t*)a.raw.latent, a.raw.latent_scale,
                        (const uint16_t*)a.raw.rope, a.raw.page_size, a.raw_pt, a.raw_pt_stride,
-                       a.window, a.scale, pw, st, es, e_pad);
+                       a.window, a.scale, pw, st, es, e_pad, a.T, nz, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 #define CSA_PV(FO)                                                                             \
-  hipLaunchKernelGGL(attn_pv_kernel<FO>, dim3(kLatent / kSlice, a.T, a.H / 64), dim3(256), 0, s, \
-                     a.H, (const uint8_t*)a.comp.latent, (const uint8_t*)a.raw.latent, es, pw, st, \
-                     e_pad, a.out)
+  hipLaunchKernelGGL(attn_pv_kernel<FO>, xcd_grid(kLatent / kSlice, nz, a.T), dim3(256), 0, s, a.H,  \
+                     (const uint8_t*)a.comp.latent, (const uint8_t*)a.raw.latent, es, pw, st, e_pad, \
+                     a.out, a.T, nz, g)
     if (a.out_fmt == CSA_F32) CSA_PV(true);
     else CSA_PV(false);
 #undef CSA_PV
