@@ -73,6 +73,33 @@ __device__ __forceinline__ int64_t entry_slot(int i, const EntryList& L, int t, 
   return -1;
 }
 
+// Workgroup coordinates (a = split, chunk, value slice or head; t = query; z =
+// head block) from a 1-D grid that groups each query's workgroups by XCD.
+// Workgroup b runs on XCD b % 8; with g = min(8, T rounded up to a power of
+// two), query t gets the workgroups with b % g == t % g, i.e. 8 / g XCDs
+// (one when T >= 8). The query's operands, P' and the cache lines its value
+// slices share are then fetched into those XCDs' L2 only, not into all eight.
+// b past the last query maps to t >= T, which the kernels skip.
+struct Coord {
+  int a, t, z;
+};
+__device__ __forceinline__ Coord block_coord(int na, int nz, int g) {
+  const int b = blockIdx.x;
+  int r = b / g;
+  const int a = r % na;
+  r /= na;
+  return {a, (r / nz) * g + b % g, r % nz};
+}
+int xcd_group(int T) {
+  int g = 1;
+  while (g < T && g < 8) g *= 2;
+  return g;
+}
+dim3 xcd_grid(int na, int nz, int T) {
+  const int g = xcd_group(T);
+  return dim3((unsigned)(g * na * nz * ((T + g - 1) / g)));
+}
+
 // Two e4m3 codes (bytes 0,1 or 2,3 of w) -> two bf16 (exact), one instruction.
 template <bool kHi>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
@@ -92,7 +119,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
                  const uint8_t* __restrict__ r_lat, const float* __restrict__ r_sc,
                  const uint16_t* __restrict__ r_rope, int r_ps, const int32_t* __restrict__ raw_pt,
                  int raw_pt_stride, int window, float scale, void* __restrict__ out,
-                 float* __restrict__ part, int split_len, int nsplit) {
+                 float* __restrict__ part, int split_len, int nsplit, int T, int nz, int g) {
   // K tile, row-major bf16 [entry][576] (latent codes as exact bf16, then the
   // RoPE dims), and the value tile transposed, bf16 [dim][entry].
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kTile * kKStride];
@@ -102,8 +129,10 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
   __shared__ int32_t s_eslot[kMaxSplit];  // entry slots of this split: slot*2 + pool, -1 masked
   __shared__ float s_escale[kMaxSplit];   // and their FP8 scales
 
-  const int t = blockIdx.y;
-  const int split = blockIdx.x;
+  const Coord bc = block_coord(nsplit, nz, g);
+  const int t = bc.t;
+  if (t >= T) return;
+  const int split = bc.a;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -117,7 +146,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
   const int e_end = min(total, e_begin + split_len);
 
   // Heads of this wave: hbase .. hbase+15 (grid.z splits H in blocks of 16*kNW).
-  const int hbase = blockIdx.z * kNW * 16 + wave * 16;
+  const int hbase = bc.z * kNW * 16 + wave * 16;
   // Query operand (A): head hbase + col, dims step*32 + grp*8 .. +7.
   v4i qa[18];
   {
@@ -318,8 +347,8 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
     // partials: [T][nsplit][H][512] O, then [T][nsplit][H] m and l
     const int64_t ph = ((int64_t)t * nsplit + split) * H;
     float* po = part;
-    float* pm = part + (int64_t)gridDim.y * nsplit * H * kLatent;
-    float* pl = pm + (int64_t)gridDim.y * nsplit * H;
+    float* pm = part + (int64_t)T * nsplit * H * kLatent;
+    float* pl = pm + (int64_t)T * nsplit * H;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t obase = (ph + h0 + r) * kLatent + col;
@@ -336,9 +365,10 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
 template <bool kOutF32>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
-                    void* __restrict__ out) {
-  const int t = blockIdx.y;
-  const int h = blockIdx.x;
+                    void* __restrict__ out, int g) {
+  const Coord bc = block_coord(H, 1, g);  // on the XCDs that wrote the query's partials
+  const int t = bc.t, h = bc.a;
+  if (t >= T) return;
   const float* pm = part + (int64_t)T * nsplit * H * kLatent;
   const float* pl = pm + (int64_t)T * nsplit * H;
   float M = -INFINITY;
@@ -412,32 +442,6 @@ __device__ __forceinline__ uint64_t pick_base(const Pick& k, const void* c, cons
   return ((uint64_t)c & k.mc) | ((uint64_t)r & k.mr) | ((uint64_t)d & k.md);
 }
 
-// Workgroup coordinates (a = chunk or value slice, t = query, z = 64-head
-// block) from a 1-D grid that groups each query's workgroups by XCD.
-// Workgroup b runs on XCD b % 8; with g = min(8, T rounded up to a power of
-// two), query t gets the workgroups with b % g == t % g, i.e. 8 / g XCDs
-// (one when T >= 8). The query's operands, P' and the cache lines its value
-// slices share are then fetched into those XCDs' L2 only, not into all eight.
-// b past the last query maps to t >= T, which the kernels skip.
-struct Coord {
-  int a, t, z;
-};
-__device__ __forceinline__ Coord block_coord(int na, int nz, int g) {
-  const int b = blockIdx.x;
-  int r = b / g;
-  const int a = r % na;
-  r /= na;
-  return {a, (r / nz) * g + b % g, r % nz};
-}
-int xcd_group(int T) {
-  int g = 1;
-  while (g < T && g < 8) g *= 2;
-  return g;
-}
-dim3 xcd_grid(int na, int nz, int T) {
-  const int g = xcd_group(T);
-  return dim3((unsigned)(g * na * nz * ((T + g - 1) / g)));
-}
 
 __global__ void __launch_bounds__(256)
 attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
@@ -872,7 +876,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const bool f32o = a.out_fmt == CSA_F32;
   float* part = nsplit > 1 ? (float*)a.ws : nullptr;
   const int nw = a.H >= 64 ? 4 : a.H / 16;  // waves per workgroup (16 heads each)
-  dim3 grid(nsplit, a.T, a.H / (16 * nw));
+  const int nz = a.H / (16 * nw);
+  const int g = xcd_group(a.T);
+  const dim3 grid = xcd_grid(nsplit, nz, a.T);
 #define CSA_ATTN(NW, FO)                                                                      \
   hipLaunchKernelGGL((attn_mfma_kernel<NW, FO>), grid, dim3(NW * 64), 0, s,                  \
                      (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,   \
@@ -880,7 +886,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
                      (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt,              \
                      a.comp_pt_stride, (const uint8_t*)a.raw.latent, a.raw.latent_scale,      \
                      (const uint16_t*)a.raw.rope, a.raw.page_size, a.raw_pt, a.raw_pt_stride, \
-                     a.window, a.scale, a.out, part, split_len, nsplit)
+                     a.window, a.scale, a.out, part, split_len, nsplit, a.T, nz, g)
   if (nw == 4) { if (f32o) CSA_ATTN(4, true); else CSA_ATTN(4, false); }
   else if (nw == 2) { if (f32o) CSA_ATTN(2, true); else CSA_ATTN(2, false); }
   else { if (f32o) CSA_ATTN(1, true); else CSA_ATTN(1, false); }
@@ -888,11 +894,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   if (f32o)
-    hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(a.H, a.T), dim3(256), 0, s, part, a.T,
-                       a.H, nsplit, a.out);
+    hipLaunchKernelGGL(attn_combine_kernel<true>, xcd_grid(a.H, 1, a.T), dim3(256), 0, s, part,
+                       a.T, a.H, nsplit, a.out, g);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<false>, dim3(a.H, a.T), dim3(256), 0, s, part, a.T,
-                       a.H, nsplit, a.out);
+    hipLaunchKernelGGL(attn_combine_kernel<false>, xcd_grid(a.H, 1, a.T), dim3(256), 0, s, part,
+                       a.T, a.H, nsplit, a.out, g);
   return hipGetLastError();
 }
 
