@@ -13,14 +13,15 @@
 // e4m3 codes are exact in bf16, so the per-entry FP8 scale is applied to the
 // latent score term and folded into P for the value product.
 //
-// A workgroup owns one query and a contiguous range of its entry list; wave w
-// owns heads 16w..16w+15. Entries are gathered 32 at a time: each thread loads
-// an 8-entry x 8-dim block of codes, converts it with v_cvt_scalef32_pk_bf16_fp8
-// and writes it both row-major (K for S) and transposed (V^T for P V) with
-// 16-byte LDS stores; the next tile's gathers are issued before the current
-// tile's matrix work. Every wave then runs its heads against the shared tile
-// with an online softmax. Long entry lists are split over several workgroups
-// whose partial (max, sum, O) are merged by a second kernel.
+// A workgroup owns one query and a contiguous range of its entry list; a pair
+// of waves owns 16 heads (one wave scores half of each tile's entries and
+// accumulates half of the value dims). Entries are gathered 32 at a time:
+// each thread loads an 8-entry x 4-dim block of codes, converts it with
+// v_cvt_scalef32_pk_bf16_fp8 and writes it both row-major (K for S) and
+// transposed (V^T for P V) to LDS; the next tile's gathers are issued before
+// the current tile's matrix work. An online softmax runs over the tiles. Long
+// entry lists are split over several workgroups whose partial (max, sum, O)
+// are merged by a second kernel.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -73,6 +74,42 @@ __device__ __forceinline__ int64_t entry_slot(int i, const EntryList& L, int t, 
   return -1;
 }
 
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations
+// only (not for its outstanding global loads, as __syncthreads would), then
+// s_barrier.
+__device__ __forceinline__ void lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Entry -> pool choice as 64-bit masks (bitwise selects keep gathers
+// straight-line; masked entries read a stand-in and are zeroed).
+struct Pick {
+  int64_t slot;
+  uint64_t mc, mr, md;
+};
+__device__ __forceinline__ Pick pick_of(int es) {
+  Pick k;
+  k.slot = es >= 0 ? (es >> 1) : 0;
+  k.md = es < 0 ? ~0ull : 0ull;
+  k.mr = (es >= 0 && (es & 1)) ? ~0ull : 0ull;
+  k.mc = ~(k.md | k.mr);
+  return k;
+}
+__device__ __forceinline__ uint64_t pick_base(const Pick& k, const void* c, const void* r,
+                                              const void* d) {
+  return ((uint64_t)c & k.mc) | ((uint64_t)r & k.mr) | ((uint64_t)d & k.md);
+}
+// A load from a device address held as an integer, as a global-memory load
+// (a plain pointer made from an integer is generic, and generic loads count
+// in the LDS counter too, so every LDS wait would also wait for them).
+template <class V>
+__device__ __forceinline__ V gload(uint64_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) V*>(addr);
+}
+
 // Workgroup coordinates (a = split, chunk, value slice or head; t = query; z =
 // head block) from a 1-D grid that groups each query's workgroups by XCD.
 // Workgroup b runs on XCD b % 8; with g = min(8, T rounded up to a power of
@@ -109,8 +146,17 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 // The two pools are passed as plain pointers so that the per-entry choice
 // between them is a register select (a struct chosen at run time would be
 // copied to private memory).
-template <int kNW, bool kOutF32>
-__global__ void __launch_bounds__(kNW * 64)
+// The two contractions of a tile split over pairs of waves: pair g owns heads
+// 16g..16g+15 of the workgroup's head block; within a pair, wave `half`
+// scores entries 16*half..+15 of each tile and accumulates value dims
+// 256*half..+255. A wave then holds a 16 x 256 output block (64 accumulators
+// per lane) instead of 16 x 512, which leaves registers for the LDS operand
+// reads to run ahead of the matrix ops, and two waves share each SIMD, so one
+// wave's LDS and softmax latency hides behind the other's matrix work. The
+// two waves of a pair exchange their tile maxima and write the two halves of
+// the tile's P through LDS.
+template <int kHG, bool kOutF32>
+__global__ void __launch_bounds__(kHG * 128)
 attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
                  const int32_t* __restrict__ q_pos, bool hca, const int32_t* __restrict__ phys_idx,
                  int k_sel, int ratio, const uint8_t* __restrict__ c_lat,
@@ -120,12 +166,14 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
                  const uint16_t* __restrict__ r_rope, int r_ps, const int32_t* __restrict__ raw_pt,
                  int raw_pt_stride, int window, float scale, void* __restrict__ out,
                  float* __restrict__ part, int split_len, int nsplit, int T, int nz, int g) {
+  constexpr int kThreads = kHG * 128;
   // K tile, row-major bf16 [entry][576] (latent codes as exact bf16, then the
   // RoPE dims), and the value tile transposed, bf16 [dim][entry].
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kTile * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[kLatent * kVtStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_p[kNW][16 * kPStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[kHG][16 * kPStride];
   __shared__ float s_scale[kTile];
+  __shared__ float s_mx[kHG][2][16];      // per pair and half: a value per head
   __shared__ int32_t s_eslot[kMaxSplit];  // entry slots of this split: slot*2 + pool, -1 masked
   __shared__ float s_escale[kMaxSplit];   // and their FP8 scales
 
@@ -135,7 +183,8 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
   const int split = bc.a;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave >> 1, half = wave & 1;
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int seq = q_seq[t];
@@ -144,9 +193,10 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
   const int total = L.n1 + L.n2;
   const int e_begin = split * split_len;
   const int e_end = min(total, e_begin + split_len);
+  const int n_split = max(0, e_end - e_begin);
 
-  // Heads of this wave: hbase .. hbase+15 (grid.z splits H in blocks of 16*kNW).
-  const int hbase = bc.z * kNW * 16 + wave * 16;
+  // Heads of this pair: hbase .. hbase+15.
+  const int hbase = bc.z * kHG * 16 + hg * 16;
   // Query operand (A): head hbase + col, dims step*32 + grp*8 .. +7.
   v4i qa[18];
   {
@@ -159,16 +209,16 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
   }
 
   float m[4], l[4];
-  v4f o[32];
+  v4f o[16];  // dims 256*half + 16n + col, rows = heads 4*grp + r
 #pragma unroll
   for (int r = 0; r < 4; ++r) { m[r] = -INFINITY; l[r] = 0.f; }
 #pragma unroll
-  for (int n = 0; n < 32; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < 16; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // Slots and scales of every entry of this split, resolved once (one round of
   // page-table / index reads for the whole split, all threads in parallel), so
   // the tile gathers below depend on LDS only.
-  for (int i = tid; i < e_end - e_begin; i += kNW * 64) {
+  for (int i = tid; i < n_split; i += kThreads) {
     int pool = 0;
     const int64_t slot = entry_slot(e_begin + i, L, t, seq, hca, phys_idx, k_sel, comp_pt,
                                     comp_pt_stride, c_ps, raw_pt, raw_pt_stride, r_ps, pool);
@@ -185,72 +235,65 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
   }
   __syncthreads();
 
-  // Staging task of this thread (256 tasks per tile: kNW*64 threads loop):
-  // an 8-entry x 8-dim block of latent codes, entries 8*eg.., dims 8*c..,
-  // plus one 8-dim RoPE chunk (entry re, dims 512 + 8*rc).
-  constexpr int kTasks = 256 / (kNW * 64);  // staging tasks per thread
-  uint2 codes[kTasks][8];
-  uint4 ropev[kTasks];
-  auto issue_loads = [&](int tile0) {
-    const int lt0 = tile0 - e_begin;  // tile start within the split
+  // Staging tasks: latent blocks of 8 entries x 4 dims (entries 8*eg.., dims
+  // 4*c..; 512 per tile) and RoPE chunks of 16 B (entry re, dims 512 + 8*rc;
+  // 256 per tile). The gathers are straight-line: a masked entry, or one past
+  // the split, reads a stand-in row and is zeroed.
+  constexpr int kLT = 512 / kThreads;
+  constexpr int kRT = (256 + kThreads - 1) / kThreads;
+  uint32_t codes[kLT][8];
+  uint4 ropev[kRT];
+  float scale_reg = 0.f;  // threads < kTile: scale of entry tile0 + tid
+  const uint8_t* dummy = c_lat;
+  const int last = max(n_split - 1, 0);  // clamped LDS index: reads stay unconditional
+  auto issue_loads = [&](int tile0) __attribute__((always_inline)) {
+    const int lt0 = tile0 - e_begin;
 #pragma unroll
-    for (int k = 0; k < kTasks; ++k) {
-      const int task = tid + k * kNW * 64;
+    for (int k = 0; k < kLT; ++k) {
+      const int task = tid + k * kThreads;
       const int eg = task & 3, c = task >> 2;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int li = lt0 + 8 * eg + j;
-        const int es = li < e_end - e_begin ? s_eslot[li] : -1;
-        uint2 v = make_uint2(0, 0);
-        if (es >= 0) {
-          const int64_t slot = es >> 1;
-          // one global load per pool under a lane predicate (a selected
-          // pointer would be lowered to a private-memory table)
-          if (es & 1) v = *reinterpret_cast<const uint2*>(r_lat + slot * kLatent + 8 * c);
-          else v = *reinterpret_cast<const uint2*>(c_lat + slot * kLatent + 8 * c);
-        }
-        codes[k][j] = v;
+        const int es = s_eslot[min(li, last)];
+        const Pick pk = pick_of(li < n_split ? es : -1);
+        const uint32_t v = gload<uint32_t>(pick_base(pk, c_lat, r_lat, dummy) +
+                                                              pk.slot * kLatent + 4 * c);
+        codes[k][j] = pk.md ? 0u : v;
       }
+    }
+#pragma unroll
+    for (int k = 0; k < kRT; ++k) {
+      const int task = (tid + k * kThreads) & 255;
       const int re = task & 31, rc = task >> 5;
       const int li = lt0 + re;
-      const int es = li < e_end - e_begin ? s_eslot[li] : -1;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (es >= 0) {
-        const int64_t slot = es >> 1;
-        if (es & 1) v = *reinterpret_cast<const uint4*>(r_rope + slot * kRope + 8 * rc);
-        else v = *reinterpret_cast<const uint4*>(c_rope + slot * kRope + 8 * rc);
-      }
-      ropev[k] = v;
+      const int es = s_eslot[min(li, last)];
+      const Pick pk = pick_of(li < n_split ? es : -1);
+      const v4i v = gload<v4i>(pick_base(pk, c_rope, r_rope, dummy) + pk.slot * (kRope * 2) + 16 * rc);
+      ropev[k] = pk.md ? make_uint4(0, 0, 0, 0)
+                       : make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
     }
-  };
-  float scale_reg = 0.f;  // threads < kTile: scale of entry tile0 + tid
-  auto issue_scale = [&](int tile0) {
-    const int li = tile0 - e_begin + tid;
-    scale_reg = (tid < kTile && li < e_end - e_begin) ? s_escale[li] : 0.f;
+    const int li = lt0 + (tid & (kTile - 1));
+    const float es = s_escale[min(li, last)];
+    scale_reg = (tid < kTile && li < n_split) ? es : 0.f;
   };
 
-  if (e_begin < e_end) {
-    issue_loads(e_begin);
-    issue_scale(e_begin);
-  }
+  issue_loads(e_begin);
   for (int tile0 = e_begin; tile0 < e_end; tile0 += kTile) {
     // ---- write the staged tile to LDS (exact fp8 -> bf16 conversion)
 #pragma unroll
-    for (int k = 0; k < kTasks; ++k) {
-      const int task = tid + k * kNW * 64;
+    for (int k = 0; k < kLT; ++k) {
+      const int task = tid + k * kThreads;
       const int eg = task & 3, c = task >> 2;
-      uint32_t kb[8][4];
+      uint32_t kb[8][2];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        kb[j][0] = fp8x2_to_bf16x2<false>(codes[k][j].x);
-        kb[j][1] = fp8x2_to_bf16x2<true>(codes[k][j].x);
-        kb[j][2] = fp8x2_to_bf16x2<false>(codes[k][j].y);
-        kb[j][3] = fp8x2_to_bf16x2<true>(codes[k][j].y);
-        *reinterpret_cast<uint4*>(&s_k[(8 * eg + j) * kKStride + 8 * c]) =
-            make_uint4(kb[j][0], kb[j][1], kb[j][2], kb[j][3]);
+        kb[j][0] = fp8x2_to_bf16x2<false>(codes[k][j]);
+        kb[j][1] = fp8x2_to_bf16x2<true>(codes[k][j]);
+        *reinterpret_cast<uint2*>(&s_k[(8 * eg + j) * kKStride + 4 * c]) = make_uint2(kb[j][0], kb[j][1]);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         const int w = i >> 1;
         uint32_t d[4];
 #pragma unroll
@@ -258,86 +301,100 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
           const uint32_t a = kb[2 * jj][w], b = kb[2 * jj + 1][w];
           d[jj] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
         }
-        *reinterpret_cast<uint4*>(&s_vt[(8 * c + i) * kVtStride + 8 * eg]) =
+        *reinterpret_cast<uint4*>(&s_vt[(4 * c + i) * kVtStride + 8 * eg]) =
             make_uint4(d[0], d[1], d[2], d[3]);
       }
-      const int re = task & 31, rc = task >> 5;
-      *reinterpret_cast<uint4*>(&s_k[re * kKStride + kLatent + 8 * rc]) = ropev[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kRT; ++k) {
+      const int task = tid + k * kThreads;
+      if (task < 256) {
+        const int re = task & 31, rc = task >> 5;
+        *reinterpret_cast<uint4*>(&s_k[re * kKStride + kLatent + 8 * rc]) = ropev[k];
+      }
     }
     if (tid < kTile) s_scale[tid] = scale_reg;
-    __syncthreads();
-    // ---- prefetch the next tile while this one is computed
-    const int next = tile0 + kTile;
-    if (next < e_end) {
-      issue_loads(next);
-      issue_scale(next);
-    }
+    lds_sync();
+    // ---- prefetch the next tile while this one is computed (past the split:
+    // stand-in rows, never used; no branch, so the waits below stay exact)
+    issue_loads(tile0 + kTile);
 
-    // ---- S = Q K^T for 16 heads x 32 entries (two 16-column blocks)
-    float sv[2][4];
+    // ---- S = Q K^T for 16 heads x the 16 entries of this half
+    const int e = half * 16 + col;
+    v4f acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int e = cb * 16 + col;
-      v4f acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(&s_k[e * kKStride + s * 32 + grp * 8]);
-        acc_l = mfma_bf16(qa[s], v4i{(int)kk.x, (int)kk.y, (int)kk.z, (int)kk.w}, acc_l);
-      }
-#pragma unroll
-      for (int s = 16; s < 18; ++s) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(&s_k[e * kKStride + s * 32 + grp * 8]);
-        acc_r = mfma_bf16(qa[s], v4i{(int)kk.x, (int)kk.y, (int)kk.z, (int)kk.w}, acc_r);
-      }
-      const bool valid = tile0 + e < e_end && s_eslot[tile0 - e_begin + e] >= 0;
-      const float sc = s_scale[e];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sv[cb][r] = valid ? scale * fmaf(sc, acc_l[r], acc_r[r]) : -INFINITY;
+    for (int s = 0; s < 16; ++s) {
+      const uint4 kk = *reinterpret_cast<const uint4*>(&s_k[e * kKStride + s * 32 + grp * 8]);
+      acc_l = mfma_bf16(qa[s], v4i{(int)kk.x, (int)kk.y, (int)kk.z, (int)kk.w}, acc_l);
     }
-    // ---- online softmax over the tile (rows = heads 4*grp + r)
+#pragma unroll
+    for (int s = 16; s < 18; ++s) {
+      const uint4 kk = *reinterpret_cast<const uint4*>(&s_k[e * kKStride + s * 32 + grp * 8]);
+      acc_r = mfma_bf16(qa[s], v4i{(int)kk.x, (int)kk.y, (int)kk.z, (int)kk.w}, acc_r);
+    }
+    const int li = tile0 - e_begin + e;
+    const bool valid = li < n_split && s_eslot[min(li, last)] >= 0;
+    const float sc = s_scale[e];
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = valid ? scale * fmaf(sc, acc_l[r], acc_r[r]) : -INFINITY;
+    // ---- tile maxima of the pair (rows = heads 4*grp + r)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mh = row16_max(sv[r]);
+      if (col == 0) s_mx[hg][half][grp * 4 + r] = mh;
+    }
+    lds_sync();
     float corr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float mt = row16_max(fmaxf(sv[0][r], sv[1][r]));
+      const float mt = fmaxf(s_mx[hg][0][grp * 4 + r], s_mx[hg][1][grp * 4 + r]);
       const float mn = fmaxf(m[r], mt);
       const bool dead = mn == -INFINITY;
       corr[r] = dead ? 1.f : __expf(m[r] - mn);
-      const float p0 = dead ? 0.f : __expf(sv[0][r] - mn);
-      const float p1 = dead ? 0.f : __expf(sv[1][r] - mn);
-      const float ps = row16_sum(p0 + p1);
-      l[r] = l[r] * corr[r] + ps;
+      const float pr = dead ? 0.f : __expf(sv[r] - mn);
+      l[r] = l[r] * corr[r] + row16_sum(pr);  // this half's entries; halves add up at the end
       m[r] = mn;
       // P' = p * (value dequant scale), bf16, stored row-major [head][entry]
-      uint16_t* prow = &s_p[wave][(grp * 4 + r) * kPStride];
-      prow[col] = f32_to_bf16(p0 * s_scale[col]);
-      prow[16 + col] = f32_to_bf16(p1 * s_scale[16 + col]);
+      s_p[hg][(grp * 4 + r) * kPStride + e] = f32_to_bf16(pr * sc);
     }
+    // a tile that raises no running maximum leaves O as it is (exactly)
+    if (__ballot(corr[0] != 1.f || corr[1] != 1.f || corr[2] != 1.f || corr[3] != 1.f)) {
 #pragma unroll
-    for (int n = 0; n < 32; ++n)
+      for (int n = 0; n < 16; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[n][r] *= corr[r];
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): P stores visible to the wave
-    __builtin_amdgcn_wave_barrier();
-    // ---- O += P V: A = P (head col, entries grp*8..+7), B = V^T rows
-    const uint4 pa8 = *reinterpret_cast<const uint4*>(&s_p[wave][col * kPStride + grp * 8]);
+        for (int r = 0; r < 4; ++r) o[n][r] *= corr[r];
+    }
+    lds_sync();  // both halves of P written
+    // ---- O += P V: A = P (head col, entries grp*8..+7), B = V^T rows of this half
+    const uint4 pa8 = *reinterpret_cast<const uint4*>(&s_p[hg][col * kPStride + grp * 8]);
     const v4i pa = v4i{(int)pa8.x, (int)pa8.y, (int)pa8.z, (int)pa8.w};
 #pragma unroll
-    for (int n = 0; n < 32; ++n) {
-      const uint4 v8 = *reinterpret_cast<const uint4*>(&s_vt[(n * 16 + col) * kVtStride + grp * 8]);
+    for (int n = 0; n < 16; ++n) {
+      const uint4 v8 = *reinterpret_cast<const uint4*>(
+          &s_vt[(half * 256 + n * 16 + col) * kVtStride + grp * 8]);
       o[n] = mfma_bf16(pa, v4i{(int)v8.x, (int)v8.y, (int)v8.z, (int)v8.w}, o[n]);
     }
-    __syncthreads();
+    lds_sync();  // the tile's LDS is free for the next one
   }
 
+  // the row sums of the two halves
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (col == 0) s_mx[hg][half][grp * 4 + r] = l[r];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) l[r] = s_mx[hg][0][grp * 4 + r] + s_mx[hg][1][grp * 4 + r];
+
   const int h0 = hbase + grp * 4;
+  const int d0 = half * 256 + col;
   if (nsplit == 1) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
-      const int64_t obase = ((int64_t)t * H + h0 + r) * kLatent + col;
+      const int64_t obase = ((int64_t)t * H + h0 + r) * kLatent + d0;
 #pragma unroll
-      for (int n = 0; n < 32; ++n) {
+      for (int n = 0; n < 16; ++n) {
         const float v = o[n][r] * inv;
         if (kOutF32) reinterpret_cast<float*>(out)[obase + n * 16] = v;
         else reinterpret_cast<uint16_t*>(out)[obase + n * 16] = f32_to_bf16(v);
@@ -351,10 +408,10 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
     float* pl = pm + (int64_t)T * nsplit * H;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t obase = (ph + h0 + r) * kLatent + col;
+      const int64_t obase = (ph + h0 + r) * kLatent + d0;
 #pragma unroll
-      for (int n = 0; n < 32; ++n) po[obase + n * 16] = o[n][r];
-      if (col == 0) {
+      for (int n = 0; n < 16; ++n) po[obase + n * 16] = o[n][r];
+      if (col == 0 && half == 0) {
         pm[ph + h0 + r] = m[r];
         pl[ph + h0 + r] = l[r];
       }
@@ -413,34 +470,6 @@ constexpr int kRounds = kTwoPhaseMaxE / kRound;
 constexpr int kPvStride = kTwoPhaseMaxE + 8;  // bf16 per V^T row in phase B's LDS
 constexpr int kMaxChunks = kTwoPhaseMaxE / kChunk;
 
-// Workgroup barrier for LDS traffic: waits for this wave's LDS operations
-// only (not for its outstanding global loads, as __syncthreads would), then
-// s_barrier.
-__device__ __forceinline__ void lds_sync() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Entry -> pool choice as 64-bit masks (bitwise selects keep gathers
-// straight-line; masked entries read a stand-in and are zeroed).
-struct Pick {
-  int64_t slot;
-  uint64_t mc, mr, md;
-};
-__device__ __forceinline__ Pick pick_of(int es) {
-  Pick k;
-  k.slot = es >= 0 ? (es >> 1) : 0;
-  k.md = es < 0 ? ~0ull : 0ull;
-  k.mr = (es >= 0 && (es & 1)) ? ~0ull : 0ull;
-  k.mc = ~(k.md | k.mr);
-  return k;
-}
-__device__ __forceinline__ uint64_t pick_base(const Pick& k, const void* c, const void* r,
-                                              const void* d) {
-  return ((uint64_t)c & k.mc) | ((uint64_t)r & k.mr) | ((uint64_t)d & k.md);
-}
 
 
 __global__ void __launch_bounds__(256)
@@ -511,7 +540,7 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   for (int k = 0; k < 8; ++k) {
     const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
     const Pick pk = pick_of(s_es[e]);
-    const v4i x = *reinterpret_cast<const v4i*>(pick_base(pk, c_lat, r_lat, dummy) +
+    const v4i x = gload<v4i>(pick_base(pk, c_lat, r_lat, dummy) +
                                                 pk.slot * kLatent + 16 * c);
     lat[k] = pk.md ? v4i{0, 0, 0, 0} : x;
   }
@@ -519,13 +548,13 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   for (int k = 0; k < 2; ++k) {
     const int idx = tid + k * 256, e = idx >> 3, c = idx & 7;
     const Pick pk = pick_of(s_es[e]);
-    rp[k] = *reinterpret_cast<const v4i*>(pick_base(pk, c_rope, r_rope, dummy) +
+    rp[k] = gload<v4i>(pick_base(pk, c_rope, r_rope, dummy) +
                                           pk.slot * (kRope * 2) + 16 * c);
   }
   float scv;
   {
     const Pick pk = pick_of(s_es[tid & (kChunk - 1)]);
-    const float x = *reinterpret_cast<const float*>(pick_base(pk, c_sc, r_sc, dummy) + pk.slot * 4);
+    const float x = gload<float>(pick_base(pk, c_sc, r_sc, dummy) + pk.slot * 4);
     scv = pk.md ? 0.f : x;
   }
 #pragma unroll
@@ -641,7 +670,7 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ c_lat, const uint8_t* __restri
       const int live = r * kRound + 8 * eg + j < e_pad;
       const int es = live ? sw[r][j >> 2][j & 3] : -1;
       const Pick pk = pick_of(es);
-      const v2i x = *reinterpret_cast<const v2i*>(pick_base(pk, c_lat, r_lat, dummy) +
+      const v2i x = gload<v2i>(pick_base(pk, c_lat, r_lat, dummy) +
                                                   pk.slot * kLatent + slice * kSlice + 8 * dg);
       codes[r][j] = pk.md ? v2i{0, 0} : x;
     }
@@ -875,12 +904,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   split_len = ((split_len + kTile - 1) / kTile) * kTile;
   const bool f32o = a.out_fmt == CSA_F32;
   float* part = nsplit > 1 ? (float*)a.ws : nullptr;
-  const int nw = a.H >= 64 ? 4 : a.H / 16;  // waves per workgroup (16 heads each)
+  const int nw = a.H >= 64 ? 4 : a.H / 16;  // pairs of waves per workgroup (16 heads each)
   const int nz = a.H / (16 * nw);
   const int g = xcd_group(a.T);
   const dim3 grid = xcd_grid(nsplit, nz, a.T);
 #define CSA_ATTN(NW, FO)                                                                      \
-  hipLaunchKernelGGL((attn_mfma_kernel<NW, FO>), grid, dim3(NW * 64), 0, s,                  \
+  hipLaunchKernelGGL((attn_mfma_kernel<NW, FO>), grid, dim3(NW * 128), 0, s,                 \
                      (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,   \
                      a.ratio, (const uint8_t*)a.comp.latent, a.comp.latent_scale,             \
                      (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt,              \
