@@ -28,13 +28,20 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags. attention.hip: its softmax never produces NaN (every
+# -inf case is guarded), and without NaN semantics each max in the row
+# reductions is one DPP-fused v_max_f32 instead of a move, a canonicalising
+# max and a max.
+EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

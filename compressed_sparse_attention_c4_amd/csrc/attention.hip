@@ -16,10 +16,11 @@
 // A workgroup owns one query and a contiguous range of its entry list; a pair
 // of waves owns 16 heads (one wave scores half of each tile's entries and
 // accumulates half of the value dims). Entries are gathered 32 at a time:
-// each thread loads an 8-entry x 4-dim block of codes, converts it with
-// v_cvt_scalef32_pk_bf16_fp8 and writes it both row-major (K for S) and
-// transposed (V^T for P V) to LDS; the next tile's gathers are issued before
-// the current tile's matrix work. An online softmax runs over the tiles. Long
+// each thread loads 32 code bytes of one entry, converts them with
+// v_cvt_scalef32_pk_bf16_fp8 and writes them row-major to one of two LDS
+// tiles; S reads K fragments from the tile and P V reads the value fragments
+// from the same tile with ds_read_b64_tr_b16. A tile's gathers are issued two
+// tiles ahead of its matrix work. An online softmax runs over the tiles. Long
 // entry lists are split over several workgroups whose partial (max, sum, O)
 // are merged by a second kernel.
 #include "csa_device.hpp"
@@ -30,12 +31,12 @@ namespace {
 
 constexpr int kTile = 32;             // entries per LDS tile
 constexpr int kKStride = kKvDim + 8;  // bf16 elements per row of the K tile
-constexpr int kVtStride = kTile + 8;  // bf16 elements per row of V^T
 constexpr int kPStride = kTile + 8;   // bf16 elements per row of P
 constexpr int kMaxSplit = 1024;       // entries one workgroup handles, at most
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma_bf16(const v4i& a, const v4i& b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -110,6 +111,12 @@ __device__ __forceinline__ V gload(uint64_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(1))) V*>(addr);
 }
 
+// A row of zeros as long as an entry's latent codes. A masked entry's gathers
+// read from here (slot 0), so they load zeros and need no select afterwards;
+// a select on a prefetched value would make the compiler wait for that load
+// where the select lands, in the middle of the matrix work.
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row[kLatent] = {};
+
 // Workgroup coordinates (a = split, chunk, value slice or head; t = query; z =
 // head block) from a 1-D grid that groups each query's workgroups by XCD.
 // Workgroup b runs on XCD b % 8; with g = min(8, T rounded up to a power of
@@ -155,6 +162,16 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 // wave's LDS and softmax latency hides behind the other's matrix work. The
 // two waves of a pair exchange their tile maxima and write the two halves of
 // the tile's P through LDS.
+//
+// Per tile, the vector ALU is the scarce unit (a wave64 VALU op issues over
+// four cycles, a tile's matrix work is 34 MFMAs per wave), so the staging is
+// built to need few VALU ops: a thread gathers 32 contiguous code bytes of one
+// entry (one address per tile), the K tile is stored once, row-major, and the
+// value operand of P V is read from it with the transposing LDS load; the
+// softmax keeps its row sums per lane until the end and rescales O only when
+// a head's maximum grows by more than kRescaleSlack.
+constexpr float kRescaleSlack = 8.f;  // p = exp(s - m_ref) <= e^8 between rescales
+
 template <int kHG, bool kOutF32>
 __global__ void __launch_bounds__(kHG * 128)
 attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
@@ -167,15 +184,14 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
                  int raw_pt_stride, int window, float scale, void* __restrict__ out,
                  float* __restrict__ part, int split_len, int nsplit, int T, int nz, int g) {
   constexpr int kThreads = kHG * 128;
-  // K tile, row-major bf16 [entry][576] (latent codes as exact bf16, then the
-  // RoPE dims), and the value tile transposed, bf16 [dim][entry].
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kTile * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kLatent * kVtStride];
+  // Two K tiles (the one being computed and the next), row-major bf16
+  // [entry][576]: latent codes as exact bf16, then the RoPE dims.
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_p[kHG][16 * kPStride];
-  __shared__ float s_scale[kTile];
-  __shared__ float s_mx[kHG][2][16];      // per pair and half: a value per head
+  __shared__ float s_scale[2][kTile];
+  __shared__ int s_valid[2][kTile];
+  __shared__ __attribute__((aligned(16))) float s_mx[kHG][2][16];  // per pair and half: a value per head
   __shared__ int32_t s_eslot[kMaxSplit];  // entry slots of this split: slot*2 + pool, -1 masked
-  __shared__ float s_escale[kMaxSplit];   // and their FP8 scales
 
   const Coord bc = block_coord(nsplit, nz, g);
   const int t = bc.t;
@@ -208,6 +224,8 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
     }
   }
 
+  // m: the reference maximum of each head (rows 4*grp + r); l: this lane's
+  // share of the row sum (its entry column, summed over the tiles).
   float m[4], l[4];
   v4f o[16];  // dims 256*half + 16n + col, rows = heads 4*grp + r
 #pragma unroll
@@ -215,7 +233,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
 #pragma unroll
   for (int n = 0; n < 16; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Slots and scales of every entry of this split, resolved once (one round of
+  // Slots of every entry of this split, resolved once (one round of
   // page-table / index reads for the whole split, all threads in parallel), so
   // the tile gathers below depend on LDS only.
   for (int i = tid; i < n_split; i += kThreads) {
@@ -223,118 +241,92 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
     const int64_t slot = entry_slot(e_begin + i, L, t, seq, hca, phys_idx, k_sel, comp_pt,
                                     comp_pt_stride, c_ps, raw_pt, raw_pt_stride, r_ps, pool);
     s_eslot[i] = slot >= 0 ? (int32_t)(slot * 2 + pool) : -1;
-    float sc = 0.f;
-    if (slot >= 0) {
-      // both loads issued (one at index 0) so they cannot be merged into a
-      // load through a selected pointer
-      const float rs = r_sc[pool ? slot : 0];
-      const float cs = c_sc[pool ? 0 : slot];
-      sc = pool ? rs : cs;
-    }
-    s_escale[i] = sc;
   }
   __syncthreads();
 
-  // Staging tasks: latent blocks of 8 entries x 4 dims (entries 8*eg.., dims
-  // 4*c..; 512 per tile) and RoPE chunks of 16 B (entry re, dims 512 + 8*rc;
-  // 256 per tile). The gathers are straight-line: a masked entry, or one past
-  // the split, reads a stand-in row and is zeroed.
-  constexpr int kLT = 512 / kThreads;
-  constexpr int kRT = (256 + kThreads - 1) / kThreads;
-  uint32_t codes[kLT][8];
-  uint4 ropev[kRT];
-  float scale_reg = 0.f;  // threads < kTile: scale of entry tile0 + tid
-  const uint8_t* dummy = c_lat;
+  // Staging tasks: entry e = task / 16 of the tile, part c = task % 16: latent
+  // codes 8c + 128j .. +7 (j < 4), RoPE chunk c % 8 (16 B; written by c < 8)
+  // and the entry's FP8 scale (written by c == 0). A masked entry, or one past
+  // the split, reads the zero row.
+  constexpr int kTasks = (kTile * 16) / kThreads;
+  v2i lat[kTasks][4];
+  v4i rope[kTasks];
+  float esc[kTasks];
+  int evalid[kTasks];
+  const uint8_t* zero = g_zero_row;
   const int last = max(n_split - 1, 0);  // clamped LDS index: reads stay unconditional
   auto issue_loads = [&](int tile0) __attribute__((always_inline)) {
-    const int lt0 = tile0 - e_begin;
 #pragma unroll
-    for (int k = 0; k < kLT; ++k) {
+    for (int k = 0; k < kTasks; ++k) {
       const int task = tid + k * kThreads;
-      const int eg = task & 3, c = task >> 2;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int li = lt0 + 8 * eg + j;
-        const int es = s_eslot[min(li, last)];
-        const Pick pk = pick_of(li < n_split ? es : -1);
-        const uint32_t v = gload<uint32_t>(pick_base(pk, c_lat, r_lat, dummy) +
-                                                              pk.slot * kLatent + 4 * c);
-        codes[k][j] = pk.md ? 0u : v;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kRT; ++k) {
-      const int task = (tid + k * kThreads) & 255;
-      const int re = task & 31, rc = task >> 5;
-      const int li = lt0 + re;
+      const int e = task >> 4, c = task & 15;
+      const int li = tile0 - e_begin + e;
       const int es = s_eslot[min(li, last)];
       const Pick pk = pick_of(li < n_split ? es : -1);
-      const v4i v = gload<v4i>(pick_base(pk, c_rope, r_rope, dummy) + pk.slot * (kRope * 2) + 16 * rc);
-      ropev[k] = pk.md ? make_uint4(0, 0, 0, 0)
-                       : make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+      evalid[k] = !pk.md;
+      const uint64_t lb = pick_base(pk, c_lat, r_lat, zero) + pk.slot * kLatent + 8 * c;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lat[k][j] = gload<v2i>(lb + 128 * j);
+      rope[k] = gload<v4i>(pick_base(pk, c_rope, r_rope, zero) + pk.slot * (kRope * 2) + 16 * (c & 7));
+      esc[k] = gload<float>(pick_base(pk, c_sc, r_sc, zero) + pk.slot * 4);
     }
-    const int li = lt0 + (tid & (kTile - 1));
-    const float es = s_escale[min(li, last)];
-    scale_reg = (tid < kTile && li < n_split) ? es : 0.f;
+  };
+  auto stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kTasks; ++k) {
+      const int task = tid + k * kThreads;
+      const int e = task >> 4, c = task & 15;
+      uint16_t* row = &s_k[buf][e * kKStride];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w0 = (uint32_t)lat[k][j][0], w1 = (uint32_t)lat[k][j][1];
+        *reinterpret_cast<uint4*>(row + 8 * c + 128 * j) =
+            make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                       fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+      }
+      if (c < 8)
+        *reinterpret_cast<uint4*>(row + kLatent + 8 * c) =
+            make_uint4((uint32_t)rope[k][0], (uint32_t)rope[k][1], (uint32_t)rope[k][2],
+                       (uint32_t)rope[k][3]);
+      if (c == 0) {
+        s_scale[buf][e] = esc[k];
+        s_valid[buf][e] = evalid[k];
+      }
+    }
   };
 
+  const int n_tiles = (n_split + kTile - 1) / kTile;
   issue_loads(e_begin);
-  for (int tile0 = e_begin; tile0 < e_end; tile0 += kTile) {
-    // ---- write the staged tile to LDS (exact fp8 -> bf16 conversion)
-#pragma unroll
-    for (int k = 0; k < kLT; ++k) {
-      const int task = tid + k * kThreads;
-      const int eg = task & 3, c = task >> 2;
-      uint32_t kb[8][2];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        kb[j][0] = fp8x2_to_bf16x2<false>(codes[k][j]);
-        kb[j][1] = fp8x2_to_bf16x2<true>(codes[k][j]);
-        *reinterpret_cast<uint2*>(&s_k[(8 * eg + j) * kKStride + 4 * c]) = make_uint2(kb[j][0], kb[j][1]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int w = i >> 1;
-        uint32_t d[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const uint32_t a = kb[2 * jj][w], b = kb[2 * jj + 1][w];
-          d[jj] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-        }
-        *reinterpret_cast<uint4*>(&s_vt[(4 * c + i) * kVtStride + 8 * eg]) =
-            make_uint4(d[0], d[1], d[2], d[3]);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kRT; ++k) {
-      const int task = tid + k * kThreads;
-      if (task < 256) {
-        const int re = task & 31, rc = task >> 5;
-        *reinterpret_cast<uint4*>(&s_k[re * kKStride + kLatent + 8 * rc]) = ropev[k];
-      }
-    }
-    if (tid < kTile) s_scale[tid] = scale_reg;
-    lds_sync();
-    // ---- prefetch the next tile while this one is computed (past the split:
-    // stand-in rows, never used; no branch, so the waits below stay exact)
-    issue_loads(tile0 + kTile);
-
-    // ---- S = Q K^T for 16 heads x the 16 entries of this half
+  stage(0);
+  issue_loads(e_begin + kTile);
+  lds_sync();
+  for (int it = 0; it < n_tiles; ++it) {
+    const int buf = it & 1;
+    const uint16_t* kt = s_k[buf];
+    // ---- S = Q K^T for 16 heads x the 16 entries of this half. The K
+    // fragments are read ahead (six in flight), so the matrix cores do not
+    // wait out an LDS round trip per step.
     const int e = half * 16 + col;
-    v4f acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
+    v4i kf[18];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const uint4 kk = *reinterpret_cast<const uint4*>(&s_k[e * kKStride + s * 32 + grp * 8]);
-      acc_l = mfma_bf16(qa[s], v4i{(int)kk.x, (int)kk.y, (int)kk.z, (int)kk.w}, acc_l);
+    for (int s = 0; s < 18; ++s) {
+      const uint4 kk = *reinterpret_cast<const uint4*>(&kt[e * kKStride + s * 32 + grp * 8]);
+      kf[s] = v4i{(int)kk.x, (int)kk.y, (int)kk.z, (int)kk.w};
     }
+    v4f acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = acc_l;
 #pragma unroll
-    for (int s = 16; s < 18; ++s) {
-      const uint4 kk = *reinterpret_cast<const uint4*>(&s_k[e * kKStride + s * 32 + grp * 8]);
-      acc_r = mfma_bf16(qa[s], v4i{(int)kk.x, (int)kk.y, (int)kk.z, (int)kk.w}, acc_r);
+    for (int s = 0; s < 16; ++s) acc_l = mfma_bf16(qa[s], kf[s], acc_l);
+    acc_r = mfma_bf16(qa[16], kf[16], acc_r);
+    acc_r = mfma_bf16(qa[17], kf[17], acc_r);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    const int li = tile0 - e_begin + e;
-    const bool valid = li < n_split && s_eslot[min(li, last)] >= 0;
-    const float sc = s_scale[e];
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    const bool valid = s_valid[buf][e] != 0;
+    const float sc = s_scale[buf][e];
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sv[r] = valid ? scale * fmaf(sc, acc_l[r], acc_r[r]) : -INFINITY;
@@ -345,43 +337,75 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
       if (col == 0) s_mx[hg][half][grp * 4 + r] = mh;
     }
     lds_sync();
+    const float4 mx0 = *reinterpret_cast<const float4*>(&s_mx[hg][0][grp * 4]);
+    const float4 mx1 = *reinterpret_cast<const float4*>(&s_mx[hg][1][grp * 4]);
+    const float mt[4] = {fmaxf(mx0.x, mx1.x), fmaxf(mx0.y, mx1.y), fmaxf(mx0.z, mx1.z),
+                         fmaxf(mx0.w, mx1.w)};
+    // Both waves of the pair see the same maxima, so they take the same
+    // rescale decisions. A head moves its reference maximum only when the
+    // tile's exceeds it by more than the slack (always, the first time).
+    bool grow = false;
     float corr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float mt = fmaxf(s_mx[hg][0][grp * 4 + r], s_mx[hg][1][grp * 4 + r]);
-      const float mn = fmaxf(m[r], mt);
-      const bool dead = mn == -INFINITY;
-      corr[r] = dead ? 1.f : __expf(m[r] - mn);
-      const float pr = dead ? 0.f : __expf(sv[r] - mn);
-      l[r] = l[r] * corr[r] + row16_sum(pr);  // this half's entries; halves add up at the end
-      m[r] = mn;
+      const bool up = mt[r] > m[r] + kRescaleSlack;
+      corr[r] = up ? __expf(m[r] - mt[r]) : 1.f;  // m = -inf: 0
+      m[r] = up ? mt[r] : m[r];
+      grow |= up;
+      const float pr = sv[r] == -INFINITY ? 0.f : __expf(sv[r] - m[r]);
+      l[r] = fmaf(l[r], corr[r], pr);
       // P' = p * (value dequant scale), bf16, stored row-major [head][entry]
       s_p[hg][(grp * 4 + r) * kPStride + e] = f32_to_bf16(pr * sc);
     }
-    // a tile that raises no running maximum leaves O as it is (exactly)
-    if (__ballot(corr[0] != 1.f || corr[1] != 1.f || corr[2] != 1.f || corr[3] != 1.f)) {
+    if (__ballot(grow)) {
 #pragma unroll
       for (int n = 0; n < 16; ++n)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[n][r] *= corr[r];
     }
     lds_sync();  // both halves of P written
-    // ---- O += P V: A = P (head col, entries grp*8..+7), B = V^T rows of this half
+    // ---- O += P V: A = P (head col, entries grp*8..+7); B = V (entries
+    // grp*8..+7, dim col of block n) read from the K tile with the
+    // transposing load: in each 16-lane group, lane j receives element j % 4
+    // of the 4-element rows fetched by lanes 4k + j/4 (k = 0..3), so lane
+    // 4a + b fetches entry 8*grp + 4h + a, dims 4b..4b+3 of the block.
     const uint4 pa8 = *reinterpret_cast<const uint4*>(&s_p[hg][col * kPStride + grp * 8]);
     const v4i pa = v4i{(int)pa8.x, (int)pa8.y, (int)pa8.z, (int)pa8.w};
+    const uint16_t* vb = kt + (8 * grp + (col >> 2)) * kKStride + half * 256 + 4 * (col & 3);
+    v4i vf[16];
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
-      const uint4 v8 = *reinterpret_cast<const uint4*>(
-          &s_vt[(half * 256 + n * 16 + col) * kVtStride + grp * 8]);
-      o[n] = mfma_bf16(pa, v4i{(int)v8.x, (int)v8.y, (int)v8.z, (int)v8.w}, o[n]);
+      const v2i lo = __builtin_bit_cast(
+          v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                   (__attribute__((address_space(3))) v4s*)(vb + n * 16)));
+      const v2i hi = __builtin_bit_cast(
+          v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                   (__attribute__((address_space(3))) v4s*)(vb + 4 * kKStride + n * 16)));
+      vf[n] = v4i{lo[0], lo[1], hi[0], hi[1]};
     }
-    lds_sync();  // the tile's LDS is free for the next one
+#pragma unroll
+    for (int n = 0; n < 16; ++n) o[n] = mfma_bf16(pa, vf[n], o[n]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // ---- the next tile (its gathers landed during this one) into the other
+    // buffer, then the gathers of the tile after it (past the split: zero
+    // rows, never used; no branch, so the waits stay exact)
+    stage(buf ^ 1);
+    issue_loads(e_begin + (it + 2) * kTile);
+    lds_sync();  // next tile and P free
   }
 
-  // the row sums of the two halves
+  // the row sums: over the lanes of each row, then the two halves
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if (col == 0) s_mx[hg][half][grp * 4 + r] = l[r];
+  for (int r = 0; r < 4; ++r) {
+    const float lr = row16_sum(l[r]);
+    if (col == 0) s_mx[hg][half][grp * 4 + r] = lr;
+  }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 4; ++r) l[r] = s_mx[hg][0][grp * 4 + r] + s_mx[hg][1][grp * 4 + r];
@@ -401,7 +425,8 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
       }
     }
   } else {
-    // partials: [T][nsplit][H][512] O, then [T][nsplit][H] m and l
+    // partials: [T][nsplit][H][512] O, then [T][nsplit][H] m and l (O and l
+    // are relative to m)
     const int64_t ph = ((int64_t)t * nsplit + split) * H;
     float* po = part;
     float* pm = part + (int64_t)T * nsplit * H * kLatent;
@@ -534,15 +559,13 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   lds_sync();
   // gathers: 64 entries x 32 latent chunks of 16 B (8 per thread, one entry
   // row per 32 lanes), 64 x 8 RoPE chunks (2 per thread), 64 scales
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(q + (int64_t)t * H * kKvDim);
+  const uint8_t* dummy = g_zero_row;
   v4i lat[8], rp[2];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
     const Pick pk = pick_of(s_es[e]);
-    const v4i x = gload<v4i>(pick_base(pk, c_lat, r_lat, dummy) +
-                                                pk.slot * kLatent + 16 * c);
-    lat[k] = pk.md ? v4i{0, 0, 0, 0} : x;
+    lat[k] = gload<v4i>(pick_base(pk, c_lat, r_lat, dummy) + pk.slot * kLatent + 16 * c);
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -554,8 +577,7 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   float scv;
   {
     const Pick pk = pick_of(s_es[tid & (kChunk - 1)]);
-    const float x = gload<float>(pick_base(pk, c_sc, r_sc, dummy) + pk.slot * 4);
-    scv = pk.md ? 0.f : x;
+    scv = gload<float>(pick_base(pk, c_sc, r_sc, dummy) + pk.slot * 4);
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -661,7 +683,7 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ c_lat, const uint8_t* __restri
   }
 
   // ---- round 2: the value slice of every entry
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(pw);
+  const uint8_t* dummy = g_zero_row;
   v2i codes[kRounds][8];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r)
@@ -670,9 +692,7 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ c_lat, const uint8_t* __restri
       const int live = r * kRound + 8 * eg + j < e_pad;
       const int es = live ? sw[r][j >> 2][j & 3] : -1;
       const Pick pk = pick_of(es);
-      const v2i x = gload<v2i>(pick_base(pk, c_lat, r_lat, dummy) +
-                                                  pk.slot * kLatent + slice * kSlice + 8 * dg);
-      codes[r][j] = pk.md ? v2i{0, 0} : x;
+      codes[r][j] = gload<v2i>(pick_base(pk, c_lat, r_lat, dummy) + pk.slot * kLatent + slice * kSlice + 8 * dg);
     }
 
   // chunk factors f_c = exp(m_c - M) / L (threads 0..63: head hb0 + tid)

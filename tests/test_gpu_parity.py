@@ -327,13 +327,15 @@ def _attn_case(g, fmt, B, Ls, H, ps_c=64, extra=3):
     return pt, c4, raw
 
 
-@pytest.mark.parametrize("H,fmt,Ls", [
-    (64, "fp8", [131072 // 16, 700, 100, 2 * 4 + 1]),  # full 512 + window, short, p < 127
-    (128, "fp8", [20000, 3000]),
-    (64, "fp8", [20 + 3 * i for i in range(130)]),  # > 128 queries: split + combine path
-    (16, "f32", [4096, 333]),
+@pytest.mark.parametrize("H,fmt,Ls,out_f32", [
+    (64, "fp8", [131072 // 16, 700, 100, 2 * 4 + 1], False),  # full 512 + window, short, p < 127
+    (128, "fp8", [20000, 3000], True),  # two-phase path, fp32 output
+    (64, "fp8", [20 + 3 * i for i in range(130)], False),  # > 128 queries: split + combine path
+    (32, "fp8", [20000, 131, 9, 3000], True),  # two 16-head pairs, fp32 output
+    (16, "fp8", [5000, 700, 9], False),  # one 16-head pair
+    (16, "f32", [4096, 333], True),
 ])
-def test_csa_attention(csa, H, fmt, Ls):
+def test_csa_attention(csa, H, fmt, Ls, out_f32):
     g = gen.rng(1000 + H)
     B = len(Ls)
     pt, c4, raw = _attn_case(g, fmt, B, Ls, H)
@@ -345,10 +347,9 @@ def test_csa_attention(csa, H, fmt, Ls):
     qf = gen.normal(g, (B, H, 576))
     if fmt == "fp8":
         q, qh = _bf16(qf)
-        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
     else:
         q, qh = t_dev(qf), qf
-        out = torch.empty((B, H, 512), dtype=torch.float32, device=DEV)
+    out = torch.empty((B, H, 512), dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
     dc4, draw = kv_pool_to_device(c4, 64), kv_pool_to_device(raw, 256)
     scale = 576 ** -0.5
     csa.csa_sparse_attn(q, t_dev(np.arange(B, dtype=np.int32)), t_dev(np.array(Ls, np.int32) - 1),
