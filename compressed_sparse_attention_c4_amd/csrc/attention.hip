@@ -485,17 +485,15 @@ attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
 // of a query's entry list, all heads' scores, the chunk's softmax max m_c and
 // sum l_c, and the weights P' = exp(s - m_c) * (value FP8 scale) in bf16;
 // phase B merges the chunks' (m_c, l_c) into the exact normaliser and sums
-// f_c * (P' V) for one 64-dim slice of the value, f_c = exp(m_c - M) / L. The
-// only intermediate is P' (2 bytes per head and entry), and no merge follows.
+// f_c * (P' V) for one 64-dim slice of the value, f_c = exp(m_c - M) / L. No
+// merge follows. Phase A also copies the latent codes it gathered into one
+// contiguous [entry][64] block per value slice, so phase B reads its values,
+// weights and statistics in a single round of independent loads (no slot
+// lookup, no gather).
 constexpr int kChunk = 64;                // entries per phase-A workgroup
 constexpr int kSlice = 64;                // value dims per phase-B workgroup
-constexpr int kRound = 256;               // entries per phase-B staging task round
-constexpr int kTwoPhaseMaxE = 768;        // entry lists up to this length (3 rounds)
-constexpr int kRounds = kTwoPhaseMaxE / kRound;
-constexpr int kPvStride = kTwoPhaseMaxE + 8;  // bf16 per V^T row in phase B's LDS
-constexpr int kMaxChunks = kTwoPhaseMaxE / kChunk;
-
-
+constexpr int kTwoPhaseMaxE = 768;        // entry lists up to this length
+constexpr int kVStride = kSlice + 8;      // bf16 per value row in phase B's LDS
 
 __global__ void __launch_bounds__(256)
 attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
@@ -507,45 +505,65 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
                    const uint16_t* __restrict__ r_rope, int r_ps,
                    const int32_t* __restrict__ raw_pt, int raw_pt_stride, int window, float scale,
                    uint16_t* __restrict__ pw, float2* __restrict__ stats,
-                   int32_t* __restrict__ eslots, int e_pad, int T, int nz, int g) {
+                   uint8_t* __restrict__ vcopy, int e_pad, int T, int nz, int g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kChunk * kKStride];
   __shared__ int32_t s_es[kChunk];
   __shared__ float s_sc[kChunk];
+  __shared__ uint64_t s_la[kChunk], s_ra[kChunk];  // latent / RoPE row addresses
   const int n_chunks = e_pad / kChunk;
   const Coord bc = block_coord(n_chunks, nz, g);
   const int chunk = bc.a, t = bc.t;
   if (t >= T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
+  const int e0 = chunk * kChunk;
+  // A selected entry's slot needs nothing of the query's position: its load
+  // goes out together with the position's, one round trip earlier than a
+  // lookup that waits for the entry list.
+  int32_t pre = -1;
+  if (!hca && tid < kChunk && e0 + tid < k_sel) pre = phys_idx[(int64_t)t * k_sel + e0 + tid];
   const int seq = q_seq[t], p = q_pos[t];
   const EntryList L = entry_list(p, k_sel, hca, ratio, window);
   const int total = min(L.n1 + L.n2, e_pad);  // a list longer than the stated bound is cut
-  const int e0 = chunk * kChunk;
   const int hb0 = bc.z * 64;
+  uint8_t* vc_t = vcopy + (int64_t)t * (kLatent / kSlice) * e_pad * kSlice;
   if (e0 >= total) {
-    // past this query's list: masked slots, zero weights, dead statistics, so
-    // that phase B reads every chunk without knowing the list's length
+    // past this query's list: zero weights, dead statistics and zero values,
+    // so that phase B reads every chunk without knowing the list's length
     const int hh = tid >> 2, part = tid & 3;
     v4i* prow = reinterpret_cast<v4i*>(pw + ((int64_t)t * H + hb0 + hh) * e_pad + e0 + part * 16);
     prow[0] = v4i{0, 0, 0, 0};
     prow[1] = v4i{0, 0, 0, 0};
-    if (tid < kChunk) {
-      stats[((int64_t)t * H + hb0 + tid) * n_chunks + chunk] = make_float2(-INFINITY, 0.f);
-      if (bc.z == 0) eslots[(int64_t)t * e_pad + e0 + tid] = -1;
+    if (tid < kChunk) stats[((int64_t)t * H + hb0 + tid) * n_chunks + chunk] = make_float2(-INFINITY, 0.f);
+    if (bc.z == 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
+        *reinterpret_cast<v4i*>(vc_t + ((int64_t)(c >> 2) * e_pad + e0 + e) * kSlice + 16 * (c & 3)) =
+            v4i{0, 0, 0, 0};
+      }
     }
     return;
   }
   const int hbase = hb0 + wave * 16;
+  float scv = 0.f;
   if (tid < kChunk) {
     const int i = e0 + tid;
     int pool = 0;
-    const int64_t slot = i < total ? entry_slot(i, L, t, seq, hca, phys_idx, k_sel, comp_pt,
-                                                comp_pt_stride, c_ps, raw_pt, raw_pt_stride,
-                                                r_ps, pool)
-                                   : -1;
+    int64_t slot = -1;
+    if (i < total) {
+      if (!hca && i < L.n1) slot = pre;
+      else
+        slot = entry_slot(i, L, t, seq, hca, phys_idx, k_sel, comp_pt, comp_pt_stride, c_ps,
+                          raw_pt, raw_pt_stride, r_ps, pool);
+    }
     const int32_t w = slot >= 0 ? (int32_t)(slot * 2 + pool) : -1;
     s_es[tid] = w;
-    if (bc.z == 0) eslots[(int64_t)t * e_pad + e0 + tid] = w;
+    // every gather of the entry starts from these (masked: the zero row)
+    const Pick pk = pick_of(w);
+    s_la[tid] = pick_base(pk, c_lat, r_lat, g_zero_row) + pk.slot * kLatent;
+    s_ra[tid] = pick_base(pk, c_rope, r_rope, g_zero_row) + pk.slot * (kRope * 2);
+    scv = gload<float>(pick_base(pk, c_sc, r_sc, g_zero_row) + pk.slot * 4);
   }
   // the query operand is loaded after the slot reads, so that waiting for
   // those does not wait for these
@@ -558,26 +576,17 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   }
   lds_sync();
   // gathers: 64 entries x 32 latent chunks of 16 B (8 per thread, one entry
-  // row per 32 lanes), 64 x 8 RoPE chunks (2 per thread), 64 scales
-  const uint8_t* dummy = g_zero_row;
+  // row per 32 lanes), 64 x 8 RoPE chunks (2 per thread)
   v4i lat[8], rp[2];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
-    const Pick pk = pick_of(s_es[e]);
-    lat[k] = gload<v4i>(pick_base(pk, c_lat, r_lat, dummy) + pk.slot * kLatent + 16 * c);
+    lat[k] = gload<v4i>(s_la[e] + 16 * c);
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int idx = tid + k * 256, e = idx >> 3, c = idx & 7;
-    const Pick pk = pick_of(s_es[e]);
-    rp[k] = gload<v4i>(pick_base(pk, c_rope, r_rope, dummy) +
-                                          pk.slot * (kRope * 2) + 16 * c);
-  }
-  float scv;
-  {
-    const Pick pk = pick_of(s_es[tid & (kChunk - 1)]);
-    scv = gload<float>(pick_base(pk, c_sc, r_sc, dummy) + pk.slot * 4);
+    rp[k] = gload<v4i>(s_ra[e] + 16 * c);
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -598,22 +607,37 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
     *reinterpret_cast<v4i*>(&s_k[e * kKStride + kLatent + 8 * c]) = rp[k];
   }
   if (tid < kChunk) s_sc[tid] = scv;
+  // the codes, as gathered, into the per-slice value copy for phase B
+  if (bc.z == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
+      *reinterpret_cast<v4i*>(vc_t + ((int64_t)(c >> 2) * e_pad + e0 + e) * kSlice + 16 * (c & 3)) = lat[k];
+    }
+  }
   lds_sync();
 
-  // scores of 16 heads x 64 entries (four 16-column blocks)
+  // scores of 16 heads x 64 entries (four 16-column blocks); K fragments read
+  // six ahead of the matrix ops
   float sv[4][4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     const int e = cb * 16 + col;
+    v4i kf[18];
+#pragma unroll
+    for (int s = 0; s < 18; ++s) kf[s] = *reinterpret_cast<const v4i*>(&s_k[e * kKStride + s * 32 + grp * 8]);
     v4f acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
-      acc_l = mfma_bf16(qa[s], *reinterpret_cast<const v4i*>(&s_k[e * kKStride + s * 32 + grp * 8]),
-                        acc_l);
+    for (int s = 0; s < 16; ++s) acc_l = mfma_bf16(qa[s], kf[s], acc_l);
+    acc_r = mfma_bf16(qa[16], kf[16], acc_r);
+    acc_r = mfma_bf16(qa[17], kf[17], acc_r);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int s = 16; s < 18; ++s)
-      acc_r = mfma_bf16(qa[s], *reinterpret_cast<const v4i*>(&s_k[e * kKStride + s * 32 + grp * 8]),
-                        acc_r);
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     const bool valid = s_es[e] >= 0;
     const float sc = s_sc[e];
 #pragma unroll
@@ -637,19 +661,19 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   }
 }
 
-// Phase B needs nothing of the query but phase A's outputs: the slot words,
-// the weights and the chunk statistics of all e_pad entries (chunks past a
-// list were written as masked / zero / dead). Round 1 loads all of those at
-// once; round 2 gathers the value slice of every entry at once; then the
-// value tile is transposed into LDS and the products run.
-template <bool kOutF32>
+// Phase B needs nothing of the query but phase A's outputs: the weights, the
+// chunk statistics and the value slice of all e_pad entries (chunks past a
+// list were written as zero / dead / zero). All of it is loaded in one round;
+// the value slice goes to LDS row-major, and the P V products read their
+// value operands from it with the transposing LDS load. kNC: chunk slots
+// computed (the list's chunk count rounded up to even; extra slots are dead).
+template <int kNC, bool kOutF32>
 __global__ void __launch_bounds__(256)
-attn_pv_kernel(int H, const uint8_t* __restrict__ c_lat, const uint8_t* __restrict__ r_lat,
-               const int32_t* __restrict__ eslots, const uint16_t* __restrict__ pw,
+attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const uint16_t* __restrict__ pw,
                const float2* __restrict__ stats, int e_pad, void* __restrict__ out, int T,
                int nz, int g) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kSlice * kPvStride];
-  __shared__ float s_f[64][kMaxChunks];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kNC * kChunk * kVStride];
+  __shared__ float s_f[64][kNC];
   const Coord bc = block_coord(kLatent / kSlice, nz, g);
   const int slice = bc.a, t = bc.t;
   if (t >= T) return;
@@ -657,104 +681,88 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ c_lat, const uint8_t* __restri
   const int col = lane & 15, grp = lane >> 4;
   const int hb0 = bc.z * 64;
   const int n_chunks = e_pad / kChunk;
-  // staging task of this thread in each round: entries r*256 + 8*eg .. +7,
-  // value dims slice*64 + 8*dg .. +7 (lanes 8k..8k+7: 64 contiguous bytes)
-  const int dg = tid & 7, eg = tid >> 3;
 
-  // ---- round 1: slot words, weights, statistics
-  v4i sw[kRounds][2];
+  // ---- one round of loads: value slice (16-B pieces j = tid + 256k: entry
+  // j / 4, dims 16 (j % 4) ..), weights (A operands: 32-entry steps of this
+  // wave's 16 heads), statistics
+  constexpr int kVP = kNC * kChunk * kSlice / 16 / 256;  // value pieces per thread
+  const int nv = e_pad * (kSlice / 16);
+  const uint8_t* vsrc = vcopy + ((int64_t)t * (kLatent / kSlice) + slice) * e_pad * kSlice;
+  v4i vp[kVP];
 #pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
-    const int e = min(r * kRound + 8 * eg, e_pad - 8);
-    const v4i* src = reinterpret_cast<const v4i*>(eslots + (int64_t)t * e_pad + e);
-    sw[r][0] = src[0];
-    sw[r][1] = src[1];
-  }
+  for (int k = 0; k < kVP; ++k) vp[k] = gload<v4i>((uint64_t)(vsrc + 16 * min(tid + 256 * k, nv - 1)));
   const uint16_t* prow = pw + ((int64_t)t * H + hb0 + wave * 16 + col) * e_pad + grp * 8;
-  v4i pa[kRounds * 8];  // A operands: 32-entry steps of this wave's 16 heads
+  v4i pa[kNC * 2];
 #pragma unroll
-  for (int ks = 0; ks < kRounds * 8; ++ks)
+  for (int ks = 0; ks < kNC * 2; ++ks)
     pa[ks] = *reinterpret_cast<const v4i*>(prow + min(ks * 32, e_pad - 32));
-  float2 st[kMaxChunks];
+  float2 st[kNC];
   {
     const float2* sp = stats + ((int64_t)t * H + hb0 + (tid & 63)) * n_chunks;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) st[c] = sp[min(c, n_chunks - 1)];
+    for (int c = 0; c < kNC; ++c) st[c] = sp[min(c, n_chunks - 1)];
   }
-
-  // ---- round 2: the value slice of every entry
-  const uint8_t* dummy = g_zero_row;
-  v2i codes[kRounds][8];
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int live = r * kRound + 8 * eg + j < e_pad;
-      const int es = live ? sw[r][j >> 2][j & 3] : -1;
-      const Pick pk = pick_of(es);
-      codes[r][j] = gload<v2i>(pick_base(pk, c_lat, r_lat, dummy) + pk.slot * kLatent + slice * kSlice + 8 * dg);
-    }
 
   // chunk factors f_c = exp(m_c - M) / L (threads 0..63: head hb0 + tid)
   if (tid < 64) {
     float M = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
+    for (int c = 0; c < kNC; ++c)
       if (c < n_chunks) M = fmaxf(M, st[c].x);
     float Ls = 0.f;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
+    for (int c = 0; c < kNC; ++c)
       if (c < n_chunks && st[c].x != -INFINITY) Ls = fmaf(st[c].y, __expf(st[c].x - M), Ls);
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
+    for (int c = 0; c < kNC; ++c)
       s_f[tid][c] = (c < n_chunks && st[c].x != -INFINITY) ? __expf(st[c].x - M) * inv : 0.f;
   }
-  // V^T [dim][entry] in bf16 (exact): an 8 x 8 block per thread and round
+  // values row-major [entry][64] in bf16 (exact); rows past e_pad are zeros
 #pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
-    uint32_t kb[8][4];
+  for (int k = 0; k < kVP; ++k) {
+    const int j = tid + 256 * k;
+    const bool live = j < nv;
+    uint32_t b[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      kb[j][0] = fp8x2_to_bf16x2<false>((uint32_t)codes[r][j][0]);
-      kb[j][1] = fp8x2_to_bf16x2<true>((uint32_t)codes[r][j][0]);
-      kb[j][2] = fp8x2_to_bf16x2<false>((uint32_t)codes[r][j][1]);
-      kb[j][3] = fp8x2_to_bf16x2<true>((uint32_t)codes[r][j][1]);
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x = live ? (uint32_t)vp[k][w] : 0u;
+      b[2 * w] = fp8x2_to_bf16x2<false>(x);
+      b[2 * w + 1] = fp8x2_to_bf16x2<true>(x);
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int w = i >> 1;
-      uint32_t d[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t a = kb[2 * jj][w], b = kb[2 * jj + 1][w];
-        d[jj] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-      }
-      *reinterpret_cast<v4i*>(&s_vt[(8 * dg + i) * kPvStride + r * kRound + 8 * eg]) =
-          v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
-    }
+    uint16_t* dst = &s_v[(j >> 2) * kVStride + 16 * (j & 3)];
+    *reinterpret_cast<v4i*>(dst) = v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    *reinterpret_cast<v4i*>(dst + 8) = v4i{(int)b[4], (int)b[5], (int)b[6], (int)b[7]};
   }
   lds_sync();
 
   // Every chunk slot is computed, straight-line: a chunk past the list has
   // f_c = 0 (and finite weights and values), and without a branch per chunk
-  // the LDS reads and matrix ops of neighbouring chunks overlap.
+  // the LDS reads and matrix ops of neighbouring chunks overlap. The value
+  // operand (entries 8*grp..+7 of the step, dim col of block db) comes from
+  // two transposing reads: lane 4a + b of a 16-lane group fetches entry
+  // 8*grp + 4h + a, dims 4b..4b+3 of the block.
+  const uint16_t* vb = s_v + (8 * grp + (col >> 2)) * kVStride + 4 * (col & 3);
   v4f o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < kNC; ++c) {
     v4f acc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        acc[db] = mfma_bf16(pa[c * 2 + ks],
-                            *reinterpret_cast<const v4i*>(
-                                &s_vt[(db * 16 + col) * kPvStride + c * kChunk + ks * 32 + grp * 8]),
-                            acc[db]);
+      for (int db = 0; db < 4; ++db) {
+        const uint16_t* src = vb + (c * kChunk + ks * 32) * kVStride + 16 * db;
+        const v2i lo = __builtin_bit_cast(
+            v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)src));
+        const v2i hi = __builtin_bit_cast(
+            v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                     (__attribute__((address_space(3))) v4s*)(src + 4 * kVStride)));
+        acc[db] = mfma_bf16(pa[c * 2 + ks], v4i{lo[0], lo[1], hi[0], hi[1]}, acc[db]);
+      }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float f = s_f[wave * 16 + grp * 4 + r][c];
@@ -778,16 +786,17 @@ bool use_two_phase(int T, int H, int max_entries) {
 }
 
 // Workspace of the two-phase path: P' [T][H][e_pad] bf16, then the chunk
-// statistics [T][H][e_pad/64] float2, then the slot words [T][e_pad] int32.
+// statistics [T][H][e_pad/64] float2, then the value copy [T][8][e_pad][64]
+// (FP8 codes, one block per 64-dim slice).
 struct TwoPhaseWs {
-  size_t pw, stats, eslots, total;
+  size_t pw, stats, vcopy, total;
 };
 TwoPhaseWs two_phase_ws(int64_t T, int H, int e_pad) {
   TwoPhaseWs w;
   w.pw = 0;
   w.stats = ((size_t)T * H * e_pad * 2 + 255) / 256 * 256;
-  w.eslots = w.stats + ((size_t)T * H * (e_pad / kChunk) * sizeof(float2) + 255) / 256 * 256;
-  w.total = w.eslots + (size_t)T * e_pad * sizeof(int32_t);
+  w.vcopy = w.stats + ((size_t)T * H * (e_pad / kChunk) * sizeof(float2) + 255) / 256 * 256;
+  w.total = w.vcopy + (size_t)T * e_pad * kLatent;
   return w;
 }
 
@@ -898,7 +907,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const TwoPhaseWs w = two_phase_ws(a.T, a.H, e_pad);
     uint16_t* pw = (uint16_t*)((char*)a.ws + w.pw);
     float2* st = (float2*)((char*)a.ws + w.stats);
-    int32_t* es = (int32_t*)((char*)a.ws + w.eslots);
+    uint8_t* vc = (uint8_t*)a.ws + w.vcopy;
     const int nz = a.H / 64;
     const int g = xcd_group(a.T);
     hipLaunchKernelGGL(attn_scores_kernel, xcd_grid(e_pad / kChunk, nz, a.T), dim3(256), 0, s,
@@ -907,15 +916,27 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
                        (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt, a.comp_pt_stride,
                        (const uint8_t*)a.raw.latent, a.raw.latent_scale,
                        (const uint16_t*)a.raw.rope, a.raw.page_size, a.raw_pt, a.raw_pt_stride,
-                       a.window, a.scale, pw, st, es, e_pad, a.T, nz, g);
+                       a.window, a.scale, pw, st, vc, e_pad, a.T, nz, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-#define CSA_PV(FO)                                                                             \
-  hipLaunchKernelGGL(attn_pv_kernel<FO>, xcd_grid(kLatent / kSlice, nz, a.T), dim3(256), 0, s, a.H,  \
-                     (const uint8_t*)a.comp.latent, (const uint8_t*)a.raw.latent, es, pw, st, e_pad, \
-                     a.out, a.T, nz, g)
-    if (a.out_fmt == CSA_F32) CSA_PV(true);
-    else CSA_PV(false);
+#define CSA_PV(NC, FO)                                                                         \
+  hipLaunchKernelGGL((attn_pv_kernel<NC, FO>), xcd_grid(kLatent / kSlice, nz, a.T), dim3(256), 0, s, \
+                     a.H, vc, pw, st, e_pad, a.out, a.T, nz, g)
+#define CSA_PV_NC(NC)                \
+  case NC:                           \
+    if (a.out_fmt == CSA_F32) CSA_PV(NC, true); \
+    else CSA_PV(NC, false);          \
+    break;
+    switch ((e_pad / kChunk + 1) / 2 * 2) {
+      CSA_PV_NC(2)
+      CSA_PV_NC(4)
+      CSA_PV_NC(6)
+      CSA_PV_NC(8)
+      CSA_PV_NC(10)
+      CSA_PV_NC(12)
+      default: return hipErrorInvalidValue;
+    }
+#undef CSA_PV_NC
 #undef CSA_PV
     return hipGetLastError();
   }
