@@ -20,7 +20,7 @@ lib = C.CDLL(LIB_PATH)
 CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = range(5)
 CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4 = range(4)
 CSA_PREP_HADAMARD, CSA_PREP_QUANT = 1, 2
-CSA_OP_INDEXER, CSA_OP_TOPK, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN = range(4)
+CSA_OP_INDEXER, CSA_OP_TOPK, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN, CSA_OP_INDEXER_TOPK = range(5)
 CSA_TOPK, CSA_C4_RATIO, CSA_HCA_RATIO, CSA_RAW_PAGE, CSA_C4_PAGE = 512, 4, 128, 256, 64
 
 
@@ -51,6 +51,9 @@ _decode_prep = _decl("csa_decode_prep", [_vp, _i32, _vp, _i32, _i32, _vp, _vp, _
                                          _IndexPoolC, _vp, _vp, _vp])
 _indexer_score = _decl("indexer_score", [_vp, _i32, _vp, _u32, _vp, _i32, _i32, _i32, _vp, _vp, _i32,
                                          _vp, _i32, _IndexPoolC, _vp, _i64, _vp, _vp, _vp, _sz, _vp])
+_indexer_topk = _decl("indexer_topk512", [_vp, _i32, _vp, _u32, _vp, _i32, _i32, _i32, _vp, _vp, _i32,
+                                          _vp, _i32, _IndexPoolC, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+                                          _vp])
 _topk = _decl("topk512_page_select", [_vp, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
 _csa_attn = _decl("csa_sparse_attn", [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _KvPoolC, _KvPoolC,
                                       _vp, _i32, _i32, _f32, _vp, _i32, _vp, _sz, _vp])
@@ -186,6 +189,29 @@ def indexer_score(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPool,
         _ptr(row_len), int(max_row_len), _ptr(page_table), page_table.shape[-1], k.c(),
         _ptr(logits), logits.shape[-1], _ptr(q_used), _ptr(q_used_scale), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def indexer_topk512(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPool, phys_idx,
+                    logical_idx=None, *, q_fmt=None, q_scale=None, prep=0, q_used=None,
+                    q_used_scale=None, ws=None, scan_done=None, stream=None):
+    """scan_done: optional torch.cuda.Event, recorded right after the scan launch."""
+    T, H_I = w.shape
+    if ws is None:
+        n = csa_workspace_size(CSA_OP_INDEXER_TOPK, T, max_row_len, H_I)
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    ev = None
+    if scan_done is not None:
+        # the handle exists after a first record; recording it here, in front
+        # of the scan, costs a few microseconds of stream time, so a caller
+        # that times the scan records its events once beforehand
+        if not scan_done.cuda_event:
+            scan_done.record()
+        ev = scan_done.cuda_event
+    _check("indexer_topk512", _indexer_topk(
+        _ptr(q), _fmt_of(q, q_fmt), _ptr(q_scale), int(prep), _ptr(w), T, H_I, k.dim, _ptr(row_seq),
+        _ptr(row_len), int(max_row_len), _ptr(page_table), page_table.shape[-1], k.c(),
+        _ptr(phys_idx), _ptr(logical_idx), _ptr(q_used), _ptr(q_used_scale), _ptr(ws),
+        ws.numel(), ev, _stream(stream)))
 
 
 def topk512_page_select(logits, row_len, row_seq, page_table, phys_idx, logical_idx=None,

@@ -2,6 +2,8 @@
 // argument checks (before any launch), then the kernel launchers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "../../include/csa.h"
 #include "csa_internal.hpp"
 
@@ -17,7 +19,68 @@ inline bool kv_pool_ok(const csa_kv_pool& p) {
   return p.fmt == CSA_F32;
 }
 
+// Argument checks shared by indexer_score and indexer_topk512 (everything but
+// the output); CSA_OK when the call may proceed.
+csa_status indexer_args(csa_fmt q_fmt, const void* q_scale, uint32_t prep, int32_t T, int32_t H_I,
+                        int32_t D_I, int32_t max_row_len, int32_t pt_stride,
+                        const csa_index_pool& k, const void* q_used, const void* q_used_scale,
+                        const void* ws, size_t ws_bytes) {
+  if (T < 0 || H_I <= 0 || max_row_len < 0 || pt_stride <= 0) return CSA_ERR_INVALID;
+  if (k.page_size <= 0 || k.dim != D_I) return CSA_ERR_INVALID;
+  if ((q_used == nullptr) != (q_used_scale == nullptr)) return CSA_ERR_INVALID;
+  if (prep & ~(CSA_PREP_HADAMARD | CSA_PREP_QUANT)) return CSA_ERR_INVALID;
+  if (k.fmt == CSA_F32) {
+    if (q_fmt != CSA_F32 || prep != 0) return CSA_ERR_INVALID;
+    if (D_I != 64 && D_I != 128) return CSA_ERR_UNSUPPORTED;
+    if ((size_t)H_I * D_I > 8192) return CSA_ERR_UNSUPPORTED;
+    if (q_used) return CSA_ERR_INVALID;
+  } else if (k.fmt == CSA_FP8_E4M3 || k.fmt == CSA_MXFP4) {
+    if (H_I != 64 || D_I != 128) return CSA_ERR_UNSUPPORTED;
+    if (k.page_size % 16 != 0) return CSA_ERR_UNSUPPORTED;
+    if (!k.scale) return CSA_ERR_INVALID;
+    if (q_fmt == CSA_BF16 || q_fmt == CSA_F32) {
+      if (!(prep & CSA_PREP_QUANT)) return CSA_ERR_INVALID;
+      if (!q_used && ws_bytes < indexer_ws_bytes(T, H_I)) return CSA_ERR_WORKSPACE;
+      if (!q_used && !ws) return CSA_ERR_WORKSPACE;
+    } else if (q_fmt == k.fmt) {
+      if (prep != 0 || !q_scale) return CSA_ERR_INVALID;
+    } else {
+      return CSA_ERR_INVALID;
+    }
+  } else {
+    return CSA_ERR_INVALID;
+  }
+  return CSA_OK;
+}
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// indexer_topk512's workspace: the query-preparation area, then either the
+// scan's top-512 candidates (fused path) or the logits and the top-512
+// workspace (two-call path); sized for whichever is larger.
+struct IdxTopkWs {
+  size_t prep, cand, logits, topk, total;
+  int64_t ld;
+};
+IdxTopkWs idx_topk_ws(int64_t T, int64_t max_row_len, int H_I) {
+  IdxTopkWs w{};
+  w.prep = align256(indexer_ws_bytes(T, H_I));
+  const int64_t chunks = indexer_scan_chunks(T, max_row_len);
+  w.cand = align256((size_t)T * chunks * CSA_TOPK * sizeof(uint32_t));
+  w.ld = std::max<int64_t>(64, (max_row_len + 63) / 64 * 64);
+  w.logits = align256((size_t)T * w.ld * sizeof(float));
+  w.topk = align256(topk_ws_bytes(T, w.ld));
+  w.total = w.prep + std::max(2 * w.cand, w.logits + w.topk);
+  return w;
+}
+
 }  // namespace
+
+namespace csa {
+size_t indexer_topk_ws_bytes(int64_t T, int64_t max_row_len, int H_I) {
+  return idx_topk_ws(T, max_row_len, H_I).total;
+}
+}  // namespace csa
 
 extern "C" {
 
@@ -41,6 +104,7 @@ size_t csa_workspace_size(int32_t op, int64_t rows, int64_t max_len, int32_t hea
     case CSA_OP_TOPK: return topk_ws_bytes(rows, max_len);  // max_len = ld
     case CSA_OP_CSA_ATTN:
     case CSA_OP_HCA_ATTN: return attention_ws_bytes(rows, max_len, heads);
+    case CSA_OP_INDEXER_TOPK: return indexer_topk_ws_bytes(rows, max_len, heads);
     default: return 0;
   }
 }
@@ -112,31 +176,10 @@ csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint
                          const int32_t* page_table, int32_t pt_stride, csa_index_pool k,
                          float* logits, int64_t ld, void* q_used, void* q_used_scale, void* ws,
                          size_t ws_bytes, hipStream_t stream) {
-  if (T < 0 || H_I <= 0 || max_row_len < 0 || pt_stride <= 0 || ld < max_row_len) return CSA_ERR_INVALID;
-  if (k.page_size <= 0 || k.dim != D_I) return CSA_ERR_INVALID;
-  if ((q_used == nullptr) != (q_used_scale == nullptr)) return CSA_ERR_INVALID;
-  if (prep & ~(CSA_PREP_HADAMARD | CSA_PREP_QUANT)) return CSA_ERR_INVALID;
-  if (k.fmt == CSA_F32) {
-    if (q_fmt != CSA_F32 || prep != 0) return CSA_ERR_INVALID;
-    if (D_I != 64 && D_I != 128) return CSA_ERR_UNSUPPORTED;
-    if ((size_t)H_I * D_I > 8192) return CSA_ERR_UNSUPPORTED;
-    if (q_used) return CSA_ERR_INVALID;
-  } else if (k.fmt == CSA_FP8_E4M3 || k.fmt == CSA_MXFP4) {
-    if (H_I != 64 || D_I != 128) return CSA_ERR_UNSUPPORTED;
-    if (k.page_size % 16 != 0) return CSA_ERR_UNSUPPORTED;
-    if (!k.scale) return CSA_ERR_INVALID;
-    if (q_fmt == CSA_BF16 || q_fmt == CSA_F32) {
-      if (!(prep & CSA_PREP_QUANT)) return CSA_ERR_INVALID;
-      if (!q_used && ws_bytes < indexer_ws_bytes(T, H_I)) return CSA_ERR_WORKSPACE;
-      if (!q_used && !ws) return CSA_ERR_WORKSPACE;
-    } else if (q_fmt == k.fmt) {
-      if (prep != 0 || !q_scale) return CSA_ERR_INVALID;
-    } else {
-      return CSA_ERR_INVALID;
-    }
-  } else {
-    return CSA_ERR_INVALID;
-  }
+  if (ld < max_row_len) return CSA_ERR_INVALID;
+  const csa_status st = indexer_args(q_fmt, q_scale, prep, T, H_I, D_I, max_row_len, pt_stride, k,
+                                     q_used, q_used_scale, ws, ws_bytes);
+  if (st != CSA_OK) return st;
   if (T == 0 || max_row_len == 0) return CSA_OK;
   if (!q || !w || !row_seq || !row_len || !page_table || !k.data || !logits) return CSA_ERR_INVALID;
   return hip_status(launch_indexer(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len,
@@ -157,6 +200,46 @@ csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
   if (need > ws_bytes || (need > 0 && !ws)) return CSA_ERR_WORKSPACE;
   return hip_status(launch_topk(logits, ld, R, row_len, row_seq, page_table, pt_stride,
                                 c4_page_size, 0, phys_idx, logical_idx, ws, stream));
+}
+
+csa_status indexer_topk512(const void* q, csa_fmt q_fmt, const void* q_scale, uint32_t prep,
+                           const float* w, int32_t T, int32_t H_I, int32_t D_I,
+                           const int32_t* row_seq, const int32_t* row_len, int32_t max_row_len,
+                           const int32_t* page_table, int32_t pt_stride, csa_index_pool k,
+                           int32_t* phys_idx, int32_t* logical_idx, void* q_used,
+                           void* q_used_scale, void* ws, size_t ws_bytes, hipEvent_t scan_done,
+                           hipStream_t stream) {
+  const csa_status st = indexer_args(q_fmt, q_scale, prep, T, H_I, D_I, max_row_len, pt_stride, k,
+                                     q_used, q_used_scale, ws, ws_bytes);
+  if (st != CSA_OK) return st;
+  if (max_row_len > topk_max_len()) return CSA_ERR_UNSUPPORTED;
+  if (T == 0) return CSA_OK;
+  const IdxTopkWs L = idx_topk_ws(T, max_row_len, H_I);
+  if (!ws || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
+  if (!q || !w || !row_seq || !row_len || !page_table || !k.data || !phys_idx) return CSA_ERR_INVALID;
+  uint8_t* base = (uint8_t*)ws;
+  const int chunks = indexer_cand_chunks(T, H_I, D_I, k, max_row_len);
+  hipError_t e;
+  if (chunks > 0) {
+    uint32_t* ck = (uint32_t*)(base + L.prep);
+    int32_t* cj = (int32_t*)(base + L.prep + L.cand);
+    e = launch_indexer(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len, max_row_len,
+                       page_table, pt_stride, k, nullptr, 0, q_used, q_used_scale, base, stream,
+                       ck, cj);
+    if (e == hipSuccess && scan_done) e = hipEventRecord(scan_done, stream);
+    if (e == hipSuccess)
+      e = launch_topk_cand_final(ck, cj, chunks * CSA_TOPK, T, row_len, row_seq, page_table,
+                                 pt_stride, k.page_size, phys_idx, logical_idx, stream);
+  } else {
+    float* logits = (float*)(base + L.prep);
+    e = launch_indexer(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len, max_row_len,
+                       page_table, pt_stride, k, logits, L.ld, q_used, q_used_scale, base, stream);
+    if (e == hipSuccess && scan_done) e = hipEventRecord(scan_done, stream);
+    if (e == hipSuccess)
+      e = launch_topk(logits, L.ld, T, row_len, row_seq, page_table, pt_stride, k.page_size, 0,
+                      phys_idx, logical_idx, base + L.prep + L.logits, stream);
+  }
+  return hip_status(e);
 }
 
 static csa_status attn_common(AttnArgs& a, hipStream_t stream) {

@@ -17,12 +17,14 @@
 // contiguous 2 KB / 1 KB read), the query sits in registers, and ReLU, the
 // head weights and the 64-head reduction run in the epilogue on the
 // accumulators.
+#include <limits.h>
 #include <stdlib.h>
 
 #include <type_traits>
 
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
+#include "topk_select.hpp"
 
 namespace csa {
 namespace {
@@ -48,21 +50,43 @@ __device__ __forceinline__ v4f mfma_fp4(const v8i& a, const v8i& b, v4f c, int s
 // that K-range is one 32-element scale block, whose e8m0 byte the lane
 // supplies as its scale. The result lane l holds rows 4*(l/16) + 0..3 of
 // column l % 16.
-template <bool kFp4, bool kPage64>
-__global__ void __launch_bounds__(kWaves * 64)
+//
+// kCand: instead of the logits, the workgroup writes its chunk's top-512
+// candidates (order-preserving keys and entry indices, in index order; a chunk
+// past the row writes padding: key 0, index INT_MAX), selected from the logits
+// in LDS exactly as the top-512 kernel's chunk pass selects them from memory.
+// Any entry of a row's top-512 is in its chunk's top-512, so the top-512 of the
+// candidates is the row's. The kCand workgroup has kSelWaves waves: the first
+// kWaves scan, all of them select (fewer keys per lane, the same barriers).
+constexpr int kSelWaves = 8;
+template <bool kCand>
+constexpr int idx_threads() { return (kCand ? kSelWaves : kWaves) * 64; }
+
+template <bool kFp4, bool kPage64, bool kCand>
+__global__ void __launch_bounds__(idx_threads<kCand>())
 indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     const float* __restrict__ w, const int32_t* __restrict__ row_seq,
                     const int32_t* __restrict__ row_len, const int32_t* __restrict__ pt,
                     int pt_stride, const uint8_t* __restrict__ kdata,
                     const void* __restrict__ kscale, int page_size, float* __restrict__ logits,
-                    int64_t ld, int chunk) {
+                    int64_t ld, int chunk, uint32_t* __restrict__ okeys,
+                    int32_t* __restrict__ ojs) {
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K / q row
   __shared__ int32_t s_pages[kMaxChunk / 16 + 2];      // physical pages of this chunk
   __shared__ __attribute__((aligned(16))) float s_out[kMaxChunk + 64];  // the chunk's logits
   const int t = blockIdx.y;
   const int n = row_len[t];
   const int c0 = blockIdx.x * chunk;
-  if (c0 >= n) return;
+  if (c0 >= n) {
+    if constexpr (kCand) {
+      for (int p = threadIdx.x; p < kTopK; p += idx_threads<kCand>()) {
+        const int64_t o = ((int64_t)t * gridDim.x + blockIdx.x) * kTopK + p;
+        okeys[o] = 0u;
+        ojs[o] = INT_MAX;
+      }
+    }
+    return;
+  }
   const int c1 = min(c0 + chunk, n);
   const int seq = row_seq[t];
   const int lane = threadIdx.x & 63;
@@ -75,8 +99,11 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   const int32_t* ptrow = pt + (int64_t)seq * pt_stride;
   const int pg0 = c0 / page_size;
   const int npg = (c1 - 1) / page_size - pg0 + 1;
-  for (int i = threadIdx.x; i < npg; i += kWaves * 64) s_pages[i] = ptrow[pg0 + i];
+  for (int i = threadIdx.x; i < npg; i += idx_threads<kCand>()) s_pages[i] = ptrow[pg0 + i];
 
+  if (kCand && wave >= kWaves) {
+    __syncthreads();  // the page ids (the scan waves pass the same barrier)
+  } else {
   // Query operands: head hb*16 + col, K-elements grp*32 .. grp*32+31.
   v8i a[4];
   int sa[4];
@@ -202,10 +229,33 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
     step(i0, std::integral_constant<int, 0>{});
     step(i0 + 1, std::integral_constant<int, 1>{});
   }
+  }  // scan waves
   __syncthreads();
-  float* orow = logits + (int64_t)t * ld + c0;
   const int n_out = c1 - c0;
-  for (int j = threadIdx.x; j < n_out; j += kWaves * 64) orow[j] = s_out[j];
+  if constexpr (kCand) {
+    // keys from LDS: element seg + 64 i + lane of this wave's segment
+    constexpr int kTH = idx_threads<kCand>();
+    constexpr int kE = kMaxChunk / kTH;
+    __shared__ TopkLds L;
+    for (int i = threadIdx.x; i < kTopkBins; i += kTH) L.hist[i] = 0u;
+    const int seg = wave * 64 * kE;
+    uint32_t kr[kE];
+#pragma unroll
+    for (int i = 0; i < kE; ++i) {
+      const int e = seg + 64 * i + lane;
+      kr[i] = e < n_out ? float_key(s_out[e]) : 0u;
+    }
+    const int K = min(kTopK, n_out);
+    topk_select<kE, kTH>(kr, n_out, K, seg, L);
+    for (int p = threadIdx.x; p < kTopK; p += kTH) {
+      const int64_t o = ((int64_t)t * gridDim.x + blockIdx.x) * kTopK + p;
+      okeys[o] = p < K ? L.out_k[p] : 0u;
+      ojs[o] = p < K ? c0 + L.out_e[p] : INT_MAX;
+    }
+  } else {
+    float* orow = logits + (int64_t)t * ld + c0;
+    for (int j = threadIdx.x; j < n_out; j += kWaves * 64) orow[j] = s_out[j];
+  }
 }
 
 // Many query rows (prefill): a workgroup of 8 waves owns 8 consecutive rows
@@ -432,11 +482,46 @@ size_t indexer_ws_bytes(int64_t T, int H_I) {
   return codes + (((size_t)T * H_I * 4 + 255) & ~(size_t)255);
 }
 
+// Entries per scan workgroup: the rows are chunked so the grid has ~256
+// workgroups (one per CU), each wave a long stream: measured on MI355X, one
+// workgroup per CU streams faster than two (fewer concurrent page streams);
+// CSA_TUNE_INDEXER_WGS overrides the target (tuning only).
+static int64_t scan_chunk(int64_t T, int64_t max_row_len) {
+  int64_t target = 256;
+  if (const char* e = getenv("CSA_TUNE_INDEXER_WGS")) target = atoll(e) > 0 ? atoll(e) : target;
+  const int64_t total = T * max_row_len;
+  int64_t chunk = total / target;
+  chunk = ((chunk + kWgEntries - 1) / kWgEntries) * kWgEntries;
+  if (chunk < kWgEntries) chunk = kWgEntries;
+  if (chunk > kMaxChunk) chunk = kMaxChunk;
+  return chunk;
+}
+
+// Many rows over 64-entry pages go to the row-block kernel.
+static bool uses_rows_kernel(int64_t T, const csa_index_pool& k) {
+  return T >= kRowsPerWG * 32 && k.page_size == 64 && !getenv("CSA_TUNE_INDEXER_NO_ROWS");
+}
+
+int64_t indexer_scan_chunks(int64_t T, int64_t max_row_len) {
+  const int64_t c = scan_chunk(T, max_row_len);
+  return (max_row_len + c - 1) / c;
+}
+
+int indexer_cand_chunks(int64_t T, int H_I, int D_I, const csa_index_pool& k,
+                        int64_t max_row_len) {
+  if (k.fmt != CSA_FP8_E4M3 && k.fmt != CSA_MXFP4) return 0;
+  if (H_I != kHeads || D_I != kDim || k.page_size % 16 != 0) return 0;
+  if (T == 0 || max_row_len == 0 || uses_rows_kernel(T, k)) return 0;
+  const int64_t chunks = indexer_scan_chunks(T, max_row_len);
+  return chunks * kTopK <= kCandFinalMax ? (int)chunks : 0;
+}
+
 hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_t prep,
                           const float* w, int T, int H_I, int D_I, const int32_t* row_seq,
                           const int32_t* row_len, int max_row_len, const int32_t* page_table,
                           int pt_stride, const csa_index_pool& k, float* logits, int64_t ld,
-                          void* q_used, void* q_used_scale, void* ws, hipStream_t s) {
+                          void* q_used, void* q_used_scale, void* ws, hipStream_t s,
+                          uint32_t* okeys, int32_t* ojs) {
   if (T == 0 || max_row_len == 0) return hipSuccess;
   if (k.fmt == CSA_F32) {
     dim3 grid((max_row_len + 255) / 256, T);
@@ -470,18 +555,8 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
       e = hipMemcpyAsync(q_used_scale, q_scale, scale_bytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
-  // Chunk the rows so the grid has ~256 workgroups (one per CU), each wave a
-  // long stream: measured on MI355X, one workgroup per CU streams faster than
-  // two (fewer concurrent page streams); CSA_TUNE_INDEXER_WGS overrides the
-  // target (tuning only).
-  int64_t target = 256;
-  if (const char* e = getenv("CSA_TUNE_INDEXER_WGS")) target = atoll(e) > 0 ? atoll(e) : target;
-  int64_t total = (int64_t)T * max_row_len;
-  int64_t chunk = total / target;
-  chunk = ((chunk + kWgEntries - 1) / kWgEntries) * kWgEntries;
-  if (chunk < kWgEntries) chunk = kWgEntries;
-  if (chunk > kMaxChunk) chunk = kMaxChunk;
-  if (T >= kRowsPerWG * 32 && k.page_size == 64 && !getenv("CSA_TUNE_INDEXER_NO_ROWS")) {
+  const int64_t chunk = scan_chunk(T, max_row_len);
+  if (!okeys && uses_rows_kernel(T, k)) {
     dim3 g2((T + kRowsPerWG - 1) / kRowsPerWG);
     if (k.fmt == CSA_MXFP4)
       hipLaunchKernelGGL(indexer_rows_kernel<true>, g2, dim3(kRowsPerWG * 64), 0, s, qc, qs, w,
@@ -494,18 +569,21 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
     return hipGetLastError();
   }
   dim3 grid((unsigned)((max_row_len + chunk - 1) / chunk), T);
-#define CSA_IDX(FP4, P64)                                                                      \
-  hipLaunchKernelGGL((indexer_mfma_kernel<FP4, P64>), grid, dim3(kWaves * 64), 0, s, qc, qs, w, \
-                     row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data, k.scale,    \
-                     k.page_size, logits, ld, (int)chunk)
-  const bool p64 = k.page_size == 64;
-  if (k.fmt == CSA_MXFP4) {
-    if (p64) CSA_IDX(true, true);
-    else CSA_IDX(true, false);
+#define CSA_IDX(FP4, P64, CAND)                                                                    \
+  hipLaunchKernelGGL((indexer_mfma_kernel<FP4, P64, CAND>), grid, dim3(idx_threads<CAND>()), 0, s, qc, qs, \
+                     w, row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data, k.scale,  \
+                     k.page_size, logits, ld, (int)chunk, okeys, ojs)
+#define CSA_IDX_P(FP4, CAND)                 \
+  if (k.page_size == 64) CSA_IDX(FP4, true, CAND); \
+  else CSA_IDX(FP4, false, CAND);
+  if (okeys) {
+    if (k.fmt == CSA_MXFP4) { CSA_IDX_P(true, true) }
+    else { CSA_IDX_P(false, true) }
   } else {
-    if (p64) CSA_IDX(false, true);
-    else CSA_IDX(false, false);
+    if (k.fmt == CSA_MXFP4) { CSA_IDX_P(true, false) }
+    else { CSA_IDX_P(false, false) }
   }
+#undef CSA_IDX_P
 #undef CSA_IDX
   return hipGetLastError();
 }

@@ -35,87 +35,16 @@
 
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
+#include "topk_select.hpp"
 
 namespace csa {
 namespace {
 
 constexpr int kThreads = 1024;             // workgroup of whole rows and of the final merge
-constexpr int kWaves = kThreads / 64;
 constexpr int kMaxE = 32;                    // keys per lane (held in registers)
 constexpr int kRegRow = kThreads * kMaxE;    // longest row selected in one launch
-constexpr int kBins = 3072;                  // >= 2049 buckets, multiple of every workgroup size
-constexpr int kCandCap = 2048;               // threshold-bucket keys listed in LDS
 
 enum Mode { kRowFinal = 0, kChunkCand = 1, kCandFinal = 2 };
-
-// Exclusive scan of one uint32 per wave (value taken from lane 0 of each
-// wave) over the workgroup's TH/64 waves; returns this wave's offset, sets total.
-template <int TH>
-__device__ __forceinline__ uint32_t wave_offsets(uint32_t v, uint32_t* sh, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) sh[wave] = v;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-  for (int w = 0; w < TH / 64; ++w) {
-    const uint32_t x = sh[w];
-    off += (w < wave) ? x : 0u;
-    tot += x;
-  }
-  __syncthreads();
-  total = tot;
-  return off;
-}
-
-// hist[bin] += 1 for every lane with valid set. Lanes that hit the same bin
-// are merged into one atomic while groups are large; once a peeled group is a
-// single lane the rest add directly.
-__device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t bin, bool valid) {
-  const int lane = threadIdx.x & 63;
-  uint64_t active = __ballot(valid);
-  for (int it = 0; it < 8 && active; ++it) {
-    const int leader = __ffsll((unsigned long long)active) - 1;
-    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
-    const uint64_t same = __ballot(valid && bin == lb) & active;
-    const uint32_t cnt = (uint32_t)__popcll(same);
-    if (lane == leader) atomicAdd(&hist[lb], cnt);
-    active &= ~same;
-    if (cnt == 1) break;
-  }
-  if ((active >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
-}
-
-// Bucket (scanning from the top of hist[0..nbins)) where the running count
-// reaches k; *sel_bin = bucket, *sel_above = count strictly above it.
-template <int TH>
-__device__ __forceinline__ void find_bucket(const uint32_t* hist, int nbins, uint32_t k,
-                                            uint32_t* scan_sh, uint32_t* sel_bin,
-                                            uint32_t* sel_above) {
-  const int per = nbins / TH;
-  uint32_t c = 0;
-  for (int q = 0; q < per; ++q) c += hist[nbins - 1 - per * threadIdx.x - q];
-  // block exclusive scan of c in thread order (thread 0 = top bins)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  (void)lane;
-  (void)wave;
-  const uint32_t x = wave_inclusive_scan(c);
-  uint32_t tot;
-  const uint32_t woff =
-      wave_offsets<TH>((uint32_t)__builtin_amdgcn_readlane((int)x, 63), scan_sh, tot);
-  uint32_t above = woff + x - c;
-  if (above < k && above + c >= k) {
-    for (int q = 0; q < per; ++q) {
-      const int bin = nbins - 1 - per * threadIdx.x - q;
-      const uint32_t h = hist[bin];
-      if (above + h >= k) {
-        *sel_bin = (uint32_t)bin;
-        *sel_above = above;
-        break;
-      }
-      above += h;
-    }
-  }
-  __syncthreads();
-}
 
 template <int kMode, int kE, int TH>
 __global__ void __launch_bounds__(TH)
@@ -126,13 +55,7 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
             int32_t* __restrict__ phys_idx, int32_t* __restrict__ logical_idx,
             uint32_t* __restrict__ okeys, int32_t* __restrict__ ojs) {
   static_assert(kE >= 1 && kE <= kMaxE, "keys per lane");
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t red[2 * kWaves];
-  __shared__ uint32_t sel_bin, sel_above;
-  __shared__ uint32_t s_thr, s_need;     // threshold of a short bucket
-  __shared__ uint32_t s_cand[kCandCap];  // keys of the threshold bucket
-  __shared__ int32_t s_out_e[kTopK];     // element placed at each output position
-  __shared__ uint32_t s_out_k[kTopK];    // and its key
+  __shared__ TopkLds L;
 
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -152,7 +75,7 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
   const int seg = wave * 64 * kE;                          // first element of this wave
 
   // the histogram is cleared while the keys are in flight
-  for (int i = threadIdx.x; i < kBins; i += TH) hist[i] = 0u;
+  for (int i = threadIdx.x; i < kTopkBins; i += TH) L.hist[i] = 0u;
   // Keys stay in registers: element seg + 64 i + lane is key kr[i] of this
   // lane (coalesced loads, all issued at once). An element's index is
   // base + e, or (candidates) re-read at emission, which touches only the
@@ -173,170 +96,17 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
       kr[i] = ok ? k : 0u;
     }
   }
-  uint32_t thr = 0, need = 0;
-  const bool take_all = n <= K;  // every element is selected
-  if (!take_all) {
-    // ---- 1. key range of the non-NaN keys
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-    for (int i = 0; i < kE; ++i) {
-      if (kr[i] != 0u) {
-        kmin = min(kmin, kr[i]);
-        kmax = max(kmax, kr[i]);
-      }
-    }
-    kmin = wave_umin(kmin);
-    kmax = wave_umax(kmax);
-    if (lane == 0) {
-      red[wave] = kmin;
-      red[kWaves + wave] = kmax;
-    }
-    __syncthreads();
-    kmin = 0xFFFFFFFFu;
-    kmax = 0u;
-    for (int w = 0; w < TH / 64; ++w) {
-      kmin = min(kmin, red[w]);
-      kmax = max(kmax, red[kWaves + w]);
-    }
-    if (kmin > kmax) kmin = kmax = 0u;  // every key is NaN
-    const uint32_t range = kmax - kmin;
-    const int sh = range == 0u ? 0 : max(0, (32 - __clz(range)) - 11);
-    auto bin_of = [&](uint32_t k) -> uint32_t { return k == 0u ? 0u : 1u + ((k - kmin) >> sh); };
-
-    // ---- 2. bucket of the K-th largest key
-#pragma unroll
-    for (int i = 0; i < kE; ++i) atomicAdd(&hist[bin_of(kr[i])], 1u);
-    __syncthreads();
-    find_bucket<TH>(hist, kBins, (uint32_t)K, red, &sel_bin, &sel_above);
-    const uint32_t bstar = sel_bin;
-    uint32_t k = (uint32_t)K - sel_above;
-
-    // ---- 3. exact threshold inside the bucket (its keys share everything
-    // above the low sh bits of key - kmin; bucket 0 holds only key 0, so it
-    // needs no refinement). The bucket's members are gathered into a short
-    // LDS list when they fit.
-    const uint32_t nb = hist[bstar];
-    const bool listed = bstar != 0u && nb <= (uint32_t)kCandCap;
-    __syncthreads();
-    if (listed) {
-      if (threadIdx.x == 0) sel_above = 0;  // reused as the list length
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kE; ++i)
-        if (bin_of(kr[i]) == bstar) s_cand[atomicAdd(&sel_above, 1u)] = kr[i];
-      __syncthreads();
-    }
-    uint32_t low = 0;  // threshold's low bits, built from the top
-    int width = bstar == 0u ? 0 : sh;
-    if (listed && nb <= (uint32_t)TH) {
-      // a short bucket: each listed key counts the keys above and equal to
-      // it; the key whose range of ranks covers k is the threshold (every
-      // thread holding that key writes the same values)
-      if (threadIdx.x < nb) {
-        const uint32_t c = s_cand[threadIdx.x];
-        uint32_t gt = 0, eq = 0;
-        int i = 0;
-        for (; i + 4 <= (int)nb; i += 4) {
-          const uint4 x = *reinterpret_cast<const uint4*>(&s_cand[i]);
-          gt += (x.x > c) + (x.y > c) + (x.z > c) + (x.w > c);
-          eq += (x.x == c) + (x.y == c) + (x.z == c) + (x.w == c);
-        }
-        for (; i < (int)nb; ++i) {
-          const uint32_t x = s_cand[i];
-          gt += x > c;
-          eq += x == c;
-        }
-        if (gt < k && k <= gt + eq) {
-          s_thr = c;
-          s_need = k - gt;
-        }
-      }
-      __syncthreads();
-      thr = s_thr;
-      need = s_need;
-      width = -1;  // done
-    }
-    uint32_t got_mask = 0;  // bits of the low part fixed so far
-    while (width > 0) {
-      const int w = min(11, width);
-      const int shift = width - w;
-      const uint32_t dmask = (1u << w) - 1u;
-      __syncthreads();
-      for (int i = threadIdx.x; i < kBins; i += TH) hist[i] = 0u;
-      __syncthreads();
-      if (listed) {
-        for (int i = threadIdx.x; i < (int)nb; i += TH) {
-          const uint32_t lo = (s_cand[i] - kmin) & ((1u << sh) - 1u);  // sh <= 21
-          if ((lo & got_mask) == low) atomicAdd(&hist[(lo >> shift) & dmask], 1u);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kE; ++i) {
-          const uint32_t kk = kr[i];
-          const uint32_t lo = (kk - kmin) & ((1u << sh) - 1u);
-          const bool in = kk != 0u && bin_of(kk) == bstar && (lo & got_mask) == low;
-          wave_hist_add(hist, (lo >> shift) & dmask, in);
-        }
-      }
-      __syncthreads();
-      find_bucket<TH>(hist, kBins, k, red, &sel_bin, &sel_above);
-      k -= sel_above;
-      low |= sel_bin << shift;
-      got_mask |= dmask << shift;
-      width -= w;
-    }
-    if (width == 0) {
-      thr = bstar == 0u ? 0u : kmin + ((bstar - 1u) << sh) + low;
-      need = k;
-    }
-  }
-
-  // ---- 4. ordered placement: pos = #(key > thr before) + min(#(key == thr before), need).
-  // Taking every present element is thr = 0 (NaN) with need = the present
-  // NaNs, which come before the absent elements. Positions are settled from
-  // ballots over the registers; the selected elements are parked in LDS by
-  // position and emitted afterwards, one output position per thread, so the
-  // index and page-table reads of all 512 run in parallel.
-  uint32_t gt_w = 0, eq_w = 0;
-#pragma unroll
-  for (int i = 0; i < kE; ++i) {
-    gt_w += (uint32_t)__popcll(__ballot(kr[i] > thr));
-    eq_w += (uint32_t)__popcll(__ballot(kr[i] == thr));
-  }
-  uint32_t tot;
-  const uint32_t off = wave_offsets<TH>(gt_w | (eq_w << 16), red, tot);
-  if (take_all) need = (uint32_t)n - (tot & 0xFFFFu);
-  uint32_t g = off & 0xFFFFu, q = off >> 16;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  // the lane index again, by a route the compiler cannot match to the one the
-  // loads used, so it does not keep kE element indices live in between
-  const int lane_b = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-#pragma unroll
-  for (int i = 0; i < kE; ++i) {
-    const bool isgt = kr[i] > thr;
-    const bool iseq = kr[i] == thr;
-    const uint64_t bg = __ballot(isgt), be = __ballot(iseq);
-    const uint32_t gb = g + (uint32_t)__popcll(bg & lt);
-    const uint32_t qb = q + (uint32_t)__popcll(be & lt);
-    if (isgt || (iseq && qb < need)) {
-      const uint32_t pos = gb + min(qb, need);
-      s_out_e[pos] = seg + 64 * i + lane_b;
-      s_out_k[pos] = kr[i];
-    }
-    g += (uint32_t)__popcll(bg);
-    q += (uint32_t)__popcll(be);
-  }
-  __syncthreads();
+  topk_select<kE, TH>(kr, n, K, seg, L);
   // ---- emission (positions K..511 are padding)
   for (int p = threadIdx.x; p < kTopK; p += TH) {
     if (kMode == kChunkCand) {
       const int64_t o = ((int64_t)r * gridDim.x + blockIdx.x) * kTopK + p;
-      okeys[o] = p < K ? s_out_k[p] : 0u;
-      ojs[o] = p < K ? base + s_out_e[p] : INT_MAX;
+      okeys[o] = p < K ? L.out_k[p] : 0u;
+      ojs[o] = p < K ? base + L.out_e[p] : INT_MAX;
     } else {
       int32_t phys = -1, j = -1;
       if (p < K) {
-        const int e = s_out_e[p];
+        const int e = L.out_e[p];
         j = kMode == kCandFinal ? cjs[(int64_t)r * ncand + e] : e;
         phys = (int32_t)((int64_t)pt[(int64_t)row_seq[r] * pt_stride + j / c4_page_size] *
                              c4_page_size +
@@ -433,6 +203,18 @@ size_t topk_ws_bytes(int64_t R, int64_t max_len) {
 }
 
 int64_t topk_max_len() { return (int64_t)(kRegRow / kTopK) * kRegRow; }
+
+hipError_t launch_topk_cand_final(const uint32_t* ckeys, const int32_t* cjs, int ncand, int R,
+                                  const int32_t* row_len, const int32_t* row_seq,
+                                  const int32_t* page_table, int pt_stride, int c4_page_size,
+                                  int32_t* phys_idx, int32_t* logical_idx, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  const int th = (R >= 128 && ncand <= 256 * kMaxE) ? 256 : kThreads;
+  launch_mode<kCandFinal>(th, keys_per_lane(ncand, th), dim3(1, R), s, nullptr, 0, ckeys, cjs,
+                          ncand, 0, row_len, row_seq, page_table, pt_stride, c4_page_size,
+                          phys_idx, logical_idx, nullptr, nullptr);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const float* logits, int64_t ld, int R, const int32_t* row_len,
                        const int32_t* row_seq, const int32_t* page_table, int pt_stride,

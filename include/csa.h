@@ -223,6 +223,36 @@ csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * indexer_topk512 -- indexer_score followed by topk512_page_select on its
+ * logits, in one call ([P1] §3 C4Indexer logits feeding §3.2's top-512
+ * transform): phys_idx / logical_idx are exactly what
+ *     indexer_score(..., logits, ld, ...);
+ *     topk512_page_select(logits, ld, T, row_len, row_seq, page_table,
+ *                         pt_stride, k.page_size, phys_idx, logical_idx, ...)
+ * would produce. The index-K pool and the c4 KV pool share page_table and the
+ * page size (k.page_size is the translation's c4_page_size), as in
+ * csa_decode_prep. For FP8 / MXFP4 pools with few rows the logits are not
+ * materialised: each scan workgroup selects the top-512 candidates of its
+ * chunk from the logits it holds on chip, and one final pass per row selects
+ * among the candidates (exact: an entry of a row's top-512 is in its chunk's
+ * top-512). Other shapes run the two calls through the workspace.
+ *   Arguments as indexer_score and topk512_page_select; max_row_len up to
+ *   2097152.
+ *   ws   csa_workspace_size(CSA_OP_INDEXER_TOPK, T, max_row_len, H_I) bytes
+ *        (always needed).
+ *   scan_done  NULL, or an event recorded on `stream` right after the scan
+ *        launch (before the final selection), so that a caller can time the
+ *        scan alone or start dependent work early.
+ */
+csa_status indexer_topk512(const void* q, csa_fmt q_fmt, const void* q_scale, uint32_t prep,
+                           const float* w, int32_t T, int32_t H_I, int32_t D_I,
+                           const int32_t* row_seq, const int32_t* row_len, int32_t max_row_len,
+                           const int32_t* page_table, int32_t pt_stride, csa_index_pool k,
+                           int32_t* phys_idx, int32_t* logical_idx, void* q_used,
+                           void* q_used_scale, void* ws, size_t ws_bytes, hipEvent_t scan_done,
+                           hipStream_t stream);
+
+/*
  * topk512_page_select -- the fixed top-512 transform ([P1] §3.2): per row, the
  * 512 largest logits among j < row_len[r], translated through the page table
  * to physical slots page_table[row_seq[r]][j / c4_page_size] * c4_page_size
@@ -292,11 +322,13 @@ csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
  *     prepared inside the call and q_used is NULL), CSA_OP_TOPK (rows = R,
  *     max_len = ld),
  *     CSA_OP_CSA_ATTN / CSA_OP_HCA_ATTN (rows = T, max_len = most entries of
- *     one query's list, heads = H). */
+ *     one query's list, heads = H), CSA_OP_INDEXER_TOPK (rows = T, max_len =
+ *     max_row_len, heads = H_I). */
 #define CSA_OP_INDEXER  0
 #define CSA_OP_TOPK     1
 #define CSA_OP_CSA_ATTN 2
 #define CSA_OP_HCA_ATTN 3
+#define CSA_OP_INDEXER_TOPK 4
 size_t csa_workspace_size(int32_t op, int64_t rows, int64_t max_len, int32_t heads);
 
 const char* csa_status_string(csa_status s);

@@ -438,6 +438,56 @@ def test_tiny_fp32_decode_end_to_end(csa, seed_offset):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("lens", [
+    [5000, 513, 64 * 7 + 3, 17, 0],     # fused: 512-entry scan chunks, ragged, an empty row
+    [20000 - 37 * i for i in range(8)],  # fused: 1024-entry chunks
+    [40000, 3000],                       # 79 chunks per row: the two-call path
+])
+def test_indexer_topk512(csa, fmt, lens):
+    """indexer_topk512 against the oracle: each row's selection equals the top-512
+    of the oracle's logits outside the near-tie band (entries within 1e-4 of the
+    row's max |logit| of the 512-th largest), the physical slots are the page
+    translation of the logical ones, and the result is bit for bit the one of
+    indexer_score + topk512_page_select."""
+    from tests.fullsize import topk_agrees
+    g = gen.rng(1300 + len(fmt) + len(lens))
+    T = len(lens)
+    pt, pool, _ = _index_case(g, fmt, T, [max(n, 1) for n in lens])
+    qraw = gen.normal(g, (T, 64, 128))
+    qcodes, qsc = O.index_prep(qraw, True, fmt)
+    w = gen.uniform(g, (T, 64))
+    qfmt = csa.CSA_FP8_E4M3 if fmt == "fp8" else csa.CSA_MXFP4
+    qs = t_dev(qsc.astype(np.float32)) if fmt == "fp8" else t_dev(qsc)
+    dpool = index_pool_to_device(pool, 64, 128)
+    row_seq, row_len, dpt = t_dev(np.arange(T, dtype=np.int32)), t_dev(np.array(lens, np.int32)), t_dev(pt)
+    maxn = max(lens)
+    phys = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    logi = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    csa.indexer_topk512(t_dev(qcodes), t_dev(w), row_seq, row_len, maxn, dpt, dpool, phys, logi,
+                        q_fmt=qfmt, q_scale=qs)
+    # the two calls
+    logits = torch.empty((T, maxn), device=DEV)
+    csa.indexer_score(t_dev(qcodes), t_dev(w), row_seq, row_len, maxn, dpt, dpool, logits,
+                      q_fmt=qfmt, q_scale=qs)
+    phys2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    logi2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    csa.topk512_page_select(logits, row_len, row_seq, dpt, phys2, logi2)
+    gp, gl = phys.cpu().numpy(), logi.cpu().numpy()
+    assert np.array_equal(gp, phys2.cpu().numpy()) and np.array_equal(gl, logi2.cpu().numpy())
+    qhat = O.index_dequant(qcodes, qsc, fmt)
+    for t, n in enumerate(lens):
+        k = min(512, n)
+        assert np.all(gl[t, k:] == -1) and np.all(gp[t, k:] == -1), f"row {t}: tail not -1"
+        if n == 0:
+            continue
+        assert np.all(np.diff(gl[t, :k]) > 0), f"row {t}: not ascending"
+        assert np.array_equal(gp[t, :k], O.page_slot(pt[t], gl[t, :k], 64)), f"row {t}: slots"
+        want = O.indexer_logits(qhat[t], w[t], pool.rows(O.page_slot(pt[t], np.arange(n), 64)))
+        ok, _, nband = topk_agrees(want, gl[t], 512, 1e-4 * np.abs(want).max())
+        assert ok, f"row {t}: selection differs outside the near-tie band ({nband} in band)"
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 def test_indexer_many_rows_causal(csa, fmt):
     """Prefill shape: hundreds of query rows of one sequence with the causal
     row length min(N, (p+1)/4), plus a block of rows from a second sequence

@@ -132,15 +132,37 @@ class CsaDecode:
         self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         n = csa.csa_workspace_size(csa.CSA_OP_TOPK, B, self.maxN, 1)
         self.topk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        n = csa.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK, B, self.maxN, wl.index_heads)
+        self.itk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         torch.cuda.synchronize()
 
-    # algorithmic bytes of one indexer launch: index-K rows + prepared q +
-    # head weights + page-table rows + logits written
+    def scan_plan(self):
+        """(selects on chip, scan chunks per row) of indexer_topk512 at these
+        sizes, by the library's rule: the scan chunk is about 1/256 of all
+        entries, rounded up to 512, within [512, 4096]; the scan workgroups
+        select their chunk's top-512 when a row's candidates (chunks x 512)
+        fit the final pass's 16384 and the rows do not take the row-block
+        kernel (256 rows or more)."""
+        chunk = min(4096, max(512, -(-(self.B * self.maxN // 256) // 512) * 512))
+        chunks = -(-self.maxN // chunk)
+        return chunks * 512 <= 16384 and self.B < 256, chunks
+
+    @property
+    def indexer_kernel(self) -> str:
+        fused, _ = self.scan_plan()
+        fp4 = "true" if self.fmt == csa.CSA_MXFP4 else "false"
+        return f"indexer_mfma_kernel<{fp4}, true, {'true' if fused else 'false'}>"
+
+    # algorithmic bytes of one indexer scan launch: index-K rows + prepared q
+    # + head weights + page-table rows + what it writes (the logits, or on
+    # the fused path the chunks' top-512 candidates: key and index, 8 B each)
     def indexer_bytes(self) -> int:
         per_entry = (self.wl.index_dim + 4) if self.fmt == csa.CSA_FP8_E4M3 else (self.wl.index_dim // 2 + 4)
         n = int(self.N.sum())
         q = self.B * self.wl.index_heads * (self.q_codes.shape[-1] + 4 + 4)
-        return n * per_entry + q + n // C4_PAGE * 4 + n * 4
+        fused, chunks = self.scan_plan()
+        out = self.B * chunks * 512 * 8 if fused else n * 4
+        return n * per_entry + q + n // C4_PAGE * 4 + out
 
     def step_bytes(self) -> int:
         """Algorithmic bytes of a whole step: indexer, top-k read of the logits
@@ -152,6 +174,13 @@ class CsaDecode:
         comp = self.x_new.numel() * 2 + self.B * ent + self.B * ent  # rows read, entry + token stored
         prep = self.k_new.numel() * 2 + self.q_idx.numel() * 2 + self.B * 132 * (1 + self.wl.index_heads)
         return self.indexer_bytes() + topk + att + comp + prep
+
+    def score_only(self, c: int):
+        """The indexer logits of the step's rows into self.logits (indexer_score:
+        the scan the step runs, writing logits instead of selecting on chip).
+        For tests; run after step(c), whose preparation it reuses."""
+        csa.indexer_score(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.maxN, self.pt,
+                          self.index_pools[c], self.logits, q_fmt=self.fmt, q_scale=self.q_scale)
 
     def step(self, c: int, ev=None):
         idx, kv = self.index_pools[c], self.c4_pools[c]
@@ -169,12 +198,12 @@ class CsaDecode:
                                self.q_codes, self.q_scale)
         if ev is not None:
             ev[0].record()
-        csa.indexer_score(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.maxN, self.pt,
-                          idx, self.logits, q_fmt=self.fmt, q_scale=self.q_scale)
-        if ev is not None:
-            ev[1].record()
-        csa.topk512_page_select(self.logits, self.row_len, self.row_seq, self.pt, self.phys,
-                                ws=self.topk_ws)
+        # indexer + top-512 in one call: the scan workgroups select their
+        # chunks' candidates on chip (the logits are not written), then one
+        # final pass per row; ev[1] marks the end of the scan
+        csa.indexer_topk512(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.maxN, self.pt,
+                            idx, self.phys, q_fmt=self.fmt, q_scale=self.q_scale, ws=self.itk_ws,
+                            scan_done=None if ev is None else ev[1])
         csa.csa_sparse_attn(self.q_attn, self.row_seq, self.q_pos, self.phys, kv, self.raw, self.pt,
                             wl.window, wl.softmax_scale, self.out, ws=self.attn_ws)
 
