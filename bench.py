@@ -128,7 +128,7 @@ def reduce_counters(d):
     k = hits[0]
     fetch = kf[k][0] * 1024 * f_scale
     write = kw[k][0] * 1024 * w_scale
-    out[name] = {"source_hash": kernel_source_hash("indexer.hip", "csa_device.hpp", "topk_select.hpp"),
+    out[name] = {"source_hash": kernel_source_hash("indexer.hip", "csa_device.hpp", "topk_select.hpp", "../build.py"),
                  "bytes_per_launch": round(fetch + write),
                  "fetch_bytes": round(fetch), "write_bytes": round(write),
                  "fetch_kib_raw": kf[k][0], "write_kib_raw": kw[k][0], "dispatches": kf[k][1],
@@ -397,7 +397,7 @@ def main():
     qps = W.B / (ms / 1e3)
     ibytes = W.indexer_bytes()
     achieved = ibytes / (idx_ms / 1e3) / 1e9
-    src_hash = kernel_source_hash("indexer.hip", "csa_device.hpp", "topk_select.hpp")
+    src_hash = kernel_source_hash("indexer.hip", "csa_device.hpp", "topk_select.hpp", "../build.py")
     assert W.indexer_kernel == DECODE_128K_SCAN, W.indexer_kernel
     traffic = stored_traffic(DECODE_128K_SCAN, src_hash)
     line = {

@@ -28,11 +28,15 @@ CFLAGS = [
 ]
 
 
-# Per-source extra flags. attention.hip: its softmax never produces NaN (every
-# -inf case is guarded), and without NaN semantics each max in the row
-# reductions is one DPP-fused v_max_f32 instead of a move, a canonicalising
+# Per-source extra flags, -fno-honor-nans: without NaN semantics fmaxf is one
+# v_max_f32 (a DPP-fused one in row reductions) instead of a canonicalising
 # max and a max.
-EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+#  - attention.hip: its softmax never produces NaN (every -inf case is guarded).
+#  - indexer.hip: ReLU(acc) and the amax of the fused query preparation see
+#    finite values (quantised codes); the top-512 keys of the fused select are
+#    built from the float's bits, so a NaN logit still ranks lowest. The
+#    epilogue of every scored entry drops from three VALU ops per head to two.
+EXTRA = {"attention.hip": ["-fno-honor-nans"], "indexer.hip": ["-fno-honor-nans"]}
 
 
 def sources():
