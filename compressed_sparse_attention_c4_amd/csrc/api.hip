@@ -70,7 +70,7 @@ IdxTopkWs idx_topk_ws(int64_t T, int64_t max_row_len, int H_I) {
   w.ld = std::max<int64_t>(64, (max_row_len + 63) / 64 * 64);
   w.logits = align256((size_t)T * w.ld * sizeof(float));
   w.topk = align256(topk_ws_bytes(T, w.ld));
-  w.total = w.prep + std::max(2 * w.cand, w.logits + w.topk);
+  w.total = w.prep + std::max(3 * w.cand, w.logits + w.topk);
   return w;
 }
 
@@ -223,12 +223,13 @@ csa_status indexer_topk512(const void* q, csa_fmt q_fmt, const void* q_scale, ui
   if (chunks > 0) {
     uint32_t* ck = (uint32_t*)(base + L.prep);
     int32_t* cj = (int32_t*)(base + L.prep + L.cand);
+    int32_t* cp = (int32_t*)(base + L.prep + 2 * L.cand);
     e = launch_indexer(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len, max_row_len,
                        page_table, pt_stride, k, nullptr, 0, q_used, q_used_scale, base, stream,
-                       ck, cj);
+                       ck, cj, cp);
     if (e == hipSuccess && scan_done) e = hipEventRecord(scan_done, stream);
     if (e == hipSuccess)
-      e = launch_topk_cand_final(ck, cj, chunks * CSA_TOPK, T, row_len, row_seq, page_table,
+      e = launch_topk_cand_final(ck, cj, cp, chunks * CSA_TOPK, T, row_len, row_seq, page_table,
                                  pt_stride, k.page_size, phys_idx, logical_idx, stream);
   } else {
     float* logits = (float*)(base + L.prep);

@@ -47,19 +47,23 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
                           const int32_t* row_len, int max_row_len, const int32_t* page_table,
                           int pt_stride, const csa_index_pool& k, float* logits, int64_t ld,
                           void* q_used, void* q_used_scale, void* ws, hipStream_t s,
-                          uint32_t* okeys = nullptr, int32_t* ojs = nullptr);
+                          uint32_t* okeys = nullptr, int32_t* ojs = nullptr,
+                          int32_t* ophys = nullptr);
 
 // Candidates per row the final top-512 pass takes in one workgroup (16 keys
 // per lane at 1024 threads).
 constexpr int kCandFinalMax = 16384;
 // Fused indexer + top-512: the scan workgroups select their chunk's top-512
-// candidates (launch_indexer with okeys / ojs), then one final pass per row.
+// candidates (launch_indexer with okeys / ojs / ophys: key, entry index and
+// physical slot), then one final pass per row, which takes the slots from the
+// candidates instead of looking them up.
 // Returns the scan chunks per row, or 0 when the shapes need the two calls.
 int indexer_cand_chunks(int64_t T, int H_I, int D_I, const csa_index_pool& k,
                         int64_t max_row_len);
 // Chunks per row of the decode scan kernel for these sizes.
 int64_t indexer_scan_chunks(int64_t T, int64_t max_row_len);
-hipError_t launch_topk_cand_final(const uint32_t* ckeys, const int32_t* cjs, int ncand, int R,
+hipError_t launch_topk_cand_final(const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys,
+                                  int ncand, int R,
                                   const int32_t* row_len, const int32_t* row_seq,
                                   const int32_t* page_table, int pt_stride, int c4_page_size,
                                   int32_t* phys_idx, int32_t* logical_idx, hipStream_t s);

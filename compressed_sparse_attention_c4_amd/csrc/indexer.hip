@@ -70,7 +70,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     int pt_stride, const uint8_t* __restrict__ kdata,
                     const void* __restrict__ kscale, int page_size, float* __restrict__ logits,
                     int64_t ld, int chunk, uint32_t* __restrict__ okeys,
-                    int32_t* __restrict__ ojs) {
+                    int32_t* __restrict__ ojs, int32_t* __restrict__ ophys) {
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K / q row
   __shared__ int32_t s_pages[kMaxChunk / 16 + 2];      // physical pages of this chunk
   __shared__ __attribute__((aligned(16))) float s_out[kMaxChunk + 64];  // the chunk's logits
@@ -83,6 +83,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
         const int64_t o = ((int64_t)t * gridDim.x + blockIdx.x) * kTopK + p;
         okeys[o] = 0u;
         ojs[o] = INT_MAX;
+        ophys[o] = -1;
       }
     }
     return;
@@ -249,8 +250,16 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
     topk_select<kE, kTH>(kr, n_out, K, seg, L);
     for (int p = threadIdx.x; p < kTopK; p += kTH) {
       const int64_t o = ((int64_t)t * gridDim.x + blockIdx.x) * kTopK + p;
-      okeys[o] = p < K ? L.out_k[p] : 0u;
-      ojs[o] = p < K ? c0 + L.out_e[p] : INT_MAX;
+      uint32_t key = 0u;  // padding past K
+      int32_t j = INT_MAX, phys = -1;
+      if (p < K) {
+        key = L.out_k[p];
+        j = c0 + L.out_e[p];
+        phys = s_pages[j / page_size - pg0] * page_size + j % page_size;  // a page of this chunk
+      }
+      okeys[o] = key;
+      ojs[o] = j;
+      ophys[o] = phys;
     }
   } else {
     float* orow = logits + (int64_t)t * ld + c0;
@@ -521,7 +530,7 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
                           const int32_t* row_len, int max_row_len, const int32_t* page_table,
                           int pt_stride, const csa_index_pool& k, float* logits, int64_t ld,
                           void* q_used, void* q_used_scale, void* ws, hipStream_t s,
-                          uint32_t* okeys, int32_t* ojs) {
+                          uint32_t* okeys, int32_t* ojs, int32_t* ophys) {
   if (T == 0 || max_row_len == 0) return hipSuccess;
   if (k.fmt == CSA_F32) {
     dim3 grid((max_row_len + 255) / 256, T);
@@ -572,7 +581,7 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
 #define CSA_IDX(FP4, P64, CAND)                                                                    \
   hipLaunchKernelGGL((indexer_mfma_kernel<FP4, P64, CAND>), grid, dim3(idx_threads<CAND>()), 0, s, qc, qs, \
                      w, row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data, k.scale,  \
-                     k.page_size, logits, ld, (int)chunk, okeys, ojs)
+                     k.page_size, logits, ld, (int)chunk, okeys, ojs, ophys)
 #define CSA_IDX_P(FP4, CAND)                 \
   if (k.page_size == 64) CSA_IDX(FP4, true, CAND); \
   else CSA_IDX(FP4, false, CAND);

@@ -49,7 +49,7 @@ enum Mode { kRowFinal = 0, kChunkCand = 1, kCandFinal = 2 };
 template <int kMode, int kE, int TH>
 __global__ void __launch_bounds__(TH)
 topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __restrict__ ckeys,
-            const int32_t* __restrict__ cjs, int ncand, int chunk,
+            const int32_t* __restrict__ cjs, const int32_t* __restrict__ cphys, int ncand, int chunk,
             const int32_t* __restrict__ row_len, const int32_t* __restrict__ row_seq,
             const int32_t* __restrict__ pt, int pt_stride, int c4_page_size,
             int32_t* __restrict__ phys_idx, int32_t* __restrict__ logical_idx,
@@ -108,9 +108,12 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
       if (p < K) {
         const int e = L.out_e[p];
         j = kMode == kCandFinal ? cjs[(int64_t)r * ncand + e] : e;
-        phys = (int32_t)((int64_t)pt[(int64_t)row_seq[r] * pt_stride + j / c4_page_size] *
-                             c4_page_size +
-                         j % c4_page_size);
+        if (kMode == kCandFinal && cphys)  // candidates that carry their slot
+          phys = cphys[(int64_t)r * ncand + e];
+        else
+          phys = (int32_t)((int64_t)pt[(int64_t)row_seq[r] * pt_stride + j / c4_page_size] *
+                               c4_page_size +
+                           j % c4_page_size);
       }
       phys_idx[(int64_t)r * kTopK + p] = phys;
       if (logical_idx) logical_idx[(int64_t)r * kTopK + p] = j;
@@ -127,13 +130,13 @@ int keys_per_lane(int64_t n, int th) {
 
 template <int kMode>
 void launch_mode(int th, int e, dim3 grid, hipStream_t s, const float* logits, int64_t ld,
-                 const uint32_t* ckeys, const int32_t* cjs, int ncand, int chunk,
+                 const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys, int ncand, int chunk,
                  const int32_t* row_len, const int32_t* row_seq, const int32_t* pt, int pt_stride,
                  int c4_page_size, int32_t* phys_idx, int32_t* logical_idx, uint32_t* okeys,
                  int32_t* ojs) {
 #define CSA_TOPK_LAUNCH(E, TH)                                                             \
   hipLaunchKernelGGL((topk_kernel<kMode, E, TH>), grid, dim3(TH), 0, s, logits, ld, ckeys,    \
-                     cjs, ncand, chunk, row_len, row_seq, pt, pt_stride, c4_page_size,         \
+                     cjs, cphys, ncand, chunk, row_len, row_seq, pt, pt_stride, c4_page_size,  \
                      phys_idx, logical_idx, okeys, ojs)
 #define CSA_TOPK_E(TH)                       \
   switch (e) {                               \
@@ -204,14 +207,15 @@ size_t topk_ws_bytes(int64_t R, int64_t max_len) {
 
 int64_t topk_max_len() { return (int64_t)(kRegRow / kTopK) * kRegRow; }
 
-hipError_t launch_topk_cand_final(const uint32_t* ckeys, const int32_t* cjs, int ncand, int R,
+hipError_t launch_topk_cand_final(const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys,
+                                  int ncand, int R,
                                   const int32_t* row_len, const int32_t* row_seq,
                                   const int32_t* page_table, int pt_stride, int c4_page_size,
                                   int32_t* phys_idx, int32_t* logical_idx, hipStream_t s) {
   if (R == 0) return hipSuccess;
   const int th = (R >= 128 && ncand <= 256 * kMaxE) ? 256 : kThreads;
   launch_mode<kCandFinal>(th, keys_per_lane(ncand, th), dim3(1, R), s, nullptr, 0, ckeys, cjs,
-                          ncand, 0, row_len, row_seq, page_table, pt_stride, c4_page_size,
+                          cphys, ncand, 0, row_len, row_seq, page_table, pt_stride, c4_page_size,
                           phys_idx, logical_idx, nullptr, nullptr);
   return hipGetLastError();
 }
@@ -225,7 +229,7 @@ hipError_t launch_topk(const float* logits, int64_t ld, int R, const int32_t* ro
   const TopkPlan p = topk_plan(R, ld);
   if (p.whole_rows) {
     launch_mode<kRowFinal>(kThreads, keys_per_lane(ld, kThreads), dim3(1, R), s, logits, ld,
-                           nullptr, nullptr, 0, 0, row_len, row_seq, page_table, pt_stride,
+                           nullptr, nullptr, nullptr, 0, 0, row_len, row_seq, page_table, pt_stride,
                            c4_page_size, phys_idx, logical_idx, nullptr, nullptr);
     return hipGetLastError();
   }
@@ -233,12 +237,12 @@ hipError_t launch_topk(const float* logits, int64_t ld, int R, const int32_t* ro
   uint32_t* ck = (uint32_t*)ws;
   int32_t* cj = (int32_t*)((uint8_t*)ws + (size_t)R * ncand * sizeof(uint32_t));
   launch_mode<kChunkCand>(p.chunk_th, keys_per_lane(p.chunk, p.chunk_th), dim3(p.chunks, R), s,
-                          logits, ld, nullptr, nullptr, 0, p.chunk, row_len, row_seq, page_table,
+                          logits, ld, nullptr, nullptr, nullptr, 0, p.chunk, row_len, row_seq, page_table,
                           pt_stride, c4_page_size, nullptr, nullptr, ck, cj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch_mode<kCandFinal>(p.final_th, keys_per_lane(ncand, p.final_th), dim3(1, R), s, nullptr,
-                          0, ck, cj, ncand, 0, row_len, row_seq, page_table, pt_stride,
+                          0, ck, cj, nullptr, ncand, 0, row_len, row_seq, page_table, pt_stride,
                           c4_page_size, phys_idx, logical_idx, nullptr, nullptr);
   return hipGetLastError();
 }
