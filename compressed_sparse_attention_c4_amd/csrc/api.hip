@@ -59,7 +59,7 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // scan's top-512 candidates (fused path) or the logits and the top-512
 // workspace (two-call path); sized for whichever is larger.
 struct IdxTopkWs {
-  size_t prep, cand, logits, topk, total;
+  size_t prep, cand, merged, logits, topk, total;
   int64_t ld;
 };
 IdxTopkWs idx_topk_ws(int64_t T, int64_t max_row_len, int H_I) {
@@ -67,10 +67,11 @@ IdxTopkWs idx_topk_ws(int64_t T, int64_t max_row_len, int H_I) {
   w.prep = align256(indexer_ws_bytes(T, H_I));
   const int64_t chunks = indexer_scan_chunks(T, max_row_len);
   w.cand = align256((size_t)T * chunks * CSA_TOPK * sizeof(uint32_t));
+  w.merged = align256((size_t)T * kCandGroups * CSA_TOPK * sizeof(uint32_t));
   w.ld = std::max<int64_t>(64, (max_row_len + 63) / 64 * 64);
   w.logits = align256((size_t)T * w.ld * sizeof(float));
   w.topk = align256(topk_ws_bytes(T, w.ld));
-  w.total = w.prep + std::max(3 * w.cand, w.logits + w.topk);
+  w.total = w.prep + std::max(3 * (w.cand + w.merged), w.logits + w.topk);
   return w;
 }
 
@@ -228,9 +229,23 @@ csa_status indexer_topk512(const void* q, csa_fmt q_fmt, const void* q_scale, ui
                        page_table, pt_stride, k, nullptr, 0, q_used, q_used_scale, base, stream,
                        ck, cj, cp);
     if (e == hipSuccess && scan_done) e = hipEventRecord(scan_done, stream);
+    int ncand = chunks * CSA_TOPK;
+    if (e == hipSuccess && ncand > kCandFinalMax) {
+      // groups of g consecutive chunks -> at most kCandGroups lists
+      const int g = (chunks + kCandGroups - 1) / kCandGroups;
+      const int groups = (chunks + g - 1) / g;
+      uint32_t* mk = (uint32_t*)(base + L.prep + 3 * L.cand);
+      int32_t* mj = (int32_t*)(base + L.prep + 3 * L.cand + L.merged);
+      int32_t* mp = (int32_t*)(base + L.prep + 3 * L.cand + 2 * L.merged);
+      e = launch_topk_cand_merge(ck, cj, cp, ncand, g * CSA_TOPK, T, row_len, mk, mj, mp, stream);
+      ck = mk;
+      cj = mj;
+      cp = mp;
+      ncand = groups * CSA_TOPK;
+    }
     if (e == hipSuccess)
-      e = launch_topk_cand_final(ck, cj, cp, chunks * CSA_TOPK, T, row_len, row_seq, page_table,
-                                 pt_stride, k.page_size, phys_idx, logical_idx, stream);
+      e = launch_topk_cand_final(ck, cj, cp, ncand, T, row_len, row_seq, page_table, pt_stride,
+                                 k.page_size, phys_idx, logical_idx, stream);
   } else {
     float* logits = (float*)(base + L.prep);
     e = launch_indexer(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len, max_row_len,

@@ -51,8 +51,11 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
                           int32_t* ophys = nullptr);
 
 // Candidates per row the final top-512 pass takes in one workgroup (16 keys
-// per lane at 1024 threads).
+// per lane at 1024 threads). Rows with more scan chunks first merge groups of
+// chunks into at most kCandGroups lists (each group at most kCandFinalMax
+// candidates), so the fused path takes up to kCandGroups * 32 chunks per row.
 constexpr int kCandFinalMax = 16384;
+constexpr int kCandGroups = 8;
 // Fused indexer + top-512: the scan workgroups select their chunk's top-512
 // candidates (launch_indexer with okeys / ojs / ophys: key, entry index and
 // physical slot), then one final pass per row, which takes the slots from the
@@ -62,6 +65,11 @@ int indexer_cand_chunks(int64_t T, int H_I, int D_I, const csa_index_pool& k,
                         int64_t max_row_len);
 // Chunks per row of the decode scan kernel for these sizes.
 int64_t indexer_scan_chunks(int64_t T, int64_t max_row_len);
+// A row's candidates in groups of `group` (a multiple of 512) reduced to one
+// top-512 list per group (okeys / ojs / ophys: R x groups x 512).
+hipError_t launch_topk_cand_merge(const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys,
+                                  int ncand, int group, int R, const int32_t* row_len,
+                                  uint32_t* okeys, int32_t* ojs, int32_t* ophys, hipStream_t s);
 hipError_t launch_topk_cand_final(const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys,
                                   int ncand, int R,
                                   const int32_t* row_len, const int32_t* row_seq,

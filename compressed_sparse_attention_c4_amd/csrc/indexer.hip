@@ -522,7 +522,7 @@ int indexer_cand_chunks(int64_t T, int H_I, int D_I, const csa_index_pool& k,
   if (H_I != kHeads || D_I != kDim || k.page_size % 16 != 0) return 0;
   if (T == 0 || max_row_len == 0 || uses_rows_kernel(T, k)) return 0;
   const int64_t chunks = indexer_scan_chunks(T, max_row_len);
-  return chunks * kTopK <= kCandFinalMax ? (int)chunks : 0;
+  return chunks * kTopK <= (int64_t)kCandGroups * kCandFinalMax ? (int)chunks : 0;
 }
 
 hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_t prep,

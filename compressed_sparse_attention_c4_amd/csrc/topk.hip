@@ -44,7 +44,12 @@ constexpr int kThreads = 1024;             // workgroup of whole rows and of the
 constexpr int kMaxE = 32;                    // keys per lane (held in registers)
 constexpr int kRegRow = kThreads * kMaxE;    // longest row selected in one launch
 
-enum Mode { kRowFinal = 0, kChunkCand = 1, kCandFinal = 2 };
+// kCandMerge: a group of `chunk` consecutive candidates of a row (several
+// chunks' top-512 lists) reduced to its own top-512 list, candidates in and
+// out (key, index, slot), so that a row with many chunks reaches the final
+// pass with few candidates. Groups are contiguous and the output keeps the
+// input's order, so the final pass sees the candidates in index order.
+enum Mode { kRowFinal = 0, kChunkCand = 1, kCandFinal = 2, kCandMerge = 3 };
 
 template <int kMode, int kE, int TH>
 __global__ void __launch_bounds__(TH)
@@ -53,7 +58,7 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
             const int32_t* __restrict__ row_len, const int32_t* __restrict__ row_seq,
             const int32_t* __restrict__ pt, int pt_stride, int c4_page_size,
             int32_t* __restrict__ phys_idx, int32_t* __restrict__ logical_idx,
-            uint32_t* __restrict__ okeys, int32_t* __restrict__ ojs) {
+            uint32_t* __restrict__ okeys, int32_t* __restrict__ ojs, int32_t* __restrict__ ophys) {
   static_assert(kE >= 1 && kE <= kMaxE, "keys per lane");
   __shared__ TopkLds L;
 
@@ -68,6 +73,9 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
   } else if (kMode == kChunkCand) {
     base = blockIdx.x * chunk;
     n = max(0, min(chunk, rl - base));
+  } else if (kMode == kCandMerge) {
+    base = blockIdx.x * chunk;
+    n = min(chunk, ncand - base);
   } else {
     n = ncand;
   }
@@ -87,12 +95,12 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
   uint32_t kr[kE];
   {
     const float* lrow = logits + (int64_t)r * ld + base;
-    const uint32_t* crow = ckeys + (int64_t)r * ncand;
+    const uint32_t* crow = ckeys + (int64_t)r * ncand + (kMode == kCandMerge ? base : 0);
 #pragma unroll
     for (int i = 0; i < kE; ++i) {
       const bool ok = 64 * i < nv;
       const int e = ok ? seg + 64 * i + lane : 0;
-      const uint32_t k = kMode == kCandFinal ? crow[e] : float_key(lrow[e]);
+      const uint32_t k = (kMode == kCandFinal || kMode == kCandMerge) ? crow[e] : float_key(lrow[e]);
       kr[i] = ok ? k : 0u;
     }
   }
@@ -103,6 +111,19 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
       const int64_t o = ((int64_t)r * gridDim.x + blockIdx.x) * kTopK + p;
       okeys[o] = p < K ? L.out_k[p] : 0u;
       ojs[o] = p < K ? base + L.out_e[p] : INT_MAX;
+    } else if (kMode == kCandMerge) {
+      const int64_t o = ((int64_t)r * gridDim.x + blockIdx.x) * kTopK + p;
+      uint32_t key = 0u;
+      int32_t j = INT_MAX, ph = -1;
+      if (p < K) {
+        const int64_t c = (int64_t)r * ncand + base + L.out_e[p];
+        key = L.out_k[p];
+        j = cjs[c];
+        ph = cphys[c];
+      }
+      okeys[o] = key;
+      ojs[o] = j;
+      ophys[o] = ph;
     } else {
       int32_t phys = -1, j = -1;
       if (p < K) {
@@ -133,11 +154,11 @@ void launch_mode(int th, int e, dim3 grid, hipStream_t s, const float* logits, i
                  const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys, int ncand, int chunk,
                  const int32_t* row_len, const int32_t* row_seq, const int32_t* pt, int pt_stride,
                  int c4_page_size, int32_t* phys_idx, int32_t* logical_idx, uint32_t* okeys,
-                 int32_t* ojs) {
+                 int32_t* ojs, int32_t* ophys = nullptr) {
 #define CSA_TOPK_LAUNCH(E, TH)                                                             \
   hipLaunchKernelGGL((topk_kernel<kMode, E, TH>), grid, dim3(TH), 0, s, logits, ld, ckeys,    \
                      cjs, cphys, ncand, chunk, row_len, row_seq, pt, pt_stride, c4_page_size,  \
-                     phys_idx, logical_idx, okeys, ojs)
+                     phys_idx, logical_idx, okeys, ojs, ophys)
 #define CSA_TOPK_E(TH)                       \
   switch (e) {                               \
     case 1: CSA_TOPK_LAUNCH(1, TH); break;   \
@@ -206,6 +227,18 @@ size_t topk_ws_bytes(int64_t R, int64_t max_len) {
 }
 
 int64_t topk_max_len() { return (int64_t)(kRegRow / kTopK) * kRegRow; }
+
+hipError_t launch_topk_cand_merge(const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys,
+                                  int ncand, int group, int R, const int32_t* row_len,
+                                  uint32_t* okeys, int32_t* ojs, int32_t* ophys, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  const int groups = (ncand + group - 1) / group;
+  const int th = (R >= 128 && group <= 256 * kMaxE) ? 256 : kThreads;
+  launch_mode<kCandMerge>(th, keys_per_lane(group, th), dim3(groups, R), s, nullptr, 0, ckeys, cjs,
+                          cphys, ncand, group, row_len, nullptr, nullptr, 1, 64, nullptr, nullptr,
+                          okeys, ojs, ophys);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk_cand_final(const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys,
                                   int ncand, int R,

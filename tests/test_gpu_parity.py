@@ -441,7 +441,7 @@ def test_tiny_fp32_decode_end_to_end(csa, seed_offset):
 @pytest.mark.parametrize("lens", [
     [5000, 513, 64 * 7 + 3, 17, 0],     # fused: 512-entry scan chunks, ragged, an empty row
     [20000 - 37 * i for i in range(8)],  # fused: 1024-entry chunks
-    [40000, 3000],                       # 79 chunks per row: the two-call path
+    [40000, 3000],                       # 79 chunks per row: merged into 8 lists first
 ])
 def test_indexer_topk512(csa, fmt, lens):
     """indexer_topk512 against the oracle: each row's selection equals the top-512
@@ -483,6 +483,35 @@ def test_indexer_topk512(csa, fmt, lens):
         assert np.all(np.diff(gl[t, :k]) > 0), f"row {t}: not ascending"
         assert np.array_equal(gp[t, :k], O.page_slot(pt[t], gl[t, :k], 64)), f"row {t}: slots"
         want = O.indexer_logits(qhat[t], w[t], pool.rows(O.page_slot(pt[t], np.arange(n), 64)))
+        ok, _, nband = topk_agrees(want, gl[t], 512, 1e-4 * np.abs(want).max())
+        assert ok, f"row {t}: selection differs outside the near-tie band ({nband} in band)"
+
+
+def test_indexer_topk512_f32_two_calls(csa):
+    """An fp32 index pool takes the two-call path (logits in the workspace):
+    the selection is the top-512 of the oracle's logits outside the near-tie
+    band, and equal to indexer_score + topk512_page_select."""
+    from tests.fullsize import topk_agrees
+    g = gen.rng(1350)
+    lens = [3000, 700, 5]
+    T = len(lens)
+    pt, pool, _ = _index_case(g, "f32", T, lens, H=8, D=64)
+    q = gen.normal(g, (T, 8, 64))
+    w = gen.uniform(g, (T, 8))
+    dpool = index_pool_to_device(pool, 64, 64)
+    row_seq, row_len, dpt = t_dev(np.arange(T, dtype=np.int32)), t_dev(np.array(lens, np.int32)), t_dev(pt)
+    phys = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    logi = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    csa.indexer_topk512(t_dev(q), t_dev(w), row_seq, row_len, max(lens), dpt, dpool, phys, logi)
+    logits = torch.empty((T, max(lens)), device=DEV)
+    csa.indexer_score(t_dev(q), t_dev(w), row_seq, row_len, max(lens), dpt, dpool, logits)
+    logi2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    phys2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    csa.topk512_page_select(logits, row_len, row_seq, dpt, phys2, logi2)
+    gl = logi.cpu().numpy()
+    assert np.array_equal(gl, logi2.cpu().numpy()) and np.array_equal(phys.cpu().numpy(), phys2.cpu().numpy())
+    for t, n in enumerate(lens):
+        want = O.indexer_logits(q[t], w[t], pool.rows(O.page_slot(pt[t], np.arange(n), 64)))
         ok, _, nband = topk_agrees(want, gl[t], 512, 1e-4 * np.abs(want).max())
         assert ok, f"row {t}: selection differs outside the near-tie band ({nband} in band)"
 

@@ -140,12 +140,12 @@ class CsaDecode:
         """(selects on chip, scan chunks per row) of indexer_topk512 at these
         sizes, by the library's rule: the scan chunk is about 1/256 of all
         entries, rounded up to 512, within [512, 4096]; the scan workgroups
-        select their chunk's top-512 when a row's candidates (chunks x 512)
-        fit the final pass's 16384 and the rows do not take the row-block
-        kernel (256 rows or more)."""
+        select their chunk's top-512 when a row has at most 256 chunks (more
+        than 32 are merged into 8 lists before the final pass) and the rows
+        do not take the row-block kernel (256 rows or more)."""
         chunk = min(4096, max(512, -(-(self.B * self.maxN // 256) // 512) * 512))
         chunks = -(-self.maxN // chunk)
-        return chunks * 512 <= 16384 and self.B < 256, chunks
+        return chunks <= 256 and self.B < 256, chunks
 
     @property
     def indexer_kernel(self) -> str:
@@ -155,13 +155,14 @@ class CsaDecode:
 
     # algorithmic bytes of one indexer scan launch: index-K rows + prepared q
     # + head weights + page-table rows + what it writes (the logits, or on
-    # the fused path the chunks' top-512 candidates: key and index, 8 B each)
+    # the fused path the chunks' top-512 candidates: key, index and slot,
+    # 12 B each)
     def indexer_bytes(self) -> int:
         per_entry = (self.wl.index_dim + 4) if self.fmt == csa.CSA_FP8_E4M3 else (self.wl.index_dim // 2 + 4)
         n = int(self.N.sum())
         q = self.B * self.wl.index_heads * (self.q_codes.shape[-1] + 4 + 4)
         fused, chunks = self.scan_plan()
-        out = self.B * chunks * 512 * 8 if fused else n * 4
+        out = self.B * chunks * 512 * 12 if fused else n * 4
         return n * per_entry + q + n // C4_PAGE * 4 + out
 
     def step_bytes(self) -> int:
