@@ -72,6 +72,10 @@ def test_workspace_sizes(lib):
     assert lib.csa_workspace_size(1, 4, 1 << 20, 1) >= 4 * 512 * 8
     assert lib.csa_workspace_size(0, 32, 0, 64) >= 32 * 64 * 132  # prepared query
     assert lib.csa_workspace_size(2, -1, 10, 64) == 0
+    # indexer + top-512: the query area, then candidates (or logits and the
+    # top-512 workspace), whichever is larger
+    assert lib.csa_workspace_size(4, 32, 32768, 64) >= 32 * 32768 * 4
+    assert lib.csa_workspace_size(4, 4, 262144, 64) >= 4 * 64 * 512 * 12
 
 
 def test_compress_rejects_bad_arguments(lib):
@@ -137,6 +141,31 @@ def test_indexer_rejects_bad_arguments(lib):
     # prepared query of the wrong format
     assert f(FAKE, 3, FAKE, 0, FAKE, 4, 64, 128, FAKE, FAKE, 100, FAKE, 2, fp8, FAKE, 100, None, None,
              None, 0, None) == INVALID
+
+
+def test_indexer_topk512_rejects_bad_arguments(lib):
+    f = lib.indexer_topk512
+    f.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_uint32, C.c_void_p, C.c_int32, C.c_int32,
+                  C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, IndexPoolC,
+                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p,
+                  C.c_void_p]
+    lib.csa_workspace_size.restype = C.c_size_t
+    lib.csa_workspace_size.argtypes = [C.c_int32, C.c_int64, C.c_int64, C.c_int32]
+    fp8 = IndexPoolC(FAKE, FAKE, 2, 128, 64, 10)
+    need = lib.csa_workspace_size(4, 4, 100, 64)
+
+    def call(q_fmt=2, prep=0, H_I=64, max_len=100, pool=fp8, phys=FAKE, ws=FAKE, ws_bytes=None):
+        return f(FAKE, q_fmt, FAKE, prep, FAKE, 4, H_I, 128, FAKE, FAKE, max_len, FAKE, 2, pool, phys,
+                 None, None, None, ws, need if ws_bytes is None else ws_bytes, None, None)
+
+    assert call(q_fmt=1, prep=1) == INVALID                 # raw bf16 query without the quant flag
+    assert call(H_I=32) == UNSUPPORTED                      # 32 heads on the MFMA path
+    assert call(q_fmt=3) == INVALID                         # prepared query of the wrong format
+    assert call(max_len=1 << 22) == UNSUPPORTED             # longer than the top-512 handles
+    assert call(ws=None) == WORKSPACE                       # the workspace is always needed
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert call(phys=None) == INVALID                       # phys_idx is required
+    assert call(max_len=-1) == INVALID
 
 
 def test_topk_and_attention_reject_bad_arguments(lib):
