@@ -19,6 +19,7 @@ struct TopkLds {
   uint32_t hist[kTopkBins];
   uint32_t red[2 * kTopkMaxWaves];
   uint32_t sel_bin, sel_above;
+  uint32_t list_n;                 // length of the threshold bucket's list
   uint32_t thr, need;              // threshold of a short bucket
   uint32_t cand[kTopkCandCap];     // keys of the threshold bucket
   int32_t out_e[kTopK];            // element placed at each output position
@@ -27,7 +28,9 @@ struct TopkLds {
 
 // Exclusive scan of one uint32 per wave (value taken from lane 0 of each
 // wave) over the workgroup's TH/64 waves; returns this wave's offset, sets total.
-template <int TH>
+// kTail = false leaves out the closing barrier (which keeps sh from being
+// overwritten while a wave still reads it) where a later barrier comes first.
+template <int TH, bool kTail = true>
 __device__ __forceinline__ uint32_t wave_offsets(uint32_t v, uint32_t* sh, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) sh[wave] = v;
@@ -38,7 +41,7 @@ __device__ __forceinline__ uint32_t wave_offsets(uint32_t v, uint32_t* sh, uint3
     off += (w < wave) ? x : 0u;
     tot += x;
   }
-  __syncthreads();
+  if (kTail) __syncthreads();
   total = tot;
   return off;
 }
@@ -77,7 +80,7 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int nbins, uin
   const uint32_t x = wave_inclusive_scan(c);
   uint32_t tot;
   const uint32_t woff =
-      wave_offsets<TH>((uint32_t)__builtin_amdgcn_readlane((int)x, 63), scan_sh, tot);
+      wave_offsets<TH, false>((uint32_t)__builtin_amdgcn_readlane((int)x, 63), scan_sh, tot);
   uint32_t above = woff + x - c;
   if (above < k && above + c >= k) {
     for (int q = 0; q < per; ++q) {
@@ -117,6 +120,7 @@ __device__ __forceinline__ void topk_select(const uint32_t (&kr)[kE], int n, int
   uint32_t* const s_cand = L.cand;
   int32_t* const s_out_e = L.out_e;
   uint32_t* const s_out_k = L.out_k;
+  if (threadIdx.x == 0) L.list_n = 0u;  // ordered before its use by the barriers below
   uint32_t thr = 0, need = 0;
   const bool take_all = n <= K;  // every element is selected
   if (!take_all) {
@@ -161,13 +165,11 @@ __device__ __forceinline__ void topk_select(const uint32_t (&kr)[kE], int n, int
     // LDS list when they fit.
     const uint32_t nb = hist[bstar];
     const bool listed = bstar != 0u && nb <= (uint32_t)kCandCap;
-    __syncthreads();
     if (listed) {
-      if (threadIdx.x == 0) sel_above = 0;  // reused as the list length
-      __syncthreads();
+      // list_n was zeroed before the first barrier
 #pragma unroll
       for (int i = 0; i < kE; ++i)
-        if (bin_of(kr[i]) == bstar) s_cand[atomicAdd(&sel_above, 1u)] = kr[i];
+        if (bin_of(kr[i]) == bstar) s_cand[atomicAdd(&L.list_n, 1u)] = kr[i];
       __syncthreads();
     }
     uint32_t low = 0;  // threshold's low bits, built from the top
@@ -248,7 +250,7 @@ __device__ __forceinline__ void topk_select(const uint32_t (&kr)[kE], int n, int
     eq_w += (uint32_t)__popcll(__ballot(kr[i] == thr));
   }
   uint32_t tot;
-  const uint32_t off = wave_offsets<TH>(gt_w | (eq_w << 16), red, tot);
+  const uint32_t off = wave_offsets<TH, false>(gt_w | (eq_w << 16), red, tot);
   if (take_all) need = (uint32_t)n - (tot & 0xFFFFu);
   uint32_t g = off & 0xFFFFu, q = off >> 16;
   const uint64_t lt = (1ull << lane) - 1ull;
