@@ -375,6 +375,21 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   __builtin_amdgcn_sched_barrier(0);
   // 64 heads x 16 entries: 4 MFMAs, ReLU, head weights, 64-head reduction,
   // logit store (lanes of rows past their row_len are dropped by the buffer)
+  // ReLU and head weights of one 16-entry group, summed over this lane's 16
+  // heads (the other heads of the entry are in the other lane rows)
+  auto head_sum = [&](const v8i& bb, int sb) __attribute__((always_inline)) {
+    v4f acc[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+      acc[hb] = kFp4 ? mfma_fp4(a[hb], bb, v4f{0.f, 0.f, 0.f, 0.f}, sa[hb], sb)
+                     : mfma_fp8(a[hb], bb, v4f{0.f, 0.f, 0.f, 0.f});
+    float v = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v = fmaf(wq[hb * 4 + r], fmaxf(acc[hb][r], 0.f), v);
+    return v;
+  };
   auto score_store = [&](const v8i& bb, int sb, float ks, int jrow) __attribute__((always_inline)) {
     v4f acc[4];
 #pragma unroll
@@ -398,12 +413,15 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
     __syncthreads();
     load_page(p + kDepth, K);  // refill the slot just written to LDS
     if (own && p * kPage < nw) {
+      // the four 16-entry groups of the page; one reduce-scatter across the
+      // lane rows then leaves the 64-head sum of group r in row r, so each
+      // lane holds one logit and the wave stores the page's 64 logits at once
+      float pk[kPage / 16];
 #pragma unroll
       for (int g = 0; g < kPage / 16; ++g) {
         const int e = g * 16 + col;
         v8i bb;
         int sb = 127;
-        float ks = 1.f;
         if (kFp4) {
           const int pos = grp ^ ((e >> 2) & 3);
           const v4i x = *reinterpret_cast<const v4i*>(&s_b[buf][e * kRowBytes + pos * 16]);
@@ -413,10 +431,13 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
           const v4i x = *reinterpret_cast<const v4i*>(&s_b[buf][e * kRowBytes + ((2 * grp) ^ (e & 7)) * 16]);
           const v4i y = *reinterpret_cast<const v4i*>(&s_b[buf][e * kRowBytes + ((2 * grp + 1) ^ (e & 7)) * 16]);
           bb = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-          ks = __uint_as_float(s_bs[buf][e]);
         }
-        score_store(bb, sb, ks, p * kPage + e);
+        pk[g] = head_sum(bb, sb);
       }
+      const float tot = rows4_reduce_scatter(pk[0], pk[1], pk[2], pk[3]);
+      const int e = grp * 16 + col;  // the entry whose logit this lane holds
+      const float ks = kFp4 ? 1.f : __uint_as_float(s_bs[buf][e]);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot * ks), out_rsrc, (p * kPage + e) * 4, 0, 0);
     }
   };
   static_assert(kDepth == 3, "the page loop below is unrolled by hand for three slots");
