@@ -36,6 +36,7 @@ constexpr int kMaxSplit = 1024;       // entries one workgroup handles, at most
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma_bf16(const v4i& a, const v4i& b, v4f c) {
@@ -486,14 +487,22 @@ attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
 // sum l_c, and the weights P' = exp(s - m_c) * (value FP8 scale) in bf16;
 // phase B merges the chunks' (m_c, l_c) into the exact normaliser and sums
 // f_c * (P' V) for one 64-dim slice of the value, f_c = exp(m_c - M) / L. No
-// merge follows. Phase A also copies the latent codes it gathered into one
-// contiguous [entry][64] block per value slice, so phase B reads its values,
-// weights and statistics in a single round of independent loads (no slot
-// lookup, no gather).
+// merge follows. Phase B gets its values one of two ways:
+//  - copy: phase A also writes the latent codes it gathered into one
+//    contiguous [entry][64] block per value slice, so phase B reads values,
+//    weights and statistics in a single round of independent loads;
+//  - gather: phase A stores each entry's slot, and phase B gathers its
+//    64-byte value slices straight from the pools (one round of loads for
+//    statistics, slots and weights, then one round of gathers).
+// The copy costs phase A 512 B of writes per entry, and a kernel's written
+// lines are flushed from L2 before the next kernel starts, so with many
+// queries (a copy of several MB) the gather is faster; with few, the copy's
+// single round is.
 constexpr int kChunk = 64;                // entries per phase-A workgroup
 constexpr int kSlice = 64;                // value dims per phase-B workgroup
 constexpr int kTwoPhaseMaxE = 768;        // entry lists up to this length
 constexpr int kVStride = kSlice + 8;      // bf16 per value row in phase B's LDS
+constexpr size_t kGatherMinCopy = 4u << 20;  // value copies this large take the gather
 
 __global__ void __launch_bounds__(256)
 attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
@@ -505,7 +514,8 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
                    const uint16_t* __restrict__ r_rope, int r_ps,
                    const int32_t* __restrict__ raw_pt, int raw_pt_stride, int window, float scale,
                    uint16_t* __restrict__ pw, float2* __restrict__ stats,
-                   uint8_t* __restrict__ vcopy, int e_pad, int T, int nz, int g) {
+                   uint8_t* __restrict__ vcopy, int32_t* __restrict__ ent, int e_pad, int T,
+                   int nz, int g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kChunk * kKStride];
   __shared__ int32_t s_es[kChunk];
   __shared__ float s_sc[kChunk];
@@ -526,21 +536,28 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   const EntryList L = entry_list(p, k_sel, hca, ratio, window);
   const int total = min(L.n1 + L.n2, e_pad);  // a list longer than the stated bound is cut
   const int hb0 = bc.z * 64;
+  // phase B's value source (copy mode: vcopy set, ent null; gather: the reverse)
   uint8_t* vc_t = vcopy + (int64_t)t * (kLatent / kSlice) * e_pad * kSlice;
+  int32_t* ent_t = ent + (int64_t)t * e_pad + e0;
   if (e0 >= total) {
-    // past this query's list: zero weights, dead statistics and zero values,
-    // so that phase B reads every chunk without knowing the list's length
+    // past this query's list: zero weights, dead statistics and masked
+    // entries, so that phase B reads every chunk without knowing the list's
+    // length
     const int hh = tid >> 2, part = tid & 3;
     v4i* prow = reinterpret_cast<v4i*>(pw + ((int64_t)t * H + hb0 + hh) * e_pad + e0 + part * 16);
     prow[0] = v4i{0, 0, 0, 0};
     prow[1] = v4i{0, 0, 0, 0};
     if (tid < kChunk) stats[((int64_t)t * H + hb0 + tid) * n_chunks + chunk] = make_float2(-INFINITY, 0.f);
     if (bc.z == 0) {
+      if (ent) {
+        if (tid < kChunk) ent_t[tid] = -1;
+      } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
-        *reinterpret_cast<v4i*>(vc_t + ((int64_t)(c >> 2) * e_pad + e0 + e) * kSlice + 16 * (c & 3)) =
-            v4i{0, 0, 0, 0};
+        for (int k = 0; k < 8; ++k) {
+          const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
+          *reinterpret_cast<v4i*>(vc_t + ((int64_t)(c >> 2) * e_pad + e0 + e) * kSlice + 16 * (c & 3)) =
+              v4i{0, 0, 0, 0};
+        }
       }
     }
     return;
@@ -559,6 +576,7 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
     }
     const int32_t w = slot >= 0 ? (int32_t)(slot * 2 + pool) : -1;
     s_es[tid] = w;
+    if (bc.z == 0 && ent) ent_t[tid] = w;  // the entries' slots for phase B's gathers
     // every gather of the entry starts from these (masked: the zero row)
     const Pick pk = pick_of(w);
     s_la[tid] = pick_base(pk, c_lat, r_lat, g_zero_row) + pk.slot * kLatent;
@@ -607,8 +625,8 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
     *reinterpret_cast<v4i*>(&s_k[e * kKStride + kLatent + 8 * c]) = rp[k];
   }
   if (tid < kChunk) s_sc[tid] = scv;
-  // the codes, as gathered, into the per-slice value copy for phase B
-  if (bc.z == 0) {
+  // copy mode: the codes, as gathered, into the per-slice value copy
+  if (bc.z == 0 && !ent) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
@@ -617,31 +635,43 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   }
   lds_sync();
 
-  // scores of 16 heads x 64 entries (four 16-column blocks); K fragments read
-  // six ahead of the matrix ops
+  // scores of 16 heads x 64 entries (four 16-column blocks). The k-steps run
+  // outermost, so consecutive matrix ops feed four independent accumulators
+  // (a chain on one accumulator would wait out each op's latency), and the K
+  // fragments are read twelve ahead of the matrix ops.
+  v4f acc_l[4], acc_r[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc_l[cb] = acc_r[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+  {
+    constexpr int kAhead = 12;
+    const uint16_t* kb = s_k + col * kKStride + grp * 8;
+    auto kfrag = [&](int j) {
+      return *reinterpret_cast<const v4i*>(kb + (j & 3) * 16 * kKStride + (j >> 2) * 32);
+    };
+    v4i kf[72];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) kf[j] = kfrag(j);
+    // one k-step per group; the scheduling fences keep the steps in order
+#pragma unroll
+    for (int s = 0; s < 18; ++s) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int j = s * 4 + cb;
+        if (j + kAhead < 72) kf[j + kAhead] = kfrag(j + kAhead);
+        if (s < 16) acc_l[cb] = mfma_bf16(qa[s], kf[j], acc_l[cb]);
+        else acc_r[cb] = mfma_bf16(qa[s], kf[j], acc_r[cb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
   float sv[4][4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     const int e = cb * 16 + col;
-    v4i kf[18];
-#pragma unroll
-    for (int s = 0; s < 18; ++s) kf[s] = *reinterpret_cast<const v4i*>(&s_k[e * kKStride + s * 32 + grp * 8]);
-    v4f acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 16; ++s) acc_l = mfma_bf16(qa[s], kf[s], acc_l);
-    acc_r = mfma_bf16(qa[16], kf[16], acc_r);
-    acc_r = mfma_bf16(qa[17], kf[17], acc_r);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     const bool valid = s_es[e] >= 0;
     const float sc = s_sc[e];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[cb][r] = valid ? scale * fmaf(sc, acc_l[r], acc_r[r]) : -INFINITY;
+    for (int r = 0; r < 4; ++r) sv[cb][r] = valid ? scale * fmaf(sc, acc_l[cb][r], acc_r[cb][r]) : -INFINITY;
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -667,9 +697,11 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
 // the value slice goes to LDS row-major, and the P V products read their
 // value operands from it with the transposing LDS load. kNC: chunk slots
 // computed (the list's chunk count rounded up to even; extra slots are dead).
-template <int kNC, bool kOutF32>
+template <int kNC, bool kOutF32, bool kGather>
 __global__ void __launch_bounds__(256)
-attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const uint16_t* __restrict__ pw,
+attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const int32_t* __restrict__ ent,
+               const uint8_t* __restrict__ c_lat, const uint8_t* __restrict__ r_lat,
+               const uint16_t* __restrict__ pw,
                const float2* __restrict__ stats, int e_pad, void* __restrict__ out, int T,
                int nz, int g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_v[kNC * kChunk * kVStride];
@@ -682,29 +714,51 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const uint16_t* __restr
   const int hb0 = bc.z * 64;
   const int n_chunks = e_pad / kChunk;
 
-  // ---- one round of loads: value slice (16-B pieces j = tid + 256k: entry
-  // j / 4, dims 16 (j % 4) ..), weights (A operands: 32-entry steps of this
-  // wave's 16 heads), statistics
-  constexpr int kVP = kNC * kChunk * kSlice / 16 / 256;  // value pieces per thread
-  const int nv = e_pad * (kSlice / 16);
-  const uint8_t* vsrc = vcopy + ((int64_t)t * (kLatent / kSlice) + slice) * e_pad * kSlice;
-  v4i vp[kVP];
-#pragma unroll
-  for (int k = 0; k < kVP; ++k) vp[k] = gload<v4i>((uint64_t)(vsrc + 16 * min(tid + 256 * k, nv - 1)));
-  const uint16_t* prow = pw + ((int64_t)t * H + hb0 + wave * 16 + col) * e_pad + grp * 8;
-  v4i pa[kNC * 2];
-#pragma unroll
-  for (int ks = 0; ks < kNC * 2; ++ks)
-    pa[ks] = *reinterpret_cast<const v4i*>(prow + min(ks * 32, e_pad - 32));
-  float2 st[kNC];
+  // ---- first round of loads: statistics (first, so that the chunk factors
+  // wait for them only), the value pieces (copy) or their slots (gather)
+  // (16-B pieces j = tid + 256k: entry j / 4, dims 16 (j % 4) .. of the
+  // slice), weights (A operands: 32-entry steps of this wave's 16 heads)
+  v2f st[kNC];  // (m_c, l_c)
   {
     const float2* sp = stats + ((int64_t)t * H + hb0 + (tid & 63)) * n_chunks;
 #pragma unroll
-    for (int c = 0; c < kNC; ++c) st[c] = sp[min(c, n_chunks - 1)];
+    for (int c = 0; c < kNC; ++c) st[c] = gload<v2f>((uint64_t)(sp + min(c, n_chunks - 1)));
+  }
+  asm volatile("" ::: "memory");  // keeps these loads ahead of the ones below
+  constexpr int kVP = kNC * kChunk * kSlice / 16 / 256;  // value pieces per thread
+  const int nv = e_pad * (kSlice / 16);
+  v4i vp[kVP];
+  int32_t es[kVP];
+  if (kGather) {
+    const int32_t* ent_t = ent + (int64_t)t * e_pad;
+#pragma unroll
+    for (int k = 0; k < kVP; ++k) es[k] = gload<int32_t>((uint64_t)(ent_t + (min(tid + 256 * k, nv - 1) >> 2)));
+  } else {
+    const uint8_t* vsrc = vcopy + ((int64_t)t * (kLatent / kSlice) + slice) * e_pad * kSlice;
+#pragma unroll
+    for (int k = 0; k < kVP; ++k) vp[k] = gload<v4i>((uint64_t)(vsrc + 16 * min(tid + 256 * k, nv - 1)));
+  }
+  asm volatile("" ::: "memory");
+  const uint64_t prow = (uint64_t)(pw + ((int64_t)t * H + hb0 + wave * 16 + col) * e_pad + grp * 8);
+  v4i pa[kNC * 2];
+#pragma unroll
+  for (int ks = 0; ks < kNC * 2; ++ks) pa[ks] = gload<v4i>(prow + 2 * min(ks * 32, e_pad - 32));
+  // gather, second round: the value pieces (a masked entry, or a piece past
+  // e_pad, reads the zero row)
+  if (kGather) {
+#pragma unroll
+    for (int k = 0; k < kVP; ++k) {
+      const int j = tid + 256 * k;
+      const Pick pk = pick_of(j < nv ? es[k] : -1);
+      vp[k] = gload<v4i>(pick_base(pk, c_lat, r_lat, g_zero_row) + pk.slot * kLatent +
+                         kSlice * slice + 16 * (j & 3));
+    }
   }
 
-  // chunk factors f_c = exp(m_c - M) / L (threads 0..63: head hb0 + tid)
-  if (tid < 64) {
+  // chunk factors f_c = exp(m_c - M) / L of head hb0 + (tid & 63); every
+  // wave computes them (a branch around the loads would let the compiler move
+  // them behind the value loads) and wave 0 stores them
+  {
     float M = -INFINITY;
 #pragma unroll
     for (int c = 0; c < kNC; ++c)
@@ -715,18 +769,19 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const uint16_t* __restr
       if (c < n_chunks && st[c].x != -INFINITY) Ls = fmaf(st[c].y, __expf(st[c].x - M), Ls);
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll
-    for (int c = 0; c < kNC; ++c)
-      s_f[tid][c] = (c < n_chunks && st[c].x != -INFINITY) ? __expf(st[c].x - M) * inv : 0.f;
+    for (int c = 0; c < kNC; ++c) {
+      const float f = (c < n_chunks && st[c].x != -INFINITY) ? __expf(st[c].x - M) * inv : 0.f;
+      if (tid < 64) s_f[tid][c] = f;
+    }
   }
   // values row-major [entry][64] in bf16 (exact); rows past e_pad are zeros
 #pragma unroll
   for (int k = 0; k < kVP; ++k) {
     const int j = tid + 256 * k;
-    const bool live = j < nv;
     uint32_t b[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t x = live ? (uint32_t)vp[k][w] : 0u;
+      const uint32_t x = (kGather || j < nv) ? (uint32_t)vp[k][w] : 0u;
       b[2 * w] = fp8x2_to_bf16x2<false>(x);
       b[2 * w + 1] = fp8x2_to_bf16x2<true>(x);
     }
@@ -743,32 +798,51 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const uint16_t* __restr
   // two transposing reads: lane 4a + b of a 16-lane group fetches entry
   // 8*grp + 4h + a, dims 4b..4b+3 of the block.
   const uint16_t* vb = s_v + (8 * grp + (col >> 2)) * kVStride + 4 * (col & 3);
+  auto vfrag = [&](int c, int ks, int db) {
+    const uint16_t* src = vb + (c * kChunk + ks * 32) * kVStride + 16 * db;
+    const v2i lo = __builtin_bit_cast(
+        v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)src));
+    const v2i hi = __builtin_bit_cast(
+        v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                 (__attribute__((address_space(3))) v4s*)(src + 4 * kVStride)));
+    return v4i{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // Software pipeline over the chunks, one step per chunk: step c reads the
+  // value fragments and factors of chunk c + 1, runs chunk c's products into
+  // its own accumulators and folds chunk c - 1's (finished a step earlier)
+  // into O, so no op waits on the one just issued. The scheduling fences keep
+  // the steps in this order.
   v4f o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4i vf[kNC][8];
+  float fc[kNC][4];
+  v4f acc[kNC][4];
 #pragma unroll
-  for (int c = 0; c < kNC; ++c) {
-    v4f acc[4];
+  for (int i = 0; i < 8; ++i) vf[0][i] = vfrag(0, i >> 2, i & 3);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < 4; ++r) fc[0][r] = s_f[wave * 16 + grp * 4 + r][0];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+  for (int c = 0; c <= kNC; ++c) {
+    if (c + 1 < kNC) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint16_t* src = vb + (c * kChunk + ks * 32) * kVStride + 16 * db;
-        const v2i lo = __builtin_bit_cast(
-            v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)src));
-        const v2i hi = __builtin_bit_cast(
-            v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                     (__attribute__((address_space(3))) v4s*)(src + 4 * kVStride)));
-        acc[db] = mfma_bf16(pa[c * 2 + ks], v4i{lo[0], lo[1], hi[0], hi[1]}, acc[db]);
-      }
+      for (int i = 0; i < 8; ++i) vf[c + 1][i] = vfrag(c + 1, i >> 2, i & 3);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float f = s_f[wave * 16 + grp * 4 + r][c];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db][r] = fmaf(f, acc[db][r], o[db][r]);
+      for (int r = 0; r < 4; ++r) fc[c + 1][r] = s_f[wave * 16 + grp * 4 + r][c + 1];
     }
+    if (c < kNC) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[c][db] = mfma_bf16(pa[c * 2], vf[c][db], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[c][db] = mfma_bf16(pa[c * 2 + 1], vf[c][4 + db], acc[c][db]);
+    }
+    if (c > 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db][r] = fmaf(fc[c - 1][r], acc[c - 1][db][r], o[db][r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -786,17 +860,22 @@ bool use_two_phase(int T, int H, int max_entries) {
 }
 
 // Workspace of the two-phase path: P' [T][H][e_pad] bf16, then the chunk
-// statistics [T][H][e_pad/64] float2, then the value copy [T][8][e_pad][64]
-// (FP8 codes, one block per 64-dim slice).
+// statistics [T][H][e_pad/64] float2, then phase B's value source: the
+// entries' slot codes [T][e_pad] int32 (slot * 2 + pool, -1 when masked) in
+// gather mode, the value copy [T][8][e_pad][64] (FP8 codes, one block per
+// 64-dim slice) in copy mode.
 struct TwoPhaseWs {
-  size_t pw, stats, vcopy, total;
+  size_t pw, stats, src, total;
+  bool gather;
 };
 TwoPhaseWs two_phase_ws(int64_t T, int H, int e_pad) {
   TwoPhaseWs w;
   w.pw = 0;
   w.stats = ((size_t)T * H * e_pad * 2 + 255) / 256 * 256;
-  w.vcopy = w.stats + ((size_t)T * H * (e_pad / kChunk) * sizeof(float2) + 255) / 256 * 256;
-  w.total = w.vcopy + (size_t)T * e_pad * kLatent;
+  w.src = w.stats + ((size_t)T * H * (e_pad / kChunk) * sizeof(float2) + 255) / 256 * 256;
+  const size_t copy = (size_t)T * e_pad * kLatent;
+  w.gather = copy >= kGatherMinCopy;
+  w.total = w.src + (w.gather ? (size_t)T * e_pad * sizeof(int32_t) : copy);
   return w;
 }
 
@@ -907,7 +986,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const TwoPhaseWs w = two_phase_ws(a.T, a.H, e_pad);
     uint16_t* pw = (uint16_t*)((char*)a.ws + w.pw);
     float2* st = (float2*)((char*)a.ws + w.stats);
-    uint8_t* vc = (uint8_t*)a.ws + w.vcopy;
+    uint8_t* vc = w.gather ? nullptr : (uint8_t*)a.ws + w.src;
+    int32_t* ent = w.gather ? (int32_t*)((char*)a.ws + w.src) : nullptr;
     const int nz = a.H / 64;
     const int g = xcd_group(a.T);
     hipLaunchKernelGGL(attn_scores_kernel, xcd_grid(e_pad / kChunk, nz, a.T), dim3(256), 0, s,
@@ -916,16 +996,22 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
                        (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt, a.comp_pt_stride,
                        (const uint8_t*)a.raw.latent, a.raw.latent_scale,
                        (const uint16_t*)a.raw.rope, a.raw.page_size, a.raw_pt, a.raw_pt_stride,
-                       a.window, a.scale, pw, st, vc, e_pad, a.T, nz, g);
+                       a.window, a.scale, pw, st, vc, ent, e_pad, a.T, nz, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-#define CSA_PV(NC, FO)                                                                         \
-  hipLaunchKernelGGL((attn_pv_kernel<NC, FO>), xcd_grid(kLatent / kSlice, nz, a.T), dim3(256), 0, s, \
-                     a.H, vc, pw, st, e_pad, a.out, a.T, nz, g)
-#define CSA_PV_NC(NC)                \
-  case NC:                           \
-    if (a.out_fmt == CSA_F32) CSA_PV(NC, true); \
-    else CSA_PV(NC, false);          \
+#define CSA_PV(NC, FO, GA)                                                                      \
+  hipLaunchKernelGGL((attn_pv_kernel<NC, FO, GA>), xcd_grid(kLatent / kSlice, nz, a.T), dim3(256), 0, \
+                     s, a.H, vc, ent, (const uint8_t*)a.comp.latent, (const uint8_t*)a.raw.latent, pw, \
+                     st, e_pad, a.out, a.T, nz, g)
+#define CSA_PV_NC(NC)                                   \
+  case NC:                                              \
+    if (a.out_fmt == CSA_F32) {                         \
+      if (w.gather) CSA_PV(NC, true, true);             \
+      else CSA_PV(NC, true, false);                     \
+    } else {                                            \
+      if (w.gather) CSA_PV(NC, false, true);            \
+      else CSA_PV(NC, false, false);                    \
+    }                                                   \
     break;
     switch ((e_pad / kChunk + 1) / 2 * 2) {
       CSA_PV_NC(2)

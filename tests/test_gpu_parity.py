@@ -329,7 +329,9 @@ def _attn_case(g, fmt, B, Ls, H, ps_c=64, extra=3):
 
 @pytest.mark.parametrize("H,fmt,Ls,out_f32", [
     (64, "fp8", [131072 // 16, 700, 100, 2 * 4 + 1], False),  # full 512 + window, short, p < 127
-    (128, "fp8", [20000, 3000], True),  # two-phase path, fp32 output
+    (128, "fp8", [20000, 3000], True),  # two-phase path (value copy), fp32 output
+    # two-phase path with 16 queries: phase B gathers its values from the pools
+    (64, "fp8", [131072 // 16 + 997 * i for i in range(14)] + [700, 9], True),
     (64, "fp8", [20 + 3 * i for i in range(130)], False),  # > 128 queries: split + combine path
     (32, "fp8", [20000, 131, 9, 3000], True),  # two 16-head pairs, fp32 output
     (16, "fp8", [5000, 700, 9], False),  # one 16-head pair
