@@ -51,7 +51,7 @@ def _args():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the 1M decode, prefill and HCA workloads")
-    ap.add_argument("--profile-only", choices=["decode_128k", "decode_1m", "prefill", "hca_ragged", "copy"],
+    ap.add_argument("--profile-only", choices=["decode_128k", "decode_1m", "spec_decode", "prefill", "hca_ragged", "copy"],
                     help="run only this workload's steps (eager, for a profiler) and print nothing else; "
                          "'copy' is a plain 1 GiB device copy that calibrates the HBM byte counters")
     ap.add_argument("--counters-from", metavar="DIR",
@@ -209,7 +209,7 @@ def secondary(a):
     replays for the step, HIP events around the indexer launch)."""
     import torch
     from workloads import specs
-    from workloads.device import CsaDecode, CsaPrefill, HcaCsaRagged, hca_build_input
+    from workloads.device import CsaDecode, CsaPrefill, CsaSpecDecode, HcaCsaRagged, hca_build_input
     import compressed_sparse_attention_c4_amd as csa
     out = {}
     steps = max(10, a.steps // 2)
@@ -225,13 +225,24 @@ def secondary(a):
                     "step_hbm_frac": round(W.step_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     del W
     torch.cuda.empty_cache()
+    # multi-token (speculative-verify) decode: 32 sequences x 4 query tokens at 128K
+    wl = specs.SPEC_DECODE_128K
+    W = CsaSpecDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
+    ms, idx_ms, _ = time_steps(W, steps, a.warmup, a.copies, graph=not a.no_graph)
+    gbs = W.indexer_bytes() / (idx_ms / 1e3) / 1e9
+    out[wl.name] = {"queries_per_s": round(W.T / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
+                    "indexer": {"kernel": W.indexer_kernel, "kernel_ms": round(idx_ms, 5),
+                                "bytes_per_launch": W.indexer_bytes(), "achieved_GBs": round(gbs, 1),
+                                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    del W
+    torch.cuda.empty_cache()
     # chunked prefill: 4096 new tokens on a 131072-token context
     wl = specs.PREFILL_4K
     W = CsaPrefill(wl)
     ms, idx_ms, _ = time_steps(W, max(5, steps // 4), 2, 1, graph=not a.no_graph)
     tf = W.indexer_flops() / (idx_ms / 1e3) / 1e12
     out[wl.name] = {"tokens_per_s": round(W.new / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
-                    "indexer_gemm": {"kernel": "indexer_rows_kernel<false>", "kernel_ms": round(idx_ms, 4),
+                    "indexer_gemm": {"kernel": "indexer_rows_kernel<false, 8>", "kernel_ms": round(idx_ms, 4),
                                      "flop_per_launch": W.indexer_flops(), "achieved_TFLOPs": round(tf, 1),
                                      "fp8_mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}}
     del W
@@ -372,6 +383,10 @@ def main():
         elif a.profile_only == "decode_1m":
             wl = specs.DECODE_1M
             W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
+        elif a.profile_only == "spec_decode":
+            from workloads.device import CsaSpecDecode
+            wl = specs.SPEC_DECODE_128K
+            W = CsaSpecDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
         elif a.profile_only == "copy":
             n = 1 << 28  # 1 GiB of float32 read and 1 GiB written per copy
             src = torch.ones(n, device="cuda")

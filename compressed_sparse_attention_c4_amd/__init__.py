@@ -12,7 +12,8 @@ from __future__ import annotations
 from ._binding import (  # noqa: F401
     CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP,
     CSA_BF16, CSA_F32, CSA_FP8_E4M3, CSA_MXFP4, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN,
-    CSA_OP_INDEXER, CSA_OP_INDEXER_TOPK, CSA_OP_TOPK, CSA_PREP_HADAMARD, CSA_PREP_QUANT, CsaError,
+    CSA_OP_INDEXER, CSA_OP_INDEXER_TOPK, CSA_OP_TOPK, CSA_PREP_HADAMARD, CSA_PREP_QUANT,
+    CSA_ROWS_PER_SEQ, CsaError,
     IndexPool, KvPool, LIB_PATH, c4_compress, csa_decode_prep, csa_index_prep, csa_sparse_attn,
     csa_status_string, csa_version, csa_workspace_size, hca_dense_attn, indexer_score,
     indexer_topk512, lib, topk512_page_select,

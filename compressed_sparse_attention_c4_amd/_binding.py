@@ -20,6 +20,11 @@ lib = C.CDLL(LIB_PATH)
 CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = range(5)
 CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4 = range(4)
 CSA_PREP_HADAMARD, CSA_PREP_QUANT = 1, 2
+
+
+def CSA_ROWS_PER_SEQ(n: int) -> int:
+    """The rows-per-sequence hint bits of an indexer call's `prep` flags."""
+    return (int(n) & 0xFF) << 8
 CSA_OP_INDEXER, CSA_OP_TOPK, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN, CSA_OP_INDEXER_TOPK = range(5)
 CSA_TOPK, CSA_C4_RATIO, CSA_HCA_RATIO, CSA_RAW_PAGE, CSA_C4_PAGE = 512, 4, 128, 256, 64
 

@@ -28,9 +28,10 @@ csa_status indexer_args(csa_fmt q_fmt, const void* q_scale, uint32_t prep, int32
   if (T < 0 || H_I <= 0 || max_row_len < 0 || pt_stride <= 0) return CSA_ERR_INVALID;
   if (k.page_size <= 0 || k.dim != D_I) return CSA_ERR_INVALID;
   if ((q_used == nullptr) != (q_used_scale == nullptr)) return CSA_ERR_INVALID;
-  if (prep & ~(CSA_PREP_HADAMARD | CSA_PREP_QUANT)) return CSA_ERR_INVALID;
+  if (prep & ~(CSA_PREP_HADAMARD | CSA_PREP_QUANT | CSA_ROWS_PER_SEQ(0xFF))) return CSA_ERR_INVALID;
+  const uint32_t prep_ops = prep & (CSA_PREP_HADAMARD | CSA_PREP_QUANT);
   if (k.fmt == CSA_F32) {
-    if (q_fmt != CSA_F32 || prep != 0) return CSA_ERR_INVALID;
+    if (q_fmt != CSA_F32 || prep_ops != 0) return CSA_ERR_INVALID;
     if (D_I != 64 && D_I != 128) return CSA_ERR_UNSUPPORTED;
     if ((size_t)H_I * D_I > 8192) return CSA_ERR_UNSUPPORTED;
     if (q_used) return CSA_ERR_INVALID;
@@ -39,11 +40,11 @@ csa_status indexer_args(csa_fmt q_fmt, const void* q_scale, uint32_t prep, int32
     if (k.page_size % 16 != 0) return CSA_ERR_UNSUPPORTED;
     if (!k.scale) return CSA_ERR_INVALID;
     if (q_fmt == CSA_BF16 || q_fmt == CSA_F32) {
-      if (!(prep & CSA_PREP_QUANT)) return CSA_ERR_INVALID;
+      if (!(prep_ops & CSA_PREP_QUANT)) return CSA_ERR_INVALID;
       if (!q_used && ws_bytes < indexer_ws_bytes(T, H_I)) return CSA_ERR_WORKSPACE;
       if (!q_used && !ws) return CSA_ERR_WORKSPACE;
     } else if (q_fmt == k.fmt) {
-      if (prep != 0 || !q_scale) return CSA_ERR_INVALID;
+      if (prep_ops != 0 || !q_scale) return CSA_ERR_INVALID;
     } else {
       return CSA_ERR_INVALID;
     }
@@ -219,7 +220,7 @@ csa_status indexer_topk512(const void* q, csa_fmt q_fmt, const void* q_scale, ui
   if (!ws || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
   if (!q || !w || !row_seq || !row_len || !page_table || !k.data || !phys_idx) return CSA_ERR_INVALID;
   uint8_t* base = (uint8_t*)ws;
-  const int chunks = indexer_cand_chunks(T, H_I, D_I, k, max_row_len);
+  const int chunks = indexer_cand_chunks(T, H_I, D_I, k, max_row_len, prep);
   hipError_t e;
   if (chunks > 0) {
     uint32_t* ck = (uint32_t*)(base + L.prep);

@@ -61,8 +61,10 @@ constexpr int kCandGroups = 8;
 // physical slot), then one final pass per row, which takes the slots from the
 // candidates instead of looking them up.
 // Returns the scan chunks per row, or 0 when the shapes need the two calls.
+// `prep` carries the rows-per-sequence hint, which may route the rows to the
+// row-block kernel (two calls).
 int indexer_cand_chunks(int64_t T, int H_I, int D_I, const csa_index_pool& k,
-                        int64_t max_row_len);
+                        int64_t max_row_len, uint32_t prep);
 // Chunks per row of the decode scan kernel for these sizes.
 int64_t indexer_scan_chunks(int64_t T, int64_t max_row_len);
 // A row's candidates in groups of `group` (a multiple of 512) reduced to one

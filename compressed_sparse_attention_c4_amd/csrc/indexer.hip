@@ -20,6 +20,7 @@
 #include <limits.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "csa_device.hpp"
@@ -267,44 +268,52 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   }
 }
 
-// Many query rows (prefill): a workgroup of 8 waves owns 8 consecutive rows
-// (one row's 64 heads per wave, in registers) and walks the index-K pages of
-// their sequence once: each 64-entry page is staged into LDS with one
-// coalesced 16-byte load per thread (double-buffered, 16-byte chunks
-// XOR-swizzled by entry so the MFMA operand reads are conflict-free) and
-// scored by all 8 waves, so index-K is read from L2 once per 8 rows instead
-// of once per row. Row ends (the causal rule) are enforced by per-row buffer
-// stores bounded to row_len. A row of another sequence than the workgroup's
-// first row reads its own pages straight from memory.
-constexpr int kRowsPerWG = 8;
+// Many query rows of few sequences (prefill; multi-token decode, whose rows
+// come in groups that share a sequence): a workgroup of 8 waves owns kRows
+// consecutive rows (8, 4 or 2; each row's 64 heads in registers, a row shared
+// by 8 / kRows waves that split each page's four 16-entry groups) and walks a
+// range of the index-K pages of their sequence once: each 64-entry page is
+// staged into LDS with one coalesced 16-byte load per thread (double-buffered,
+// 16-byte chunks XOR-swizzled by entry so the MFMA operand reads are
+// conflict-free) and scored by all the rows, so index-K is read once per
+// kRows rows instead of once per row. blockIdx.y picks the range (pages
+// [y * ppc, (y + 1) * ppc)), so that a few row groups still fill the chip. Row
+// ends (the causal rule) are enforced by per-row buffer stores bounded to
+// row_len. A row of another sequence than the workgroup's first row reads its
+// own pages straight from memory.
+constexpr int kRowsPerWG = 8;  // waves per workgroup (and rows, at most)
 
-template <bool kFp4>
+template <bool kFp4, int kRows>
 __global__ void __launch_bounds__(kRowsPerWG * 64)
 indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     const float* __restrict__ w, const int32_t* __restrict__ row_seq,
                     const int32_t* __restrict__ row_len, int T, const int32_t* __restrict__ pt,
                     int pt_stride, const uint8_t* __restrict__ kdata,
-                    const void* __restrict__ kscale, float* __restrict__ logits, int64_t ld) {
+                    const void* __restrict__ kscale, float* __restrict__ logits, int64_t ld,
+                    int ppc) {
+  static_assert(kRows == 8 || kRows == 4 || kRows == 2, "rows per workgroup");
+  constexpr int kWpr = kRowsPerWG / kRows;  // waves per row
   constexpr int kPage = 64;                          // entries per page (= tile)
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K row
   constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per row
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kPage * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint32_t s_bs[2][kPage];  // fp32 scale / 4 e8m0 bytes
-  __shared__ int s_len[kRowsPerWG];
+  __shared__ int s_len[kRows];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the row state scalar
+  const int sub = wave % kWpr;  // this wave scores the groups g with g % kWpr == sub
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int t0 = blockIdx.x * kRowsPerWG;
-  const int t = t0 + wave;
+  const int t0 = blockIdx.x * kRows;
+  const int t = t0 + wave / kWpr;
   const bool row_ok = t < T;
   const int seq0 = row_seq[t0];
   const int seqw = row_ok ? row_seq[t] : seq0;
   const bool own = seqw == seq0;
   const int nw = row_ok ? row_len[t] : 0;
-  if (lane == 0) s_len[wave] = own ? nw : -nw - 1;  // rows of another sequence stored negated
+  if (lane == 0 && sub == 0) s_len[wave / kWpr] = own ? nw : -nw - 1;  // other sequence: negated
 
   // query operands and head weights of this wave's row
   v8i a[4];
@@ -335,13 +344,15 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   __syncthreads();
   int maxown = 0, maxall = 0;  // staging covers the first sequence's rows only
 #pragma unroll
-  for (int i = 0; i < kRowsPerWG; ++i) {
+  for (int i = 0; i < kRows; ++i) {
     const int v = s_len[i];
     maxown = max(maxown, v);
     maxall = max(maxall, v >= 0 ? v : -v - 1);
   }
-  const int npages = (maxall + kPage - 1) / kPage;
-  const int nstage = (maxown + kPage - 1) / kPage;
+  // this workgroup's page range [pc0, pc1)
+  const int pc0 = blockIdx.y * ppc, pc1 = pc0 + ppc;
+  const int npages = min((maxall + kPage - 1) / kPage, pc1);
+  const int nstage = min((maxown + kPage - 1) / kPage, pc1);
   const __amdgpu_buffer_rsrc_t out_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(logits + (int64_t)tq * ld, (short)0, nw * 4, 0x00020000);
   const int32_t* pt0 = pt + (int64_t)seq0 * pt_stride;
@@ -367,11 +378,11 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
     sstage[k] = *reinterpret_cast<const v4i*>(reinterpret_cast<const uint8_t*>(kscale) + (base + sce) * 4);
   };
   // issue order fixed (slot 0 oldest) so the loop head waits only for slot 0
-  load_page(0, std::integral_constant<int, 0>{});
+  load_page(pc0, std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
-  load_page(1, std::integral_constant<int, 1>{});
+  load_page(pc0 + 1, std::integral_constant<int, 1>{});
   __builtin_amdgcn_sched_barrier(0);
-  load_page(2, std::integral_constant<int, 2>{});
+  load_page(pc0 + 2, std::integral_constant<int, 2>{});
   __builtin_amdgcn_sched_barrier(0);
   // 64 heads x 16 entries: 4 MFMAs, ReLU, head weights, 64-head reduction,
   // logit store (lanes of rows past their row_len are dropped by the buffer)
@@ -412,13 +423,15 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
     if (scaler) *reinterpret_cast<v4i*>(&s_bs[buf][sce]) = sstage[k];
     __syncthreads();
     load_page(p + kDepth, K);  // refill the slot just written to LDS
-    if (own && p * kPage < nw) {
+    if (own && p * kPage < nw && p < pc1) {  // (the loop runs past pc1 to a multiple of kDepth)
       // the four 16-entry groups of the page; one reduce-scatter across the
       // lane rows then leaves the 64-head sum of group r in row r, so each
       // lane holds one logit and the wave stores the page's 64 logits at once
       float pk[kPage / 16];
 #pragma unroll
       for (int g = 0; g < kPage / 16; ++g) {
+        pk[g] = 0.f;
+        if (g % kWpr != sub) continue;  // another wave of the row scores group g
         const int e = g * 16 + col;
         v8i bb;
         int sb = 127;
@@ -437,20 +450,23 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
       const float tot = rows4_reduce_scatter(pk[0], pk[1], pk[2], pk[3]);
       const int e = grp * 16 + col;  // the entry whose logit this lane holds
       const float ks = kFp4 ? 1.f : __uint_as_float(s_bs[buf][e]);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot * ks), out_rsrc, (p * kPage + e) * 4, 0, 0);
+      const int off = grp % kWpr == sub ? (p * kPage + e) * 4 : 0x7FFFFFFF;  // past the buffer: dropped
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot * ks), out_rsrc, off, 0, 0);
     }
   };
   static_assert(kDepth == 3, "the page loop below is unrolled by hand for three slots");
   // steps past the last page only stage (clamped) and synchronise: no branch
   // inside the loop keeps the load counters exact across its back edge
-  for (int p0 = 0; p0 < npages; p0 += kDepth) {
+  for (int p0 = pc0; p0 < npages; p0 += kDepth) {
     page_step(p0, std::integral_constant<int, 0>{});
     page_step(p0 + 1, std::integral_constant<int, 1>{});
     page_step(p0 + 2, std::integral_constant<int, 2>{});
   }
-  // a row of another sequence: its own pages, read straight from memory
+  // a row of another sequence: its own pages of the range, read straight from
+  // memory (the row's waves take turns by 16-entry group)
   if (!own && row_ok) {
-    for (int j0 = 0; j0 < nw; j0 += 16) {
+    const int jend = min(nw, pc1 * kPage);
+    for (int j0 = pc0 * kPage + 16 * sub; j0 < jend; j0 += 16 * kWpr) {
       const int e = j0 + col;
       const int ee = min(e, nw - 1);
       const int64_t slot = (int64_t)ptw[ee / kPage] * kPage + ee % kPage;
@@ -527,9 +543,16 @@ static int64_t scan_chunk(int64_t T, int64_t max_row_len) {
   return chunk;
 }
 
-// Many rows over 64-entry pages go to the row-block kernel.
-static bool uses_rows_kernel(int64_t T, const csa_index_pool& k) {
-  return T >= kRowsPerWG * 32 && k.page_size == 64 && !getenv("CSA_TUNE_INDEXER_NO_ROWS");
+// Rows per workgroup of the row-block kernel for this call, or 0 for the
+// per-row scan. Rows that come in groups sharing a sequence (the prep flags'
+// rows-per-sequence hint: a multiple of 2, 4 or 8) take it with the largest of
+// 8, 4, 2 that divides the group; otherwise many rows (prefill) take it with
+// 8. Only 64-entry pages.
+static int rows_kernel_rows(int64_t T, const csa_index_pool& k, uint32_t prep) {
+  if (k.page_size != 64 || getenv("CSA_TUNE_INDEXER_NO_ROWS")) return 0;
+  const uint32_t g = (prep >> 8) & 0xFFu;
+  if (g >= 2) return g % 8 == 0 ? 8 : g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 0;
+  return T >= kRowsPerWG * 32 ? 8 : 0;
 }
 
 int64_t indexer_scan_chunks(int64_t T, int64_t max_row_len) {
@@ -538,10 +561,10 @@ int64_t indexer_scan_chunks(int64_t T, int64_t max_row_len) {
 }
 
 int indexer_cand_chunks(int64_t T, int H_I, int D_I, const csa_index_pool& k,
-                        int64_t max_row_len) {
+                        int64_t max_row_len, uint32_t prep) {
   if (k.fmt != CSA_FP8_E4M3 && k.fmt != CSA_MXFP4) return 0;
   if (H_I != kHeads || D_I != kDim || k.page_size % 16 != 0) return 0;
-  if (T == 0 || max_row_len == 0 || uses_rows_kernel(T, k)) return 0;
+  if (T == 0 || max_row_len == 0 || rows_kernel_rows(T, k, prep)) return 0;
   const int64_t chunks = indexer_scan_chunks(T, max_row_len);
   return chunks * kTopK <= (int64_t)kCandGroups * kCandFinalMax ? (int)chunks : 0;
 }
@@ -572,7 +595,8 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
       dst = ws;
       dsts = (uint8_t*)ws + (((size_t)T * H_I * kDim + 255) & ~(size_t)255);
     }
-    hipError_t e = launch_index_prep(q, q_fmt, (int64_t)T * H_I, D_I, prep, k.fmt, dst, dsts,
+    hipError_t e = launch_index_prep(q, q_fmt, (int64_t)T * H_I, D_I,
+                                     prep & (CSA_PREP_HADAMARD | CSA_PREP_QUANT), k.fmt, dst, dsts,
                                      nullptr, s);
     if (e != hipSuccess) return e;
     qc = (const uint8_t*)dst;
@@ -586,16 +610,27 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
     if (e != hipSuccess) return e;
   }
   const int64_t chunk = scan_chunk(T, max_row_len);
-  if (!okeys && uses_rows_kernel(T, k)) {
-    dim3 g2((T + kRowsPerWG - 1) / kRowsPerWG);
-    if (k.fmt == CSA_MXFP4)
-      hipLaunchKernelGGL(indexer_rows_kernel<true>, g2, dim3(kRowsPerWG * 64), 0, s, qc, qs, w,
-                         row_seq, row_len, T, page_table, pt_stride, (const uint8_t*)k.data,
-                         k.scale, logits, ld);
-    else
-      hipLaunchKernelGGL(indexer_rows_kernel<false>, g2, dim3(kRowsPerWG * 64), 0, s, qc, qs, w,
-                         row_seq, row_len, T, page_table, pt_stride, (const uint8_t*)k.data,
-                         k.scale, logits, ld);
+  const int rows = okeys ? 0 : rows_kernel_rows(T, k, prep);
+  if (rows) {
+    // page ranges: enough workgroups to cover the CUs when the row groups are few
+    const int groups = (int)((T + rows - 1) / rows);
+    const int pages = (int)((max_row_len + 63) / 64);
+    const int ranges = std::max(1, std::min(pages, (256 + groups - 1) / groups));
+    const int ppc = (pages + ranges - 1) / ranges;
+    dim3 g2(groups, (pages + ppc - 1) / ppc);
+#define CSA_ROWS(FP4, R)                                                                          \
+  hipLaunchKernelGGL((indexer_rows_kernel<FP4, R>), g2, dim3(kRowsPerWG * 64), 0, s, qc, qs, w,   \
+                     row_seq, row_len, T, page_table, pt_stride, (const uint8_t*)k.data, k.scale, \
+                     logits, ld, ppc)
+    const bool fp4 = k.fmt == CSA_MXFP4;
+    if (rows == 8) {
+      if (fp4) CSA_ROWS(true, 8); else CSA_ROWS(false, 8);
+    } else if (rows == 4) {
+      if (fp4) CSA_ROWS(true, 4); else CSA_ROWS(false, 4);
+    } else {
+      if (fp4) CSA_ROWS(true, 2); else CSA_ROWS(false, 2);
+    }
+#undef CSA_ROWS
     return hipGetLastError();
   }
   dim3 grid((unsigned)((max_row_len + chunk - 1) / chunk), T);

@@ -85,6 +85,17 @@ typedef enum {
 /* Index preparation flags ([P1] §4: q and K go rope -> hadamard -> quant). */
 #define CSA_PREP_HADAMARD 1u  /* v <- H_D v / sqrt(D), Sylvester order */
 #define CSA_PREP_QUANT    2u  /* quantise to the index pool's format   */
+/*
+ * Rows-per-sequence hint for indexer_score / indexer_topk512 (OR-ed into
+ * `prep`; n in 0..255, 0 = no hint): the query rows come in consecutive groups
+ * of n that share a sequence, row_seq[t] == row_seq[n * (t / n)], as the q_len
+ * query tokens of each sequence in multi-token (speculative-verify) decode.
+ * Results are the same with or without it. When n is a multiple of 2, 4 or 8
+ * and the pool has 64-entry pages, each index-K page is read once for up to 8
+ * rows of a group instead of once per row (a row whose sequence differs from
+ * its group's first row is still scored correctly, from its own pages).
+ */
+#define CSA_ROWS_PER_SEQ(n) ((((uint32_t)(n)) & 0xFFu) << 8)
 
 typedef struct {
   void*   latent;        /* see the KV entry layout above */
@@ -205,7 +216,7 @@ csa_status csa_decode_prep(const void* x, csa_fmt x_fmt, const int32_t* pos, int
  *            [T][H_I][D_I/32] e8m0 for MXFP4). A prepared q must match k.fmt.
  *   prep     0 or CSA_PREP_HADAMARD | CSA_PREP_QUANT for raw q: rotate and
  *            quantise q exactly as csa_index_prep does, to k.fmt. An F32 pool takes
- *            raw F32 q with prep 0.
+ *            raw F32 q with prep 0. Either may be OR-ed with CSA_ROWS_PER_SEQ(n).
  *   w        float [T][H_I] head weights (w >= 0).
  *   row_seq, row_len  int32 [T]: sequence and visible length of each query row
  *            (decode: row_len = c4 length; prefill: row_len = min(N, (p+1)/4)).

@@ -71,6 +71,7 @@ class SeqState:
         self.ipool = O.IndexPool(codes, sc, wl.index_fmt)
         self.c4 = LazyKVPool(kv_fn, wl.kv_fmt)
         self.raw = O.KVPool(*O.quant_kv_entries(raw_rows, wl.kv_fmt), wl.kv_fmt)
+        self._raw_rows = raw_rows
         self.raw_pos0 = raw_pos0
         self.q_idx, self.w_idx, self.q_attn = q_idx, w_idx, q_attn
         self.p, self.row_len = p, row_len
@@ -131,6 +132,25 @@ def decode_seq(W, b: int) -> SeqState:
     raw_pos0, raw_rows = decode_raw_tail(W, b, stepped=True)
     return SeqState(wl, kraw, kv_fn, raw_pos0, raw_rows, host(W.q_idx)[b], host(W.w_idx)[b],
                     host(W.q_attn)[b], L - 1, N)
+
+
+def spec_decode_row(W, t: int) -> SeqState:
+    """Query row t of a CsaSpecDecode after one step: sequence b = t // 4 at
+    position L - 4 + t % 4; the step stored the block's four rows at raw
+    positions L - 4 .. L - 1 and completed block N - 1."""
+    b = t // W.wl.q_len
+    st = decode_seq(W, b)
+    L = int(W.lens[b])
+    x_new = host(W.x_new).reshape(W.B, 4, 576)[b]
+    for i in range(3):
+        st_row = O.compress_blocks(x_new[i:i + 1], L - 4 + i, 1, np.zeros(576), np.zeros(1))[0]
+        rows = np.array(st._raw_rows)
+        rows[L - 4 + i - st.raw_pos0] = st_row
+        st._raw_rows = rows
+    st.raw = O.KVPool(*O.quant_kv_entries(st._raw_rows, W.wl.kv_fmt), W.wl.kv_fmt)
+    st.q_idx, st.w_idx, st.q_attn = host(W.q_idx)[t], host(W.w_idx)[t], host(W.q_attn)[t]
+    st.p, st.row_len = int(W.pos_host[t]), int(W.rows_len_host[t])
+    return st
 
 
 def hca_oracle(Wh, b: int) -> np.ndarray:

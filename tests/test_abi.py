@@ -166,6 +166,10 @@ def test_indexer_topk512_rejects_bad_arguments(lib):
     assert call(ws_bytes=need - 1) == WORKSPACE
     assert call(phys=None) == INVALID                       # phys_idx is required
     assert call(max_len=-1) == INVALID
+    # the rows-per-sequence hint occupies bits 8..15 of prep; other bits are invalid
+    assert call(prep=1 << 16) == INVALID
+    assert call(q_fmt=3, prep=4 << 8) == INVALID            # the hint does not mask other errors
+    assert call(phys=None, prep=4 << 8) == INVALID           # (checks run before any launch)
 
 
 def test_topk_and_attention_reject_bad_arguments(lib):

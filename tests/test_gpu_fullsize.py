@@ -122,6 +122,27 @@ def test_decode_128k_sampled(csa):
     assert compared >= 1, "no sampled sequence had an unambiguous top-512"
 
 
+def test_spec_decode_128k_sampled(csa):
+    """32 x 128K multi-token decode (4 query rows per sequence, the indexer's
+    rows-per-sequence hint): the step's selection is the top-512 of its
+    scan's logits; sampled rows (causal row lengths N-1 and N, windows ending
+    at their own positions) against the oracle."""
+    from workloads import specs
+    from workloads.device import CsaSpecDecode
+    wl = specs.SPEC_DECODE_128K
+    W = CsaSpecDecode(wl, [wl.seq_len] * wl.batch, copies=1, pool_pages=wl.pool_pages)
+    W.step(0)
+    torch.cuda.synchronize()
+    gp, go = W.phys.cpu().numpy(), W.out.float().cpu().numpy()
+    gl = _scan_logits(csa, W)
+    compared = 0
+    for t in (0, 3, 54, 127):
+        st = F.spec_decode_row(W, t)
+        b = t // wl.q_len
+        compared += _check_csa_row(st, gl[t], gp[t], W.pt_host[b], go[t], f"row {t}")
+    assert compared >= 1
+
+
 def test_decode_1m_sampled(csa):
     """4 x 1M decode (MXFP4 index-K, 128 attention heads)."""
     from workloads import specs

@@ -559,6 +559,57 @@ def test_indexer_many_rows_causal(csa, fmt):
         assert np.all(np.isnan(got[t, n:])), f"row {t} wrote past row_len"
 
 
+@pytest.mark.parametrize("fmt,q_len", [("fp8", 4), ("mxfp4", 8), ("fp8", 2), ("fp8", 6)])
+def test_indexer_rows_per_seq(csa, fmt, q_len):
+    """Multi-token decode: q_len query rows per sequence (positions L-q_len ..
+    L-1, causal row length min(N, (p+1)/4)) with the CSA_ROWS_PER_SEQ hint,
+    which sends each group's rows to the row-block kernel over page ranges.
+    Every row within 1e-4 of its max of the oracle's logits; rows past their
+    row_len untouched; a row whose sequence differs from its group's (the hint
+    broken on purpose) still scored from its own pages; indexer_topk512 with
+    the hint equal to indexer_score + topk512_page_select."""
+    g = gen.rng(1250 + q_len + len(fmt))
+    lens = [131072 // 8 + 4 * 997 + 3, 20000, 4096 + 1, 900]  # raw lengths
+    S = len(lens)
+    Ns = [L // 4 for L in lens]
+    pt, pool, _ = _index_case(g, fmt, S, Ns)
+    T = S * q_len
+    row_seq = np.repeat(np.arange(S, dtype=np.int32), q_len)
+    pos = np.concatenate([np.arange(L - q_len, L) for L in lens])
+    row_len = np.minimum(np.repeat(Ns, q_len), (pos + 1) // 4).astype(np.int32)
+    row_seq[q_len + 1] = 3  # breaks the hint: read from its own pages
+    row_len[q_len + 1] = Ns[3]
+    qraw = gen.normal(g, (T, 64, 128))
+    qcodes, qsc = O.index_prep(qraw, True, fmt)
+    w = gen.uniform(g, (T, 64))
+    maxn = max(Ns)
+    qfmt = csa.CSA_FP8_E4M3 if fmt == "fp8" else csa.CSA_MXFP4
+    qs = t_dev(qsc.astype(np.float32)) if fmt == "fp8" else t_dev(qsc)
+    dpool = index_pool_to_device(pool, 64, 128)
+    hint = csa.CSA_ROWS_PER_SEQ(q_len)
+    drs, drl, dpt = t_dev(row_seq), t_dev(row_len), t_dev(pt)
+    logits = torch.full((T, maxn), float("nan"), device=DEV)
+    csa.indexer_score(t_dev(qcodes), t_dev(w), drs, drl, maxn, dpt, dpool, logits, q_fmt=qfmt,
+                      q_scale=qs, prep=hint)
+    got = logits.cpu().numpy()
+    qhat = O.index_dequant(qcodes, qsc, fmt)
+    for t in range(T):
+        n = int(row_len[t])
+        want = O.indexer_logits(qhat[t], w[t], pool.rows(O.page_slot(pt[row_seq[t]], np.arange(n), 64)))
+        np.testing.assert_allclose(got[t, :n], want, rtol=0, atol=1e-4 * np.abs(want).max(),
+                                   err_msg=f"row {t}")
+        assert np.all(np.isnan(got[t, n:])), f"row {t} wrote past row_len"
+    phys = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    logi = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    csa.indexer_topk512(t_dev(qcodes), t_dev(w), drs, drl, maxn, dpt, dpool, phys, logi, q_fmt=qfmt,
+                        q_scale=qs, prep=hint)
+    phys2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    logi2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    csa.topk512_page_select(logits.nan_to_num(nan=-float("inf")), drl, drs, dpt, phys2, logi2)
+    assert np.array_equal(phys.cpu().numpy(), phys2.cpu().numpy())
+    assert np.array_equal(logi.cpu().numpy(), logi2.cpu().numpy())
+
+
 # ------------------------------------------------------------------ fused decode preparation
 
 

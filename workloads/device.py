@@ -209,6 +209,96 @@ class CsaDecode:
                             wl.window, wl.softmax_scale, self.out, ws=self.attn_ws)
 
 
+class CsaSpecDecode(CsaDecode):
+    """One multi-token (speculative-verify) decode step: each of B sequences
+    of raw length L gains q_len = 4 tokens (positions L-4 .. L-1, one complete
+    C4 block, L % 4 == 0) and runs q_len query rows. The cache writes are the
+    block's compressed entry and index-K row and the four raw rows; each query
+    row has its causal row length min(N, (p+1)/4) and its own window; the
+    indexer gets the rows-per-sequence hint, so each index-K page is read once
+    per sequence, not once per row."""
+
+    def __init__(self, wl: Workload, lens, copies: int = 3, pool_pages: int | None = None):
+        super().__init__(wl, lens, copies=copies, pool_pages=pool_pages)
+        assert wl.q_len == 4 and all(int(L) % 4 == 0 for L in self.lens)
+        B, Q, H = self.B, wl.q_len, self.H
+        self.T = T = B * Q
+        seed = self.seed
+        pos = np.concatenate([np.arange(int(L) - Q, int(L)) for L in self.lens])
+        self.pos_host = pos
+        self.rows_len_host = np.minimum(np.repeat(self.N, Q), (pos + 1) // 4)
+        self.row_seq = _i32(np.repeat(np.arange(B), Q))
+        self.row_len = _i32(self.rows_len_host)
+        self.q_pos = _i32(pos)
+        self.last_pos = _i32(self.lens - 1)
+        # the block's first three rows go to the raw pool in a ratio-1 store
+        self.x_early = self.x_new.view(B, 4, 576)[:, :3].contiguous()
+        self.early_cu = _i32(np.arange(B + 1) * 3)
+        self.early_start = _i32(self.lens - 4)
+        self.q_idx = gen.device_normal((T, wl.index_heads, wl.index_dim), seed + 16)
+        self.w_idx = gen.device_uniform((T, wl.index_heads), seed + 17)
+        self.q_attn = gen.device_normal((T, H, 576), seed + 18)
+        self.phys = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+        self.out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=DEV)
+        n = csa.csa_workspace_size(csa.CSA_OP_CSA_ATTN, T, 512 + wl.window, H)
+        self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        n = csa.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK, T, self.maxN, wl.index_heads)
+        self.itk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        qbytes = wl.index_dim if self.fmt == csa.CSA_FP8_E4M3 else wl.index_dim // 2
+        self.q_codes = torch.empty((T, wl.index_heads, qbytes), dtype=torch.uint8, device=DEV)
+        if self.fmt == csa.CSA_FP8_E4M3:
+            self.q_scale = torch.empty((T, wl.index_heads), dtype=torch.float32, device=DEV)
+        else:
+            self.q_scale = torch.empty((T, wl.index_heads, wl.index_dim // 32), dtype=torch.uint8,
+                                       device=DEV)
+        self.zero_w, self.zero_b = torch.zeros(576, device=DEV), torch.zeros(1, device=DEV)
+        self.logits = torch.empty((T, self.maxN), dtype=torch.float32, device=DEV)
+        torch.cuda.synchronize()
+
+    @property
+    def indexer_kernel(self) -> str:
+        fp4 = "true" if self.fmt == csa.CSA_MXFP4 else "false"
+        return f"indexer_rows_kernel<{fp4}, {self.wl.q_len}>"
+
+    def indexer_bytes(self) -> int:
+        """Algorithmic bytes of the indexer launch: index-K rows of each
+        sequence once (shared by its rows), the prepared queries and head
+        weights, page-table rows and the logits written."""
+        per_entry = (self.wl.index_dim + 4) if self.fmt == csa.CSA_FP8_E4M3 else (self.wl.index_dim // 2 + 4)
+        n = int(self.N.sum())
+        q = self.T * self.wl.index_heads * (self.wl.index_dim + 4 + 4)
+        return n * per_entry + q + n // C4_PAGE * 4 + int(self.rows_len_host.sum()) * 4
+
+    def score_only(self, c: int):
+        """The step's indexer logits into self.logits (the same kernel as the
+        step: indexer_score with the hint). For tests; run after step(c)."""
+        csa.indexer_score(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.maxN, self.pt,
+                          self.index_pools[c], self.logits, q_fmt=self.fmt, q_scale=self.q_scale,
+                          prep=csa.CSA_ROWS_PER_SEQ(self.wl.q_len))
+
+    def step(self, c: int, ev=None):
+        idx, kv = self.index_pools[c], self.c4_pools[c]
+        wl = self.wl
+        # the block the four tokens complete (compressed entry, index-K row) and
+        # the last token's raw row, then the three earlier raw rows
+        csa.csa_decode_prep(self.x_new.view(self.B, 4, 576), self.last_pos, self.gate_w, self.gate_b,
+                            self.pt, kv, self.pt, self.raw, k_rows=self.k_new, kpool=idx,
+                            flags=csa.CSA_PREP_HADAMARD)
+        csa.c4_compress(self.x_early, self.early_cu, self.early_start, 3, 1, self.zero_w, self.zero_b,
+                        self.pt, self.raw)
+        csa.csa_index_prep(self.q_idx, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt, self.q_codes,
+                           self.q_scale)
+        if ev is not None:
+            ev[0].record()
+        # the hint routes each sequence's four rows to one page walk
+        csa.indexer_topk512(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.maxN, self.pt,
+                            idx, self.phys, q_fmt=self.fmt, q_scale=self.q_scale,
+                            prep=csa.CSA_ROWS_PER_SEQ(wl.q_len), ws=self.itk_ws,
+                            scan_done=None if ev is None else ev[1])
+        csa.csa_sparse_attn(self.q_attn, self.row_seq, self.q_pos, self.phys, kv, self.raw, self.pt,
+                            wl.window, wl.softmax_scale, self.out, ws=self.attn_ws)
+
+
 class CsaPrefill:
     """Chunked prefill: `new` query tokens appended to a context of `ctx` raw
     tokens (batch 1). One step: compress the new tokens' blocks and append

@@ -36,6 +36,7 @@ class Workload:
     new_tokens: int = 0            # prefill: new query tokens appended to the context
     hca_ratio: int = 0             # > 0: an HCA layer runs beside the CSA layer
     ragged: tuple = field(default=())  # (n_seqs, lo, hi) for log-uniform raw lengths
+    q_len: int = 1                 # query tokens per sequence and step (multi-token decode)
     window: int = WINDOW
     softmax_scale: float = KV_DIM ** -0.5
 
@@ -55,6 +56,11 @@ DECODE_1M = Workload(
     index_fmt="mxfp4", index_heads=64, index_dim=128, hadamard=True, heads=128,
     q_dtype="bf16", out_dtype="bf16", pool_pages=16384)
 
+SPEC_DECODE_128K = Workload(
+    name="csa_spec_decode_128k_b32_q4", seed=1006, batch=32, seq_len=131072, kv_fmt="fp8",
+    index_fmt="fp8", index_heads=64, index_dim=128, hadamard=True, heads=64,
+    q_dtype="bf16", out_dtype="bf16", pool_pages=16384, q_len=4)
+
 PREFILL_4K = Workload(
     name="csa_prefill_4096_on_128k", seed=1004, batch=1, seq_len=131072 + 4096, kv_fmt="fp8",
     index_fmt="fp8", index_heads=64, index_dim=128, hadamard=True, heads=64,
@@ -65,5 +71,5 @@ HCA_RAGGED = Workload(
     index_fmt="fp8", index_heads=64, index_dim=128, hadamard=True, heads=64,
     q_dtype="bf16", out_dtype="bf16", hca_ratio=128, ragged=(16, 8192, 1048576))
 
-ALL = (TINY_FP32_DECODE, DECODE_128K, DECODE_1M, PREFILL_4K, HCA_RAGGED)
+ALL = (TINY_FP32_DECODE, DECODE_128K, DECODE_1M, SPEC_DECODE_128K, PREFILL_4K, HCA_RAGGED)
 BY_NAME = {w.name: w for w in ALL}
