@@ -855,8 +855,11 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const int32_t* __restri
   }
 }
 
+// The two-phase path for up to 64 (query, 64-head block) units: at 128 (32
+// sequences x 4 query tokens at 128K) the split kernel with two splits and the
+// combine took 50 us against 58 us for the two phases.
 bool use_two_phase(int T, int H, int max_entries) {
-  return H % 64 == 0 && T * (H / 64) <= 128 && max_entries <= kTwoPhaseMaxE && max_entries > 0;
+  return H % 64 == 0 && T * (H / 64) <= 64 && max_entries <= kTwoPhaseMaxE && max_entries > 0;
 }
 
 // Workspace of the two-phase path: P' [T][H][e_pad] bf16, then the chunk
