@@ -270,8 +270,9 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
 
 // Many query rows of few sequences (prefill; multi-token decode, whose rows
 // come in groups that share a sequence): a workgroup of 8 waves owns kRows
-// consecutive rows (8, 4 or 2; each row's 64 heads in registers, a row shared
-// by 8 / kRows waves that split each page's four 16-entry groups) and walks a
+// consecutive rows (2..8; each row's 64 heads in registers, a row shared by
+// 8 / kRows waves that split each page's four 16-entry groups, the waves past
+// kRows * (8 / kRows) only stage) and walks a
 // range of the index-K pages of their sequence once: each 64-entry page is
 // staged into LDS with one coalesced 16-byte load per thread (double-buffered,
 // 16-byte chunks XOR-swizzled by entry so the MFMA operand reads are
@@ -291,7 +292,7 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     int pt_stride, const uint8_t* __restrict__ kdata,
                     const void* __restrict__ kscale, float* __restrict__ logits, int64_t ld,
                     int ppc) {
-  static_assert(kRows == 8 || kRows == 4 || kRows == 2, "rows per workgroup");
+  static_assert(kRows >= 2 && kRows <= kRowsPerWG, "rows per workgroup");
   constexpr int kWpr = kRowsPerWG / kRows;  // waves per row
   constexpr int kPage = 64;                          // entries per page (= tile)
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K row
@@ -308,12 +309,13 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   const int grp = lane >> 4;
   const int t0 = blockIdx.x * kRows;
   const int t = t0 + wave / kWpr;
-  const bool row_ok = t < T;
+  const bool live = wave < kRows * kWpr;  // the other waves only stage
+  const bool row_ok = live && t < T;
   const int seq0 = row_seq[t0];
   const int seqw = row_ok ? row_seq[t] : seq0;
   const bool own = seqw == seq0;
   const int nw = row_ok ? row_len[t] : 0;
-  if (lane == 0 && sub == 0) s_len[wave / kWpr] = own ? nw : -nw - 1;  // other sequence: negated
+  if (lane == 0 && sub == 0 && live) s_len[wave / kWpr] = own ? nw : -nw - 1;  // other sequence: negated
 
   // query operands and head weights of this wave's row
   v8i a[4];
@@ -545,13 +547,17 @@ static int64_t scan_chunk(int64_t T, int64_t max_row_len) {
 
 // Rows per workgroup of the row-block kernel for this call, or 0 for the
 // per-row scan. Rows that come in groups sharing a sequence (the prep flags'
-// rows-per-sequence hint: a multiple of 2, 4 or 8) take it with the largest of
-// 8, 4, 2 that divides the group; otherwise many rows (prefill) take it with
-// 8. Only 64-entry pages.
+// rows-per-sequence hint g >= 2) take it with the largest divisor of g in
+// 2..8 (none: a prime above 8); otherwise many rows (prefill) take it with 8.
+// Only 64-entry pages.
 static int rows_kernel_rows(int64_t T, const csa_index_pool& k, uint32_t prep) {
   if (k.page_size != 64 || getenv("CSA_TUNE_INDEXER_NO_ROWS")) return 0;
-  const uint32_t g = (prep >> 8) & 0xFFu;
-  if (g >= 2) return g % 8 == 0 ? 8 : g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 0;
+  const int g = (int)((prep >> 8) & 0xFFu);
+  if (g >= 2) {
+    for (int r = kRowsPerWG; r >= 2; --r)
+      if (g % r == 0) return r;
+    return 0;
+  }
   return T >= kRowsPerWG * 32 ? 8 : 0;
 }
 
@@ -623,13 +629,21 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
                      row_seq, row_len, T, page_table, pt_stride, (const uint8_t*)k.data, k.scale, \
                      logits, ld, ppc)
     const bool fp4 = k.fmt == CSA_MXFP4;
-    if (rows == 8) {
-      if (fp4) CSA_ROWS(true, 8); else CSA_ROWS(false, 8);
-    } else if (rows == 4) {
-      if (fp4) CSA_ROWS(true, 4); else CSA_ROWS(false, 4);
-    } else {
-      if (fp4) CSA_ROWS(true, 2); else CSA_ROWS(false, 2);
+#define CSA_ROWS_CASE(R)                        \
+  case R:                                       \
+    if (fp4) CSA_ROWS(true, R);                 \
+    else CSA_ROWS(false, R);                    \
+    break;
+    switch (rows) {
+      CSA_ROWS_CASE(2)
+      CSA_ROWS_CASE(3)
+      CSA_ROWS_CASE(4)
+      CSA_ROWS_CASE(5)
+      CSA_ROWS_CASE(6)
+      CSA_ROWS_CASE(7)
+      default: CSA_ROWS_CASE(8)
     }
+#undef CSA_ROWS_CASE
 #undef CSA_ROWS
     return hipGetLastError();
   }

@@ -90,10 +90,11 @@ typedef enum {
  * `prep`; n in 0..255, 0 = no hint): the query rows come in consecutive groups
  * of n that share a sequence, row_seq[t] == row_seq[n * (t / n)], as the q_len
  * query tokens of each sequence in multi-token (speculative-verify) decode.
- * Results are the same with or without it. When n is a multiple of 2, 4 or 8
- * and the pool has 64-entry pages, each index-K page is read once for up to 8
- * rows of a group instead of once per row (a row whose sequence differs from
- * its group's first row is still scored correctly, from its own pages).
+ * Results are the same with or without it. When n has a divisor r in 2..8
+ * (the largest is taken) and the pool has 64-entry pages, each index-K page is
+ * read once per r rows of a group instead of once per row (a row whose
+ * sequence differs from its group's first row is still scored correctly,
+ * from its own pages).
  */
 #define CSA_ROWS_PER_SEQ(n) ((((uint32_t)(n)) & 0xFFu) << 8)
 

@@ -559,7 +559,8 @@ def test_indexer_many_rows_causal(csa, fmt):
         assert np.all(np.isnan(got[t, n:])), f"row {t} wrote past row_len"
 
 
-@pytest.mark.parametrize("fmt,q_len", [("fp8", 4), ("mxfp4", 8), ("fp8", 2), ("fp8", 6)])
+@pytest.mark.parametrize("fmt,q_len", [("fp8", 4), ("mxfp4", 8), ("fp8", 2), ("fp8", 6), ("fp8", 5),
+                                       ("mxfp4", 3), ("fp8", 10)])
 def test_indexer_rows_per_seq(csa, fmt, q_len):
     """Multi-token decode: q_len query rows per sequence (positions L-q_len ..
     L-1, causal row length min(N, (p+1)/4)) with the CSA_ROWS_PER_SEQ hint,
