@@ -247,7 +247,8 @@ csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint
  * materialised: each scan workgroup selects the top-512 candidates of its
  * chunk from the logits it holds on chip, and one final pass per row selects
  * among the candidates (exact: an entry of a row's top-512 is in its chunk's
- * top-512). Other shapes run the two calls through the workspace.
+ * top-512). Other shapes (many rows, rows grouped by CSA_ROWS_PER_SEQ, an F32
+ * pool) run the two calls through the workspace.
  *   Arguments as indexer_score and topk512_page_select; max_row_len up to
  *   2097152.
  *   ws   csa_workspace_size(CSA_OP_INDEXER_TOPK, T, max_row_len, H_I) bytes
