@@ -183,7 +183,8 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
                  const uint8_t* __restrict__ r_lat, const float* __restrict__ r_sc,
                  const uint16_t* __restrict__ r_rope, int r_ps, const int32_t* __restrict__ raw_pt,
                  int raw_pt_stride, int window, float scale, void* __restrict__ out,
-                 float* __restrict__ part, int split_len, int nsplit, int T, int nz, int g) {
+                 float* __restrict__ part, int split_len, int nsplit, int T, int nz, int g,
+                 int2* __restrict__ qsplit) {
   constexpr int kThreads = kHG * 128;
   // Two K tiles (the one being computed and the next), row-major bf16
   // [entry][576]: latent codes as exact bf16, then the RoPE dims.
@@ -194,10 +195,62 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
   __shared__ __attribute__((aligned(16))) float s_mx[kHG][2][16];  // per pair and half: a value per head
   __shared__ int32_t s_eslot[kMaxSplit];  // entry slots of this split: slot*2 + pool, -1 masked
 
-  const Coord bc = block_coord(nsplit, nz, g);
-  const int t = bc.t;
-  if (t >= T) return;
-  const int split = bc.a;
+  // Uniform splits (qsplit null): query t's list is cut into nsplit pieces of
+  // split_len entries. Balanced (qsplit set, one head block, T <= 64): the
+  // grid's nsplit workgroups are shared out in proportion to the queries'
+  // list lengths, every workgroup deriving the same assignment: a piece of
+  // `target` entries each, target = the smallest multiple of a tile that
+  // leaves at most nsplit pieces; query t owns workgroups off_t .. off_t +
+  // ceil(len_t / target) - 1, and workgroup 0 records (off_t, count) for the
+  // combine.
+  Coord bc;
+  int t, split, e_len;
+  if (qsplit) {
+    __shared__ int s_off[65];
+    __shared__ int s_len[64];
+    __shared__ int s_target;
+    if (threadIdx.x < 64) {
+      int n = 0;
+      if ((int)threadIdx.x < T) {
+        const EntryList Lq = entry_list(q_pos[threadIdx.x], k_sel, hca, ratio, window);
+        n = Lq.n1 + Lq.n2;
+      }
+      s_len[threadIdx.x] = n;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int64_t sum = 0;
+      for (int i = 0; i < T; ++i) sum += s_len[i];
+      const int64_t free_slots = nsplit - T;  // >= 1: the host sizes the grid
+      int64_t target = (sum + free_slots - 1) / free_slots;
+      target = (target + kTile - 1) / kTile * kTile;
+      target = target < kTile ? kTile : (target > kMaxSplit ? kMaxSplit : target);
+      int off = 0;
+      for (int i = 0; i < T; ++i) {
+        s_off[i] = off;
+        off += (int)((s_len[i] + target - 1) / target);
+      }
+      s_off[T] = off;
+      s_target = (int)target;
+    }
+    __syncthreads();
+    const int w = blockIdx.x;
+    if (w == 0 && (int)threadIdx.x < T)
+      qsplit[threadIdx.x] = make_int2(s_off[threadIdx.x], s_off[threadIdx.x + 1] - s_off[threadIdx.x]);
+    if (w >= s_off[T]) return;  // past the last piece (uniform across the workgroup)
+    int tq = 0;
+    while (tq + 1 < T && s_off[tq + 1] <= w) ++tq;
+    t = tq;
+    split = w - s_off[tq];
+    e_len = s_target;
+    bc = Coord{split, t, 0};
+  } else {
+    bc = block_coord(nsplit, nz, g);
+    t = bc.t;
+    if (t >= T) return;
+    split = bc.a;
+    e_len = split_len;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -208,8 +261,8 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
   const int p = q_pos[t];
   const EntryList L = entry_list(p, k_sel, hca, ratio, window);
   const int total = L.n1 + L.n2;
-  const int e_begin = split * split_len;
-  const int e_end = min(total, e_begin + split_len);
+  const int e_begin = split * e_len;
+  const int e_end = min(total, e_begin + e_len);
   const int n_split = max(0, e_end - e_begin);
 
   // Heads of this pair: hbase .. hbase+15.
@@ -426,12 +479,14 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
       }
     }
   } else {
-    // partials: [T][nsplit][H][512] O, then [T][nsplit][H] m and l (O and l
-    // are relative to m)
-    const int64_t ph = ((int64_t)t * nsplit + split) * H;
+    // partials: [slot][H][512] O, then [slot][H] m and l (O and l are
+    // relative to m); slot = t * nsplit + split (uniform) or the workgroup
+    // (balanced, nsplit slots in all)
+    const int64_t nslot = qsplit ? nsplit : (int64_t)T * nsplit;
+    const int64_t ph = (qsplit ? (int64_t)blockIdx.x : (int64_t)t * nsplit + split) * H;
     float* po = part;
-    float* pm = part + (int64_t)T * nsplit * H * kLatent;
-    float* pl = pm + (int64_t)T * nsplit * H;
+    float* pm = part + nslot * H * kLatent;
+    float* pl = pm + nslot * H;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t obase = (ph + h0 + r) * kLatent + d0;
@@ -448,22 +503,34 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
 template <bool kOutF32>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
-                    void* __restrict__ out, int g) {
+                    void* __restrict__ out, int g, const int2* __restrict__ qsplit) {
   const Coord bc = block_coord(H, 1, g);  // on the XCDs that wrote the query's partials
   const int t = bc.t, h = bc.a;
   if (t >= T) return;
-  const float* pm = part + (int64_t)T * nsplit * H * kLatent;
-  const float* pl = pm + (int64_t)T * nsplit * H;
+  // the query's slots: t * nsplit .. + nsplit (uniform) or qsplit[t] (balanced)
+  const int64_t nslot = qsplit ? nsplit : (int64_t)T * nsplit;
+  int64_t s0 = (int64_t)t * nsplit;
+  int ns = nsplit;
+  if (qsplit) {
+    const int2 q = qsplit[t];
+    s0 = q.x;
+    ns = q.y;
+  }
+  const float* pm = part + nslot * H * kLatent;
+  const float* pl = pm + nslot * H;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pm[((int64_t)t * nsplit + s) * H + h]);
+#pragma unroll 8
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[(s0 + s) * H + h]);
   float Lsum = 0.f;
   float acc0 = 0.f, acc1 = 0.f;
   const int d0 = threadIdx.x, d1 = threadIdx.x + 256;
-  for (int s = 0; s < nsplit; ++s) {
-    const int64_t idx = ((int64_t)t * nsplit + s) * H + h;
+  // branch-free, so that the loads of several slots are in flight together
+  // (an empty slot's partial is written as zeros, and its factor is 0)
+#pragma unroll 8
+  for (int s = 0; s < ns; ++s) {
+    const int64_t idx = (s0 + s) * H + h;
     const float ms = pm[idx];
-    if (ms == -INFINITY) continue;
-    const float f = __expf(ms - M);
+    const float f = ms == -INFINITY ? 0.f : __expf(ms - M);
     Lsum = fmaf(pl[idx], f, Lsum);
     acc0 = fmaf(part[idx * kLatent + d0], f, acc0);
     acc1 = fmaf(part[idx * kLatent + d1], f, acc1);
@@ -963,14 +1030,41 @@ int pick_splits(int T, int H, int max_entries) {
   return s < 1 ? 1 : s;
 }
 
+// How the split kernel divides the entry lists. Uniform: nsplit pieces of
+// split_len per query. Balanced (few queries of one head block, e.g. HCA over
+// ragged lengths, where a uniform cut leaves the longest list's pieces
+// setting the kernel's span): `slots` workgroups shared out by list length
+// inside the kernel, at least 256 and enough for pieces of at most kMaxSplit.
+struct SplitPlan {
+  bool balanced;
+  int nsplit, split_len, slots;
+  size_t part_bytes, qsplit_bytes;
+};
+SplitPlan split_plan(int T, int H, int max_entries) {
+  SplitPlan p{};
+  p.nsplit = pick_splits(T, H, max_entries);
+  const int nw = H >= 64 ? 4 : H / 16;
+  const int nz = H / (16 * nw);
+  p.balanced = p.nsplit > 1 && T <= 64 && nz == 1;
+  if (p.balanced) {
+    p.slots = std::max(256, T * ((max_entries + kMaxSplit - 1) / kMaxSplit) + T);
+    p.part_bytes = (size_t)p.slots * H * (kLatent + 2) * sizeof(float);
+    p.qsplit_bytes = (size_t)T * sizeof(int2);
+  } else {
+    p.slots = T * p.nsplit;
+    p.split_len = ((max_entries + p.nsplit - 1) / p.nsplit + kTile - 1) / kTile * kTile;
+    p.part_bytes = p.nsplit > 1 ? (size_t)T * p.nsplit * H * (kLatent + 2) * sizeof(float) : 0;
+  }
+  return p;
+}
+
 }  // namespace
 
 size_t attention_ws_bytes(int64_t T, int64_t max_entries, int H) {
   if (use_two_phase((int)T, H, (int)max_entries))
     return two_phase_ws(T, H, (int)((max_entries + kChunk - 1) / kChunk * kChunk)).total;
-  const int s = pick_splits((int)T, H, (int)max_entries);
-  if (s <= 1) return 0;
-  return (size_t)T * s * H * (kLatent + 2) * sizeof(float);
+  const SplitPlan p = split_plan((int)T, H, (int)max_entries);
+  return p.part_bytes + p.qsplit_bytes;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
@@ -1029,15 +1123,16 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 #undef CSA_PV
     return hipGetLastError();
   }
-  const int nsplit = pick_splits(a.T, a.H, max_entries);
-  int split_len = (max_entries + nsplit - 1) / nsplit;
-  split_len = ((split_len + kTile - 1) / kTile) * kTile;
+  const SplitPlan sp = split_plan(a.T, a.H, max_entries);
+  const int nsplit = sp.balanced ? sp.slots : sp.nsplit;  // the kernels' nsplit argument
+  const int split_len = sp.split_len;
   const bool f32o = a.out_fmt == CSA_F32;
-  float* part = nsplit > 1 ? (float*)a.ws : nullptr;
+  float* part = sp.nsplit > 1 ? (float*)a.ws : nullptr;
+  int2* qsplit = sp.balanced ? (int2*)((char*)a.ws + sp.part_bytes) : nullptr;
   const int nw = a.H >= 64 ? 4 : a.H / 16;  // pairs of waves per workgroup (16 heads each)
   const int nz = a.H / (16 * nw);
   const int g = xcd_group(a.T);
-  const dim3 grid = xcd_grid(nsplit, nz, a.T);
+  const dim3 grid = sp.balanced ? dim3((unsigned)sp.slots) : xcd_grid(nsplit, nz, a.T);
 #define CSA_ATTN(NW, FO)                                                                      \
   hipLaunchKernelGGL((attn_mfma_kernel<NW, FO>), grid, dim3(NW * 128), 0, s,                 \
                      (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,   \
@@ -1045,19 +1140,19 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
                      (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt,              \
                      a.comp_pt_stride, (const uint8_t*)a.raw.latent, a.raw.latent_scale,      \
                      (const uint16_t*)a.raw.rope, a.raw.page_size, a.raw_pt, a.raw_pt_stride, \
-                     a.window, a.scale, a.out, part, split_len, nsplit, a.T, nz, g)
+                     a.window, a.scale, a.out, part, split_len, nsplit, a.T, nz, g, qsplit)
   if (nw == 4) { if (f32o) CSA_ATTN(4, true); else CSA_ATTN(4, false); }
   else if (nw == 2) { if (f32o) CSA_ATTN(2, true); else CSA_ATTN(2, false); }
   else { if (f32o) CSA_ATTN(1, true); else CSA_ATTN(1, false); }
 #undef CSA_ATTN
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
+  if (e != hipSuccess || sp.nsplit == 1) return e;
   if (f32o)
     hipLaunchKernelGGL(attn_combine_kernel<true>, xcd_grid(a.H, 1, a.T), dim3(256), 0, s, part,
-                       a.T, a.H, nsplit, a.out, g);
+                       a.T, a.H, nsplit, a.out, g, qsplit);
   else
     hipLaunchKernelGGL(attn_combine_kernel<false>, xcd_grid(a.H, 1, a.T), dim3(256), 0, s, part,
-                       a.T, a.H, nsplit, a.out, g);
+                       a.T, a.H, nsplit, a.out, g, qsplit);
   return hipGetLastError();
 }
 
