@@ -372,6 +372,8 @@ def test_csa_attention(csa, H, fmt, Ls, out_f32):
 @pytest.mark.parametrize("fmt,Ls,H", [("fp8", [100, 128 * 40 + 77, 60000], 64),  # two-phase path
                                       ("fp8", [100, 128 * 40 + 77, 1048576 // 8], 64),
                                       ("fp8", [400000, 1000], 64),  # long list: many splits
+                                      # 64 ragged lists (the most the length-balanced splits take)
+                                      ("fp8", [int(500 * 1.085 ** i) for i in range(64)], 64),
                                       ("f32", [127, 128 * 9], 16)])
 def test_hca_attention(csa, fmt, Ls, H):
     g = gen.rng(1100 + H)
