@@ -504,8 +504,10 @@ template <bool kOutF32>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
                     void* __restrict__ out, int g, const int2* __restrict__ qsplit) {
-  const Coord bc = block_coord(H, 1, g);  // on the XCDs that wrote the query's partials
-  const int t = bc.t, h = bc.a;
+  // four heads per workgroup, one wave each; a lane holds 8 of the 512 dims
+  const Coord bc = block_coord(H / 4, 1, g);  // on the XCDs that wrote the query's partials
+  const int t = bc.t, h = bc.a * 4 + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (t >= T) return;
   // the query's slots: t * nsplit .. + nsplit (uniform) or qsplit[t] (balanced)
   const int64_t nslot = qsplit ? nsplit : (int64_t)T * nsplit;
@@ -522,27 +524,26 @@ attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
 #pragma unroll 8
   for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[(s0 + s) * H + h]);
   float Lsum = 0.f;
-  float acc0 = 0.f, acc1 = 0.f;
-  const int d0 = threadIdx.x, d1 = threadIdx.x + 256;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
   // branch-free, so that the loads of several slots are in flight together
   // (an empty slot's partial is written as zeros, and its factor is 0)
-#pragma unroll 8
+#pragma unroll 4
   for (int s = 0; s < ns; ++s) {
     const int64_t idx = (s0 + s) * H + h;
     const float ms = pm[idx];
     const float f = ms == -INFINITY ? 0.f : __expf(ms - M);
     Lsum = fmaf(pl[idx], f, Lsum);
-    acc0 = fmaf(part[idx * kLatent + d0], f, acc0);
-    acc1 = fmaf(part[idx * kLatent + d1], f, acc1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(part[idx * kLatent + lane + 64 * k], f, acc[k]);
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  const int64_t ob = ((int64_t)t * H + h) * kLatent;
-  if (kOutF32) {
-    reinterpret_cast<float*>(out)[ob + d0] = acc0 * inv;
-    reinterpret_cast<float*>(out)[ob + d1] = acc1 * inv;
-  } else {
-    reinterpret_cast<uint16_t*>(out)[ob + d0] = f32_to_bf16(acc0 * inv);
-    reinterpret_cast<uint16_t*>(out)[ob + d1] = f32_to_bf16(acc1 * inv);
+  const int64_t ob = ((int64_t)t * H + h) * kLatent + lane;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (kOutF32) reinterpret_cast<float*>(out)[ob + 64 * k] = acc[k] * inv;
+    else reinterpret_cast<uint16_t*>(out)[ob + 64 * k] = f32_to_bf16(acc[k] * inv);
   }
 }
 
@@ -1148,11 +1149,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.nsplit == 1) return e;
   if (f32o)
-    hipLaunchKernelGGL(attn_combine_kernel<true>, xcd_grid(a.H, 1, a.T), dim3(256), 0, s, part,
-                       a.T, a.H, nsplit, a.out, g, qsplit);
+    hipLaunchKernelGGL(attn_combine_kernel<true>, xcd_grid(a.H / 4, 1, a.T), dim3(256), 0, s,
+                       part, a.T, a.H, nsplit, a.out, g, qsplit);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<false>, xcd_grid(a.H, 1, a.T), dim3(256), 0, s, part,
-                       a.T, a.H, nsplit, a.out, g, qsplit);
+    hipLaunchKernelGGL(attn_combine_kernel<false>, xcd_grid(a.H / 4, 1, a.T), dim3(256), 0, s,
+                       part, a.T, a.H, nsplit, a.out, g, qsplit);
   return hipGetLastError();
 }
 
