@@ -170,6 +170,8 @@ void launch_mode(int th, int e, dim3 grid, hipStream_t s, const float* logits, i
   }
   if (th == 256) {
     CSA_TOPK_E(256)
+  } else if (th == 512) {
+    CSA_TOPK_E(512)
   } else {
     CSA_TOPK_E(1024)
   }
@@ -246,7 +248,9 @@ hipError_t launch_topk_cand_final(const uint32_t* ckeys, const int32_t* cjs, con
                                   const int32_t* page_table, int pt_stride, int c4_page_size,
                                   int32_t* phys_idx, int32_t* logical_idx, hipStream_t s) {
   if (R == 0) return hipSuccess;
-  const int th = (R >= 128 && ncand <= 256 * kMaxE) ? 256 : kThreads;
+  // (few rows: 512 threads; measured against 1024 for 32 rows x 4096
+  // candidates: 5.7 vs 6.0 us)
+  const int th = (R >= 128 && ncand <= 256 * kMaxE) ? 256 : (ncand <= 512 * 8 ? 512 : kThreads);
   launch_mode<kCandFinal>(th, keys_per_lane(ncand, th), dim3(1, R), s, nullptr, 0, ckeys, cjs,
                           cphys, ncand, 0, row_len, row_seq, page_table, pt_stride, c4_page_size,
                           phys_idx, logical_idx, nullptr, nullptr);
