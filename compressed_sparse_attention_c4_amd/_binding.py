@@ -107,6 +107,19 @@ def _fmt_of(t: torch.Tensor, declared: int | None = None) -> int:
     raise ValueError(f"cannot infer a csa format from {t.dtype}; pass fmt")
 
 
+def _scratch(nbytes, device, stream):
+    """A temporary workspace for one call, or None for 0 bytes. torch allocates
+    it on the current stream; when the call is enqueued on another stream the
+    allocator is told (record_stream), so that the block is not handed to
+    another tensor before that stream's kernels have finished with it."""
+    if not nbytes:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
+
+
 def _check(name, status):
     if status != CSA_OK:
         raise CsaError(name, status)
@@ -187,8 +200,7 @@ def indexer_score(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPool,
     T, H_I = w.shape
     D_I = k.dim
     if ws is None and prep & CSA_PREP_QUANT and q_used is None:
-        n = csa_workspace_size(CSA_OP_INDEXER, T, max_row_len, H_I)
-        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+        ws = _scratch(csa_workspace_size(CSA_OP_INDEXER, T, max_row_len, H_I), q.device, stream)
     _check("indexer_score", _indexer_score(
         _ptr(q), _fmt_of(q, q_fmt), _ptr(q_scale), int(prep), _ptr(w), T, H_I, D_I, _ptr(row_seq),
         _ptr(row_len), int(max_row_len), _ptr(page_table), page_table.shape[-1], k.c(),
@@ -202,8 +214,7 @@ def indexer_topk512(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPoo
     """scan_done: optional torch.cuda.Event, recorded right after the scan launch."""
     T, H_I = w.shape
     if ws is None:
-        n = csa_workspace_size(CSA_OP_INDEXER_TOPK, T, max_row_len, H_I)
-        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+        ws = _scratch(csa_workspace_size(CSA_OP_INDEXER_TOPK, T, max_row_len, H_I), q.device, stream)
     ev = None
     if scan_done is not None:
         # the handle exists after a first record; recording it here, in front
@@ -216,7 +227,7 @@ def indexer_topk512(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPoo
         _ptr(q), _fmt_of(q, q_fmt), _ptr(q_scale), int(prep), _ptr(w), T, H_I, k.dim, _ptr(row_seq),
         _ptr(row_len), int(max_row_len), _ptr(page_table), page_table.shape[-1], k.c(),
         _ptr(phys_idx), _ptr(logical_idx), _ptr(q_used), _ptr(q_used_scale), _ptr(ws),
-        ws.numel(), ev, _stream(stream)))
+        0 if ws is None else ws.numel(), ev, _stream(stream)))
 
 
 def topk512_page_select(logits, row_len, row_seq, page_table, phys_idx, logical_idx=None,
@@ -224,26 +235,24 @@ def topk512_page_select(logits, row_len, row_seq, page_table, phys_idx, logical_
     R = row_len.numel()
     ld = logits.shape[-1]
     if ws is None:
-        n = csa_workspace_size(CSA_OP_TOPK, R, ld, 1)
-        ws = torch.empty(n, dtype=torch.uint8, device=logits.device) if n else None
+        ws = _scratch(csa_workspace_size(CSA_OP_TOPK, R, ld, 1), logits.device, stream)
     _check("topk512_page_select", _topk(
         _ptr(logits), ld, R, _ptr(row_len), _ptr(row_seq), _ptr(page_table),
         page_table.shape[-1], int(c4_page_size), _ptr(phys_idx), _ptr(logical_idx), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
 
 
-def _attn_ws(op, T, entries, H, device, ws):
+def _attn_ws(op, T, entries, H, device, ws, stream):
     if ws is not None:
         return ws
-    n = csa_workspace_size(op, T, entries, H)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    return _scratch(csa_workspace_size(op, T, entries, H), device, stream)
 
 
 def csa_sparse_attn(q, q_seq, q_pos, phys_idx, c4: KvPool, raw: KvPool, raw_page_table, window,
                     softmax_scale, out, ws=None, stream=None):
     T, H = q.shape[0], q.shape[1]
     k_sel = phys_idx.shape[-1]
-    ws = _attn_ws(CSA_OP_CSA_ATTN, T, k_sel + window, H, q.device, ws)
+    ws = _attn_ws(CSA_OP_CSA_ATTN, T, k_sel + window, H, q.device, ws, stream)
     _check("csa_sparse_attn", _csa_attn(
         _ptr(q), _fmt_of(q), T, H, _ptr(q_seq), _ptr(q_pos), _ptr(phys_idx), k_sel, c4.c(), raw.c(),
         _ptr(raw_page_table), raw_page_table.shape[-1], int(window), float(softmax_scale),
@@ -253,7 +262,7 @@ def csa_sparse_attn(q, q_seq, q_pos, phys_idx, c4: KvPool, raw: KvPool, raw_page
 def hca_dense_attn(q, q_seq, q_pos, max_len, ratio, hca: KvPool, hca_page_table, raw: KvPool,
                    raw_page_table, window, softmax_scale, out, ws=None, stream=None):
     T, H = q.shape[0], q.shape[1]
-    ws = _attn_ws(CSA_OP_HCA_ATTN, T, max_len // ratio + window, H, q.device, ws)
+    ws = _attn_ws(CSA_OP_HCA_ATTN, T, max_len // ratio + window, H, q.device, ws, stream)
     _check("hca_dense_attn", _hca_attn(
         _ptr(q), _fmt_of(q), T, H, _ptr(q_seq), _ptr(q_pos), int(max_len), int(ratio), hca.c(),
         _ptr(hca_page_table), hca_page_table.shape[-1], raw.c(), _ptr(raw_page_table),

@@ -532,11 +532,9 @@ size_t indexer_ws_bytes(int64_t T, int H_I) {
 
 // Entries per scan workgroup: the rows are chunked so the grid has ~256
 // workgroups (one per CU), each wave a long stream: measured on MI355X, one
-// workgroup per CU streams faster than two (fewer concurrent page streams);
-// CSA_TUNE_INDEXER_WGS overrides the target (tuning only).
+// workgroup per CU streams faster than two (fewer concurrent page streams).
 static int64_t scan_chunk(int64_t T, int64_t max_row_len) {
-  int64_t target = 256;
-  if (const char* e = getenv("CSA_TUNE_INDEXER_WGS")) target = atoll(e) > 0 ? atoll(e) : target;
+  const int64_t target = 256;
   const int64_t total = T * max_row_len;
   int64_t chunk = total / target;
   chunk = ((chunk + kWgEntries - 1) / kWgEntries) * kWgEntries;
@@ -551,7 +549,7 @@ static int64_t scan_chunk(int64_t T, int64_t max_row_len) {
 // 2..8 (none: a prime above 8); otherwise many rows (prefill) take it with 8.
 // Only 64-entry pages.
 static int rows_kernel_rows(int64_t T, const csa_index_pool& k, uint32_t prep) {
-  if (k.page_size != 64 || getenv("CSA_TUNE_INDEXER_NO_ROWS")) return 0;
+  if (k.page_size != 64) return 0;
   const int g = (int)((prep >> 8) & 0xFFu);
   if (g >= 2) {
     for (int r = kRowsPerWG; r >= 2; --r)

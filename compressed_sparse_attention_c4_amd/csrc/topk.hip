@@ -202,9 +202,7 @@ TopkPlan topk_plan(int64_t R, int64_t ld) {
   }
   int64_t c;
   if (R >= 128) {
-    int ke = 16;
-    if (const char* v = getenv("CSA_TUNE_TOPK_KE")) ke = std::min(32, std::max(1, atoi(v)));
-    c = 256 * (int64_t)ke;
+    c = 256 * 16;  // 16 keys per lane of a 256-thread workgroup
   } else {
     const int64_t want = (128 + R - 1) / R;
     c = std::max<int64_t>((ld + want - 1) / want, 4096);

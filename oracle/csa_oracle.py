@@ -205,35 +205,61 @@ def hadamard_rotate(v: np.ndarray) -> np.ndarray:
     return y / np.sqrt(D)
 
 
-def hadamard_rotate_f32(v: np.ndarray) -> np.ndarray:
-    """The same rotation evaluated in float32 by the textbook fast Walsh-Hadamard
-    butterflies (y_e = a + b, y_{e+h} = a - b for spans h = 1, 2, 4, ..., D/2 in
-    that order), then one float32 multiply by fl32(1/sqrt(D)). Every step is a
-    correctly rounded float32 add, subtract or multiply, so this fixes the exact
-    float32 value on which a quantisation decision is taken."""
-    y = np.array(v, dtype=np.float32, copy=True)
+# ---------------------------------------------------------------------------
+# Rotary position embedding of the indexer rows ([P1] §3.1: the indexer query
+# is prepared by a fused rope -> hadamard -> quant step that takes a cos/sin
+# table (`freqs_cis`) and the token positions; §4: the index-K rows go through
+# the same rope -> hadamard -> quant before they are written to the cache)
+# ---------------------------------------------------------------------------
+
+
+def rope_cos_sin(pos, rope_dim: int, theta: float = 10000.0):
+    """(cos, sin) float64 [len(pos), rope_dim/2] of the rotary angles
+    pos * theta**(-2i/rope_dim), i = 0 .. rope_dim/2 - 1 (the textbook RoPE
+    frequencies). Reading: the pages pass a precomputed table; this is what
+    the table holds, before the caller stores it (float32) for the GPU."""
+    pos = np.asarray(pos, dtype=np.float64).reshape(-1)
+    i = np.arange(rope_dim // 2, dtype=np.float64)
+    inv = theta ** (-2.0 * i / rope_dim)
+    ang = pos[:, None] * inv[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def rope_rotate(v: np.ndarray, cos: np.ndarray, sin: np.ndarray, rope_dim: int) -> np.ndarray:
+    """Rotary embedding of the last rope_dim dims of each row, pairs (2i, 2i+1)
+    of that slice rotated by the angle whose cosine and sine are cos[..., i],
+    sin[..., i]:  x' = x cos - y sin,  y' = x sin + y cos  (float64).
+    v [..., D]; cos, sin broadcast against [..., rope_dim/2]. Readings: the
+    rotated dims are the last rope_dim of the row (the KV entry's layout puts
+    its RoPE dims last), pairs are adjacent (the complex view of freqs_cis)."""
+    y = np.array(v, dtype=np.float64, copy=True)
     D = y.shape[-1]
-    assert D & (D - 1) == 0, "Hadamard size must be a power of two"
-    h = 1
-    while h < D:
-        y = y.reshape(y.shape[:-1] + (D // (2 * h), 2, h))
-        a = y[..., 0, :].copy()
-        b = y[..., 1, :].copy()
-        y[..., 0, :] = a + b
-        y[..., 1, :] = a - b
-        y = y.reshape(y.shape[:-3] + (D,))
-        h *= 2
-    return (y * np.float32(1.0 / np.sqrt(D))).astype(np.float32)
+    r = y[..., D - rope_dim:]
+    x0 = r[..., 0::2].copy()
+    x1 = r[..., 1::2].copy()
+    c = np.asarray(cos, dtype=np.float64)
+    s_ = np.asarray(sin, dtype=np.float64)
+    r[..., 0::2] = x0 * c - x1 * s_
+    r[..., 1::2] = x0 * s_ + x1 * c
+    return y
 
 
-def index_prep(v: np.ndarray, hadamard: bool, fmt: str):
-    """Indexer row preparation ([P1] §3.1, §4): optional Hadamard rotation, then
-    quantisation to fmt ('fp8', 'mxfp4' or 'f32'). Reading: the quantised codes
-    are decided in float32, on the float32 butterfly evaluation of the rotation
-    (hadamard_rotate_f32). Returns (codes, scale) or (float32 rows, None)."""
-    x32 = np.asarray(v, dtype=np.float32)
+def index_prep(v: np.ndarray, hadamard: bool, fmt: str, rope=None):
+    """Indexer row preparation ([P1] §3.1, §4): optional RoPE, optional
+    Hadamard rotation, then quantisation to fmt ('fp8', 'mxfp4' or 'f32').
+    The rotations are evaluated exactly in float64 and the result is rounded
+    once to float32; the quantiser then takes its decisions on that float32
+    value (the stored formats carry float32 scales).
+    rope: None, or (cos, sin, rope_dim) with cos / sin broadcastable to
+    [..., rope_dim/2] (the caller's table values for each row's position).
+    Returns (codes, scale), or (float32 rows, None) for 'f32'."""
+    x = np.asarray(v, dtype=np.float64)
+    if rope is not None:
+        cos, sin, rope_dim = rope
+        x = rope_rotate(x, cos, sin, rope_dim)
     if hadamard:
-        x32 = hadamard_rotate_f32(x32)
+        x = hadamard_rotate(x)
+    x32 = x.astype(np.float32)
     if fmt == "fp8":
         return quant_fp8_rows(x32)
     if fmt == "mxfp4":

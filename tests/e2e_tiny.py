@@ -5,7 +5,10 @@ C4 compression to 1024 entries, 8 x 64 indexer, top-512 of 1024, 16 heads,
 Both sides start from the same seeded raw draws. The compressed KV is
 compared to 2e-5 relative; the logits to 1e-4 of the row max; the top-512
 sets outside the near-tie band (|logit - s_512| <= 1e-3 |s_512|) must agree;
-when the sets agree, the attention output must be within 1e-4 of the row max.
+the attention output must be within 1e-4 of each head's max, against the
+oracle's attention over the entries the GPU selected (the selection itself is
+checked against the oracle's logits above; where several selections are
+correct, the attention over the one taken must still be right).
 Used by the GPU test suite and by the smoke check.
 """
 from __future__ import annotations
@@ -69,18 +72,17 @@ def run_tiny_decode_check(csa, torch, seed_offset: int = 0) -> dict:
     band = np.abs(o_logits - s512) <= 1e-3 * abs(s512)
     outside = ~band
     assert np.array_equal(np.isin(np.arange(N), sel_o) & outside, np.isin(np.arange(N), sel_g) & outside)
-    assert len(sel_g) == 512
+    assert len(sel_g) == 512 and len(np.unique(sel_g)) == 512
     phys_ok = np.array_equal(phys.cpu().numpy()[0], logical.cpu().numpy()[0])  # identity table
     assert phys_ok
     res = {"compress_rel_err": comp_err, "logits_rel_err": lerr, "topk_equal": bool(np.array_equal(sel_o, sel_g))}
-    if res["topk_equal"]:
-        c4_rows = O.quant_kv_entries(c, "f32")
-        c4p = O.KVPool(*c4_rows, "f32")
-        rawp = O.KVPool(*O.quant_kv_entries(x, "f32"), "f32")
-        want = O.csa_attention_query(q[0], c4p.rows(sel_o), rawp.rows(O.window_positions(L - 1, wl.window)),
-                                     wl.softmax_scale)
-        got = out.cpu().numpy()[0]
-        aerr = float((np.abs(got - want).max(axis=1) / np.abs(want).max(axis=1)).max())
-        assert aerr <= 1e-4, f"attention differs ({aerr})"
-        res["attn_rel_err"] = aerr
+    # attention over the GPU's selection (identity page table: slot = entry)
+    c4p = O.KVPool(*O.quant_kv_entries(c, "f32"), "f32")
+    rawp = O.KVPool(*O.quant_kv_entries(x, "f32"), "f32")
+    want = O.csa_attention_query(q[0], c4p.rows(sel_g), rawp.rows(O.window_positions(L - 1, wl.window)),
+                                 wl.softmax_scale)
+    got = out.cpu().numpy()[0]
+    aerr = float((np.abs(got - want).max(axis=1) / np.abs(want).max(axis=1)).max())
+    assert aerr <= 1e-4, f"attention differs ({aerr})"
+    res["attn_rel_err"] = aerr
     return res

@@ -17,6 +17,7 @@ import numpy as np
 import torch
 
 from oracle import csa_oracle as O
+from tests import quant_band as Q
 from workloads import gen
 from workloads.device import _CHUNK
 
@@ -63,12 +64,21 @@ class LazyKVPool:
 
 class SeqState:
     """Oracle copy of one sequence's index-K rows, compressed KV entries and
-    raw window rows after the step, with the query inputs of one row."""
+    raw window rows after the step, with the query inputs of one row.
+
+    Besides the oracle's own quantised rows it keeps, for every index-K row
+    and query element, the value step a correct float32 evaluation of the
+    rotation may legitimately take instead (tests/quant_band.py): nonzero only
+    where the exact value lies within the evaluation band of a rounding
+    midpoint. The logit tolerance of an entry is widened by exactly what those
+    steps can change."""
 
     def __init__(self, wl, kraw, kv_fn, raw_pos0, raw_rows, q_idx, w_idx, q_attn, p, row_len):
         self.wl = wl
         codes, sc = O.index_prep(kraw, wl.hadamard, wl.index_fmt)
         self.ipool = O.IndexPool(codes, sc, wl.index_fmt)
+        self.dk = Q.band_delta(Q.exact_rotated(kraw, wl.hadamard),
+                               Q.rotation_error_bound(kraw, wl.index_dim), wl.index_fmt)
         self.c4 = LazyKVPool(kv_fn, wl.kv_fmt)
         self.raw = O.KVPool(*O.quant_kv_entries(raw_rows, wl.kv_fmt), wl.kv_fmt)
         self._raw_rows = raw_rows
@@ -83,15 +93,26 @@ class SeqState:
         m[self.raw_pos0:] = np.arange(self.p + 1 - self.raw_pos0)
         return m
 
-    def csa(self):
-        """(logits [row_len], selected logical j, out [H, 512]) of the oracle."""
+    def scores(self):
+        """(oracle logits [row_len], slack [row_len]): the slack bounds what
+        in-band codes of the query and of each index-K row can change."""
         wl = self.wl
         qc, qs = O.index_prep(self.q_idx, wl.hadamard, wl.index_fmt)
         qhat = O.index_dequant(qc, qs, wl.index_fmt)
-        return O.csa_query(qhat, self.w_idx, self.ipool, self.c4, self.raw,
-                           identity_pages(self.n_entries, 64), self.raw_map(), self.row_len, self.p,
-                           self.q_attn, wl.window, wl.softmax_scale, c4_page_size=64,
-                           raw_page_size=1)
+        n = self.row_len
+        khat = self.ipool.rows(np.arange(n))
+        logits = O.indexer_logits(qhat, self.w_idx, khat)
+        dq = Q.band_delta(Q.exact_rotated(self.q_idx, wl.hadamard),
+                          Q.rotation_error_bound(self.q_idx, wl.index_dim), wl.index_fmt)
+        return logits, Q.logit_slack(qhat, dq, self.w_idx, khat, self.dk[:n])
+
+    def attend(self, sel) -> np.ndarray:
+        """Oracle attention [H, 512] over the compressed entries `sel` (logical
+        indices) and the query's window."""
+        wl = self.wl
+        c4_rows = self.c4.rows(np.asarray(sel, dtype=np.int64))
+        win = self.raw_map()[O.window_positions(self.p, wl.window)]
+        return O.csa_attention_query(self.q_attn, c4_rows, self.raw.rows(win), wl.softmax_scale)
 
 
 def decode_raw_tail(W, b: int, stepped: bool):
@@ -210,11 +231,13 @@ def logical_of_phys(phys_row: np.ndarray, page_table_row: np.ndarray, page: int 
     return out
 
 
-def topk_agrees(o_logits: np.ndarray, got_logical: np.ndarray, k: int, tol: float):
+def topk_agrees(o_logits: np.ndarray, got_logical: np.ndarray, k: int, tol):
     """The library's selection against the oracle's logits: k distinct entries
     (or all of them when fewer), equal to the oracle's top-k except for
     entries whose logit lies within tol of the k-th largest, where either
-    choice is correct. Returns (ok, sets_equal, n_in_band)."""
+    choice is correct. tol is a scalar or per entry (then an entry is in the
+    band when |logit - s_k| <= its tol + the k-th entry's tol).
+    Returns (ok, sets_equal, n_in_band)."""
     n = len(o_logits)
     kk = min(k, n)
     sel = got_logical[got_logical >= 0]
@@ -223,8 +246,10 @@ def topk_agrees(o_logits: np.ndarray, got_logical: np.ndarray, k: int, tol: floa
     want = O.topk_logical(o_logits, n, k)
     if kk == n:
         return bool(np.array_equal(np.sort(sel), want)), True, 0
-    s_k = np.sort(o_logits)[::-1][kk - 1]
-    band = np.abs(o_logits - s_k) <= tol
+    order = np.lexsort((np.arange(n), -o_logits))
+    s_k = o_logits[order[kk - 1]]
+    tol = np.broadcast_to(np.asarray(tol, dtype=np.float64), o_logits.shape)
+    band = np.abs(o_logits - s_k) <= tol + tol[order[kk - 1]]
     a = np.zeros(n, bool)
     a[want] = True
     g = np.zeros(n, bool)

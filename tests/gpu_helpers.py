@@ -1,7 +1,5 @@
-"""Helpers shared by the GPU parity tests: moving oracle-format pools to the
-device layout and back, and the near-rounding-midpoint exclusion used when a
-quantisation decision may legitimately differ by one code between two correct
-fp32 evaluations (different summation order in the rotation / pooling)."""
+"""Helpers shared by the GPU parity tests: moving oracle-format pools (seeded
+draws quantised by the oracle) to the library's device layout."""
 from __future__ import annotations
 
 import numpy as np
@@ -47,35 +45,3 @@ def index_pool_to_device(pool: O.IndexPool, page_size: int, dim: int):
                              csa.CSA_MXFP4, dim, page_size)
     return csa.IndexPool(t_dev(pool.data.reshape(P, page_size, dim).astype(np.float32)), None,
                          csa.CSA_F32, dim, page_size)
-
-
-def fp8_codes_match(gpu_codes, ora_codes, ora_ratio, rel=1e-5):
-    """GPU and oracle e4m3 codes decode to the same value (+0 and -0 are the
-    same value), except adjacent codes where the oracle's pre-rounding value
-    (ora_ratio = v / scale in fp32, in code units up to 448) lies within
-    rel * (|midpoint| + 16) of the midpoint between them: the rounding error of
-    an fp32 sum is on the scale of its inputs, not of each output element.
-    Returns (ok, n_mismatch)."""
-    g = np.asarray(gpu_codes).astype(np.int64).ravel()
-    o = np.asarray(ora_codes).astype(np.int64).ravel()
-    r = np.asarray(ora_ratio, dtype=np.float64).ravel()
-    bad = np.flatnonzero(O.E4M3_VALUES[g] != O.E4M3_VALUES[o])
-    for i in bad:
-        a, b = O.E4M3_VALUES[g[i]], O.E4M3_VALUES[o[i]]
-        mid = (a + b) / 2
-        if abs(r[i] - mid) > rel * (abs(mid) + 16.0):
-            return False, len(bad)
-        # adjacent on the number line: no representable value strictly between
-        lo, hi = min(a, b), max(a, b)
-        fin = O.E4M3_VALUES[np.isfinite(O.E4M3_VALUES)]
-        if np.any((fin > lo) & (fin < hi)):
-            return False, len(bad)
-    return True, len(bad)
-
-
-def unpack_e2m1(packed):
-    p = np.asarray(packed, dtype=np.uint8)
-    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
-    out[..., 0::2] = p & 0xF
-    out[..., 1::2] = p >> 4
-    return out

@@ -5,10 +5,13 @@ replay), checked on sampled sequences / query rows against the oracle, which
 rebuilds those rows from the same seeded draws (tests/fullsize.py).
 
 Bars (as in the small parity tests): logits within 1e-4 of the row's largest
-|logit|; the top-512 equal to the oracle's outside the band of entries whose
-logit is within that tolerance of the 512-th largest; attention (bf16 out)
-within 2e-2 absolute where the selections are equal; the step's freshly
-compressed KV entry / index-K row checked directly.
+|logit|, plus, per entry, what the few index-K / query codes whose exact value
+lies within the float32 evaluation band of a rounding midpoint can change
+(tests/quant_band.py); the top-512 equal to the oracle's outside the band of
+entries whose logit is within that tolerance of the 512-th largest; attention
+(bf16 out) within 2e-2 absolute of the oracle's attention over the entries the
+GPU selected, on every sampled row; the step's freshly compressed KV entry /
+index-K row checked directly.
 """
 from __future__ import annotations
 
@@ -18,7 +21,7 @@ import torch
 
 from oracle import csa_oracle as O
 from tests import fullsize as F
-from tests.gpu_helpers import fp8_codes_match
+from tests import quant_band as Q
 
 pytestmark = pytest.mark.gpu
 
@@ -35,17 +38,19 @@ def csa():
 
 
 def _check_csa_row(st: F.SeqState, g_logits, g_phys, pt_row, g_out, label):
-    o_logits, o_sel, o_out = st.csa()
+    """Logits, selection and attention of one row against the oracle."""
+    o_logits, slack = st.scores()
     n = st.row_len
-    tol = LOGIT_TOL * np.abs(o_logits).max()
-    err = np.abs(g_logits[:n] - o_logits).max()
-    assert err <= tol, f"{label}: logits differ by {err} (tol {tol})"
+    tol = LOGIT_TOL * np.abs(o_logits).max() + slack
+    err = np.abs(g_logits[:n] - o_logits)
+    worst = int(np.argmax(err - tol))
+    assert np.all(err <= tol), f"{label}: logit {worst} differs by {err[worst]} (tol {tol[worst]})"
     g_log = F.logical_of_phys(g_phys, pt_row)
     ok, equal, nband = F.topk_agrees(o_logits, g_log, 512, tol)
     assert ok, f"{label}: top-512 differs outside the near-tie band ({nband} in band)"
-    if equal:
-        aerr = np.abs(g_out - o_out).max()
-        assert aerr <= ATTN_TOL, f"{label}: attention differs by {aerr}"
+    want = st.attend(g_log[g_log >= 0])
+    aerr = np.abs(g_out - want).max()
+    assert aerr <= ATTN_TOL, f"{label}: attention differs by {aerr}"
     return equal
 
 
@@ -55,22 +60,25 @@ def _check_step_writes(W, b, label):
     slot = int(O.page_slot(W.pt_host[b], N - 1, 64))
     x_new = F.host(W.x_new).reshape(W.B, 4, 576)[b]
     c = O.compress_blocks(x_new, L - 4, 4, F.host(W.gate_w), F.host(W.gate_b))
-    oc, osc, orope = O.quant_kv_entries(c, "fp8")
+    cerr = Q.compress_error_bound(x_new, F.host(W.gate_w))
     kv = W.c4_pools[0]
     lat = kv.latent.view(-1, 512)[slot].cpu().numpy()[None]
-    sc = kv.scale.view(-1)[slot].cpu().numpy()
-    np.testing.assert_allclose(sc, osc[0], rtol=3e-6, err_msg=label)
-    ok, _ = fp8_codes_match(lat, oc, c[:, :512].astype(np.float32) / osc[:, None], rel=2e-5)
-    assert ok, f"{label}: compressed latent differs"
-    rope = kv.rope.view(-1, 64)[slot].float().cpu().numpy()
-    orr = O.bf16_decode(orope[0])
-    assert np.all(np.abs(rope - orr) <= 2.0 ** -7 * np.abs(orr) + 1e-5), f"{label}: rope differs"
-    codes, scale = O.index_prep(F.host(W.k_new)[b:b + 1], W.wl.hadamard, W.wl.index_fmt)
+    sc = kv.scale.view(-1)[slot:slot + 1].cpu().numpy()
+    ok, msg, _ = Q.fp8_rows_match(lat, sc, c[:, :512], cerr[None, :512])
+    assert ok, f"{label}: compressed latent: {msg}"
+    rope = kv.rope.view(-1, 64)[slot].cpu().view(torch.int16).numpy().view(np.uint16)
+    ok, msg = Q.bf16_match(rope, c[0, 512:], cerr[512:])
+    assert ok, f"{label}: compressed RoPE dims: {msg}"
+    k = F.host(W.k_new)[b:b + 1]
+    ke, kerr = Q.exact_rotated(k, W.wl.hadamard), Q.rotation_error_bound(k, W.wl.index_dim)
     idx = W.index_pools[0]
-    g_codes = idx.data.view(-1, idx.data.shape[-1])[slot].cpu().numpy()
+    g_codes = idx.data.view(-1, idx.data.shape[-1])[slot].cpu().numpy()[None]
     g_scale = idx.scale.view(idx.data.view(-1, idx.data.shape[-1]).shape[0], -1)[slot].cpu().numpy()
-    assert np.array_equal(g_codes, codes[0]), f"{label}: index-K codes differ"
-    assert np.array_equal(g_scale.reshape(-1), np.asarray(scale[0]).reshape(-1)), f"{label}: index-K scale differs"
+    if W.wl.index_fmt == "fp8":
+        ok, msg, _ = Q.fp8_rows_match(g_codes, g_scale.view(np.float32), ke, kerr)
+    else:
+        ok, msg, _ = Q.mxfp4_rows_match(g_codes, g_scale[None], ke, kerr)
+    assert ok, f"{label}: index-K row: {msg}"
 
 
 def _scan_logits(csa, W):
@@ -114,12 +122,10 @@ def test_decode_128k_sampled(csa):
         assert torch.equal(W.out.view(torch.int16), out.view(torch.int16))
     gl = _scan_logits(csa, W)
     gp, go = phys.cpu().numpy(), out.float().cpu().numpy()
-    compared = 0
-    for b in (0, 13, 31):
+    for b in (0, 4, 9, 13, 18, 22, 27, 31):
         _check_step_writes(W, b, f"seq {b}")
         st = F.decode_seq(W, b)
-        compared += _check_csa_row(st, gl[b], gp[b], W.pt_host[b], go[b], f"seq {b}")
-    assert compared >= 1, "no sampled sequence had an unambiguous top-512"
+        _check_csa_row(st, gl[b], gp[b], W.pt_host[b], go[b], f"seq {b}")
 
 
 def test_spec_decode_128k_sampled(csa):
@@ -135,12 +141,10 @@ def test_spec_decode_128k_sampled(csa):
     torch.cuda.synchronize()
     gp, go = W.phys.cpu().numpy(), W.out.float().cpu().numpy()
     gl = _scan_logits(csa, W)
-    compared = 0
-    for t in (0, 3, 54, 127):
+    for t in (0, 3, 21, 54, 66, 91, 110, 127):
         st = F.spec_decode_row(W, t)
         b = t // wl.q_len
-        compared += _check_csa_row(st, gl[t], gp[t], W.pt_host[b], go[t], f"row {t}")
-    assert compared >= 1
+        _check_csa_row(st, gl[t], gp[t], W.pt_host[b], go[t], f"row {t}")
 
 
 def test_decode_1m_sampled(csa):
@@ -153,11 +157,11 @@ def test_decode_1m_sampled(csa):
     torch.cuda.synchronize()
     gp, go = W.phys.cpu().numpy(), W.out.float().cpu().numpy()
     gl = _scan_logits(csa, W)
-    compared = 0
-    for b in (1, 3):
+    for b in range(W.B):
+        if b in (0, 3):
+            _check_step_writes(W, b, f"seq {b}")
         st = F.decode_seq(W, b)
-        compared += _check_csa_row(st, gl[b], gp[b], W.pt_host[b], go[b], f"seq {b}")
-    assert compared >= 1
+        _check_csa_row(st, gl[b], gp[b], W.pt_host[b], go[b], f"seq {b}")
 
 
 def test_prefill_4096_on_128k_sampled(csa):
@@ -168,15 +172,13 @@ def test_prefill_4096_on_128k_sampled(csa):
     W = CsaPrefill(specs.PREFILL_4K)
     W.step(0)
     torch.cuda.synchronize()
-    compared = 0
-    for t in (0, 1709, 4095):
+    for t in (0, 1, 2, 3, 1709, 2048, 3001, 4095):
         st = F.prefill_row(W, t)
         gl = W.logits[t].cpu().numpy()
         gp, go = W.phys[t].cpu().numpy(), W.out[t].float().cpu().numpy()
-        compared += _check_csa_row(st, gl, gp, W.pt_host[0], go, f"row {t}")
+        _check_csa_row(st, gl, gp, W.pt_host[0], go, f"row {t}")
         n = st.row_len
         assert np.all(np.isfinite(gl[:n]))
-    assert compared >= 1
 
 
 def test_hca_csa_ragged_sampled(csa):
@@ -192,11 +194,10 @@ def test_hca_csa_ragged_sampled(csa):
     gp, go = W.phys.cpu().numpy(), W.out.float().cpu().numpy()
     gl = _scan_logits(csa, W)
     order = np.argsort(Wh.lens)
-    compared = 0
-    for b in (int(order[0]), int(order[7]), int(order[-1])):
+    for b in range(Wh.B):
         want = F.hca_oracle(Wh, b)
         err = np.abs(ho[b] - want).max()
         assert err <= ATTN_TOL, f"HCA seq {b} (L={Wh.lens[b]}): differs by {err}"
+    for b in (int(order[0]), int(order[3]), int(order[7]), int(order[11]), int(order[-1])):
         st = F.decode_seq(W, b)
-        compared += _check_csa_row(st, gl[b], gp[b], W.pt_host[b], go[b], f"CSA seq {b}")
-    assert compared >= 1
+        _check_csa_row(st, gl[b], gp[b], W.pt_host[b], go[b], f"CSA seq {b}")

@@ -96,7 +96,7 @@ def test_e2m1_table_matches_ocp_spec():
 
 def test_mxfp4_hand_worked_blocks():
     for ln in read_golden("mxfp4_blocks.txt"):
-        vals, sbyte, codes = [p.split() for p in ln.split("|")]
+        vals, sbyte, codes, decoded = [p.split() for p in ln.split("|")]
         v = np.zeros(32, dtype=np.float32)
         v[:4] = [float(x) for x in vals]
         packed, sc = O.quant_mxfp4_rows(v[None])
@@ -105,6 +105,59 @@ def test_mxfp4_hand_worked_blocks():
         unpacked[1::2] = packed[0] >> 4
         assert int(sc[0, 0]) == int(sbyte[0])
         assert [int(c) for c in unpacked[:4]] == [int(c) for c in codes]
+        # and back: the stored bytes decode to the hand-worked values, sign of zero included
+        deq = O.dequant_mxfp4_rows(packed, sc)[0]
+        want = np.array([float(x) for x in decoded])
+        assert np.array_equal(deq[:4], want) and np.array_equal(np.signbit(deq[:4]), np.signbit(want))
+        assert np.all(deq[4:] == 0.0)
+
+
+def test_mxfp4_decode_hand_decoded_bytes():
+    """Bytes decoded by hand from the OCP MX v1.0 definitions (fixture): fixes
+    the nibble order, the sign bit and the e8m0 bias, extremes included."""
+    for ln in read_golden("mxfp4_decode.txt"):
+        hexes, sbyte, vals = [p.split() for p in ln.split("|")]
+        n = len(hexes)
+        packed = np.zeros(16, dtype=np.uint8)
+        packed[:n] = [int(h, 16) for h in hexes]
+        deq = O.dequant_mxfp4_rows(packed[None], np.array([[int(sbyte[0])]], dtype=np.uint8))[0]
+        want = np.array([float(x) for x in vals])
+        assert np.array_equal(deq[:2 * n], want), (ln, deq[:2 * n])
+        assert np.array_equal(np.signbit(deq[:2 * n]), np.signbit(want))
+
+
+def test_mxfp4_decode_every_code_and_scale():
+    """All 16 e2m1 codes in both nibble positions, times 2^(byte - 127) for
+    e8m0 bytes across the range, against the OCP table of the fixture."""
+    table = {int(c): float(v) for c, v in (ln.split() for ln in read_golden("e2m1_codes.txt"))}
+    for byte in (0, 1, 100, 126, 127, 128, 131, 200, 253, 254):
+        for c in range(16):
+            packed = np.zeros((1, 16), dtype=np.uint8)
+            packed[0, 0] = c | ((15 - c) << 4)   # element 0 = c, element 1 = 15 - c
+            packed[0, 5] = (c << 4) | 0x1        # element 10 = 0.5, element 11 = c
+            deq = O.dequant_mxfp4_rows(packed, np.array([[byte]], dtype=np.uint8))[0]
+            sc = math.ldexp(1.0, byte - 127)
+            assert deq[0] == table[c] * sc and deq[1] == table[15 - c] * sc
+            assert deq[10] == 0.5 * sc and deq[11] == table[c] * sc
+            assert np.signbit(deq[0]) == (c >= 8)
+
+
+def test_mxfp4_roundtrip_error_bound():
+    """quant then dequant: within half a grid step of the value (the e2m1 grid
+    at scale 2^X has steps 0.5, 1, 2 below 2, 4, 6), except values beyond
+    6 * 2^X, which saturate to +-6 * 2^X."""
+    g = np.random.default_rng(31)
+    v = (g.standard_normal((400, 128)) * np.exp(g.uniform(-6, 6, (400, 1)))).astype(np.float32)
+    packed, sc = O.quant_mxfp4_rows(v)
+    deq = O.dequant_mxfp4_rows(packed, sc)
+    X = np.repeat(sc.astype(np.float64) - 127, 32, axis=1)
+    a = np.abs(v.astype(np.float64)) / np.exp2(X)
+    half = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0)) * np.exp2(X)
+    sat = a > 6
+    err = np.abs(deq - v)
+    assert np.all(err[~sat] <= half[~sat])
+    assert np.array_equal(np.abs(deq[sat]), 6 * np.exp2(X[sat]))
+    assert np.all(np.sign(deq[deq != 0]) == np.sign(v[deq != 0]))
 
 
 def test_mxfp4_brute_force_nearest_even():
@@ -151,20 +204,6 @@ def test_hadamard_equals_sylvester_matrix(D):
     assert np.array_equal(H @ H.T, D * np.eye(D))
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_hadamard_f32_butterflies_within_rounding_of_exact(D):
-    """The float32 butterfly evaluation differs from the exact rotation only by
-    float32 rounding: at most log2(D) + 1 roundings of values bounded by the
-    row's 2-norm."""
-    g = np.random.default_rng(40 + D)
-    v = g.standard_normal((500, D)).astype(np.float32)
-    exact = v.astype(np.float64) @ scipy.linalg.hadamard(D).T / math.sqrt(D)
-    got = O.hadamard_rotate_f32(v).astype(np.float64)
-    bound = (math.log2(D) + 2) * 2.0 ** -24 * np.linalg.norm(v, axis=1, keepdims=True) * math.sqrt(D)
-    assert np.all(np.abs(got - exact) <= bound)
-    assert O.hadamard_rotate_f32(v).dtype == np.float32
-
-
 def test_hadamard_preserves_scores():
     """Rotating both q and k leaves unquantised indexer logits unchanged."""
     g = np.random.default_rng(1)
@@ -174,6 +213,98 @@ def test_hadamard_preserves_scores():
     a = O.indexer_logits(q, w, k)
     b = O.indexer_logits(O.hadamard_rotate(q), w, O.hadamard_rotate(k))
     np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-9)
+
+
+def test_index_prep_rotates_exactly_then_rounds_once():
+    """index_prep with the Hadamard flag and 'f32' output is the float32
+    rounding of the exact product with scipy's Sylvester matrix (library
+    routine), and the quantised formats quantise that float32 value."""
+    g = np.random.default_rng(44)
+    v = g.standard_normal((300, 128)).astype(np.float32)
+    exact = v.astype(np.float64) @ scipy.linalg.hadamard(128).T / math.sqrt(128)
+    got, _ = O.index_prep(v, True, "f32")
+    assert got.dtype == np.float32
+    np.testing.assert_array_equal(got, exact.astype(np.float32))
+    c, s = O.index_prep(v, True, "fp8")
+    c2, s2 = O.quant_fp8_rows(exact.astype(np.float32))
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+
+
+# ---------------------------------------------------------------- RoPE ([P1] §3.1, §4)
+
+
+def _rot2(angle):
+    return np.array([[math.cos(angle), -math.sin(angle)], [math.sin(angle), math.cos(angle)]])
+
+
+def test_rope_worked_example_and_layout():
+    """One pair rotated by a quarter turn: (1, 0) -> (0, 1), (0, 1) -> (-1, 0)
+    (counter-clockwise, x' = x cos - y sin); only the last rope_dim dims move."""
+    v = np.array([[5.0, 7.0, 1.0, 0.0], [5.0, 7.0, 0.0, 1.0]])
+    out = O.rope_rotate(v, np.array([[0.0], [0.0]]), np.array([[1.0], [1.0]]), 2)
+    np.testing.assert_array_equal(out, [[5.0, 7.0, 0.0, 1.0], [5.0, 7.0, -1.0, 0.0]])
+
+
+def test_rope_frequencies_closed_form():
+    """Angle of pair i at position p is p * theta^(-2i/d): pair 0 turns by p
+    radians, the angles form a geometric sequence of ratio theta^(-2/d)."""
+    cos, sin = O.rope_cos_sin([0, 1, 3, 1000], 64, 10000.0)
+    assert np.all(cos[0] == 1.0) and np.all(sin[0] == 0.0)  # position 0: identity
+    ang = np.arctan2(sin[1], cos[1])
+    np.testing.assert_allclose(ang, 10000.0 ** (-np.arange(32) / 32), rtol=1e-13)
+    assert sin[2, 0] == math.sin(3.0) and cos[2, 0] == math.cos(3.0)
+
+
+def test_rope_matches_explicit_block_rotation_matrix():
+    """rope_rotate equals the block-diagonal matrix of 2 x 2 rotations acting
+    on the last rope_dim dims (pairs of adjacent dims)."""
+    g = np.random.default_rng(45)
+    D, rd = 128, 64
+    v = g.standard_normal((6, D))
+    pos = np.array([0, 1, 5, 4095, 131071, 1048575])
+    cos, sin = O.rope_cos_sin(pos, rd)
+    got = O.rope_rotate(v, cos, sin, rd)
+    for r, p in enumerate(pos):
+        M = np.eye(D)
+        for i in range(rd // 2):
+            a = p * 10000.0 ** (-2 * i / rd)
+            M[D - rd + 2 * i:D - rd + 2 * i + 2, D - rd + 2 * i:D - rd + 2 * i + 2] = _rot2(a)
+        np.testing.assert_allclose(got[r], M @ v[r], rtol=1e-9, atol=1e-9)
+
+
+def test_rope_norm_and_relative_position():
+    """Rotations preserve the norm, and a rotated query and key interact only
+    through their position difference: (R_m q) . (R_n k) = (R_{m-n} q) . k."""
+    g = np.random.default_rng(46)
+    q = g.standard_normal((50, 128))
+    k = g.standard_normal((50, 128))
+    m = g.integers(0, 1 << 20, 50)
+    n = g.integers(0, 1 << 20, 50)
+    cm, sm = O.rope_cos_sin(m, 64)
+    cn, sn = O.rope_cos_sin(n, 64)
+    cd, sd = O.rope_cos_sin(m - n, 64)
+    qm = O.rope_rotate(q, cm, sm, 64)
+    np.testing.assert_allclose(np.linalg.norm(qm, axis=1), np.linalg.norm(q, axis=1), rtol=1e-12)
+    lhs = (qm * O.rope_rotate(k, cn, sn, 64)).sum(1)
+    rhs = (O.rope_rotate(q, cd, sd, 64) * k).sum(1)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-7, atol=1e-7)
+
+
+def test_index_prep_order_rope_then_hadamard():
+    """[P1] §4 fixes the order rope -> hadamard -> quant: index_prep with both
+    equals H (R v) / sqrt(D), which differs from R (H v) / sqrt(D)."""
+    g = np.random.default_rng(47)
+    v = g.standard_normal((20, 128))
+    pos = g.integers(1, 5000, 20)
+    cos, sin = O.rope_cos_sin(pos, 64)
+    H = scipy.linalg.hadamard(128) / math.sqrt(128)
+    Rv = np.stack([np.concatenate([v[r, :64]] + [
+        _rot2(p * 10000.0 ** (-2 * i / 64)) @ v[r, 64 + 2 * i:66 + 2 * i] for i in range(32)])
+        for r, p in enumerate(pos)])
+    got, _ = O.index_prep(v, True, "f32", rope=(cos, sin, 64))
+    np.testing.assert_array_equal(got, (Rv @ H.T).astype(np.float32))
+    other = O.rope_rotate(v @ H.T, cos, sin, 64).astype(np.float32)
+    assert not np.allclose(got, other, atol=1e-3)
 
 
 # ---------------------------------------------------------------- compressor ([P1] §2.1, [P2])
