@@ -1,28 +1,41 @@
 #!/usr/bin/env python3
-"""Benchmark of the CSA decode step on one MI355X.
+"""Benchmark of the CSA / HCA step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Workload: CSA decode at 128K context, batch 32 (32768 compressed entries per
-sequence, paged 64 per page under a random page table over 16384 pages;
-FP8 index-K with Hadamard rotation, 64 indexer heads x 128; 64 attention
-heads; top-512 plus a 128-token window). One step = the whole hot path for one
-new token of every sequence: compress the block the token completes, append
-the token to the raw window pool, prepare its index-K row, rotate + quantise
-the indexer query, score every compressed entry, select the top 512 through
-the page table, attend. Inputs are resident in HBM before timing; three
-copies of the large pools rotate across steps so no step is served from the
-last-level cache by its predecessor.
+Headline workload: CSA decode at 128K context, batch 32 (32768 compressed
+entries per sequence, paged 64 per page under a random page table over 16384
+pages; FP8 index-K with Hadamard rotation, 64 indexer heads x 128; 64
+attention heads; top-512 plus a 128-token window). One step = the whole hot
+path for one new token of every sequence: compress the block the token
+completes, append the token to the raw window pool, prepare its index-K row,
+rotate + quantise the indexer query, score every compressed entry, select the
+top 512 through the page table, attend.
 
-Prints one JSON line. `roofline` is for the dominant kernel (the indexer scan),
-timed with HIP events on the launch stream; `cpu_baseline` is the plain CPU
-oracle timed on a bounded sample of the same step.
+Secondary lines (`secondary` in the same JSON line), each measured the same
+way and each with its own roofline and CPU-oracle baseline: the tiny fp32
+decode (latency), decode at 1M context (MXFP4 index-K), multi-token decode at
+128K, chunked prefill of 4096 tokens on 128K, the ragged HCA + CSA step, and
+the HCA cache build.
+
+Inputs are resident in HBM before timing. Enough copies of the large pools
+rotate across steps that a pool is re-read only after more than 1.5x the 256 MB
+last-level cache has been streamed, so no step is served from the cache by an
+earlier one. Steps are captured into HIP graphs and replayed.
+
+Prints one JSON line. `roofline` is for the dominant kernel of the workload
+(the indexer scan), its duration measured with HIP events on the launch stream;
+`cpu_baseline` is the plain CPU oracle timed on a bounded sample of the same
+step on this host.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -33,11 +46,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-FP8_PEAK_TFLOPS = 5000.0
-# the scan kernel of the 128K decode step (FP8 index-K, 64-entry pages, the
-# chunk top-512 selected on chip): the roofline kernel
-DECODE_128K_SCAN = "indexer_mfma_kernel<false, true, true>"
-SPIN_CYCLES = 2_000_000  # ~1 ms of GPU spin ahead of each eager timing step
+FP8_PEAK_TFLOPS = 5000.0    # dense FP8 matrix peak
+BF16_PEAK_TFLOPS = 2500.0   # dense BF16 matrix peak
+LLC_BYTES = 256 << 20       # MI355X last-level (Infinity) cache
+SPIN_CYCLES = 2_000_000     # ~1 ms of GPU spin ahead of each eager timing step
+SIMD_COUNT = 256 * 4        # SIMDs on the chip (MFMA busy normalisation)
+COPY_BYTES = 4 << 28        # bytes read (and written) by one launch of the calibration copy
+PROFILE_GAP_S = 1.0         # idle gap between setup and the profiled steps
+KERNEL_SOURCES = ("indexer.hip", "csa_device.hpp", "topk_select.hpp", "../build.py")
+
+PROFILE_CHOICES = ["tiny", "decode_128k", "decode_1m", "spec_decode", "prefill", "hca_ragged", "copy"]
 
 
 def _args():
@@ -45,19 +63,27 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--copies", type=int, default=0,
+                    help="pool copies rotated across steps (0: enough for a 1.5x LLC reuse distance)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-queries", type=int, default=32)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the 1M decode, prefill and HCA workloads")
-    ap.add_argument("--profile-only", choices=["decode_128k", "decode_1m", "spec_decode", "prefill", "hca_ragged", "copy"],
+                    help="only the headline (128K decode) workload")
+    ap.add_argument("--profile-only", choices=PROFILE_CHOICES,
                     help="run only this workload's steps (eager, for a profiler) and print nothing else; "
                          "'copy' is a plain 1 GiB device copy that calibrates the HBM byte counters")
     ap.add_argument("--counters-from", metavar="DIR",
-                    help="reduce rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv output of the decode_128k and "
-                         "copy runs under DIR into profiles/counters.json, then exit (no GPU)")
+                    help="reduce rocprofv3 --pmc csv output under DIR (FETCH_SIZE / WRITE_SIZE runs of "
+                         "the copy and the decode workloads, MFMA counters of the prefill) into "
+                         "profiles/counters.json, then exit (no GPU)")
+    ap.add_argument("--trace-from", metavar="DIR",
+                    help="reduce a rocprofv3 --kernel-trace csv under DIR into a per-step kernel table "
+                         "(printed), then exit (no GPU)")
+    ap.add_argument("--trace-steps", type=int, default=0, help="eager steps in the traced run")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------- profiles
 
 
 def kernel_source_hash(*names) -> str:
@@ -68,28 +94,23 @@ def kernel_source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel: str, src_hash: str, launches_bytes_key="bytes_per_launch"):
-    """HBM traffic per launch measured by rocprofv3 counters (FETCH_SIZE +
-    WRITE_SIZE, scaled by a plain copy kernel), if taken on this exact kernel
-    source; else None."""
+def stored_counters(kernel: str):
+    """Counter figures of `kernel` from profiles/counters.json if they were
+    taken on the current kernel source, else None."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
     e = d.get(kernel)
-    if not e or e.get("source_hash") != src_hash:
+    if not e or e.get("source_hash") != kernel_source_hash(*KERNEL_SOURCES):
         return None
-    return e.get(launches_bytes_key)
-
-
-COPY_BYTES = 4 << 28  # bytes read (and written) by one launch of the calibration copy
+    return e
 
 
 def _counter_means(csv_path, counter):
     """Mean value of `counter` per dispatch, by kernel name, from a rocprofv3
     counter_collection.csv."""
-    import csv
     tot, cnt = {}, {}
     with open(csv_path) as f:
         for r in csv.DictReader(f):
@@ -101,44 +122,115 @@ def _counter_means(csv_path, counter):
     return {k: (tot[k] / cnt[k], cnt[k]) for k in tot}
 
 
-def _find_csv(d, stem):
-    import glob
-    hits = sorted(glob.glob(os.path.join(d, "**", f"{stem}*counter_collection.csv"), recursive=True))
-    if not hits:
-        raise SystemExit(f"no {stem}*counter_collection.csv under {d}")
-    return hits[-1]
+def _find_csv(d, stem, kind="counter_collection"):
+    hits = sorted(glob.glob(os.path.join(d, "**", f"{stem}*{kind}.csv"), recursive=True))
+    return hits[-1] if hits else None
+
+
+def _one_kernel(means, name):
+    hits = [k for k in means if name in k]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one {name} in the counter run, found {hits}")
+    return means[hits[0]]
+
+
+# kernels whose HBM bytes are taken from FETCH_SIZE / WRITE_SIZE runs: stem -> kernel
+COUNTER_KERNELS = {
+    "decode128k": "indexer_mfma_kernel<false, true, true>",
+    "decode1m": "indexer_mfma_kernel<true, true, true>",
+    "prefill": "indexer_rows_kernel<false, 8>",
+}
 
 
 def reduce_counters(d):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode indexer,
-    scaled by what the same counters read for a copy of COPY_BYTES, written
-    with the hash of the kernel source they were taken on."""
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each roofline kernel,
+    scaled by what the same counters read for a copy of COPY_BYTES, and the
+    prefill indexer's MFMA counters, written with the hash of the kernel
+    source they were taken on."""
     out = {}
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if os.path.exists(path):
+        with open(path) as f:
+            out = json.load(f)
+    src = kernel_source_hash(*KERNEL_SOURCES)
     cf = _counter_means(_find_csv(d, "copy_fetch"), "FETCH_SIZE")
     cw = _counter_means(_find_csv(d, "copy_write"), "WRITE_SIZE")
     copy_k = max(cf, key=lambda k: cf[k][0])  # the copy is the largest reader in its run
     f_scale = COPY_BYTES / (cf[copy_k][0] * 1024)
     w_scale = COPY_BYTES / (cw[copy_k][0] * 1024)
-    kf = _counter_means(_find_csv(d, "decode128k_fetch"), "FETCH_SIZE")
-    kw = _counter_means(_find_csv(d, "decode128k_write"), "WRITE_SIZE")
-    name = DECODE_128K_SCAN
-    hits = [k for k in kf if name in k]
-    if len(hits) != 1:
-        raise SystemExit(f"expected one {name} in the fetch run, found {hits}")
-    k = hits[0]
-    fetch = kf[k][0] * 1024 * f_scale
-    write = kw[k][0] * 1024 * w_scale
-    out[name] = {"source_hash": kernel_source_hash("indexer.hip", "csa_device.hpp", "topk_select.hpp", "../build.py"),
-                 "bytes_per_launch": round(fetch + write),
-                 "fetch_bytes": round(fetch), "write_bytes": round(write),
-                 "fetch_kib_raw": kf[k][0], "write_kib_raw": kw[k][0], "dispatches": kf[k][1],
-                 "copy_kernel": copy_k, "copy_fetch_kib": cf[copy_k][0], "copy_write_kib": cw[copy_k][0],
-                 "fetch_scale": f_scale, "write_scale": w_scale}
-    path = os.path.join(ROOT, "profiles", "counters.json")
+    for stem, name in COUNTER_KERNELS.items():
+        ff, fw = _find_csv(d, f"{stem}_fetch"), _find_csv(d, f"{stem}_write")
+        if not ff or not fw:
+            continue
+        kf = _one_kernel(_counter_means(ff, "FETCH_SIZE"), name)
+        kw = _one_kernel(_counter_means(fw, "WRITE_SIZE"), name)
+        fetch, write = kf[0] * 1024 * f_scale, kw[0] * 1024 * w_scale
+        e = out.get(name, {}) if out.get(name, {}).get("source_hash") == src else {}
+        e.update({"source_hash": src, "bytes_per_launch": round(fetch + write),
+                  "fetch_bytes": round(fetch), "write_bytes": round(write),
+                  "fetch_kib_raw": kf[0], "write_kib_raw": kw[0], "dispatches": kf[1],
+                  "copy_kernel": copy_k, "copy_fetch_kib": cf[copy_k][0],
+                  "copy_write_kib": cw[copy_k][0], "fetch_scale": f_scale, "write_scale": w_scale})
+        out[name] = e
+    fm = _find_csv(d, "prefill_mfma")
+    if fm:
+        name = COUNTER_KERNELS["prefill"]
+        mops = _one_kernel(_counter_means(fm, "SQ_INSTS_VALU_MFMA_MOPS_F8"), name)
+        busy = _one_kernel(_counter_means(fm, "SQ_VALU_MFMA_BUSY_CYCLES"), name)
+        gui = _one_kernel(_counter_means(fm, "GRBM_GUI_ACTIVE"), name)
+        e = out.get(name, {}) if out.get(name, {}).get("source_hash") == src else {}
+        e.update({"source_hash": src, "mfma_f8_flops": mops[0] * 512,
+                  "mfma_busy_cycles": busy[0], "gui_active_cycles": gui[0],
+                  "mfma_busy_frac": busy[0] / (gui[0] * SIMD_COUNT), "mfma_dispatches": mops[1]})
+        out[name] = e
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
+
+
+def reduce_trace(d, steps):
+    """Per-step kernel table of a --profile-only run traced with
+    rocprofv3 --kernel-trace: the dispatches after the run's idle gap between
+    setup and the steps, grouped by kernel."""
+    path = _find_csv(d, "", "kernel_trace")
+    if not path:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    start = 0
+    for i in range(1, len(rows)):
+        if rows[i][0] - rows[i - 1][1] > PROFILE_GAP_S * 0.5e9:
+            start = i
+    rows = rows[start:]
+    by = {}
+    for s, e, k in rows:
+        by.setdefault(k, []).append((e - s) / 1e3)
+    print(f"# kernel                                                     per_step    avg_us    min_us    max_us   us/step")
+    tot = 0.0
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        short = k.split("(")[0].replace("void ", "").replace("csa::(anonymous namespace)::", "")
+        per = len(v) / steps if steps else float("nan")
+        us = sum(v) / steps if steps else float("nan")
+        tot += us
+        print(f"  {short:<58s} {per:8.0f} {np.mean(v):9.2f} {np.min(v):9.2f} {np.max(v):9.2f} {us:9.2f}")
+    wall = (rows[-1][1] - rows[0][0]) / 1e3 / steps if steps else float("nan")
+    print(f"# kernel time per step {tot:.1f} us; eager wall time per step {wall:.1f} us "
+          f"(the timed bench step replays a HIP graph of the same launches)")
+
+
+# ---------------------------------------------------------------- timing
+
+
+def auto_copies(bytes_per_copy: int, override: int) -> int:
+    """Pool copies so that a copy is re-read only after 1.5x the LLC has been
+    streamed from the others."""
+    if override:
+        return override
+    return max(3, math.ceil(1.5 * LLC_BYTES / max(bytes_per_copy, 1)) + 1)
 
 
 def capture_graphs(W, copies):
@@ -163,9 +255,9 @@ def capture_graphs(W, copies):
 
 
 def time_steps(W, steps, warmup, copies, graph=True):
-    """(ms per step over the timed region, mean / median indexer kernel ms).
+    """(ms per step over the timed region, mean / median roofline-kernel ms).
     The step time is taken over `steps` graph replays (or eager steps); the
-    indexer kernel's duration from HIP events recorded around its launch on
+    roofline kernel's duration from HIP events recorded around its launch on
     the launch stream during `steps` eager steps of the same work."""
     import torch
     for i in range(warmup):
@@ -200,70 +292,232 @@ def time_steps(W, steps, warmup, copies, graph=True):
         torch.cuda._sleep(SPIN_CYCLES)
         W.step(i % copies, evs[i])
     torch.cuda.synchronize()
-    idx_ms = [a.elapsed_time(b) for a, b in evs]
-    return ms, float(np.mean(idx_ms)), float(np.median(idx_ms))
+    k_ms = [a.elapsed_time(b) for a, b in evs]
+    del graphs
+    return ms, float(np.mean(k_ms)), float(np.median(k_ms))
+
+
+def hbm_roofline(kernel, nbytes, k_ms):
+    gbs = nbytes / (k_ms / 1e3) / 1e9
+    c = stored_counters(kernel)
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None if not c or "bytes_per_launch" not in c else c["bytes_per_launch"],
+            "kernel": kernel, "kernel_ms": round(k_ms, 5), "bytes_per_launch": int(nbytes)}
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+
+
+def cpu_info():
+    """Threads the oracle's numpy BLAS uses (capped by this process's CPU
+    affinity), the affinity size and the CPU model."""
+    from threadpoolctl import threadpool_info
+    aff = len(os.sched_getaffinity(0))
+    blas = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            blas = max(blas, int(info.get("num_threads", 1)))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cores": min(blas, aff), "affinity_cpus": aff, "cpu_model": model}
+
+
+def _cpu_line(n, dt, unit, sample):
+    d = {"value": round(n / dt, 3), "unit": unit, "kind": "oracle", "sample": sample + f"; {dt:.2f} s of CPU work"}
+    d.update(cpu_info())
+    return d
+
+
+def cpu_decode_rows(states, unit, what):
+    """The oracle's whole step (query preparation, indexer over every visible
+    entry in float64, top-512, attention) for each prepared row state; the
+    states (the oracle's pools, rebuilt from the seeded draws) are untimed
+    setup."""
+    t0 = time.perf_counter()
+    for st in states:
+        st.oracle_query()
+    dt = time.perf_counter() - t0
+    return _cpu_line(len(states), dt, unit, what)
+
+
+def cpu_baseline_decode(W, seqs):
+    from tests import fullsize as F
+    states = [F.decode_seq(W, b, bands=False) for b in seqs]
+    n = int(W.N[seqs[0]])
+    return cpu_decode_rows(states, "queries/s",
+                           f"{len(seqs)} of {W.B} decode queries ({n} entries x {W.wl.index_heads} index heads "
+                           f"in float64, top-512, attention over 512 + {W.wl.window} entries x {W.H} heads)")
+
+
+def cpu_baseline_spec(W, rows):
+    from tests import fullsize as F
+    states = [F.spec_decode_row(W, t, bands=False) for t in rows]
+    return cpu_decode_rows(states, "queries/s",
+                           f"{len(rows)} of {W.T} query rows of the multi-token decode (each row's indexer, "
+                           f"top-512 and attention)")
+
+
+def cpu_baseline_prefill(W, rows):
+    from tests import fullsize as F
+    states = [F.prefill_row(W, t, bands=False) for t in rows]
+    return cpu_decode_rows(states, "tokens/s",
+                           f"{len(rows)} of {W.new} query rows of the chunk, spread over it (causal "
+                           f"indexer, top-512, attention per row; the chunk's compression not timed)")
+
+
+def cpu_baseline_hca(Wh, seqs):
+    from tests import fullsize as F
+    hs = [F.hca_state(Wh, b) for b in seqs]
+    cs = [F.decode_seq(Wh.csa, b, bands=False) for b in seqs]
+    t0 = time.perf_counter()
+    for h, st in zip(hs, cs):
+        F.hca_query_of(*h)
+        st.oracle_query()
+    dt = time.perf_counter() - t0
+    return _cpu_line(len(seqs), dt, "queries/s",
+                     f"{len(seqs)} of {Wh.B} ragged sequences (HCA layer over every visible entry + "
+                     f"window, CSA layer: indexer, top-512, attention)")
+
+
+def cpu_baseline_tiny(W, reps):
+    """The tiny fp32 decode step in the oracle: indexer, top-512, attention
+    (the compressed pool is untimed setup)."""
+    from oracle import csa_oracle as O
+    from workloads import gen
+    wl = W.wl
+    g = gen.rng(wl.seed)
+    L, N = W.L, W.N
+    x = gen.normal(g, (L, 576))
+    gw, gb = gen.gate_params(g, 4)
+    kraw = gen.normal(g, (N, wl.index_dim))
+    q_idx = gen.normal(g, (1, wl.index_heads, wl.index_dim))[0]
+    w_idx = gen.uniform(g, (1, wl.index_heads))[0]
+    q = gen.normal(g, (1, wl.heads, 576))[0]
+    c4 = O.KVPool(*O.quant_kv_entries(O.compress_blocks(x, 0, 4, gw, gb), "f32"), "f32")
+    raw = O.KVPool(*O.quant_kv_entries(x, "f32"), "f32")
+    ip = O.IndexPool(kraw, None, "f32")
+    ident = np.arange(L // 256)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        O.csa_query(q_idx, w_idx, ip, c4, raw, ident, ident, N, L - 1, q, wl.window, wl.softmax_scale)
+    dt = time.perf_counter() - t0
+    return _cpu_line(reps, dt, "queries/s", f"the one decode query, {reps} times")
+
+
+# ---------------------------------------------------------------- workloads
+
+
+def line_decode(W, a, copies, roofline_kernel, cpu=None):
+    ms, k_ms, _ = time_steps(W, a.steps, a.warmup, copies, graph=not a.no_graph)
+    rows = getattr(W, "T", W.B)
+    d = {"queries_per_s": round(rows / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
+         "pool_copies": copies,
+         "roofline": hbm_roofline(roofline_kernel, W.indexer_bytes(), k_ms),
+         "step_bytes": int(W.step_bytes()),
+         "step_hbm_frac": round(W.step_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if cpu is not None and not a.no_cpu_baseline:
+        d["cpu_baseline"] = cpu(W)
+    return d
 
 
 def secondary(a):
-    """The other workloads of the method, each timed the same way (graph
-    replays for the step, HIP events around the indexer launch)."""
     import torch
-    from workloads import specs
-    from workloads.device import CsaDecode, CsaPrefill, CsaSpecDecode, HcaCsaRagged, hca_build_input
+    from workloads import gen, specs
+    from workloads.device import (CsaDecode, CsaPrefill, CsaSpecDecode, HcaCsaRagged, TinyDecode,
+                                  hca_build_input)
     import compressed_sparse_attention_c4_amd as csa
     out = {}
     steps = max(10, a.steps // 2)
+    sa = argparse.Namespace(**vars(a))
+    sa.steps = steps
+
+    # tiny all-fp32 decode: latency of one step
+    W = TinyDecode(specs.TINY_FP32_DECODE)
+    ms, k_ms, _ = time_steps(W, steps, a.warmup, 1, graph=not a.no_graph)
+    out[specs.TINY_FP32_DECODE.name] = {
+        "queries_per_s": round(1 / (ms / 1e3), 1), "latency_us": round(ms * 1e3, 2),
+        "step_bytes": W.step_bytes(),
+        "roofline": {"bound": "latency", "note": "1.8 MB per step is 0.2 us at 8 TB/s: launch and "
+                     "latency bound; the step time is the figure", "frac": None},
+        **({} if a.no_cpu_baseline else {"cpu_baseline": cpu_baseline_tiny(W, 400)})}
+    del W
+
     # decode at 1M context, batch 4, MXFP4 index-K, 128 heads
     wl = specs.DECODE_1M
-    W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
-    ms, idx_ms, _ = time_steps(W, steps, a.warmup, a.copies, graph=not a.no_graph)
-    gbs = W.indexer_bytes() / (idx_ms / 1e3) / 1e9
-    out[wl.name] = {"queries_per_s": round(W.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
-                    "indexer": {"kernel": W.indexer_kernel, "kernel_ms": round(idx_ms, 5),
-                                "bytes_per_launch": W.indexer_bytes(), "achieved_GBs": round(gbs, 1),
-                                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
-                    "step_hbm_frac": round(W.step_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    probe = int(wl.batch * (wl.seq_len // 4) * (wl.index_dim // 2 + 4))
+    copies = auto_copies(probe, a.copies)
+    W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
+    out[wl.name] = line_decode(W, sa, copies, W.indexer_kernel,
+                               lambda W: cpu_baseline_decode(W, list(range(W.B))))
     del W
     torch.cuda.empty_cache()
+
     # multi-token (speculative-verify) decode: 32 sequences x 4 query tokens at 128K
     wl = specs.SPEC_DECODE_128K
-    W = CsaSpecDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
-    ms, idx_ms, _ = time_steps(W, steps, a.warmup, a.copies, graph=not a.no_graph)
-    gbs = W.indexer_bytes() / (idx_ms / 1e3) / 1e9
-    out[wl.name] = {"queries_per_s": round(W.T / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
-                    "indexer": {"kernel": W.indexer_kernel, "kernel_ms": round(idx_ms, 5),
-                                "bytes_per_launch": W.indexer_bytes(), "achieved_GBs": round(gbs, 1),
-                                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    probe = int(wl.batch * (wl.seq_len // 4) * (wl.index_dim + 4))
+    copies = auto_copies(probe, a.copies)
+    W = CsaSpecDecode(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
+    out[wl.name] = line_decode(W, sa, copies, W.indexer_kernel,
+                               lambda W: cpu_baseline_spec(W, [0, 1, 2, 3, 40, 41, 42, 43, 124, 125, 126, 127]))
     del W
     torch.cuda.empty_cache()
+
     # chunked prefill: 4096 new tokens on a 131072-token context
     wl = specs.PREFILL_4K
     W = CsaPrefill(wl)
-    ms, idx_ms, _ = time_steps(W, max(5, steps // 4), 2, 1, graph=not a.no_graph)
-    tf = W.indexer_flops() / (idx_ms / 1e3) / 1e12
-    out[wl.name] = {"tokens_per_s": round(W.new / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
-                    "indexer_gemm": {"kernel": "indexer_rows_kernel<false, 8>", "kernel_ms": round(idx_ms, 4),
-                                     "flop_per_launch": W.indexer_flops(), "achieved_TFLOPs": round(tf, 1),
-                                     "fp8_mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}}
+    ms, k_ms, _ = time_steps(W, max(5, steps // 4), 2, 1, graph=not a.no_graph)
+    tf = W.indexer_flops() / (k_ms / 1e3) / 1e12
+    kname = "indexer_rows_kernel<false, 8>"
+    c = stored_counters(kname) or {}
+    line = {"tokens_per_s": round(W.new / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                         "traffic": c.get("bytes_per_launch"), "kernel": kname,
+                         "kernel_ms": round(k_ms, 4), "flop_per_launch": W.indexer_flops(),
+                         "counter_mfma_f8_flops": c.get("mfma_f8_flops"),
+                         "counter_mfma_busy_frac": (None if c.get("mfma_busy_frac") is None
+                                                    else round(c["mfma_busy_frac"], 4))}}
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(W, [0, 511, 1024, 1709, 2048, 2600, 3001, 3500,
+                                                        3800, 4000, 4094, 4095])
+    out[wl.name] = line
     del W
     torch.cuda.empty_cache()
+
     # HCA layer + CSA layer over 16 ragged sequences
     wl = specs.HCA_RAGGED
-    W = HcaCsaRagged(wl, copies=a.copies)
-    ms, idx_ms, _ = time_steps(W, steps, a.warmup, a.copies, graph=not a.no_graph)
+    n, lo, hi = wl.ragged
+    lens = gen.ragged_lengths(gen.rng(wl.seed), n, lo, hi)
+    per_copy = int((lens // 4).sum()) * (wl.index_dim + 4) + int((lens // wl.hca_ratio).sum()) * 644
+    copies = auto_copies(per_copy, a.copies)
+    W = HcaCsaRagged(wl, copies=copies)
+    ms, k_ms, _ = time_steps(W, steps, a.warmup, copies, graph=not a.no_graph)
     step_bytes = W.csa.step_bytes() + W.hca_bytes()
-    out[wl.name] = {"queries_per_s": round(W.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
-                    "raw_lengths": [int(x) for x in W.lens],
-                    "step_hbm_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
-    lens = W.lens
+    line = {"queries_per_s": round(W.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
+            "pool_copies": copies, "raw_lengths": [int(x) for x in W.lens],
+            "roofline": hbm_roofline(W.csa.indexer_kernel, W.csa.indexer_bytes(), k_ms),
+            "step_bytes": int(step_bytes),
+            "step_hbm_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if not a.no_cpu_baseline:
+        order = [int(b) for b in np.argsort(W.lens)]
+        line["cpu_baseline"] = cpu_baseline_hca(W, order[::2])
+    out[wl.name] = line
     del W
     torch.cuda.empty_cache()
+
     # HCA cache build (ratio 128 over every raw row)
     x, cu, st = hca_build_input(lens, wl.seed * 10 + 11)
-    from workloads import gen
     gw, gb = gen.gate_params(gen.rng(wl.seed + 3), wl.hca_ratio)
     gw, gb = torch.from_numpy(gw).cuda(), torch.from_numpy(gb).cuda()
-    hpages = [int(l) // wl.hca_ratio // 64 + 1 for l in lens]
+    hpages = [int(n) // wl.hca_ratio // 64 + 1 for n in lens]
     pool = csa.alloc_kv_pool(sum(hpages), 64, csa.CSA_FP8_E4M3)
     pt = np.zeros((len(lens), max(hpages)), np.int32)
     o = 0
@@ -283,82 +537,51 @@ def secondary(a):
     bms = e0.elapsed_time(e1) / 3
     nbytes = x.numel() * 2 + int(np.sum(np.asarray(lens) // wl.hca_ratio)) * 644
     out["hca_cache_build_r128"] = {"raw_rows": int(np.sum(lens)), "ms": round(bms, 3),
-                                   "GBs": round(nbytes / (bms / 1e3) / 1e9, 1),
-                                   "hbm_frac": round(nbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+                                   "roofline": {"bound": "hbm", "achieved": round(nbytes / (bms / 1e3) / 1e9, 1),
+                                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                "frac": round(nbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                                "traffic": None, "kernel": "compress_kernel",
+                                                "bytes_per_launch": nbytes}}
     del x, pool
     torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(W, n_queries: int):
-    """The oracle, as it stands, on n_queries of the same decode step: rotate +
-    quantise the query, score all entries, top-512 through the page table,
-    attend. The oracle's pools are quantised by the oracle from the same
-    seeded raw draws (setup, not timed)."""
+def profile_only(a):
     import torch
-    from oracle import csa_oracle as O
-    from workloads import gen
-    from workloads.device import _CHUNK
-    from threadpoolctl import threadpool_info
-
-    wl = W.wl
-    seed = wl.seed * 10
-    n_queries = min(n_queries, W.B)
-    rows_needed = {}
-    for b in range(n_queries):
-        n = int(W.N[b])
-        rows_needed[b] = O.page_slot(W.pt_host[b], np.arange(n), 64)
-    all_rows = np.unique(np.concatenate(list(rows_needed.values())))
-
-    def regen(rows, dim, seed_base):
-        out = np.empty((len(rows), dim), np.float32)
-        chunks = rows // _CHUNK
-        for c in np.unique(chunks):
-            sel = np.flatnonzero(chunks == c)
-            n = min(_CHUNK, W.P * 64 - c * _CHUNK)
-            v = gen.device_normal((n, dim), seed_base * 1000 + int(c))
-            out[sel] = v[torch.as_tensor(rows[sel] - c * _CHUNK, device="cuda")].float().cpu().numpy()
-        return out
-
-    kraw = regen(all_rows, wl.index_dim, seed + 1)
-    kvraw = regen(all_rows, 576, seed + 2)
-    codes, sc = O.index_prep(kraw, wl.hadamard, wl.index_fmt)
-    ipool_rows = {r: i for i, r in enumerate(all_rows)}
-    lat, lsc, rope = O.quant_kv_entries(kvraw, "fp8")
-    q_idx = W.q_idx[:n_queries].float().cpu().numpy()
-    w_idx = W.w_idx[:n_queries].cpu().numpy()
-    q_att = W.q_attn[:n_queries].float().cpu().numpy()
-    # window rows: regenerate the raw tail draw
-    tail = 2 * 256
-    x = gen.device_normal((int(sum(np.minimum(W.lens, tail))), 576), seed + 3).float().cpu().numpy()
-    raw_rows = O.quant_kv_entries(x, "fp8")
-    cu = np.concatenate([[0], np.cumsum(np.minimum(W.lens, tail))])
-
-    t0 = time.perf_counter()
-    for b in range(n_queries):
-        slots = rows_needed[b]
-        loc = np.array([ipool_rows[s] for s in slots])
-        n = len(slots)
-        qc, qs = O.index_prep(q_idx[b], wl.hadamard, wl.index_fmt)
-        qhat = O.index_dequant(qc, qs, wl.index_fmt)
-        khat = O.index_dequant(codes[loc], sc[loc], wl.index_fmt)
-        logits = O.indexer_logits(qhat, w_idx[b], khat)
-        sel = O.topk_logical(logits, n)
-        c4rows = O.dequant_kv_entries(lat[loc[sel]], lsc[loc[sel]], rope[loc[sel]], "fp8")
-        p = int(W.lens[b]) - 1
-        wpos = O.window_positions(p, wl.window) - (int(W.lens[b]) - min(int(W.lens[b]), tail))
-        r0 = cu[b]
-        rr = O.dequant_kv_entries(raw_rows[0][r0 + wpos], raw_rows[1][r0 + wpos], raw_rows[2][r0 + wpos], "fp8")
-        O.csa_attention_query(q_att[b], c4rows, rr, wl.softmax_scale)
-    dt = time.perf_counter() - t0
-    threads = 1
-    for info in threadpool_info():
-        if info.get("user_api") == "blas":
-            threads = max(threads, int(info.get("num_threads", 1)))
-    return {"value": n_queries / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_queries} of {W.B} decode queries at 128K (q prep, indexer over "
-                      f"{int(W.N[0])} entries x 64 heads in float64, top-512, attention); "
-                      f"{dt:.2f} s of CPU work"}
+    from workloads import specs
+    from workloads.device import CsaDecode, CsaPrefill, CsaSpecDecode, HcaCsaRagged, TinyDecode
+    copies = a.copies or 3
+    if a.profile_only == "copy":
+        n = 1 << 28  # 1 GiB of float32 read and 1 GiB written per copy
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(a.warmup + a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"profiled copy: {a.warmup + a.steps} copies of {4 * n} B", flush=True)
+        return
+    if a.profile_only == "tiny":
+        W, copies = TinyDecode(specs.TINY_FP32_DECODE), 1
+    elif a.profile_only == "decode_128k":
+        wl = specs.DECODE_128K
+        W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
+    elif a.profile_only == "decode_1m":
+        wl = specs.DECODE_1M
+        W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
+    elif a.profile_only == "spec_decode":
+        wl = specs.SPEC_DECODE_128K
+        W = CsaSpecDecode(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
+    elif a.profile_only == "prefill":
+        W, copies = CsaPrefill(specs.PREFILL_4K), 1
+    else:
+        W = HcaCsaRagged(specs.HCA_RAGGED, copies=copies)
+    torch.cuda.synchronize()
+    time.sleep(PROFILE_GAP_S)  # marks the start of the steps in a kernel trace
+    for i in range(a.warmup + a.steps):
+        W.step(i % copies)
+    torch.cuda.synchronize()
+    print(f"profiled {a.profile_only}: {a.warmup + a.steps} eager steps", flush=True)
 
 
 def main():
@@ -370,51 +593,23 @@ def main():
     if a.counters_from:
         reduce_counters(a.counters_from)
         return
+    if a.trace_from:
+        reduce_trace(a.trace_from, a.trace_steps)
+        return
     import torch
     from workloads import specs
     from workloads.device import CsaDecode
 
     torch.cuda.set_device(0)
     if a.profile_only:
-        from workloads.device import CsaPrefill, HcaCsaRagged
-        if a.profile_only == "decode_128k":
-            wl = specs.DECODE_128K
-            W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
-        elif a.profile_only == "decode_1m":
-            wl = specs.DECODE_1M
-            W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
-        elif a.profile_only == "spec_decode":
-            from workloads.device import CsaSpecDecode
-            wl = specs.SPEC_DECODE_128K
-            W = CsaSpecDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
-        elif a.profile_only == "copy":
-            n = 1 << 28  # 1 GiB of float32 read and 1 GiB written per copy
-            src = torch.ones(n, device="cuda")
-            dst = torch.empty_like(src)
-            for _ in range(a.warmup + a.steps):
-                dst.copy_(src)
-            torch.cuda.synchronize()
-            print(f"profiled copy: {a.warmup + a.steps} copies of {4 * n} B", flush=True)
-            return
-        elif a.profile_only == "prefill":
-            W = CsaPrefill(specs.PREFILL_4K)
-            a.copies = 1
-        else:
-            W = HcaCsaRagged(specs.HCA_RAGGED, copies=a.copies)
-        for i in range(a.warmup + a.steps):
-            W.step(i % a.copies)
-        torch.cuda.synchronize()
-        print(f"profiled {a.profile_only}: {a.warmup + a.steps} eager steps", flush=True)
+        profile_only(a)
         return
     wl = specs.DECODE_128K
-    W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=a.copies, pool_pages=wl.pool_pages)
-    ms, idx_ms, idx_med = time_steps(W, a.steps, a.warmup, a.copies, graph=not a.no_graph)
+    copies = auto_copies(int(wl.batch * (wl.seq_len // 4) * (wl.index_dim + 4)), a.copies)
+    W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
+    kernel = W.indexer_kernel
+    ms, k_ms, _ = time_steps(W, a.steps, a.warmup, copies, graph=not a.no_graph)
     qps = W.B / (ms / 1e3)
-    ibytes = W.indexer_bytes()
-    achieved = ibytes / (idx_ms / 1e3) / 1e9
-    src_hash = kernel_source_hash("indexer.hip", "csa_device.hpp", "topk_select.hpp", "../build.py")
-    assert W.indexer_kernel == DECODE_128K_SCAN, W.indexer_kernel
-    traffic = stored_traffic(DECODE_128K_SCAN, src_hash)
     line = {
         "metric": "CSA decode queries/s @128K ctx",
         "value": round(qps, 1),
@@ -431,16 +626,13 @@ def main():
         "config": {"workload": wl.name, "batch": W.B, "seq_len": wl.seq_len,
                    "compressed_entries": int(W.N[0]), "index_format": "fp8_e4m3+hadamard",
                    "index_heads": wl.index_heads, "attn_heads": wl.heads, "topk": 512,
-                   "window": wl.window, "pool_copies": a.copies, "hip_graph": not a.no_graph},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": DECODE_128K_SCAN,
-                     "kernel_ms": round(idx_ms, 5), "bytes_per_launch": ibytes},
+                   "window": wl.window, "pool_copies": copies, "hip_graph": not a.no_graph},
+        "roofline": hbm_roofline(kernel, W.indexer_bytes(), k_ms),
+        "step_bytes": int(W.step_bytes()),
         "step_hbm_frac": round(W.step_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
     }
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(W, a.cpu_queries)
-        line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 3)
+        line["cpu_baseline"] = cpu_baseline_decode(W, list(range(W.B)))
     del W
     torch.cuda.empty_cache()
     if not a.no_secondary:

@@ -73,12 +73,15 @@ class SeqState:
     midpoint. The logit tolerance of an entry is widened by exactly what those
     steps can change."""
 
-    def __init__(self, wl, kraw, kv_fn, raw_pos0, raw_rows, q_idx, w_idx, q_attn, p, row_len):
+    def __init__(self, wl, kraw, kv_fn, raw_pos0, raw_rows, q_idx, w_idx, q_attn, p, row_len,
+                 bands: bool = True):
         self.wl = wl
         codes, sc = O.index_prep(kraw, wl.hadamard, wl.index_fmt)
         self.ipool = O.IndexPool(codes, sc, wl.index_fmt)
-        self.dk = Q.band_delta(Q.exact_rotated(kraw, wl.hadamard),
-                               Q.rotation_error_bound(kraw, wl.index_dim), wl.index_fmt)
+        self.dk = None
+        if bands:
+            self.dk = Q.band_delta(Q.exact_rotated(kraw, wl.hadamard),
+                                   Q.rotation_error_bound(kraw, wl.index_dim), wl.index_fmt)
         self.c4 = LazyKVPool(kv_fn, wl.kv_fmt)
         self.raw = O.KVPool(*O.quant_kv_entries(raw_rows, wl.kv_fmt), wl.kv_fmt)
         self._raw_rows = raw_rows
@@ -106,6 +109,18 @@ class SeqState:
                           Q.rotation_error_bound(self.q_idx, wl.index_dim), wl.index_fmt)
         return logits, Q.logit_slack(qhat, dq, self.w_idx, khat, self.dk[:n])
 
+    def oracle_query(self):
+        """The oracle's whole step for this query row ([P1] §1 pipeline): query
+        preparation, logits of every visible entry, top-512, attention over the
+        selection and the window. (logits, selected j, out [H, 512])."""
+        wl = self.wl
+        qc, qs = O.index_prep(self.q_idx, wl.hadamard, wl.index_fmt)
+        qhat = O.index_dequant(qc, qs, wl.index_fmt)
+        return O.csa_query(qhat, self.w_idx, self.ipool, self.c4, self.raw,
+                           identity_pages(self.n_entries, 64), self.raw_map(), self.row_len, self.p,
+                           self.q_attn, wl.window, wl.softmax_scale, c4_page_size=64,
+                           raw_page_size=1)
+
     def attend(self, sel) -> np.ndarray:
         """Oracle attention [H, 512] over the compressed entries `sel` (logical
         indices) and the query's window."""
@@ -131,7 +146,7 @@ def decode_raw_tail(W, b: int, stepped: bool):
     return raw_pos0, rows
 
 
-def decode_seq(W, b: int) -> SeqState:
+def decode_seq(W, b: int, bands: bool = True) -> SeqState:
     """Sequence b of a CsaDecode after one step."""
     wl = W.wl
     L, N = int(W.lens[b]), int(W.N[b])
@@ -152,15 +167,15 @@ def decode_seq(W, b: int) -> SeqState:
 
     raw_pos0, raw_rows = decode_raw_tail(W, b, stepped=True)
     return SeqState(wl, kraw, kv_fn, raw_pos0, raw_rows, host(W.q_idx)[b], host(W.w_idx)[b],
-                    host(W.q_attn)[b], L - 1, N)
+                    host(W.q_attn)[b], L - 1, N, bands=bands)
 
 
-def spec_decode_row(W, t: int) -> SeqState:
+def spec_decode_row(W, t: int, bands: bool = True) -> SeqState:
     """Query row t of a CsaSpecDecode after one step: sequence b = t // 4 at
     position L - 4 + t % 4; the step stored the block's four rows at raw
     positions L - 4 .. L - 1 and completed block N - 1."""
     b = t // W.wl.q_len
-    st = decode_seq(W, b)
+    st = decode_seq(W, b, bands=bands)
     L = int(W.lens[b])
     x_new = host(W.x_new).reshape(W.B, 4, 576)[b]
     for i in range(3):
@@ -178,6 +193,18 @@ def hca_oracle(Wh, b: int) -> np.ndarray:
     """HCA output of sequence b of an HcaCsaRagged step: every visible HCA
     entry plus the window, which the HCA layer reads before the CSA layer
     stores the current token. float64 [H, 512]."""
+    return hca_query_of(*hca_state(Wh, b))
+
+
+def hca_query_of(pool, raw, m, L, q, wl) -> np.ndarray:
+    n = L // wl.hca_ratio
+    return O.hca_query(pool, raw, identity_pages(max(n, 1), 64), m, L - 1, wl.hca_ratio,
+                       q, wl.window, wl.softmax_scale, hca_page_size=64, raw_page_size=1)
+
+
+def hca_state(Wh, b: int):
+    """The oracle's inputs of sequence b's HCA query: (HCA pool in logical
+    order, raw window pool, raw position map, L, query, workload)."""
     wl = Wh.wl
     L = int(Wh.lens[b])
     n = L // wl.hca_ratio
@@ -188,12 +215,10 @@ def hca_oracle(Wh, b: int) -> np.ndarray:
     raw = O.KVPool(*O.quant_kv_entries(raw_rows, wl.kv_fmt), wl.kv_fmt)
     m = np.zeros(L, dtype=np.int64)
     m[raw_pos0:] = np.arange(L - raw_pos0)
-    return O.hca_query(pool, raw, identity_pages(max(n, 1), 64), m, L - 1, wl.hca_ratio,
-                       host(Wh.q_hca)[b], wl.window, wl.softmax_scale, hca_page_size=64,
-                       raw_page_size=1)
+    return pool, raw, m, L, host(Wh.q_hca)[b], wl
 
 
-def prefill_row(W, t: int) -> SeqState:
+def prefill_row(W, t: int, bands: bool = True) -> SeqState:
     """Query row t (position ctx + t) of a CsaPrefill after its step."""
     wl = W.wl
     ctx, new = W.ctx, W.new
@@ -217,7 +242,7 @@ def prefill_row(W, t: int) -> SeqState:
     xt = host(gen.device_normal((256, 576), W.seed + 3))  # positions ctx - 256 .. ctx - 1
     raw_rows = np.concatenate([xt, x_new[:t + 1]]).astype(np.float64)
     return SeqState(wl, kraw, kv_fn, ctx - 256, raw_rows, host(W.q_idx[t]), host(W.w_idx[t]),
-                    host(W.q_attn[t]), pos, n_vis)
+                    host(W.q_attn[t]), pos, n_vis, bands=bands)
 
 
 def logical_of_phys(phys_row: np.ndarray, page_table_row: np.ndarray, page: int = 64) -> np.ndarray:

@@ -153,28 +153,32 @@ class CsaDecode:
         fp4 = "true" if self.fmt == csa.CSA_MXFP4 else "false"
         return f"indexer_mfma_kernel<{fp4}, true, {'true' if fused else 'false'}>"
 
-    # algorithmic bytes of one indexer scan launch: index-K rows + prepared q
-    # + head weights + page-table rows + what it writes (the logits, or on
-    # the fused path the chunks' top-512 candidates: key, index and slot,
-    # 12 B each)
     def indexer_bytes(self) -> int:
+        """Algorithmic bytes of one indexer scan launch: what the definition
+        reads (index-K rows and scales of every visible entry, the prepared
+        queries and their scales, the head weights, the page-table rows). The
+        scan's own intermediates (the chunks' top-512 candidates on the fused
+        path) are not counted."""
         per_entry = (self.wl.index_dim + 4) if self.fmt == csa.CSA_FP8_E4M3 else (self.wl.index_dim // 2 + 4)
         n = int(self.N.sum())
         q = self.B * self.wl.index_heads * (self.q_codes.shape[-1] + 4 + 4)
-        fused, chunks = self.scan_plan()
-        out = self.B * chunks * 512 * 12 if fused else n * 4
-        return n * per_entry + q + n // C4_PAGE * 4 + out
+        return n * per_entry + q + n // C4_PAGE * 4
 
     def step_bytes(self) -> int:
-        """Algorithmic bytes of a whole step: indexer, top-k read of the logits
-        and writes of 512 indices, attention gathers (selected + window
-        entries, 644 B each) plus q and output, compress / prep writes."""
+        """Algorithmic bytes of a whole decode step: the indexer's inputs, the
+        selection written (512 slots per query), the attention's gathers
+        (selected + window entries, 644 B each) plus its q and output, and the
+        step's cache writes and query preparation (the block's 4 raw rows read,
+        the compressed entry, the token and the index-K row written; the raw
+        index q read and prepared)."""
         ent = 644
+        sel = self.B * 512 * 4
         att = self.B * (512 + self.wl.window) * ent + self.q_attn.numel() * 2 + self.out.numel() * 2
-        topk = int(self.N.sum()) * 4 + self.B * 512 * 4
-        comp = self.x_new.numel() * 2 + self.B * ent + self.B * ent  # rows read, entry + token stored
-        prep = self.k_new.numel() * 2 + self.q_idx.numel() * 2 + self.B * 132 * (1 + self.wl.index_heads)
-        return self.indexer_bytes() + topk + att + comp + prep
+        comp = self.x_new.numel() * 2 + self.B * ent + self.B * ent
+        krow = (self.wl.index_dim + 4) if self.fmt == csa.CSA_FP8_E4M3 else (self.wl.index_dim // 2 + 4)
+        prep = (self.k_new.numel() * 2 + self.q_idx.numel() * 2
+                + self.B * krow * (1 + self.wl.index_heads))
+        return self.indexer_bytes() + sel + att + comp + prep
 
     def score_only(self, c: int):
         """The indexer logits of the step's rows into self.logits (indexer_score:
@@ -263,11 +267,27 @@ class CsaSpecDecode(CsaDecode):
     def indexer_bytes(self) -> int:
         """Algorithmic bytes of the indexer launch: index-K rows of each
         sequence once (shared by its rows), the prepared queries and head
-        weights, page-table rows and the logits written."""
+        weights, page-table rows and the logits written (this kernel's output
+        is the logits, which the top-512 pass then reads)."""
         per_entry = (self.wl.index_dim + 4) if self.fmt == csa.CSA_FP8_E4M3 else (self.wl.index_dim // 2 + 4)
         n = int(self.N.sum())
         q = self.T * self.wl.index_heads * (self.wl.index_dim + 4 + 4)
         return n * per_entry + q + n // C4_PAGE * 4 + int(self.rows_len_host.sum()) * 4
+
+    def step_bytes(self) -> int:
+        """Algorithmic bytes of the multi-token step: the indexer launch (with
+        its logits), the top-512 reading those logits and writing 512 slots per
+        row, the attention's gathers, q and output per row, and the cache
+        writes and query preparation."""
+        ent = 644
+        T = self.T
+        topk = int(self.rows_len_host.sum()) * 4 + T * 512 * 4
+        att = T * (512 + self.wl.window) * ent + self.q_attn.numel() * 2 + self.out.numel() * 2
+        comp = self.x_new.numel() * 2 + self.B * ent + self.B * 4 * ent
+        krow = (self.wl.index_dim + 4) if self.fmt == csa.CSA_FP8_E4M3 else (self.wl.index_dim // 2 + 4)
+        prep = (self.k_new.numel() * 2 + self.q_idx.numel() * 2
+                + (self.B + T * self.wl.index_heads) * krow)
+        return self.indexer_bytes() + topk + att + comp + prep
 
     def score_only(self, c: int):
         """The step's indexer logits into self.logits (the same kernel as the
@@ -447,3 +467,66 @@ def hca_build_input(lens, seed: int):
         x[r0:r1] = gen.device_normal((r1 - r0, 576), seed * 1000 + i)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     return x, _i32(cu), _i32(np.zeros(len(lens)))
+
+
+class TinyDecode:
+    """The tiny all-fp32 CSA decode: batch 1, raw length 4096 compressed 4:1 to
+    1024 entries (identity page table), 8 x 64 fp32 indexer, top-512 of 1024,
+    16 heads over the 576-dim KV plus a 128-token window. The pools are built
+    once (c4_compress of the seeded raw rows; the index-K rows stored as
+    drawn); one step is the indexer, the top-512 and the attention."""
+
+    def __init__(self, wl: Workload):
+        self.wl = wl
+        g = gen.rng(wl.seed)
+        L = wl.seq_len
+        N = L // 4
+        self.B, self.L, self.N = 1, L, N
+        self.lens = np.array([L], dtype=np.int64)
+        x = gen.normal(g, (L, 576))
+        gw, gb = gen.gate_params(g, 4)
+        kraw = gen.normal(g, (N, wl.index_dim))
+        self.q_idx = torch.from_numpy(gen.normal(g, (1, wl.index_heads, wl.index_dim))).to(DEV)
+        self.w_idx = torch.from_numpy(gen.uniform(g, (1, wl.index_heads))).to(DEV)
+        self.q = torch.from_numpy(gen.normal(g, (1, wl.heads, 576))).to(DEV)
+        P = L // RAW_PAGE
+        ident = _i32(np.arange(P)[None])
+        self.pt = ident
+        self.c4 = csa.alloc_kv_pool(P, C4_PAGE, csa.CSA_F32)
+        self.raw = csa.alloc_kv_pool(P, RAW_PAGE, csa.CSA_F32)
+        xd = torch.from_numpy(x).to(DEV)
+        cu, st = _i32([0, L]), _i32([0])
+        csa.c4_compress(xd, cu, st, L, 4, torch.from_numpy(gw).to(DEV), torch.from_numpy(gb).to(DEV),
+                        ident, self.c4)
+        csa.c4_compress(xd, cu, st, L, 1, torch.zeros(576, device=DEV), torch.zeros(1, device=DEV),
+                        ident, self.raw)
+        self.kpool = csa.alloc_index_pool(P, C4_PAGE, wl.index_dim, csa.CSA_F32)
+        csa.csa_index_prep(torch.from_numpy(kraw).to(DEV), wl.index_dim, 0, csa.CSA_F32,
+                           self.kpool.data.view(-1, wl.index_dim))
+        self.row_seq = _i32([0])
+        self.row_len = _i32([N])
+        self.q_pos = _i32([L - 1])
+        self.phys = torch.empty((1, 512), dtype=torch.int32, device=DEV)
+        self.out = torch.empty((1, wl.heads, 512), dtype=torch.float32, device=DEV)
+        n = csa.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK, 1, N, wl.index_heads)
+        self.itk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        n = csa.csa_workspace_size(csa.CSA_OP_CSA_ATTN, 1, 512 + wl.window, wl.heads)
+        self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        torch.cuda.synchronize()
+
+    def step_bytes(self) -> int:
+        """Index-K rows (fp32), q and weights, selected + window entries (fp32,
+        576 dims), output."""
+        wl = self.wl
+        return (self.N * wl.index_dim * 4 + wl.index_heads * (wl.index_dim + 1) * 4
+                + (512 + wl.window) * 576 * 4 + wl.heads * (576 + 512) * 4 + 512 * 4)
+
+    def step(self, c: int = 0, ev=None):
+        wl = self.wl
+        if ev is not None:
+            ev[0].record()
+        csa.indexer_topk512(self.q_idx, self.w_idx, self.row_seq, self.row_len, self.N, self.pt,
+                            self.kpool, self.phys, ws=self.itk_ws,
+                            scan_done=None if ev is None else ev[1])
+        csa.csa_sparse_attn(self.q, self.row_seq, self.q_pos, self.phys, self.c4, self.raw, self.pt,
+                            wl.window, wl.softmax_scale, self.out, ws=self.attn_ws)
