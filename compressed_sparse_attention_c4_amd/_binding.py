@@ -27,6 +27,7 @@ def CSA_ROWS_PER_SEQ(n: int) -> int:
     return (int(n) & 0xFF) << 8
 CSA_OP_INDEXER, CSA_OP_TOPK, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN, CSA_OP_INDEXER_TOPK = range(5)
 CSA_TOPK, CSA_C4_RATIO, CSA_HCA_RATIO, CSA_RAW_PAGE, CSA_C4_PAGE = 512, 4, 128, 256, 64
+CSA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class _KvPoolC(C.Structure):
@@ -59,6 +60,9 @@ _indexer_score = _decl("indexer_score", [_vp, _i32, _vp, _u32, _vp, _i32, _i32, 
 _indexer_topk = _decl("indexer_topk512", [_vp, _i32, _vp, _u32, _vp, _i32, _i32, _i32, _vp, _vp, _i32,
                                           _vp, _i32, _IndexPoolC, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
                                           _vp])
+_indexer_topk_na = _decl("indexer_topk512_noalloc", [_vp, _i32, _vp, _u32, _vp, _i32, _i32, _i32, _vp,
+                                                     _vp, _i32, _vp, _i32, _IndexPoolC, _vp, _vp, _vp,
+                                                     _vp, _vp])
 _topk = _decl("topk512_page_select", [_vp, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
 _csa_attn = _decl("csa_sparse_attn", [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _KvPoolC, _KvPoolC,
                                       _vp, _i32, _i32, _f32, _vp, _i32, _vp, _sz, _vp])
@@ -228,6 +232,19 @@ def indexer_topk512(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPoo
         _ptr(row_len), int(max_row_len), _ptr(page_table), page_table.shape[-1], k.c(),
         _ptr(phys_idx), _ptr(logical_idx), _ptr(q_used), _ptr(q_used_scale), _ptr(ws),
         0 if ws is None else ws.numel(), ev, _stream(stream)))
+
+
+def indexer_topk512_noalloc(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPool, phys_idx,
+                            logical_idx=None, *, q_fmt=None, q_scale=None, prep=0, q_used=None,
+                            q_used_scale=None, stream=None):
+    """indexer_topk512 on the library's own device scratch (no workspace, no
+    allocation); raises CsaError (CSA_ERR_WORKSPACE) when the call needs more
+    than CSA_NOALLOC_SCRATCH_BYTES."""
+    T, H_I = w.shape
+    _check("indexer_topk512_noalloc", _indexer_topk_na(
+        _ptr(q), _fmt_of(q, q_fmt), _ptr(q_scale), int(prep), _ptr(w), T, H_I, k.dim, _ptr(row_seq),
+        _ptr(row_len), int(max_row_len), _ptr(page_table), page_table.shape[-1], k.c(),
+        _ptr(phys_idx), _ptr(logical_idx), _ptr(q_used), _ptr(q_used_scale), _stream(stream)))
 
 
 def topk512_page_select(logits, row_len, row_seq, page_table, phys_idx, logical_idx=None,

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/csa.h"
 #include "csa_internal.hpp"
@@ -204,13 +205,19 @@ csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
                                 c4_page_size, 0, phys_idx, logical_idx, ws, stream));
 }
 
-csa_status indexer_topk512(const void* q, csa_fmt q_fmt, const void* q_scale, uint32_t prep,
-                           const float* w, int32_t T, int32_t H_I, int32_t D_I,
-                           const int32_t* row_seq, const int32_t* row_len, int32_t max_row_len,
-                           const int32_t* page_table, int32_t pt_stride, csa_index_pool k,
-                           int32_t* phys_idx, int32_t* logical_idx, void* q_used,
-                           void* q_used_scale, void* ws, size_t ws_bytes, hipEvent_t scan_done,
-                           hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// indexer_topk512 with its workspace given (a caller's buffer, or the
+// library's own scratch array for indexer_topk512_noalloc).
+csa_status indexer_topk512_ws(const void* q, csa_fmt q_fmt, const void* q_scale, uint32_t prep,
+                              const float* w, int32_t T, int32_t H_I, int32_t D_I,
+                              const int32_t* row_seq, const int32_t* row_len, int32_t max_row_len,
+                              const int32_t* page_table, int32_t pt_stride, csa_index_pool k,
+                              int32_t* phys_idx, int32_t* logical_idx, void* q_used,
+                              void* q_used_scale, void* ws, size_t ws_bytes, hipEvent_t scan_done,
+                              hipStream_t stream) {
   const csa_status st = indexer_args(q_fmt, q_scale, prep, T, H_I, D_I, max_row_len, pt_stride, k,
                                      q_used, q_used_scale, ws, ws_bytes);
   if (st != CSA_OK) return st;
@@ -257,6 +264,63 @@ csa_status indexer_topk512(const void* q, csa_fmt q_fmt, const void* q_scale, ui
                       phys_idx, logical_idx, base + L.prep + L.logits, stream);
   }
   return hip_status(e);
+}
+
+// The library's own workspace for callers that cannot allocate: one array per
+// GPU in device memory, held until the process ends. Host code never uses the
+// array's name as an address (on the host it is only a stand-in): each
+// device's address comes from hipGetSymbolAddress, looked up once per device
+// with that device current, and is what the kernels receive.
+constexpr size_t kScratchBytes = CSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch array (nullptr on failure).
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status indexer_topk512(const void* q, csa_fmt q_fmt, const void* q_scale, uint32_t prep,
+                           const float* w, int32_t T, int32_t H_I, int32_t D_I,
+                           const int32_t* row_seq, const int32_t* row_len, int32_t max_row_len,
+                           const int32_t* page_table, int32_t pt_stride, csa_index_pool k,
+                           int32_t* phys_idx, int32_t* logical_idx, void* q_used,
+                           void* q_used_scale, void* ws, size_t ws_bytes, hipEvent_t scan_done,
+                           hipStream_t stream) {
+  return indexer_topk512_ws(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len, max_row_len,
+                            page_table, pt_stride, k, phys_idx, logical_idx, q_used, q_used_scale,
+                            ws, ws_bytes, scan_done, stream);
+}
+
+csa_status indexer_topk512_noalloc(const void* q, csa_fmt q_fmt, const void* q_scale,
+                                   uint32_t prep, const float* w, int32_t T, int32_t H_I,
+                                   int32_t D_I, const int32_t* row_seq, const int32_t* row_len,
+                                   int32_t max_row_len, const int32_t* page_table,
+                                   int32_t pt_stride, csa_index_pool k, int32_t* phys_idx,
+                                   int32_t* logical_idx, void* q_used, void* q_used_scale,
+                                   hipStream_t stream) {
+  if (T < 0 || max_row_len < 0 || H_I <= 0) return CSA_ERR_INVALID;
+  if (max_row_len > topk_max_len()) return CSA_ERR_UNSUPPORTED;
+  if (indexer_topk_ws_bytes(T, max_row_len, H_I) > kScratchBytes) return CSA_ERR_WORKSPACE;
+  void* ws = scratch_for_current_device();
+  if (!ws) return CSA_ERR_HIP;
+  return indexer_topk512_ws(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len, max_row_len,
+                            page_table, pt_stride, k, phys_idx, logical_idx, q_used, q_used_scale,
+                            ws, kScratchBytes, nullptr, stream);
 }
 
 static csa_status attn_common(AttnArgs& a, hipStream_t stream) {

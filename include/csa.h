@@ -15,6 +15,8 @@
  *  - Every pointer argument is DEVICE memory owned by the caller, unless the
  *    argument's comment says otherwise. The library never allocates, frees or
  *    synchronises; it only enqueues kernels on the given stream and returns.
+ *    (indexer_topk512_noalloc alone uses a fixed array of the library's own,
+ *    in device memory, instead of a caller's workspace; see there.)
  *  - All shape / format / null checks run on the host before any launch. On a
  *    failed check the call returns CSA_ERR_INVALID (or CSA_ERR_UNSUPPORTED for a
  *    well-formed but unimplemented combination) and touches no buffer.
@@ -24,8 +26,9 @@
  *    cannot be checked on the host: a page id outside [0, num_pages), a length
  *    beyond the row's capacity or a position beyond the pool is a breach of
  *    the caller's contract and its result is undefined.
- *  - The library holds no mutable global state: calls on different streams are
- *    independent and every call can be captured into a HIP graph.
+ *  - Apart from that array, the library holds no mutable global state: calls on
+ *    different streams are independent and every call can be captured into a
+ *    HIP graph.
  *
  * KV entry (one compressed or raw token), 576 dims = 512 latent + 64 RoPE
  * ([P2] "低精度與儲存策略的配合": most KV dims in FP8, RoPE dims in BF16):
@@ -264,6 +267,33 @@ csa_status indexer_topk512(const void* q, csa_fmt q_fmt, const void* q_scale, ui
                            int32_t* phys_idx, int32_t* logical_idx, void* q_used,
                            void* q_used_scale, void* ws, size_t ws_bytes, hipEvent_t scan_done,
                            hipStream_t stream);
+
+/*
+ * indexer_topk512_noalloc -- indexer_topk512 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments and results, without `ws` and
+ * `scan_done`. The workspace is the library's own array in device memory,
+ * CSA_NOALLOC_SCRATCH_BYTES per GPU, which the library holds until the process
+ * ends; the call itself allocates and frees nothing.
+ *   Limit: calls whose workspace, csa_workspace_size(CSA_OP_INDEXER_TOPK, T,
+ *   max_row_len, H_I), exceeds CSA_NOALLOC_SCRATCH_BYTES return
+ *   CSA_ERR_WORKSPACE and launch nothing (decode shapes fit: 32 rows x 128K,
+ *   4 rows x 1M, 128 multi-token rows x 128K; a 4096-row prefill does not).
+ *   Every call on one GPU uses that GPU's single array, so calls that overlap
+ *   on one GPU (different streams, or different host threads without ordering)
+ *   race on it and their results are undefined; calls ordered on one stream
+ *   are fine. `stream` must belong to the current device. The array keeps the
+ *   last call's contents; nothing in it needs to start cleared.
+ *   Returns CSA_ERR_HIP if the array's device address cannot be looked up.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+csa_status indexer_topk512_noalloc(const void* q, csa_fmt q_fmt, const void* q_scale,
+                                   uint32_t prep, const float* w, int32_t T, int32_t H_I,
+                                   int32_t D_I, const int32_t* row_seq, const int32_t* row_len,
+                                   int32_t max_row_len, const int32_t* page_table,
+                                   int32_t pt_stride, csa_index_pool k, int32_t* phys_idx,
+                                   int32_t* logical_idx, void* q_used, void* q_used_scale,
+                                   hipStream_t stream);
 
 /*
  * topk512_page_select -- the fixed top-512 transform ([P1] §3.2): per row, the

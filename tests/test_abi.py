@@ -192,3 +192,20 @@ def test_topk_and_attention_reject_bad_arguments(lib):
     assert a(FAKE, 1, 2, 48, FAKE, FAKE, FAKE, 512, fp8, raw, FAKE, 4, 128, 0.04, FAKE, 1, FAKE, 1 << 30, None) == UNSUPPORTED
     # two queries over 640 entries are split over several workgroups: needs a workspace
     assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 512, fp8, raw, FAKE, 4, 128, 0.04, FAKE, 1, None, 0, None) == WORKSPACE
+
+
+def test_noalloc_refuses_oversized_and_bad_sizes(lib):
+    """indexer_topk512_noalloc checks its sizes against its fixed scratch on
+    the host before touching the GPU: too large a call is CSA_ERR_WORKSPACE,
+    negative sizes CSA_ERR_INVALID."""
+    f = lib.indexer_topk512_noalloc
+    f.restype = C.c_int
+    f.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_uint32, C.c_void_p, C.c_int32, C.c_int32,
+                  C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, IndexPoolC,
+                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+    pool = IndexPoolC(FAKE, FAKE, 2, 128, 64, 1000)
+    args = lambda T, n: (FAKE, 2, FAKE, 0, FAKE, T, 64, 128, FAKE, FAKE, n, FAKE, 600, pool, FAKE,
+                         None, None, None, None)
+    assert f(*args(4096, 33792)) == WORKSPACE
+    assert f(*args(-1, 1000)) == INVALID
+    assert f(*args(4, -5)) == INVALID
