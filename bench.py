@@ -212,7 +212,8 @@ def reduce_trace(d, steps):
     print(f"# kernel                                                     per_step    avg_us    min_us    max_us   us/step")
     tot = 0.0
     for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
-        short = k.split("(")[0].replace("void ", "").replace("csa::(anonymous namespace)::", "")
+        short = k.replace("(anonymous namespace)::", "").replace("csa::", "").replace("void ", "")
+        short = short.split("(")[0]
         per = len(v) / steps if steps else float("nan")
         us = sum(v) / steps if steps else float("nan")
         tot += us

@@ -25,7 +25,8 @@ CSA_PREP_HADAMARD, CSA_PREP_QUANT = 1, 2
 def CSA_ROWS_PER_SEQ(n: int) -> int:
     """The rows-per-sequence hint bits of an indexer call's `prep` flags."""
     return (int(n) & 0xFF) << 8
-CSA_OP_INDEXER, CSA_OP_TOPK, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN, CSA_OP_INDEXER_TOPK = range(5)
+(CSA_OP_INDEXER, CSA_OP_TOPK, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN, CSA_OP_INDEXER_TOPK,
+ CSA_OP_CSA_ATTN_F32, CSA_OP_HCA_ATTN_F32) = range(7)
 CSA_TOPK, CSA_C4_RATIO, CSA_HCA_RATIO, CSA_RAW_PAGE, CSA_C4_PAGE = 512, 4, 128, 256, 64
 CSA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -269,7 +270,8 @@ def csa_sparse_attn(q, q_seq, q_pos, phys_idx, c4: KvPool, raw: KvPool, raw_page
                     softmax_scale, out, ws=None, stream=None):
     T, H = q.shape[0], q.shape[1]
     k_sel = phys_idx.shape[-1]
-    ws = _attn_ws(CSA_OP_CSA_ATTN, T, k_sel + window, H, q.device, ws, stream)
+    op = CSA_OP_CSA_ATTN_F32 if c4.fmt == CSA_F32 else CSA_OP_CSA_ATTN
+    ws = _attn_ws(op, T, k_sel + window, H, q.device, ws, stream)
     _check("csa_sparse_attn", _csa_attn(
         _ptr(q), _fmt_of(q), T, H, _ptr(q_seq), _ptr(q_pos), _ptr(phys_idx), k_sel, c4.c(), raw.c(),
         _ptr(raw_page_table), raw_page_table.shape[-1], int(window), float(softmax_scale),
@@ -279,7 +281,8 @@ def csa_sparse_attn(q, q_seq, q_pos, phys_idx, c4: KvPool, raw: KvPool, raw_page
 def hca_dense_attn(q, q_seq, q_pos, max_len, ratio, hca: KvPool, hca_page_table, raw: KvPool,
                    raw_page_table, window, softmax_scale, out, ws=None, stream=None):
     T, H = q.shape[0], q.shape[1]
-    ws = _attn_ws(CSA_OP_HCA_ATTN, T, max_len // ratio + window, H, q.device, ws, stream)
+    op = CSA_OP_HCA_ATTN_F32 if hca.fmt == CSA_F32 else CSA_OP_HCA_ATTN
+    ws = _attn_ws(op, T, max_len // ratio + window, H, q.device, ws, stream)
     _check("hca_dense_attn", _hca_attn(
         _ptr(q), _fmt_of(q), T, H, _ptr(q_seq), _ptr(q_pos), int(max_len), int(ratio), hca.c(),
         _ptr(hca_page_table), hca_page_table.shape[-1], raw.c(), _ptr(raw_page_table),

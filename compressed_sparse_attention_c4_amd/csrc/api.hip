@@ -107,6 +107,8 @@ size_t csa_workspace_size(int32_t op, int64_t rows, int64_t max_len, int32_t hea
     case CSA_OP_TOPK: return topk_ws_bytes(rows, max_len);  // max_len = ld
     case CSA_OP_CSA_ATTN:
     case CSA_OP_HCA_ATTN: return attention_ws_bytes(rows, max_len, heads);
+    case CSA_OP_CSA_ATTN_F32:
+    case CSA_OP_HCA_ATTN_F32: return attention_f32_ws_bytes(rows, max_len, heads);
     case CSA_OP_INDEXER_TOPK: return indexer_topk_ws_bytes(rows, max_len, heads);
     default: return 0;
   }
@@ -329,7 +331,9 @@ static csa_status attn_common(AttnArgs& a, hipStream_t stream) {
   if (a.raw_pt_stride <= 0) return CSA_ERR_INVALID;
   if (a.comp.fmt == CSA_F32) {
     if (a.q_fmt != CSA_F32 || a.out_fmt != CSA_F32) return CSA_ERR_INVALID;
-    if ((size_t)(a.max_comp + a.window) * 4 + 576 * 4 > 150 * 1024) return CSA_ERR_UNSUPPORTED;
+    if ((int64_t)a.max_comp + a.window > 32768) return CSA_ERR_UNSUPPORTED;
+    const size_t need = attention_f32_ws_bytes(a.T, a.max_comp + a.window, a.H);
+    if (need > a.ws_bytes || (need > 0 && !a.ws)) return CSA_ERR_WORKSPACE;
   } else {
     if (a.q_fmt != CSA_BF16) return CSA_ERR_INVALID;
     if (a.out_fmt != CSA_BF16 && a.out_fmt != CSA_F32) return CSA_ERR_INVALID;

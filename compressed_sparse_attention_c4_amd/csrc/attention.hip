@@ -950,73 +950,226 @@ TwoPhaseWs two_phase_ws(int64_t T, int H, int e_pad) {
   return w;
 }
 
-// fp32 pools and queries (small configurations): one workgroup per (query,
-// head); scores in LDS, exact two-pass softmax, then the value sum.
+// fp32 pools and queries (small configurations). A query's entry list is cut
+// into 32-entry chunks; a workgroup stages one chunk (576 floats per entry,
+// read as coalesced 16-byte loads) and the query rows of up to 16 heads in
+// LDS, scores the chunk, takes each head's max and exponent sum over it and
+// the partial P V. attn_f32_combine_kernel merges the chunks of a (query,
+// head) exactly (each partial rescaled by exp(m_c - M)); with a single chunk
+// the first kernel writes the output itself. An empty list gives zeros.
+constexpr int kF32Chunk = 32;  // entries per workgroup
+constexpr int kF32Heads = 16;  // heads per workgroup
+constexpr int kF32Row = kKvDim + 4;  // LDS row stride (floats)
+
 __global__ void __launch_bounds__(256)
-attn_f32_kernel(const float* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
-                const int32_t* __restrict__ q_pos, bool hca, const int32_t* __restrict__ phys_idx,
-                int k_sel, int ratio, csa_kv_pool comp, const int32_t* __restrict__ comp_pt,
-                int comp_pt_stride, csa_kv_pool raw, const int32_t* __restrict__ raw_pt,
-                int raw_pt_stride, int window, float scale, float* __restrict__ out) {
-  extern __shared__ float sh[];  // q[576], then scores[total], then red[8]
-  const int t = blockIdx.y, h = blockIdx.x;
+attn_f32_chunk_kernel(const float* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
+                      const int32_t* __restrict__ q_pos, bool hca,
+                      const int32_t* __restrict__ phys_idx, int k_sel, int ratio, csa_kv_pool comp,
+                      const int32_t* __restrict__ comp_pt, int comp_pt_stride, csa_kv_pool raw,
+                      const int32_t* __restrict__ raw_pt, int raw_pt_stride, int window,
+                      float scale, float* __restrict__ out, float* __restrict__ part, int nchunk) {
+  __shared__ __attribute__((aligned(16))) float s_kv[kF32Chunk * kF32Row];
+  __shared__ __attribute__((aligned(16))) float s_q[kF32Heads * kF32Row];
+  __shared__ float s_p[kF32Chunk][kF32Heads + 1];
+  __shared__ float s_m[kF32Heads], s_l[kF32Heads];
+  __shared__ int64_t s_slot[kF32Chunk];
+  __shared__ int s_pool[kF32Chunk];
+  const int c = blockIdx.x, t = blockIdx.z;
+  const int h0 = blockIdx.y * kF32Heads;
+  const int nh = min(kF32Heads, H - h0);
+  const int tid = threadIdx.x;
   const int seq = q_seq[t], p = q_pos[t];
   const EntryList L = entry_list(p, k_sel, hca, ratio, window);
   const int total = L.n1 + L.n2;
-  float* sq = sh;
-  float* ss = sh + kKvDim;
-  float* red = ss + total;
-  for (int i = threadIdx.x; i < kKvDim; i += blockDim.x) sq[i] = q[((int64_t)t * H + h) * kKvDim + i];
-  __syncthreads();
-  float lmax = -INFINITY;
-  for (int i = threadIdx.x; i < total; i += blockDim.x) {
-    int pool;
-    const int64_t slot = entry_slot(i, L, t, seq, hca, phys_idx, k_sel, comp_pt, comp_pt_stride,
-                                    comp.page_size, raw_pt, raw_pt_stride, raw.page_size, pool);
-    float s = -INFINITY;
-    if (slot >= 0) {
-      const csa_kv_pool& P = pool ? raw : comp;
-      const float* lat = (const float*)P.latent + slot * kLatent;
-      const float* rp = (const float*)P.rope + slot * kRope;
-      float d = 0.f;
-      for (int k = 0; k < kLatent; ++k) d = fmaf(sq[k], lat[k], d);
-      for (int k = 0; k < kRope; ++k) d = fmaf(sq[kLatent + k], rp[k], d);
-      s = d * scale;
+  const int e0 = c * kF32Chunk;
+  if (tid < kF32Chunk) {
+    int pool = 0;
+    int64_t slot = -1;
+    if (e0 + tid < total)
+      slot = entry_slot(e0 + tid, L, t, seq, hca, phys_idx, k_sel, comp_pt, comp_pt_stride,
+                        comp.page_size, raw_pt, raw_pt_stride, raw.page_size, pool);
+    s_slot[tid] = slot;
+    s_pool[tid] = pool;
+  }
+  // query rows of this workgroup's heads (rows past nh are zero): all of a
+  // thread's loads are issued before any is stored, so they overlap
+  constexpr int kQv = kF32Heads * (kKvDim / 4) / 256;  // float4 per thread
+  {
+    float4 v[kQv];
+#pragma unroll
+    for (int r = 0; r < kQv; ++r) {
+      const int i = tid + 256 * r, h = i / (kKvDim / 4), f = i % (kKvDim / 4);
+      v[r] = h < nh ? reinterpret_cast<const float4*>(q + ((int64_t)t * H + h0 + h) * kKvDim)[f]
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    ss[i] = s;
-    lmax = fmaxf(lmax, s);
-  }
-  lmax = wave_max(lmax);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = lmax;
-  __syncthreads();
-  float M = -INFINITY;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) M = fmaxf(M, red[i]);
-  __syncthreads();
-  float lsum = 0.f;
-  for (int i = threadIdx.x; i < total; i += blockDim.x) {
-    const float e = ss[i] == -INFINITY ? 0.f : expf(ss[i] - M);
-    ss[i] = e;
-    lsum += e;
-  }
-  lsum = wave_sum(lsum);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = lsum;
-  __syncthreads();
-  float S = 0.f;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) S += red[i];
-  const float inv = 1.f / S;
-  for (int d = threadIdx.x; d < kLatent; d += blockDim.x) {
-    float acc = 0.f;
-    for (int i = 0; i < total; ++i) {
-      const float pe = ss[i];
-      if (pe == 0.f) continue;
-      int pool;
-      const int64_t slot = entry_slot(i, L, t, seq, hca, phys_idx, k_sel, comp_pt, comp_pt_stride,
-                                      comp.page_size, raw_pt, raw_pt_stride, raw.page_size, pool);
-      const csa_kv_pool& P = pool ? raw : comp;
-      acc = fmaf(pe, ((const float*)P.latent)[slot * kLatent + d], acc);
+#pragma unroll
+    for (int r = 0; r < kQv; ++r) {
+      const int i = tid + 256 * r, h = i / (kKvDim / 4), f = i % (kKvDim / 4);
+      *reinterpret_cast<float4*>(&s_q[h * kF32Row + 4 * f]) = v[r];
     }
-    out[((int64_t)t * H + h) * kLatent + d] = acc * inv;
   }
+  __syncthreads();
+  // the chunk's entries: 128 float4 of latent and 16 of RoPE dims each, all
+  // loads in flight at once
+  constexpr int kKv = kF32Chunk * (kKvDim / 4) / 256;  // float4 per thread
+  {
+    float4 v[kKv];
+#pragma unroll
+    for (int r = 0; r < kKv; ++r) {
+      const int i = tid + 256 * r, e = i / (kKvDim / 4), f = i % (kKvDim / 4);
+      const int64_t slot = s_slot[e];
+      const csa_kv_pool& P = s_pool[e] ? raw : comp;
+      const int64_t sl = slot >= 0 ? slot : 0;
+      const float4* src = f < kLatent / 4
+                              ? reinterpret_cast<const float4*>(P.latent) + sl * (kLatent / 4) + f
+                              : reinterpret_cast<const float4*>(P.rope) + sl * (kRope / 4) + f - kLatent / 4;
+      v[r] = slot >= 0 ? *src : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int r = 0; r < kKv; ++r) {
+      const int i = tid + 256 * r, e = i / (kKvDim / 4), f = i % (kKvDim / 4);
+      *reinterpret_cast<float4*>(&s_kv[e * kF32Row + 4 * f]) = v[r];
+    }
+  }
+  __syncthreads();
+  {  // scores: lane (eb, hb, kp) forms the 4 x 4 block of entries 4 eb.. and
+     // heads 4 hb.. over dims [72 kp, 72 kp + 72); the eight dim parts are
+     // summed across adjacent lanes (kp = lane % 8)
+    const int kp = tid & 7, hb = (tid >> 3) & 3, eb = tid >> 5;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll 2
+    for (int k = kp * 72; k < kp * 72 + 72; k += 4) {
+      float4 kv[4], qv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kv[i] = *reinterpret_cast<const float4*>(&s_kv[(eb * 4 + i) * kF32Row + k]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qv[j] = *reinterpret_cast<const float4*>(&s_q[(hb * 4 + j) * kF32Row + k]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = fmaf(qv[j].x, kv[i].x, fmaf(qv[j].y, kv[i].y,
+                      fmaf(qv[j].z, kv[i].z, fmaf(qv[j].w, kv[i].w, acc[i][j]))));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v = acc[i][j];
+        v += lane_xor<1>(v);
+        v += lane_xor<2>(v);
+        v += lane_xor<4>(v);
+        acc[i][j] = v;
+      }
+    // lane kp writes entries / heads (i, j) with 4 i + j in {2 kp, 2 kp + 1}
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((4 * i + j) >> 1 == kp) {
+          const int e = eb * 4 + i;
+          s_p[e][hb * 4 + j] = s_slot[e] >= 0 ? acc[i][j] * scale : -INFINITY;
+        }
+  }
+  __syncthreads();
+  {  // the chunk's max and exponent sum per head: a 16-lane row per head,
+     // two entries per lane
+    const int h = tid >> 4, r = tid & 15;
+    const float s0 = s_p[r][h], s1 = s_p[r + 16][h];
+    const float m = row16_max(fmaxf(s0, s1));
+    const float p0 = s0 == -INFINITY ? 0.f : expf(s0 - m);
+    const float p1 = s1 == -INFINITY ? 0.f : expf(s1 - m);
+    const float l = row16_sum(p0 + p1);
+    s_p[r][h] = p0;
+    s_p[r + 16][h] = p1;
+    if (r == 0) {
+      s_m[h] = m;
+      s_l[h] = l;
+    }
+  }
+  __syncthreads();
+  // P V over the chunk: this thread's value dims 2 tid, 2 tid + 1, every head
+  float acc[kF32Heads][2];
+#pragma unroll
+  for (int h = 0; h < kF32Heads; ++h) acc[h][0] = acc[h][1] = 0.f;
+  for (int e = 0; e < kF32Chunk; ++e) {
+    const float2 v = *reinterpret_cast<const float2*>(&s_kv[e * kF32Row + 2 * tid]);
+#pragma unroll
+    for (int h = 0; h < kF32Heads; ++h) {
+      const float pe = s_p[e][h];
+      acc[h][0] = fmaf(pe, v.x, acc[h][0]);
+      acc[h][1] = fmaf(pe, v.y, acc[h][1]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kF32Heads; ++h) {
+    if (h >= nh) continue;
+    if (nchunk == 1) {
+      const float l = s_l[h];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      *reinterpret_cast<float2*>(out + ((int64_t)t * H + h0 + h) * kLatent + 2 * tid) =
+          make_float2(acc[h][0] * inv, acc[h][1] * inv);
+    } else {
+      float* dst = part + (((int64_t)t * nchunk + c) * H + h0 + h) * (kLatent + 2);
+      if (tid == 0) {
+        dst[0] = s_m[h];
+        dst[1] = s_l[h];
+      }
+      dst[2 + 2 * tid] = acc[h][0];
+      dst[3 + 2 * tid] = acc[h][1];
+    }
+  }
+}
+
+// Merge of the chunks of one (query, head): O = sum_c e^(m_c - M) O_c /
+// sum_c e^(m_c - M) l_c over the chunks with entries (l_c > 0). The chunks'
+// (m, l) come in with one parallel load into LDS; each thread then reads its
+// two value dims of every chunk with independent loads.
+constexpr int kF32MaxChunks = 1024;  // chunks merged by one workgroup
+__global__ void __launch_bounds__(256)
+attn_f32_combine_kernel(const float* __restrict__ part, int H, int nchunk, float* __restrict__ out) {
+  __shared__ float s_f[kF32MaxChunks];
+  __shared__ float s_red[8];
+  const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int64_t cs = (int64_t)H * (kLatent + 2);
+  const float* base = part + ((int64_t)t * nchunk * H + h) * (kLatent + 2);
+  float mx = -INFINITY;
+  for (int c = tid; c < nchunk; c += 256) {
+    const float2 ml = *reinterpret_cast<const float2*>(base + c * cs);
+    s_f[c] = ml.y > 0.f ? ml.x : -INFINITY;
+    mx = fmaxf(mx, s_f[c]);
+  }
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float ls = 0.f;
+  for (int c = tid; c < nchunk; c += 256) {
+    const float l = base[c * cs + 1];
+    const float f = s_f[c] == -INFINITY ? 0.f : expf(s_f[c] - M);
+    s_f[c] = f;
+    ls = fmaf(l, f, ls);
+  }
+  ls = wave_sum(ls);
+  __syncthreads();
+  if ((tid & 63) == 0) s_red[4 + (tid >> 6)] = ls;
+  __syncthreads();
+  const float L = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < nchunk; ++c) {
+    const float2 v = *reinterpret_cast<const float2*>(base + c * cs + 2 + 2 * tid);
+    const float f = s_f[c];
+    o0 = fmaf(f, v.x, o0);
+    o1 = fmaf(f, v.y, o1);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<float2*>(out + ((int64_t)t * H + h) * kLatent + 2 * tid) =
+      make_float2(o0 * inv, o1 * inv);
 }
 
 int pick_splits(int T, int H, int max_entries) {
@@ -1061,6 +1214,11 @@ SplitPlan split_plan(int T, int H, int max_entries) {
 
 }  // namespace
 
+size_t attention_f32_ws_bytes(int64_t T, int64_t max_entries, int H) {
+  const int64_t nchunk = (max_entries + kF32Chunk - 1) / kF32Chunk;
+  return nchunk > 1 ? (size_t)T * nchunk * H * (kLatent + 2) * sizeof(float) : 0;
+}
+
 size_t attention_ws_bytes(int64_t T, int64_t max_entries, int H) {
   if (use_two_phase((int)T, H, (int)max_entries))
     return two_phase_ws(T, H, (int)((max_entries + kChunk - 1) / kChunk * kChunk)).total;
@@ -1072,10 +1230,16 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int max_entries = a.max_comp + a.window;
   if (a.comp.fmt == CSA_F32) {
-    const size_t lds = (kKvDim + max_entries + 8) * sizeof(float);
-    hipLaunchKernelGGL(attn_f32_kernel, dim3(a.H, a.T), dim3(256), lds, s, (const float*)a.q,
-                       a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel, a.ratio, a.comp, a.comp_pt,
-                       a.comp_pt_stride, a.raw, a.raw_pt, a.raw_pt_stride, a.window, a.scale,
+    const int nchunk = std::max(1, (max_entries + kF32Chunk - 1) / kF32Chunk);
+    if (nchunk > kF32MaxChunks) return hipErrorInvalidValue;
+    float* part = (float*)a.ws;
+    hipLaunchKernelGGL(attn_f32_chunk_kernel, dim3(nchunk, (a.H + kF32Heads - 1) / kF32Heads, a.T),
+                       dim3(256), 0, s, (const float*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx,
+                       a.k_sel, a.ratio, a.comp, a.comp_pt, a.comp_pt_stride, a.raw, a.raw_pt,
+                       a.raw_pt_stride, a.window, a.scale, (float*)a.out, part, nchunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nchunk == 1) return e;
+    hipLaunchKernelGGL(attn_f32_combine_kernel, dim3(a.H, a.T), dim3(256), 0, s, part, a.H, nchunk,
                        (float*)a.out);
     return hipGetLastError();
   }

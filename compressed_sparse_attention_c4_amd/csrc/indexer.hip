@@ -490,36 +490,58 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   }
 }
 
-// fp32 path (small indexers, any H_I, D_I in {64, 128}): one thread per entry,
-// the row's query in LDS.
+// fp32 path (small indexers: H_I * D_I <= 8192, D_I in {64, 128}). A wave
+// scores 16 consecutive entries: lane (e, part) = (lane / 4, lane % 4) holds a
+// quarter of entry e's row in registers (the wave reads 16 rows of a page as
+// coalesced 16-byte loads), the query and head weights sit in LDS (read as
+// broadcasts), and each head's dot product is finished across the four lanes
+// of a quad by two DPP moves.
+template <int kD>
 __global__ void __launch_bounds__(256)
-indexer_f32_kernel(const float* __restrict__ q, const float* __restrict__ w, int H, int D,
+indexer_f32_kernel(const float* __restrict__ q, const float* __restrict__ w, int H,
                    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_len,
                    const int32_t* __restrict__ pt, int pt_stride,
                    const float* __restrict__ kdata, int page_size, float* __restrict__ logits,
                    int64_t ld) {
-  extern __shared__ float sq[];  // [H][D] then w[H]
+  constexpr int kQ = kD / 4;  // floats of a row per lane
+  extern __shared__ __attribute__((aligned(16))) float sq[];  // [H][kD] then w[H]
   const int t = blockIdx.y;
-  for (int i = threadIdx.x; i < H * D; i += blockDim.x) sq[i] = q[(int64_t)t * H * D + i];
-  for (int i = threadIdx.x; i < H; i += blockDim.x) sq[H * D + i] = w[(int64_t)t * H + i];
+  for (int i = threadIdx.x; i < H * kD / 4; i += blockDim.x)
+    reinterpret_cast<float4*>(sq)[i] = reinterpret_cast<const float4*>(q + (int64_t)t * H * kD)[i];
+  for (int i = threadIdx.x; i < H; i += blockDim.x) sq[H * kD + i] = w[(int64_t)t * H + i];
   __syncthreads();
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= row_len[t]) return;
-  const int64_t slot = (int64_t)pt[(int64_t)row_seq[t] * pt_stride + j / page_size] * page_size + j % page_size;
-  const float* k = kdata + slot * D;
+  const int n = row_len[t];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = lane >> 2, part = lane & 3;
+  const int jw = blockIdx.x * 64 + wave * 16;  // first entry of this wave
+  if (jw >= n) return;                          // wave-uniform; no barrier follows
+  const int j = jw + e;
+  const int jj = min(j, n - 1);
+  const int64_t slot =
+      (int64_t)pt[(int64_t)row_seq[t] * pt_stride + jj / page_size] * page_size + jj % page_size;
+  float k[kQ];
+#pragma unroll
+  for (int i = 0; i < kQ; i += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(kdata + slot * kD + part * kQ + i);
+    k[i] = v.x;
+    k[i + 1] = v.y;
+    k[i + 2] = v.z;
+    k[i + 3] = v.w;
+  }
   float acc = 0.f;
   for (int h = 0; h < H; ++h) {
+    const float* qh = sq + h * kD + part * kQ;
     float d = 0.f;
-    for (int i = 0; i < D; i += 4) {
-      float4 kv = *reinterpret_cast<const float4*>(k + i);
-      d = fmaf(sq[h * D + i], kv.x, d);
-      d = fmaf(sq[h * D + i + 1], kv.y, d);
-      d = fmaf(sq[h * D + i + 2], kv.z, d);
-      d = fmaf(sq[h * D + i + 3], kv.w, d);
+#pragma unroll
+    for (int i = 0; i < kQ; i += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(qh + i);
+      d = fmaf(a.x, k[i], fmaf(a.y, k[i + 1], fmaf(a.z, k[i + 2], fmaf(a.w, k[i + 3], d))));
     }
-    acc = fmaf(sq[H * D + h], fmaxf(d, 0.f), acc);
+    d += lane_xor<1>(d);
+    d += lane_xor<2>(d);
+    acc = fmaf(sq[H * kD + h], fmaxf(d, 0.f), acc);
   }
-  logits[(int64_t)t * ld + j] = acc;
+  if (part == 0 && j < n) logits[(int64_t)t * ld + j] = acc;
 }
 
 }  // namespace
@@ -581,11 +603,16 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
                           uint32_t* okeys, int32_t* ojs, int32_t* ophys) {
   if (T == 0 || max_row_len == 0) return hipSuccess;
   if (k.fmt == CSA_F32) {
-    dim3 grid((max_row_len + 255) / 256, T);
+    dim3 grid((max_row_len + 63) / 64, T);
     const size_t lds = ((size_t)H_I * D_I + H_I) * sizeof(float);
-    hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), lds, s, (const float*)q, w, H_I,
-                       D_I, row_seq, row_len, page_table, pt_stride, (const float*)k.data,
-                       k.page_size, logits, ld);
+    if (D_I == 64)
+      hipLaunchKernelGGL(indexer_f32_kernel<64>, grid, dim3(256), lds, s, (const float*)q, w, H_I,
+                         row_seq, row_len, page_table, pt_stride, (const float*)k.data, k.page_size,
+                         logits, ld);
+    else
+      hipLaunchKernelGGL(indexer_f32_kernel<128>, grid, dim3(256), lds, s, (const float*)q, w, H_I,
+                         row_seq, row_len, page_table, pt_stride, (const float*)k.data, k.page_size,
+                         logits, ld);
     return hipGetLastError();
   }
   const uint8_t* qc = (const uint8_t*)q;

@@ -328,12 +328,14 @@ csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
  *   out[t][h][:] = sum_e softmax(score)_e * kv_e[0:512]
  * kv_e is the dequantised entry. All H heads share the KV (MQA).
  *   q    [T][H][576]: CSA_BF16 with FP8 pools (H a multiple of 16, <= 128), or
- *        CSA_F32 with F32 pools (any H). out [T][H][512] CSA_BF16 or CSA_F32
+ *        CSA_F32 with F32 pools (any H; lists of up to 32768 entries). out [T][H][512] CSA_BF16 or CSA_F32
  *        (F32 pools: CSA_F32 only).
  *   c4 and raw pools must have the same fmt; raw.page_size is the raw page size.
  *   Requires 1 <= window <= 4096 and 0 <= k_sel <= 512.
  *   ws   workspace of csa_workspace_size(CSA_OP_CSA_ATTN, T, k_sel + window, H)
- *        bytes (may be 0 bytes / NULL when that size is 0).
+ *        bytes for FP8 pools, CSA_OP_CSA_ATTN_F32 for F32 pools (may be 0
+ *        bytes / NULL when that size is 0).
+
  */
 csa_status csa_sparse_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
                            const int32_t* q_seq, const int32_t* q_pos,
@@ -349,7 +351,8 @@ csa_status csa_sparse_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
  * sliding window as CSA. As csa_sparse_attn with
  *   E = { hca entry j of sequence s : ratio*j + ratio - 1 <= p }  U  window(p).
  *   max_len HOST: an upper bound of q_pos[t] + 1 (sizes the split of the entry
- *           list); ws: csa_workspace_size(CSA_OP_HCA_ATTN, T, max_len/ratio + window, H).
+ *           list); ws: csa_workspace_size(CSA_OP_HCA_ATTN, T, max_len/ratio + window, H)
+ *           (CSA_OP_HCA_ATTN_F32 for F32 pools).
  */
 csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
                           const int32_t* q_seq, const int32_t* q_pos, int32_t max_len,
@@ -365,13 +368,16 @@ csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
  *     prepared inside the call and q_used is NULL), CSA_OP_TOPK (rows = R,
  *     max_len = ld),
  *     CSA_OP_CSA_ATTN / CSA_OP_HCA_ATTN (rows = T, max_len = most entries of
- *     one query's list, heads = H), CSA_OP_INDEXER_TOPK (rows = T, max_len =
- *     max_row_len, heads = H_I). */
+ *     one query's list, heads = H; FP8 pools), CSA_OP_CSA_ATTN_F32 /
+ *     CSA_OP_HCA_ATTN_F32 (the same for F32 pools), CSA_OP_INDEXER_TOPK
+ *     (rows = T, max_len = max_row_len, heads = H_I). */
 #define CSA_OP_INDEXER  0
 #define CSA_OP_TOPK     1
 #define CSA_OP_CSA_ATTN 2
 #define CSA_OP_HCA_ATTN 3
 #define CSA_OP_INDEXER_TOPK 4
+#define CSA_OP_CSA_ATTN_F32 5
+#define CSA_OP_HCA_ATTN_F32 6
 size_t csa_workspace_size(int32_t op, int64_t rows, int64_t max_len, int32_t heads);
 
 const char* csa_status_string(csa_status s);

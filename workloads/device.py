@@ -510,7 +510,7 @@ class TinyDecode:
         self.out = torch.empty((1, wl.heads, 512), dtype=torch.float32, device=DEV)
         n = csa.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK, 1, N, wl.index_heads)
         self.itk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
-        n = csa.csa_workspace_size(csa.CSA_OP_CSA_ATTN, 1, 512 + wl.window, wl.heads)
+        n = csa.csa_workspace_size(csa.CSA_OP_CSA_ATTN_F32, 1, 512 + wl.window, wl.heads)
         self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         torch.cuda.synchronize()
 
