@@ -19,7 +19,7 @@ lib = C.CDLL(LIB_PATH)
 # ---- constants (mirror include/csa.h)
 CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = range(5)
 CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4 = range(4)
-CSA_PREP_HADAMARD, CSA_PREP_QUANT = 1, 2
+CSA_PREP_HADAMARD, CSA_PREP_QUANT, CSA_PREP_ROPE = 1, 2, 4
 
 
 def CSA_ROWS_PER_SEQ(n: int) -> int:
@@ -34,6 +34,19 @@ CSA_NOALLOC_SCRATCH_BYTES = 32 << 20
 class _KvPoolC(C.Structure):
     _fields_ = [("latent", C.c_void_p), ("latent_scale", C.c_void_p), ("rope", C.c_void_p),
                 ("fmt", C.c_int32), ("page_size", C.c_int32), ("num_pages", C.c_int64)]
+
+
+class _RopeC(C.Structure):
+    _fields_ = [("pos", C.c_void_p), ("cos_sin", C.c_void_p), ("dim", C.c_int32),
+                ("rows_per_pos", C.c_int32)]
+
+
+def _rope(pos, table, rows_per_pos=1):
+    """csa_rope from positions (int32 tensor or None) and a cos/sin table
+    [positions, dim/2, 2] float32 tensor (or None)."""
+    if table is None:
+        return _RopeC(None, None, 0, 1)
+    return _RopeC(_ptr(pos), _ptr(table), 2 * table.shape[-2], int(rows_per_pos))
 
 
 class _IndexPoolC(C.Structure):
@@ -52,9 +65,9 @@ def _decl(name, args, res=C.c_int):
 
 
 _c4_compress = _decl("c4_compress", [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _KvPoolC, _vp])
-_csa_index_prep = _decl("csa_index_prep", [_vp, _i32, _i64, _i32, _u32, _i32, _vp, _vp, _vp, _vp])
+_csa_index_prep = _decl("csa_index_prep", [_vp, _i32, _i64, _i32, _u32, _i32, _vp, _vp, _vp, _RopeC, _vp])
 _decode_prep = _decl("csa_decode_prep", [_vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _KvPoolC,
-                                         _vp, _i32, _KvPoolC, _vp, _vp, _i32, _i32, _u32,
+                                         _vp, _i32, _KvPoolC, _vp, _vp, _i32, _i32, _u32, _RopeC,
                                          _IndexPoolC, _vp, _vp, _vp])
 _indexer_score = _decl("indexer_score", [_vp, _i32, _vp, _u32, _vp, _i32, _i32, _i32, _vp, _vp, _i32,
                                          _vp, _i32, _IndexPoolC, _vp, _i64, _vp, _vp, _vp, _sz, _vp])
@@ -177,17 +190,22 @@ def c4_compress(x, cu_rows, start_pos, max_rows, ratio, gate_w, gate_b, page_tab
         _stream(stream)))
 
 
-def csa_index_prep(v, dim, flags, out_fmt, out, out_scale=None, dst_rows=None, stream=None):
+def csa_index_prep(v, dim, flags, out_fmt, out, out_scale=None, dst_rows=None, stream=None, *,
+                   rope_pos=None, rope_table=None, rows_per_pos=1):
+    """rope_table [positions, rope_dim/2, 2] float32 (cos, sin) and rope_pos
+    int32 (one per rows_per_pos rows) are used with CSA_PREP_ROPE in flags."""
     rows = v.numel() // dim
     _check("csa_index_prep", _csa_index_prep(
         _ptr(v), _fmt_of(v), rows, int(dim), int(flags), int(out_fmt), _ptr(out), _ptr(out_scale),
-        _ptr(dst_rows), _stream(stream)))
+        _ptr(dst_rows), _rope(rope_pos, rope_table, rows_per_pos), _stream(stream)))
 
 
 def csa_decode_prep(x, pos, gate_w, gate_b, page_table, c4: KvPool, raw_page_table, raw: KvPool,
                     k_rows=None, q_rows=None, kpool: IndexPool | None = None, q_out=None,
-                    q_out_scale=None, flags=CSA_PREP_HADAMARD, stream=None):
-    """x [B][ratio][576]; pos int32 [B]; k_rows [B][dim], q_rows [B][H_I][dim] (bf16 or f32)."""
+                    q_out_scale=None, flags=CSA_PREP_HADAMARD, stream=None, rope_table=None):
+    """x [B][ratio][576]; pos int32 [B]; k_rows [B][dim], q_rows [B][H_I][dim] (bf16 or f32);
+    rope_table [positions, rope_dim/2, 2] float32 with CSA_PREP_ROPE in flags (both the
+    block's index-K row and the query rows are rotated at pos[b])."""
     B, ratio = x.shape[0], x.shape[1]
     kq = k_rows if k_rows is not None else q_rows
     H_I = q_rows.shape[1] if q_rows is not None else 0
@@ -196,7 +214,7 @@ def csa_decode_prep(x, pos, gate_w, gate_b, page_table, c4: KvPool, raw_page_tab
         _ptr(x), _fmt_of(x), _ptr(pos), B, ratio, _ptr(gate_w), _ptr(gate_b), _ptr(page_table),
         page_table.shape[-1], c4.c(), _ptr(raw_page_table), raw_page_table.shape[-1], raw.c(),
         _ptr(k_rows), _ptr(q_rows), _fmt_of(kq) if kq is not None else CSA_BF16, H_I, int(flags),
-        kp, _ptr(q_out), _ptr(q_out_scale), _stream(stream)))
+        _rope(pos, rope_table), kp, _ptr(q_out), _ptr(q_out_scale), _stream(stream)))
 
 
 def indexer_score(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPool, logits, *,

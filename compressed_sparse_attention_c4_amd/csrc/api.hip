@@ -57,6 +57,13 @@ csa_status indexer_args(csa_fmt q_fmt, const void* q_scale, uint32_t prep, int32
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// A rotary embedding description used with CSA_PREP_ROPE on rows of `dim`.
+inline bool rope_ok(const csa_rope& r, int dim, bool need_groups) {
+  if (!r.pos || !r.cos_sin) return false;
+  if (r.dim < 2 || r.dim > dim || (r.dim & 1)) return false;
+  return !need_groups || r.rows_per_pos >= 1;
+}
+
 // indexer_topk512's workspace: the query-preparation area, then either the
 // scan's top-512 candidates (fused path) or the logits and the top-512
 // workspace (two-call path); sized for whichever is larger.
@@ -129,15 +136,16 @@ csa_status c4_compress(const void* x, csa_fmt x_fmt, const int32_t* cu_rows,
 
 csa_status csa_index_prep(const void* v, csa_fmt v_fmt, int64_t rows, int32_t dim,
                           uint32_t flags, csa_fmt out_fmt, void* out, void* out_scale,
-                          const int32_t* dst_rows, hipStream_t stream) {
+                          const int32_t* dst_rows, csa_rope rope, hipStream_t stream) {
   if (rows < 0 || (dim != 64 && dim != 128)) return CSA_ERR_INVALID;
   if (v_fmt != CSA_BF16 && v_fmt != CSA_F32) return CSA_ERR_INVALID;
-  if (flags & ~(CSA_PREP_HADAMARD | CSA_PREP_QUANT)) return CSA_ERR_INVALID;
+  if (flags & ~(CSA_PREP_HADAMARD | CSA_PREP_QUANT | CSA_PREP_ROPE)) return CSA_ERR_INVALID;
+  if ((flags & CSA_PREP_ROPE) && !rope_ok(rope, dim, true)) return CSA_ERR_INVALID;
   if (out_fmt != CSA_F32 && out_fmt != CSA_FP8_E4M3 && out_fmt != CSA_MXFP4) return CSA_ERR_INVALID;
   if (rows == 0) return CSA_OK;
   if (!v || !out || (out_fmt != CSA_F32 && !out_scale)) return CSA_ERR_INVALID;
   return hip_status(launch_index_prep(v, v_fmt, rows, dim, flags, out_fmt, out, out_scale,
-                                      dst_rows, stream));
+                                      dst_rows, rope, stream));
 }
 
 csa_status csa_decode_prep(const void* x, csa_fmt x_fmt, const int32_t* pos, int32_t B,
@@ -145,14 +153,19 @@ csa_status csa_decode_prep(const void* x, csa_fmt x_fmt, const int32_t* pos, int
                            const int32_t* page_table, int32_t pt_stride, csa_kv_pool c4,
                            const int32_t* raw_page_table, int32_t raw_pt_stride,
                            csa_kv_pool raw, const void* k_rows, const void* q_rows,
-                           csa_fmt kq_fmt, int32_t H_I, uint32_t flags, csa_index_pool kpool,
-                           void* q_out, void* q_out_scale, hipStream_t stream) {
+                           csa_fmt kq_fmt, int32_t H_I, uint32_t flags, csa_rope rope,
+                           csa_index_pool kpool, void* q_out, void* q_out_scale,
+                           hipStream_t stream) {
   if (B < 0 || ratio < 1 || ratio > 128 || pt_stride <= 0 || raw_pt_stride <= 0 || H_I < 0)
     return CSA_ERR_INVALID;
   if (x_fmt != CSA_BF16 && x_fmt != CSA_F32) return CSA_ERR_INVALID;
   if (!kv_pool_ok(c4) || !kv_pool_ok(raw) || c4.fmt != raw.fmt) return CSA_ERR_INVALID;
-  if (flags & ~(uint32_t)CSA_PREP_HADAMARD) return CSA_ERR_INVALID;
+  if (flags & ~(uint32_t)(CSA_PREP_HADAMARD | CSA_PREP_ROPE)) return CSA_ERR_INVALID;
   const bool kq = k_rows || q_rows;
+  if (kq && (flags & CSA_PREP_ROPE)) {
+    rope.pos = pos;  // decode rotates at each sequence's token position
+    if (!rope_ok(rope, kpool.dim, false)) return CSA_ERR_INVALID;
+  }
   if (kq) {
     if (kq_fmt != CSA_BF16 && kq_fmt != CSA_F32) return CSA_ERR_INVALID;
     if (kpool.dim != 64 && kpool.dim != 128) return CSA_ERR_INVALID;
@@ -170,6 +183,7 @@ csa_status csa_decode_prep(const void* x, csa_fmt x_fmt, const int32_t* pos, int
   a.gate_b = gate_b; a.page_table = page_table; a.pt_stride = pt_stride; a.c4 = c4;
   a.raw_page_table = raw_page_table; a.raw_pt_stride = raw_pt_stride; a.raw = raw;
   a.k_rows = k_rows; a.q_rows = q_rows; a.kq_fmt = kq_fmt; a.H_I = H_I; a.flags = flags;
+  a.rope = rope;
   a.kpool = kpool; a.q_out = q_out; a.q_out_scale = q_out_scale;
   if (!kq) a.kpool.dim = 128;  // sizes the (unused) row layout only
   return hip_status(launch_decode_prep(a, stream));

@@ -32,6 +32,7 @@ struct DecodePrepArgs {
   int kq_fmt;
   int H_I;
   uint32_t flags;
+  csa_rope rope;
   csa_index_pool kpool;
   void* q_out;
   void* q_out_scale;
@@ -40,7 +41,7 @@ hipError_t launch_decode_prep(const DecodePrepArgs& a, hipStream_t s);
 
 hipError_t launch_index_prep(const void* v, int v_fmt, int64_t rows, int dim, uint32_t flags,
                              int out_fmt, void* out, void* out_scale, const int32_t* dst_rows,
-                             hipStream_t s);
+                             const csa_rope& rope, hipStream_t s);
 
 hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_t prep,
                           const float* w, int T, int H_I, int D_I, const int32_t* row_seq,

@@ -3,9 +3,9 @@
 //
 // "Token 的一生：DSV4 架构与 DSpark" §1 (the new token updates the compressed cache,
 // the raw window and the indexer's K cache before the indexer runs), §2.1
-// (block k = raw positions [4k, 4k+3], emitted once 4k+3 exists), §3 and §4
-// (index-K rows and indexer queries rotated by a Hadamard transform, then FP8
-// or FP4 quantised). The four writes are independent per sequence; as separate
+// (block k = raw positions [4k, 4k+3], emitted once 4k+3 exists), §3.1 and §4
+// (index-K rows and indexer queries: rope -> hadamard -> FP8 or FP4 quant, the
+// rope at the token's position). The four writes are independent per sequence; as separate
 // launches each costs a launch and a memory round trip for a few KB of work.
 //
 // Workgroup b < B handles sequence b with three wavefronts:
@@ -16,6 +16,8 @@
 //   wave 2: if a block is completed, its index-K row (rotated, quantised, as
 //           csa_index_prep) into the index pool at the block's entry.
 // Workgroups from B on prepare the query rows, one row per wave and pass.
+#include <algorithm>
+
 #include "compress_dev.hpp"
 #include "csa_internal.hpp"
 #include "index_prep_dev.hpp"
@@ -34,7 +36,8 @@ decode_prep_kernel(const void* __restrict__ x, const int32_t* __restrict__ pos, 
                    const int32_t* __restrict__ rpt, int rpt_stride, void* __restrict__ r_lat,
                    float* __restrict__ r_sc, void* __restrict__ r_rope, int r_ps,
                    const void* __restrict__ k_rows, const void* __restrict__ q_rows, bool kq_f32,
-                   int64_t q_count, bool hadamard, int kq_fmt, void* __restrict__ k_data,
+                   int64_t q_count, int H_I, bool hadamard, bool rope, const float* __restrict__ cos_sin,
+                   int rope_dim, int kq_fmt, void* __restrict__ k_data,
                    void* __restrict__ k_scale, void* __restrict__ q_out,
                    void* __restrict__ q_out_scale) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -63,6 +66,7 @@ decode_prep_kernel(const void* __restrict__ x, const int32_t* __restrict__ pos, 
       if (valid) {
         if (kq_f32) load_pair<true>(k_rows, (int64_t)b * D + e0, x0, x1);
         else load_pair<false>(k_rows, (int64_t)b * D + e0, x0, x1);
+        if (rope) rope_pair<D>(x0, x1, e0 / 2, p, cos_sin, rope_dim);
       }
       prep_and_store<D>(x0, x1, valid, hadamard, kq_fmt, k_data, k_scale, slot);
     }
@@ -79,6 +83,7 @@ decode_prep_kernel(const void* __restrict__ x, const int32_t* __restrict__ pos, 
     if (valid) {
       if (kq_f32) load_pair<true>(q_rows, r * D + e0, x0, x1);
       else load_pair<false>(q_rows, r * D + e0, x0, x1);
+      if (rope) rope_pair<D>(x0, x1, e0 / 2, pos[r / H_I], cos_sin, rope_dim);
     }
     prep_and_store<D>(x0, x1, valid, hadamard, kq_fmt, q_out, q_out_scale, valid ? r : 0);
   }
@@ -101,8 +106,9 @@ hipError_t launch_decode_prep(const DecodePrepArgs& a, hipStream_t s) {
                      a.B, a.ratio, a.gate_w, a.gate_b, a.page_table, a.pt_stride, a.c4.latent,     \
                      a.c4.latent_scale, a.c4.rope, a.c4.page_size, a.raw_page_table,               \
                      a.raw_pt_stride, a.raw.latent, a.raw.latent_scale, a.raw.rope,                \
-                     a.raw.page_size, a.k_rows, a.q_rows, kq_f32, q_count,                         \
-                     (a.flags & CSA_PREP_HADAMARD) != 0, (int)a.kpool.fmt, a.kpool.data,           \
+                     a.raw.page_size, a.k_rows, a.q_rows, kq_f32, q_count, std::max(a.H_I, 1),     \
+                     (a.flags & CSA_PREP_HADAMARD) != 0, (a.flags & CSA_PREP_ROPE) != 0,           \
+                     a.rope.cos_sin, a.rope.dim, (int)a.kpool.fmt, a.kpool.data,                   \
                      a.kpool.scale, a.q_out, a.q_out_scale)
 #define CSA_DP_D(FI, FO) \
   if (a.kpool.dim == 128) CSA_DP(FI, FO, 128); else CSA_DP(FI, FO, 64)

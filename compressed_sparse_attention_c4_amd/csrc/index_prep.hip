@@ -1,10 +1,13 @@
-// index_prep.hip -- Hadamard rotation and FP8 / MXFP4 quantisation of indexer
-// rows ("Token 的一生：DSV4 架构与 DSpark" §3.1: FP8 or FP4 query plus scale
-// factors; §4: q and index-K go rope -> hadamard -> quant; RoPE is upstream).
+// index_prep.hip -- rotary embedding, Hadamard rotation and FP8 / MXFP4
+// quantisation of indexer rows ("Token 的一生：DSV4 架构与 DSpark" §3.1: FP8 or
+// FP4 query plus scale factors, prepared with the rope table and positions;
+// §4: q and index-K go rope -> hadamard -> quant).
 //
 // A wavefront prepares one 128-dim row (two elements per lane) or two 64-dim
-// rows (one per half-wave); the rotation is a shuffle-based fast Walsh-Hadamard
-// transform in registers, so the row is read once and written once.
+// rows (one per half-wave). A lane's two elements are an adjacent pair, so the
+// rotary embedding is a 2 x 2 rotation in the lane; the Hadamard rotation is a
+// shuffle-based fast Walsh-Hadamard transform in registers, so the row is read
+// once and written once.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 #include "index_prep_dev.hpp"
@@ -18,7 +21,7 @@ template <int D, bool kF32In>
 __global__ void __launch_bounds__(kWavesPerWG * 64)
 index_prep_kernel(const void* __restrict__ v, int64_t rows, uint32_t flags, int out_fmt,
                   void* __restrict__ out, void* __restrict__ out_scale,
-                  const int32_t* __restrict__ dst_rows) {
+                  const int32_t* __restrict__ dst_rows, csa_rope rope) {
   constexpr int kRowsPerWave = 128 / D;
   const int lane = threadIdx.x & 63;
   const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
@@ -29,7 +32,11 @@ index_prep_kernel(const void* __restrict__ v, int64_t rows, uint32_t flags, int 
     const int64_t r = r0 + sub;
     const bool valid = r < rows;
     float x0 = 0.f, x1 = 0.f;
-    if (valid) load_pair<kF32In>(v, r * D + e0, x0, x1);
+    if (valid) {
+      load_pair<kF32In>(v, r * D + e0, x0, x1);
+      if (flags & CSA_PREP_ROPE)
+        rope_pair<D>(x0, x1, e0 / 2, rope.pos[r / rope.rows_per_pos], rope.cos_sin, rope.dim);
+    }
     const int64_t d = valid ? (dst_rows ? (int64_t)dst_rows[r] : r) : 0;
     const bool store = valid && d >= 0;  // a negative destination skips the row
     prep_and_store<D>(x0, x1, store, flags & CSA_PREP_HADAMARD, out_fmt, out, out_scale,
@@ -41,7 +48,7 @@ index_prep_kernel(const void* __restrict__ v, int64_t rows, uint32_t flags, int 
 
 hipError_t launch_index_prep(const void* v, int v_fmt, int64_t rows, int dim, uint32_t flags,
                              int out_fmt, void* out, void* out_scale, const int32_t* dst_rows,
-                             hipStream_t s) {
+                             const csa_rope& rope, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int64_t rows_per_wg = kWavesPerWG * (128 / dim);
   int64_t nblocks = (rows + rows_per_wg - 1) / rows_per_wg;
@@ -49,11 +56,11 @@ hipError_t launch_index_prep(const void* v, int v_fmt, int64_t rows, int dim, ui
   dim3 grid((unsigned)nblocks), block(kWavesPerWG * 64);
   const bool f32 = v_fmt == CSA_F32;
   if (dim == 128) {
-    if (f32) hipLaunchKernelGGL((index_prep_kernel<128, true>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows);
-    else hipLaunchKernelGGL((index_prep_kernel<128, false>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows);
+    if (f32) hipLaunchKernelGGL((index_prep_kernel<128, true>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows, rope);
+    else hipLaunchKernelGGL((index_prep_kernel<128, false>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows, rope);
   } else {
-    if (f32) hipLaunchKernelGGL((index_prep_kernel<64, true>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows);
-    else hipLaunchKernelGGL((index_prep_kernel<64, false>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows);
+    if (f32) hipLaunchKernelGGL((index_prep_kernel<64, true>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows, rope);
+    else hipLaunchKernelGGL((index_prep_kernel<64, false>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows, rope);
   }
   return hipGetLastError();
 }

@@ -19,6 +19,24 @@ __device__ __forceinline__ void load_pair(const void* v, int64_t idx, float& x0,
   }
 }
 
+// Rotary embedding of one row held two elements per lane (lane index li
+// within the row holds elements 2 li, 2 li + 1, an adjacent pair): the pairs
+// of the last rope_dim dims are rotated by the (cos, sin) of the row's
+// position, in fp32 ("Token 的一生：DSV4 架构与 DSpark" §4: rope before the
+// Hadamard rotation and the quantisation).
+template <int D>
+__device__ __forceinline__ void rope_pair(float& x0, float& x1, int li, int64_t pos,
+                                          const float* __restrict__ cos_sin, int rope_dim) {
+  const int i = li - (D - rope_dim) / 2;
+  if (i >= 0) {
+    const float2 cs = reinterpret_cast<const float2*>(cos_sin)[pos * (rope_dim / 2) + i];
+    const float a = x0 * cs.x - x1 * cs.y;
+    const float b = x0 * cs.y + x1 * cs.x;
+    x0 = a;
+    x1 = b;
+  }
+}
+
 // Rotate (optionally) and quantise one row of D in {64, 128} held two elements
 // per lane (D == 64: a half-wave per row), and store it as output row `dst`.
 // Every lane of the wave must call this (it uses cross-lane shuffles).

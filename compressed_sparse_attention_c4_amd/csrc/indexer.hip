@@ -626,9 +626,10 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
       dst = ws;
       dsts = (uint8_t*)ws + (((size_t)T * H_I * kDim + 255) & ~(size_t)255);
     }
+    const csa_rope no_rope{nullptr, nullptr, 0, 1};
     hipError_t e = launch_index_prep(q, q_fmt, (int64_t)T * H_I, D_I,
                                      prep & (CSA_PREP_HADAMARD | CSA_PREP_QUANT), k.fmt, dst, dsts,
-                                     nullptr, s);
+                                     nullptr, no_rope, s);
     if (e != hipSuccess) return e;
     qc = (const uint8_t*)dst;
     qs = dsts;

@@ -88,6 +88,7 @@ typedef enum {
 /* Index preparation flags ([P1] §4: q and K go rope -> hadamard -> quant). */
 #define CSA_PREP_HADAMARD 1u  /* v <- H_D v / sqrt(D), Sylvester order */
 #define CSA_PREP_QUANT    2u  /* quantise to the index pool's format   */
+#define CSA_PREP_ROPE     4u  /* rotary embedding first (see csa_rope)  */
 /*
  * Rows-per-sequence hint for indexer_score / indexer_topk512 (OR-ed into
  * `prep`; n in 0..255, 0 = no hint): the query rows come in consecutive groups
@@ -100,6 +101,29 @@ typedef enum {
  * from its own pages).
  */
 #define CSA_ROWS_PER_SEQ(n) ((((uint32_t)(n)) & 0xFFu) << 8)
+
+/*
+ * Rotary position embedding of indexer rows ([P1] §3.1: the fused query
+ * preparation takes a cos/sin table `freqs_cis` and the token positions; §4:
+ * rope -> hadamard -> quant for q and for the index-K rows). The last `dim`
+ * dims of a row are rotated in adjacent pairs: pair i = (x[D-dim+2i],
+ * x[D-dim+2i+1]) at position p becomes (x c - y s, x s + y c) with
+ * (c, s) = (cos_sin[(p * dim/2 + i) * 2], cos_sin[(p * dim/2 + i) * 2 + 1]).
+ * The caller owns the table (float32, any frequencies it chooses; e.g. the
+ * textbook theta^(-2i/dim) angles) and guarantees every position used is a
+ * row of it.
+ *   pos           device int32: the position of each group of rows
+ *   cos_sin       device float [positions][dim/2][2]
+ *   dim           even, 2 <= dim <= the row dim
+ *   rows_per_pos  csa_index_prep: rows r of the call use pos[r / rows_per_pos]
+ *                 (1 for index-K rows, H_I for [T][H_I] query rows)
+ */
+typedef struct {
+  const int32_t* pos;
+  const float*   cos_sin;
+  int32_t dim;
+  int32_t rows_per_pos;
+} csa_rope;
 
 typedef struct {
   void*   latent;        /* see the KV entry layout above */
@@ -152,11 +176,13 @@ csa_status c4_compress(const void* x, csa_fmt x_fmt, const int32_t* cu_rows,
                        csa_kv_pool out, hipStream_t stream);
 
 /*
- * csa_index_prep -- Hadamard rotation and quantisation of indexer rows (q rows
- * or index-K rows): [P1] §3.1 and §4 (rope -> hadamard -> FP8/FP4 quant; RoPE
- * is applied upstream of this library).
+ * csa_index_prep -- rotary embedding, Hadamard rotation and quantisation of
+ * indexer rows (q rows or index-K rows): [P1] §3.1 and §4 (rope -> hadamard ->
+ * FP8/FP4 quant).
  *   v       [rows][dim] CSA_BF16 or CSA_F32.
- *   flags   CSA_PREP_HADAMARD: v <- H v / sqrt(dim), H the Sylvester Hadamard
+ *   flags   CSA_PREP_ROPE: first rotate the last rope.dim dims of each row by
+ *           its position (csa_rope), in fp32.
+ *           CSA_PREP_HADAMARD: v <- H v / sqrt(dim), H the Sylvester Hadamard
  *           matrix (dim a power of two, <= 128), computed in fp32.
  *   out_fmt CSA_FP8_E4M3: out uint8 [*][dim] + out_scale float[*], per row
  *                         scale = max(amax, FLT_MIN)/448, code = e4m3_rne(v/scale).
@@ -168,10 +194,13 @@ csa_status c4_compress(const void* x, csa_fmt x_fmt, const int32_t* cu_rows,
  *           (e.g. a pool slot), and not written at all when dst_rows[i] < 0 (a
  *           decode step where a sequence completes no block); NULL writes row i
  *           to output row i.
+ *   rope    used with CSA_PREP_ROPE (ignored otherwise); rope.pos / cos_sin
+ *           must be set and rope.dim, rope.rows_per_pos valid, else
+ *           CSA_ERR_INVALID.
  */
 csa_status csa_index_prep(const void* v, csa_fmt v_fmt, int64_t rows, int32_t dim,
                           uint32_t flags, csa_fmt out_fmt, void* out, void* out_scale,
-                          const int32_t* dst_rows, hipStream_t stream);
+                          const int32_t* dst_rows, csa_rope rope, hipStream_t stream);
 
 /*
  * csa_decode_prep -- every per-sequence write and the query preparation of one
@@ -195,7 +224,11 @@ csa_status csa_index_prep(const void* v, csa_fmt v_fmt, int64_t rows, int32_t di
  *  raw_page_table int32 [B][raw_pt_stride] over raw.page_size-token pages.
  *  k_rows, q_rows  [B][dim] and [B][H_I][dim] in kq_fmt (CSA_BF16 / CSA_F32),
  *           dim = kpool.dim; either may be NULL.
- *  flags    0 or CSA_PREP_HADAMARD, for both k and q rows.
+ *  flags    CSA_PREP_HADAMARD and / or CSA_PREP_ROPE, for both k and q rows;
+ *           with CSA_PREP_ROPE both are rotated at the token's position pos[b]
+ *           (the block's index-K row takes the position of the token that
+ *           completes it), from rope.cos_sin; rope.pos and rope.rows_per_pos
+ *           are not used.
  * c4 and raw must have the same format (FP8 or F32). Returns CSA_ERR_INVALID
  * on a bad pointer, size or format, CSA_OK (nothing enqueued) when B == 0.
  */
@@ -204,8 +237,9 @@ csa_status csa_decode_prep(const void* x, csa_fmt x_fmt, const int32_t* pos, int
                            const int32_t* page_table, int32_t pt_stride, csa_kv_pool c4,
                            const int32_t* raw_page_table, int32_t raw_pt_stride,
                            csa_kv_pool raw, const void* k_rows, const void* q_rows,
-                           csa_fmt kq_fmt, int32_t H_I, uint32_t flags, csa_index_pool kpool,
-                           void* q_out, void* q_out_scale, hipStream_t stream);
+                           csa_fmt kq_fmt, int32_t H_I, uint32_t flags, csa_rope rope,
+                           csa_index_pool kpool, void* q_out, void* q_out_scale,
+                           hipStream_t stream);
 
 /*
  * indexer_score -- lightning-indexer logits of every visible compressed entry

@@ -39,6 +39,13 @@ def regen_fill_rows(slots, dim: int, seed: int, total_slots: int) -> np.ndarray:
     return out
 
 
+def rope_cs(positions, rope_dim):
+    """(cos, sin) float64 [len(positions), rope_dim/2] of the RoPE table the
+    library was given (the float32 values of the seeded input table)."""
+    cs = gen.rope_rows(positions, rope_dim).astype(np.float64)
+    return cs[..., 0], cs[..., 1]
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     """A seeded device draw (an input, not a library result) as float32."""
     return t.float().cpu().numpy()
@@ -74,20 +81,30 @@ class SeqState:
     steps can change."""
 
     def __init__(self, wl, kraw, kv_fn, raw_pos0, raw_rows, q_idx, w_idx, q_attn, p, row_len,
-                 bands: bool = True):
+                 bands: bool = True, k_rope=None):
+        """k_rope: None, or (rows, positions): the index-K rows written by the
+        step, which the library rotated (RoPE) at those positions."""
         self.wl = wl
-        codes, sc = O.index_prep(kraw, wl.hadamard, wl.index_fmt)
+        kin = np.asarray(kraw, dtype=np.float64)
+        if k_rope is not None and wl.rope_dim:
+            rows, kpos = k_rope
+            kin = kin.copy()
+            cos, sin = rope_cs(kpos, wl.rope_dim)
+            kin[rows] = O.rope_rotate(kin[rows], cos, sin, wl.rope_dim)  # exact; then index_prep rounds once
+        codes, sc = O.index_prep(kin, wl.hadamard, wl.index_fmt)
         self.ipool = O.IndexPool(codes, sc, wl.index_fmt)
         self.dk = None
         if bands:
-            self.dk = Q.band_delta(Q.exact_rotated(kraw, wl.hadamard),
-                                   Q.rotation_error_bound(kraw, wl.index_dim), wl.index_fmt)
+            self.dk = Q.band_delta(Q.exact_rotated(kin, wl.hadamard),
+                                   Q.rotation_error_bound(kraw, wl.index_dim, rope=bool(wl.rope_dim)),
+                                   wl.index_fmt)
         self.c4 = LazyKVPool(kv_fn, wl.kv_fmt)
         self.raw = O.KVPool(*O.quant_kv_entries(raw_rows, wl.kv_fmt), wl.kv_fmt)
         self._raw_rows = raw_rows
         self.raw_pos0 = raw_pos0
         self.q_idx, self.w_idx, self.q_attn = q_idx, w_idx, q_attn
         self.p, self.row_len = p, row_len
+        self.q_pos = p  # the query's RoPE position
         self.n_entries = kraw.shape[0]
 
     def raw_map(self) -> np.ndarray:
@@ -96,17 +113,25 @@ class SeqState:
         m[self.raw_pos0:] = np.arange(self.p + 1 - self.raw_pos0)
         return m
 
+    def q_rope(self):
+        """The oracle's RoPE argument for the query rows (None without RoPE)."""
+        if not self.wl.rope_dim:
+            return None
+        cos, sin = rope_cs([self.q_pos], self.wl.rope_dim)
+        return cos, sin, self.wl.rope_dim
+
     def scores(self):
         """(oracle logits [row_len], slack [row_len]): the slack bounds what
         in-band codes of the query and of each index-K row can change."""
         wl = self.wl
-        qc, qs = O.index_prep(self.q_idx, wl.hadamard, wl.index_fmt)
+        qc, qs = O.index_prep(self.q_idx, wl.hadamard, wl.index_fmt, rope=self.q_rope())
         qhat = O.index_dequant(qc, qs, wl.index_fmt)
         n = self.row_len
         khat = self.ipool.rows(np.arange(n))
         logits = O.indexer_logits(qhat, self.w_idx, khat)
-        dq = Q.band_delta(Q.exact_rotated(self.q_idx, wl.hadamard),
-                          Q.rotation_error_bound(self.q_idx, wl.index_dim), wl.index_fmt)
+        dq = Q.band_delta(Q.exact_rotated(self.q_idx, wl.hadamard, rope=self.q_rope()),
+                          Q.rotation_error_bound(self.q_idx, wl.index_dim, rope=bool(wl.rope_dim)),
+                          wl.index_fmt)
         return logits, Q.logit_slack(qhat, dq, self.w_idx, khat, self.dk[:n])
 
     def oracle_query(self):
@@ -114,7 +139,7 @@ class SeqState:
         preparation, logits of every visible entry, top-512, attention over the
         selection and the window. (logits, selected j, out [H, 512])."""
         wl = self.wl
-        qc, qs = O.index_prep(self.q_idx, wl.hadamard, wl.index_fmt)
+        qc, qs = O.index_prep(self.q_idx, wl.hadamard, wl.index_fmt, rope=self.q_rope())
         qhat = O.index_dequant(qc, qs, wl.index_fmt)
         return O.csa_query(qhat, self.w_idx, self.ipool, self.c4, self.raw,
                            identity_pages(self.n_entries, 64), self.raw_map(), self.row_len, self.p,
@@ -166,8 +191,9 @@ def decode_seq(W, b: int, bands: bool = True) -> SeqState:
         return rows
 
     raw_pos0, raw_rows = decode_raw_tail(W, b, stepped=True)
+    k_rope = ([N - 1], [L - 1]) if last is not None else None
     return SeqState(wl, kraw, kv_fn, raw_pos0, raw_rows, host(W.q_idx)[b], host(W.w_idx)[b],
-                    host(W.q_attn)[b], L - 1, N, bands=bands)
+                    host(W.q_attn)[b], L - 1, N, bands=bands, k_rope=k_rope)
 
 
 def spec_decode_row(W, t: int, bands: bool = True) -> SeqState:
@@ -186,6 +212,7 @@ def spec_decode_row(W, t: int, bands: bool = True) -> SeqState:
     st.raw = O.KVPool(*O.quant_kv_entries(st._raw_rows, W.wl.kv_fmt), W.wl.kv_fmt)
     st.q_idx, st.w_idx, st.q_attn = host(W.q_idx)[t], host(W.w_idx)[t], host(W.q_attn)[t]
     st.p, st.row_len = int(W.pos_host[t]), int(W.rows_len_host[t])
+    st.q_pos = st.p
     return st
 
 
@@ -241,8 +268,10 @@ def prefill_row(W, t: int, bands: bool = True) -> SeqState:
 
     xt = host(gen.device_normal((256, 576), W.seed + 3))  # positions ctx - 256 .. ctx - 1
     raw_rows = np.concatenate([xt, x_new[:t + 1]]).astype(np.float64)
+    new_rows = np.arange(e0, n_vis)
+    k_rope = (new_rows, 4 * new_rows + 3) if len(new_rows) else None
     return SeqState(wl, kraw, kv_fn, ctx - 256, raw_rows, host(W.q_idx[t]), host(W.w_idx[t]),
-                    host(W.q_attn[t]), pos, n_vis, bands=bands)
+                    host(W.q_attn[t]), pos, n_vis, bands=bands, k_rope=k_rope)
 
 
 def logical_of_phys(phys_row: np.ndarray, page_table_row: np.ndarray, page: int = 64) -> np.ndarray:

@@ -46,6 +46,14 @@ class KvPoolC(C.Structure):
                 ("fmt", C.c_int32), ("page_size", C.c_int32), ("num_pages", C.c_int64)]
 
 
+class RopeC(C.Structure):
+    _fields_ = [("pos", C.c_void_p), ("cos_sin", C.c_void_p), ("dim", C.c_int32),
+                ("rows_per_pos", C.c_int32)]
+
+
+NO_ROPE = RopeC(None, None, 0, 1)
+
+
 class IndexPoolC(C.Structure):
     _fields_ = [("data", C.c_void_p), ("scale", C.c_void_p), ("fmt", C.c_int32),
                 ("dim", C.c_int32), ("page_size", C.c_int32), ("num_pages", C.c_int64)]
@@ -96,28 +104,43 @@ def test_decode_prep_rejects_bad_arguments(lib):
     f = lib.csa_decode_prep
     f.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                   C.c_void_p, C.c_int32, KvPoolC, C.c_void_p, C.c_int32, KvPoolC, C.c_void_p,
-                  C.c_void_p, C.c_int32, C.c_int32, C.c_uint32, IndexPoolC, C.c_void_p,
+                  C.c_void_p, C.c_int32, C.c_int32, C.c_uint32, RopeC, IndexPoolC, C.c_void_p,
                   C.c_void_p, C.c_void_p]
     c4 = KvPoolC(FAKE, FAKE, FAKE, 2, 64, 10)
     raw = KvPoolC(FAKE, FAKE, FAKE, 2, 256, 10)
     kp = IndexPoolC(FAKE, FAKE, 2, 128, 64, 10)
 
     def call(x=FAKE, x_fmt=1, B=2, ratio=4, c4p=c4, rawp=raw, k=FAKE, q=FAKE, kq_fmt=1, H_I=64,
-             flags=1, kpool=kp, q_out=FAKE, q_sc=FAKE):
+             flags=1, rope=NO_ROPE, kpool=kp, q_out=FAKE, q_sc=FAKE):
         return f(x, x_fmt, FAKE, B, ratio, FAKE, FAKE, FAKE, 8, c4p, FAKE, 4, rawp, k, q, kq_fmt,
-                 H_I, flags, kpool, q_out, q_sc, None)
+                 H_I, flags, rope, kpool, q_out, q_sc, None)
 
     assert call(ratio=0) == INVALID
     assert call(ratio=129) == INVALID
     assert call(x_fmt=2) == INVALID                                    # x must be bf16 / f32
     assert call(rawp=KvPoolC(FAKE, FAKE, FAKE, 0, 256, 10)) == INVALID  # c4 FP8, raw F32
-    assert call(flags=2) == INVALID                                    # only the Hadamard flag
+    assert call(flags=2) == INVALID                                    # Hadamard / rope flags only
+    assert call(flags=5) == INVALID                                    # rope without a table
+    assert call(flags=5, rope=RopeC(None, FAKE, 63, 1)) == INVALID     # odd rope dim
+    assert call(flags=5, rope=RopeC(None, FAKE, 130, 1)) == INVALID    # rope dim > row dim
     assert call(kpool=IndexPoolC(FAKE, FAKE, 2, 96, 64, 10)) == INVALID  # dim 96
     assert call(kpool=IndexPoolC(FAKE, FAKE, 2, 128, 32, 10)) == INVALID  # page size != c4's
     assert call(q_out=None) == INVALID                                 # q rows without an output
     assert call(kq_fmt=2) == INVALID                                   # k / q rows must be raw
     assert call(x=None) == INVALID
     assert call(B=0) == 0                                              # nothing to do
+
+
+def test_index_prep_rejects_bad_arguments(lib):
+    f = lib.csa_index_prep
+    f.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_uint32, C.c_int32, C.c_void_p,
+                  C.c_void_p, C.c_void_p, RopeC, C.c_void_p]
+    ok_rope = RopeC(FAKE, FAKE, 64, 64)
+    assert f(FAKE, 1, 10, 128, 5, 2, FAKE, FAKE, None, NO_ROPE, None) == INVALID     # rope, no table
+    assert f(FAKE, 1, 10, 128, 5, 2, FAKE, FAKE, None, RopeC(FAKE, FAKE, 64, 0), None) == INVALID
+    assert f(FAKE, 1, 10, 64, 5, 2, FAKE, FAKE, None, RopeC(FAKE, FAKE, 66, 1), None) == INVALID
+    assert f(FAKE, 1, 10, 128, 8, 2, FAKE, FAKE, None, ok_rope, None) == INVALID       # unknown flag
+    assert f(FAKE, 1, 0, 128, 5, 2, FAKE, FAKE, None, ok_rope, None) == 0              # no rows
 
 
 def test_indexer_rejects_bad_arguments(lib):

@@ -70,7 +70,12 @@ def _check_step_writes(W, b, label):
     ok, msg = Q.bf16_match(rope, c[0, 512:], cerr[512:])
     assert ok, f"{label}: compressed RoPE dims: {msg}"
     k = F.host(W.k_new)[b:b + 1]
-    ke, kerr = Q.exact_rotated(k, W.wl.hadamard), Q.rotation_error_bound(k, W.wl.index_dim)
+    rope = None
+    if W.wl.rope_dim:  # the block's index-K row is rotated at the completing token's position
+        cos, sin = F.rope_cs([L - 1], W.wl.rope_dim)
+        rope = (cos, sin, W.wl.rope_dim)
+    ke = Q.exact_rotated(k, W.wl.hadamard, rope=rope)
+    kerr = Q.rotation_error_bound(k, W.wl.index_dim, rope=bool(W.wl.rope_dim))
     idx = W.index_pools[0]
     g_codes = idx.data.view(-1, idx.data.shape[-1])[slot].cpu().numpy()[None]
     g_scale = idx.scale.view(idx.data.view(-1, idx.data.shape[-1]).shape[0], -1)[slot].cpu().numpy()

@@ -63,6 +63,54 @@ def test_index_prep_mxfp4_hadamard(csa, rows):
     assert ok, msg
 
 
+def _rope_table(max_pos, rope_dim):
+    """The caller's cos/sin table (float32 [max_pos, rope_dim/2, 2]) of the
+    textbook RoPE angles, from the oracle's definition."""
+    cos, sin = O.rope_cos_sin(np.arange(max_pos), rope_dim)
+    return np.stack([cos, sin], axis=-1).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt,hadamard", [("fp8", True), ("mxfp4", True), ("f32", True),
+                                          ("f32", False)])
+def test_index_prep_rope(csa, fmt, hadamard):
+    """rope -> hadamard -> quant of query-shaped rows [T][64][128] (64 rows per
+    position) against the oracle's exact rotation of the same rows with the
+    same table values, within the float32 evaluation band."""
+    g = gen.rng(150 + len(fmt) + hadamard)
+    T, H, D, rd = 7, 64, 128, 64
+    pos = np.array([0, 1, 5, 4095, 65536, 131071, 140000 - 1], np.int32)
+    table = _rope_table(140000, rd)
+    v, vh = _bf16(gen.normal(g, (T * H, D)))
+    out = torch.full((T * H, D // 2 if fmt == "mxfp4" else D), 0xAB, dtype=torch.uint8, device=DEV)
+    if fmt == "f32":
+        out = torch.full((T * H, D), float("nan"), dtype=torch.float32, device=DEV)
+        sc = None
+    elif fmt == "fp8":
+        sc = torch.empty(T * H, dtype=torch.float32, device=DEV)
+    else:
+        sc = torch.empty((T * H, D // 32), dtype=torch.uint8, device=DEV)
+    flags = csa.CSA_PREP_ROPE | (csa.CSA_PREP_HADAMARD if hadamard else 0)
+    ofmt = {"fp8": csa.CSA_FP8_E4M3, "mxfp4": csa.CSA_MXFP4, "f32": csa.CSA_F32}[fmt]
+    csa.csa_index_prep(v, D, flags, ofmt, out, sc, rope_pos=t_dev(pos), rope_table=t_dev(table),
+                       rows_per_pos=H)
+    cs = table[np.repeat(pos, H)].astype(np.float64)
+    rope = (cs[..., 0], cs[..., 1], rd)
+    exact = Q.exact_rotated(vh, hadamard, rope=rope)
+    err = Q.rotation_error_bound(vh, D, rope=True) if hadamard else 2.0 ** -22 * np.abs(vh).sum(axis=1)
+    if fmt == "fp8":
+        ok, msg, _ = Q.fp8_rows_match(out.cpu().numpy(), sc.cpu().numpy(), exact, err)
+    elif fmt == "mxfp4":
+        ok, msg, _ = Q.mxfp4_rows_match(out.cpu().numpy(), sc.cpu().numpy(), exact, err)
+    else:
+        got = out.cpu().numpy()
+        ok = bool(np.all(np.abs(got - exact) <= err[:, None] + 2.0 ** -24 * np.abs(exact)))
+        msg = f"max deviation {np.abs(got - exact).max()}"
+        # the first D - rope_dim dims of an unrotated row are untouched
+        if not hadamard:
+            ok = ok and np.array_equal(got[:, :D - rd], vh[:, :D - rd])
+    assert ok, msg
+
+
 def test_index_prep_f32_dst_rows(csa):
     """Rows go to dst_rows[i]; a negative destination skips the row."""
     g = gen.rng(300)
@@ -622,8 +670,9 @@ def test_indexer_rows_per_seq(csa, fmt, q_len):
 # ------------------------------------------------------------------ fused decode preparation
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-def test_decode_prep(csa, fmt):
+@pytest.mark.parametrize("fmt,with_rope", [("fp8", False), ("mxfp4", False), ("fp8", True),
+                                           ("mxfp4", True)])
+def test_decode_prep(csa, fmt, with_rope):
     """csa_decode_prep against the oracle: the block a token completes (and only
     then) is compressed into the C4 pool and its index-K row prepared into the
     index pool; the token is stored in the raw pool; the query rows are
@@ -650,8 +699,18 @@ def test_decode_prep(csa, fmt):
     else:
         q_out = torch.empty((B, H_I, 64), dtype=torch.uint8, device=DEV)
         q_sc = torch.empty((B, H_I, 4), dtype=torch.uint8, device=DEV)
+    table = _rope_table(int(lens.max()), 64) if with_rope else None
+    flags = csa.CSA_PREP_HADAMARD | (csa.CSA_PREP_ROPE if with_rope else 0)
     csa.csa_decode_prep(x, t_dev(pos), t_dev(w), t_dev(b), t_dev(pt), c4, t_dev(pt), raw,
-                        k_rows=k, q_rows=q, kpool=kpool, q_out=q_out, q_out_scale=q_sc)
+                        k_rows=k, q_rows=q, kpool=kpool, q_out=q_out, q_out_scale=q_sc, flags=flags,
+                        rope_table=None if table is None else t_dev(table))
+
+    def rope_of(p, n):
+        """The oracle's rope argument for n rows at position p (or None)."""
+        if table is None:
+            return None
+        cs = np.repeat(table[p][None].astype(np.float64), n, axis=0)
+        return (cs[..., 0], cs[..., 1], 64)
     torch.cuda.synchronize()
     lat = c4.latent.cpu().numpy().reshape(-1, 512)
     sc = c4.scale.cpu().numpy().reshape(-1)
@@ -672,7 +731,8 @@ def test_decode_prep(csa, fmt):
         assert ok, f"sequence {s}: compressed latent: {msg}"
         ok, msg = Q.bf16_match(rope[slot], c[0, 512:], err[512:])
         assert ok, f"sequence {s}: compressed RoPE dims: {msg}"
-        ke, kerr = Q.exact_rotated(kh[s:s + 1], True), Q.rotation_error_bound(kh[s:s + 1], 128)
+        ke = Q.exact_rotated(kh[s:s + 1], True, rope=rope_of(int(pos[s]), 1))
+        kerr = Q.rotation_error_bound(kh[s:s + 1], 128, rope=with_rope)
         if fmt == "fp8":
             ok, msg, _ = Q.fp8_rows_match(kd[slot][None], ks[slot].view(np.float32), ke, kerr)
         else:
@@ -693,6 +753,10 @@ def test_decode_prep(csa, fmt):
     # the prepared query rows
     qr = qh.reshape(-1, 128)
     match = Q.fp8_rows_match if fmt == "fp8" else Q.mxfp4_rows_match
+    qrope = None
+    if table is not None:
+        cs = table[np.repeat(pos, H_I)].astype(np.float64)
+        qrope = (cs[..., 0], cs[..., 1], 64)
     ok, msg, _ = match(q_out.cpu().numpy().reshape(B * H_I, -1), q_sc.cpu().numpy().reshape(B * H_I, -1),
-                       Q.exact_rotated(qr, True), Q.rotation_error_bound(qr, 128))
+                       Q.exact_rotated(qr, True, rope=qrope), Q.rotation_error_bound(qr, 128, rope=with_rope))
     assert ok, f"query rows: {msg}"

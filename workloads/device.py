@@ -122,6 +122,13 @@ class CsaDecode:
             self.q_scale = torch.empty((B, wl.index_heads, wl.index_dim // 32), dtype=torch.uint8, device=DEV)
         self.fmt = fmt
         self.maxN = int(self.N.max())
+        # the caller's RoPE table over every position of the batch (the step's
+        # index-K row and queries are rotated at the token's position)
+        self.rope_table = None
+        self.prep_flags = csa.CSA_PREP_HADAMARD if wl.hadamard else 0
+        if wl.rope_dim:
+            self.rope_table = torch.from_numpy(gen.rope_table(int(self.lens.max()), wl.rope_dim)).to(DEV)
+            self.prep_flags |= csa.CSA_PREP_ROPE
         self.logits = torch.empty((B, self.maxN), dtype=torch.float32, device=DEV)
         self.row_seq = _i32(np.arange(B))
         self.row_len = _i32(self.N)
@@ -197,10 +204,12 @@ class CsaDecode:
             csa.csa_decode_prep(self.x_new.view(self.B, 4, 576), self.q_pos, self.gate_w,
                                 self.gate_b, self.pt, kv, self.pt, self.raw, k_rows=self.k_new,
                                 q_rows=self.q_idx, kpool=idx, q_out=self.q_codes,
-                                q_out_scale=self.q_scale, flags=csa.CSA_PREP_HADAMARD)
+                                q_out_scale=self.q_scale, flags=self.prep_flags,
+                                rope_table=self.rope_table)
         else:
-            csa.csa_index_prep(self.q_idx, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt,
-                               self.q_codes, self.q_scale)
+            csa.csa_index_prep(self.q_idx, wl.index_dim, self.prep_flags, self.fmt,
+                               self.q_codes, self.q_scale, rope_pos=self.q_pos,
+                               rope_table=self.rope_table, rows_per_pos=wl.index_heads)
         if ev is not None:
             ev[0].record()
         # indexer + top-512 in one call: the scan workgroups select their
@@ -303,11 +312,12 @@ class CsaSpecDecode(CsaDecode):
         # the last token's raw row, then the three earlier raw rows
         csa.csa_decode_prep(self.x_new.view(self.B, 4, 576), self.last_pos, self.gate_w, self.gate_b,
                             self.pt, kv, self.pt, self.raw, k_rows=self.k_new, kpool=idx,
-                            flags=csa.CSA_PREP_HADAMARD)
+                            flags=self.prep_flags, rope_table=self.rope_table)
         csa.c4_compress(self.x_early, self.early_cu, self.early_start, 3, 1, self.zero_w, self.zero_b,
                         self.pt, self.raw)
-        csa.csa_index_prep(self.q_idx, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt, self.q_codes,
-                           self.q_scale)
+        csa.csa_index_prep(self.q_idx, wl.index_dim, self.prep_flags, self.fmt, self.q_codes,
+                           self.q_scale, rope_pos=self.q_pos, rope_table=self.rope_table,
+                           rows_per_pos=wl.index_heads)
         if ev is not None:
             ev[0].record()
         # the hint routes each sequence's four rows to one page walk
@@ -360,6 +370,14 @@ class CsaPrefill:
         self.k_new = gen.device_normal((nk, wl.index_dim), seed + 5)
         ent = np.arange(ctx // 4, ctx // 4 + nk)
         self.k_dst = _i32(pt[0, ent // C4_PAGE] * C4_PAGE + ent % C4_PAGE)
+        # RoPE: entry k's index-K row at the position that completes its block
+        # (4k + 3), each query at its own position
+        self.k_pos = _i32(4 * ent + 3)
+        self.prep_flags = csa.CSA_PREP_HADAMARD if wl.hadamard else 0
+        self.rope_table = None
+        if wl.rope_dim:
+            self.rope_table = torch.from_numpy(gen.rope_table(L, wl.rope_dim)).to(DEV)
+            self.prep_flags |= csa.CSA_PREP_ROPE
         self.q_idx = gen.device_normal((new, wl.index_heads, wl.index_dim), seed + 6)
         self.w_idx = gen.device_uniform((new, wl.index_heads), seed + 7)
         self.q_attn = gen.device_normal((new, wl.heads, 576), seed + 8)
@@ -392,9 +410,11 @@ class CsaPrefill:
                         self.zero_b, self.pt, self.raw)
         kd = self.idx.data.view(-1, self.idx.data.shape[-1])
         ks = self.idx.scale.view(kd.shape[0], -1)
-        csa.csa_index_prep(self.k_new, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt, kd, ks, self.k_dst)
-        csa.csa_index_prep(self.q_idx, wl.index_dim, csa.CSA_PREP_HADAMARD, self.fmt, self.q_codes,
-                           self.q_scale)
+        csa.csa_index_prep(self.k_new, wl.index_dim, self.prep_flags, self.fmt, kd, ks, self.k_dst,
+                           rope_pos=self.k_pos, rope_table=self.rope_table, rows_per_pos=1)
+        csa.csa_index_prep(self.q_idx, wl.index_dim, self.prep_flags, self.fmt, self.q_codes,
+                           self.q_scale, rope_pos=self.q_pos, rope_table=self.rope_table,
+                           rows_per_pos=wl.index_heads)
         if ev is not None:
             ev[0].record()
         csa.indexer_score(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.N, self.pt,

@@ -79,3 +79,27 @@ def device_uniform(shape, seed: int, device="cuda"):
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     return torch.rand(shape, generator=gen, device=device, dtype=torch.float32)
+
+
+def rope_rows(positions, rope_dim: int, theta: float = 10000.0) -> np.ndarray:
+    """Rows of the rotary-embedding table at the given positions, float32
+    [len(positions), rope_dim/2, 2]: (cos, sin) of the angle p * theta^(-2i/rope_dim)
+    of pair i at position p, evaluated in float64, stored as float32."""
+    i = np.arange(rope_dim // 2, dtype=np.float64)
+    inv = theta ** (-2.0 * i / rope_dim)
+    ang = np.asarray(positions, dtype=np.float64).reshape(-1)[:, None] * inv[None, :]
+    out = np.empty(ang.shape + (2,), dtype=np.float32)
+    out[..., 0] = np.cos(ang)
+    out[..., 1] = np.sin(ang)
+    return out
+
+
+def rope_table(max_pos: int, rope_dim: int, theta: float = 10000.0) -> np.ndarray:
+    """The caller's rotary-embedding table, float32 [max_pos, rope_dim/2, 2],
+    rows 0 .. max_pos - 1 of rope_rows (the textbook RoPE table; an input of
+    the indexer preparation, like the head weights)."""
+    out = np.empty((max_pos, rope_dim // 2, 2), dtype=np.float32)
+    step = 1 << 16
+    for p0 in range(0, max_pos, step):
+        out[p0:p0 + step] = rope_rows(np.arange(p0, min(max_pos, p0 + step)), rope_dim, theta)
+    return out

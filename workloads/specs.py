@@ -37,6 +37,7 @@ class Workload:
     hca_ratio: int = 0             # > 0: an HCA layer runs beside the CSA layer
     ragged: tuple = field(default=())  # (n_seqs, lo, hi) for log-uniform raw lengths
     q_len: int = 1                 # query tokens per sequence and step (multi-token decode)
+    rope_dim: int = 0              # > 0: the step's indexer q / K rows get RoPE on their last rope_dim dims
     window: int = WINDOW
     softmax_scale: float = KV_DIM ** -0.5
 
@@ -49,27 +50,27 @@ TINY_FP32_DECODE = Workload(
 DECODE_128K = Workload(
     name="csa_decode_128k_b32", seed=1002, batch=32, seq_len=131072, kv_fmt="fp8",
     index_fmt="fp8", index_heads=64, index_dim=128, hadamard=True, heads=64,
-    q_dtype="bf16", out_dtype="bf16", pool_pages=16384)
+    q_dtype="bf16", out_dtype="bf16", pool_pages=16384, rope_dim=64)
 
 DECODE_1M = Workload(
     name="csa_decode_1m_b4", seed=1003, batch=4, seq_len=1048576, kv_fmt="fp8",
     index_fmt="mxfp4", index_heads=64, index_dim=128, hadamard=True, heads=128,
-    q_dtype="bf16", out_dtype="bf16", pool_pages=16384)
+    q_dtype="bf16", out_dtype="bf16", pool_pages=16384, rope_dim=64)
 
 SPEC_DECODE_128K = Workload(
     name="csa_spec_decode_128k_b32_q4", seed=1006, batch=32, seq_len=131072, kv_fmt="fp8",
     index_fmt="fp8", index_heads=64, index_dim=128, hadamard=True, heads=64,
-    q_dtype="bf16", out_dtype="bf16", pool_pages=16384, q_len=4)
+    q_dtype="bf16", out_dtype="bf16", pool_pages=16384, q_len=4, rope_dim=64)
 
 PREFILL_4K = Workload(
     name="csa_prefill_4096_on_128k", seed=1004, batch=1, seq_len=131072 + 4096, kv_fmt="fp8",
     index_fmt="fp8", index_heads=64, index_dim=128, hadamard=True, heads=64,
-    q_dtype="bf16", out_dtype="bf16", new_tokens=4096)
+    q_dtype="bf16", out_dtype="bf16", new_tokens=4096, rope_dim=64)
 
 HCA_RAGGED = Workload(
     name="hca_csa_ragged_b16", seed=1005, batch=16, seq_len=None, kv_fmt="fp8",
     index_fmt="fp8", index_heads=64, index_dim=128, hadamard=True, heads=64,
-    q_dtype="bf16", out_dtype="bf16", hca_ratio=128, ragged=(16, 8192, 1048576))
+    q_dtype="bf16", out_dtype="bf16", hca_ratio=128, ragged=(16, 8192, 1048576), rope_dim=64)
 
 ALL = (TINY_FP32_DECODE, DECODE_128K, DECODE_1M, SPEC_DECODE_128K, PREFILL_4K, HCA_RAGGED)
 BY_NAME = {w.name: w for w in ALL}
