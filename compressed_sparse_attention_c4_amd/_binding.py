@@ -26,9 +26,10 @@ def CSA_ROWS_PER_SEQ(n: int) -> int:
     """The rows-per-sequence hint bits of an indexer call's `prep` flags."""
     return (int(n) & 0xFF) << 8
 (CSA_OP_INDEXER, CSA_OP_TOPK, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN, CSA_OP_INDEXER_TOPK,
- CSA_OP_CSA_ATTN_F32, CSA_OP_HCA_ATTN_F32) = range(7)
+ CSA_OP_CSA_ATTN_F32, CSA_OP_HCA_ATTN_F32, CSA_OP_TOPK_K) = range(8)
 CSA_TOPK, CSA_C4_RATIO, CSA_HCA_RATIO, CSA_RAW_PAGE, CSA_C4_PAGE = 512, 4, 128, 256, 64
 CSA_NOALLOC_SCRATCH_BYTES = 32 << 20
+CSA_TOPK_MAX = 2048
 
 
 class _KvPoolC(C.Structure):
@@ -77,6 +78,8 @@ _indexer_topk = _decl("indexer_topk512", [_vp, _i32, _vp, _u32, _vp, _i32, _i32,
 _indexer_topk_na = _decl("indexer_topk512_noalloc", [_vp, _i32, _vp, _u32, _vp, _i32, _i32, _i32, _vp,
                                                      _vp, _i32, _vp, _i32, _IndexPoolC, _vp, _vp, _vp,
                                                      _vp, _vp])
+_topk_k = _decl("topk_page_select", [_vp, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp,
+                                     _sz, _vp])
 _topk = _decl("topk512_page_select", [_vp, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
 _csa_attn = _decl("csa_sparse_attn", [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _KvPoolC, _KvPoolC,
                                       _vp, _i32, _i32, _f32, _vp, _i32, _vp, _sz, _vp])
@@ -275,6 +278,20 @@ def topk512_page_select(logits, row_len, row_seq, page_table, phys_idx, logical_
     _check("topk512_page_select", _topk(
         _ptr(logits), ld, R, _ptr(row_len), _ptr(row_seq), _ptr(page_table),
         page_table.shape[-1], int(c4_page_size), _ptr(phys_idx), _ptr(logical_idx), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def topk_page_select(logits, row_len, row_seq, page_table, k, phys_idx, logical_idx=None,
+                     page_size=CSA_C4_PAGE, ws=None, stream=None):
+    """The generic top-k (1 <= k <= 2048) with page translation; phys_idx /
+    logical_idx are [R, k] int32."""
+    R = row_len.numel()
+    ld = logits.shape[-1]
+    if ws is None:
+        ws = _scratch(csa_workspace_size(CSA_OP_TOPK_K, R, ld, int(k)), logits.device, stream)
+    _check("topk_page_select", _topk_k(
+        _ptr(logits), ld, R, _ptr(row_len), _ptr(row_seq), _ptr(page_table), page_table.shape[-1],
+        int(page_size), int(k), _ptr(phys_idx), _ptr(logical_idx), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
 
 

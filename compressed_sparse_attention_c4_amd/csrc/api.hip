@@ -79,7 +79,7 @@ IdxTopkWs idx_topk_ws(int64_t T, int64_t max_row_len, int H_I) {
   w.merged = align256((size_t)T * kCandGroups * CSA_TOPK * sizeof(uint32_t));
   w.ld = std::max<int64_t>(64, (max_row_len + 63) / 64 * 64);
   w.logits = align256((size_t)T * w.ld * sizeof(float));
-  w.topk = align256(topk_ws_bytes(T, w.ld));
+  w.topk = align256(topk_ws_bytes(T, w.ld, CSA_TOPK));
   w.total = w.prep + std::max(3 * (w.cand + w.merged), w.logits + w.topk);
   return w;
 }
@@ -111,7 +111,9 @@ size_t csa_workspace_size(int32_t op, int64_t rows, int64_t max_len, int32_t hea
   if (rows < 0 || max_len < 0 || heads <= 0) return 0;
   switch (op) {
     case CSA_OP_INDEXER: return indexer_ws_bytes(rows, heads);
-    case CSA_OP_TOPK: return topk_ws_bytes(rows, max_len);  // max_len = ld
+    case CSA_OP_TOPK: return topk_ws_bytes(rows, max_len, CSA_TOPK);  // max_len = ld
+    case CSA_OP_TOPK_K:  // max_len = ld, heads = k
+      return heads <= CSA_TOPK_MAX ? topk_ws_bytes(rows, max_len, heads) : 0;
     case CSA_OP_CSA_ATTN:
     case CSA_OP_HCA_ATTN: return attention_ws_bytes(rows, max_len, heads);
     case CSA_OP_CSA_ATTN_F32:
@@ -206,19 +208,28 @@ csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint
                                    q_used_scale, ws, stream));
 }
 
+csa_status topk_page_select(const float* logits, int64_t ld, int32_t R, const int32_t* row_len,
+                            const int32_t* row_seq, const int32_t* page_table, int32_t pt_stride,
+                            int32_t page_size, int32_t k, int32_t* phys_idx,
+                            int32_t* logical_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (R < 0 || ld < 0 || pt_stride <= 0 || page_size <= 0) return CSA_ERR_INVALID;
+  if (k < 1 || k > CSA_TOPK_MAX) return CSA_ERR_INVALID;
+  if (ld > topk_max_len(k)) return CSA_ERR_UNSUPPORTED;
+  if (R == 0) return CSA_OK;
+  if (!logits || !row_len || !row_seq || !page_table || !phys_idx) return CSA_ERR_INVALID;
+  const size_t need = topk_ws_bytes(R, ld, k);
+  if (need > ws_bytes || (need > 0 && !ws)) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_topk(logits, ld, R, row_len, row_seq, page_table, pt_stride, page_size,
+                                k, phys_idx, logical_idx, ws, stream));
+}
+
 csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
                                const int32_t* row_len, const int32_t* row_seq,
                                const int32_t* page_table, int32_t pt_stride,
                                int32_t c4_page_size, int32_t* phys_idx, int32_t* logical_idx,
                                void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (R < 0 || ld < 0 || pt_stride <= 0 || c4_page_size <= 0) return CSA_ERR_INVALID;
-  if (ld > topk_max_len()) return CSA_ERR_UNSUPPORTED;
-  if (R == 0) return CSA_OK;
-  if (!logits || !row_len || !row_seq || !page_table || !phys_idx) return CSA_ERR_INVALID;
-  const size_t need = topk_ws_bytes(R, ld);
-  if (need > ws_bytes || (need > 0 && !ws)) return CSA_ERR_WORKSPACE;
-  return hip_status(launch_topk(logits, ld, R, row_len, row_seq, page_table, pt_stride,
-                                c4_page_size, 0, phys_idx, logical_idx, ws, stream));
+  return topk_page_select(logits, ld, R, row_len, row_seq, page_table, pt_stride, c4_page_size,
+                          CSA_TOPK, phys_idx, logical_idx, ws, ws_bytes, stream);
 }
 
 }  // extern "C"
@@ -237,7 +248,7 @@ csa_status indexer_topk512_ws(const void* q, csa_fmt q_fmt, const void* q_scale,
   const csa_status st = indexer_args(q_fmt, q_scale, prep, T, H_I, D_I, max_row_len, pt_stride, k,
                                      q_used, q_used_scale, ws, ws_bytes);
   if (st != CSA_OK) return st;
-  if (max_row_len > topk_max_len()) return CSA_ERR_UNSUPPORTED;
+  if (max_row_len > topk_max_len(CSA_TOPK)) return CSA_ERR_UNSUPPORTED;
   if (T == 0) return CSA_OK;
   const IdxTopkWs L = idx_topk_ws(T, max_row_len, H_I);
   if (!ws || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
@@ -276,8 +287,8 @@ csa_status indexer_topk512_ws(const void* q, csa_fmt q_fmt, const void* q_scale,
                        page_table, pt_stride, k, logits, L.ld, q_used, q_used_scale, base, stream);
     if (e == hipSuccess && scan_done) e = hipEventRecord(scan_done, stream);
     if (e == hipSuccess)
-      e = launch_topk(logits, L.ld, T, row_len, row_seq, page_table, pt_stride, k.page_size, 0,
-                      phys_idx, logical_idx, base + L.prep + L.logits, stream);
+      e = launch_topk(logits, L.ld, T, row_len, row_seq, page_table, pt_stride, k.page_size,
+                      CSA_TOPK, phys_idx, logical_idx, base + L.prep + L.logits, stream);
   }
   return hip_status(e);
 }
@@ -330,7 +341,7 @@ csa_status indexer_topk512_noalloc(const void* q, csa_fmt q_fmt, const void* q_s
                                    int32_t* logical_idx, void* q_used, void* q_used_scale,
                                    hipStream_t stream) {
   if (T < 0 || max_row_len < 0 || H_I <= 0) return CSA_ERR_INVALID;
-  if (max_row_len > topk_max_len()) return CSA_ERR_UNSUPPORTED;
+  if (max_row_len > topk_max_len(CSA_TOPK)) return CSA_ERR_UNSUPPORTED;
   if (indexer_topk_ws_bytes(T, max_row_len, H_I) > kScratchBytes) return CSA_ERR_WORKSPACE;
   void* ws = scratch_for_current_device();
   if (!ws) return CSA_ERR_HIP;
@@ -340,7 +351,9 @@ csa_status indexer_topk512_noalloc(const void* q, csa_fmt q_fmt, const void* q_s
 }
 
 static csa_status attn_common(AttnArgs& a, hipStream_t stream) {
-  if (a.T < 0 || a.H <= 0 || a.window < 1 || a.window > 4096) return CSA_ERR_INVALID;
+  if (a.T < 0 || a.H <= 0 || a.window < 0 || a.window > 4096) return CSA_ERR_INVALID;
+  if (!a.hca && a.k_sel + a.window < 1) return CSA_ERR_INVALID;
+  if (a.hca && a.window < 1) return CSA_ERR_INVALID;
   if (!kv_pool_ok(a.comp) || !kv_pool_ok(a.raw) || a.comp.fmt != a.raw.fmt) return CSA_ERR_INVALID;
   if (a.raw_pt_stride <= 0) return CSA_ERR_INVALID;
   if (a.comp.fmt == CSA_F32) {
@@ -366,7 +379,7 @@ csa_status csa_sparse_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
                            const int32_t* raw_page_table, int32_t raw_pt_stride, int32_t window,
                            float softmax_scale, void* out, csa_fmt out_fmt, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
-  if (k_sel < 0 || k_sel > CSA_TOPK) return CSA_ERR_INVALID;
+  if (k_sel < 0 || k_sel > CSA_TOPK_MAX) return CSA_ERR_INVALID;
   if (k_sel > 0 && !phys_idx && T > 0) return CSA_ERR_INVALID;
   AttnArgs a{};
   a.q = q; a.q_fmt = q_fmt; a.T = T; a.H = H; a.q_seq = q_seq; a.q_pos = q_pos;

@@ -79,10 +79,12 @@ hipError_t launch_topk_cand_final(const uint32_t* ckeys, const int32_t* cjs, con
                                   const int32_t* page_table, int pt_stride, int c4_page_size,
                                   int32_t* phys_idx, int32_t* logical_idx, hipStream_t s);
 
+// Top-k (1 <= k <= 2048) of each row's logits, translated through the page
+// table; rows of phys_idx / logical_idx hold k entries.
 hipError_t launch_topk(const float* logits, int64_t ld, int R, const int32_t* row_len,
                        const int32_t* row_seq, const int32_t* page_table, int pt_stride,
-                       int c4_page_size, int max_row_len, int32_t* phys_idx,
-                       int32_t* logical_idx, void* ws, hipStream_t s);
+                       int c4_page_size, int k, int32_t* phys_idx, int32_t* logical_idx, void* ws,
+                       hipStream_t s);
 
 struct AttnArgs {
   const void* q;
@@ -112,8 +114,8 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 size_t attention_ws_bytes(int64_t T, int64_t max_entries, int H);
 size_t attention_f32_ws_bytes(int64_t T, int64_t max_entries, int H);
-size_t topk_ws_bytes(int64_t R, int64_t max_len);
-int64_t topk_max_len();
+size_t topk_ws_bytes(int64_t R, int64_t max_len, int k);
+int64_t topk_max_len(int k);
 size_t indexer_ws_bytes(int64_t T, int H_I);
 size_t indexer_topk_ws_bytes(int64_t T, int64_t max_row_len, int H_I);
 

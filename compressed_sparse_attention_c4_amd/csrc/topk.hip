@@ -43,6 +43,7 @@ namespace {
 constexpr int kThreads = 1024;             // workgroup of whole rows and of the final merge
 constexpr int kMaxE = 32;                    // keys per lane (held in registers)
 constexpr int kRegRow = kThreads * kMaxE;    // longest row selected in one launch
+constexpr int kTopkMaxK = 2048;              // largest k of the generic top-k
 
 // kCandMerge: a group of `chunk` consecutive candidates of a row (several
 // chunks' top-512 lists) reduced to its own top-512 list, candidates in and
@@ -51,16 +52,18 @@ constexpr int kRegRow = kThreads * kMaxE;    // longest row selected in one laun
 // input's order, so the final pass sees the candidates in index order.
 enum Mode { kRowFinal = 0, kChunkCand = 1, kCandFinal = 2, kCandMerge = 3 };
 
-template <int kMode, int kE, int TH>
+// ksel (<= kK) entries are selected per row; candidate lists and output rows
+// hold ksel entries each.
+template <int kMode, int kE, int TH, int kK>
 __global__ void __launch_bounds__(TH)
 topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __restrict__ ckeys,
             const int32_t* __restrict__ cjs, const int32_t* __restrict__ cphys, int ncand, int chunk,
             const int32_t* __restrict__ row_len, const int32_t* __restrict__ row_seq,
-            const int32_t* __restrict__ pt, int pt_stride, int c4_page_size,
+            const int32_t* __restrict__ pt, int pt_stride, int c4_page_size, int ksel,
             int32_t* __restrict__ phys_idx, int32_t* __restrict__ logical_idx,
             uint32_t* __restrict__ okeys, int32_t* __restrict__ ojs, int32_t* __restrict__ ophys) {
   static_assert(kE >= 1 && kE <= kMaxE, "keys per lane");
-  __shared__ TopkLds L;
+  __shared__ TopkLdsT<kK> L;
 
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -79,7 +82,7 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
   } else {
     n = ncand;
   }
-  const int K = min(kTopK, kMode == kCandFinal ? rl : n);  // entries to select
+  const int K = min(ksel, kMode == kCandFinal ? rl : n);  // entries to select
   const int seg = wave * 64 * kE;                          // first element of this wave
 
   // the histogram is cleared while the keys are in flight
@@ -105,14 +108,14 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
     }
   }
   topk_select<kE, TH>(kr, n, K, seg, L);
-  // ---- emission (positions K..511 are padding)
-  for (int p = threadIdx.x; p < kTopK; p += TH) {
+  // ---- emission (positions K..ksel-1 are padding)
+  for (int p = threadIdx.x; p < ksel; p += TH) {
     if (kMode == kChunkCand) {
-      const int64_t o = ((int64_t)r * gridDim.x + blockIdx.x) * kTopK + p;
+      const int64_t o = ((int64_t)r * gridDim.x + blockIdx.x) * ksel + p;
       okeys[o] = p < K ? L.out_k[p] : 0u;
       ojs[o] = p < K ? base + L.out_e[p] : INT_MAX;
     } else if (kMode == kCandMerge) {
-      const int64_t o = ((int64_t)r * gridDim.x + blockIdx.x) * kTopK + p;
+      const int64_t o = ((int64_t)r * gridDim.x + blockIdx.x) * ksel + p;
       uint32_t key = 0u;
       int32_t j = INT_MAX, ph = -1;
       if (p < K) {
@@ -136,8 +139,8 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
                                c4_page_size +
                            j % c4_page_size);
       }
-      phys_idx[(int64_t)r * kTopK + p] = phys;
-      if (logical_idx) logical_idx[(int64_t)r * kTopK + p] = j;
+      phys_idx[(int64_t)r * ksel + p] = phys;
+      if (logical_idx) logical_idx[(int64_t)r * ksel + p] = j;
     }
   }
 }
@@ -149,16 +152,34 @@ int keys_per_lane(int64_t n, int th) {
   return e;
 }
 
+// Launch of topk_kernel<kMode, e, th, kK> selecting ksel entries: kK = 512
+// for ksel <= 512 (any workgroup size), else kK = 2048 (1024 threads).
 template <int kMode>
 void launch_mode(int th, int e, dim3 grid, hipStream_t s, const float* logits, int64_t ld,
                  const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys, int ncand, int chunk,
                  const int32_t* row_len, const int32_t* row_seq, const int32_t* pt, int pt_stride,
                  int c4_page_size, int32_t* phys_idx, int32_t* logical_idx, uint32_t* okeys,
-                 int32_t* ojs, int32_t* ophys = nullptr) {
+                 int32_t* ojs, int32_t* ophys = nullptr, int ksel = kTopK) {
+  if (ksel > kTopK) {
+#define CSA_TOPK_LAUNCH_W(E)                                                                     \
+  hipLaunchKernelGGL((topk_kernel<kMode, E, kThreads, kTopkMaxK>), grid, dim3(kThreads), 0, s,   \
+                     logits, ld, ckeys, cjs, cphys, ncand, chunk, row_len, row_seq, pt,          \
+                     pt_stride, c4_page_size, ksel, phys_idx, logical_idx, okeys, ojs, ophys)
+    switch (e) {
+      case 1: CSA_TOPK_LAUNCH_W(1); break;
+      case 2: CSA_TOPK_LAUNCH_W(2); break;
+      case 4: CSA_TOPK_LAUNCH_W(4); break;
+      case 8: CSA_TOPK_LAUNCH_W(8); break;
+      case 16: CSA_TOPK_LAUNCH_W(16); break;
+      default: CSA_TOPK_LAUNCH_W(32); break;
+    }
+#undef CSA_TOPK_LAUNCH_W
+    return;
+  }
 #define CSA_TOPK_LAUNCH(E, TH)                                                             \
-  hipLaunchKernelGGL((topk_kernel<kMode, E, TH>), grid, dim3(TH), 0, s, logits, ld, ckeys,    \
-                     cjs, cphys, ncand, chunk, row_len, row_seq, pt, pt_stride, c4_page_size,  \
-                     phys_idx, logical_idx, okeys, ojs, ophys)
+  hipLaunchKernelGGL((topk_kernel<kMode, E, TH, kTopK>), grid, dim3(TH), 0, s, logits, ld,   \
+                     ckeys, cjs, cphys, ncand, chunk, row_len, row_seq, pt, pt_stride,        \
+                     c4_page_size, ksel, phys_idx, logical_idx, okeys, ojs, ophys)
 #define CSA_TOPK_E(TH)                       \
   switch (e) {                               \
     case 1: CSA_TOPK_LAUNCH(1, TH); break;   \
@@ -183,50 +204,54 @@ void launch_mode(int th, int e, dim3 grid, hipStream_t s, const float* logits, i
 // keys per lane (16 preferred: 32 costs spills at 1024 threads).
 //  - Whole rows, one 1024-thread workgroup each, when a row fits 16 keys per
 //    lane and either the rows alone fill the GPU (>= 128) or they are short.
-//  - Otherwise chunks of a row are reduced to their top-512 candidates and the
-//    candidates of a row are reduced again. With >= 128 rows the rows already
-//    fill the GPU: chunks of 256 x 16 keys go to 256-thread workgroups, several
-//    of which share a CU, so one workgroup's barrier waits overlap another's
-//    work. With fewer rows, ~128 workgroups of 1024 threads, each >= 4096 keys.
-//  - At most 64 chunks per row, so a row's candidates fit one final workgroup.
+//  - Otherwise chunks of a row are reduced to their top-k candidates and the
+//    candidates of a row are reduced again. With >= 128 rows (k = 512) the rows
+//    already fill the GPU: chunks of 256 x 16 keys go to 256-thread workgroups,
+//    several of which share a CU, so one workgroup's barrier waits overlap
+//    another's work. With fewer rows, ~128 workgroups of 1024 threads, each
+//    >= 4096 keys.
+//  - At most kRegRow / k chunks per row, so a row's candidates fit one final
+//    workgroup. Rows longer than that are not supported (topk_max_len).
+//  - k > 512 runs on 1024-thread workgroups only.
 struct TopkPlan {
   bool whole_rows;
   int chunks, chunk, chunk_th, final_th;
 };
 
-TopkPlan topk_plan(int64_t R, int64_t ld) {
+TopkPlan topk_plan(int64_t R, int64_t ld, int k) {
   TopkPlan p{false, 1, (int)ld, kThreads, kThreads};
   if (ld <= kRegRow / 2 && (R >= 128 || ld <= 8192)) {
     p.whole_rows = true;
     return p;
   }
+  const bool wide = k > kTopK;
   int64_t c;
-  if (R >= 128) {
+  if (R >= 128 && !wide) {
     c = 256 * 16;  // 16 keys per lane of a 256-thread workgroup
   } else {
     const int64_t want = (128 + R - 1) / R;
-    c = std::max<int64_t>((ld + want - 1) / want, 4096);
+    c = std::max<int64_t>((ld + want - 1) / want, std::max<int64_t>(4096, 2 * (int64_t)k));
     c = std::min<int64_t>(c, kRegRow / 2);
   }
   int64_t chunks = (ld + c - 1) / c;
-  if (chunks * kTopK > kRegRow) chunks = kRegRow / kTopK;
+  if (chunks * k > kRegRow) chunks = kRegRow / k;
   c = (ld + chunks - 1) / chunks;
   p.chunks = (int)((ld + c - 1) / c);
   p.chunk = (int)c;
-  p.chunk_th = (R >= 128 && c <= 256 * kMaxE) ? 256 : kThreads;
-  p.final_th = (R >= 128 && (int64_t)p.chunks * kTopK <= 256 * kMaxE) ? 256 : kThreads;
+  p.chunk_th = (R >= 128 && !wide && c <= 256 * kMaxE) ? 256 : kThreads;
+  p.final_th = (R >= 128 && !wide && (int64_t)p.chunks * k <= 256 * kMaxE) ? 256 : kThreads;
   return p;
 }
 
 }  // namespace
 
-size_t topk_ws_bytes(int64_t R, int64_t max_len) {
-  const TopkPlan p = topk_plan(R, max_len);
+size_t topk_ws_bytes(int64_t R, int64_t max_len, int k) {
+  const TopkPlan p = topk_plan(R, max_len, k);
   if (p.whole_rows) return 0;
-  return (size_t)R * p.chunks * kTopK * (sizeof(uint32_t) + sizeof(int32_t));
+  return (size_t)R * p.chunks * k * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
-int64_t topk_max_len() { return (int64_t)(kRegRow / kTopK) * kRegRow; }
+int64_t topk_max_len(int k) { return (int64_t)(kRegRow / k) * kRegRow; }
 
 hipError_t launch_topk_cand_merge(const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys,
                                   int ncand, int group, int R, const int32_t* row_len,
@@ -257,28 +282,27 @@ hipError_t launch_topk_cand_final(const uint32_t* ckeys, const int32_t* cjs, con
 
 hipError_t launch_topk(const float* logits, int64_t ld, int R, const int32_t* row_len,
                        const int32_t* row_seq, const int32_t* page_table, int pt_stride,
-                       int c4_page_size, int max_row_len, int32_t* phys_idx,
-                       int32_t* logical_idx, void* ws, hipStream_t s) {
-  (void)max_row_len;
+                       int c4_page_size, int k, int32_t* phys_idx, int32_t* logical_idx, void* ws,
+                       hipStream_t s) {
   if (R == 0) return hipSuccess;
-  const TopkPlan p = topk_plan(R, ld);
+  const TopkPlan p = topk_plan(R, ld, k);
   if (p.whole_rows) {
     launch_mode<kRowFinal>(kThreads, keys_per_lane(ld, kThreads), dim3(1, R), s, logits, ld,
                            nullptr, nullptr, nullptr, 0, 0, row_len, row_seq, page_table, pt_stride,
-                           c4_page_size, phys_idx, logical_idx, nullptr, nullptr);
+                           c4_page_size, phys_idx, logical_idx, nullptr, nullptr, nullptr, k);
     return hipGetLastError();
   }
-  const int ncand = p.chunks * kTopK;
+  const int ncand = p.chunks * k;
   uint32_t* ck = (uint32_t*)ws;
   int32_t* cj = (int32_t*)((uint8_t*)ws + (size_t)R * ncand * sizeof(uint32_t));
   launch_mode<kChunkCand>(p.chunk_th, keys_per_lane(p.chunk, p.chunk_th), dim3(p.chunks, R), s,
                           logits, ld, nullptr, nullptr, nullptr, 0, p.chunk, row_len, row_seq, page_table,
-                          pt_stride, c4_page_size, nullptr, nullptr, ck, cj);
+                          pt_stride, c4_page_size, nullptr, nullptr, ck, cj, nullptr, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch_mode<kCandFinal>(p.final_th, keys_per_lane(ncand, p.final_th), dim3(1, R), s, nullptr,
                           0, ck, cj, nullptr, ncand, 0, row_len, row_seq, page_table, pt_stride,
-                          c4_page_size, phys_idx, logical_idx, nullptr, nullptr);
+                          c4_page_size, phys_idx, logical_idx, nullptr, nullptr, nullptr, k);
   return hipGetLastError();
 }
 

@@ -14,17 +14,19 @@ constexpr int kTopkBins = 3072;     // >= 2049 buckets, multiple of every workgr
 constexpr int kTopkCandCap = 2048;  // threshold-bucket keys listed in LDS
 constexpr int kTopkMaxWaves = 16;   // largest workgroup: 1024 threads
 
-// LDS working set of one selection.
-struct TopkLds {
+// LDS working set of one selection of at most kK elements.
+template <int kK>
+struct TopkLdsT {
   uint32_t hist[kTopkBins];
   uint32_t red[2 * kTopkMaxWaves];
   uint32_t sel_bin, sel_above;
   uint32_t list_n;                 // length of the threshold bucket's list
   uint32_t thr, need;              // threshold of a short bucket
   uint32_t cand[kTopkCandCap];     // keys of the threshold bucket
-  int32_t out_e[kTopK];            // element placed at each output position
-  uint32_t out_k[kTopK];           // and its key
+  int32_t out_e[kK];               // element placed at each output position
+  uint32_t out_k[kK];              // and its key
 };
+using TopkLds = TopkLdsT<kTopK>;
 
 // Exclusive scan of one uint32 per wave (value taken from lane 0 of each
 // wave) over the workgroup's TH/64 waves; returns this wave's offset, sets total.
@@ -97,15 +99,15 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int nbins, uin
   __syncthreads();
 }
 
-// Selects the K largest of the n elements held in registers (element
+// Selects the K largest (K <= the Lds capacity) of the n elements held in registers (element
 // seg + 64 i + lane is key kr[i] of this lane; elements >= n hold key 0) and
 // parks them in L.out_e / L.out_k by output position, in ascending element
 // order. K <= n. Every thread of the TH-thread workgroup calls it; L.hist must
 // have been cleared by the workgroup before the call (the first barrier
 // inside orders the clear before any use). Ends with a barrier.
-template <int kE, int TH>
+template <int kE, int TH, class Lds>
 __device__ __forceinline__ void topk_select(const uint32_t (&kr)[kE], int n, int K, int seg,
-                                            TopkLds& L) {
+                                            Lds& L) {
   constexpr int kBins = kTopkBins;
   constexpr int kCandCap = kTopkCandCap;
   constexpr int kWaves = kTopkMaxWaves;

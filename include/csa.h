@@ -62,6 +62,7 @@ extern "C" {
 
 /* Fixed sizes of the method. */
 #define CSA_TOPK        512   /* [P1] §3.2: top-512 compressed entries per query   */
+#define CSA_TOPK_MAX    2048  /* largest k of topk_page_select (DSA-style top-k)   */
 #define CSA_C4_RATIO    4     /* [P1] §2.1: 4 raw tokens -> 1 compressed entry     */
 #define CSA_HCA_RATIO   128   /* [P2] HCA paragraph: about 128x compression        */
 #define CSA_RAW_PAGE    256   /* [P1] §2.2: page_size = 256 raw tokens            */
@@ -351,6 +352,24 @@ csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
                                hipStream_t stream);
 
 /*
+ * topk_page_select -- the generic top-k transform, k in [1, CSA_TOPK_MAX]: the
+ * selection DSA makes over raw tokens ([P1] §1: in DSA the indexer picks the
+ * top-k tokens and attention reads only their KV; §3.2 contrasts the fixed-k
+ * transform with a generic top-k; §2.2: DSA pages hold 64 tokens). Same rules
+ * as topk512_page_select with k in place of 512: per row the k largest logits
+ * among j < row_len[r] (larger first, equal logits by lower j, -0 == +0, NaN
+ * below -inf; all of them if row_len <= k), in ascending j, translated through
+ * the page table with `page_size` entries per page; rows of phys_idx /
+ * logical_idx hold k entries, the unused tail -1.
+ *   ws   csa_workspace_size(CSA_OP_TOPK_K, R, ld, k) bytes.
+ *   ld   up to (32768 / k) * 32768 (k = 2048: 524288), else CSA_ERR_UNSUPPORTED.
+ */
+csa_status topk_page_select(const float* logits, int64_t ld, int32_t R, const int32_t* row_len,
+                            const int32_t* row_seq, const int32_t* page_table, int32_t pt_stride,
+                            int32_t page_size, int32_t k, int32_t* phys_idx,
+                            int32_t* logical_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * csa_sparse_attn -- MLA-style sparse attention of each query over its selected
  * compressed entries plus a sliding window of raw tokens ([P1] §1: attention
  * reads the 512 selected compressed KV; [P2] CSA paragraph: a sliding-window
@@ -365,7 +384,12 @@ csa_status topk512_page_select(const float* logits, int64_t ld, int32_t R,
  *        CSA_F32 with F32 pools (any H; lists of up to 32768 entries). out [T][H][512] CSA_BF16 or CSA_F32
  *        (F32 pools: CSA_F32 only).
  *   c4 and raw pools must have the same fmt; raw.page_size is the raw page size.
- *   Requires 1 <= window <= 4096 and 0 <= k_sel <= 512.
+ *   Requires 0 <= window <= 4096, 0 <= k_sel <= CSA_TOPK_MAX and
+ *   k_sel + window >= 1. k_sel up to 2048 with window 0 is the DSA mode: the
+ *   selection is over raw tokens (topk_page_select over an index pool of raw
+ *   tokens), `c4` is then the raw KV pool, and no window is added ([P1] §1,
+ *   DSA: attention reads the k selected raw tokens). A query must have at
+ *   least one entry (a selected entry or a window token).
  *   ws   workspace of csa_workspace_size(CSA_OP_CSA_ATTN, T, k_sel + window, H)
  *        bytes for FP8 pools, CSA_OP_CSA_ATTN_F32 for F32 pools (may be 0
  *        bytes / NULL when that size is 0).
@@ -404,7 +428,8 @@ csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
  *     CSA_OP_CSA_ATTN / CSA_OP_HCA_ATTN (rows = T, max_len = most entries of
  *     one query's list, heads = H; FP8 pools), CSA_OP_CSA_ATTN_F32 /
  *     CSA_OP_HCA_ATTN_F32 (the same for F32 pools), CSA_OP_INDEXER_TOPK
- *     (rows = T, max_len = max_row_len, heads = H_I). */
+ *     (rows = T, max_len = max_row_len, heads = H_I), CSA_OP_TOPK_K
+ *     (topk_page_select: rows = R, max_len = ld, heads = k). */
 #define CSA_OP_INDEXER  0
 #define CSA_OP_TOPK     1
 #define CSA_OP_CSA_ATTN 2
@@ -412,6 +437,7 @@ csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
 #define CSA_OP_INDEXER_TOPK 4
 #define CSA_OP_CSA_ATTN_F32 5
 #define CSA_OP_HCA_ATTN_F32 6
+#define CSA_OP_TOPK_K       7
 size_t csa_workspace_size(int32_t op, int64_t rows, int64_t max_len, int32_t heads);
 
 const char* csa_status_string(csa_status s);

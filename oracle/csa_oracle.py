@@ -480,3 +480,18 @@ def hca_query(hca_pool: KVPool, raw_pool: KVPool, hca_page_table_row, raw_page_t
     hca_rows = hca_pool.rows(page_slot(hca_page_table_row, np.arange(n), hca_page_size))
     raw_rows = raw_pool.rows(page_slot(raw_page_table_row, window_positions(p, window), raw_page_size))
     return csa_attention_query(q_attn, hca_rows, raw_rows, softmax_scale)
+
+
+def dsa_query(q_idx_hat, w, index_pool: IndexPool, kv_pool: KVPool, page_table_row, p: int,
+              q_attn, k: int, softmax_scale: float, page_size: int = 64):
+    """One query of the DSA step, the ratio-1 mode ([P1] §1: in DSA the indexer
+    scores the raw tokens, keeps the top-k and attention reads only their KV;
+    §2.2: DSA pages hold 64 tokens). The query at raw position p sees tokens
+    j <= p; there is no separate window (the recent tokens compete in the
+    top-k like the rest). Returns (logits [p + 1], selected j, out [H, 512])."""
+    n = p + 1
+    slots = page_slot(page_table_row, np.arange(n), page_size)
+    logits = indexer_logits(q_idx_hat, w, index_pool.rows(slots))
+    sel = topk_logical(logits, n, k)
+    rows = kv_pool.rows(page_slot(page_table_row, sel, page_size))
+    return logits, sel, attend(q_attn, rows, softmax_scale)

@@ -202,6 +202,13 @@ def test_topk_and_attention_reject_bad_arguments(lib):
     assert t(FAKE, 100, 2, FAKE, FAKE, FAKE, 4, 0, FAKE, None, None, 0, None) == INVALID
     assert t(FAKE, 100, 2, FAKE, FAKE, FAKE, 4, 64, None, None, None, 0, None) == INVALID
     assert t(FAKE, 100, 0, FAKE, FAKE, FAKE, 4, 64, FAKE, None, None, 0, None) == 0
+    g = lib.topk_page_select
+    g.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                  C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    assert g(FAKE, 100, 2, FAKE, FAKE, FAKE, 4, 64, 0, FAKE, None, None, 0, None) == INVALID      # k = 0
+    assert g(FAKE, 100, 2, FAKE, FAKE, FAKE, 4, 64, 2049, FAKE, None, None, 0, None) == INVALID   # k > 2048
+    assert g(FAKE, 1 << 20, 2, FAKE, FAKE, FAKE, 4, 64, 2048, FAKE, None, None, 0, None) == UNSUPPORTED
+    assert g(FAKE, 200000, 2, FAKE, FAKE, FAKE, 4, 64, 2048, FAKE, None, None, 0, None) == WORKSPACE
     a = lib.csa_sparse_attn
     a.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                   C.c_int32, KvPoolC, KvPoolC, C.c_void_p, C.c_int32, C.c_int32, C.c_float,
@@ -209,9 +216,10 @@ def test_topk_and_attention_reject_bad_arguments(lib):
     fp8 = KvPoolC(FAKE, FAKE, FAKE, 2, 64, 10)
     raw = KvPoolC(FAKE, FAKE, FAKE, 2, 256, 10)
     f32 = KvPoolC(FAKE, None, FAKE, 0, 256, 10)
-    assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 513, fp8, raw, FAKE, 4, 128, 0.04, FAKE, 1, FAKE, 1 << 30, None) == INVALID
+    assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 2049, fp8, raw, FAKE, 4, 128, 0.04, FAKE, 1, FAKE, 1 << 30, None) == INVALID
     assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 512, fp8, f32, FAKE, 4, 128, 0.04, FAKE, 1, FAKE, 1 << 30, None) == INVALID
-    assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 512, fp8, raw, FAKE, 4, 0, 0.04, FAKE, 1, FAKE, 1 << 30, None) == INVALID
+    assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 512, fp8, raw, FAKE, 4, -1, 0.04, FAKE, 1, FAKE, 1 << 30, None) == INVALID
+    assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 0, fp8, raw, FAKE, 4, 0, 0.04, FAKE, 1, FAKE, 1 << 30, None) == INVALID
     assert a(FAKE, 1, 2, 48, FAKE, FAKE, FAKE, 512, fp8, raw, FAKE, 4, 128, 0.04, FAKE, 1, FAKE, 1 << 30, None) == UNSUPPORTED
     # two queries over 640 entries are split over several workgroups: needs a workspace
     assert a(FAKE, 1, 2, 64, FAKE, FAKE, FAKE, 512, fp8, raw, FAKE, 4, 128, 0.04, FAKE, 1, None, 0, None) == WORKSPACE

@@ -760,3 +760,89 @@ def test_decode_prep(csa, fmt, with_rope):
     ok, msg, _ = match(q_out.cpu().numpy().reshape(B * H_I, -1), q_sc.cpu().numpy().reshape(B * H_I, -1),
                        Q.exact_rotated(qr, True, rope=qrope), Q.rotation_error_bound(qr, 128, rope=with_rope))
     assert ok, f"query rows: {msg}"
+
+
+# ------------------------------------------------------------------ generic top-k and DSA mode
+
+
+@pytest.mark.parametrize("k,lens", [
+    (1, [5000, 1, 0, 30000]),
+    (100, [99, 100, 101, 16384, 70000]),
+    (512, [8192, 200000]),                       # the generic entry at k = 512
+    (1000, [999, 5000, 40000, 131072]),
+    (2048, [2048, 2049, 16384, 131072]),          # whole rows, chunked rows
+    (2048, [500000]),                             # near the longest row k = 2048 takes
+])
+def test_topk_generic_k_bit_exact(csa, k, lens):
+    """topk_page_select for k != 512 (DSA's generic top-k) against the oracle,
+    bit for bit: ties (rounded logits), -0 / +0, a NaN, a short row, an empty
+    row; slots through a 64-entry page table."""
+    g = gen.rng(1400 + k + len(lens))
+    R, L = len(lens), max(max(lens), 1)
+    pps = (L + 63) // 64
+    pt = gen.page_table(g, R, pps, R * pps + 5)
+    logits = (np.round(g.standard_normal((R, L)) * 16) / 16).astype(np.float32)
+    logits[0, 1:200:3] = -0.0
+    logits[-1, 7] = np.nan
+    phys = torch.full((R, k), -7, dtype=torch.int32, device=DEV)
+    logi = torch.full((R, k), -7, dtype=torch.int32, device=DEV)
+    csa.topk_page_select(t_dev(logits), t_dev(np.array(lens, np.int32)), t_dev(np.arange(R, dtype=np.int32)),
+                         t_dev(pt), k, phys, logi, page_size=64)
+    gp, gl = phys.cpu().numpy(), logi.cpu().numpy()
+    for r, n in enumerate(lens):
+        wp, wl = O.topk_page_select(logits[r], n, pt[r], 64, k)
+        assert np.array_equal(gl[r], wl), f"row {r} (len {n}): logical indices differ"
+        assert np.array_equal(gp[r], wp), f"row {r} (len {n}): physical slots differ"
+
+
+def _kv_pool_chunked(g, n_rows, fmt="fp8", step=1 << 14):
+    """An oracle KV pool of n_rows seeded N(0,1) entries, quantised in pieces."""
+    parts = [O.quant_kv_entries(gen.normal(g, (min(step, n_rows - r0), 576)), fmt)
+             for r0 in range(0, n_rows, step)]
+    return O.KVPool(np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
+                    np.concatenate([p[2] for p in parts]), fmt)
+
+
+def test_dsa_decode_end_to_end(csa):
+    """The DSA (ratio-1) decode step over raw tokens: index-K and KV pools of
+    raw tokens in 64-token pages, indexer_score over tokens j <= p,
+    topk_page_select with k = 2048, csa_sparse_attn over the selection with no
+    window. Logits within 1e-4 of the row max; the selection equal to the
+    oracle's top-2048 outside the near-tie band; attention within 2e-2 of the
+    oracle's over the GPU's selection."""
+    from tests.fullsize import topk_agrees
+    g = gen.rng(1500)
+    lens = [1500, 20000, 70000]  # raw tokens; the first is shorter than k
+    B, k, H = len(lens), 2048, 64
+    pps = max((n + 63) // 64 for n in lens)
+    P = B * pps + 3
+    pt = gen.page_table(g, B, pps, P)
+    kdata, ksc = O.index_prep(gen.normal(g, (P * 64, 128)), True, "fp8")
+    ipool = O.IndexPool(kdata, ksc, "fp8")
+    kv = _kv_pool_chunked(g, P * 64)
+    qcodes, qsc = O.index_prep(gen.normal(g, (B, 64, 128)), True, "fp8")
+    w = gen.uniform(g, (B, 64))
+    q, qh = _bf16(gen.normal(g, (B, H, 576)))
+    dpt, rs, rl = t_dev(pt), t_dev(np.arange(B, dtype=np.int32)), t_dev(np.array(lens, np.int32))
+    logits = torch.full((B, max(lens)), float("nan"), device=DEV)
+    csa.indexer_score(t_dev(qcodes), t_dev(w), rs, rl, max(lens), dpt, index_pool_to_device(ipool, 64, 128),
+                      logits, q_fmt=csa.CSA_FP8_E4M3, q_scale=t_dev(qsc.astype(np.float32)))
+    phys = torch.full((B, k), -7, dtype=torch.int32, device=DEV)
+    logi = torch.full((B, k), -7, dtype=torch.int32, device=DEV)
+    csa.topk_page_select(logits, rl, rs, dpt, k, phys, logi, page_size=64)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    dkv = kv_pool_to_device(kv, 64)
+    csa.csa_sparse_attn(q, rs, t_dev(np.array(lens, np.int32) - 1), phys, dkv, dkv, dpt, 0, 576 ** -0.5, out)
+    gl_, gp, gq = logits.cpu().numpy(), phys.cpu().numpy(), logi.cpu().numpy()
+    go = out.float().cpu().numpy()
+    qhat = O.dequant_fp8_rows(qcodes, qsc)
+    for b, n in enumerate(lens):
+        o_logits, o_sel, _ = O.dsa_query(qhat[b], w[b], ipool, kv, pt[b], n - 1, qh[b], k, 576 ** -0.5)
+        tol = 1e-4 * np.abs(o_logits).max()
+        assert np.abs(gl_[b, :n] - o_logits).max() <= tol, f"seq {b}: logits"
+        ok, _, nband = topk_agrees(o_logits, gq[b], k, tol)
+        assert ok, f"seq {b}: top-{k} differs outside the near-tie band ({nband} in band)"
+        sel = gq[b][gq[b] >= 0]
+        assert np.array_equal(gp[b][:len(sel)], O.page_slot(pt[b], sel, 64))
+        want = O.attend(qh[b], kv.rows(O.page_slot(pt[b], sel, 64)), 576 ** -0.5)
+        assert np.abs(go[b] - want).max() <= 2e-2, f"seq {b}: attention"

@@ -448,6 +448,19 @@ def test_topk_signed_zero_nan_and_inf():
     assert np.array_equal(sel[90:], np.array([j for j in range(90, 600) if j != 100][:422]))
 
 
+@pytest.mark.parametrize("k", [1, 100, 2048])
+def test_topk_generic_k_equals_stable_argsort(k):
+    """The generic top-k (DSA's selection) is the first k of a stable argsort
+    by descending logit; k = 1 is the first index of the maximum."""
+    g = np.random.default_rng(160 + k)
+    for n in (k, k + 1, 3 * k + 5, 40000):
+        logits = np.round(g.standard_normal(n) * 6) / 6
+        ref = np.sort(np.argsort(-logits, kind="stable")[:k])
+        assert np.array_equal(O.topk_logical(logits, n, k), ref)
+    v = np.array([1.0, 3.0, -2.0, 3.0])
+    assert np.array_equal(O.topk_logical(v, 4, 1), [1])
+
+
 def test_topk_respects_row_len():
     v = np.arange(3000, dtype=np.float64)
     assert np.array_equal(O.topk_logical(v, 1000), np.arange(488, 1000))
@@ -583,3 +596,47 @@ def test_prefill_query_equals_decode_at_that_length():
         assert n_vis == (p + 1) // 4
     assert O.causal_row_len(131075, 33792) == 32769
     assert O.hca_visible(127, 128) == 1 and O.hca_visible(126, 128) == 0
+
+
+# ---------------------------------------------------------------- DSA mode ([P1] §1, §2.2)
+
+
+def test_dsa_short_context_is_dense_causal_attention():
+    """k >= p + 1: every visible raw token is selected, so the DSA query is
+    dense attention over tokens 0..p (torch SDPA in float64)."""
+    g = np.random.default_rng(50)
+    n_tok = 64 * 6
+    kv, _, ip = _mk_pools(g, n_tok, 64, fmt="fp8", idx_fmt="fp8", D=128)
+    pt = g.permutation(6)
+    p = 300
+    qc, qs = O.index_prep(g.standard_normal((64, 128)), True, "fp8")
+    q = g.standard_normal((16, 576))
+    logits, sel, out = O.dsa_query(O.dequant_fp8_rows(qc, qs), g.uniform(0, 1, 64), ip, kv, pt, p, q,
+                                   2048, 0.05)
+    assert len(logits) == p + 1 and np.array_equal(sel, np.arange(p + 1))
+    rows = kv.rows(O.page_slot(pt, np.arange(p + 1), 64))
+    np.testing.assert_allclose(out, _sdpa(q, rows, 0.05), rtol=1e-10, atol=1e-12)
+
+
+def test_dsa_brute_force_masked_attention():
+    """Brute force: score every visible token, keep the k best by (logit
+    descending, index ascending) through an explicit sort, mask the rest to
+    -inf, softmax, compare (random 64-token page table, k = 100)."""
+    g = np.random.default_rng(51)
+    kv, _, ip = _mk_pools(g, 64 * 10, 64, fmt="fp8", idx_fmt="fp8", D=128)
+    pt = g.permutation(10)
+    p, k = 575, 100
+    qc, qs = O.index_prep(g.standard_normal((64, 128)), True, "fp8")
+    qhat = O.dequant_fp8_rows(qc, qs)
+    w = g.uniform(0, 1, 64)
+    q = g.standard_normal((8, 576))
+    logits, sel, out = O.dsa_query(qhat, w, ip, kv, pt, p, q, k, 0.04)
+    allrows = kv.rows(O.page_slot(pt, np.arange(p + 1), 64))
+    order = sorted(range(p + 1), key=lambda j: (-logits[j], j))[:k]
+    mask = np.full(p + 1, -np.inf)
+    mask[order] = 0.0
+    sc = 0.04 * q @ allrows.T + mask
+    pr = np.exp(sc - sc.max(1, keepdims=True))
+    pr /= pr.sum(1, keepdims=True)
+    np.testing.assert_allclose(out, pr @ allrows[:, :512], rtol=1e-10, atol=1e-12)
+    assert np.array_equal(sel, np.sort(order))
