@@ -17,7 +17,7 @@ from ._binding import (  # noqa: F401
     IndexPool, KvPool, LIB_PATH, c4_compress, csa_decode_prep, csa_index_prep, csa_sparse_attn,
     csa_status_string, csa_version, csa_workspace_size, hca_dense_attn, indexer_score,
     indexer_topk512, indexer_topk512_noalloc, lib, topk512_page_select, topk_page_select,
-    CSA_OP_TOPK_K, CSA_TOPK_MAX,
+    CSA_OP_TOPK_K, CSA_TOPK_MAX, hisparse_swap_in,
     CSA_NOALLOC_SCRATCH_BYTES,
     CSA_TOPK, CSA_C4_PAGE, CSA_RAW_PAGE, CSA_C4_RATIO, CSA_HCA_RATIO,
 )

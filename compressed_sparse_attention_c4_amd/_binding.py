@@ -80,6 +80,8 @@ _indexer_topk_na = _decl("indexer_topk512_noalloc", [_vp, _i32, _vp, _u32, _vp, 
                                                      _vp, _vp])
 _topk_k = _decl("topk_page_select", [_vp, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp,
                                      _sz, _vp])
+_hisparse = _decl("hisparse_swap_in", [_vp, _i32, _i32, _vp, _KvPoolC, _vp, _i32, _KvPoolC, _i32, _vp,
+                                       _i64, _vp, _vp, _i32, _vp, _vp])
 _topk = _decl("topk512_page_select", [_vp, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
 _csa_attn = _decl("csa_sparse_attn", [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _KvPoolC, _KvPoolC,
                                       _vp, _i32, _i32, _f32, _vp, _i32, _vp, _sz, _vp])
@@ -293,6 +295,17 @@ def topk_page_select(logits, row_len, row_seq, page_table, k, phys_idx, logical_
         _ptr(logits), ld, R, _ptr(row_len), _ptr(row_seq), _ptr(page_table), page_table.shape[-1],
         int(page_size), int(k), _ptr(phys_idx), _ptr(logical_idx), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def hisparse_swap_in(logical_idx, row_seq, far: KvPool, far_page_table, near: KvPool, hot_slots,
+                     slot_of, owner, last_use, step, near_idx, stream=None):
+    """Stage the selection logical_idx [R, k] in the near pool; slot_of
+    [S, max_entries], owner / last_use [S, hot_slots] int32 state; near_idx [R, k]."""
+    R, k = logical_idx.shape
+    _check("hisparse_swap_in", _hisparse(
+        _ptr(logical_idx), R, k, _ptr(row_seq), far.c(), _ptr(far_page_table), far_page_table.shape[-1],
+        near.c(), int(hot_slots), _ptr(slot_of), slot_of.shape[-1], _ptr(owner), _ptr(last_use),
+        int(step), _ptr(near_idx), _stream(stream)))
 
 
 def _attn_ws(op, T, entries, H, device, ws, stream):

@@ -350,6 +350,24 @@ csa_status indexer_topk512_noalloc(const void* q, csa_fmt q_fmt, const void* q_s
                             ws, kScratchBytes, nullptr, stream);
 }
 
+csa_status hisparse_swap_in(const int32_t* logical_idx, int32_t R, int32_t k,
+                            const int32_t* row_seq, csa_kv_pool far,
+                            const int32_t* far_page_table, int32_t far_pt_stride,
+                            csa_kv_pool near, int32_t hot_slots, int32_t* slot_of,
+                            int64_t max_entries, int32_t* owner, int32_t* last_use, int32_t step,
+                            int32_t* near_idx, hipStream_t stream) {
+  if (R < 0 || k < 1 || k > hisparse_max_sel() || far_pt_stride <= 0) return CSA_ERR_INVALID;
+  if (hot_slots < k || hot_slots > hisparse_max_hot()) return CSA_ERR_INVALID;
+  if (max_entries < 1 || step < 0) return CSA_ERR_INVALID;
+  if (!kv_pool_ok(far) || !kv_pool_ok(near) || far.fmt != near.fmt) return CSA_ERR_INVALID;
+  if (R == 0) return CSA_OK;
+  if (!logical_idx || !row_seq || !far_page_table || !slot_of || !owner || !last_use || !near_idx)
+    return CSA_ERR_INVALID;
+  return hip_status(launch_hisparse_swap(logical_idx, R, k, row_seq, far, far_page_table,
+                                         far_pt_stride, near, hot_slots, slot_of, max_entries,
+                                         owner, last_use, step, near_idx, stream));
+}
+
 static csa_status attn_common(AttnArgs& a, hipStream_t stream) {
   if (a.T < 0 || a.H <= 0 || a.window < 0 || a.window > 4096) return CSA_ERR_INVALID;
   if (!a.hca && a.k_sel + a.window < 1) return CSA_ERR_INVALID;

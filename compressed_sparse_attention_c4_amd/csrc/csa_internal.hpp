@@ -86,6 +86,16 @@ hipError_t launch_topk(const float* logits, int64_t ld, int R, const int32_t* ro
                        int c4_page_size, int k, int32_t* phys_idx, int32_t* logical_idx, void* ws,
                        hipStream_t s);
 
+// HiSparse staging of one step's selected entries into the per-sequence hot
+// slots of the near pool (see hisparse.hip).
+hipError_t launch_hisparse_swap(const int32_t* sel, int R, int k, const int32_t* row_seq,
+                                const csa_kv_pool& far, const int32_t* far_pt, int far_pt_stride,
+                                const csa_kv_pool& near, int hot, int32_t* slot_of,
+                                int64_t max_entries, int32_t* owner, int32_t* last_use, int step,
+                                int32_t* near_idx, hipStream_t s);
+int hisparse_max_hot();
+int hisparse_max_sel();
+
 struct AttnArgs {
   const void* q;
   int q_fmt;

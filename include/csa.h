@@ -370,6 +370,41 @@ csa_status topk_page_select(const float* logits, int64_t ld, int32_t R, const in
                             int32_t* logical_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * hisparse_swap_in -- HiSparse staging of each step's selected compressed
+ * entries in a near (hot) KV pool ([P1] §5: the coordinator swaps the step's
+ * top-512 compressed tokens into fast storage, keyed by the top-k result's raw
+ * (logical) indices, and attention reads them there; entries selected again
+ * stay resident). Sequence s owns the near-pool slots [s * hot_slots,
+ * (s + 1) * hot_slots). For query row r of sequence s = row_seq[r], with its
+ * selection logical_idx[r][0..k) (-1 = empty):
+ *   - an entry already resident (slot_of[s][j] = h >= 0) is used in place;
+ *   - the m entries that are not are assigned, in selection order, the m
+ *     least recently used hot slots of s that no entry of this step uses
+ *     (empty slots first, then the smallest last_use, equal stamps by lower
+ *     slot), in ascending slot order; the slot's previous entry is unmapped;
+ *     the entry (latent, scale, RoPE dims) is copied from `far` (logical entry
+ *     j at far_page_table[s][j / page] * page + j % page, page = far.page_size);
+ *   - every used slot gets last_use = step; near_idx[r][i] is the near-pool
+ *     slot s * hot_slots + h of logical_idx[r][i] (-1 where it is -1).
+ * Attention then runs as csa_sparse_attn(..., near_idx, k, near pool, ...).
+ * State, owned by the caller (device int32): slot_of [S][max_entries]
+ * (logical entry -> hot slot or -1), owner [S][hot_slots] (hot slot ->
+ * logical entry or -1) and last_use [S][hot_slots]; start with slot_of and
+ * owner all -1. `far` may be any memory the device can read (an HBM pool, or
+ * host memory mapped for the device).
+ * Requires 1 <= k <= 512, k <= hot_slots <= 4096, step >= 0, pools of the same
+ * format; rows of one call must belong to different sequences (rows of one
+ * sequence in one call race), the near pool must hold S * hot_slots slots and
+ * max_entries cover every selected index (caller's contract).
+ */
+csa_status hisparse_swap_in(const int32_t* logical_idx, int32_t R, int32_t k,
+                            const int32_t* row_seq, csa_kv_pool far,
+                            const int32_t* far_page_table, int32_t far_pt_stride,
+                            csa_kv_pool near, int32_t hot_slots, int32_t* slot_of,
+                            int64_t max_entries, int32_t* owner, int32_t* last_use, int32_t step,
+                            int32_t* near_idx, hipStream_t stream);
+
+/*
  * csa_sparse_attn -- MLA-style sparse attention of each query over its selected
  * compressed entries plus a sliding window of raw tokens ([P1] §1: attention
  * reads the 512 selected compressed KV; [P2] CSA paragraph: a sliding-window

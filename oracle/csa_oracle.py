@@ -495,3 +495,57 @@ def dsa_query(q_idx_hat, w, index_pool: IndexPool, kv_pool: KVPool, page_table_r
     sel = topk_logical(logits, n, k)
     rows = kv_pool.rows(page_slot(page_table_row, sel, page_size))
     return logits, sel, attend(q_attn, rows, softmax_scale)
+
+
+# ---------------------------------------------------------------------------
+# HiSparse staging ([P1] §5: the step's top-k compressed entries are swapped
+# into a near tier for attention; entries selected again stay there)
+# ---------------------------------------------------------------------------
+
+
+class HotSet:
+    """The near-tier state of one sequence: `hot_slots` slots, each empty (-1)
+    or holding one logical entry, the reverse map, and each slot's last step
+    of use."""
+
+    def __init__(self, hot_slots: int):
+        self.hot = hot_slots
+        self.owner = [-1] * hot_slots
+        self.slot_of = {}
+        self.last_use = [0] * hot_slots
+
+
+def hisparse_swap_in(state: HotSet, selected, step: int):
+    """One step's staging of the selection `selected` (logical entries in
+    order, -1 = empty). Entries already resident stay where they are. The
+    others take, in selection order, the least recently used slots among those
+    this step does not use -- empty slots first, then the oldest last use,
+    equal stamps by the lower slot -- those slots taken in ascending order;
+    a slot's previous entry leaves the near tier. Every slot used this step is
+    stamped with `step`. Readings: least-recently-used replacement (the pages
+    say only that hot entries stay near); the victims' order is ascending.
+    Returns (near slot of each selected entry, -1 for -1; list of (entry, slot)
+    copies made)."""
+    hits = {j: state.slot_of[j] for j in selected if j >= 0 and j in state.slot_of}
+    used = set(hits.values())
+    misses = [j for j in selected if j >= 0 and j not in state.slot_of]
+    free = [h for h in range(state.hot) if h not in used]
+    free.sort(key=lambda h: (state.owner[h] >= 0, state.last_use[h] if state.owner[h] >= 0 else 0, h))
+    victims = sorted(free[:len(misses)])
+    assert len(victims) == len(misses), "more misses than free hot slots"
+    copies = []
+    for j, h in zip(misses, victims):
+        old = state.owner[h]
+        if old >= 0:
+            del state.slot_of[old]
+        state.owner[h] = j
+        state.slot_of[j] = h
+        copies.append((j, h))
+    near = []
+    for j in selected:
+        if j >= 0:
+            state.last_use[state.slot_of[j]] = step
+            near.append(state.slot_of[j])
+        else:
+            near.append(-1)
+    return near, copies

@@ -240,3 +240,24 @@ def test_noalloc_refuses_oversized_and_bad_sizes(lib):
     assert f(*args(4096, 33792)) == WORKSPACE
     assert f(*args(-1, 1000)) == INVALID
     assert f(*args(4, -5)) == INVALID
+
+
+def test_hisparse_rejects_bad_arguments(lib):
+    f = lib.hisparse_swap_in
+    f.restype = C.c_int
+    f.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, KvPoolC, C.c_void_p, C.c_int32, KvPoolC,
+                  C.c_int32, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                  C.c_void_p]
+    fp8 = KvPoolC(FAKE, FAKE, FAKE, 2, 64, 10)
+    f32 = KvPoolC(FAKE, None, FAKE, 0, 64, 10)
+
+    def call(R=2, k=512, hot=1024, far=fp8, near=fp8, step=0, max_entries=1000, sel=FAKE):
+        return f(sel, R, k, FAKE, far, FAKE, 4, near, hot, FAKE, max_entries, FAKE, FAKE, step, FAKE, None)
+
+    assert call(k=513) == INVALID           # more than 512 selected entries per row
+    assert call(hot=511) == INVALID         # fewer hot slots than selected entries
+    assert call(hot=4097) == INVALID
+    assert call(near=f32) == INVALID        # far and near formats differ
+    assert call(step=-1) == INVALID
+    assert call(sel=None) == INVALID
+    assert call(R=0) == 0

@@ -846,3 +846,70 @@ def test_dsa_decode_end_to_end(csa):
         assert np.array_equal(gp[b][:len(sel)], O.page_slot(pt[b], sel, 64))
         want = O.attend(qh[b], kv.rows(O.page_slot(pt[b], sel, 64)), 576 ** -0.5)
         assert np.abs(go[b] - want).max() <= 2e-2, f"seq {b}: attention"
+
+
+def test_hisparse_swap_in_against_oracle(csa):
+    """HiSparse staging over six steps of overlapping selections (three
+    sequences, 1024 hot slots, top-512): near-pool slots, the residency maps
+    and stamps equal the oracle's exactly; the staged rows equal the far
+    pool's bytes; attention over the near pool equals attention over the far
+    pool bit for bit."""
+    g = gen.rng(1600)
+    S, N, hot, k = 3, 20000, 1024, 512
+    pps = (N + 63) // 64
+    P = S * pps + 2
+    pt = gen.page_table(g, S, pps, P)
+    far = _kv_pool_chunked(g, P * 64)
+    dfar = kv_pool_to_device(far, 64)
+    near = csa.alloc_kv_pool(S * hot // 64, 64, csa.CSA_FP8_E4M3)
+    slot_of = torch.full((S, N), -1, dtype=torch.int32, device=DEV)
+    owner = torch.full((S, hot), -1, dtype=torch.int32, device=DEV)
+    last_use = torch.zeros((S, hot), dtype=torch.int32, device=DEV)
+    states = [O.HotSet(hot) for _ in range(S)]
+    rs = t_dev(np.arange(S, dtype=np.int32))
+    dpt = t_dev(pt)
+    q, _ = _bf16(gen.normal(g, (S, 64, 576)))
+    prev = [np.sort(g.choice(N, size=k, replace=False)) for _ in range(S)]
+    for step in range(6):
+        sel = np.full((S, k), -1, np.int32)
+        for s in range(S):
+            keep = prev[s][g.random(len(prev[s])) < 0.7]
+            new = g.choice(N, size=k, replace=False)
+            cur = np.unique(np.concatenate([keep, new]))[:k]
+            if s == 2 and step % 2:
+                cur = cur[:300]  # a short selection, -1 padded
+            cur = np.sort(cur)
+            sel[s, :len(cur)] = cur
+            prev[s] = cur
+        near_idx = torch.full((S, k), -7, dtype=torch.int32, device=DEV)
+        csa.hisparse_swap_in(t_dev(sel), rs, dfar, dpt, near, hot, slot_of, owner, last_use, step, near_idx)
+        torch.cuda.synchronize()
+        gn = near_idx.cpu().numpy()
+        for s in range(S):
+            want, _ = O.hisparse_swap_in(states[s], [int(j) for j in sel[s]], step)
+            want = np.array([s * hot + h if h >= 0 else -1 for h in want])
+            assert np.array_equal(gn[s], want), f"step {step} seq {s}: near slots differ"
+            own = owner[s].cpu().numpy()
+            assert np.array_equal(own, np.array(states[s].owner)), f"step {step} seq {s}: owners"
+            assert np.array_equal(last_use[s].cpu().numpy(), np.array(states[s].last_use))
+            so = slot_of[s].cpu().numpy()
+            res = np.flatnonzero(so >= 0)
+            assert sorted(res.tolist()) == sorted(states[s].slot_of.keys())
+            assert all(so[j] == states[s].slot_of[j] for j in res)
+        # the staged rows are the far rows of the selected entries
+        ok = sel >= 0
+        fslots = np.where(ok, np.stack([O.page_slot(pt[s], np.maximum(sel[s], 0), 64) for s in range(S)]), 0)
+        nl = near.latent.view(-1, 512).cpu().numpy()
+        ns = near.scale.view(-1).cpu().numpy()
+        nr = near.rope.view(-1, 64).cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(nl[gn[ok]], far.latent[fslots[ok]])
+        assert np.array_equal(ns[gn[ok]], far.scale[fslots[ok]])
+        assert np.array_equal(nr[gn[ok]], far.rope[fslots[ok]])
+        # attention over the near pool == over the far pool (same rows, same order)
+        pos = t_dev(np.full(S, 4 * N, np.int32))
+        o_near = torch.empty((S, 64, 512), dtype=torch.bfloat16, device=DEV)
+        o_far = torch.empty((S, 64, 512), dtype=torch.bfloat16, device=DEV)
+        csa.csa_sparse_attn(q, rs, pos, near_idx, near, near, dpt, 0, 576 ** -0.5, o_near)
+        csa.csa_sparse_attn(q, rs, pos, t_dev(np.where(ok, fslots, -1).astype(np.int32)), dfar, dfar, dpt,
+                            0, 576 ** -0.5, o_far)
+        assert torch.equal(o_near.view(torch.int16), o_far.view(torch.int16)), f"step {step}: attention"

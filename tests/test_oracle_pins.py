@@ -640,3 +640,68 @@ def test_dsa_brute_force_masked_attention():
     pr /= pr.sum(1, keepdims=True)
     np.testing.assert_allclose(out, pr @ allrows[:, :512], rtol=1e-10, atol=1e-12)
     assert np.array_equal(sel, np.sort(order))
+
+
+# ---------------------------------------------------------------- HiSparse ([P1] §5)
+
+
+def test_hisparse_hand_worked_steps():
+    st = O.HotSet(4)
+    for ln in read_golden("hisparse_lru.txt"):
+        step, sel, near, copies = [p.split() for p in ln.split("|")]
+        got_near, got_copies = O.hisparse_swap_in(st, [int(x) for x in sel], int(step[0]))
+        assert got_near == [int(x) for x in near], ln
+        assert got_copies == [tuple(int(v) for v in c.split(":")) for c in copies], ln
+
+
+def test_hisparse_invariants_over_many_steps():
+    """Maps stay inverse, every selected entry is resident after its step, hits
+    copy nothing, nothing selected this step is evicted, and a slot is evicted
+    only if no older-stamped free slot was left."""
+    g = np.random.default_rng(70)
+    hot, k = 64, 24
+    st = O.HotSet(hot)
+    prev = []
+    for step in range(40):
+        keep = [j for j in prev if g.random() < 0.6]
+        new = list(g.choice(400, size=k, replace=False))
+        sel = sorted(set(keep + new))[:k]
+        sel += [-1] * (k - len(sel))
+        before = dict(st.slot_of)
+        stamps = list(st.last_use)
+        owners = list(st.owner)
+        near, copies = O.hisparse_swap_in(st, sel, step)
+        assert all(st.owner[h] == j for j, h in st.slot_of.items())
+        assert all(j == -1 or st.slot_of[j] == h for j, h in zip(sel, near))
+        assert {j for j, _ in copies} == {j for j in sel if j >= 0 and j not in before}
+        used = {h for h in near if h >= 0}
+        victims = {h for _, h in copies}
+        for h in victims:  # an evicted slot is at least as old as every free slot kept
+            kept = [x for x in range(hot) if x not in used and x not in victims]
+            if owners[h] >= 0:
+                assert all(owners[x] >= 0 and stamps[x] >= stamps[h] for x in kept)
+        prev = [j for j in sel if j >= 0]
+
+
+def test_hisparse_attention_over_near_tier_equals_far():
+    """Attention over the staged near-tier rows equals attention over the far
+    pool's rows of the same selection (the staging only moves entries)."""
+    g = np.random.default_rng(71)
+    far_c4, raw, _ = _mk_pools(g, 64 * 20, 256 * 2, fmt="fp8")
+    pt = g.permutation(20)
+    hot = 600
+    st = O.HotSet(hot)
+    near_lat = np.zeros((hot, 512), np.uint8)
+    near_sc = np.zeros(hot, np.float32)
+    near_rope = np.zeros((hot, 64), np.uint16)
+    q = g.standard_normal((8, 576))
+    for step in range(3):
+        sel = np.sort(g.choice(64 * 20, size=512, replace=False))
+        near, copies = O.hisparse_swap_in(st, list(sel), step)
+        for j, h in copies:
+            f = O.page_slot(pt, j, 64)
+            near_lat[h], near_sc[h], near_rope[h] = far_c4.latent[f], far_c4.scale[f], far_c4.rope[f]
+        near_pool = O.KVPool(near_lat, near_sc, near_rope, "fp8")
+        a = O.attend(q, near_pool.rows(near), 0.04)
+        b = O.attend(q, far_c4.rows(O.page_slot(pt, sel, 64)), 0.04)
+        np.testing.assert_array_equal(a, b)
