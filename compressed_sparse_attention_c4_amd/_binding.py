@@ -130,14 +130,15 @@ def _fmt_of(t: torch.Tensor, declared: int | None = None) -> int:
     raise ValueError(f"cannot infer a csa format from {t.dtype}; pass fmt")
 
 
-def _scratch(nbytes, device, stream):
-    """A temporary workspace for one call, or None for 0 bytes. torch allocates
-    it on the current stream; when the call is enqueued on another stream the
-    allocator is told (record_stream), so that the block is not handed to
-    another tensor before that stream's kernels have finished with it."""
+def _scratch(nbytes, device, stream, zero=False):
+    """A temporary workspace for one call, or None for 0 bytes (zero-filled if
+    asked). torch allocates it on the current stream; when the call is
+    enqueued on another stream the allocator is told (record_stream), so that
+    the block is not handed to another tensor before that stream's kernels
+    have finished with it."""
     if not nbytes:
         return None
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ws = (torch.zeros if zero else torch.empty)(nbytes, dtype=torch.uint8, device=device)
     if stream is not None:
         ws.record_stream(stream)
     return ws
@@ -239,10 +240,13 @@ def indexer_score(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPool,
 def indexer_topk512(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPool, phys_idx,
                     logical_idx=None, *, q_fmt=None, q_scale=None, prep=0, q_used=None,
                     q_used_scale=None, ws=None, scan_done=None, stream=None):
-    """scan_done: optional torch.cuda.Event, recorded right after the scan launch."""
+    """scan_done: optional torch.cuda.Event, recorded right after the scan launch.
+    A caller's ws must start zero-filled (its first bytes are counters that every
+    call leaves at zero)."""
     T, H_I = w.shape
-    if ws is None:
-        ws = _scratch(csa_workspace_size(CSA_OP_INDEXER_TOPK, T, max_row_len, H_I), q.device, stream)
+    if ws is None:  # zero-filled: the fused selection's counters start at zero
+        ws = _scratch(csa_workspace_size(CSA_OP_INDEXER_TOPK, T, max_row_len, H_I), q.device, stream,
+                      zero=True)
     ev = None
     if scan_done is not None:
         # the handle exists after a first record; recording it here, in front

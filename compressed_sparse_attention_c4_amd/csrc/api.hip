@@ -67,13 +67,15 @@ inline bool rope_ok(const csa_rope& r, int dim, bool need_groups) {
 // indexer_topk512's workspace: the query-preparation area, then either the
 // scan's top-512 candidates (fused path) or the logits and the top-512
 // workspace (two-call path); sized for whichever is larger.
+// Layout: [the fused finish's counters, fixed size][query preparation][...].
 struct IdxTopkWs {
-  size_t prep, cand, merged, logits, topk, total;
+  size_t ctr, prep, cand, merged, logits, topk, total;
   int64_t ld;
 };
 IdxTopkWs idx_topk_ws(int64_t T, int64_t max_row_len, int H_I) {
   IdxTopkWs w{};
-  w.prep = align256(indexer_ws_bytes(T, H_I));
+  w.ctr = align256(kCandCounterBytes);
+  w.prep = w.ctr + align256(indexer_ws_bytes(T, H_I));
   const int64_t chunks = indexer_scan_chunks(T, max_row_len);
   w.cand = align256((size_t)T * chunks * CSA_TOPK * sizeof(uint32_t));
   w.merged = align256((size_t)T * kCandGroups * CSA_TOPK * sizeof(uint32_t));
@@ -254,24 +256,43 @@ csa_status indexer_topk512_ws(const void* q, csa_fmt q_fmt, const void* q_scale,
   if (!ws || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
   if (!q || !w || !row_seq || !row_len || !page_table || !k.data || !phys_idx) return CSA_ERR_INVALID;
   uint8_t* base = (uint8_t*)ws;
+  uint8_t* prep_ws = base + L.ctr;  // the prepared query, when prepared in the call
   const int chunks = indexer_cand_chunks(T, H_I, D_I, k, max_row_len, prep);
   hipError_t e;
   if (chunks > 0) {
-    uint32_t* ck = (uint32_t*)(base + L.prep);
-    int32_t* cj = (int32_t*)(base + L.prep + L.cand);
-    int32_t* cp = (int32_t*)(base + L.prep + 2 * L.cand);
+    CandOut co{};
+    co.keys = (uint32_t*)(base + L.prep);
+    co.js = (int32_t*)(base + L.prep + L.cand);
+    co.phys = (int32_t*)(base + L.prep + 2 * L.cand);
+    uint32_t* mk = (uint32_t*)(base + L.prep + 3 * L.cand);
+    int32_t* mj = (int32_t*)(base + L.prep + 3 * L.cand + L.merged);
+    int32_t* mp = (int32_t*)(base + L.prep + 3 * L.cand + 2 * L.merged);
+    // rows of 9..64 chunks finish their selection inside the scan (groups of
+    // at most 8 chunks, at most 8 groups), which saves the merge launch; with
+    // at most 8 chunks a row goes straight to the final pass
+    if (chunks > kCandGroups && chunks <= kCandFusedChunks && T < kCandFusedRows) {
+      co.cnt = (uint32_t*)base;
+      co.gsize = (chunks + kCandGroups - 1) / kCandGroups;
+      co.ngroups = (chunks + co.gsize - 1) / co.gsize;
+      co.mkeys = mk;
+      co.mjs = mj;
+      co.mphys = mp;
+      co.phys_idx = phys_idx;
+      co.logical_idx = logical_idx;
+    }
     e = launch_indexer(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len, max_row_len,
-                       page_table, pt_stride, k, nullptr, 0, q_used, q_used_scale, base, stream,
-                       ck, cj, cp);
+                       page_table, pt_stride, k, nullptr, 0, q_used, q_used_scale, prep_ws, stream,
+                       &co);
     if (e == hipSuccess && scan_done) e = hipEventRecord(scan_done, stream);
+    if (co.ngroups > 0) return hip_status(e);
+    uint32_t* ck = co.keys;
+    int32_t* cj = co.js;
+    int32_t* cp = co.phys;
     int ncand = chunks * CSA_TOPK;
     if (e == hipSuccess && ncand > kCandFinalMax) {
       // groups of g consecutive chunks -> at most kCandGroups lists
       const int g = (chunks + kCandGroups - 1) / kCandGroups;
       const int groups = (chunks + g - 1) / g;
-      uint32_t* mk = (uint32_t*)(base + L.prep + 3 * L.cand);
-      int32_t* mj = (int32_t*)(base + L.prep + 3 * L.cand + L.merged);
-      int32_t* mp = (int32_t*)(base + L.prep + 3 * L.cand + 2 * L.merged);
       e = launch_topk_cand_merge(ck, cj, cp, ncand, g * CSA_TOPK, T, row_len, mk, mj, mp, stream);
       ck = mk;
       cj = mj;
@@ -284,7 +305,7 @@ csa_status indexer_topk512_ws(const void* q, csa_fmt q_fmt, const void* q_scale,
   } else {
     float* logits = (float*)(base + L.prep);
     e = launch_indexer(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len, max_row_len,
-                       page_table, pt_stride, k, logits, L.ld, q_used, q_used_scale, base, stream);
+                       page_table, pt_stride, k, logits, L.ld, q_used, q_used_scale, prep_ws, stream);
     if (e == hipSuccess && scan_done) e = hipEventRecord(scan_done, stream);
     if (e == hipSuccess)
       e = launch_topk(logits, L.ld, T, row_len, row_seq, page_table, pt_stride, k.page_size,

@@ -43,13 +43,33 @@ hipError_t launch_index_prep(const void* v, int v_fmt, int64_t rows, int dim, ui
                              int out_fmt, void* out, void* out_scale, const int32_t* dst_rows,
                              const csa_rope& rope, hipStream_t s);
 
+// Where the fused decode scan puts its top-512 candidates (indexer_topk512).
+// Each scan workgroup writes its chunk's candidates (keys, js, phys: [T][chunks]
+// [512]). With ngroups > 0 the selection also finishes inside the scan: the
+// last workgroup of each group of gsize chunks (found with a counter in cnt)
+// merges the group's candidates, into mkeys / mjs / mphys [T][ngroups][512]
+// when ngroups > 1, and the last group of a row selects the row's top-512 into
+// phys_idx / logical_idx. cnt [T][kCandGroups + 1] must hold zeros; every
+// counter is returned to zero by the workgroup that completes it.
+struct CandOut {
+  uint32_t* keys;
+  int32_t* js;
+  int32_t* phys;
+  uint32_t* cnt;
+  int gsize, ngroups;
+  uint32_t* mkeys;
+  int32_t* mjs;
+  int32_t* mphys;
+  int32_t* phys_idx;
+  int32_t* logical_idx;
+};
+
 hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_t prep,
                           const float* w, int T, int H_I, int D_I, const int32_t* row_seq,
                           const int32_t* row_len, int max_row_len, const int32_t* page_table,
                           int pt_stride, const csa_index_pool& k, float* logits, int64_t ld,
                           void* q_used, void* q_used_scale, void* ws, hipStream_t s,
-                          uint32_t* okeys = nullptr, int32_t* ojs = nullptr,
-                          int32_t* ophys = nullptr);
+                          const CandOut* cand = nullptr);
 
 // Candidates per row the final top-512 pass takes in one workgroup (16 keys
 // per lane at 1024 threads). Rows with more scan chunks first merge groups of
@@ -57,6 +77,14 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
 // candidates), so the fused path takes up to kCandGroups * 32 chunks per row.
 constexpr int kCandFinalMax = 16384;
 constexpr int kCandGroups = 8;
+// The fused finish inside the scan takes groups of at most 4096 candidates
+// (8 chunks), so rows of at most kCandGroups * 8 chunks; rows of fewer than
+// kCandFusedRows rows. Its counters sit at the start of the workspace, in a
+// region of fixed size, so that calls of any shape find them where the last
+// call left them (zero).
+constexpr int kCandFusedChunks = kCandGroups * 8;
+constexpr int kCandFusedRows = 256;
+constexpr size_t kCandCounterBytes = (size_t)kCandFusedRows * (kCandGroups + 1) * sizeof(uint32_t);
 // Fused indexer + top-512: the scan workgroups select their chunk's top-512
 // candidates (launch_indexer with okeys / ojs / ophys: key, entry index and
 // physical slot), then one final pass per row, which takes the slots from the

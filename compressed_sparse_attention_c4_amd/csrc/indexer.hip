@@ -63,6 +63,110 @@ constexpr int kSelWaves = 8;
 template <bool kCand>
 constexpr int idx_threads() { return (kCand ? kSelWaves : kWaves) * 64; }
 
+// Candidate lists that one workgroup of the scan writes and another reads in
+// the same launch go around the caches: the eight XCDs' L2 caches are not
+// coherent with each other, and making them so with a device-scope fence costs
+// a write-back of the whole L2 per workgroup. System-scope stores write
+// through to memory and system-scope loads read from it; the writer waits for
+// its stores to complete (vmcnt 0) before it counts itself in.
+template <class T>
+__device__ __forceinline__ void st_through(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+template <class T>
+__device__ __forceinline__ T ld_through(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Top-K of n <= kTH * kE candidates (keys, entry indices, slots; in index
+// order) by one workgroup, emitted either as a candidate list (out_keys /
+// out_js / out_phys: 512 entries, padding past K: key 0, index INT_MAX, slot
+// -1) or as the row's selection (phys_idx / logical_idx: 512 entries, -1
+// past K). L.hist must be clear; ends with the emission (no barrier).
+template <int kTH, int kE>
+__device__ __forceinline__ void cand_select_emit(const uint32_t* keys, const int32_t* js,
+                                                 const int32_t* phys, int n, int K, TopkLds& L,
+                                                 uint32_t* out_keys, int32_t* out_js,
+                                                 int32_t* out_phys, int32_t* phys_idx,
+                                                 int32_t* logical_idx) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int seg = wave * 64 * kE;
+  uint32_t kr[kE];
+#pragma unroll
+  for (int i = 0; i < kE; ++i) {
+    const int e = seg + 64 * i + lane;
+    kr[i] = e < n ? ld_through(keys + e) : 0u;
+  }
+  topk_select<kE, kTH>(kr, n, K, seg, L);
+  for (int p = threadIdx.x; p < kTopK; p += kTH) {
+    const int e = p < K ? L.out_e[p] : 0;
+    const int32_t ph = p < K ? ld_through(phys + e) : -1;
+    const int32_t jj = p < K ? ld_through(js + e) : -1;
+    if (phys_idx) {
+      phys_idx[p] = ph;
+      if (logical_idx) logical_idx[p] = jj;
+    } else {
+      st_through(out_keys + p, p < K ? L.out_k[p] : 0u);
+      st_through(out_js + p, p < K ? jj : (int32_t)INT_MAX);
+      st_through(out_phys + p, ph);
+    }
+  }
+}
+
+// Counts this workgroup in at *c once every thread's write-through stores have
+// completed; true in every thread of the workgroup that brings the count to
+// `members`, which also returns the counter to zero.
+__device__ __forceinline__ bool last_arrival(uint32_t* c, int members, int* s_flag) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are done
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // system scope: performed at memory, where every XCD's workgroups meet
+    const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const bool last = old + 1u == (uint32_t)members;
+    if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// The finish of the fused selection, run by every scan workgroup whose chunk
+// holds entries of the row (`live` such chunks, the first ones) after it has
+// written its chunk's candidates: the last workgroup of its group of chunks
+// merges the group (or, when the row's live chunks form one group, selects
+// the row); the last group of the row selects the row from the groups' lists.
+template <int kTH, int kE>
+__device__ __forceinline__ void cand_finish(const CandOut& co, int t, int rl, int live, TopkLds& L) {
+  __shared__ int s_flag;
+  const int nch = gridDim.x;
+  const int g = blockIdx.x / co.gsize;
+  const int members = min(co.gsize, live - g * co.gsize);
+  const int groups = (live + co.gsize - 1) / co.gsize;
+  uint32_t* const cnt = co.cnt + (int64_t)t * (kCandGroups + 1);
+  if (!last_arrival(cnt + g, members, &s_flag)) return;
+  for (int i = threadIdx.x; i < kTopkBins; i += kTH) L.hist[i] = 0u;
+  const int64_t cb = ((int64_t)t * nch + (int64_t)g * co.gsize) * kTopK;
+  const int n1 = members * kTopK;
+  if (groups == 1) {
+    cand_select_emit<kTH, kE>(co.keys + cb, co.js + cb, co.phys + cb, n1, min(kTopK, rl), L,
+                              nullptr, nullptr, nullptr, co.phys_idx + (int64_t)t * kTopK,
+                              co.logical_idx ? co.logical_idx + (int64_t)t * kTopK : nullptr);
+    return;
+  }
+  const int64_t mb = ((int64_t)t * co.ngroups + g) * kTopK;
+  cand_select_emit<kTH, kE>(co.keys + cb, co.js + cb, co.phys + cb, n1, min(kTopK, n1), L,
+                            co.mkeys + mb, co.mjs + mb, co.mphys + mb, nullptr, nullptr);
+  if (!last_arrival(cnt + kCandGroups, groups, &s_flag)) return;
+  for (int i = threadIdx.x; i < kTopkBins; i += kTH) L.hist[i] = 0u;
+  const int64_t rb = (int64_t)t * co.ngroups * kTopK;
+  cand_select_emit<kTH, kE>(co.mkeys + rb, co.mjs + rb, co.mphys + rb, groups * kTopK,
+                            min(kTopK, rl), L, nullptr, nullptr, nullptr,
+                            co.phys_idx + (int64_t)t * kTopK,
+                            co.logical_idx ? co.logical_idx + (int64_t)t * kTopK : nullptr);
+}
+
 template <bool kFp4, bool kPage64, bool kCand>
 __global__ void __launch_bounds__(idx_threads<kCand>())
 indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
@@ -70,21 +174,34 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     const int32_t* __restrict__ row_len, const int32_t* __restrict__ pt,
                     int pt_stride, const uint8_t* __restrict__ kdata,
                     const void* __restrict__ kscale, int page_size, float* __restrict__ logits,
-                    int64_t ld, int chunk, uint32_t* __restrict__ okeys,
-                    int32_t* __restrict__ ojs, int32_t* __restrict__ ophys) {
+                    int64_t ld, int chunk, CandOut co) {
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K / q row
+  constexpr int kTH = idx_threads<kCand>();
+  constexpr int kSelE = kMaxChunk / kTH;  // keys per lane of the selections
   __shared__ int32_t s_pages[kMaxChunk / 16 + 2];      // physical pages of this chunk
   __shared__ __attribute__((aligned(16))) float s_out[kMaxChunk + 64];  // the chunk's logits
+  __shared__ TopkLds L;                                  // the selections (kCand)
   const int t = blockIdx.y;
   const int n = row_len[t];
   const int c0 = blockIdx.x * chunk;
+  const int live = (n + chunk - 1) / chunk;  // chunks holding entries of the row
   if (c0 >= n) {
     if constexpr (kCand) {
-      for (int p = threadIdx.x; p < kTopK; p += idx_threads<kCand>()) {
-        const int64_t o = ((int64_t)t * gridDim.x + blockIdx.x) * kTopK + p;
-        okeys[o] = 0u;
-        ojs[o] = INT_MAX;
-        ophys[o] = -1;
+      if (co.ngroups > 0) {
+        // past the row: no part in the fused finish; an empty row's selection
+        // is written here
+        if (n == 0 && blockIdx.x == 0)
+          for (int p = threadIdx.x; p < kTopK; p += kTH) {
+            co.phys_idx[(int64_t)t * kTopK + p] = -1;
+            if (co.logical_idx) co.logical_idx[(int64_t)t * kTopK + p] = -1;
+          }
+      } else {
+        for (int p = threadIdx.x; p < kTopK; p += kTH) {
+          const int64_t o = ((int64_t)t * gridDim.x + blockIdx.x) * kTopK + p;
+          co.keys[o] = 0u;
+          co.js[o] = INT_MAX;
+          co.phys[o] = -1;
+        }
       }
     }
     return;
@@ -236,9 +353,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   const int n_out = c1 - c0;
   if constexpr (kCand) {
     // keys from LDS: element seg + 64 i + lane of this wave's segment
-    constexpr int kTH = idx_threads<kCand>();
-    constexpr int kE = kMaxChunk / kTH;
-    __shared__ TopkLds L;
+    constexpr int kE = kSelE;
     for (int i = threadIdx.x; i < kTopkBins; i += kTH) L.hist[i] = 0u;
     const int seg = wave * 64 * kE;
     uint32_t kr[kE];
@@ -258,10 +373,17 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
         j = c0 + L.out_e[p];
         phys = s_pages[j / page_size - pg0] * page_size + j % page_size;  // a page of this chunk
       }
-      okeys[o] = key;
-      ojs[o] = j;
-      ophys[o] = phys;
+      if (co.ngroups > 0) {  // read by another workgroup of this launch
+        st_through(co.keys + o, key);
+        st_through(co.js + o, j);
+        st_through(co.phys + o, phys);
+      } else {
+        co.keys[o] = key;
+        co.js[o] = j;
+        co.phys[o] = phys;
+      }
     }
+    if (co.ngroups > 0) cand_finish<kTH, kSelE>(co, t, n, live, L);
   } else {
     float* orow = logits + (int64_t)t * ld + c0;
     for (int j = threadIdx.x; j < n_out; j += kWaves * 64) orow[j] = s_out[j];
@@ -600,7 +722,7 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
                           const int32_t* row_len, int max_row_len, const int32_t* page_table,
                           int pt_stride, const csa_index_pool& k, float* logits, int64_t ld,
                           void* q_used, void* q_used_scale, void* ws, hipStream_t s,
-                          uint32_t* okeys, int32_t* ojs, int32_t* ophys) {
+                          const CandOut* cand) {
   if (T == 0 || max_row_len == 0) return hipSuccess;
   if (k.fmt == CSA_F32) {
     dim3 grid((max_row_len + 63) / 64, T);
@@ -642,7 +764,7 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
     if (e != hipSuccess) return e;
   }
   const int64_t chunk = scan_chunk(T, max_row_len);
-  const int rows = okeys ? 0 : rows_kernel_rows(T, k, prep);
+  const int rows = cand ? 0 : rows_kernel_rows(T, k, prep);
   if (rows) {
     // page ranges: about two workgroups per CU when the row groups are few
     // (measured for 32 sequences x 4 rows at 128K: 58 us with 256 workgroups,
@@ -676,14 +798,15 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
     return hipGetLastError();
   }
   dim3 grid((unsigned)((max_row_len + chunk - 1) / chunk), T);
+  const CandOut co = cand ? *cand : CandOut{};
 #define CSA_IDX(FP4, P64, CAND)                                                                    \
   hipLaunchKernelGGL((indexer_mfma_kernel<FP4, P64, CAND>), grid, dim3(idx_threads<CAND>()), 0, s, qc, qs, \
                      w, row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data, k.scale,  \
-                     k.page_size, logits, ld, (int)chunk, okeys, ojs, ophys)
+                     k.page_size, logits, ld, (int)chunk, co)
 #define CSA_IDX_P(FP4, CAND)                 \
   if (k.page_size == 64) CSA_IDX(FP4, true, CAND); \
   else CSA_IDX(FP4, false, CAND);
-  if (okeys) {
+  if (cand) {
     if (k.fmt == CSA_MXFP4) { CSA_IDX_P(true, true) }
     else { CSA_IDX_P(false, true) }
   } else {

@@ -283,14 +283,20 @@ csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint
  * page size (k.page_size is the translation's c4_page_size), as in
  * csa_decode_prep. For FP8 / MXFP4 pools with few rows the logits are not
  * materialised: each scan workgroup selects the top-512 candidates of its
- * chunk from the logits it holds on chip, and one final pass per row selects
- * among the candidates (exact: an entry of a row's top-512 is in its chunk's
- * top-512). Other shapes (many rows, rows grouped by CSA_ROWS_PER_SEQ, an F32
- * pool) run the two calls through the workspace.
+ * chunk from the logits it holds on chip. Rows of 9 to 64 scan chunks finish
+ * inside the same launch: the last-arriving workgroup of each group of chunks
+ * merges the group and the last group of a row selects the row; shorter rows
+ * take one final pass per row, longer ones one merge and one final pass (exact
+ * either way: an entry of a row's top-512 is in its chunk's top-512). Other shapes (many rows, rows
+ * grouped by CSA_ROWS_PER_SEQ, an F32 pool) run the two calls through the
+ * workspace.
  *   Arguments as indexer_score and topk512_page_select; max_row_len up to
  *   2097152.
  *   ws   csa_workspace_size(CSA_OP_INDEXER_TOPK, T, max_row_len, H_I) bytes
- *        (always needed).
+ *        (always needed). Its first 9216 bytes are counters that the fused
+ *        selection finds at zero and leaves at zero: they must be zero before
+ *        the first call with a workspace (a zero-filled allocation), and stay
+ *        untouched between calls.
  *   scan_done  NULL, or an event recorded on `stream` right after the scan
  *        launch (before the final selection), so that a caller can time the
  *        scan alone or start dependent work early.

@@ -140,7 +140,7 @@ class CsaDecode:
         n = csa.csa_workspace_size(csa.CSA_OP_TOPK, B, self.maxN, 1)
         self.topk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         n = csa.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK, B, self.maxN, wl.index_heads)
-        self.itk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        self.itk_ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=DEV)  # counters start at 0
         torch.cuda.synchronize()
 
     def scan_plan(self):
@@ -256,7 +256,7 @@ class CsaSpecDecode(CsaDecode):
         n = csa.csa_workspace_size(csa.CSA_OP_CSA_ATTN, T, 512 + wl.window, H)
         self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         n = csa.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK, T, self.maxN, wl.index_heads)
-        self.itk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        self.itk_ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=DEV)
         qbytes = wl.index_dim if self.fmt == csa.CSA_FP8_E4M3 else wl.index_dim // 2
         self.q_codes = torch.empty((T, wl.index_heads, qbytes), dtype=torch.uint8, device=DEV)
         if self.fmt == csa.CSA_FP8_E4M3:
@@ -529,7 +529,7 @@ class TinyDecode:
         self.phys = torch.empty((1, 512), dtype=torch.int32, device=DEV)
         self.out = torch.empty((1, wl.heads, 512), dtype=torch.float32, device=DEV)
         n = csa.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK, 1, N, wl.index_heads)
-        self.itk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        self.itk_ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=DEV)
         n = csa.csa_workspace_size(csa.CSA_OP_CSA_ATTN_F32, 1, 512 + wl.window, wl.heads)
         self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         torch.cuda.synchronize()
