@@ -16,7 +16,11 @@ namespace csa {
 namespace {
 
 constexpr int kWavesPerWG = 4;
+constexpr int kBatch = 8;  // row slots a wave loads before preparing them
 
+// A wave takes kBatch row slots (a slot: one 128-dim row, or two 64-dim
+// rows) at a time and issues all their loads (and rope-table reads) before it
+// rotates and stores any, so that a slot's load latency overlaps the others'.
 template <int D, bool kF32In>
 __global__ void __launch_bounds__(kWavesPerWG * 64)
 index_prep_kernel(const void* __restrict__ v, int64_t rows, uint32_t flags, int out_fmt,
@@ -28,19 +32,32 @@ index_prep_kernel(const void* __restrict__ v, int64_t rows, uint32_t flags, int 
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerWG;
   const int sub = (D == 64) ? (lane >> 5) : 0;       // which row of the pair
   const int e0 = 2 * ((D == 64) ? (lane & 31) : lane);  // first element of this lane
-  for (int64_t r0 = wave_id * kRowsPerWave; r0 < rows; r0 += nwaves * kRowsPerWave) {
-    const int64_t r = r0 + sub;
-    const bool valid = r < rows;
-    float x0 = 0.f, x1 = 0.f;
-    if (valid) {
-      load_pair<kF32In>(v, r * D + e0, x0, x1);
-      if (flags & CSA_PREP_ROPE)
-        rope_pair<D>(x0, x1, e0 / 2, rope.pos[r / rope.rows_per_pos], rope.cos_sin, rope.dim);
+  const bool do_rope = (flags & CSA_PREP_ROPE) != 0;
+  for (int64_t b0 = wave_id * kBatch * kRowsPerWave; b0 < rows; b0 += nwaves * kBatch * kRowsPerWave) {
+    float x0[kBatch], x1[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t r = b0 + i * kRowsPerWave + sub;
+      x0[i] = x1[i] = 0.f;
+      if (r < rows) load_pair<kF32In>(v, r * D + e0, x0[i], x1[i]);
     }
-    const int64_t d = valid ? (dst_rows ? (int64_t)dst_rows[r] : r) : 0;
-    const bool store = valid && d >= 0;  // a negative destination skips the row
-    prep_and_store<D>(x0, x1, store, flags & CSA_PREP_HADAMARD, out_fmt, out, out_scale,
-                      store ? d : 0);
+    if (do_rope) {
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int64_t r = b0 + i * kRowsPerWave + sub;
+        if (r < rows)
+          rope_pair<D>(x0[i], x1[i], e0 / 2, rope.pos[r / rope.rows_per_pos], rope.cos_sin, rope.dim);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t r = b0 + i * kRowsPerWave + sub;
+      const bool valid = r < rows;
+      const int64_t d = valid ? (dst_rows ? (int64_t)dst_rows[r] : r) : 0;
+      const bool store = valid && d >= 0;  // a negative destination skips the row
+      prep_and_store<D>(x0[i], x1[i], store, flags & CSA_PREP_HADAMARD, out_fmt, out, out_scale,
+                        store ? d : 0);
+    }
   }
 }
 
@@ -50,7 +67,7 @@ hipError_t launch_index_prep(const void* v, int v_fmt, int64_t rows, int dim, ui
                              int out_fmt, void* out, void* out_scale, const int32_t* dst_rows,
                              const csa_rope& rope, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  const int64_t rows_per_wg = kWavesPerWG * (128 / dim);
+  const int64_t rows_per_wg = kWavesPerWG * kBatch * (128 / dim);
   int64_t nblocks = (rows + rows_per_wg - 1) / rows_per_wg;
   if (nblocks > 65536) nblocks = 65536;
   dim3 grid((unsigned)nblocks), block(kWavesPerWG * 64);
