@@ -138,7 +138,7 @@ def _one_kernel(means, name):
 COUNTER_KERNELS = {
     "decode128k": "indexer_mfma_kernel<false, true, true>",
     "decode1m": "indexer_mfma_kernel<true, true, true>",
-    "prefill": "indexer_rows_kernel<false, 8>",
+    "prefill": "indexer_rows_kernel<false, 8, true>",
 }
 
 
@@ -476,7 +476,7 @@ def secondary(a):
     W = CsaPrefill(wl)
     ms, k_ms, _ = time_steps(W, max(5, steps // 4), 2, 1, graph=not a.no_graph)
     tf = W.indexer_flops() / (k_ms / 1e3) / 1e12
-    kname = "indexer_rows_kernel<false, 8>"
+    kname = "indexer_rows_kernel<false, 8, true>"
     c = stored_counters(kname) or {}
     line = {"tokens_per_s": round(W.new / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,

@@ -69,7 +69,7 @@ inline bool rope_ok(const csa_rope& r, int dim, bool need_groups) {
 // workspace (two-call path); sized for whichever is larger.
 // Layout: [the fused finish's counters, fixed size][query preparation][...].
 struct IdxTopkWs {
-  size_t ctr, prep, cand, merged, logits, topk, total;
+  size_t ctr, prep, cand, merged, logits, topk, rsel, total;
   int64_t ld;
 };
 IdxTopkWs idx_topk_ws(int64_t T, int64_t max_row_len, int H_I) {
@@ -82,7 +82,9 @@ IdxTopkWs idx_topk_ws(int64_t T, int64_t max_row_len, int H_I) {
   w.ld = std::max<int64_t>(64, (max_row_len + 63) / 64 * 64);
   w.logits = align256((size_t)T * w.ld * sizeof(float));
   w.topk = align256(topk_ws_bytes(T, w.ld, CSA_TOPK));
-  w.total = w.prep + std::max(3 * (w.cand + w.merged), w.logits + w.topk);
+  // the row-block selection's per-range candidates (several page ranges)
+  w.rsel = align256((size_t)T * indexer_rows_sel_cands(T, max_row_len) * sizeof(uint32_t));
+  w.total = w.prep + std::max({3 * (w.cand + w.merged), w.logits + w.topk, 3 * w.rsel});
   return w;
 }
 
@@ -258,8 +260,27 @@ csa_status indexer_topk512_ws(const void* q, csa_fmt q_fmt, const void* q_scale,
   uint8_t* base = (uint8_t*)ws;
   uint8_t* prep_ws = base + L.ctr;  // the prepared query, when prepared in the call
   const int chunks = indexer_cand_chunks(T, H_I, D_I, k, max_row_len, prep);
+  const int ranges = indexer_rows_sel_ranges(T, H_I, D_I, k, max_row_len, prep);
   hipError_t e;
-  if (chunks > 0) {
+  if (ranges > 0) {
+    // many rows per sequence: the row-block kernel keeps each row's top-512
+    // as it scores; with several page ranges per row a final pass merges the
+    // ranges' candidates
+    CandOut co{};
+    co.rows_sel = 1;
+    co.phys_idx = phys_idx;
+    co.logical_idx = logical_idx;
+    co.keys = (uint32_t*)(base + L.prep);
+    co.js = (int32_t*)(base + L.prep + L.rsel);
+    co.phys = (int32_t*)(base + L.prep + 2 * L.rsel);
+    e = launch_indexer(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len, max_row_len,
+                       page_table, pt_stride, k, nullptr, 0, q_used, q_used_scale, prep_ws, stream,
+                       &co);
+    if (e == hipSuccess && scan_done) e = hipEventRecord(scan_done, stream);
+    if (e == hipSuccess && ranges > 1)
+      e = launch_topk_cand_final(co.keys, co.js, co.phys, ranges * CSA_TOPK, T, row_len, row_seq,
+                                 page_table, pt_stride, k.page_size, phys_idx, logical_idx, stream);
+  } else if (chunks > 0) {
     CandOut co{};
     co.keys = (uint32_t*)(base + L.prep);
     co.js = (int32_t*)(base + L.prep + L.cand);

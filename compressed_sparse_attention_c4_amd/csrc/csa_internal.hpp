@@ -51,6 +51,10 @@ hipError_t launch_index_prep(const void* v, int v_fmt, int64_t rows, int dim, ui
 // when ngroups > 1, and the last group of a row selects the row's top-512 into
 // phys_idx / logical_idx. cnt [T][kCandGroups + 1] must hold zeros; every
 // counter is returned to zero by the workgroup that completes it.
+// With rows_sel the row-block kernel selects instead (8 rows per workgroup,
+// the ranges given by indexer_rows_sel_ranges): one range writes phys_idx /
+// logical_idx, several write keys / js / phys [T][ranges][512] for
+// launch_topk_cand_final.
 struct CandOut {
   uint32_t* keys;
   int32_t* js;
@@ -62,6 +66,7 @@ struct CandOut {
   int32_t* mphys;
   int32_t* phys_idx;
   int32_t* logical_idx;
+  int rows_sel;
 };
 
 hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_t prep,
@@ -96,6 +101,12 @@ int indexer_cand_chunks(int64_t T, int H_I, int D_I, const csa_index_pool& k,
                         int64_t max_row_len, uint32_t prep);
 // Chunks per row of the decode scan kernel for these sizes.
 int64_t indexer_scan_chunks(int64_t T, int64_t max_row_len);
+// Page ranges of the row-block kernel's fused selection for this call, or 0
+// when the call does not take it (it takes 8 rows per workgroup).
+int indexer_rows_sel_ranges(int64_t T, int H_I, int D_I, const csa_index_pool& k,
+                            int64_t max_row_len, uint32_t prep);
+// Largest ranges * 512 candidates per row that calls of these sizes can need.
+int64_t indexer_rows_sel_cands(int64_t T, int64_t max_row_len);
 // A row's candidates in groups of `group` (a multiple of 512) reduced to one
 // top-512 list per group (okeys / ojs / ophys: R x groups x 512).
 hipError_t launch_topk_cand_merge(const uint32_t* ckeys, const int32_t* cjs, const int32_t* cphys,

@@ -26,6 +26,7 @@
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 #include "topk_select.hpp"
+#include "wave_topk.hpp"
 
 namespace csa {
 namespace {
@@ -404,17 +405,29 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
 // ends (the causal rule) are enforced by per-row buffer stores bounded to
 // row_len. A row of another sequence than the workgroup's first row reads its
 // own pages straight from memory.
+//
+// kSel (8 rows, one wave per row): no logits are written. Each wave keeps the
+// running top-512 of its row's logits in LDS as they are produced (WaveTopk:
+// a candidate buffer and a rising threshold), and at the end writes either the
+// row's selection (one page range: physical slots through the page table and
+// entry indices, as the top-512 kernel writes them) or its range's top-512
+// candidates (key, index, slot; key 0 / INT_MAX / -1 padding) for the final
+// pass over the ranges. Any entry of the row's top-512 is in its range's
+// top-512, so the result is exact.
 constexpr int kRowsPerWG = 8;  // waves per workgroup (and rows, at most)
+constexpr int kSelCap = 1024;  // per-row candidate buffer of the fused selection
+constexpr int kSelSpan = 65536;  // entries per page range, at most (16-bit offsets in the buffer)
 
-template <bool kFp4, int kRows>
-__global__ void __launch_bounds__(kRowsPerWG * 64)
+template <bool kFp4, int kRows, bool kSel>
+__global__ void __launch_bounds__(kRowsPerWG * 64) __attribute__((amdgpu_waves_per_eu(4)))
 indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     const float* __restrict__ w, const int32_t* __restrict__ row_seq,
                     const int32_t* __restrict__ row_len, int T, const int32_t* __restrict__ pt,
                     int pt_stride, const uint8_t* __restrict__ kdata,
                     const void* __restrict__ kscale, float* __restrict__ logits, int64_t ld,
-                    int ppc) {
+                    int ppc, CandOut co) {
   static_assert(kRows >= 2 && kRows <= kRowsPerWG, "rows per workgroup");
+  static_assert(!kSel || kRows == kRowsPerWG, "the fused selection takes one wave per row");
   constexpr int kWpr = kRowsPerWG / kRows;  // waves per row
   constexpr int kPage = 64;                          // entries per page (= tile)
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K row
@@ -422,6 +435,13 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kPage * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint32_t s_bs[2][kPage];  // fp32 scale / 4 e8m0 bytes
   __shared__ int s_len[kRows];
+  // fused selection: per wave, candidate keys, 16-bit index offsets and a
+  // 256-bin histogram; s_cflag[i]: some wave asks every wave to compact at the
+  // next page of slot i (so that the waves' compactions overlap instead of
+  // each one holding the workgroup at the next page's barrier)
+  constexpr int kSelWords = kSelCap + kSelCap / 2 + 256;
+  __shared__ __attribute__((aligned(16))) uint32_t s_sel[kSel ? kRowsPerWG * kSelWords : 4];
+  __shared__ int s_cflag[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -438,6 +458,13 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   const bool own = seqw == seq0;
   const int nw = row_ok ? row_len[t] : 0;
   if (lane == 0 && sub == 0 && live) s_len[wave / kWpr] = own ? nw : -nw - 1;  // other sequence: negated
+  WaveTopk<kSelCap, kTopK> sel;
+  if constexpr (kSel) {
+    sel.key = s_sel + wave * kSelWords;
+    sel.idx = reinterpret_cast<uint16_t*>(sel.key + kSelCap);
+    sel.hist = sel.key + kSelCap + kSelCap / 2;
+    if (tid < 3) s_cflag[tid] = 0;  // ordered before use by the barrier below
+  }
 
   // query operands and head weights of this wave's row
   v8i a[4];
@@ -475,10 +502,11 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   }
   // this workgroup's page range [pc0, pc1)
   const int pc0 = blockIdx.y * ppc, pc1 = pc0 + ppc;
+  const int jbase = pc0 * kPage;  // the selection buffer holds entry - jbase
   const int npages = min((maxall + kPage - 1) / kPage, pc1);
   const int nstage = min((maxown + kPage - 1) / kPage, pc1);
-  const __amdgpu_buffer_rsrc_t out_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(logits + (int64_t)tq * ld, (short)0, nw * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      kSel ? nullptr : logits + (int64_t)tq * ld, (short)0, kSel ? 0 : nw * 4, 0x00020000);
   const int32_t* pt0 = pt + (int64_t)seq0 * pt_stride;
   const int32_t* ptw = pt + (int64_t)seqw * pt_stride;
 
@@ -489,17 +517,18 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   const int stid = tid % (kPage * kChunks);
   const int se = stid / kChunks, sc = stid % kChunks;
   const int sw = kFp4 ? (sc ^ ((se >> 2) & 3)) : (sc ^ (se & 7));  // swizzled chunk position
-  const bool scaler = tid < kPage / 4;  // 16 threads also move the page's 256 B of scales
-  const int sce = (tid % (kPage / 4)) * 4;  // first of 4 entries whose scales this thread moves
+  const bool scaler = tid < kPage;  // one wave also moves the page's 256 B of scales
+  const int sce = tid % kPage;        // the entry whose 4 scale bytes this thread moves
   // pages are loaded kDepth pages ahead into a register ring (slot p % kDepth)
   constexpr int kDepth = 3;
-  v4i stage[kDepth], sstage[kDepth];  // native vectors (HIP's uint4 struct blocks promotion)
+  v4i stage[kDepth];  // native vectors (HIP's uint4 struct blocks promotion)
+  uint32_t sstage[kDepth];
   auto load_page = [&](int p, auto K) __attribute__((always_inline)) {
     constexpr int k = decltype(K)::value;
     // clamped, never skipped; with no page to stage, pool page 0 stands in
     const int64_t base = nstage > 0 ? (int64_t)pt0[min(p, nstage - 1)] * kPage : 0;
     stage[k] = *reinterpret_cast<const v4i*>(kdata + (base + se) * kRowBytes + sc * 16);
-    sstage[k] = *reinterpret_cast<const v4i*>(reinterpret_cast<const uint8_t*>(kscale) + (base + sce) * 4);
+    sstage[k] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(kscale) + (base + sce) * 4);
   };
   // issue order fixed (slot 0 oldest) so the loop head waits only for slot 0
   load_page(pc0, std::integral_constant<int, 0>{});
@@ -537,16 +566,30 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
 #pragma unroll
       for (int r = 0; r < 4; ++r) v = fmaf(wq[hb * 4 + r], fmaxf(acc[hb][r], 0.f), v);
     v = cross_row_sum(v);
-    const int off = grp == 0 ? jrow * 4 : 0x7FFFFFFF;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * ks), out_rsrc, off, 0, 0);
+    if constexpr (kSel) {
+      sel.push(v * ks, (uint32_t)(jrow - jbase), grp == 0 && jrow < nw);
+    } else {
+      const int off = grp == 0 ? jrow * 4 : 0x7FFFFFFF;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * ks), out_rsrc, off, 0, 0);
+    }
   };
   auto page_step = [&](const int p, auto K) __attribute__((always_inline)) {
     constexpr int k = decltype(K)::value;
     const int buf = p & 1;
     if (stager) *reinterpret_cast<v4i*>(&s_b[buf][se * kRowBytes + sw * 16]) = stage[k];
-    if (scaler) *reinterpret_cast<v4i*>(&s_bs[buf][sce]) = sstage[k];
+    if (scaler) s_bs[buf][sce] = sstage[k];
     __syncthreads();
     load_page(p + kDepth, K);  // refill the slot just written to LDS
+    // a compaction asked for at the previous page: every wave with more than
+    // 512 candidates compacts at this one, together, before its push (the
+    // flag is read here and used after the scoring, which hides the read);
+    // the flag read one page ago is cleared (its readers have all passed this
+    // page's barrier)
+    int cflag = 0;
+    if constexpr (kSel) {
+      cflag = s_cflag[k];
+      if (tid == 0) s_cflag[(k + 2) % 3] = 0;
+    }
     if (own && p * kPage < nw && p < pc1) {  // (the loop runs past pc1 to a multiple of kDepth)
       // the four 16-entry groups of the page; one reduce-scatter across the
       // lane rows then leaves the 64-head sum of group r in row r, so each
@@ -574,8 +617,15 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
       const float tot = rows4_reduce_scatter(pk[0], pk[1], pk[2], pk[3]);
       const int e = grp * 16 + col;  // the entry whose logit this lane holds
       const float ks = kFp4 ? 1.f : __uint_as_float(s_bs[buf][e]);
-      const int off = grp % kWpr == sub ? (p * kPage + e) * 4 : 0x7FFFFFFF;  // past the buffer: dropped
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot * ks), out_rsrc, off, 0, 0);
+      if constexpr (kSel) {
+        const int j = p * kPage + e;
+        if (cflag && sel.cnt > kTopK) sel.compact(false);
+        sel.push(tot * ks, (uint32_t)(j - jbase), j < nw);
+        if (lane == 0 && sel.short_of_room()) s_cflag[(k + 1) % 3] = 1;
+      } else {
+        const int off = grp % kWpr == sub ? (p * kPage + e) * 4 : 0x7FFFFFFF;  // past the buffer: dropped
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot * ks), out_rsrc, off, 0, 0);
+      }
     }
   };
   static_assert(kDepth == 3, "the page loop below is unrolled by hand for three slots");
@@ -608,6 +658,26 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
         ks = reinterpret_cast<const float*>(kscale)[slot];
       }
       score_store(bb, sb, ks, e);
+    }
+  }
+  if constexpr (kSel) {
+    if (!row_ok) return;
+    sel.finish();
+    const int32_t* ptr = pt + (int64_t)seqw * pt_stride;
+    const bool direct = gridDim.y == 1;  // one range: the row's selection itself
+    const int64_t o = ((int64_t)t * gridDim.y + blockIdx.y) * kTopK;
+    for (int q = lane; q < kTopK; q += 64) {
+      const bool have = q < sel.cnt;
+      const int32_t j = have ? jbase + (int32_t)sel.idx[q] : -1;
+      const int32_t phys = have ? (int32_t)((int64_t)ptr[j / kPage] * kPage + j % kPage) : -1;
+      if (direct) {
+        co.phys_idx[o + q] = phys;
+        if (co.logical_idx) co.logical_idx[o + q] = j;
+      } else {
+        co.keys[o + q] = have ? sel.key[q] : 0u;
+        co.js[o + q] = have ? j : INT_MAX;
+        co.phys[o + q] = phys;
+      }
     }
   }
 }
@@ -703,6 +773,43 @@ static int rows_kernel_rows(int64_t T, const csa_index_pool& k, uint32_t prep) {
   return T >= kRowsPerWG * 32 ? 8 : 0;
 }
 
+// Page ranges of the row-block kernel (blockIdx.y) and pages per range: about
+// two workgroups per CU when the row groups are few (measured for 32 sequences
+// x 4 rows at 128K: 58 us with 256 workgroups, 47 with 512, 51 with 1024). The
+// fused selection takes at least 8 pages (512 entries) per range, so that only
+// a row's last ranges write padding candidates, after all its entries, at most
+// kCandFinalMax / 512 ranges, the final pass's capacity, and at most kSelSpan
+// entries per range (its buffer holds 16-bit entry offsets); rows beyond
+// kCandFinalMax / 512 * kSelSpan entries do not take it.
+static int rows_ranges(int64_t T, int rows, int64_t max_row_len, bool sel, int& ppc) {
+  const int64_t groups = (T + rows - 1) / rows;
+  const int64_t pages = (max_row_len + 63) / 64;
+  int64_t ranges = std::max<int64_t>(1, std::min<int64_t>(pages, (512 + groups - 1) / groups));
+  if (sel) {
+    const int64_t span = (pages * 64 + kSelSpan - 1) / kSelSpan;  // 16-bit offsets within a range
+    ranges = std::max<int64_t>(span, std::min<int64_t>({ranges, pages / 8, kCandFinalMax / kTopK}));
+  }
+  ppc = (int)((pages + ranges - 1) / ranges);
+  return (int)((pages + ppc - 1) / ppc);
+}
+
+int indexer_rows_sel_ranges(int64_t T, int H_I, int D_I, const csa_index_pool& k,
+                            int64_t max_row_len, uint32_t prep) {
+  if (k.fmt != CSA_FP8_E4M3 && k.fmt != CSA_MXFP4) return 0;
+  if (H_I != kHeads || D_I != kDim || T == 0 || max_row_len == 0) return 0;
+  if (rows_kernel_rows(T, k, prep) != kRowsPerWG) return 0;
+  int ppc;
+  const int ranges = rows_ranges(T, kRowsPerWG, max_row_len, true, ppc);
+  return ranges * kTopK <= kCandFinalMax ? ranges : 0;
+}
+
+int64_t indexer_rows_sel_cands(int64_t T, int64_t max_row_len) {
+  if (T == 0 || max_row_len == 0) return 0;
+  int ppc;
+  const int ranges = rows_ranges(T, kRowsPerWG, max_row_len, true, ppc);
+  return ranges > 1 && ranges * kTopK <= kCandFinalMax ? (int64_t)ranges * kTopK : 0;
+}
+
 int64_t indexer_scan_chunks(int64_t T, int64_t max_row_len) {
   const int64_t c = scan_chunk(T, max_row_len);
   return (max_row_len + c - 1) / c;
@@ -764,25 +871,28 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
     if (e != hipSuccess) return e;
   }
   const int64_t chunk = scan_chunk(T, max_row_len);
-  const int rows = cand ? 0 : rows_kernel_rows(T, k, prep);
+  const bool rsel = cand && cand->rows_sel;
+  const int rows = rsel ? kRowsPerWG : (cand ? 0 : rows_kernel_rows(T, k, prep));
   if (rows) {
-    // page ranges: about two workgroups per CU when the row groups are few
-    // (measured for 32 sequences x 4 rows at 128K: 58 us with 256 workgroups,
-    // 47 with 512, 51 with 1024)
     const int groups = (int)((T + rows - 1) / rows);
-    const int pages = (int)((max_row_len + 63) / 64);
-    const int ranges = std::max(1, std::min(pages, (512 + groups - 1) / groups));
-    const int ppc = (pages + ranges - 1) / ranges;
-    dim3 g2(groups, (pages + ppc - 1) / ppc);
-#define CSA_ROWS(FP4, R)                                                                          \
-  hipLaunchKernelGGL((indexer_rows_kernel<FP4, R>), g2, dim3(kRowsPerWG * 64), 0, s, qc, qs, w,   \
-                     row_seq, row_len, T, page_table, pt_stride, (const uint8_t*)k.data, k.scale, \
-                     logits, ld, ppc)
+    int ppc;
+    const int ranges = rows_ranges(T, rows, max_row_len, rsel, ppc);
+    dim3 g2(groups, ranges);
+    const CandOut co = rsel ? *cand : CandOut{};
+#define CSA_ROWS(FP4, R, SEL)                                                                     \
+  hipLaunchKernelGGL((indexer_rows_kernel<FP4, R, SEL>), g2, dim3(kRowsPerWG * 64), 0, s, qc, qs, \
+                     w, row_seq, row_len, T, page_table, pt_stride, (const uint8_t*)k.data,       \
+                     k.scale, logits, ld, ppc, co)
     const bool fp4 = k.fmt == CSA_MXFP4;
+    if (rsel) {
+      if (fp4) CSA_ROWS(true, kRowsPerWG, true);
+      else CSA_ROWS(false, kRowsPerWG, true);
+      return hipGetLastError();
+    }
 #define CSA_ROWS_CASE(R)                        \
   case R:                                       \
-    if (fp4) CSA_ROWS(true, R);                 \
-    else CSA_ROWS(false, R);                    \
+    if (fp4) CSA_ROWS(true, R, false);          \
+    else CSA_ROWS(false, R, false);             \
     break;
     switch (rows) {
       CSA_ROWS_CASE(2)

@@ -615,6 +615,66 @@ def test_indexer_many_rows_causal(csa, fmt):
         assert np.all(np.isnan(got[t, n:])), f"row {t} wrote past row_len"
 
 
+@pytest.mark.parametrize("fmt,case", [("fp8", "ranges"), ("mxfp4", "ranges"), ("fp8", "direct"),
+                                      ("mxfp4", "direct"), ("fp8", "ties_direct"),
+                                      ("fp8", "ties_ranges")])
+def test_indexer_topk512_many_rows(csa, fmt, case):
+    """Prefill shape through indexer_topk512: the row-block kernel keeps each
+    row's top-512 as it scores (no logits written). With one page range per
+    row it writes the selection itself ("direct"), with several a final pass
+    merges the ranges' candidates ("ranges"). Bit for bit the result of
+    indexer_score + topk512_page_select, including rows of another sequence
+    than their group's first row, empty rows, rows shorter than 512, and index
+    pools whose rows repeat (many exactly equal logits: equal keys go to the
+    lower index)."""
+    g = gen.rng(1400 + len(fmt) + len(case))
+    ties = case.startswith("ties")
+    if case.endswith("ranges"):
+        L1, L2, T = 21000, 9000, 300   # 83 pages: 10 ranges of 9 pages
+    else:
+        L1, L2, T = 3600, 2000, 520    # 15 pages: one range
+    N1, N2 = L1 // 4, L2 // 4
+    pt, pool, num_pages = _index_case(g, fmt, 2, [N1, N2])
+    if ties:  # index-K rows repeat with period 7: logits repeat exactly
+        rows = np.arange(num_pages * 64) % 7
+        pool = O.IndexPool(pool.data[rows], pool.scale[rows], fmt)
+    pos = np.arange(L1 - T, L1)
+    row_seq = np.zeros(T, np.int32)
+    row_len = np.minimum(N1, (pos + 1) // 4).astype(np.int32)
+    row_len[:8] = [0, 1, 63, 64, 65, 511, 512, 513]
+    row_seq[100:108] = 1
+    row_len[100:108] = N2 - np.arange(8)
+    row_len[200:204] = 0
+    row_seq[204:208] = 1
+    row_len[204:208] = N2 // 2 + np.arange(4)
+    qraw = gen.normal(g, (T, 64, 128))
+    qcodes, qsc = O.index_prep(qraw, True, fmt)
+    w = gen.uniform(g, (T, 64))
+    qfmt = csa.CSA_FP8_E4M3 if fmt == "fp8" else csa.CSA_MXFP4
+    qs = t_dev(qsc.astype(np.float32)) if fmt == "fp8" else t_dev(qsc)
+    dpool = index_pool_to_device(pool, 64, 128)
+    drs, drl, dpt = t_dev(row_seq), t_dev(row_len), t_dev(pt)
+    phys = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    logi = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    csa.indexer_topk512(t_dev(qcodes), t_dev(w), drs, drl, N1, dpt, dpool, phys, logi, q_fmt=qfmt,
+                        q_scale=qs)
+    logits = torch.full((T, N1), float("nan"), device=DEV)
+    csa.indexer_score(t_dev(qcodes), t_dev(w), drs, drl, N1, dpt, dpool, logits, q_fmt=qfmt,
+                      q_scale=qs)
+    phys2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    logi2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    csa.topk512_page_select(logits, drl, drs, dpt, phys2, logi2)
+    gp, gl = phys.cpu().numpy(), logi.cpu().numpy()
+    wp, wl = phys2.cpu().numpy(), logi2.cpu().numpy()
+    bad = [t for t in range(T) if not (np.array_equal(gl[t], wl[t]) and np.array_equal(gp[t], wp[t]))]
+    assert not bad, f"{len(bad)} rows differ from the two calls, first {bad[:5]}"
+    if ties:  # the case has many equal logits to break
+        lg = logits.cpu().numpy()
+        t = T - 1
+        kth = np.sort(lg[t, :row_len[t]])[-512]
+        assert np.sum(lg[t, :row_len[t]] == kth) > 1
+
+
 @pytest.mark.parametrize("fmt,q_len", [("fp8", 4), ("mxfp4", 8), ("fp8", 2), ("fp8", 6), ("fp8", 5),
                                        ("mxfp4", 3), ("fp8", 10)])
 def test_indexer_rows_per_seq(csa, fmt, q_len):

@@ -383,7 +383,6 @@ class CsaPrefill:
         self.q_attn = gen.device_normal((new, wl.heads, 576), seed + 8)
         self.q_codes = torch.empty((new, wl.index_heads, wl.index_dim), dtype=torch.uint8, device=DEV)
         self.q_scale = torch.empty((new, wl.index_heads), dtype=torch.float32, device=DEV)
-        self.logits = torch.empty((new, N), dtype=torch.float32, device=DEV)
         pos = ctx + np.arange(new)
         self.pos_host = pos
         self.row_len_host = np.minimum(N, (pos + 1) // 4)
@@ -394,13 +393,23 @@ class CsaPrefill:
         self.out = torch.empty((new, wl.heads, 512), dtype=torch.bfloat16, device=DEV)
         n = csa.csa_workspace_size(csa.CSA_OP_CSA_ATTN, new, 512 + wl.window, wl.heads)
         self.attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
-        n = csa.csa_workspace_size(csa.CSA_OP_TOPK, new, N, 1)
-        self.topk_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        # the fused indexer + top-512 (its workspace starts zero-filled)
+        n = csa.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK, new, N, wl.index_heads)
+        self.itk_ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=DEV)
         torch.cuda.synchronize()
 
     def indexer_flops(self) -> float:
         """Causal indexer GEMM flops: 2 * heads * dim per visible (query, entry)."""
         return 2.0 * self.wl.index_heads * self.wl.index_dim * float(self.row_len_host.sum())
+
+    def score_only(self, c: int = 0):
+        """The step's indexer logits into self.logits (indexer_score: the same
+        row-block kernel, writing logits instead of selecting on chip). For
+        tests; run after step(c), whose preparation it reuses."""
+        if getattr(self, "logits", None) is None:
+            self.logits = torch.empty((self.new, self.N), dtype=torch.float32, device=DEV)
+        csa.indexer_score(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.N, self.pt,
+                          self.idx, self.logits, q_fmt=self.fmt, q_scale=self.q_scale)
 
     def step(self, c: int = 0, ev=None):
         wl = self.wl
@@ -415,14 +424,15 @@ class CsaPrefill:
         csa.csa_index_prep(self.q_idx, wl.index_dim, self.prep_flags, self.fmt, self.q_codes,
                            self.q_scale, rope_pos=self.q_pos, rope_table=self.rope_table,
                            rows_per_pos=wl.index_heads)
+        # the row-block scan keeps each query row's top-512 as it scores (one
+        # page range per row at this size: no logits and no second pass)
         if ev is not None:
             ev[0].record()
-        csa.indexer_score(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.N, self.pt,
-                          self.idx, self.logits, q_fmt=self.fmt, q_scale=self.q_scale)
+        csa.indexer_topk512(self.q_codes, self.w_idx, self.row_seq, self.row_len, self.N, self.pt,
+                            self.idx, self.phys, q_fmt=self.fmt, q_scale=self.q_scale,
+                            ws=self.itk_ws)
         if ev is not None:
             ev[1].record()
-        csa.topk512_page_select(self.logits, self.row_len, self.row_seq, self.pt, self.phys,
-                                ws=self.topk_ws)
         csa.csa_sparse_attn(self.q_attn, self.row_seq, self.q_pos, self.phys, self.c4, self.raw,
                             self.pt, wl.window, wl.softmax_scale, self.out, ws=self.attn_ws)
 
