@@ -10,7 +10,8 @@ kernels; there is no fallback. Importing fails if libcsa.so is not built
 from __future__ import annotations
 
 from ._binding import (  # noqa: F401
-    CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP,
+    CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP, CSA_ERR_BOUNDS,
+    csa_set_debug, csa_debug_enabled,
     CSA_BF16, CSA_F32, CSA_FP8_E4M3, CSA_MXFP4, CSA_OP_CSA_ATTN, CSA_OP_HCA_ATTN,
     CSA_OP_INDEXER, CSA_OP_INDEXER_TOPK, CSA_OP_TOPK, CSA_OP_CSA_ATTN_F32, CSA_OP_HCA_ATTN_F32, CSA_PREP_HADAMARD, CSA_PREP_QUANT, CSA_PREP_ROPE,
     CSA_ROWS_PER_SEQ, CsaError,

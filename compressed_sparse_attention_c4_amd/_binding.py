@@ -17,7 +17,7 @@ if not os.path.exists(LIB_PATH):
 lib = C.CDLL(LIB_PATH)
 
 # ---- constants (mirror include/csa.h)
-CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = range(5)
+CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP, CSA_ERR_BOUNDS = range(6)
 CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4 = range(4)
 CSA_PREP_HADAMARD, CSA_PREP_QUANT, CSA_PREP_ROPE = 1, 2, 4
 
@@ -90,6 +90,8 @@ _hca_attn = _decl("hca_dense_attn", [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32
 _ws_size = _decl("csa_workspace_size", [_i32, _i64, _i64, _i32], _sz)
 _status_string = _decl("csa_status_string", [C.c_int], C.c_char_p)
 _version = _decl("csa_version", [], C.c_char_p)
+_set_debug = _decl("csa_set_debug", [_i32], None)
+_debug_enabled = _decl("csa_debug_enabled", [], C.c_int32)
 
 
 class CsaError(RuntimeError):
@@ -104,6 +106,17 @@ def csa_status_string(status: int) -> str:
 
 def csa_version() -> str:
     return _version().decode()
+
+
+def csa_set_debug(on: bool) -> None:
+    """Debug mode: the checked calls first verify their page ids, lengths,
+    positions and slots on the device (synchronising) and raise CsaError with
+    status CSA_ERR_BOUNDS, launching nothing else, on a violation."""
+    _set_debug(1 if on else 0)
+
+
+def csa_debug_enabled() -> bool:
+    return bool(_debug_enabled())
 
 
 def csa_workspace_size(op: int, rows: int, max_len: int, heads: int) -> int:

@@ -2,6 +2,8 @@
 // argument checks (before any launch), then the kernel launchers.
 #include <hip/hip_runtime.h>
 
+#include <limits.h>
+
 #include <algorithm>
 #include <mutex>
 
@@ -100,6 +102,9 @@ extern "C" {
 
 const char* csa_version(void) { return "0.1.0"; }
 
+void csa_set_debug(int32_t on) { set_debug(on); }
+int32_t csa_debug_enabled(void) { return debug_on() ? 1 : 0; }
+
 const char* csa_status_string(csa_status s) {
   switch (s) {
     case CSA_OK: return "ok";
@@ -107,6 +112,7 @@ const char* csa_status_string(csa_status s) {
     case CSA_ERR_UNSUPPORTED: return "unsupported format or shape";
     case CSA_ERR_WORKSPACE: return "workspace too small";
     case CSA_ERR_HIP: return "HIP runtime error";
+    case CSA_ERR_BOUNDS: return "device data out of range (debug mode)";
   }
   return "unknown status";
 }
@@ -136,6 +142,13 @@ csa_status c4_compress(const void* x, csa_fmt x_fmt, const int32_t* cu_rows,
   if (!kv_pool_ok(out)) return CSA_ERR_INVALID;
   if (B == 0 || max_rows < ratio) return CSA_OK;
   if (!x || !cu_rows || !start_pos || !gate_w || !gate_b || !page_table) return CSA_ERR_INVALID;
+  if (debug_on()) {
+    DebugCheck d("c4_compress", stream);
+    d.rows(kCheckCompress, B, nullptr, start_pos, 0, ratio, 0, cu_rows, page_table, pt_stride,
+           out.page_size, out.num_pages);
+    const csa_status st = d.result();
+    if (st != CSA_OK) return st;
+  }
   return hip_status(launch_compress(x, x_fmt, cu_rows, start_pos, B, max_rows, ratio, gate_w,
                                     gate_b, page_table, pt_stride, out, stream));
 }
@@ -184,6 +197,16 @@ csa_status csa_decode_prep(const void* x, csa_fmt x_fmt, const int32_t* pos, int
   }
   if (B == 0) return CSA_OK;
   if (!x || !pos || !gate_w || !gate_b || !page_table || !raw_page_table) return CSA_ERR_INVALID;
+  if (debug_on()) {
+    DebugCheck d("csa_decode_prep", stream);
+    const int64_t c4_pages = k_rows ? std::min(c4.num_pages, kpool.num_pages) : c4.num_pages;
+    d.rows(kCheckDecode, B, nullptr, pos, 0, ratio, 0, nullptr, page_table, pt_stride,
+           c4.page_size, c4_pages);
+    d.rows(kCheckDecode, B, nullptr, pos, 0, 1, 0, nullptr, raw_page_table, raw_pt_stride,
+           raw.page_size, raw.num_pages);
+    const csa_status st = d.result();
+    if (st != CSA_OK) return st;
+  }
   DecodePrepArgs a{};
   a.x = x; a.x_fmt = x_fmt; a.pos = pos; a.B = B; a.ratio = ratio; a.gate_w = gate_w;
   a.gate_b = gate_b; a.page_table = page_table; a.pt_stride = pt_stride; a.c4 = c4;
@@ -207,6 +230,13 @@ csa_status indexer_score(const void* q, csa_fmt q_fmt, const void* q_scale, uint
   if (st != CSA_OK) return st;
   if (T == 0 || max_row_len == 0) return CSA_OK;
   if (!q || !w || !row_seq || !row_len || !page_table || !k.data || !logits) return CSA_ERR_INVALID;
+  if (debug_on()) {
+    DebugCheck d("indexer_score", stream);
+    d.rows(kCheckRowLen, T, row_seq, row_len, max_row_len, 1, 0, nullptr, page_table, pt_stride,
+           k.page_size, k.num_pages);
+    const csa_status st = d.result();
+    if (st != CSA_OK) return st;
+  }
   return hip_status(launch_indexer(q, q_fmt, q_scale, prep, w, T, H_I, D_I, row_seq, row_len,
                                    max_row_len, page_table, pt_stride, k, logits, ld, q_used,
                                    q_used_scale, ws, stream));
@@ -223,6 +253,13 @@ csa_status topk_page_select(const float* logits, int64_t ld, int32_t R, const in
   if (!logits || !row_len || !row_seq || !page_table || !phys_idx) return CSA_ERR_INVALID;
   const size_t need = topk_ws_bytes(R, ld, k);
   if (need > ws_bytes || (need > 0 && !ws)) return CSA_ERR_WORKSPACE;
+  if (debug_on()) {  // (no pool here: page ids are checked against their sign only)
+    DebugCheck d("topk_page_select", stream);
+    d.rows(kCheckRowLen, R, row_seq, row_len, ld, 1, 0, nullptr, page_table, pt_stride, page_size,
+           INT32_MAX);
+    const csa_status st = d.result();
+    if (st != CSA_OK) return st;
+  }
   return hip_status(launch_topk(logits, ld, R, row_len, row_seq, page_table, pt_stride, page_size,
                                 k, phys_idx, logical_idx, ws, stream));
 }
@@ -257,6 +294,13 @@ csa_status indexer_topk512_ws(const void* q, csa_fmt q_fmt, const void* q_scale,
   const IdxTopkWs L = idx_topk_ws(T, max_row_len, H_I);
   if (!ws || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
   if (!q || !w || !row_seq || !row_len || !page_table || !k.data || !phys_idx) return CSA_ERR_INVALID;
+  if (debug_on()) {
+    DebugCheck d("indexer_topk512", stream);
+    d.rows(kCheckRowLen, T, row_seq, row_len, max_row_len, 1, 0, nullptr, page_table, pt_stride,
+           k.page_size, k.num_pages);
+    const csa_status st = d.result();
+    if (st != CSA_OK) return st;
+  }
   uint8_t* base = (uint8_t*)ws;
   uint8_t* prep_ws = base + L.ctr;  // the prepared query, when prepared in the call
   const int chunks = indexer_cand_chunks(T, H_I, D_I, k, max_row_len, prep);
@@ -405,6 +449,12 @@ csa_status hisparse_swap_in(const int32_t* logical_idx, int32_t R, int32_t k,
   if (R == 0) return CSA_OK;
   if (!logical_idx || !row_seq || !far_page_table || !slot_of || !owner || !last_use || !near_idx)
     return CSA_ERR_INVALID;
+  if (debug_on()) {
+    DebugCheck d("hisparse_swap_in", stream);
+    d.idx((int64_t)R * k, k, logical_idx, max_entries, kBadEntry);
+    const csa_status st = d.result();
+    if (st != CSA_OK) return st;
+  }
   return hip_status(launch_hisparse_swap(logical_idx, R, k, row_seq, far, far_page_table,
                                          far_pt_stride, near, hot_slots, slot_of, max_entries,
                                          owner, last_use, step, near_idx, stream));
@@ -430,6 +480,19 @@ static csa_status attn_common(AttnArgs& a, hipStream_t stream) {
   }
   if (a.T == 0) return CSA_OK;
   if (!a.q || !a.q_seq || !a.q_pos || !a.raw_pt || !a.out) return CSA_ERR_INVALID;
+  if (debug_on()) {
+    DebugCheck d(a.hca ? "hca_dense_attn" : "csa_sparse_attn", stream);
+    if (a.hca)
+      d.rows(kCheckHca, a.T, a.q_seq, a.q_pos, 0, a.ratio, 0, nullptr, a.comp_pt,
+             a.comp_pt_stride, a.comp.page_size, a.comp.num_pages);
+    else if (a.k_sel > 0)
+      d.idx((int64_t)a.T * a.k_sel, a.k_sel, a.phys_idx, a.comp.num_pages * a.comp.page_size,
+            kBadSlot);
+    d.rows(kCheckWindow, a.T, a.q_seq, a.q_pos, 0, 1, a.window, nullptr, a.raw_pt,
+           a.raw_pt_stride, a.raw.page_size, a.raw.num_pages);
+    const csa_status st = d.result();
+    if (st != CSA_OK) return st;
+  }
   return hip_status(launch_attention(a, stream));
 }
 

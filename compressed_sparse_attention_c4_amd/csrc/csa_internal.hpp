@@ -135,6 +135,38 @@ hipError_t launch_hisparse_swap(const int32_t* sel, int R, int k, const int32_t*
 int hisparse_max_hot();
 int hisparse_max_sel();
 
+// Debug mode (debug_check.hip): device-side checks of the integers a call
+// follows, run before its kernels; result() synchronises the stream and
+// returns CSA_ERR_BOUNDS on a violation (printed to stderr).
+bool debug_on();
+void set_debug(int on);
+enum CheckMode { kCheckRowLen = 0, kCheckWindow = 1, kCheckHca = 2, kCheckCompress = 3,
+                 kCheckDecode = 4 };
+enum CheckCode { kBadRowLen = 1, kBadPosition = 2, kBadSequence = 3, kBadTableWidth = 4,
+                 kBadPage = 5, kBadSlot = 6, kBadEntry = 7 };
+class DebugCheck {
+ public:
+  DebugCheck(const char* entry, hipStream_t s);
+  // rows r < R: entry range by mode (kCheckRowLen: [0, lens[r]) with
+  // lens[r] <= cap; kCheckWindow: the `window` positions up to lens[r];
+  // kCheckHca: [0, (lens[r] + 1) / ratio); kCheckCompress: the entries the
+  // rows cu_rows[r]..cu_rows[r+1] starting at position lens[r] complete;
+  // kCheckDecode: the entry position lens[r] completes), sequence row_seq[r]
+  // (or r), pages of that range in pt, each in [0, num_pages)
+  void rows(int mode, int R, const int32_t* row_seq, const int32_t* lens, int64_t cap, int ratio,
+            int window, const int32_t* cu_rows, const int32_t* pt, int pt_stride, int page_size,
+            int64_t num_pages);
+  // n values of v (rows of k): each -1 or in [0, limit)
+  void idx(int64_t n, int k, const int32_t* v, int64_t limit, int32_t code);
+  csa_status result();
+
+ private:
+  const char* entry_;
+  hipStream_t s_;
+  int32_t* rec_ = nullptr;
+  hipError_t err_ = hipSuccess;
+};
+
 struct AttnArgs {
   const void* q;
   int q_fmt;

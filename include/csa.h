@@ -76,7 +76,10 @@ typedef enum {
   CSA_ERR_INVALID = 1,      /* bad argument; nothing launched, nothing written  */
   CSA_ERR_UNSUPPORTED = 2,  /* valid but unimplemented format / shape combo     */
   CSA_ERR_WORKSPACE = 3,    /* workspace too small (see csa_workspace_size)     */
-  CSA_ERR_HIP = 4           /* the HIP runtime reported a launch error          */
+  CSA_ERR_HIP = 4,          /* the HIP runtime reported a launch error          */
+  CSA_ERR_BOUNDS = 5        /* debug mode: a device-resident page id, length,
+                               position or slot is out of range; the call's own
+                               kernels were not launched (see csa_set_debug)   */
 } csa_status;
 
 typedef enum {
@@ -482,6 +485,29 @@ csa_status hca_dense_attn(const void* q, csa_fmt q_fmt, int32_t T, int32_t H,
 size_t csa_workspace_size(int32_t op, int64_t rows, int64_t max_len, int32_t heads);
 
 const char* csa_status_string(csa_status s);
+
+/*
+ * csa_set_debug -- debug mode on (nonzero) or off; csa_debug_enabled returns
+ * the current mode. The mode starts on when the environment holds CSA_DEBUG
+ * set to anything but "" or "0" when the library first needs it.
+ *   In debug mode c4_compress, csa_decode_prep, indexer_score,
+ *   indexer_topk512 (and _noalloc), topk_page_select / topk512_page_select,
+ *   hisparse_swap_in, csa_sparse_attn and hca_dense_attn first check on the
+ *   device the integers they are about to follow, within the extents the
+ *   host-side arguments give: row lengths within their capacity (max_row_len,
+ *   ld), non-negative positions and sequence indices, every page id of the
+ *   pages a row touches in [0, num_pages) and within the page-table row
+ *   (pt_stride), selected slots in [-1, num_pages * page_size), HiSparse
+ *   logical entries in [-1, max_entries). The first violation is printed to
+ *   stderr (entry point, kind, row, index, value) and the call returns
+ *   CSA_ERR_BOUNDS without launching its kernels. The checks synchronise the
+ *   stream: debug mode is for finding a caller's bad tables, not for graph
+ *   capture or timing. A page-table row past the caller's last sequence
+ *   cannot be known to the library and is not checked.
+ *   Thread-safe to read; set it while no call is in flight.
+ */
+void csa_set_debug(int32_t on);
+int32_t csa_debug_enabled(void);
 
 /* Library version, e.g. "0.1.0". */
 const char* csa_version(void);

@@ -69,6 +69,22 @@ def test_status_strings_and_version(lib):
     assert lib.csa_status_string(0) == b"ok"
     assert lib.csa_status_string(1) == b"invalid argument"
     assert lib.csa_version().count(b".") == 2
+    assert b"debug" in lib.csa_status_string(5)
+
+
+def test_debug_mode_switch(lib):
+    """csa_set_debug / csa_debug_enabled are host state only; the mode starts
+    from CSA_DEBUG (unset here)."""
+    lib.csa_debug_enabled.restype = C.c_int32
+    lib.csa_set_debug.argtypes = [C.c_int32]
+    start = lib.csa_debug_enabled()
+    try:
+        lib.csa_set_debug(1)
+        assert lib.csa_debug_enabled() == 1
+        lib.csa_set_debug(0)
+        assert lib.csa_debug_enabled() == 0
+    finally:
+        lib.csa_set_debug(start)
 
 
 def test_workspace_sizes(lib):
