@@ -51,9 +51,10 @@ BF16_PEAK_TFLOPS = 2500.0   # dense BF16 matrix peak
 LLC_BYTES = 256 << 20       # MI355X last-level (Infinity) cache
 SPIN_CYCLES = 2_000_000     # ~1 ms of GPU spin ahead of each eager timing step
 SIMD_COUNT = 256 * 4        # SIMDs on the chip (MFMA busy normalisation)
+XCD_COUNT = 8               # GRBM_GUI_ACTIVE reads as the sum over the XCDs' clocks
 COPY_BYTES = 4 << 28        # bytes read (and written) by one launch of the calibration copy
 PROFILE_GAP_S = 1.0         # idle gap between setup and the profiled steps
-KERNEL_SOURCES = ("indexer.hip", "csa_device.hpp", "topk_select.hpp", "../build.py")
+KERNEL_SOURCES = ("indexer.hip", "csa_device.hpp", "topk_select.hpp", "wave_topk.hpp", "../build.py")
 
 PROFILE_CHOICES = ["tiny", "decode_128k", "decode_1m", "spec_decode", "prefill", "hca_ragged", "copy"]
 
@@ -181,7 +182,10 @@ def reduce_counters(d):
         e = out.get(name, {}) if out.get(name, {}).get("source_hash") == src else {}
         e.update({"source_hash": src, "mfma_f8_flops": mops[0] * 512,
                   "mfma_busy_cycles": busy[0], "gui_active_cycles": gui[0],
-                  "mfma_busy_frac": busy[0] / (gui[0] * SIMD_COUNT), "mfma_dispatches": mops[1]})
+                  # busy cycles summed over the SIMDs, against the kernel's
+                  # active cycles on one XCD times the SIMD count
+                  "mfma_busy_frac": busy[0] / (gui[0] / XCD_COUNT * SIMD_COUNT),
+                  "mfma_dispatches": mops[1]})
         out[name] = e
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -551,8 +555,8 @@ def secondary(a):
 def profile_only(a):
     import torch
     from workloads import specs
+    from workloads import gen
     from workloads.device import CsaDecode, CsaPrefill, CsaSpecDecode, HcaCsaRagged, TinyDecode
-    copies = a.copies or 3
     if a.profile_only == "copy":
         n = 1 << 28  # 1 GiB of float32 read and 1 GiB written per copy
         src = torch.ones(n, device="cuda")
@@ -564,25 +568,30 @@ def profile_only(a):
         return
     if a.profile_only == "tiny":
         W, copies = TinyDecode(specs.TINY_FP32_DECODE), 1
-    elif a.profile_only == "decode_128k":
-        wl = specs.DECODE_128K
-        W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
-    elif a.profile_only == "decode_1m":
-        wl = specs.DECODE_1M
-        W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
-    elif a.profile_only == "spec_decode":
-        wl = specs.SPEC_DECODE_128K
-        W = CsaSpecDecode(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
+    elif a.profile_only in ("decode_128k", "decode_1m", "spec_decode"):
+        # the pool copies of the timed bench run of the same workload
+        wl = {"decode_128k": specs.DECODE_128K, "decode_1m": specs.DECODE_1M,
+              "spec_decode": specs.SPEC_DECODE_128K}[a.profile_only]
+        row = wl.index_dim // 2 + 4 if wl.index_fmt == "mxfp4" else wl.index_dim + 4
+        copies = auto_copies(int(wl.batch * (wl.seq_len // 4) * row), a.copies)
+        cls = CsaSpecDecode if a.profile_only == "spec_decode" else CsaDecode
+        W = cls(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
     elif a.profile_only == "prefill":
         W, copies = CsaPrefill(specs.PREFILL_4K), 1
     else:
-        W = HcaCsaRagged(specs.HCA_RAGGED, copies=copies)
+        wl = specs.HCA_RAGGED
+        n, lo, hi = wl.ragged
+        lens = gen.ragged_lengths(gen.rng(wl.seed), n, lo, hi)
+        per_copy = int((lens // 4).sum()) * (wl.index_dim + 4) + int((lens // wl.hca_ratio).sum()) * 644
+        copies = auto_copies(per_copy, a.copies)
+        W = HcaCsaRagged(wl, copies=copies)
     torch.cuda.synchronize()
     time.sleep(PROFILE_GAP_S)  # marks the start of the steps in a kernel trace
     for i in range(a.warmup + a.steps):
         W.step(i % copies)
     torch.cuda.synchronize()
-    print(f"profiled {a.profile_only}: {a.warmup + a.steps} eager steps", flush=True)
+    print(f"profiled {a.profile_only}: {a.warmup + a.steps} eager steps over {copies} pool copies",
+          flush=True)
 
 
 def main():

@@ -16,12 +16,16 @@ namespace csa {
 namespace {
 
 constexpr int kWavesPerWG = 4;
-constexpr int kBatch = 8;  // row slots a wave loads before preparing them
+// Row slots a wave loads before preparing them: 8 for many rows (a slot's
+// load latency then overlaps the others'), 1 for fewer, where the grid needs
+// the workgroups more than a wave needs the overlap.
+constexpr int kBatchMany = 8;
+constexpr int64_t kManyRows = 65536;
 
 // A wave takes kBatch row slots (a slot: one 128-dim row, or two 64-dim
 // rows) at a time and issues all their loads (and rope-table reads) before it
-// rotates and stores any, so that a slot's load latency overlaps the others'.
-template <int D, bool kF32In>
+// rotates and stores any.
+template <int D, bool kF32In, int kBatch>
 __global__ void __launch_bounds__(kWavesPerWG * 64)
 index_prep_kernel(const void* __restrict__ v, int64_t rows, uint32_t flags, int out_fmt,
                   void* __restrict__ out, void* __restrict__ out_scale,
@@ -67,18 +71,25 @@ hipError_t launch_index_prep(const void* v, int v_fmt, int64_t rows, int dim, ui
                              int out_fmt, void* out, void* out_scale, const int32_t* dst_rows,
                              const csa_rope& rope, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  const int64_t rows_per_wg = kWavesPerWG * kBatch * (128 / dim);
+  const int batch = rows >= kManyRows ? kBatchMany : 1;
+  const int64_t rows_per_wg = kWavesPerWG * batch * (128 / dim);
   int64_t nblocks = (rows + rows_per_wg - 1) / rows_per_wg;
   if (nblocks > 65536) nblocks = 65536;
   dim3 grid((unsigned)nblocks), block(kWavesPerWG * 64);
   const bool f32 = v_fmt == CSA_F32;
+#define CSA_IP(D, F32, B)                                                                        \
+  hipLaunchKernelGGL((index_prep_kernel<D, F32, B>), grid, block, 0, s, v, rows, flags, out_fmt, \
+                     out, out_scale, dst_rows, rope)
+#define CSA_IP_B(D, F32)                 \
+  if (batch == 1) CSA_IP(D, F32, 1);     \
+  else CSA_IP(D, F32, kBatchMany);
   if (dim == 128) {
-    if (f32) hipLaunchKernelGGL((index_prep_kernel<128, true>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows, rope);
-    else hipLaunchKernelGGL((index_prep_kernel<128, false>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows, rope);
+    if (f32) { CSA_IP_B(128, true) } else { CSA_IP_B(128, false) }
   } else {
-    if (f32) hipLaunchKernelGGL((index_prep_kernel<64, true>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows, rope);
-    else hipLaunchKernelGGL((index_prep_kernel<64, false>), grid, block, 0, s, v, rows, flags, out_fmt, out, out_scale, dst_rows, rope);
+    if (f32) { CSA_IP_B(64, true) } else { CSA_IP_B(64, false) }
   }
+#undef CSA_IP_B
+#undef CSA_IP
   return hipGetLastError();
 }
 

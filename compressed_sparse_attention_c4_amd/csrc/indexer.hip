@@ -59,10 +59,16 @@ __device__ __forceinline__ v4f mfma_fp4(const v8i& a, const v8i& b, v4f c, int s
 // in LDS exactly as the top-512 kernel's chunk pass selects them from memory.
 // Any entry of a row's top-512 is in its chunk's top-512, so the top-512 of the
 // candidates is the row's. The kCand workgroup has kSelWaves waves: the first
-// kWaves scan, all of them select (fewer keys per lane, the same barriers).
+// kScanWaves scan, all of them select (fewer keys per lane, the same barriers).
 constexpr int kSelWaves = 8;
 template <bool kCand>
 constexpr int idx_threads() { return (kCand ? kSelWaves : kWaves) * 64; }
+// Scan waves: kWaves, or (MXFP4 with the selection) all kSelWaves: an MXFP4
+// row is half as many bytes for the same matrix and epilogue work per entry,
+// so its scan is bound by the latency of that work more than by HBM, and a
+// second wave per SIMD hides it.
+template <bool kFp4, bool kCand>
+constexpr int kScanWaves() { return kFp4 && kCand ? kSelWaves : kWaves; }
 
 // Candidate lists that one workgroup of the scan writes and another reads in
 // the same launch go around the caches: the eight XCDs' L2 caches are not
@@ -179,6 +185,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K / q row
   constexpr int kTH = idx_threads<kCand>();
   constexpr int kSelE = kMaxChunk / kTH;  // keys per lane of the selections
+  constexpr int kSW = kScanWaves<kFp4, kCand>();  // waves that scan
   __shared__ int32_t s_pages[kMaxChunk / 16 + 2];      // physical pages of this chunk
   __shared__ __attribute__((aligned(16))) float s_out[kMaxChunk + 64];  // the chunk's logits
   __shared__ TopkLds L;                                  // the selections (kCand)
@@ -221,7 +228,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   const int npg = (c1 - 1) / page_size - pg0 + 1;
   for (int i = threadIdx.x; i < npg; i += idx_threads<kCand>()) s_pages[i] = ptrow[pg0 + i];
 
-  if (kCand && wave >= kWaves) {
+  if (kCand && wave >= kSW) {
     __syncthreads();  // the page ids (the scan waves pass the same barrier)
   } else {
   // Query operands: head hb*16 + col, K-elements grp*32 .. grp*32+31.
@@ -259,8 +266,8 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   // Entries go in batches of 64 (four 16-entry groups; a group never
   // straddles a page since page_size % 16 == 0 and the chunk starts on a
   // multiple of 16, so its page is wave-uniform). Wave w takes batches w,
-  // w + kWaves, ... and keeps kRing batches of loads in flight (a register
-  // ring, slot = batch % kRing). After the 16 MFMAs of a batch, one
+  // w + kWaves, ... and keeps kR batches of loads in flight (a register
+  // ring, slot = batch % kR). After the 16 MFMAs of a batch, one
   // reduce-scatter across the four lane rows leaves in row r the 64-head sum
   // of group r, so each lane stores one logit and a wave writes the batch's
   // 64 logits as one contiguous 256-byte store; the lane also loads the FP8
@@ -270,10 +277,11 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   // is branch-free: batches past the chunk load entry 0 of its first page (or
   // their page), and their logits land in LDS past the chunk and are dropped.
   const int nbatch = (c1 - c0 + 63) / 64;
-  const int nb = (nbatch - wave + kWaves - 1) / kWaves;  // batches of this wave
-  v8i b[kRing][4];
-  int sb[kRing][4];
-  float ks[kRing];
+  const int nb = (nbatch - wave + kSW - 1) / kSW;  // batches of this wave
+  constexpr int kR = kRing;  // (measured on the MXFP4 scan at 1M: a 4-batch ring is slower)
+  v8i b[kR][4];
+  int sb[kR][4];
+  float ks[kR];
   auto slot_of = [&](int j, int g0) __attribute__((always_inline)) {
     const int pg = s_pages[g0 < c1 ? g0 / page_size - pg0 : 0];
     return (j < c1) ? (int64_t)pg * page_size + j % page_size : (int64_t)s_pages[0] * page_size;
@@ -283,11 +291,11 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   // anyway (their logits are dropped)
   const int last_pg = npg - 1;
   auto batch_page = [&](int i) __attribute__((always_inline)) {
-    return (int64_t)s_pages[min(i * kWaves + wave, last_pg)] * 64;
+    return (int64_t)s_pages[min(i * kSW + wave, last_pg)] * 64;
   };
   auto issue = [&](int i, auto R) __attribute__((always_inline)) {
     constexpr int r = decltype(R)::value;
-    const int e0 = c0 + (i * kWaves + wave) * 64;  // first entry of the batch
+    const int e0 = c0 + (i * kSW + wave) * 64;  // first entry of the batch
     const int64_t pbase = kPage64 ? batch_page(i) : 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -338,16 +346,24 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
     const float tot = rows4_reduce_scatter(pk[0], pk[1], pk[2], pk[3]);
     // entry within the chunk; a batch past this wave's last lands in the
     // spare 64 slots at the end
-    const int jl = i < nb ? (i * kWaves + wave) * 64 + 16 * grp + col : kMaxChunk + lane;
+    const int jl = i < nb ? (i * kSW + wave) * 64 + 16 * grp + col : kMaxChunk + lane;
     s_out[jl] = tot * ks[r];
-    issue(i + kRing, R);  // refill the slot just consumed
+    issue(i + kR, R);  // refill the slot just consumed
   };
-  static_assert(kRing == 2, "the batch loop below is unrolled by hand for two slots");
+  static_assert(kR == 2 || kR == 4, "the batch loop below is unrolled by hand for 2 or 4 slots");
   issue(0, std::integral_constant<int, 0>{});
   issue(1, std::integral_constant<int, 1>{});
-  for (int i0 = 0; i0 < nb; i0 += kRing) {
+  if constexpr (kR == 4) {
+    issue(2, std::integral_constant<int, 2>{});
+    issue(3, std::integral_constant<int, 3>{});
+  }
+  for (int i0 = 0; i0 < nb; i0 += kR) {
     step(i0, std::integral_constant<int, 0>{});
     step(i0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (kR == 4) {
+      step(i0 + 2, std::integral_constant<int, 2>{});
+      step(i0 + 3, std::integral_constant<int, 3>{});
+    }
   }
   }  // scan waves
   __syncthreads();
