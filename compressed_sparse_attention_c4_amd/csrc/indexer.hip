@@ -443,8 +443,9 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     const void* __restrict__ kscale, float* __restrict__ logits, int64_t ld,
                     int ppc, CandOut co) {
   static_assert(kRows >= 2 && kRows <= kRowsPerWG, "rows per workgroup");
-  static_assert(!kSel || kRows == kRowsPerWG, "the fused selection takes one wave per row");
-  constexpr int kWpr = kRowsPerWG / kRows;  // waves per row
+  // waves per row: with the fused selection one (its running top-512 belongs
+  // to one wave; the waves past kRows only stage), else 8 / kRows
+  constexpr int kWpr = kSel ? 1 : kRowsPerWG / kRows;
   constexpr int kPage = 64;                          // entries per page (= tile)
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K row
   constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per row
@@ -813,9 +814,13 @@ int indexer_rows_sel_ranges(int64_t T, int H_I, int D_I, const csa_index_pool& k
                             int64_t max_row_len, uint32_t prep) {
   if (k.fmt != CSA_FP8_E4M3 && k.fmt != CSA_MXFP4) return 0;
   if (H_I != kHeads || D_I != kDim || T == 0 || max_row_len == 0) return 0;
-  if (rows_kernel_rows(T, k, prep) != kRowsPerWG) return 0;
+  const int rows = rows_kernel_rows(T, k, prep);
+  // 8 rows only: with fewer, one wave per row (the selection's unit) leaves
+  // waves idle (multi-token decode, 4 rows: 77.8 us vs 49.5 + 20.0 us of
+  // logits and two-pass top-512)
+  if (rows != kRowsPerWG) return 0;
   int ppc;
-  const int ranges = rows_ranges(T, kRowsPerWG, max_row_len, true, ppc);
+  const int ranges = rows_ranges(T, rows, max_row_len, true, ppc);
   return ranges * kTopK <= kCandFinalMax ? ranges : 0;
 }
 
@@ -888,7 +893,7 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
   }
   const int64_t chunk = scan_chunk(T, max_row_len);
   const bool rsel = cand && cand->rows_sel;
-  const int rows = rsel ? kRowsPerWG : (cand ? 0 : rows_kernel_rows(T, k, prep));
+  const int rows = (rsel || !cand) ? rows_kernel_rows(T, k, prep) : 0;
   if (rows) {
     const int groups = (int)((T + rows - 1) / rows);
     int ppc;
@@ -900,7 +905,7 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
                      w, row_seq, row_len, T, page_table, pt_stride, (const uint8_t*)k.data,       \
                      k.scale, logits, ld, ppc, co)
     const bool fp4 = k.fmt == CSA_MXFP4;
-    if (rsel) {
+    if (rsel) {  // rows == 8 (indexer_rows_sel_ranges)
       if (fp4) CSA_ROWS(true, kRowsPerWG, true);
       else CSA_ROWS(false, kRowsPerWG, true);
       return hipGetLastError();
