@@ -11,8 +11,9 @@
 // key seen so far. Elements arrive with a cheaper pre-key (the sign-flip image
 // of the float's bits: equal to the key except that -0 sits one below +0 and
 // NaNs fall outside the keys of -inf..+inf); the buffer's pre-keys are turned
-// into keys when it is compacted, and thr is never the one value (that of -0)
-// where comparing a pre-key and comparing the key against it could differ. An element whose key is not above thr is dropped as it
+// into keys when it is compacted and when it is finished, and thr is never
+// the one value (that of -0) where comparing a pre-key and comparing the key
+// against it could differ. An element whose key is not above thr is dropped as it
 // arrives: at least K elements seen before it have a key >= thr >= its key and
 // a lower index, so all of them rank above it. When the buffer runs short of
 // room it is compacted. A histogram of the buffer's keys (this wave alone; 256
@@ -74,9 +75,23 @@ struct WaveTopk {
   // True when the buffer may not take two more 64-element batches.
   __device__ __forceinline__ bool short_of_room() const { return cnt > kCap - 128; }
 
-  // Reduces the buffer to its exact top K (when it holds more), in order.
+  // The key of a pre-key: -0 ranks as +0, NaN as 0.
+  static __device__ __forceinline__ uint32_t key_of(uint32_t pk) {
+    return pk == 0x7FFFFFFFu ? 0x80000000u : (pk > 0xFF800000u || pk < 0x007FFFFFu ? 0u : pk);
+  }
+
+  // Reduces the buffer to its exact top K (when it holds more), in order, and
+  // leaves keys (not pre-keys) in all of it.
   __device__ __forceinline__ void finish() {
-    if (cnt > kK) compact(true);
+    if (cnt > kK) {
+      compact(true);
+      return;
+    }
+    const int lane = threadIdx.x & 63;
+    __builtin_amdgcn_wave_barrier();
+    for (int e = nkey + lane; e < cnt; e += 64) key[e] = key_of(key[e]);
+    __builtin_amdgcn_wave_barrier();
+    nkey = cnt;
   }
 
   __device__ __forceinline__ void compact(bool exact) {
@@ -89,8 +104,8 @@ struct WaveTopk {
     for (int i = 0; i < kPer; ++i) {
       const int e = i * 64 + lane;
       uint32_t kv = key[e];
-      if (e >= nkey && e < cnt) {  // pre-key -> key: -0 ranks as +0, NaN as 0
-        kv = kv == 0x7FFFFFFFu ? 0x80000000u : (kv > 0xFF800000u || kv < 0x007FFFFFu ? 0u : kv);
+      if (e >= nkey && e < cnt) {  // pre-key -> key
+        kv = key_of(kv);
         key[e] = kv;
       }
       if (e < cnt) {

@@ -675,6 +675,73 @@ def test_indexer_topk512_many_rows(csa, fmt, case):
         assert np.sum(lg[t, :row_len[t]] == kth) > 1
 
 
+@pytest.mark.parametrize("case", ["rising", "special"])
+def test_indexer_topk512_many_rows_adversarial(csa, case):
+    """The row-block kernel's running top-512 on the inputs that are hardest
+    for it, bit for bit against indexer_score + topk512_page_select:
+    "rising": every index-K row holds the same FP8 codes with a scale that
+    grows with the entry, so each row's logits rise with j and every page's
+    entries pass the threshold (a compaction every few pages);
+    "special": head weights with NaN, +-inf, -0 and negative values in some
+    rows, giving NaN, infinite and signed-zero logits (NaN ranks lowest, -0
+    equals +0)."""
+    g = gen.rng(1450 + len(case))
+    L1, T = 12000, 264            # 3000 entries per row at most, 47 pages, 5 ranges
+    N1 = L1 // 4
+    pt, pool, num_pages = _index_case(g, "fp8", 1, [N1])
+    if case == "rising":
+        data = np.broadcast_to(pool.data[:1], pool.data.shape).copy()
+        # entry j's scale grows with its logical index j: slot -> j through the table
+        slot_j = np.zeros(num_pages * 64, np.int64)
+        pages = pt[0]
+        for j in range(N1):
+            slot_j[pages[j // 64] * 64 + j % 64] = j
+        scale = (pool.scale[0] * (1.0 + slot_j / N1)).astype(np.float32)
+        pool = O.IndexPool(data, scale, "fp8")
+    pos = np.arange(L1 - T, L1)
+    row_seq = np.zeros(T, np.int32)
+    row_len = np.minimum(N1, (pos + 1) // 4).astype(np.int32)
+    qraw = gen.normal(g, (T, 64, 128))
+    if case == "rising":
+        # q sign-aligned with the shared K codes (no rotation of q, so that
+        # every head's dot product is positive)
+        qraw = np.abs(qraw) * np.sign(pool.data[0].view(np.int8).astype(np.float64) + 0.5)[None, None, :]
+    qcodes, qsc = O.index_prep(qraw, case != "rising", "fp8")
+    w = gen.uniform(g, (T, 64)).astype(np.float32)
+    if case == "special":
+        w[3, :] = np.nan                     # every logit NaN
+        w[5, 7] = np.inf                     # +inf or NaN logits
+        w[6, :] = -0.0                       # all logits zero (+0 or -0)
+        w[7, :] = -w[7, :]                   # all logits <= 0
+        w[9, 11] = -np.inf
+    dpool = index_pool_to_device(pool, 64, 128)
+    drs, drl, dpt = t_dev(row_seq), t_dev(row_len), t_dev(pt)
+    qs = t_dev(qsc.astype(np.float32))
+    phys = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    logi = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    csa.indexer_topk512(t_dev(qcodes), t_dev(w), drs, drl, N1, dpt, dpool, phys, logi,
+                        q_fmt=csa.CSA_FP8_E4M3, q_scale=qs)
+    logits = torch.full((T, N1), float("nan"), device=DEV)
+    csa.indexer_score(t_dev(qcodes), t_dev(w), drs, drl, N1, dpt, dpool, logits,
+                      q_fmt=csa.CSA_FP8_E4M3, q_scale=qs)
+    phys2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    logi2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    csa.topk512_page_select(logits, drl, drs, dpt, phys2, logi2)
+    gl, wl = logi.cpu().numpy(), logi2.cpu().numpy()
+    bad = [t for t in range(T) if not np.array_equal(gl[t], wl[t])]
+    assert not bad, f"{len(bad)} rows differ from the two calls, first {bad[:5]}"
+    assert np.array_equal(phys.cpu().numpy(), phys2.cpu().numpy())
+    lg = logits.cpu().numpy()
+    if case == "rising":  # the logits do rise with j: the selection is each row's last 512
+        t = T - 1
+        n = row_len[t]
+        assert np.all(np.diff(lg[t, :n]) >= 0)
+        assert np.array_equal(gl[t], np.arange(n - 512, n))
+    else:
+        assert np.isnan(lg[3, :row_len[3]]).all()
+        assert np.array_equal(gl[3], np.arange(512))  # all NaN: the lowest indices
+
+
 @pytest.mark.parametrize("fmt,q_len", [("fp8", 4), ("mxfp4", 8), ("fp8", 2), ("fp8", 6), ("fp8", 5),
                                        ("mxfp4", 3), ("fp8", 10)])
 def test_indexer_rows_per_seq(csa, fmt, q_len):
