@@ -742,6 +742,76 @@ def test_indexer_topk512_many_rows_adversarial(csa, case):
         assert np.array_equal(gl[3], np.arange(512))  # all NaN: the lowest indices
 
 
+@pytest.mark.parametrize("shape", ["wide", "long"])
+@pytest.mark.parametrize("case", ["ties", "outliers", "special"])
+def test_indexer_topk512_decode_adversarial(csa, case, shape):
+    """The decode scan's selection on inputs that defeat its shortcuts, bit
+    for bit against indexer_score + topk512_page_select. Shapes: "wide", 32
+    rows of ~32K entries (4096-entry chunks, 8 per row, a final pass);
+    "long", 4 rows of ~131K (2048-entry chunks, 64 per row, finished inside
+    the scan from the candidates that reach the chunks' bounds). Cases:
+    "ties": index-K rows drawn from six distinct rows, so a row's logits take
+    six values (every candidate reaches the bound); "outliers": a few entries
+    with scales 1000x the rest, so the key range is wide and the threshold's
+    bucket crowded; "special": head weights with NaN, +-inf, -0 and negative
+    values (NaN logits rank lowest, -0 equals +0)."""
+    g = gen.rng(1470 + len(case) + 10 * len(shape))
+    if shape == "wide":
+        T, pps = 32, 512
+        lens = [32768 - 997 * (t % 5) for t in range(T)]
+    else:
+        T, pps = 4, 2048
+        lens = [131072, 131072 - 700, 131072 - 2048 * 9 - 5, 70000]
+    num_pages = T * pps + 3
+    pt = gen.page_table(g, T, pps, num_pages)
+    distinct = 6 if case == "ties" else 4096
+    kraw = gen.normal(g, (distinct, 128))
+    d0, s0 = O.index_prep(kraw, True, "fp8")
+    pick = g.integers(0, distinct, num_pages * 64)
+    data, scale = d0[pick], s0[pick].astype(np.float32)
+    if case == "outliers":
+        scale[g.integers(0, num_pages * 64, 40)] *= 1000.0
+    pool = O.IndexPool(data, scale, "fp8")
+    qraw = gen.normal(g, (T, 64, 128))
+    qcodes, qsc = O.index_prep(qraw, True, "fp8")
+    w = gen.uniform(g, (T, 64)).astype(np.float32)
+    nan_row = 3 if shape == "wide" else 1
+    if case == "special":
+        w[nan_row, :] = np.nan
+        w[2, 7] = np.inf
+        w[T - 1, :] = -0.0
+        w[0, :] = -w[0, :]
+        w[T - 2, 11] = -np.inf
+    dpool = index_pool_to_device(pool, 64, 128)
+    drs, drl, dpt = t_dev(np.arange(T, dtype=np.int32)), t_dev(np.array(lens, np.int32)), t_dev(pt)
+    qs = t_dev(qsc.astype(np.float32))
+    N = max(lens)
+    phys = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    logi = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    csa.indexer_topk512(t_dev(qcodes), t_dev(w), drs, drl, N, dpt, dpool, phys, logi,
+                        q_fmt=csa.CSA_FP8_E4M3, q_scale=qs)
+    logits = torch.full((T, N), float("nan"), device=DEV)
+    csa.indexer_score(t_dev(qcodes), t_dev(w), drs, drl, N, dpt, dpool, logits,
+                      q_fmt=csa.CSA_FP8_E4M3, q_scale=qs)
+    phys2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    logi2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    csa.topk512_page_select(logits, drl, drs, dpt, phys2, logi2)
+    gl, wl = logi.cpu().numpy(), logi2.cpu().numpy()
+    bad = [t for t in range(T) if not np.array_equal(gl[t], wl[t])]
+    assert not bad, f"{len(bad)} rows differ from the two calls, first {bad[:5]}"
+    assert np.array_equal(phys.cpu().numpy(), phys2.cpu().numpy())
+    lg = logits.cpu().numpy()
+    if case == "special":
+        assert np.isnan(lg[nan_row, :lens[nan_row]]).all()
+        assert np.array_equal(gl[nan_row], np.arange(512))  # all NaN: the lowest indices
+    else:
+        # each row's selection is the top-512 by (logit desc, index asc) of its logits
+        for t in (0, 1, T - 1):
+            n = lens[t]
+            order = np.lexsort((np.arange(n), -lg[t, :n].astype(np.float64)))[:512]
+            assert np.array_equal(gl[t], np.sort(order)), f"row {t}"
+
+
 @pytest.mark.parametrize("fmt,q_len", [("fp8", 4), ("mxfp4", 8), ("fp8", 2), ("fp8", 6), ("fp8", 5),
                                        ("mxfp4", 3), ("fp8", 10)])
 def test_indexer_rows_per_seq(csa, fmt, q_len):
