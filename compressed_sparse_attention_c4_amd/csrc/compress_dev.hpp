@@ -91,11 +91,8 @@ __device__ __forceinline__ void compress_entry(const void* __restrict__ x, int64
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(c[i]));
     amax = wave_max(amax);
     const float sc = fmaxf(amax, kFltMin) / kE4m3Max;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(c[i] / sc) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(c[4 + i] / sc) << (8 * i);
+    const uint32_t lo = e4m3x2(c[0] / sc, c[1] / sc) | (e4m3x2(c[2] / sc, c[3] / sc) << 16);
+    const uint32_t hi = e4m3x2(c[4] / sc, c[5] / sc) | (e4m3x2(c[6] / sc, c[7] / sc) << 16);
     uint8_t* lat = reinterpret_cast<uint8_t*>(out_latent) + slot * kLatent + 8 * lane;
     *reinterpret_cast<uint2*>(lat) = make_uint2(lo, hi);
     reinterpret_cast<uint16_t*>(out_rope)[slot * kRope + lane] = f32_to_bf16(c[8]);

@@ -59,7 +59,7 @@ __device__ __forceinline__ void prep_and_store(float x0, float x1, bool valid, b
     float amax = fmaxf(fabsf(x0), fabsf(x1));
     amax = group_max<D / 2>(amax);
     const float sc = fmaxf(amax, kFltMin) / kE4m3Max;
-    const uint32_t c = f32_to_e4m3(x0 / sc) | (f32_to_e4m3(x1 / sc) << 8);
+    const uint32_t c = e4m3x2(x0 / sc, x1 / sc);
     if (valid) {
       reinterpret_cast<uint16_t*>(out)[dst * (D / 2) + li] = (uint16_t)c;
       if (li == 0) reinterpret_cast<float*>(out_scale)[dst] = sc;
