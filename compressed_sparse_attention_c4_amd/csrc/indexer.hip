@@ -558,12 +558,17 @@ indexer_rows_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
   // logit store (lanes of rows past their row_len are dropped by the buffer)
   // ReLU and head weights of one 16-entry group, summed over this lane's 16
   // heads (the other heads of the entry are in the other lane rows)
+  // (a wave issuing its matrix ops runs at raised priority, so that the
+  // matrix cores are fed first and the other waves' epilogues fill the gaps:
+  // prefill 1187 -> 1129 us)
   auto head_sum = [&](const v8i& bb, int sb) __attribute__((always_inline)) {
     v4f acc[4];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
       acc[hb] = kFp4 ? mfma_fp4(a[hb], bb, v4f{0.f, 0.f, 0.f, 0.f}, sa[hb], sb)
                      : mfma_fp8(a[hb], bb, v4f{0.f, 0.f, 0.f, 0.f});
+    __builtin_amdgcn_s_setprio(0);
     float v = 0.f;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
