@@ -200,9 +200,17 @@ class IndexPool:
                            self.num_pages)
 
 
+def _gate_sizes(name, gate_w, gate_b, ratio):
+    # the kernels read 576 gate weights and one positional bias per block row
+    if gate_w.numel() < 576 or gate_b.numel() < ratio:
+        raise ValueError(f"{name}: gate_w needs 576 values and gate_b {ratio} (one per block row), "
+                         f"got {gate_w.numel()} and {gate_b.numel()}")
+
+
 def c4_compress(x, cu_rows, start_pos, max_rows, ratio, gate_w, gate_b, page_table, out: KvPool,
                 stream=None):
     B = cu_rows.numel() - 1
+    _gate_sizes("c4_compress", gate_w, gate_b, int(ratio))
     _check("c4_compress", _c4_compress(
         _ptr(x), _fmt_of(x), _ptr(cu_rows), _ptr(start_pos), B, int(max_rows), int(ratio),
         _ptr(gate_w), _ptr(gate_b), _ptr(page_table), page_table.shape[-1], out.c(),
@@ -226,6 +234,7 @@ def csa_decode_prep(x, pos, gate_w, gate_b, page_table, c4: KvPool, raw_page_tab
     rope_table [positions, rope_dim/2, 2] float32 with CSA_PREP_ROPE in flags (both the
     block's index-K row and the query rows are rotated at pos[b])."""
     B, ratio = x.shape[0], x.shape[1]
+    _gate_sizes("csa_decode_prep", gate_w, gate_b, ratio)
     kq = k_rows if k_rows is not None else q_rows
     H_I = q_rows.shape[1] if q_rows is not None else 0
     kp = kpool.c() if kpool is not None else _IndexPoolC(None, None, CSA_F32, 128, c4.page_size, 0)

@@ -164,7 +164,7 @@ def test_debug_compress_bad_page(csa):
     x = torch.from_numpy(gen.normal(g, (B * rows, 576)).astype(np.float32)).to(DEV).to(torch.bfloat16)
     cu = t_dev(np.array([0, rows, 2 * rows], np.int32))
     start = t_dev(np.array([0, 64 * 4], np.int32))  # second sequence: entries 64..79, page 1
-    gw, gb = torch.zeros(576, device=DEV), torch.zeros(1, device=DEV)
+    gw, gb = torch.zeros(576, device=DEV), torch.zeros(ratio, device=DEV)
     bad = pt.copy()
     bad[1, 1] = pool.num_pages + 1  # the second spare page
     _expect_bounds(csa, lambda: csa.c4_compress(x, cu, start, rows, ratio, gw, gb, t_dev(bad), pool))
