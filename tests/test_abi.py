@@ -277,3 +277,26 @@ def test_hisparse_rejects_bad_arguments(lib):
     assert call(step=-1) == INVALID
     assert call(sel=None) == INVALID
     assert call(R=0) == 0
+
+
+def test_binding_rejects_short_gate_parameters():
+    """The binding checks the gate sizes before calling the library: the
+    compressor reads 576 weights and one positional bias per block row, so a
+    shorter tensor would be read past its end."""
+    if not os.path.exists(LIB):
+        pytest.skip("libcsa.so not built")
+    import torch
+    import compressed_sparse_attention_c4_amd as csa
+    x = torch.zeros(8, 576)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    start = torch.zeros(1, dtype=torch.int32)
+    pt = torch.zeros(1, 1, dtype=torch.int32)
+    pool = csa.KvPool(torch.zeros(1, 64, 512, dtype=torch.uint8), torch.zeros(1, 64),
+                      torch.zeros(1, 64, 64, dtype=torch.bfloat16), csa.CSA_FP8_E4M3, 64)
+    with pytest.raises(ValueError, match="gate_b"):
+        csa.c4_compress(x, cu, start, 8, 4, torch.zeros(576), torch.zeros(1), pt, pool)
+    with pytest.raises(ValueError, match="gate_w"):
+        csa.c4_compress(x, cu, start, 8, 4, torch.zeros(64), torch.zeros(4), pt, pool)
+    with pytest.raises(ValueError, match="gate_b"):
+        csa.csa_decode_prep(torch.zeros(2, 4, 576), torch.zeros(2, dtype=torch.int32),
+                            torch.zeros(576), torch.zeros(3), pt, pool, pt, pool)
