@@ -675,10 +675,13 @@ def test_indexer_topk512_many_rows(csa, fmt, case):
         assert np.sum(lg[t, :row_len[t]] == kth) > 1
 
 
+@pytest.mark.parametrize("per_seq", [0, 4])
 @pytest.mark.parametrize("case", ["rising", "special"])
-def test_indexer_topk512_many_rows_adversarial(csa, case):
+def test_indexer_topk512_many_rows_adversarial(csa, case, per_seq):
     """The row-block kernel's running top-512 on the inputs that are hardest
-    for it, bit for bit against indexer_score + topk512_page_select:
+    for it, bit for bit against indexer_score + topk512_page_select, with 8
+    rows per workgroup (a wave per row) and, with the rows-per-sequence hint
+    4, with 4 rows per workgroup (two waves per row, lists merged):
     "rising": every index-K row holds the same FP8 codes with a scale that
     grows with the entry, so each row's logits rise with j and every page's
     entries pass the threshold (a compaction every few pages);
@@ -717,13 +720,14 @@ def test_indexer_topk512_many_rows_adversarial(csa, case):
     dpool = index_pool_to_device(pool, 64, 128)
     drs, drl, dpt = t_dev(row_seq), t_dev(row_len), t_dev(pt)
     qs = t_dev(qsc.astype(np.float32))
+    hint = csa.CSA_ROWS_PER_SEQ(per_seq) if per_seq else 0
     phys = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
     logi = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
     csa.indexer_topk512(t_dev(qcodes), t_dev(w), drs, drl, N1, dpt, dpool, phys, logi,
-                        q_fmt=csa.CSA_FP8_E4M3, q_scale=qs)
+                        q_fmt=csa.CSA_FP8_E4M3, q_scale=qs, prep=hint)
     logits = torch.full((T, N1), float("nan"), device=DEV)
     csa.indexer_score(t_dev(qcodes), t_dev(w), drs, drl, N1, dpt, dpool, logits,
-                      q_fmt=csa.CSA_FP8_E4M3, q_scale=qs)
+                      q_fmt=csa.CSA_FP8_E4M3, q_scale=qs, prep=hint)
     phys2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
     logi2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
     csa.topk512_page_select(logits, drl, drs, dpt, phys2, logi2)
