@@ -200,6 +200,13 @@ class IndexPool:
                            self.num_pages)
 
 
+def _need(name, what, t, n):
+    """The library takes raw pointers and cannot see a tensor's size: a tensor
+    smaller than the call implies would be read or written past its end."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name}: {what} has {t.numel()} elements, the call needs {n}")
+
+
 def _gate_sizes(name, gate_w, gate_b, ratio):
     # the kernels read 576 gate weights and one positional bias per block row
     if gate_w.numel() < 576 or gate_b.numel() < ratio:
@@ -222,6 +229,14 @@ def csa_index_prep(v, dim, flags, out_fmt, out, out_scale=None, dst_rows=None, s
     """rope_table [positions, rope_dim/2, 2] float32 (cos, sin) and rope_pos
     int32 (one per rows_per_pos rows) are used with CSA_PREP_ROPE in flags."""
     rows = v.numel() // dim
+    if dst_rows is None:  # (with dst_rows the destinations are device values)
+        row_bytes = {CSA_F32: 4 * dim, CSA_FP8_E4M3: dim, CSA_MXFP4: dim // 2}.get(int(out_fmt), 0)
+        scale_bytes = {CSA_FP8_E4M3: 4, CSA_MXFP4: dim // 32}.get(int(out_fmt), 0)
+        for what, t, nb in (("out", out, rows * row_bytes), ("out_scale", out_scale, rows * scale_bytes)):
+            if t is not None and t.numel() * t.element_size() < nb:
+                raise ValueError(f"csa_index_prep: {what} has {t.numel() * t.element_size()} bytes, "
+                                 f"the call needs {nb}")
+    _need("csa_index_prep", "dst_rows", dst_rows, rows)
     _check("csa_index_prep", _csa_index_prep(
         _ptr(v), _fmt_of(v), rows, int(dim), int(flags), int(out_fmt), _ptr(out), _ptr(out_scale),
         _ptr(dst_rows), _rope(rope_pos, rope_table, rows_per_pos), _stream(stream)))
@@ -250,6 +265,10 @@ def indexer_score(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPool,
                   stream=None):
     T, H_I = w.shape
     D_I = k.dim
+    for what, t in (("row_seq", row_seq), ("row_len", row_len)):
+        _need("indexer_score", what, t, T)
+    if logits.dim() < 2 or logits.shape[0] < T:
+        raise ValueError(f"indexer_score: logits needs {T} rows of at least {max_row_len}")
     if ws is None and prep & CSA_PREP_QUANT and q_used is None:
         ws = _scratch(csa_workspace_size(CSA_OP_INDEXER, T, max_row_len, H_I), q.device, stream)
     _check("indexer_score", _indexer_score(
@@ -266,6 +285,10 @@ def indexer_topk512(q, w, row_seq, row_len, max_row_len, page_table, k: IndexPoo
     A caller's ws must start zero-filled (its first bytes are counters that every
     call leaves at zero)."""
     T, H_I = w.shape
+    for what, t in (("row_seq", row_seq), ("row_len", row_len)):
+        _need("indexer_topk512", what, t, T)
+    _need("indexer_topk512", "phys_idx", phys_idx, T * CSA_TOPK)
+    _need("indexer_topk512", "logical_idx", logical_idx, T * CSA_TOPK)
     if ws is None:  # zero-filled: the fused selection's counters start at zero
         ws = _scratch(csa_workspace_size(CSA_OP_INDEXER_TOPK, T, max_row_len, H_I), q.device, stream,
                       zero=True)
@@ -291,6 +314,10 @@ def indexer_topk512_noalloc(q, w, row_seq, row_len, max_row_len, page_table, k: 
     allocation); raises CsaError (CSA_ERR_WORKSPACE) when the call needs more
     than CSA_NOALLOC_SCRATCH_BYTES."""
     T, H_I = w.shape
+    for what, t in (("row_seq", row_seq), ("row_len", row_len)):
+        _need("indexer_topk512_noalloc", what, t, T)
+    _need("indexer_topk512_noalloc", "phys_idx", phys_idx, T * CSA_TOPK)
+    _need("indexer_topk512_noalloc", "logical_idx", logical_idx, T * CSA_TOPK)
     _check("indexer_topk512_noalloc", _indexer_topk_na(
         _ptr(q), _fmt_of(q, q_fmt), _ptr(q_scale), int(prep), _ptr(w), T, H_I, k.dim, _ptr(row_seq),
         _ptr(row_len), int(max_row_len), _ptr(page_table), page_table.shape[-1], k.c(),
@@ -301,6 +328,10 @@ def topk512_page_select(logits, row_len, row_seq, page_table, phys_idx, logical_
                         c4_page_size=CSA_C4_PAGE, ws=None, stream=None):
     R = row_len.numel()
     ld = logits.shape[-1]
+    _need("topk512_page_select", "logits", logits, R * ld)
+    _need("topk512_page_select", "row_seq", row_seq, R)
+    _need("topk512_page_select", "phys_idx", phys_idx, R * CSA_TOPK)
+    _need("topk512_page_select", "logical_idx", logical_idx, R * CSA_TOPK)
     if ws is None:
         ws = _scratch(csa_workspace_size(CSA_OP_TOPK, R, ld, 1), logits.device, stream)
     _check("topk512_page_select", _topk(
@@ -315,6 +346,10 @@ def topk_page_select(logits, row_len, row_seq, page_table, k, phys_idx, logical_
     logical_idx are [R, k] int32."""
     R = row_len.numel()
     ld = logits.shape[-1]
+    _need("topk_page_select", "logits", logits, R * ld)
+    _need("topk_page_select", "row_seq", row_seq, R)
+    _need("topk_page_select", "phys_idx", phys_idx, R * int(k))
+    _need("topk_page_select", "logical_idx", logical_idx, R * int(k))
     if ws is None:
         ws = _scratch(csa_workspace_size(CSA_OP_TOPK_K, R, ld, int(k)), logits.device, stream)
     _check("topk_page_select", _topk_k(
@@ -328,6 +363,8 @@ def hisparse_swap_in(logical_idx, row_seq, far: KvPool, far_page_table, near: Kv
     """Stage the selection logical_idx [R, k] in the near pool; slot_of
     [S, max_entries], owner / last_use [S, hot_slots] int32 state; near_idx [R, k]."""
     R, k = logical_idx.shape
+    _need("hisparse_swap_in", "row_seq", row_seq, R)
+    _need("hisparse_swap_in", "near_idx", near_idx, R * k)
     _check("hisparse_swap_in", _hisparse(
         _ptr(logical_idx), R, k, _ptr(row_seq), far.c(), _ptr(far_page_table), far_page_table.shape[-1],
         near.c(), int(hot_slots), _ptr(slot_of), slot_of.shape[-1], _ptr(owner), _ptr(last_use),
@@ -344,6 +381,10 @@ def csa_sparse_attn(q, q_seq, q_pos, phys_idx, c4: KvPool, raw: KvPool, raw_page
                     softmax_scale, out, ws=None, stream=None):
     T, H = q.shape[0], q.shape[1]
     k_sel = phys_idx.shape[-1]
+    for what, t in (("q_seq", q_seq), ("q_pos", q_pos)):
+        _need("csa_sparse_attn", what, t, T)
+    _need("csa_sparse_attn", "phys_idx", phys_idx, T * k_sel)
+    _need("csa_sparse_attn", "out", out, T * H * 512)
     op = CSA_OP_CSA_ATTN_F32 if c4.fmt == CSA_F32 else CSA_OP_CSA_ATTN
     ws = _attn_ws(op, T, k_sel + window, H, q.device, ws, stream)
     _check("csa_sparse_attn", _csa_attn(
@@ -355,6 +396,9 @@ def csa_sparse_attn(q, q_seq, q_pos, phys_idx, c4: KvPool, raw: KvPool, raw_page
 def hca_dense_attn(q, q_seq, q_pos, max_len, ratio, hca: KvPool, hca_page_table, raw: KvPool,
                    raw_page_table, window, softmax_scale, out, ws=None, stream=None):
     T, H = q.shape[0], q.shape[1]
+    for what, t in (("q_seq", q_seq), ("q_pos", q_pos)):
+        _need("hca_dense_attn", what, t, T)
+    _need("hca_dense_attn", "out", out, T * H * 512)
     op = CSA_OP_HCA_ATTN_F32 if hca.fmt == CSA_F32 else CSA_OP_HCA_ATTN
     ws = _attn_ws(op, T, max_len // ratio + window, H, q.device, ws, stream)
     _check("hca_dense_attn", _hca_attn(

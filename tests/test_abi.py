@@ -300,3 +300,35 @@ def test_binding_rejects_short_gate_parameters():
     with pytest.raises(ValueError, match="gate_b"):
         csa.csa_decode_prep(torch.zeros(2, 4, 576), torch.zeros(2, dtype=torch.int32),
                             torch.zeros(576), torch.zeros(3), pt, pool, pt, pool)
+
+
+def test_binding_rejects_short_buffers():
+    """The binding compares the tensors it passes with the sizes the call
+    implies (the library sees only pointers)."""
+    if not os.path.exists(LIB):
+        pytest.skip("libcsa.so not built")
+    import torch
+    import compressed_sparse_attention_c4_amd as csa
+    T = 4
+    q, w = torch.zeros(T, 64, 128), torch.zeros(T, 64)
+    rs, rl = torch.zeros(T, dtype=torch.int32), torch.zeros(T, dtype=torch.int32)
+    pt = torch.zeros(T, 1, dtype=torch.int32)
+    pool = csa.IndexPool(torch.zeros(1, 64, 128, dtype=torch.uint8), torch.zeros(1, 64),
+                         csa.CSA_FP8_E4M3, 128, 64)
+    with pytest.raises(ValueError, match="phys_idx"):
+        csa.indexer_topk512(q, w, rs, rl, 64, pt, pool, torch.zeros(T, 100, dtype=torch.int32))
+    with pytest.raises(ValueError, match="row_len"):
+        csa.indexer_topk512(q, w, rs, rl[:2], 64, pt, pool, torch.zeros(T, 512, dtype=torch.int32))
+    with pytest.raises(ValueError, match="logits"):
+        csa.indexer_score(q, w, rs, rl, 64, pt, pool, torch.zeros(T - 1, 64))
+    with pytest.raises(ValueError, match="phys_idx"):
+        csa.topk_page_select(torch.zeros(T, 64), rl, rs, pt, 8, torch.zeros(T, 4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="out"):
+        csa.csa_index_prep(torch.zeros(T, 128), 128, 0, csa.CSA_FP8_E4M3, torch.zeros(T * 64, dtype=torch.uint8),
+                           torch.zeros(T))
+    kv = csa.KvPool(torch.zeros(1, 64, 512, dtype=torch.uint8), torch.zeros(1, 64),
+                    torch.zeros(1, 64, 64, dtype=torch.bfloat16), csa.CSA_FP8_E4M3, 64)
+    with pytest.raises(ValueError, match="out"):
+        csa.csa_sparse_attn(torch.zeros(T, 64, 576, dtype=torch.bfloat16), rs, rs,
+                            torch.zeros(T, 512, dtype=torch.int32), kv, kv, pt, 128, 0.04,
+                            torch.zeros(T, 64, 256, dtype=torch.bfloat16))
