@@ -951,13 +951,13 @@ TwoPhaseWs two_phase_ws(int64_t T, int H, int e_pad) {
 }
 
 // fp32 pools and queries (small configurations). A query's entry list is cut
-// into 32-entry chunks; a workgroup stages one chunk (576 floats per entry,
+// into 16-entry chunks; a workgroup stages one chunk (576 floats per entry,
 // read as coalesced 16-byte loads) and the query rows of up to 16 heads in
 // LDS, scores the chunk, takes each head's max and exponent sum over it and
 // the partial P V. attn_f32_combine_kernel merges the chunks of a (query,
 // head) exactly (each partial rescaled by exp(m_c - M)); with a single chunk
 // the first kernel writes the output itself. An empty list gives zeros.
-constexpr int kF32Chunk = 32;  // entries per workgroup
+constexpr int kF32Chunk = 16;  // entries per workgroup (16: the tiny decode's 640 entries make 40 workgroups)
 constexpr int kF32Heads = 16;  // heads per workgroup
 constexpr int kF32Row = kKvDim + 4;  // LDS row stride (floats)
 
@@ -1032,17 +1032,18 @@ attn_f32_chunk_kernel(const float* __restrict__ q, int H, const int32_t* __restr
     }
   }
   __syncthreads();
+  static_assert(kF32Chunk == 16 && kF32Heads == 16, "the lane layouts below");
   {  // scores: lane (eb, hb, kp) forms the 4 x 4 block of entries 4 eb.. and
-     // heads 4 hb.. over dims [72 kp, 72 kp + 72); the eight dim parts are
-     // summed across adjacent lanes (kp = lane % 8)
-    const int kp = tid & 7, hb = (tid >> 3) & 3, eb = tid >> 5;
+     // heads 4 hb.. over dims [36 kp, 36 kp + 36); the sixteen dim parts are
+     // summed across a 16-lane row (kp = lane % 16)
+    const int kp = tid & 15, hb = (tid >> 4) & 3, eb = tid >> 6;
     float acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-#pragma unroll 2
-    for (int k = kp * 72; k < kp * 72 + 72; k += 4) {
+#pragma unroll 3
+    for (int k = kp * 36; k < kp * 36 + 36; k += 4) {
       float4 kv[4], qv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) kv[i] = *reinterpret_cast<const float4*>(&s_kv[(eb * 4 + i) * kF32Row + k]);
@@ -1063,29 +1064,28 @@ attn_f32_chunk_kernel(const float* __restrict__ q, int H, const int32_t* __restr
         v += lane_xor<1>(v);
         v += lane_xor<2>(v);
         v += lane_xor<4>(v);
+        v += lane_xor<8>(v);
         acc[i][j] = v;
       }
-    // lane kp writes entries / heads (i, j) with 4 i + j in {2 kp, 2 kp + 1}
+    // lane kp writes entry / head (i, j) with 4 i + j == kp
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if ((4 * i + j) >> 1 == kp) {
+        if (4 * i + j == kp) {
           const int e = eb * 4 + i;
           s_p[e][hb * 4 + j] = s_slot[e] >= 0 ? acc[i][j] * scale : -INFINITY;
         }
   }
   __syncthreads();
   {  // the chunk's max and exponent sum per head: a 16-lane row per head,
-     // two entries per lane
+     // one entry per lane
     const int h = tid >> 4, r = tid & 15;
-    const float s0 = s_p[r][h], s1 = s_p[r + 16][h];
-    const float m = row16_max(fmaxf(s0, s1));
+    const float s0 = s_p[r][h];
+    const float m = row16_max(s0);
     const float p0 = s0 == -INFINITY ? 0.f : expf(s0 - m);
-    const float p1 = s1 == -INFINITY ? 0.f : expf(s1 - m);
-    const float l = row16_sum(p0 + p1);
+    const float l = row16_sum(p0);
     s_p[r][h] = p0;
-    s_p[r + 16][h] = p1;
     if (r == 0) {
       s_m[h] = m;
       s_l[h] = l;
@@ -1129,7 +1129,7 @@ attn_f32_chunk_kernel(const float* __restrict__ q, int H, const int32_t* __restr
 // sum_c e^(m_c - M) l_c over the chunks with entries (l_c > 0). The chunks'
 // (m, l) come in with one parallel load into LDS; each thread then reads its
 // two value dims of every chunk with independent loads.
-constexpr int kF32MaxChunks = 1024;  // chunks merged by one workgroup
+constexpr int kF32MaxChunks = 2048;  // chunks merged by one workgroup (32768 entries)
 __global__ void __launch_bounds__(256)
 attn_f32_combine_kernel(const float* __restrict__ part, int H, int nchunk, float* __restrict__ out) {
   __shared__ float s_f[kF32MaxChunks];
