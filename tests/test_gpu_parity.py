@@ -500,6 +500,7 @@ def test_tiny_fp32_decode_end_to_end(csa, seed_offset):
     [5000, 513, 64 * 7 + 3, 17, 0],     # fused: 512-entry scan chunks, ragged, an empty row
     [20000 - 37 * i for i in range(8)],  # fused: 1024-entry chunks
     [40000, 3000],                       # 79 chunks per row: merged into 8 lists first
+    [60000] + [1000 + 37 * i for i in range(19)],  # ragged: 300 chunk workgroups (two rounds)
 ])
 def test_indexer_topk512(csa, fmt, lens):
     """indexer_topk512 against the oracle: each row's selection equals the top-512
@@ -746,22 +747,23 @@ def test_indexer_topk512_many_rows_adversarial(csa, case, per_seq):
         assert np.array_equal(gl[3], np.arange(512))  # all NaN: the lowest indices
 
 
-@pytest.mark.parametrize("shape", ["wide", "long"])
+@pytest.mark.parametrize("shape", ["wide", "long", "wide40"])
 @pytest.mark.parametrize("case", ["ties", "outliers", "special"])
 def test_indexer_topk512_decode_adversarial(csa, case, shape):
     """The decode scan's selection on inputs that defeat its shortcuts, bit
     for bit against indexer_score + topk512_page_select. Shapes: "wide", 32
     rows of ~32K entries (4096-entry chunks, 8 per row, a final pass);
     "long", 4 rows of ~131K (2048-entry chunks, 64 per row, finished inside
-    the scan from the candidates that reach the chunks' bounds). Cases:
+    the scan); "wide40", 40 rows of ~32K (320 chunk workgroups, more than
+    CUs). Cases:
     "ties": index-K rows drawn from six distinct rows, so a row's logits take
     six values (every candidate reaches the bound); "outliers": a few entries
     with scales 1000x the rest, so the key range is wide and the threshold's
     bucket crowded; "special": head weights with NaN, +-inf, -0 and negative
     values (NaN logits rank lowest, -0 equals +0)."""
     g = gen.rng(1470 + len(case) + 10 * len(shape))
-    if shape == "wide":
-        T, pps = 32, 512
+    if shape in ("wide", "wide40"):
+        T, pps = (32 if shape == "wide" else 40), 512
         lens = [32768 - 997 * (t % 5) for t in range(T)]
     else:
         T, pps = 4, 2048
