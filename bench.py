@@ -140,6 +140,7 @@ COUNTER_KERNELS = {
     "decode128k": "indexer_mfma_kernel<false, true, true>",
     "decode1m": "indexer_mfma_kernel<true, true, true>",
     "prefill": "indexer_rows_kernel<false, 8, true>",
+    "spec": "indexer_rows_kernel<false, 4, false>",
 }
 
 

@@ -271,7 +271,7 @@ class CsaSpecDecode(CsaDecode):
     @property
     def indexer_kernel(self) -> str:
         fp4 = "true" if self.fmt == csa.CSA_MXFP4 else "false"
-        return f"indexer_rows_kernel<{fp4}, {self.wl.q_len}>"
+        return f"indexer_rows_kernel<{fp4}, {self.wl.q_len}, false>"
 
     def indexer_bytes(self) -> int:
         """Algorithmic bytes of the indexer launch: index-K rows of each
