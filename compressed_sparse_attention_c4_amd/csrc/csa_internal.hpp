@@ -67,6 +67,7 @@ struct CandOut {
   int32_t* phys_idx;
   int32_t* logical_idx;
   int rows_sel;
+  int wide_rows, wide_chunks;  // set by launch_indexer for a long ragged batch's scan
 };
 
 hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_t prep,

@@ -37,6 +37,12 @@ constexpr int kWaves = 4;
 constexpr int kRing = 2;     // 64-entry batches in flight per wave
 constexpr int kWgEntries = kWaves * kRing * 64;
 constexpr int kMaxChunk = 8 * kWgEntries;  // entries per workgroup, at most
+constexpr int kScanSlots = 256;            // scan workgroups resident at once (one per CU)
+// Long ragged batches (more live 4096-entry chunks than kScanSlots): the scan
+// takes chunks of up to kWideChunk entries, their length chosen on the device
+// from the rows' lengths (wide_chunk), for rows of at most kWideRows rows.
+constexpr int kWideChunk = kMaxChunk + 2 * kWgEntries;
+constexpr int kWideRows = 256;
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, v4f c) {
   // format 0 = FP8 e4m3 for both operands; e8m0 scale 127 = 2^0
@@ -145,10 +151,10 @@ __device__ __forceinline__ bool last_arrival(uint32_t* c, int members, int* s_fl
 // merges the group (or, when the row's live chunks form one group, selects
 // the row); the last group of the row selects the row from the groups' lists.
 template <int kTH, int kE>
-__device__ __forceinline__ void cand_finish(const CandOut& co, int t, int rl, int live, TopkLds& L) {
+__device__ __forceinline__ void cand_finish(const CandOut& co, int t, int x, int nch, int rl,
+                                            int live, TopkLds& L) {
   __shared__ int s_flag;
-  const int nch = gridDim.x;
-  const int g = blockIdx.x / co.gsize;
+  const int g = x / co.gsize;
   const int members = min(co.gsize, live - g * co.gsize);
   const int groups = (live + co.gsize - 1) / co.gsize;
   uint32_t* const cnt = co.cnt + (int64_t)t * (kCandGroups + 1);
@@ -174,38 +180,140 @@ __device__ __forceinline__ void cand_finish(const CandOut& co, int t, int rl, in
                             co.logical_idx ? co.logical_idx + (int64_t)t * kTopK : nullptr);
 }
 
-template <bool kFp4, bool kPage64, bool kCand>
-__global__ void __launch_bounds__(idx_threads<kCand>())
-indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
-                    const float* __restrict__ w, const int32_t* __restrict__ row_seq,
-                    const int32_t* __restrict__ row_len, const int32_t* __restrict__ pt,
-                    int pt_stride, const uint8_t* __restrict__ kdata,
-                    const void* __restrict__ kscale, int page_size, float* __restrict__ logits,
-                    int64_t ld, int chunk, CandOut co) {
+// The scan over a long ragged batch (kWide): workgroup j takes work item j
+// (the grid has one workgroup per 4096-entry chunk slot of every row, at
+// least as many as there are items; those past the last item exit). The chunk
+// length is chosen from the rows' lengths: of 4096, 4608 and 5120 entries,
+// the one whose live chunks, taken kScanSlots at a time, scan the fewest
+// entries per workgroup slot (rounds x length; ties to the shorter). The
+// items are first every row's live chunks, row after row (an empty row whose
+// selection finishes in the scan counts one, where its empty selection is
+// written), then, when the candidates go to the final pass, the rows'
+// remaining chunk slots (their padding is written). Consecutive items go to
+// consecutive workgroups and so round-robin over the XCDs: the live chunks
+// spread evenly over them whatever the rows' lengths, and the workgroups with
+// no item come after all of them. Every workgroup computes the same plan
+// from the same row lengths (rows 64 k + lane are this lane's, k < 4: at most
+// kWideRows rows) and takes from it item j: its row t and chunk slot x, the
+// chunk length, and the number of items (j >= total: none).
+template <int kBlocks>
+__device__ __forceinline__ void wide_item_k(const int32_t* __restrict__ row_len, int T, int nch,
+                                            bool fused, int j, int& t, int& x, int& chunk,
+                                            int& total, int& n_t) {
+  const int lane = threadIdx.x & 63;
+  int n[kBlocks];
+#pragma unroll
+  for (int k = 0; k < kBlocks; ++k) {
+    const int r = 64 * k + lane;
+    n[k] = r < T ? max(row_len[r], 0) : 0;
+  }
+  // live chunks per row for each candidate length (divisions by constants)
+  int cnt[3][kBlocks];
+  int vbest = 0;
+  uint64_t best_cost = ~0ull;
+#pragma unroll
+  for (int v = 0; v < 3; ++v) {
+    constexpr int kLen0 = kMaxChunk;
+    const uint32_t len = kLen0 + v * kWgEntries;
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kBlocks; ++k) {
+      cnt[v][k] = (int)(((uint32_t)n[k] + len - 1) / len);
+      c += (uint32_t)cnt[v][k];
+    }
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(c), 63);
+    const uint64_t cost = (uint64_t)((tot + kScanSlots - 1) / kScanSlots) * len;
+    if (cost < best_cost) {
+      best_cost = cost;
+      vbest = v;
+    }
+  }
+  chunk = kMaxChunk + vbest * kWgEntries;
+  // items of the first kind (live chunks; an empty row's one) and of the
+  // second (the remaining slots) per row, and their inclusive prefixes
+  int lv[kBlocks], a[kBlocks], ai[kBlocks], bi[kBlocks];
+  int ca = 0, cb = 0;
+#pragma unroll
+  for (int k = 0; k < kBlocks; ++k) {
+    const bool in = 64 * k + lane < T;
+    lv[k] = min(vbest == 0 ? cnt[0][k] : vbest == 1 ? cnt[1][k] : cnt[2][k], nch);
+    a[k] = in ? (fused && n[k] == 0 ? 1 : lv[k]) : 0;
+    const int sa = (int)wave_inclusive_scan((uint32_t)a[k]);
+    ai[k] = ca + sa;
+    ca += __builtin_amdgcn_readlane(sa, 63);
+    if (!fused) {
+      const int sb = (int)wave_inclusive_scan((uint32_t)(in ? nch - lv[k] : 0));
+      bi[k] = cb + sb;
+      cb += __builtin_amdgcn_readlane(sb, 63);
+    } else {
+      bi[k] = 0;
+    }
+  }
+  total = ca + cb;
+  t = 0;
+  x = 0;
+  n_t = 0;
+  if (j >= total) return;
+  const bool second = j >= ca;
+  const int d = second ? j - ca : j;
+#pragma unroll
+  for (int k = 0; k < kBlocks; ++k) {
+    const int inc = second ? bi[k] : ai[k];
+    const uint64_t m = __ballot(inc > d);
+    if (m) {
+      const int l = __ffsll((unsigned long long)m) - 1;  // the first row whose items reach past d
+      const int lvl = __builtin_amdgcn_readlane(lv[k], l);
+      const int cnt_l = second ? nch - lvl : __builtin_amdgcn_readlane(a[k], l);
+      const int excl = __builtin_amdgcn_readlane(inc, l) - cnt_l;
+      t = 64 * k + l;
+      x = (second ? lvl : 0) + d - excl;
+      n_t = __builtin_amdgcn_readlane(n[k], l);
+      return;
+    }
+  }
+}
+
+__device__ __forceinline__ void wide_item(const int32_t* __restrict__ row_len, int T, int nch,
+                                          bool fused, int j, int& t, int& x, int& chunk,
+                                          int& total, int& n_t) {
+  if (T <= 64) wide_item_k<1>(row_len, T, nch, fused, j, t, x, chunk, total, n_t);
+  else wide_item_k<4>(row_len, T, nch, fused, j, t, x, chunk, total, n_t);
+}
+
+// One scan work item: chunk slot x (entries x * chunk ..) of row t, of
+// length n, whose candidates or logits sit in slot x of nch per row.
+template <bool kFp4, bool kPage64, bool kCand, int kCap>
+__device__ __forceinline__ void scan_chunk_item(
+    int t, int x, int nch, int chunk, int n, const uint8_t* __restrict__ qc, const void* __restrict__ qs,
+    const float* __restrict__ w, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ pt, int pt_stride,
+    const uint8_t* __restrict__ kdata, const void* __restrict__ kscale, int page_size,
+    float* __restrict__ logits, int64_t ld, const CandOut& co) {
   constexpr int kRowBytes = kFp4 ? kDim / 2 : kDim;  // bytes per index-K / q row
   constexpr int kTH = idx_threads<kCand>();
-  constexpr int kSelE = kMaxChunk / kTH;  // keys per lane of the selections
+  constexpr int kSelE = kCap / kTH;      // keys per lane of the chunk's selection
+  constexpr int kFinE = kMaxChunk / kTH;  // and of the finish (at most 8 x 512 candidates)
   constexpr int kSW = kScanWaves<kFp4, kCand>();  // waves that scan
-  __shared__ int32_t s_pages[kMaxChunk / 16 + 2];      // physical pages of this chunk
-  __shared__ __attribute__((aligned(16))) float s_out[kMaxChunk + 64];  // the chunk's logits
+  __shared__ int32_t s_pages[kCap / 16 + 2];      // physical pages of this chunk
+  __shared__ __attribute__((aligned(16))) float s_out[kCap + 64];  // the chunk's logits
   __shared__ TopkLds L;                                  // the selections (kCand)
-  const int t = blockIdx.y;
-  const int n = row_len[t];
-  const int c0 = blockIdx.x * chunk;
-  const int live = (n + chunk - 1) / chunk;  // chunks holding entries of the row
+  const int c0 = x * chunk;
+  // chunks holding entries of the row (a row longer than the call's bound
+  // is cut at nch chunks, as the grid covers no more)
+  const int live = min((n + chunk - 1) / chunk, nch);
   if (c0 >= n) {
     if constexpr (kCand) {
       if (co.ngroups > 0) {
         // past the row: no part in the fused finish; an empty row's selection
         // is written here
-        if (n == 0 && blockIdx.x == 0)
+        if (n == 0 && x == 0)
           for (int p = threadIdx.x; p < kTopK; p += kTH) {
             co.phys_idx[(int64_t)t * kTopK + p] = -1;
             if (co.logical_idx) co.logical_idx[(int64_t)t * kTopK + p] = -1;
           }
       } else {
         for (int p = threadIdx.x; p < kTopK; p += kTH) {
-          const int64_t o = ((int64_t)t * gridDim.x + blockIdx.x) * kTopK + p;
+          const int64_t o = ((int64_t)t * nch + x) * kTopK + p;
           co.keys[o] = 0u;
           co.js[o] = INT_MAX;
           co.phys[o] = -1;
@@ -346,7 +454,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
     const float tot = rows4_reduce_scatter(pk[0], pk[1], pk[2], pk[3]);
     // entry within the chunk; a batch past this wave's last lands in the
     // spare 64 slots at the end
-    const int jl = i < nb ? (i * kSW + wave) * 64 + 16 * grp + col : kMaxChunk + lane;
+    const int jl = i < nb ? (i * kSW + wave) * 64 + 16 * grp + col : kCap + lane;
     s_out[jl] = tot * ks[r];
     issue(i + kR, R);  // refill the slot just consumed
   };
@@ -382,7 +490,7 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
     const int K = min(kTopK, n_out);
     topk_select<kE, kTH>(kr, n_out, K, seg, L);
     for (int p = threadIdx.x; p < kTopK; p += kTH) {
-      const int64_t o = ((int64_t)t * gridDim.x + blockIdx.x) * kTopK + p;
+      const int64_t o = ((int64_t)t * nch + x) * kTopK + p;
       uint32_t key = 0u;  // padding past K
       int32_t j = INT_MAX, phys = -1;
       if (p < K) {
@@ -400,10 +508,37 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
         co.phys[o] = phys;
       }
     }
-    if (co.ngroups > 0) cand_finish<kTH, kSelE>(co, t, n, live, L);
+    if (co.ngroups > 0) cand_finish<kTH, kFinE>(co, t, x, nch, n, live, L);
   } else {
     float* orow = logits + (int64_t)t * ld + c0;
     for (int j = threadIdx.x; j < n_out; j += kWaves * 64) orow[j] = s_out[j];
+  }
+}
+
+// The decode scan: workgroup (x, t) takes chunk x of row t, or (kWide) the
+// work items of WideItems, co.wide_rows rows of co.wide_chunks chunk slots.
+template <bool kFp4, bool kPage64, bool kCand, bool kWide = false>
+__global__ void __launch_bounds__(idx_threads<kCand>())
+indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
+                    const float* __restrict__ w, const int32_t* __restrict__ row_seq,
+                    const int32_t* __restrict__ row_len, const int32_t* __restrict__ pt,
+                    int pt_stride, const uint8_t* __restrict__ kdata,
+                    const void* __restrict__ kscale, int page_size, float* __restrict__ logits,
+                    int64_t ld, int chunk, CandOut co) {
+  static_assert(!kWide || (kCand && kPage64), "long ragged batches: fused selection, 64-entry pages");
+  if constexpr (!kWide) {
+    scan_chunk_item<kFp4, kPage64, kCand, kMaxChunk>(blockIdx.y, blockIdx.x, gridDim.x, chunk,
+                                                     row_len[blockIdx.y], qc, qs, w, row_seq, pt,
+                                                     pt_stride, kdata, kscale, page_size, logits,
+                                                     ld, co);
+  } else {
+    int t, x, ch, total, n;
+    wide_item(row_len, co.wide_rows, co.wide_chunks, co.ngroups > 0, (int)blockIdx.x, t, x, ch,
+              total, n);
+    if ((int)blockIdx.x >= total) return;
+    scan_chunk_item<kFp4, kPage64, kCand, kWideChunk>(t, x, co.wide_chunks, ch, n, qc, qs, w,
+                                                      row_seq, pt, pt_stride, kdata, kscale,
+                                                      page_size, logits, ld, co);
   }
 }
 
@@ -770,7 +905,7 @@ size_t indexer_ws_bytes(int64_t T, int H_I) {
 // workgroups (one per CU), each wave a long stream: measured on MI355X, one
 // workgroup per CU streams faster than two (fewer concurrent page streams).
 static int64_t scan_chunk(int64_t T, int64_t max_row_len) {
-  const int64_t target = 256;
+  const int64_t target = kScanSlots;
   const int64_t total = T * max_row_len;
   int64_t chunk = total / target;
   chunk = ((chunk + kWgEntries - 1) / kWgEntries) * kWgEntries;
@@ -933,16 +1068,29 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
 #undef CSA_ROWS
     return hipGetLastError();
   }
+  // The grid covers the rows in 4096-entry chunks; with long ragged rows
+  // (more entries than kScanSlots such chunks) the workgroups take chunks of
+  // the length wide_chunk picks, and those past a row's end exit as usual.
   dim3 grid((unsigned)((max_row_len + chunk - 1) / chunk), T);
-  const CandOut co = cand ? *cand : CandOut{};
-#define CSA_IDX(FP4, P64, CAND)                                                                    \
-  hipLaunchKernelGGL((indexer_mfma_kernel<FP4, P64, CAND>), grid, dim3(idx_threads<CAND>()), 0, s, qc, qs, \
-                     w, row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data, k.scale,  \
-                     k.page_size, logits, ld, (int)chunk, co)
+  CandOut co = cand ? *cand : CandOut{};
+  const bool wide = cand && k.page_size == 64 && T <= kWideRows &&
+                    (int64_t)T * max_row_len > (int64_t)kScanSlots * kMaxChunk;
+  if (wide) {  // the chunk slots stay those of 4096-entry chunks
+    co.wide_rows = T;
+    co.wide_chunks = (int)grid.x;
+    grid = dim3(grid.x * grid.y);
+  }
+#define CSA_IDX(FP4, P64, CAND, WIDE)                                                             \
+  hipLaunchKernelGGL((indexer_mfma_kernel<FP4, P64, CAND, WIDE>), grid, dim3(idx_threads<CAND>()), 0, s, \
+                     qc, qs, w, row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data,   \
+                     k.scale, k.page_size, logits, ld, (int)chunk, co)
 #define CSA_IDX_P(FP4, CAND)                 \
-  if (k.page_size == 64) CSA_IDX(FP4, true, CAND); \
-  else CSA_IDX(FP4, false, CAND);
-  if (cand) {
+  if (k.page_size == 64) CSA_IDX(FP4, true, CAND, false); \
+  else CSA_IDX(FP4, false, CAND, false);
+  if (wide) {
+    if (k.fmt == CSA_MXFP4) CSA_IDX(true, true, true, true);
+    else CSA_IDX(false, true, true, true);
+  } else if (cand) {
     if (k.fmt == CSA_MXFP4) { CSA_IDX_P(true, true) }
     else { CSA_IDX_P(false, true) }
   } else {

@@ -546,6 +546,89 @@ def test_indexer_topk512(csa, fmt, lens):
         assert ok, f"row {t}: selection differs outside the near-tie band ({nband} in band)"
 
 
+_LONG_POOLS = {}
+
+
+def _long_pool(fmt, pages):
+    """A pool of `pages` 64-entry pages of prepared index-K rows, drawn once per format."""
+    if (fmt, pages) not in _LONG_POOLS:
+        g = gen.rng(1390 + len(fmt))
+        data, sc = O.index_prep(gen.normal(g, (pages * 64, 128)), True, fmt)
+        _LONG_POOLS[(fmt, pages)] = O.IndexPool(data, sc, fmt)
+    return _LONG_POOLS[(fmt, pages)]
+
+
+def _long_chunk(lens, slots=256):
+    """The scan chunk length the library takes for a batch with more live
+    4096-entry chunks than workgroups resident at once: of 4096, 4608 and
+    5120 entries, the fewest entries per workgroup slot over the rounds."""
+    best = None
+    for c in (4096, 4608, 5120):
+        live = sum((n + c - 1) // c for n in lens)
+        cost = -(-live // slots) * c
+        if best is None or cost < best[0]:
+            best = (cost, c)
+    return best[1]
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("case", ["ragged16_c5120", "rows30_c4608", "rows40_final_c4608"])
+def test_indexer_topk512_long_batches(csa, fmt, case):
+    """Batches with more live 4096-entry scan chunks than the GPU holds at
+    once take longer chunks, chosen from the rows' lengths: 16 ragged rows of
+    3K-234K entries (5120-entry chunks, finished inside the scan in up to 6
+    groups), 30 rows of ~36000 (4608, finished inside the scan) and 40 rows of
+    ~27000 (4608, through the final pass, a chunk of padding per row). Bit for
+    bit the two-call path; sampled rows against the oracle's top-512."""
+    from tests.fullsize import topk_agrees
+    if case == "ragged16_c5120":
+        lens = [int(n) for n in gen.ragged_lengths(gen.rng(1005), 16, 8192, 1 << 20) // 4]
+        want_chunk = 5120
+    elif case == "rows30_c4608":
+        lens = [36000 - 3 * i for i in range(30)]
+        want_chunk = 4608
+    else:
+        lens = [27000 - 5 * i for i in range(40)]
+        want_chunk = 4608
+    assert sum((n + 4095) // 4096 for n in lens) > 256 and _long_chunk(lens) == want_chunk
+    g = gen.rng(1380 + len(fmt) + len(case))
+    T = len(lens)
+    # one pool of 4096 pages; each row's page table a prefix of its own
+    # permutation (no page twice in a row; rows share pages)
+    pool_pages = 4096
+    pps = max((n + 63) // 64 for n in lens)
+    pt = np.stack([g.permutation(pool_pages)[:pps] for _ in lens]).astype(np.int32)
+    pool = _long_pool(fmt, pool_pages)
+    qcodes, qsc = O.index_prep(gen.normal(g, (T, 64, 128)), True, fmt)
+    w = gen.uniform(g, (T, 64))
+    qfmt = csa.CSA_FP8_E4M3 if fmt == "fp8" else csa.CSA_MXFP4
+    qs = t_dev(qsc.astype(np.float32)) if fmt == "fp8" else t_dev(qsc)
+    dpool = index_pool_to_device(pool, 64, 128)
+    row_seq, row_len, dpt = t_dev(np.arange(T, dtype=np.int32)), t_dev(np.array(lens, np.int32)), t_dev(pt)
+    maxn = max(lens)
+    phys = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    logi = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    csa.indexer_topk512(t_dev(qcodes), t_dev(w), row_seq, row_len, maxn, dpt, dpool, phys, logi,
+                        q_fmt=qfmt, q_scale=qs)
+    logits = torch.empty((T, maxn), device=DEV)
+    csa.indexer_score(t_dev(qcodes), t_dev(w), row_seq, row_len, maxn, dpt, dpool, logits,
+                      q_fmt=qfmt, q_scale=qs)
+    phys2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    logi2 = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    csa.topk512_page_select(logits, row_len, row_seq, dpt, phys2, logi2)
+    gp, gl = phys.cpu().numpy(), logi.cpu().numpy()
+    assert np.array_equal(gp, phys2.cpu().numpy()) and np.array_equal(gl, logi2.cpu().numpy())
+    qhat = O.index_dequant(qcodes, qsc, fmt)
+    order = np.argsort(lens)
+    for t in (int(order[-1]), int(order[len(order) // 2]), int(order[0])):
+        n = lens[t]
+        assert np.all(np.diff(gl[t]) > 0), f"row {t}: not ascending"
+        assert np.array_equal(gp[t], O.page_slot(pt[t], gl[t], 64)), f"row {t}: slots"
+        want = O.indexer_logits(qhat[t], w[t], pool.rows(O.page_slot(pt[t], np.arange(n), 64)))
+        ok, _, nband = topk_agrees(want, gl[t], 512, 1e-4 * np.abs(want).max())
+        assert ok, f"row {t}: selection differs outside the near-tie band ({nband} in band)"
+
+
 def test_indexer_topk512_f32_two_calls(csa):
     """An fp32 index pool takes the two-call path (logits in the workspace):
     the selection is the top-512 of the oracle's logits outside the near-tie
