@@ -141,6 +141,7 @@ COUNTER_KERNELS = {
     "decode1m": "indexer_mfma_kernel<true, true, true>",
     "prefill": "indexer_rows_kernel<false, 8, true>",
     "spec": "indexer_rows_kernel<false, 4, false>",
+    "ragged": "indexer_wide_kernel<false>",
 }
 
 

@@ -515,9 +515,8 @@ __device__ __forceinline__ void scan_chunk_item(
   }
 }
 
-// The decode scan: workgroup (x, t) takes chunk x of row t, or (kWide) the
-// work items of WideItems, co.wide_rows rows of co.wide_chunks chunk slots.
-template <bool kFp4, bool kPage64, bool kCand, bool kWide = false>
+// The decode scan: workgroup (x, t) takes chunk x of row t.
+template <bool kFp4, bool kPage64, bool kCand>
 __global__ void __launch_bounds__(idx_threads<kCand>())
 indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     const float* __restrict__ w, const int32_t* __restrict__ row_seq,
@@ -525,21 +524,28 @@ indexer_mfma_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
                     int pt_stride, const uint8_t* __restrict__ kdata,
                     const void* __restrict__ kscale, int page_size, float* __restrict__ logits,
                     int64_t ld, int chunk, CandOut co) {
-  static_assert(!kWide || (kCand && kPage64), "long ragged batches: fused selection, 64-entry pages");
-  if constexpr (!kWide) {
-    scan_chunk_item<kFp4, kPage64, kCand, kMaxChunk>(blockIdx.y, blockIdx.x, gridDim.x, chunk,
-                                                     row_len[blockIdx.y], qc, qs, w, row_seq, pt,
-                                                     pt_stride, kdata, kscale, page_size, logits,
-                                                     ld, co);
-  } else {
-    int t, x, ch, total, n;
-    wide_item(row_len, co.wide_rows, co.wide_chunks, co.ngroups > 0, (int)blockIdx.x, t, x, ch,
-              total, n);
-    if ((int)blockIdx.x >= total) return;
-    scan_chunk_item<kFp4, kPage64, kCand, kWideChunk>(t, x, co.wide_chunks, ch, n, qc, qs, w,
-                                                      row_seq, pt, pt_stride, kdata, kscale,
-                                                      page_size, logits, ld, co);
-  }
+  scan_chunk_item<kFp4, kPage64, kCand, kMaxChunk>(blockIdx.y, blockIdx.x, gridDim.x, chunk,
+                                                   row_len[blockIdx.y], qc, qs, w, row_seq, pt,
+                                                   pt_stride, kdata, kscale, page_size, logits, ld,
+                                                   co);
+}
+
+// The decode scan of a long ragged batch (64-entry pages, fused selection):
+// workgroup j takes item j of the plan of wide_item, over co.wide_rows rows
+// of co.wide_chunks chunk slots.
+template <bool kFp4>
+__global__ void __launch_bounds__(idx_threads<true>())
+indexer_wide_kernel(const uint8_t* __restrict__ qc, const void* __restrict__ qs,
+                    const float* __restrict__ w, const int32_t* __restrict__ row_seq,
+                    const int32_t* __restrict__ row_len, const int32_t* __restrict__ pt,
+                    int pt_stride, const uint8_t* __restrict__ kdata,
+                    const void* __restrict__ kscale, CandOut co) {
+  int t, x, ch, total, n;
+  wide_item(row_len, co.wide_rows, co.wide_chunks, co.ngroups > 0, (int)blockIdx.x, t, x, ch,
+            total, n);
+  if ((int)blockIdx.x >= total) return;
+  scan_chunk_item<kFp4, true, true, kWideChunk>(t, x, co.wide_chunks, ch, n, qc, qs, w, row_seq,
+                                                pt, pt_stride, kdata, kscale, 64, nullptr, 0, co);
 }
 
 // Many query rows of few sequences (prefill; multi-token decode, whose rows
@@ -1078,19 +1084,23 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
   if (wide) {  // the chunk slots stay those of 4096-entry chunks
     co.wide_rows = T;
     co.wide_chunks = (int)grid.x;
-    grid = dim3(grid.x * grid.y);
+    const dim3 g1(grid.x * grid.y);
+#define CSA_WIDE(FP4)                                                                             \
+  hipLaunchKernelGGL((indexer_wide_kernel<FP4>), g1, dim3(idx_threads<true>()), 0, s, qc, qs, w, \
+                     row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data, k.scale, co)
+    if (k.fmt == CSA_MXFP4) CSA_WIDE(true);
+    else CSA_WIDE(false);
+#undef CSA_WIDE
+    return hipGetLastError();
   }
-#define CSA_IDX(FP4, P64, CAND, WIDE)                                                             \
-  hipLaunchKernelGGL((indexer_mfma_kernel<FP4, P64, CAND, WIDE>), grid, dim3(idx_threads<CAND>()), 0, s, \
-                     qc, qs, w, row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data,   \
-                     k.scale, k.page_size, logits, ld, (int)chunk, co)
+#define CSA_IDX(FP4, P64, CAND)                                                                    \
+  hipLaunchKernelGGL((indexer_mfma_kernel<FP4, P64, CAND>), grid, dim3(idx_threads<CAND>()), 0, s, qc, qs, \
+                     w, row_seq, row_len, page_table, pt_stride, (const uint8_t*)k.data, k.scale,  \
+                     k.page_size, logits, ld, (int)chunk, co)
 #define CSA_IDX_P(FP4, CAND)                 \
-  if (k.page_size == 64) CSA_IDX(FP4, true, CAND, false); \
-  else CSA_IDX(FP4, false, CAND, false);
-  if (wide) {
-    if (k.fmt == CSA_MXFP4) CSA_IDX(true, true, true, true);
-    else CSA_IDX(false, true, true, true);
-  } else if (cand) {
+  if (k.page_size == 64) CSA_IDX(FP4, true, CAND); \
+  else CSA_IDX(FP4, false, CAND);
+  if (cand) {
     if (k.fmt == CSA_MXFP4) { CSA_IDX_P(true, true) }
     else { CSA_IDX_P(false, true) }
   } else {

@@ -158,6 +158,9 @@ class CsaDecode:
     def indexer_kernel(self) -> str:
         fused, _ = self.scan_plan()
         fp4 = "true" if self.fmt == csa.CSA_MXFP4 else "false"
+        if fused and self.B <= 256 and self.B * self.maxN > 256 * 4096:
+            # more entries than 256 chunks of 4096: chunks planned on the device
+            return f"indexer_wide_kernel<{fp4}>"
         return f"indexer_mfma_kernel<{fp4}, true, {'true' if fused else 'false'}>"
 
     def indexer_bytes(self) -> int:
