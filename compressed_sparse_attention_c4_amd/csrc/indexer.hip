@@ -104,17 +104,22 @@ __device__ __forceinline__ void cand_select_emit(const uint32_t* keys, const int
                                                  int32_t* logical_idx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int seg = wave * 64 * kE;
+  // keys, entry indices and slots in one round of loads; the selected ones'
+  // indices and slots are parked beside them
   uint32_t kr[kE];
+  int32_t ja[kE], pa[kE];
 #pragma unroll
   for (int i = 0; i < kE; ++i) {
     const int e = seg + 64 * i + lane;
-    kr[i] = e < n ? ld_through(keys + e) : 0u;
+    const bool ok = e < n;
+    kr[i] = ok ? ld_through(keys + e) : 0u;
+    ja[i] = ok ? ld_through(js + e) : -1;
+    pa[i] = ok ? ld_through(phys + e) : -1;
   }
-  topk_select<kE, kTH>(kr, n, K, seg, L);
+  topk_select_pay<kE, kTH>(kr, ja, pa, n, K, seg, L);
   for (int p = threadIdx.x; p < kTopK; p += kTH) {
-    const int e = p < K ? L.out_e[p] : 0;
-    const int32_t ph = p < K ? ld_through(phys + e) : -1;
-    const int32_t jj = p < K ? ld_through(js + e) : -1;
+    const int32_t ph = p < K ? topk_pay_b(L)[p] : -1;
+    const int32_t jj = p < K ? topk_pay_a(L)[p] : -1;
     if (phys_idx) {
       phys_idx[p] = ph;
       if (logical_idx) logical_idx[p] = jj;

@@ -95,19 +95,29 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
   // (present NaNs come first by index), and K <= n, so none is ever selected
   // and no pass needs a separate validity mask.
   const int nv = n - seg - lane;  // element i of this lane exists iff 64*i < nv
+  // Candidates of a 512-selection with few keys per lane load their entry
+  // index and slot with the key; the select parks the selected ones' beside
+  // them, so the emission reads them from LDS.
+  constexpr bool kPay = (kMode == kCandFinal || kMode == kCandMerge) && kE <= 8 && kK == kTopK;
   uint32_t kr[kE];
+  int32_t ja[kE], pa[kE];
   {
     const float* lrow = logits + (int64_t)r * ld + base;
-    const uint32_t* crow = ckeys + (int64_t)r * ncand + (kMode == kCandMerge ? base : 0);
+    const int64_t c0 = (int64_t)r * ncand + (kMode == kCandMerge ? base : 0);
 #pragma unroll
     for (int i = 0; i < kE; ++i) {
       const bool ok = 64 * i < nv;
       const int e = ok ? seg + 64 * i + lane : 0;
-      const uint32_t k = (kMode == kCandFinal || kMode == kCandMerge) ? crow[e] : float_key(lrow[e]);
+      const uint32_t k = (kMode == kCandFinal || kMode == kCandMerge) ? ckeys[c0 + e] : float_key(lrow[e]);
       kr[i] = ok ? k : 0u;
+      if constexpr (kPay) {
+        ja[i] = ok ? cjs[c0 + e] : -1;
+        pa[i] = ok && cphys ? cphys[c0 + e] : -1;
+      }
     }
   }
-  topk_select<kE, TH>(kr, n, K, seg, L);
+  if constexpr (kPay) topk_select_pay<kE, TH>(kr, ja, pa, n, K, seg, L);
+  else topk_select<kE, TH>(kr, n, K, seg, L);
   // ---- emission (positions K..ksel-1 are padding)
   for (int p = threadIdx.x; p < ksel; p += TH) {
     if (kMode == kChunkCand) {
@@ -119,10 +129,15 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
       uint32_t key = 0u;
       int32_t j = INT_MAX, ph = -1;
       if (p < K) {
-        const int64_t c = (int64_t)r * ncand + base + L.out_e[p];
         key = L.out_k[p];
-        j = cjs[c];
-        ph = cphys[c];
+        if constexpr (kPay) {
+          j = topk_pay_a(L)[p];
+          ph = topk_pay_b(L)[p];
+        } else {
+          const int64_t c = (int64_t)r * ncand + base + L.out_e[p];
+          j = cjs[c];
+          ph = cphys[c];
+        }
       }
       okeys[o] = key;
       ojs[o] = j;
@@ -131,9 +146,10 @@ topk_kernel(const float* __restrict__ logits, int64_t ld, const uint32_t* __rest
       int32_t phys = -1, j = -1;
       if (p < K) {
         const int e = L.out_e[p];
-        j = kMode == kCandFinal ? cjs[(int64_t)r * ncand + e] : e;
+        if constexpr (kPay) j = topk_pay_a(L)[p];
+        else j = kMode == kCandFinal ? cjs[(int64_t)r * ncand + e] : e;
         if (kMode == kCandFinal && cphys)  // candidates that carry their slot
-          phys = cphys[(int64_t)r * ncand + e];
+          phys = kPay ? topk_pay_b(L)[p] : cphys[(int64_t)r * ncand + e];
         else
           phys = (int32_t)((int64_t)pt[(int64_t)row_seq[r] * pt_stride + j / c4_page_size] *
                                c4_page_size +

@@ -105,9 +105,24 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int nbins, uin
 // order. K <= n. Every thread of the TH-thread workgroup calls it; L.hist must
 // have been cleared by the workgroup before the call (the first barrier
 // inside orders the clear before any use). Ends with a barrier.
-template <int kE, int TH, class Lds>
-__device__ __forceinline__ void topk_select(const uint32_t (&kr)[kE], int n, int K, int seg,
-                                            Lds& L) {
+// With kPay, two 32-bit payloads of each element (pa[i], pb[i], e.g. its
+// entry index and slot, loaded with the key) are parked beside it, at
+// topk_pay_a(L)[pos] and topk_pay_b(L)[pos] (K <= 512), so an emission needs
+// no second round of loads.
+template <class Lds>
+__device__ __forceinline__ int32_t* topk_pay_a(Lds& L) {
+  return reinterpret_cast<int32_t*>(L.cand);
+}
+template <class Lds>
+__device__ __forceinline__ int32_t* topk_pay_b(Lds& L) {
+  return reinterpret_cast<int32_t*>(L.cand) + kTopK;
+}
+
+template <int kE, int TH, bool kPay, class Lds>
+__device__ __forceinline__ void topk_select_impl(const uint32_t (&kr)[kE], const int32_t (&pa)[kE],
+                                                 const int32_t (&pb)[kE], int n, int K, int seg,
+                                                 Lds& L) {
+  static_assert(2 * kTopK <= kTopkCandCap, "payloads live in the threshold list's space");
   constexpr int kBins = kTopkBins;
   constexpr int kCandCap = kTopkCandCap;
   constexpr int kWaves = kTopkMaxWaves;
@@ -270,11 +285,29 @@ __device__ __forceinline__ void topk_select(const uint32_t (&kr)[kE], int n, int
       const uint32_t pos = gb + min(qb, need);
       s_out_e[pos] = seg + 64 * i + lane_b;
       s_out_k[pos] = kr[i];
+      if constexpr (kPay) {  // the list's keys are dead here (barriers since their last read)
+        topk_pay_a(L)[pos] = pa[i];
+        topk_pay_b(L)[pos] = pb[i];
+      }
     }
     g += (uint32_t)__popcll(bg);
     q += (uint32_t)__popcll(be);
   }
   __syncthreads();
+}
+
+template <int kE, int TH, class Lds>
+__device__ __forceinline__ void topk_select(const uint32_t (&kr)[kE], int n, int K, int seg,
+                                            Lds& L) {
+  const int32_t(&none)[kE] = reinterpret_cast<const int32_t(&)[kE]>(kr);
+  topk_select_impl<kE, TH, false>(kr, none, none, n, K, seg, L);
+}
+
+template <int kE, int TH, class Lds>
+__device__ __forceinline__ void topk_select_pay(const uint32_t (&kr)[kE], const int32_t (&pa)[kE],
+                                                const int32_t (&pb)[kE], int n, int K, int seg,
+                                                Lds& L) {
+  topk_select_impl<kE, TH, true>(kr, pa, pb, n, K, seg, L);
 }
 
 }  // namespace csa
