@@ -438,7 +438,7 @@ __device__ __forceinline__ void scan_chunk_item(
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads together, in issue order
   };
-  auto step = [&](int i, auto R) __attribute__((always_inline)) {
+  auto step = [&](int i, auto R, auto Last) __attribute__((always_inline)) {
     constexpr int r = decltype(R)::value;
     float pk[4];
 #pragma unroll
@@ -461,21 +461,42 @@ __device__ __forceinline__ void scan_chunk_item(
     // spare 64 slots at the end
     const int jl = i < nb ? (i * kSW + wave) * 64 + 16 * grp + col : kCap + lane;
     s_out[jl] = tot * ks[r];
-    issue(i + kR, R);  // refill the slot just consumed
+    // refill the slot just consumed. In the last round of the loop no load
+    // goes past this wave's last batch (a step past it reads stale registers
+    // and drops its logits), so none is still in flight when the selection
+    // reuses the registers; the main loop's refills stay unconditional (a
+    // branch there makes the compiler drain every load before it).
+    if constexpr (decltype(Last)::value) {
+      if (i + kR < nb) issue(i + kR, R);
+    } else {
+      issue(i + kR, R);
+    }
   };
   static_assert(kR == 2 || kR == 4, "the batch loop below is unrolled by hand for 2 or 4 slots");
-  issue(0, std::integral_constant<int, 0>{});
-  issue(1, std::integral_constant<int, 1>{});
+  if (0 < nb) issue(0, std::integral_constant<int, 0>{});
+  if (1 < nb) issue(1, std::integral_constant<int, 1>{});
   if constexpr (kR == 4) {
-    issue(2, std::integral_constant<int, 2>{});
-    issue(3, std::integral_constant<int, 3>{});
+    if (2 < nb) issue(2, std::integral_constant<int, 2>{});
+    if (3 < nb) issue(3, std::integral_constant<int, 3>{});
   }
-  for (int i0 = 0; i0 < nb; i0 += kR) {
-    step(i0, std::integral_constant<int, 0>{});
-    step(i0 + 1, std::integral_constant<int, 1>{});
+  using std::integral_constant;
+  const integral_constant<bool, false> body;
+  const integral_constant<bool, true> last;
+  int i0 = 0;
+  for (; i0 + 2 * kR <= nb; i0 += kR) {  // every refill is a batch of this wave
+    step(i0, integral_constant<int, 0>{}, body);
+    step(i0 + 1, integral_constant<int, 1>{}, body);
     if constexpr (kR == 4) {
-      step(i0 + 2, std::integral_constant<int, 2>{});
-      step(i0 + 3, std::integral_constant<int, 3>{});
+      step(i0 + 2, integral_constant<int, 2>{}, body);
+      step(i0 + 3, integral_constant<int, 3>{}, body);
+    }
+  }
+  for (; i0 < nb; i0 += kR) {
+    step(i0, integral_constant<int, 0>{}, last);
+    step(i0 + 1, integral_constant<int, 1>{}, last);
+    if constexpr (kR == 4) {
+      step(i0 + 2, integral_constant<int, 2>{}, last);
+      step(i0 + 3, integral_constant<int, 3>{}, last);
     }
   }
   }  // scan waves
@@ -486,12 +507,18 @@ __device__ __forceinline__ void scan_chunk_item(
     constexpr int kE = kSelE;
     for (int i = threadIdx.x; i < kTopkBins; i += kTH) L.hist[i] = 0u;
     const int seg = wave * 64 * kE;
+    // all of the lane's logits loaded at once (e < kCap: in bounds), then
+    // keyed; the empty asm keeps the compiler from sinking each load into a
+    // branch of its own, one LDS round trip after another
+    float v[kE];
+#pragma unroll
+    for (int i = 0; i < kE; ++i) v[i] = s_out[seg + 64 * i + lane];
+#pragma unroll
+    for (int i = 0; i < kE; ++i) asm volatile("" : "+v"(v[i]));
     uint32_t kr[kE];
 #pragma unroll
-    for (int i = 0; i < kE; ++i) {
-      const int e = seg + 64 * i + lane;
-      kr[i] = e < n_out ? float_key(s_out[e]) : 0u;
-    }
+    for (int i = 0; i < kE; ++i)  // masked, not branched: key 0 past the chunk
+      kr[i] = float_key(v[i]) & (0u - (uint32_t)(seg + 64 * i + lane < n_out));
     const int K = min(kTopK, n_out);
     topk_select<kE, kTH>(kr, n_out, K, seg, L);
     for (int p = threadIdx.x; p < kTopK; p += kTH) {

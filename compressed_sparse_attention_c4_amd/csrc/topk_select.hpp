@@ -141,29 +141,28 @@ __device__ __forceinline__ void topk_select_impl(const uint32_t (&kr)[kE], const
   uint32_t thr = 0, need = 0;
   const bool take_all = n <= K;  // every element is selected
   if (!take_all) {
-    // ---- 1. key range of the non-NaN keys
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    // ---- 1. key range of the non-NaN keys: the minimum of key - 1 (key 0
+    // wraps to the top) plus one; the maximum is unaffected by key 0
+    uint32_t kmin1 = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
     for (int i = 0; i < kE; ++i) {
-      if (kr[i] != 0u) {
-        kmin = min(kmin, kr[i]);
-        kmax = max(kmax, kr[i]);
-      }
+      kmin1 = min(kmin1, kr[i] - 1u);
+      kmax = max(kmax, kr[i]);
     }
-    kmin = wave_umin(kmin);
+    kmin1 = wave_umin(kmin1);
     kmax = wave_umax(kmax);
     if (lane == 0) {
-      red[wave] = kmin;
+      red[wave] = kmin1;
       red[kWaves + wave] = kmax;
     }
     __syncthreads();
-    kmin = 0xFFFFFFFFu;
+    kmin1 = 0xFFFFFFFFu;
     kmax = 0u;
     for (int w = 0; w < TH / 64; ++w) {
-      kmin = min(kmin, red[w]);
+      kmin1 = min(kmin1, red[w]);
       kmax = max(kmax, red[kWaves + w]);
     }
-    if (kmin > kmax) kmin = kmax = 0u;  // every key is NaN
+    uint32_t kmin = kmin1 + 1u;  // 0 when every key is NaN (then kmax = 0 too)
     const uint32_t range = kmax - kmin;
     const int sh = range == 0u ? 0 : max(0, (32 - __clz(range)) - 11);
     auto bin_of = [&](uint32_t k) -> uint32_t { return k == 0u ? 0u : 1u + ((k - kmin) >> sh); };
