@@ -145,16 +145,17 @@ def _fmt_of(t: torch.Tensor, declared: int | None = None) -> int:
 
 def _scratch(nbytes, device, stream, zero=False):
     """A temporary workspace for one call, or None for 0 bytes (zero-filled if
-    asked). torch allocates it on the current stream; when the call is
-    enqueued on another stream the allocator is told (record_stream), so that
-    the block is not handed to another tensor before that stream's kernels
-    have finished with it."""
+    asked). It is allocated, and zero-filled, on the stream the call is
+    enqueued on: the caching allocator then keeps the block until that
+    stream's kernels have finished with it, and the fill is ordered before
+    them."""
     if not nbytes:
         return None
-    ws = (torch.zeros if zero else torch.empty)(nbytes, dtype=torch.uint8, device=device)
-    if stream is not None:
-        ws.record_stream(stream)
-    return ws
+    alloc = torch.zeros if zero else torch.empty
+    if stream is None:
+        return alloc(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return alloc(nbytes, dtype=torch.uint8, device=device)
 
 
 def _check(name, status):

@@ -629,6 +629,33 @@ def test_indexer_topk512_long_batches(csa, fmt, case):
         assert ok, f"row {t}: selection differs outside the near-tie band ({nband} in band)"
 
 
+def test_indexer_topk512_side_stream(csa):
+    """A call enqueued on a stream other than the current one, with the
+    library's temporary workspace: it is allocated and zero-filled on that
+    stream (the in-scan finish counts arrivals in it), and the selection is
+    bit for bit the one made on the current stream."""
+    g = gen.rng(1395)
+    lens = [20000 - 37 * i for i in range(8)]  # 20 chunks per row: finished inside the scan
+    T = len(lens)
+    pt, pool, _ = _index_case(g, "fp8", T, lens)
+    qcodes, qsc = O.index_prep(gen.normal(g, (T, 64, 128)), True, "fp8")
+    w = gen.uniform(g, (T, 64))
+    dpool = index_pool_to_device(pool, 64, 128)
+    args = (t_dev(qcodes), t_dev(w), t_dev(np.arange(T, dtype=np.int32)),
+            t_dev(np.array(lens, np.int32)), max(lens), t_dev(pt), dpool)
+    qs = t_dev(qsc.astype(np.float32))
+    p1 = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    csa.indexer_topk512(*args, p1, q_fmt=csa.CSA_FP8_E4M3, q_scale=qs)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    p2 = torch.full((T, 512), -7, dtype=torch.int32, device=DEV)
+    for _ in range(3):  # repeated: each call's counters must start at zero
+        csa.indexer_topk512(*args, p2, q_fmt=csa.CSA_FP8_E4M3, q_scale=qs, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2)
+
+
 def test_indexer_topk512_f32_two_calls(csa):
     """An fp32 index pool takes the two-call path (logits in the workspace):
     the selection is the top-512 of the oracle's logits outside the near-tie
