@@ -572,14 +572,18 @@ def _long_chunk(lens, slots=256):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-@pytest.mark.parametrize("case", ["ragged16_c5120", "rows30_c4608", "rows40_final_c4608"])
+@pytest.mark.parametrize("case", ["ragged16_c5120", "rows30_c4608", "rows40_final_c4608",
+                                  "rows100_final_c5120", "rows70_c4096"])
 def test_indexer_topk512_long_batches(csa, fmt, case):
     """Batches with more live 4096-entry scan chunks than the GPU holds at
     once take longer chunks, chosen from the rows' lengths: 16 ragged rows of
     3K-234K entries (5120-entry chunks, finished inside the scan in up to 6
-    groups), 30 rows of ~36000 (4608, finished inside the scan) and 40 rows of
-    ~27000 (4608, through the final pass, a chunk of padding per row). Bit for
-    bit the two-call path; sampled rows against the oracle's top-512."""
+    groups), 30 rows of ~36000 (4608, finished inside the scan), 40 rows of
+    ~27000 (4608, through the final pass, a chunk of padding per row), and
+    with more than 64 rows (the plan over four 64-row blocks per lane) 100
+    rows of ~10000 (5120, final pass) and 70 rows of ~40000 (4096 in three
+    rounds, finished inside the scan). Bit for bit the two-call path; sampled
+    rows against the oracle's top-512."""
     from tests.fullsize import topk_agrees
     if case == "ragged16_c5120":
         lens = [int(n) for n in gen.ragged_lengths(gen.rng(1005), 16, 8192, 1 << 20) // 4]
@@ -587,9 +591,15 @@ def test_indexer_topk512_long_batches(csa, fmt, case):
     elif case == "rows30_c4608":
         lens = [36000 - 3 * i for i in range(30)]
         want_chunk = 4608
-    else:
+    elif case == "rows40_final_c4608":
         lens = [27000 - 5 * i for i in range(40)]
         want_chunk = 4608
+    elif case == "rows100_final_c5120":
+        lens = [10000 - 3 * i for i in range(100)]
+        want_chunk = 5120
+    else:
+        lens = [40000 - 7 * i for i in range(70)]
+        want_chunk = 4096
     assert sum((n + 4095) // 4096 for n in lens) > 256 and _long_chunk(lens) == want_chunk
     g = gen.rng(1380 + len(fmt) + len(case))
     T = len(lens)
