@@ -573,7 +573,8 @@ def _long_chunk(lens, slots=256):
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("case", ["ragged16_c5120", "rows30_c4608", "rows40_final_c4608",
-                                  "rows100_final_c5120", "rows70_c4096"])
+                                  "rows100_final_c5120", "rows70_c4096", "rows70_empty_short",
+                                  "rows100_final_empty_short"])
 def test_indexer_topk512_long_batches(csa, fmt, case):
     """Batches with more live 4096-entry scan chunks than the GPU holds at
     once take longer chunks, chosen from the rows' lengths: 16 ragged rows of
@@ -582,8 +583,10 @@ def test_indexer_topk512_long_batches(csa, fmt, case):
     ~27000 (4608, through the final pass, a chunk of padding per row), and
     with more than 64 rows (the plan over four 64-row blocks per lane) 100
     rows of ~10000 (5120, final pass) and 70 rows of ~40000 (4096 in three
-    rounds, finished inside the scan). Bit for bit the two-call path; sampled
-    rows against the oracle's top-512."""
+    rounds, finished inside the scan); both last ones again with empty rows
+    and rows shorter than 512. Bit for bit the two-call path; sampled rows
+    (the longest, a middle one, the shortest non-empty one) against the
+    oracle's top-512."""
     from tests.fullsize import topk_agrees
     if case == "ragged16_c5120":
         lens = [int(n) for n in gen.ragged_lengths(gen.rng(1005), 16, 8192, 1 << 20) // 4]
@@ -594,12 +597,17 @@ def test_indexer_topk512_long_batches(csa, fmt, case):
     elif case == "rows40_final_c4608":
         lens = [27000 - 5 * i for i in range(40)]
         want_chunk = 4608
-    elif case == "rows100_final_c5120":
+    elif case.startswith("rows100_final"):
         lens = [10000 - 3 * i for i in range(100)]
         want_chunk = 5120
     else:
         lens = [40000 - 7 * i for i in range(70)]
         want_chunk = 4096
+    if case.endswith("empty_short"):
+        for i in (0, 5, 17, len(lens) - 1):
+            lens[i] = 0
+        for i in (6, 41):
+            lens[i] = 300 + i
     assert sum((n + 4095) // 4096 for n in lens) > 256 and _long_chunk(lens) == want_chunk
     g = gen.rng(1380 + len(fmt) + len(case))
     T = len(lens)
@@ -629,11 +637,16 @@ def test_indexer_topk512_long_batches(csa, fmt, case):
     gp, gl = phys.cpu().numpy(), logi.cpu().numpy()
     assert np.array_equal(gp, phys2.cpu().numpy()) and np.array_equal(gl, logi2.cpu().numpy())
     qhat = O.index_dequant(qcodes, qsc, fmt)
-    order = np.argsort(lens)
+    for t, n in enumerate(lens):
+        if n == 0:
+            assert np.all(gl[t] == -1) and np.all(gp[t] == -1), f"row {t}: empty row not -1"
+    order = [t for t in np.argsort(lens) if lens[t] > 0]
     for t in (int(order[-1]), int(order[len(order) // 2]), int(order[0])):
         n = lens[t]
-        assert np.all(np.diff(gl[t]) > 0), f"row {t}: not ascending"
-        assert np.array_equal(gp[t], O.page_slot(pt[t], gl[t], 64)), f"row {t}: slots"
+        k = min(512, n)
+        assert np.all(gl[t, k:] == -1) and np.all(gp[t, k:] == -1), f"row {t}: tail not -1"
+        assert np.all(np.diff(gl[t, :k]) > 0), f"row {t}: not ascending"
+        assert np.array_equal(gp[t, :k], O.page_slot(pt[t], gl[t, :k], 64)), f"row {t}: slots"
         want = O.indexer_logits(qhat[t], w[t], pool.rows(O.page_slot(pt[t], np.arange(n), 64)))
         ok, _, nband = topk_agrees(want, gl[t], 512, 1e-4 * np.abs(want).max())
         assert ok, f"row {t}: selection differs outside the near-tie band ({nband} in band)"
