@@ -38,9 +38,10 @@ constexpr int kRing = 2;     // 64-entry batches in flight per wave
 constexpr int kWgEntries = kWaves * kRing * 64;
 constexpr int kMaxChunk = 8 * kWgEntries;  // entries per workgroup, at most
 constexpr int kScanSlots = 256;            // scan workgroups resident at once (one per CU)
-// Long ragged batches (more live 4096-entry chunks than kScanSlots): the scan
-// takes chunks of up to kWideChunk entries, their length chosen on the device
-// from the rows' lengths (wide_chunk), for rows of at most kWideRows rows.
+// Long ragged batches (more entries than kScanSlots chunks of 4096, at most
+// kWideRows rows): the scan takes chunks of up to kWideChunk entries, their
+// length and the work items planned on the device from the rows' lengths
+// (wide_item).
 constexpr int kWideChunk = kMaxChunk + 2 * kWgEntries;
 constexpr int kWideRows = 256;
 
@@ -185,7 +186,7 @@ __device__ __forceinline__ void cand_finish(const CandOut& co, int t, int x, int
                             co.logical_idx ? co.logical_idx + (int64_t)t * kTopK : nullptr);
 }
 
-// The scan over a long ragged batch (kWide): workgroup j takes work item j
+// The scan over a long ragged batch (indexer_wide_kernel): workgroup j takes work item j
 // (the grid has one workgroup per 4096-entry chunk slot of every row, at
 // least as many as there are items; those past the last item exit). The chunk
 // length is chosen from the rows' lengths: of 4096, 4608 and 5120 entries,
@@ -1106,14 +1107,15 @@ hipError_t launch_indexer(const void* q, int q_fmt, const void* q_scale, uint32_
 #undef CSA_ROWS
     return hipGetLastError();
   }
-  // The grid covers the rows in 4096-entry chunks; with long ragged rows
-  // (more entries than kScanSlots such chunks) the workgroups take chunks of
-  // the length wide_chunk picks, and those past a row's end exit as usual.
+  // The grid covers the rows in 4096-entry chunks. A long ragged batch (more
+  // entries than kScanSlots such chunks) takes indexer_wide_kernel over as
+  // many workgroups, one per work item of the plan wide_item makes on the
+  // device (the candidate slots stay those of 4096-entry chunks).
   dim3 grid((unsigned)((max_row_len + chunk - 1) / chunk), T);
   CandOut co = cand ? *cand : CandOut{};
   const bool wide = cand && k.page_size == 64 && T <= kWideRows &&
                     (int64_t)T * max_row_len > (int64_t)kScanSlots * kMaxChunk;
-  if (wide) {  // the chunk slots stay those of 4096-entry chunks
+  if (wide) {
     co.wide_rows = T;
     co.wide_chunks = (int)grid.x;
     const dim3 g1(grid.x * grid.y);
