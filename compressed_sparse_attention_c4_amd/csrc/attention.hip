@@ -566,12 +566,15 @@ attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
 // lines are flushed from L2 before the next kernel starts, so with many
 // queries (a copy of several MB) the gather is faster; with few, the copy's
 // single round is.
-constexpr int kChunk = 64;                // entries per phase-A workgroup
+constexpr int kChunk = 64;                // entries per phase-A workgroup (or kChunkWide)
+constexpr int kChunkWide = 96;
+constexpr int kAttnCUs = 256;             // CUs of the GPU (32 per XCD)
 constexpr int kSlice = 64;                // value dims per phase-B workgroup
 constexpr int kTwoPhaseMaxE = 768;        // entry lists up to this length
 constexpr int kVStride = kSlice + 8;      // bf16 per value row in phase B's LDS
 constexpr size_t kGatherMinCopy = 4u << 20;  // value copies this large take the gather
 
+template <int kCh>
 __global__ void __launch_bounds__(256)
 attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restrict__ q_seq,
                    const int32_t* __restrict__ q_pos, bool hca, const int32_t* __restrict__ phys_idx,
@@ -584,22 +587,23 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
                    uint16_t* __restrict__ pw, float2* __restrict__ stats,
                    uint8_t* __restrict__ vcopy, int32_t* __restrict__ ent, int e_pad, int T,
                    int nz, int g) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kChunk * kKStride];
-  __shared__ int32_t s_es[kChunk];
-  __shared__ float s_sc[kChunk];
-  __shared__ uint64_t s_la[kChunk], s_ra[kChunk];  // latent / RoPE row addresses
-  const int n_chunks = e_pad / kChunk;
+  constexpr int kCB = kCh / 16;  // 16-entry column blocks of the chunk
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kCh * kKStride];
+  __shared__ int32_t s_es[kCh];
+  __shared__ float s_sc[kCh];
+  __shared__ uint64_t s_la[kCh], s_ra[kCh];  // latent / RoPE row addresses
+  const int n_chunks = e_pad / kCh;
   const Coord bc = block_coord(n_chunks, nz, g);
   const int chunk = bc.a, t = bc.t;
   if (t >= T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int e0 = chunk * kChunk;
+  const int e0 = chunk * kCh;
   // A selected entry's slot needs nothing of the query's position: its load
   // goes out together with the position's, one round trip earlier than a
   // lookup that waits for the entry list.
   int32_t pre = -1;
-  if (!hca && tid < kChunk && e0 + tid < k_sel) pre = phys_idx[(int64_t)t * k_sel + e0 + tid];
+  if (!hca && tid < kCh && e0 + tid < k_sel) pre = phys_idx[(int64_t)t * k_sel + e0 + tid];
   const int seq = q_seq[t], p = q_pos[t];
   const EntryList L = entry_list(p, k_sel, hca, ratio, window);
   const int total = min(L.n1 + L.n2, e_pad);  // a list longer than the stated bound is cut
@@ -611,17 +615,17 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
     // past this query's list: zero weights, dead statistics and masked
     // entries, so that phase B reads every chunk without knowing the list's
     // length
-    const int hh = tid >> 2, part = tid & 3;
-    v4i* prow = reinterpret_cast<v4i*>(pw + ((int64_t)t * H + hb0 + hh) * e_pad + e0 + part * 16);
-    prow[0] = v4i{0, 0, 0, 0};
-    prow[1] = v4i{0, 0, 0, 0};
-    if (tid < kChunk) stats[((int64_t)t * H + hb0 + tid) * n_chunks + chunk] = make_float2(-INFINITY, 0.f);
+    const int hh = tid >> 2, part = tid & 3;  // head, quarter of the chunk
+    v4i* prow = reinterpret_cast<v4i*>(pw + ((int64_t)t * H + hb0 + hh) * e_pad + e0 + part * (kCh / 4));
+#pragma unroll
+    for (int k = 0; k < kCh / 32; ++k) prow[k] = v4i{0, 0, 0, 0};
+    if (tid < 64) stats[((int64_t)t * H + hb0 + tid) * n_chunks + chunk] = make_float2(-INFINITY, 0.f);
     if (bc.z == 0) {
       if (ent) {
-        if (tid < kChunk) ent_t[tid] = -1;
+        if (tid < kCh) ent_t[tid] = -1;
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < kCh / 8; ++k) {
           const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
           *reinterpret_cast<v4i*>(vc_t + ((int64_t)(c >> 2) * e_pad + e0 + e) * kSlice + 16 * (c & 3)) =
               v4i{0, 0, 0, 0};
@@ -632,7 +636,7 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
   }
   const int hbase = hb0 + wave * 16;
   float scv = 0.f;
-  if (tid < kChunk) {
+  if (tid < kCh) {
     const int i = e0 + tid;
     int pool = 0;
     int64_t slot = -1;
@@ -661,21 +665,21 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
     for (int s = 0; s < 18; ++s) qa[s] = *reinterpret_cast<const v4i*>(qrow + s * 32);
   }
   lds_sync();
-  // gathers: 64 entries x 32 latent chunks of 16 B (8 per thread, one entry
-  // row per 32 lanes), 64 x 8 RoPE chunks (2 per thread)
-  v4i lat[8], rp[2];
+  // gathers: kCh entries x 32 latent chunks of 16 B (kCh / 8 per thread, one
+  // entry row per 32 lanes), kCh x 8 RoPE chunks (kCh / 32 per thread)
+  v4i lat[kCh / 8], rp[kCh / 32];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < kCh / 8; ++k) {
     const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
     lat[k] = gload<v4i>(s_la[e] + 16 * c);
   }
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kCh / 32; ++k) {
     const int idx = tid + k * 256, e = idx >> 3, c = idx & 7;
     rp[k] = gload<v4i>(s_ra[e] + 16 * c);
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < kCh / 8; ++k) {
     const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
     uint32_t b[8];
 #pragma unroll
@@ -688,53 +692,53 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
     *reinterpret_cast<v4i*>(dst + 8) = v4i{(int)b[4], (int)b[5], (int)b[6], (int)b[7]};
   }
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kCh / 32; ++k) {
     const int idx = tid + k * 256, e = idx >> 3, c = idx & 7;
     *reinterpret_cast<v4i*>(&s_k[e * kKStride + kLatent + 8 * c]) = rp[k];
   }
-  if (tid < kChunk) s_sc[tid] = scv;
+  if (tid < kCh) s_sc[tid] = scv;
   // copy mode: the codes, as gathered, into the per-slice value copy
   if (bc.z == 0 && !ent) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < kCh / 8; ++k) {
       const int idx = tid + k * 256, e = idx >> 5, c = idx & 31;
       *reinterpret_cast<v4i*>(vc_t + ((int64_t)(c >> 2) * e_pad + e0 + e) * kSlice + 16 * (c & 3)) = lat[k];
     }
   }
   lds_sync();
 
-  // scores of 16 heads x 64 entries (four 16-column blocks). The k-steps run
-  // outermost, so consecutive matrix ops feed four independent accumulators
+  // scores of 16 heads x kCh entries (kCB 16-column blocks). The k-steps run
+  // outermost, so consecutive matrix ops feed kCB independent accumulators
   // (a chain on one accumulator would wait out each op's latency), and the K
   // fragments are read twelve ahead of the matrix ops.
-  v4f acc_l[4], acc_r[4];
+  v4f acc_l[kCB], acc_r[kCB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) acc_l[cb] = acc_r[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < kCB; ++cb) acc_l[cb] = acc_r[cb] = v4f{0.f, 0.f, 0.f, 0.f};
   {
-    constexpr int kAhead = 12;
+    constexpr int kAhead = 12, kNF = 18 * kCB;
     const uint16_t* kb = s_k + col * kKStride + grp * 8;
     auto kfrag = [&](int j) {
-      return *reinterpret_cast<const v4i*>(kb + (j & 3) * 16 * kKStride + (j >> 2) * 32);
+      return *reinterpret_cast<const v4i*>(kb + (j % kCB) * 16 * kKStride + (j / kCB) * 32);
     };
-    v4i kf[72];
+    v4i kf[kNF];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) kf[j] = kfrag(j);
     // one k-step per group; the scheduling fences keep the steps in order
 #pragma unroll
     for (int s = 0; s < 18; ++s) {
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int j = s * 4 + cb;
-        if (j + kAhead < 72) kf[j + kAhead] = kfrag(j + kAhead);
+      for (int cb = 0; cb < kCB; ++cb) {
+        const int j = s * kCB + cb;
+        if (j + kAhead < kNF) kf[j + kAhead] = kfrag(j + kAhead);
         if (s < 16) acc_l[cb] = mfma_bf16(qa[s], kf[j], acc_l[cb]);
         else acc_r[cb] = mfma_bf16(qa[s], kf[j], acc_r[cb]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  float sv[4][4];
+  float sv[kCB][4];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < kCB; ++cb) {
     const int e = cb * 16 + col;
     const bool valid = s_es[e] >= 0;
     const float sc = s_sc[e];
@@ -744,12 +748,15 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = hbase + grp * 4 + r;
-    const float m = row16_max(fmaxf(fmaxf(sv[0][r], sv[1][r]), fmaxf(sv[2][r], sv[3][r])));
+    float mr = sv[0][r];
+#pragma unroll
+    for (int cb = 1; cb < kCB; ++cb) mr = fmaxf(mr, sv[cb][r]);
+    const float m = row16_max(mr);
     const bool dead = m == -INFINITY;
     float ps = 0.f;
     uint16_t* prow = pw + ((int64_t)t * H + h) * e_pad + e0;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
       const float pr = dead ? 0.f : __expf(sv[cb][r] - m);
       ps += pr;
       prow[cb * 16 + col] = f32_to_bf16(pr * s_sc[cb * 16 + col]);
@@ -765,14 +772,14 @@ attn_scores_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restr
 // the value slice goes to LDS row-major, and the P V products read their
 // value operands from it with the transposing LDS load. kNC: chunk slots
 // computed (the list's chunk count rounded up to even; extra slots are dead).
-template <int kNC, bool kOutF32, bool kGather>
+template <int kCh, int kNC, bool kOutF32, bool kGather>
 __global__ void __launch_bounds__(256)
 attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const int32_t* __restrict__ ent,
                const uint8_t* __restrict__ c_lat, const uint8_t* __restrict__ r_lat,
                const uint16_t* __restrict__ pw,
                const float2* __restrict__ stats, int e_pad, void* __restrict__ out, int T,
                int nz, int g) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[kNC * kChunk * kVStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kNC * kCh * kVStride];
   __shared__ float s_f[64][kNC];
   const Coord bc = block_coord(kLatent / kSlice, nz, g);
   const int slice = bc.a, t = bc.t;
@@ -780,7 +787,8 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const int32_t* __restri
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int hb0 = bc.z * 64;
-  const int n_chunks = e_pad / kChunk;
+  const int n_chunks = e_pad / kCh;
+  constexpr int kKS = kCh / 32;  // 32-entry k-steps per chunk
 
   // ---- first round of loads: statistics (first, so that the chunk factors
   // wait for them only), the value pieces (copy) or their slots (gather)
@@ -793,7 +801,7 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const int32_t* __restri
     for (int c = 0; c < kNC; ++c) st[c] = gload<v2f>((uint64_t)(sp + min(c, n_chunks - 1)));
   }
   asm volatile("" ::: "memory");  // keeps these loads ahead of the ones below
-  constexpr int kVP = kNC * kChunk * kSlice / 16 / 256;  // value pieces per thread
+  constexpr int kVP = kNC * kCh * kSlice / 16 / 256;  // value pieces per thread
   const int nv = e_pad * (kSlice / 16);
   v4i vp[kVP];
   int32_t es[kVP];
@@ -808,9 +816,9 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const int32_t* __restri
   }
   asm volatile("" ::: "memory");
   const uint64_t prow = (uint64_t)(pw + ((int64_t)t * H + hb0 + wave * 16 + col) * e_pad + grp * 8);
-  v4i pa[kNC * 2];
+  v4i pa[kNC * kKS];
 #pragma unroll
-  for (int ks = 0; ks < kNC * 2; ++ks) pa[ks] = gload<v4i>(prow + 2 * min(ks * 32, e_pad - 32));
+  for (int ks = 0; ks < kNC * kKS; ++ks) pa[ks] = gload<v4i>(prow + 2 * min(ks * 32, e_pad - 32));
   // gather, second round: the value pieces (a masked entry, or a piece past
   // e_pad, reads the zero row)
   if (kGather) {
@@ -867,7 +875,7 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const int32_t* __restri
   // 8*grp + 4h + a, dims 4b..4b+3 of the block.
   const uint16_t* vb = s_v + (8 * grp + (col >> 2)) * kVStride + 4 * (col & 3);
   auto vfrag = [&](int c, int ks, int db) {
-    const uint16_t* src = vb + (c * kChunk + ks * 32) * kVStride + 16 * db;
+    const uint16_t* src = vb + (c * kCh + ks * 32) * kVStride + 16 * db;
     const v2i lo = __builtin_bit_cast(
         v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)src));
     const v2i hi = __builtin_bit_cast(
@@ -883,26 +891,28 @@ attn_pv_kernel(int H, const uint8_t* __restrict__ vcopy, const int32_t* __restri
   v4f o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
-  v4i vf[kNC][8];
+  v4i vf[kNC][4 * kKS];
   float fc[kNC][4];
   v4f acc[kNC][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) vf[0][i] = vfrag(0, i >> 2, i & 3);
+  for (int i = 0; i < 4 * kKS; ++i) vf[0][i] = vfrag(0, i >> 2, i & 3);
 #pragma unroll
   for (int r = 0; r < 4; ++r) fc[0][r] = s_f[wave * 16 + grp * 4 + r][0];
 #pragma unroll
   for (int c = 0; c <= kNC; ++c) {
     if (c + 1 < kNC) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) vf[c + 1][i] = vfrag(c + 1, i >> 2, i & 3);
+      for (int i = 0; i < 4 * kKS; ++i) vf[c + 1][i] = vfrag(c + 1, i >> 2, i & 3);
 #pragma unroll
       for (int r = 0; r < 4; ++r) fc[c + 1][r] = s_f[wave * 16 + grp * 4 + r][c + 1];
     }
     if (c < kNC) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[c][db] = mfma_bf16(pa[c * 2], vf[c][db], v4f{0.f, 0.f, 0.f, 0.f});
+      for (int db = 0; db < 4; ++db) acc[c][db] = mfma_bf16(pa[c * kKS], vf[c][db], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[c][db] = mfma_bf16(pa[c * 2 + 1], vf[c][4 + db], acc[c][db]);
+      for (int ks = 1; ks < kKS; ++ks)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[c][db] = mfma_bf16(pa[c * kKS + ks], vf[c][4 * ks + db], acc[c][db]);
     }
     if (c > 0) {
 #pragma unroll
@@ -930,8 +940,23 @@ bool use_two_phase(int T, int H, int max_entries) {
   return H % 64 == 0 && T * (H / 64) <= 64 && max_entries <= kTwoPhaseMaxE && max_entries > 0;
 }
 
+// Entries per phase-A workgroup: 64, or 96 when 64-entry chunks make more
+// workgroups than the GPU has CUs and 96-entry ones do not. Phase A's
+// workgroups run one round, and a CU that holds two of them takes about 1.5x
+// as long as one that holds one (32 queries x 64 heads x 640 entries: 320
+// workgroups, 11.6 us; the same list for 24 queries, 240 workgroups, 7.7
+// us), so the kernel lasts as long as its doubly loaded CUs. Every query's
+// workgroups sit on its own XCD (block_coord), so the count that matters is
+// the grid's.
+int two_phase_chunk(int T, int H, int max_entries) {
+  const int nz = H / 64;
+  const unsigned g64 = xcd_grid((max_entries + kChunk - 1) / kChunk, nz, T).x;
+  const unsigned gw = xcd_grid((max_entries + kChunkWide - 1) / kChunkWide, nz, T).x;
+  return (g64 > (unsigned)kAttnCUs && gw <= (unsigned)kAttnCUs) ? kChunkWide : kChunk;
+}
+
 // Workspace of the two-phase path: P' [T][H][e_pad] bf16, then the chunk
-// statistics [T][H][e_pad/64] float2, then phase B's value source: the
+// statistics [T][H][e_pad/ch] float2 (ch = two_phase_chunk), then phase B's value source: the
 // entries' slot codes [T][e_pad] int32 (slot * 2 + pool, -1 when masked) in
 // gather mode, the value copy [T][8][e_pad][64] (FP8 codes, one block per
 // 64-dim slice) in copy mode.
@@ -939,11 +964,11 @@ struct TwoPhaseWs {
   size_t pw, stats, src, total;
   bool gather;
 };
-TwoPhaseWs two_phase_ws(int64_t T, int H, int e_pad) {
+TwoPhaseWs two_phase_ws(int64_t T, int H, int e_pad, int ch) {
   TwoPhaseWs w;
   w.pw = 0;
   w.stats = ((size_t)T * H * e_pad * 2 + 255) / 256 * 256;
-  w.src = w.stats + ((size_t)T * H * (e_pad / kChunk) * sizeof(float2) + 255) / 256 * 256;
+  w.src = w.stats + ((size_t)T * H * (e_pad / ch) * sizeof(float2) + 255) / 256 * 256;
   const size_t copy = (size_t)T * e_pad * kLatent;
   w.gather = copy >= kGatherMinCopy;
   w.total = w.src + (w.gather ? (size_t)T * e_pad * sizeof(int32_t) : copy);
@@ -1220,8 +1245,10 @@ size_t attention_f32_ws_bytes(int64_t T, int64_t max_entries, int H) {
 }
 
 size_t attention_ws_bytes(int64_t T, int64_t max_entries, int H) {
-  if (use_two_phase((int)T, H, (int)max_entries))
-    return two_phase_ws(T, H, (int)((max_entries + kChunk - 1) / kChunk * kChunk)).total;
+  if (use_two_phase((int)T, H, (int)max_entries)) {
+    const int ch = two_phase_chunk((int)T, H, (int)max_entries);
+    return two_phase_ws(T, H, (int)((max_entries + ch - 1) / ch * ch), ch).total;
+  }
   const SplitPlan p = split_plan((int)T, H, (int)max_entries);
   return p.part_bytes + p.qsplit_bytes;
 }
@@ -1244,45 +1271,62 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (use_two_phase(a.T, a.H, max_entries)) {
-    const int e_pad = (max_entries + kChunk - 1) / kChunk * kChunk;
-    const TwoPhaseWs w = two_phase_ws(a.T, a.H, e_pad);
+    const int ch = two_phase_chunk(a.T, a.H, max_entries);
+    const int e_pad = (max_entries + ch - 1) / ch * ch;
+    const TwoPhaseWs w = two_phase_ws(a.T, a.H, e_pad, ch);
     uint16_t* pw = (uint16_t*)((char*)a.ws + w.pw);
     float2* st = (float2*)((char*)a.ws + w.stats);
     uint8_t* vc = w.gather ? nullptr : (uint8_t*)a.ws + w.src;
     int32_t* ent = w.gather ? (int32_t*)((char*)a.ws + w.src) : nullptr;
     const int nz = a.H / 64;
     const int g = xcd_group(a.T);
-    hipLaunchKernelGGL(attn_scores_kernel, xcd_grid(e_pad / kChunk, nz, a.T), dim3(256), 0, s,
-                       (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,
-                       a.ratio, (const uint8_t*)a.comp.latent, a.comp.latent_scale,
-                       (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt, a.comp_pt_stride,
-                       (const uint8_t*)a.raw.latent, a.raw.latent_scale,
-                       (const uint16_t*)a.raw.rope, a.raw.page_size, a.raw_pt, a.raw_pt_stride,
-                       a.window, a.scale, pw, st, vc, ent, e_pad, a.T, nz, g);
+#define CSA_SCORES(CH)                                                                        \
+  hipLaunchKernelGGL((attn_scores_kernel<CH>), xcd_grid(e_pad / CH, nz, a.T), dim3(256), 0, s,     \
+                     (const uint16_t*)a.q, a.H, a.q_seq, a.q_pos, a.hca, a.phys_idx, a.k_sel,      \
+                     a.ratio, (const uint8_t*)a.comp.latent, a.comp.latent_scale,                \
+                     (const uint16_t*)a.comp.rope, a.comp.page_size, a.comp_pt, a.comp_pt_stride, \
+                     (const uint8_t*)a.raw.latent, a.raw.latent_scale,                            \
+                     (const uint16_t*)a.raw.rope, a.raw.page_size, a.raw_pt, a.raw_pt_stride,     \
+                     a.window, a.scale, pw, st, vc, ent, e_pad, a.T, nz, g)
+    if (ch == kChunkWide) CSA_SCORES(kChunkWide);
+    else CSA_SCORES(kChunk);
+#undef CSA_SCORES
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-#define CSA_PV(NC, FO, GA)                                                                      \
-  hipLaunchKernelGGL((attn_pv_kernel<NC, FO, GA>), xcd_grid(kLatent / kSlice, nz, a.T), dim3(256), 0, \
-                     s, a.H, vc, ent, (const uint8_t*)a.comp.latent, (const uint8_t*)a.raw.latent, pw, \
-                     st, e_pad, a.out, a.T, nz, g)
-#define CSA_PV_NC(NC)                                   \
+#define CSA_PV(CH, NC, FO, GA)                                                                  \
+  hipLaunchKernelGGL((attn_pv_kernel<CH, NC, FO, GA>), xcd_grid(kLatent / kSlice, nz, a.T), dim3(256), \
+                     0, s, a.H, vc, ent, (const uint8_t*)a.comp.latent, (const uint8_t*)a.raw.latent, \
+                     pw, st, e_pad, a.out, a.T, nz, g)
+#define CSA_PV_NC(CH, NC)                               \
   case NC:                                              \
     if (a.out_fmt == CSA_F32) {                         \
-      if (w.gather) CSA_PV(NC, true, true);             \
-      else CSA_PV(NC, true, false);                     \
+      if (w.gather) CSA_PV(CH, NC, true, true);         \
+      else CSA_PV(CH, NC, true, false);                 \
     } else {                                            \
-      if (w.gather) CSA_PV(NC, false, true);            \
-      else CSA_PV(NC, false, false);                    \
+      if (w.gather) CSA_PV(CH, NC, false, true);        \
+      else CSA_PV(CH, NC, false, false);                \
     }                                                   \
     break;
-    switch ((e_pad / kChunk + 1) / 2 * 2) {
-      CSA_PV_NC(2)
-      CSA_PV_NC(4)
-      CSA_PV_NC(6)
-      CSA_PV_NC(8)
-      CSA_PV_NC(10)
-      CSA_PV_NC(12)
-      default: return hipErrorInvalidValue;
+    // chunk slots: the list's chunks rounded up to even (the extra one is dead)
+    const int nc = (e_pad / ch + 1) / 2 * 2;
+    if (ch == kChunkWide) {
+      switch (nc) {
+        CSA_PV_NC(kChunkWide, 2)
+        CSA_PV_NC(kChunkWide, 4)
+        CSA_PV_NC(kChunkWide, 6)
+        CSA_PV_NC(kChunkWide, 8)
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (nc) {
+        CSA_PV_NC(kChunk, 2)
+        CSA_PV_NC(kChunk, 4)
+        CSA_PV_NC(kChunk, 6)
+        CSA_PV_NC(kChunk, 8)
+        CSA_PV_NC(kChunk, 10)
+        CSA_PV_NC(kChunk, 12)
+        default: return hipErrorInvalidValue;
+      }
     }
 #undef CSA_PV_NC
 #undef CSA_PV

@@ -387,6 +387,10 @@ def _attn_case(g, fmt, B, Ls, H, ps_c=64, extra=3):
     # two-phase path with 16 queries: phase B gathers its values from the pools
     (64, "fp8", [131072 // 16 + 997 * i for i in range(14)] + [700, 9], True),
     (64, "fp8", [20 + 3 * i for i in range(130)], False),  # > 128 queries: split + combine path
+    # 32 and 31 queries: more 64-entry chunks than CUs, so 96-entry chunks
+    # (the last one partly past the list)
+    (64, "fp8", [131072 // 16 + 997 * i for i in range(28)] + [700, 100, 9, 5000], False),
+    (64, "fp8", [20000 + 4099 * i for i in range(29)] + [130, 9], True),
     (32, "fp8", [20000, 131, 9, 3000], True),  # two 16-head pairs, fp32 output
     (16, "fp8", [5000, 700, 9], False),  # one 16-head pair
     (16, "f32", [4096, 333], True),
@@ -426,6 +430,8 @@ def test_csa_attention(csa, H, fmt, Ls, out_f32):
 @pytest.mark.parametrize("fmt,Ls,H", [("fp8", [100, 128 * 40 + 77, 60000], 64),  # two-phase path
                                       ("fp8", [100, 128 * 40 + 77, 1048576 // 8], 64),
                                       ("fp8", [400000, 1000], 64),  # long list: many splits
+                                      # 32 lists of up to 748 entries: 96-entry chunks
+                                      ("fp8", [int(2000 * 1.126 ** i) for i in range(32)], 64),
                                       # 64 ragged lists (the most the length-balanced splits take)
                                       ("fp8", [int(500 * 1.085 ** i) for i in range(64)], 64),
                                       ("f32", [127, 128 * 9], 16)])
