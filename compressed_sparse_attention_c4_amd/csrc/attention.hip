@@ -547,6 +547,61 @@ attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
   }
 }
 
+// The merge for length-balanced splits, where a long list owns many slots
+// (HCA over ragged lengths: the longest of 16 lists takes ~50 of 256): one
+// head per workgroup, its slots dealt round-robin to the four waves, whose
+// partial sums meet in LDS. A wave then walks a quarter of the slots, so the
+// longest list's merge is four times shorter than with one wave per head.
+template <bool kOutF32>
+__global__ void __launch_bounds__(256)
+attn_combine_slots_kernel(const float* __restrict__ part, int T, int H, int nslot,
+                          void* __restrict__ out, int g, const int2* __restrict__ qsplit) {
+  __shared__ float s_acc[4][kLatent];
+  __shared__ float s_red[8];
+  const Coord bc = block_coord(H, 1, g);
+  const int t = bc.t, h = bc.a;
+  if (t >= T) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int2 qs = qsplit[t];
+  const int64_t s0 = qs.x;
+  const int ns = qs.y;
+  const float* pm = part + (int64_t)nslot * H * kLatent;
+  const float* pl = pm + (int64_t)nslot * H;
+  // the query's maximum over its slots (every wave, lanes over the slots)
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, pm[(s0 + s) * H + h]);
+  M = wave_max(M);
+  float Lsum = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  // branch-free within a wave's turn, so that the loads of several slots are
+  // in flight together (an empty slot's partial is zeros, its factor 0)
+#pragma unroll 4
+  for (int s = wave; s < ns; s += 4) {
+    const int64_t idx = (s0 + s) * H + h;
+    const float ms = pm[idx];
+    const float f = ms == -INFINITY ? 0.f : __expf(ms - M);
+    Lsum = fmaf(pl[idx], f, Lsum);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(part[idx * kLatent + lane + 64 * k], f, acc[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s_acc[wave][lane + 64 * k] = acc[k];
+  if (lane == 0) s_red[wave] = Lsum;
+  __syncthreads();
+  const float L = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int64_t ob = ((int64_t)t * H + h) * kLatent;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int d = tid + 256 * k;
+    const float v = ((s_acc[0][d] + s_acc[1][d]) + (s_acc[2][d] + s_acc[3][d])) * inv;
+    if (kOutF32) reinterpret_cast<float*>(out)[ob + d] = v;
+    else reinterpret_cast<uint16_t*>(out)[ob + d] = f32_to_bf16(v);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Two-phase path for few queries (decode). With T small, the split kernel
 // needs many splits per query and each writes a 64 x 512 fp32 partial, more
@@ -1356,7 +1411,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 #undef CSA_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.nsplit == 1) return e;
-  if (f32o)
+  if (sp.balanced) {
+    if (f32o)
+      hipLaunchKernelGGL(attn_combine_slots_kernel<true>, xcd_grid(a.H, 1, a.T), dim3(256), 0, s,
+                         part, a.T, a.H, nsplit, a.out, g, qsplit);
+    else
+      hipLaunchKernelGGL(attn_combine_slots_kernel<false>, xcd_grid(a.H, 1, a.T), dim3(256), 0, s,
+                         part, a.T, a.H, nsplit, a.out, g, qsplit);
+  } else if (f32o)
     hipLaunchKernelGGL(attn_combine_kernel<true>, xcd_grid(a.H / 4, 1, a.T), dim3(256), 0, s,
                        part, a.T, a.H, nsplit, a.out, g, qsplit);
   else

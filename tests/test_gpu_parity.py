@@ -391,6 +391,9 @@ def _attn_case(g, fmt, B, Ls, H, ps_c=64, extra=3):
     # (the last one partly past the list)
     (64, "fp8", [131072 // 16 + 997 * i for i in range(28)] + [700, 100, 9, 5000], False),
     (64, "fp8", [20000 + 4099 * i for i in range(29)] + [130, 9], True),
+    # 48 queries: more workgroups than CUs even with 96-entry chunks, so
+    # 64-entry chunks, two workgroups per CU
+    (64, "fp8", [9000 + 131 * i for i in range(47)] + [77], True),
     (32, "fp8", [20000, 131, 9, 3000], True),  # two 16-head pairs, fp32 output
     (16, "fp8", [5000, 700, 9], False),  # one 16-head pair
     (16, "f32", [4096, 333], True),
