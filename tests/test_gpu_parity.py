@@ -387,6 +387,8 @@ def _attn_case(g, fmt, B, Ls, H, ps_c=64, extra=3):
     # two-phase path with 16 queries: phase B gathers its values from the pools
     (64, "fp8", [131072 // 16 + 997 * i for i in range(14)] + [700, 9], True),
     (64, "fp8", [20 + 3 * i for i in range(130)], False),  # > 128 queries: split + combine path
+    # 70 queries x 2 head blocks: two uniform splits + combine, fp32 output
+    (128, "fp8", [2050 + 3 * i for i in range(69)] + [9], True),
     # 32 and 31 queries: more 64-entry chunks than CUs, so 96-entry chunks
     # (the last one partly past the list)
     (64, "fp8", [131072 // 16 + 997 * i for i in range(28)] + [700, 100, 9, 5000], False),
