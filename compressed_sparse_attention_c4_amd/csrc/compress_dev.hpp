@@ -52,28 +52,39 @@ __device__ __forceinline__ void compress_entry(const void* __restrict__ x, int64
 
   // rows in batches of kRowBatch, all loads of a batch issued before any of
   // its rows is used (rows past the block repeat its first row, unused)
-  constexpr int kRowBatch = 4;
+  constexpr int kRowBatch = 4;  // (the batch sum of p below is written for four)
   for (int r0 = 0; r0 < ratio; r0 += kRowBatch) {
     float v[kRowBatch][9];
 #pragma unroll
     for (int u = 0; u < kRowBatch; ++u) load_row<kF32In>(x, rbase + (r0 + u < ratio ? r0 + u : 0), v[u]);
+    // the batch's gates (independent reductions), then one rescale of the
+    // running sums to the batch's maximum; rows past the block get gate -inf:
+    // weight 0 (the block's first row keeps the maximum finite)
+    float g[kRowBatch];
 #pragma unroll
     for (int u = 0; u < kRowBatch; ++u) {
-      // rows past the block get gate -inf: weight 0, and the running max
-      // (finite from the block's first row on) is unchanged
       const bool in = r0 + u < ratio;
       float d = 0.f;
 #pragma unroll
       for (int i = 0; i < 9; ++i) d = fmaf(w[i], v[u][i], d);
-      const float g = in ? wave_sum(d) + gate_b[in ? r0 + u : 0] : -INFINITY;
-      const float mn = fmaxf(m, g);
-      const float corr = expf(m - mn);  // exp(-inf) = 0 on the first row
-      const float p = expf(g - mn);
-      l = l * corr + p;
-#pragma unroll
-      for (int i = 0; i < 9; ++i) acc[i] = fmaf(p, v[u][i], acc[i] * corr);
-      m = mn;
+      g[u] = in ? wave_sum(d) + gate_b[in ? r0 + u : 0] : -INFINITY;
     }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) mn = fmaxf(mn, g[u]);
+    const float corr = expf(m - mn);  // exp(-inf) = 0 on the first batch
+    float p[kRowBatch];
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) p[u] = expf(g[u] - mn);
+    l = l * corr + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      float a = acc[i] * corr;
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) a = fmaf(p[u], v[u][i], a);
+      acc[i] = a;
+    }
+    m = mn;
   }
   const float inv = 1.0f / l;
   float c[9];
