@@ -262,8 +262,10 @@ def capture_graphs(W, copies):
 
 
 def time_steps(W, steps, warmup, copies, graph=True):
-    """(ms per step over the timed region, mean / median roofline-kernel ms).
-    The step time is taken over `steps` graph replays (or eager steps); the
+    """(ms per step over the timed region, mean / median roofline-kernel ms,
+    per-step percentiles). The step time is taken over `steps` graph replays
+    (or eager steps); the percentiles (p10 / p50 / p90, ms) over as many
+    replays after it, each bracketed by its own events behind a GPU spin; the
     roofline kernel's duration from HIP events recorded around its launch on
     the launch stream during `steps` eager steps of the same work."""
     import torch
@@ -285,6 +287,25 @@ def time_steps(W, steps, warmup, copies, graph=True):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    # per-step times: a spin ahead of each step lets the host queue it before
+    # the GPU reaches its first event
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in sev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        torch.cuda._sleep(SPIN_CYCLES)
+        sev[i][0].record()
+        if graphs:
+            graphs[i % copies].replay()
+        else:
+            W.step(i % copies)
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in sev])
+    dist = {f"p{q}": round(float(np.percentile(per, q)), 5) for q in (10, 50, 90)}
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     # the events' handles exist after a first record; made here, so that no
@@ -301,7 +322,7 @@ def time_steps(W, steps, warmup, copies, graph=True):
     torch.cuda.synchronize()
     k_ms = [a.elapsed_time(b) for a, b in evs]
     del graphs
-    return ms, float(np.mean(k_ms)), float(np.median(k_ms))
+    return ms, float(np.mean(k_ms)), float(np.median(k_ms)), dist
 
 
 def hbm_roofline(kernel, nbytes, k_ms):
@@ -432,10 +453,10 @@ def cpu_baseline_tiny(W, reps):
 
 
 def line_decode(W, a, copies, roofline_kernel, cpu=None):
-    ms, k_ms, _ = time_steps(W, a.steps, a.warmup, copies, graph=not a.no_graph)
+    ms, k_ms, _, dist = time_steps(W, a.steps, a.warmup, copies, graph=not a.no_graph)
     rows = getattr(W, "T", W.B)
     d = {"queries_per_s": round(rows / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
-         "pool_copies": copies,
+         "step_ms_percentiles": dist, "pool_copies": copies,
          "roofline": hbm_roofline(roofline_kernel, W.indexer_bytes(), k_ms),
          "step_bytes": int(W.step_bytes()),
          "step_hbm_frac": round(W.step_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -457,9 +478,10 @@ def secondary(a):
 
     # tiny all-fp32 decode: latency of one step
     W = TinyDecode(specs.TINY_FP32_DECODE)
-    ms, k_ms, _ = time_steps(W, steps, a.warmup, 1, graph=not a.no_graph)
+    ms, k_ms, _, dist = time_steps(W, steps, a.warmup, 1, graph=not a.no_graph)
     out[specs.TINY_FP32_DECODE.name] = {
         "queries_per_s": round(1 / (ms / 1e3), 1), "latency_us": round(ms * 1e3, 2),
+        "step_ms_percentiles": dist,
         "step_bytes": W.step_bytes(),
         "roofline": {"bound": "latency", "note": "1.8 MB per step is 0.2 us at 8 TB/s: launch and "
                      "latency bound; the step time is the figure", "frac": None},
@@ -489,11 +511,12 @@ def secondary(a):
     # chunked prefill: 4096 new tokens on a 131072-token context
     wl = specs.PREFILL_4K
     W = CsaPrefill(wl)
-    ms, k_ms, _ = time_steps(W, max(5, steps // 4), 2, 1, graph=not a.no_graph)
+    ms, k_ms, _, dist = time_steps(W, max(5, steps // 4), 2, 1, graph=not a.no_graph)
     tf = W.indexer_flops() / (k_ms / 1e3) / 1e12
     kname = "indexer_rows_kernel<false, 8, true>"
     c = stored_counters(kname) or {}
     line = {"tokens_per_s": round(W.new / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+            "step_ms_percentiles": dist,
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
                          "traffic": c.get("bytes_per_launch"), "kernel": kname,
@@ -515,10 +538,11 @@ def secondary(a):
     per_copy = int((lens // 4).sum()) * (wl.index_dim + 4) + int((lens // wl.hca_ratio).sum()) * 644
     copies = auto_copies(per_copy, a.copies)
     W = HcaCsaRagged(wl, copies=copies)
-    ms, k_ms, _ = time_steps(W, steps, a.warmup, copies, graph=not a.no_graph)
+    ms, k_ms, _, dist = time_steps(W, steps, a.warmup, copies, graph=not a.no_graph)
     step_bytes = W.csa.step_bytes() + W.hca_bytes()
     line = {"queries_per_s": round(W.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
-            "pool_copies": copies, "raw_lengths": [int(x) for x in W.lens],
+            "step_ms_percentiles": dist, "pool_copies": copies,
+            "raw_lengths": [int(x) for x in W.lens],
             "roofline": hbm_roofline(W.csa.indexer_kernel, W.csa.indexer_bytes(), k_ms),
             "step_bytes": int(step_bytes),
             "step_hbm_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -629,7 +653,7 @@ def main():
     copies = auto_copies(int(wl.batch * (wl.seq_len // 4) * (wl.index_dim + 4)), a.copies)
     W = CsaDecode(wl, [wl.seq_len] * wl.batch, copies=copies, pool_pages=wl.pool_pages)
     kernel = W.indexer_kernel
-    ms, k_ms, _ = time_steps(W, a.steps, a.warmup, copies, graph=not a.no_graph)
+    ms, k_ms, _, dist = time_steps(W, a.steps, a.warmup, copies, graph=not a.no_graph)
     qps = W.B / (ms / 1e3)
     line = {
         "metric": "CSA decode queries/s @128K ctx",
@@ -639,6 +663,7 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms, 5),
+        "step_ms_percentiles": dist,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
