@@ -605,8 +605,8 @@ attn_combine_slots_kernel(const float* __restrict__ part, int T, int H, int nslo
 // ---------------------------------------------------------------------------
 // Two-phase path for few queries (decode). With T small, the split kernel
 // needs many splits per query and each writes a 64 x 512 fp32 partial, more
-// bytes than the KV it reads. Here phase A computes, for each 64-entry chunk
-// of a query's entry list, all heads' scores, the chunk's softmax max m_c and
+// bytes than the KV it reads. Here phase A computes, for each chunk (64 or 96
+// entries, two_phase_chunk) of a query's entry list, all heads' scores, the chunk's softmax max m_c and
 // sum l_c, and the weights P' = exp(s - m_c) * (value FP8 scale) in bf16;
 // phase B merges the chunks' (m_c, l_c) into the exact normaliser and sums
 // f_c * (P' V) for one 64-dim slice of the value, f_c = exp(m_c - M) / L. No
@@ -1000,9 +1000,8 @@ bool use_two_phase(int T, int H, int max_entries) {
 // workgroups run one round, and a CU that holds two of them takes about 1.5x
 // as long as one that holds one (32 queries x 64 heads x 640 entries: 320
 // workgroups, 11.6 us; the same list for 24 queries, 240 workgroups, 7.7
-// us), so the kernel lasts as long as its doubly loaded CUs. Every query's
-// workgroups sit on its own XCD (block_coord), so the count that matters is
-// the grid's.
+// us), so the kernel lasts as long as its doubly loaded CUs. The grid's size
+// decides: block_coord spreads it evenly over the eight XCDs of 32 CUs.
 int two_phase_chunk(int T, int H, int max_entries) {
   const int nz = H / 64;
   const unsigned g64 = xcd_grid((max_entries + kChunk - 1) / kChunk, nz, T).x;
@@ -1011,8 +1010,8 @@ int two_phase_chunk(int T, int H, int max_entries) {
 }
 
 // Workspace of the two-phase path: P' [T][H][e_pad] bf16, then the chunk
-// statistics [T][H][e_pad/ch] float2 (ch = two_phase_chunk), then phase B's value source: the
-// entries' slot codes [T][e_pad] int32 (slot * 2 + pool, -1 when masked) in
+// statistics [T][H][e_pad/ch] float2 (ch = two_phase_chunk), then phase B's
+// value source: the entries' slot codes [T][e_pad] int32 (slot * 2 + pool, -1 when masked) in
 // gather mode, the value copy [T][8][e_pad][64] (FP8 codes, one block per
 // 64-dim slice) in copy mode.
 struct TwoPhaseWs {
