@@ -224,9 +224,10 @@ void launch_mode(int th, int e, dim3 grid, hipStream_t s, const float* logits, i
 //    candidates of a row are reduced again. With >= 128 rows (k = 512) the rows
 //    already fill the GPU: chunks of 256 x 16 keys go to 256-thread workgroups,
 //    several of which share a CU, so one workgroup's barrier waits overlap
-//    another's work; rows longer than four such chunks take chunks of
-//    1024 x 16 keys instead, so that the final pass has fewer candidates
-//    (128 rows x 32768: 8 chunks, 11.8 + 8.5 us; 2 chunks, 11.8 + 5.8 us).
+//    another's work. Where chunks of 1024 x 16 keys on 1024-thread
+//    workgroups still make at most 512 workgroups, those are taken instead,
+//    so that the final pass has fewer candidates (128 rows x 32768: 8 chunks,
+//    11.8 + 8.5 us; 2 chunks, 11.8 + 5.8 us).
 //    With fewer rows, ~128 workgroups of 1024 threads, each >= 4096 keys.
 //  - At most kRegRow / k chunks per row, so a row's candidates fit one final
 //    workgroup. Rows longer than that are not supported (topk_max_len).
@@ -245,7 +246,9 @@ TopkPlan topk_plan(int64_t R, int64_t ld, int k) {
   const bool wide = k > kTopK;
   int64_t c;
   if (R >= 128 && !wide) {
-    c = ld > 4 * 256 * 16 ? kThreads * 16 : 256 * 16;  // 16 keys per lane
+    // 16 keys per lane; 1024-thread chunks while they still make about one
+    // round of workgroups
+    c = R * ((ld + kThreads * 16 - 1) / (kThreads * 16)) <= 512 ? kThreads * 16 : 256 * 16;
   } else {
     const int64_t want = (128 + R - 1) / R;
     c = std::max<int64_t>((ld + want - 1) / want, std::max<int64_t>(4096, 2 * (int64_t)k));
