@@ -481,7 +481,10 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
   } else {
     // partials: [slot][H][512] O, then [slot][H] m and l (O and l are
     // relative to m); slot = t * nsplit + split (uniform) or the workgroup
-    // (balanced, nsplit slots in all)
+    // (balanced, nsplit slots in all). O is fp32 for fp32 output and bf16
+    // for bf16 output (the merge reads half the bytes; the rounding adds at
+    // most 2^-9 of the largest value to the output, beside P's 2^-9), in the
+    // front of the fp32-sized region.
     const int64_t nslot = qsplit ? nsplit : (int64_t)T * nsplit;
     const int64_t ph = (qsplit ? (int64_t)blockIdx.x : (int64_t)t * nsplit + split) * H;
     float* po = part;
@@ -491,13 +494,22 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int H, const int32_t* __restric
     for (int r = 0; r < 4; ++r) {
       const int64_t obase = (ph + h0 + r) * kLatent + d0;
 #pragma unroll
-      for (int n = 0; n < 16; ++n) po[obase + n * 16] = o[n][r];
+      for (int n = 0; n < 16; ++n) {
+        if (kOutF32) po[obase + n * 16] = o[n][r];
+        else reinterpret_cast<uint16_t*>(po)[obase + n * 16] = f32_to_bf16(o[n][r]);
+      }
       if (col == 0 && half == 0) {
         pm[ph + h0 + r] = m[r];
         pl[ph + h0 + r] = l[r];
       }
     }
   }
+}
+
+// Element i of the O partials: fp32, or bf16 for bf16 output.
+template <bool kF32>
+__device__ __forceinline__ float part_o(const float* part, int64_t i) {
+  return kF32 ? part[i] : bf16_to_f32(reinterpret_cast<const uint16_t*>(part)[i]);
 }
 
 template <bool kOutF32>
@@ -536,7 +548,7 @@ attn_combine_kernel(const float* __restrict__ part, int T, int H, int nsplit,
     const float f = ms == -INFINITY ? 0.f : __expf(ms - M);
     Lsum = fmaf(pl[idx], f, Lsum);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = fmaf(part[idx * kLatent + lane + 64 * k], f, acc[k]);
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(part_o<kOutF32>(part, idx * kLatent + lane + 64 * k), f, acc[k]);
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
   const int64_t ob = ((int64_t)t * H + h) * kLatent + lane;
@@ -584,7 +596,7 @@ attn_combine_slots_kernel(const float* __restrict__ part, int T, int H, int nslo
     const float f = ms == -INFINITY ? 0.f : __expf(ms - M);
     Lsum = fmaf(pl[idx], f, Lsum);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = fmaf(part[idx * kLatent + lane + 64 * k], f, acc[k]);
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(part_o<kOutF32>(part, idx * kLatent + lane + 64 * k), f, acc[k]);
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) s_acc[wave][lane + 64 * k] = acc[k];
