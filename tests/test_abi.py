@@ -102,6 +102,32 @@ def test_workspace_sizes(lib):
     assert lib.csa_workspace_size(4, 4, 262144, 64) >= 4 * 64 * 512 * 12
 
 
+def _two_phase_bytes(T, H, e_pad, ch):
+    # P' bf16 [T][H][e_pad], chunk statistics float2 [T][H][e_pad / ch], then
+    # the entries' slots int32 [T][e_pad] (value copies of 4 MB or more gather)
+    up = lambda n: (n + 255) // 256 * 256
+    src = up(T * H * e_pad * 2) + up(T * H * (e_pad // ch) * 8)
+    copy = T * e_pad * 512
+    return src + (T * e_pad * 4 if copy >= 4 << 20 else copy)
+
+
+def test_decode_attention_chunk_plan(lib):
+    """Decode attention's phase A takes 64-entry chunks while their grid fits
+    the 256 CUs, else 96-entry chunks when those fit (the workspace size shows
+    which: its chunk statistics and padding follow the chunk length)."""
+    lib.csa_workspace_size.restype = C.c_size_t
+    lib.csa_workspace_size.argtypes = [C.c_int32, C.c_int64, C.c_int64, C.c_int32]
+    csa_attn = 2
+    # 24 queries x 10 chunks of 64: 240 workgroups
+    assert lib.csa_workspace_size(csa_attn, 24, 640, 64) == _two_phase_bytes(24, 64, 640, 64)
+    # 32 queries: 320 workgroups of 64 entries, 224 of 96 (7 chunks, 672 padded)
+    assert lib.csa_workspace_size(csa_attn, 32, 640, 64) == _two_phase_bytes(32, 64, 672, 96)
+    # 48 queries: neither fits one round; 64-entry chunks
+    assert lib.csa_workspace_size(csa_attn, 48, 640, 64) == _two_phase_bytes(48, 64, 640, 64)
+    # 4 queries x 128 heads (value copy, no gather)
+    assert lib.csa_workspace_size(csa_attn, 4, 640, 128) == _two_phase_bytes(4, 128, 640, 64)
+
+
 def test_compress_rejects_bad_arguments(lib):
     f = lib.c4_compress
     f.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
