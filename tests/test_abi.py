@@ -91,7 +91,8 @@ def test_workspace_sizes(lib):
     lib.csa_workspace_size.restype = C.c_size_t
     lib.csa_workspace_size.argtypes = [C.c_int32, C.c_int64, C.c_int64, C.c_int32]
     assert lib.csa_workspace_size(1, 128, 16384, 1) == 0          # one launch per row
-    assert lib.csa_workspace_size(1, 128, 32768, 1) >= 128 * 2 * 512 * 8  # chunked
+    assert lib.csa_workspace_size(1, 128, 32768, 1) == 128 * 2 * 512 * 8  # two 16384-key chunks
+    assert lib.csa_workspace_size(1, 4096, 33792, 1) == 4096 * 9 * 512 * 8  # nine 4096-key chunks
     assert lib.csa_workspace_size(1, 32, 32768, 1) >= 32 * 512 * 8  # chunk candidates
     assert lib.csa_workspace_size(1, 4, 1 << 20, 1) >= 4 * 512 * 8
     assert lib.csa_workspace_size(0, 32, 0, 64) >= 32 * 64 * 132  # prepared query
